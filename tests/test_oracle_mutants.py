@@ -1,0 +1,69 @@
+"""Plants plausible mistakes in a copy of the oracle (on the CPU) and checks
+that the pins catch each one: a dropped term, a wrong sign, index or bit
+order, a transposed operand, a wrong constant."""
+import os
+import subprocess
+
+import pytest
+
+import oracle
+import pins
+
+_SRC = os.path.join(os.path.dirname(os.path.abspath(oracle.__file__)), "bsp_oracle.c")
+
+# (name, [(original text, mutated text), ...]); every original must occur in the source.
+MUTANTS = [
+    ("nibble_order_swapped", [
+        ("if (e % 2 == 0) payload[e / 2]", "if (e % 2 == 1) payload[e / 2]"),
+        ("int code = (e % 2 == 0) ?", "int code = (e % 2 == 1) ?"),
+        ("else            payload[e / 2] = (uint8_t)((payload[e / 2] & 0x0F) | (code << 4));",
+         "else            payload[e / 2] = (uint8_t)((payload[e / 2] & 0x0F) | (code << 4)); /*m*/"),
+    ]),
+    ("rank_skips_bit0", [("for (int i = 0; i < j; ++i)", "for (int i = 1; i < j; ++i)")]),
+    ("bit_order_reversed", [
+        ("word |= (uint64_t)1 << j;", "word |= (uint64_t)1 << (63 - j);"),
+        ("int bit = (int)((word >> j) & 1u);", "int bit = (int)((word >> (63 - j)) & 1u);"),
+    ]),
+    ("sign_extension_off_by_one", [("return code >= 8 ? code - 16 : code;", "return code > 8 ? code - 16 : code;")]),
+    ("x_transposed", [("acc += (int64_t)Wd[m * K + k] * (int64_t)Xd[n * K + k];",
+                       "acc += (int64_t)Wd[m * K + k] * (int64_t)Xd[(k % N) * K + (k / N) + 0 * n];")]),
+    ("matmul_drops_last_k", [("for (int64_t k = 0; k < K; ++k)\n                acc += (int64_t)Wd",
+                              "for (int64_t k = 0; k + 1 < K; ++k)\n                acc += (int64_t)Wd")]),
+    ("decode_uses_previous_offset", [("int64_t e = (int64_t)offsets[g] + or_rank(word, j);",
+                                      "int64_t e = (int64_t)offsets[g > 0 ? g - 1 : 0] + or_rank(word, j);")]),
+    ("offsets_shifted_by_one", [("if (offsets) offsets[g] = (uint32_t)off;",
+                                   "if (offsets) offsets[g] = (uint32_t)(off > 0 ? off - 1 : 0);")]),
+    ("popcount_misses_bit63", [("for (int j = 0; j < 64; ++j)\n        if ((w >> j) & 1u) c++;",
+                                "for (int j = 0; j < 63; ++j)\n        if ((w >> j) & 1u) c++;")]),
+    ("f16_exponent_bias", [("expo - 25", "expo - 24")]),
+    ("f16_subnormal_scale", [("ldexp((double)frac, -24)", "ldexp((double)frac, -25)")]),
+    ("f16_negative_zero_stored", [("return (h & 0x7FFF) == 0;", "return h == 0;")]),
+    ("f16_product_sign_dropped", [("acc += or_f16_to_f64(Wd[m * K + k]) * or_f16_to_f64(Xh[n * K + k]);",
+                                   "acc += fabs(or_f16_to_f64(Wd[m * K + k])) * or_f16_to_f64(Xh[n * K + k]);")]),
+]
+
+
+@pytest.mark.parametrize("name,edits", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_mutant(name, edits, tmp_path):
+    src = open(_SRC).read()
+    for old, new in edits:
+        assert old in src, f"mutation anchor not found: {old!r}"
+        src = src.replace(old, new)
+    c = tmp_path / "mutant.c"
+    c.write_text(src)
+    so = tmp_path / "libmutant.so"
+    subprocess.check_call(["gcc", "-O1", "-std=c99", "-shared", "-fPIC", str(c), "-o", str(so), "-lm"])
+    prev = oracle.swap_library(str(so))
+    caught = []
+    try:
+        for pin in pins.ALL_PINS:
+            try:
+                pin()
+            except AssertionError:
+                caught.append(pin.__name__)
+            except ValueError:
+                caught.append(pin.__name__ + "(error)")
+    finally:
+        oracle.swap_library(None)
+        oracle._lib = prev
+    assert caught, f"no pin catches mutant {name}"

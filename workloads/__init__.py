@@ -1,0 +1,185 @@
+"""Seeded synthetic inputs for the bitmap int4 / fp16 SpMM workloads.
+
+This module only draws random numbers into dense arrays. It holds none of the
+method's arithmetic (no bitmap encoding, no packing, no products): both the
+oracle side and the GPU side start from the dense arrays returned here.
+
+The shapes follow the decode-phase projection / FFN layers that UnionSparse
+(IEEE TCAD, "UnionSparse: An Index-Efficient Sparsity Framework for Low-Bit
+Sparse LLM Inference on Edge") evaluates in Sec. VII-A: W4A4 weights with
+30-70 % unstructured sparsity and decode widths N = 1..32. The fp16 case
+follows SPDP ("Unified Static-Dynamic Pruning for Efficient LLM Inference"),
+Sec. 2.2 (static magnitude pruning with a fixed mask). The pages' model
+weights are not available, so iid masks stand in for pruned real weights.
+
+Recipe (numpy ``default_rng(seed)``, PCG64), draw order inside a config is
+mask -> values -> X:
+
+* int4 nonzeros: ``rng.integers(0, 15)`` mapped d -> d-8 if d < 8 else d-7,
+  i.e. uniform over {-8..-1, 1..7};
+* int4 activations: ``rng.integers(-8, 8)``, uniform over [-8, 7];
+* masks: ``rng.random(dtype=float32) < keep`` per element;
+* per-row density (low-sparsity case): ``rng.uniform(0.6, 0.8, M)`` drawn
+  before the mask, then element kept with its row's probability;
+* fp16 case: W = N(0, 0.02) cast to fp16, then the round(0.6*M*K) entries of
+  smallest |W| (stable argsort on the flat index) are set to +0; X = N(0, 1)
+  cast to fp16.
+
+X is returned as an ``[N][K]`` array (the K x N activation matrix stored
+column by column), drawn at the largest N of the config; a smaller N uses the
+leading rows.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Dict, List, Tuple
+
+import numpy as np
+
+__all__ = ["Problem", "CONFIGS", "make", "int4_nonzero_values", "int4_mask_matrix",
+           "random_int4_problem", "config_names"]
+
+
+@dataclass
+class Problem:
+    """One W (M x K) and X ([N][K]) pair. ``dtype`` is "int4" or "fp16"."""
+    name: str
+    dtype: str
+    W: np.ndarray            # int8 values in [-8, 7] or float16, shape (M, K)
+    X: np.ndarray            # int8 values in [-8, 7] or float16, shape (N, K)
+    meta: Dict[str, object] = field(default_factory=dict)
+
+    @property
+    def M(self) -> int:
+        return int(self.W.shape[0])
+
+    @property
+    def K(self) -> int:
+        return int(self.W.shape[1])
+
+    @property
+    def N(self) -> int:
+        return int(self.X.shape[0])
+
+    def with_n(self, n: int) -> "Problem":
+        """The same W with the first ``n`` activation columns."""
+        if n < 0 or n > self.X.shape[0]:
+            raise ValueError(f"n={n} outside 0..{self.X.shape[0]}")
+        return Problem(self.name, self.dtype, self.W, self.X[:n], dict(self.meta, N=n))
+
+
+def int4_nonzero_values(rng: np.random.Generator, size) -> np.ndarray:
+    d = rng.integers(0, 15, size=size, dtype=np.int16)
+    return np.where(d < 8, d - 8, d - 7).astype(np.int8)
+
+
+def int4_activations(rng: np.random.Generator, size) -> np.ndarray:
+    return rng.integers(-8, 8, size=size, dtype=np.int16).astype(np.int8)
+
+
+def int4_mask_matrix(rng: np.random.Generator, M: int, K: int, keep) -> np.ndarray:
+    """Bernoulli keep-mask. ``keep`` is a scalar or a per-row array of length M."""
+    keep = np.asarray(keep, dtype=np.float32)
+    if keep.ndim == 1:
+        keep = keep[:, None]
+    return rng.random((M, K), dtype=np.float32) < keep
+
+
+def _int4_weights(rng, M, K, keep) -> np.ndarray:
+    mask = int4_mask_matrix(rng, M, K, keep)
+    vals = int4_nonzero_values(rng, (M, K))
+    return np.where(mask, vals, np.int8(0)).astype(np.int8)
+
+
+def random_int4_problem(seed: int, M: int, K: int, N: int, keep: float = 0.5,
+                        name: str = "random") -> Problem:
+    """Small seeded int4 case of any shape (tests, edge cases)."""
+    rng = np.random.default_rng(seed)
+    W = _int4_weights(rng, M, K, keep)
+    X = int4_activations(rng, (N, K))
+    return Problem(name, "int4", W, X, dict(seed=seed, keep=keep, N=N))
+
+
+def random_fp16_problem(seed: int, M: int, K: int, N: int, sparsity: float = 0.6,
+                        name: str = "random_f16") -> Problem:
+    rng = np.random.default_rng(seed)
+    W = _fp16_pruned(rng, M, K, sparsity)
+    X = rng.normal(0.0, 1.0, size=(N, K)).astype(np.float16)
+    return Problem(name, "fp16", W, X, dict(seed=seed, sparsity=sparsity, N=N))
+
+
+def _fp16_pruned(rng, M, K, sparsity) -> np.ndarray:
+    W = rng.normal(0.0, 0.02, size=(M, K)).astype(np.float16)
+    n_prune = int(round(sparsity * M * K))
+    flat = W.reshape(-1)
+    order = np.argsort(np.abs(flat.astype(np.float32)), kind="stable")
+    flat[order[:n_prune]] = np.float16(0.0)
+    return flat.reshape(M, K)
+
+
+# ---------------------------------------------------------------------------
+# The five named workloads.
+
+def _c1() -> List[Problem]:
+    rng = np.random.default_rng(0)
+    W = _int4_weights(rng, 512, 512, 0.5)
+    X = int4_activations(rng, (1, 512))
+    return [Problem("tiny_512x512_n1", "int4", W, X, dict(seed=0, keep=0.5, N=1))]
+
+
+def _c2() -> List[Problem]:
+    rng = np.random.default_rng(1)
+    W = _int4_weights(rng, 12288, 4096, 0.5)
+    X = int4_activations(rng, (32, 4096))   # drawn at 32 so the N sweep shares one X
+    return [Problem("qkv_12288x4096", "int4", W, X[:8], dict(seed=1, keep=0.5, N=8, X_full=X))]
+
+
+def _c3() -> List[Problem]:
+    rng = np.random.default_rng(2)
+    Wu = _int4_weights(rng, 11008, 4096, 0.3)
+    Xu = int4_activations(rng, (16, 4096))
+    Wd = _int4_weights(rng, 4096, 11008, 0.3)
+    Xd = int4_activations(rng, (16, 11008))
+    return [Problem("ffn_up_11008x4096", "int4", Wu, Xu, dict(seed=2, keep=0.3, N=16)),
+            Problem("ffn_down_4096x11008", "int4", Wd, Xd, dict(seed=2, keep=0.3, N=16))]
+
+
+def _c4() -> List[Problem]:
+    rng = np.random.default_rng(3)
+    dens = rng.uniform(0.6, 0.8, size=8192)
+    W = _int4_weights(rng, 8192, 8192, dens)
+    X = int4_activations(rng, (32, 8192))
+    return [Problem("lowsparse_8192x8192", "int4", W, X, dict(seed=3, keep="U[0.6,0.8] per row", N=32))]
+
+
+def _c5() -> List[Problem]:
+    rng = np.random.default_rng(4)
+    W = _fp16_pruned(rng, 4096, 4096, 0.6)
+    X = rng.normal(0.0, 1.0, size=(32, 4096)).astype(np.float16)
+    return [Problem("fp16_4096x4096_n1", "fp16", W, X[:1], dict(seed=4, sparsity=0.6, N=1)),
+            Problem("fp16_4096x4096_n32", "fp16", W, X, dict(seed=4, sparsity=0.6, N=32))]
+
+
+CONFIGS = {
+    "tiny": _c1,
+    "qkv": _c2,
+    "ffn": _c3,
+    "lowsparse": _c4,
+    "fp16": _c5,
+}
+
+
+def config_names() -> List[str]:
+    return list(CONFIGS)
+
+
+_CACHE: Dict[str, List[Problem]] = {}
+
+
+def make(config: str) -> List[Problem]:
+    """Problems of a named workload (cached per process)."""
+    if config not in CONFIGS:
+        raise KeyError(f"unknown workload {config!r}; have {list(CONFIGS)}")
+    if config not in _CACHE:
+        _CACHE[config] = CONFIGS[config]()
+    return _CACHE[config]

@@ -1,0 +1,259 @@
+"""Bitmap-tiled int4 / fp16 sparse x dense matmul on AMD MI355X (gfx950).
+
+A thin ctypes binding over ``libbitmap_spmm.so`` (C ABI in
+``include/bitmap_spmm.h``). Host arrays are numpy; device memory and streams
+come from PyTorch tensors. Every step of the SpMM runs in the library's HIP
+kernels; there is no CPU fallback: if the library is missing, importing the
+SpMM functions raises.
+
+    import bit_unstructured_sparse_amd as bsp
+    enc = bsp.encode(W_int8)                 # host, UnionSparse Sec. V-A with Q = 1
+    dev = enc.to_device("cuda")              # torch tensors
+    Xp  = bsp.pack_int4(X_int8)              # [N][ceil(K/2)] bytes
+    Y   = bsp.spmm_w4a4(dev, torch.from_numpy(Xp).cuda(), N)   # int32 [N][M]
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+
+__all__ = ["load_library", "encode", "pack_int4", "Encoded", "DeviceMatrix", "spmm_w4a4", "spmm_f16",
+           "select", "describe", "BspError", "ALGO_AUTO", "ALGO_ROWWAVE", "ALGO_VALU", "ALGO_MFMA",
+           "INT4", "FP16", "PAYLOAD_ALIGN", "MAX_N", "library_path"]
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(HERE, "libbitmap_spmm.so")
+
+OK, E_ARG, E_RANGE, E_CAPACITY, E_OVERFLOW, E_HIP = 0, 1, 2, 3, 4, 5
+INT4, FP16 = 0, 1
+ALGO_AUTO, ALGO_ROWWAVE, ALGO_VALU, ALGO_MFMA = 0, 1, 2, 3
+PAYLOAD_ALIGN = 16
+MAX_N = 32
+
+# Every symbol include/bitmap_spmm.h declares.
+EXPORTS = ["encode_bitmap_tiles", "pack_int4_activations", "spmm_bitmap_w4a4", "spmm_bitmap_w4a4_algo",
+           "spmm_bitmap_f16", "spmm_bitmap_f16_algo", "bsp_select", "bsp_describe_selection",
+           "bsp_status_string", "bsp_version"]
+
+
+class BspError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+
+
+_lib = None
+
+
+def load_library():
+    """Load libbitmap_spmm.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(library_path):
+            raise ImportError(f"{library_path} is missing; build it with "
+                              "`python -m bit_unstructured_sparse_amd.build`")
+        L = ctypes.CDLL(library_path)
+        P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        L.encode_bitmap_tiles.argtypes = [I32, P, I64, I64, I64, P, P, P, I64, P, P]
+        L.encode_bitmap_tiles.restype = I32
+        L.pack_int4_activations.argtypes, L.pack_int4_activations.restype = [P, I64, I64, I64, P], I32
+        L.spmm_bitmap_w4a4.argtypes = [P, P, P, I64, I64, I64, P, I64, P, P]
+        L.spmm_bitmap_w4a4.restype = I32
+        L.spmm_bitmap_w4a4_algo.argtypes = [P, P, P, I64, I64, I64, P, I64, P, I32, P]
+        L.spmm_bitmap_w4a4_algo.restype = I32
+        L.spmm_bitmap_f16.argtypes = [P, P, P, I64, I64, I64, P, I64, P, P]
+        L.spmm_bitmap_f16.restype = I32
+        L.spmm_bitmap_f16_algo.argtypes = [P, P, P, I64, I64, I64, P, I64, P, I32, P]
+        L.spmm_bitmap_f16_algo.restype = I32
+        L.bsp_select.argtypes, L.bsp_select.restype = [I32, I64, I64, I64, I64], I32
+        L.bsp_describe_selection.argtypes = [I32, I64, I64, I64, I64, ctypes.c_char_p, ctypes.c_size_t]
+        L.bsp_describe_selection.restype = I32
+        L.bsp_status_string.argtypes, L.bsp_status_string.restype = [I32], ctypes.c_char_p
+        L.bsp_version.argtypes, L.bsp_version.restype = [], ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return load_library().bsp_status_string(status).decode()
+
+
+def _np_ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _check(rc: int, what: str):
+    if rc != OK:
+        raise BspError(rc, what)
+
+
+@dataclass
+class Encoded:
+    """Host-side BT64 stream: bitmaps uint64[M*T], offsets uint32[M*T+1],
+    payload uint8[ceil(nnz/2)] (int4) or uint16[nnz] (fp16)."""
+    dtype: int
+    M: int
+    K: int
+    nnz: int
+    bitmaps: np.ndarray
+    offsets: np.ndarray
+    payload: np.ndarray
+
+    @property
+    def T(self) -> int:
+        return (self.K + 63) // 64
+
+    @property
+    def payload_bytes(self) -> int:
+        return int(self.payload.nbytes)
+
+    def to_device(self, device="cuda") -> "DeviceMatrix":
+        import torch
+        pad = (-self.payload_bytes) % PAYLOAD_ALIGN
+        raw = np.zeros(self.payload_bytes + pad, np.uint8)
+        raw[: self.payload_bytes] = self.payload.view(np.uint8)
+        if raw.size == 0:
+            raw = np.zeros(PAYLOAD_ALIGN, np.uint8)
+        return DeviceMatrix(
+            dtype=self.dtype, M=self.M, K=self.K, nnz=self.nnz,
+            bitmaps=torch.from_numpy(self.bitmaps.view(np.int64)).to(device),
+            offsets=torch.from_numpy(self.offsets.view(np.int32)).to(device),
+            payload=torch.from_numpy(raw).to(device))
+
+
+@dataclass
+class DeviceMatrix:
+    """The BT64 stream in device memory (torch tensors). ``payload`` is padded
+    with zeros to a whole number of PAYLOAD_ALIGN bytes."""
+    dtype: int
+    M: int
+    K: int
+    nnz: int
+    bitmaps: "object"
+    offsets: "object"
+    payload: "object"
+
+    @property
+    def T(self) -> int:
+        return (self.K + 63) // 64
+
+    def stream_bytes(self, with_offsets: bool = True) -> int:
+        """Bytes of the encoded stream proper (unpadded payload)."""
+        G = self.M * self.T
+        pb = (self.nnz + 1) // 2 if self.dtype == INT4 else 2 * self.nnz
+        return 8 * G + (4 * (G + 1) if with_offsets else 0) + pb
+
+
+def encode(W: np.ndarray) -> Encoded:
+    """Encode a dense host matrix: int8 (int4 values in [-8, 7]) or float16."""
+    L = load_library()
+    if W.dtype == np.int8:
+        dt = INT4
+    elif W.dtype == np.float16:
+        dt = FP16
+        W = W.view(np.uint16)
+    elif W.dtype == np.uint16:
+        dt = FP16
+    else:
+        raise TypeError("W must be int8 (int4 values) or float16")
+    if W.ndim != 2:
+        raise ValueError("W must be 2-D")
+    M, K = W.shape
+    ldw = W.strides[0] // W.itemsize if W.strides[1] == W.itemsize else None
+    if ldw is None or ldw < K:
+        W = np.ascontiguousarray(W)
+        ldw = K
+    nnz, nbytes = ctypes.c_int64(0), ctypes.c_int64(0)
+    _check(L.encode_bitmap_tiles(dt, _np_ptr(W), M, K, ldw, None, None, None, 0,
+                                 ctypes.byref(nnz), ctypes.byref(nbytes)), "encode_bitmap_tiles (size)")
+    T = (K + 63) // 64
+    bitmaps = np.empty(M * T, np.uint64)
+    offsets = np.empty(M * T + 1, np.uint32)
+    payload = np.empty(nnz.value if dt == FP16 else nbytes.value, np.uint16 if dt == FP16 else np.uint8)
+    _check(L.encode_bitmap_tiles(dt, _np_ptr(W), M, K, ldw, _np_ptr(bitmaps), _np_ptr(offsets),
+                                 _np_ptr(payload), payload.nbytes, ctypes.byref(nnz), ctypes.byref(nbytes)),
+           "encode_bitmap_tiles")
+    return Encoded(dt, M, K, int(nnz.value), bitmaps, offsets, payload)
+
+
+def pack_int4(X: np.ndarray) -> np.ndarray:
+    """int8 [N][K] activations in [-8, 7] -> packed uint8 [N][ceil(K/2)]."""
+    if X.dtype != np.int8 or X.ndim != 2:
+        raise TypeError("X must be a 2-D int8 array")
+    X = np.ascontiguousarray(X)
+    N, K = X.shape
+    out = np.zeros((N, (K + 1) // 2), np.uint8)
+    _check(load_library().pack_int4_activations(_np_ptr(X), N, K, K, _np_ptr(out)), "pack_int4_activations")
+    return out
+
+
+def _dptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream_handle(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check_dev(t, name, dtype, numel=None):
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} has {t.numel()} elements, expected {numel}")
+
+
+def spmm_w4a4(W: DeviceMatrix, X, N: int, Y=None, algo: int = ALGO_AUTO, stream=None):
+    """Y[n][m] = sum_k W[m][k] X[k][n] (int32) on the GPU. X: uint8 [N][ceil(K/2)]."""
+    import torch
+    if W.dtype != INT4:
+        raise TypeError("spmm_w4a4 needs an int4 DeviceMatrix")
+    _check_dev(X, "X", torch.uint8, N * ((W.K + 1) // 2))
+    if Y is None:
+        Y = torch.empty((N, W.M), dtype=torch.int32, device=X.device)
+    _check_dev(Y, "Y", torch.int32, N * W.M)
+    rc = load_library().spmm_bitmap_w4a4_algo(
+        _dptr(W.bitmaps), _dptr(W.offsets), _dptr(W.payload), W.payload.numel(), W.M, W.K,
+        _dptr(X), N, _dptr(Y), algo, _stream_handle(stream))
+    _check(rc, "spmm_bitmap_w4a4")
+    return Y
+
+
+def spmm_f16(W: DeviceMatrix, X, Y=None, algo: int = ALGO_AUTO, stream=None):
+    """fp16 Y [N][M] = W X with fp32 accumulation. X: float16 [N][K]."""
+    import torch
+    if W.dtype != FP16:
+        raise TypeError("spmm_f16 needs an fp16 DeviceMatrix")
+    if X.dim() != 2 or X.shape[1] != W.K:
+        raise ValueError("X must be [N][K]")
+    N = int(X.shape[0])
+    _check_dev(X, "X", torch.float16)
+    if Y is None:
+        Y = torch.empty((N, W.M), dtype=torch.float16, device=X.device)
+    _check_dev(Y, "Y", torch.float16, N * W.M)
+    rc = load_library().spmm_bitmap_f16_algo(
+        _dptr(W.bitmaps), _dptr(W.offsets), _dptr(W.payload), W.payload.numel(), W.M, W.K,
+        _dptr(X), N, _dptr(Y), algo, _stream_handle(stream))
+    _check(rc, "spmm_bitmap_f16")
+    return Y
+
+
+def select(dtype: int, M: int, K: int, N: int, nnz: int = -1) -> int:
+    return int(load_library().bsp_select(dtype, M, K, N, nnz))
+
+
+def describe(dtype: int, M: int, K: int, N: int, nnz: int = -1) -> str:
+    buf = ctypes.create_string_buffer(256)
+    _check(load_library().bsp_describe_selection(dtype, M, K, N, nnz, buf, 256), "bsp_describe_selection")
+    return buf.value.decode()

@@ -1,0 +1,186 @@
+/*
+ * bitmap_spmm.h -- C ABI of the bitmap-tiled sparse x dense matmul for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * Computes Y = W_sparse * X, the problem statement of SPDP ("Unified
+ * Static-Dynamic Pruning for Efficient LLM Inference", Sec. 2.2) and of the
+ * UnionSparse SpMM kernel ("UnionSparse: An Index-Efficient Sparsity
+ * Framework for Low-Bit Sparse LLM Inference on Edge", IEEE TCAD, Sec. VI),
+ * for the decode-phase shapes those pages study: W is M x K with 30-70 %
+ * unstructured sparsity, X is a skinny K x N activation matrix, N = 1..32.
+ *
+ * ---------------------------------------------------------------------------
+ * Encoded format ("BT64"): UnionSparse Sec. V-A, "IE-BME Representation",
+ * with one area per tile (R_A = C_A = 1, Q = 1) on 1 x 64 row tiles.
+ *   T = ceil(K/64) tiles per row; G = M*T tiles; tile g = m*T + t covers
+ *   columns 64t .. 64t+63 of row m (row-major tile order).
+ *   bitmaps[g]   uint64. Bit j is set iff W[m][64t+j] != 0; bit 0 is the
+ *                first column (the LSB-first packing of the Fig. 7 example).
+ *                Bits of columns >= K are zero.
+ *   offsets[g]   uint32, the number of nonzeros in tiles 0..g-1 ("Union Value
+ *                Offsets" with Q = 1); offsets[G] = nnz. G+1 entries.
+ *   payload      the nonzeros in tile order and, inside a tile, in column
+ *                order: value (m, 64t+j) is element offsets[g] + rank, rank =
+ *                popcount(bitmaps[g] & ((1<<j)-1)) ("Compressed Values").
+ *                int4: element e is byte e>>1, low nibble when e is even, a
+ *                4-bit two's-complement code; ceil(nnz/2) bytes, an odd count
+ *                leaves the final high nibble zero.
+ *                fp16: element e is uint16 e (IEEE binary16 bits); 2*nnz bytes.
+ * Activations: X is K x N stored column by column, i.e. an [N][K] array.
+ *   int4: packed along K, two per byte, low nibble = even k, row stride
+ *   ceil(K/2) bytes. fp16: row stride K elements.
+ * Output: Y is M x N stored column by column, i.e. [N][M]; int32 for the int4
+ *   path, fp16 for the fp16 path. Y is fully overwritten, never accumulated.
+ * ---------------------------------------------------------------------------
+ *
+ * Conventions
+ *   - Every entry point returns a bsp_status. No C++ exception crosses the ABI.
+ *   - Arguments are checked on the host before any HIP call, so a bad call
+ *     returns an error code without touching the GPU.
+ *   - SpMM calls are asynchronous on `stream` (NULL = the null stream); a fault
+ *     inside a kernel surfaces at the caller's next synchronisation. The
+ *     content of the encoded stream is not validated on the device (that
+ *     would cost a full extra pass over HBM): a corrupt stream gives a wrong
+ *     Y, never an out-of-bounds access, because every payload read is bounded
+ *     by `payload_bytes` in hardware (buffer-resource loads).
+ *   - The calls hold no state between calls, allocate no memory and are
+ *     reentrant; concurrent calls on different streams are allowed.
+ */
+#ifndef BITMAP_SPMM_H
+#define BITMAP_SPMM_H
+
+#include <stdint.h>
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum bsp_status {
+    BSP_OK = 0,
+    BSP_E_ARG = 1,       /* null pointer, negative size, N > 32, ldw < K, unknown dtype/algo */
+    BSP_E_RANGE = 2,     /* an int4 weight outside [-8, 7] */
+    BSP_E_CAPACITY = 3,  /* payload buffer smaller than the encoded payload */
+    BSP_E_OVERFLOW = 4,  /* nnz >= 2^32, K >= 2^25 (int32 sums could overflow), or an index beyond 2^31 */
+    BSP_E_HIP = 5        /* a HIP launch error (hipGetLastError after the launch) */
+} bsp_status;
+
+typedef enum bsp_dtype { BSP_INT4 = 0, BSP_FP16 = 1 } bsp_dtype;
+
+/* Kernel choice for the *_algo entry points. BSP_ALGO_AUTO applies the
+ * library's shape-aware selection (by N, density, M, K). */
+typedef enum bsp_algo {
+    BSP_ALGO_AUTO = 0,
+    BSP_ALGO_ROWWAVE = 1,   /* one wavefront per output row; plain per-nonzero decode */
+    BSP_ALGO_VALU = 2,      /* lane-per-tile SWAR decode + dot8 / fp32 FMA contraction */
+    BSP_ALGO_MFMA = 3       /* lane-per-tile SWAR decode + int8 / fp16 MFMA contraction */
+} bsp_algo;
+
+/* The device payload allocation handed to the SpMM calls is a whole number
+ * of 16-byte units (zero-filled past the encoded payload): kernels read it in
+ * whole dwords, and the hardware range check is applied to whole dwords. */
+#define BSP_PAYLOAD_ALIGN 16
+
+/* Largest N the SpMM entry points accept. */
+#define BSP_MAX_N 32
+/* K bound that keeps every int4 x int4 sum inside int32: |Y| <= 64*K < 2^31. */
+#define BSP_MAX_K ((int64_t)1 << 25)
+
+/*
+ * encode_bitmap_tiles -- host-side encoder (UnionSparse Sec. V-A, Q = 1 on
+ * 1 x 64 tiles; the encoded form is produced offline and cached, Sec. V-B).
+ *
+ *   dtype    BSP_INT4: W is const int8_t*, values in [-8, 7];
+ *            BSP_FP16: W is const uint16_t* holding IEEE binary16 bits
+ *            (+0 and -0 are zero; every other pattern, NaN included, is stored).
+ *   W        HOST memory, row-major M x K with leading dimension ldw >= K.
+ *   bitmaps  HOST, caller-allocated, M*T entries (T = ceil(K/64)), or NULL.
+ *   offsets  HOST, caller-allocated, M*T+1 entries, or NULL.
+ *   payload  HOST, caller-allocated, payload_capacity_bytes bytes, or NULL for
+ *            a size query (then bitmaps/offsets may also be NULL).
+ *   nnz_out, payload_bytes_out  written on BSP_OK and on BSP_E_CAPACITY
+ *            (either may be NULL). payload_bytes = ceil(nnz/2) (int4) or
+ *            2*nnz (fp16).
+ * Returns BSP_E_ARG, BSP_E_RANGE (nothing written), BSP_E_OVERFLOW
+ * (nnz >= 2^32), BSP_E_CAPACITY (counts written, arrays untouched) or BSP_OK.
+ * Multi-threaded over rows; the output does not depend on the thread count.
+ */
+int encode_bitmap_tiles(int dtype, const void *W, int64_t M, int64_t K, int64_t ldw,
+                        uint64_t *bitmaps, uint32_t *offsets,
+                        void *payload, int64_t payload_capacity_bytes,
+                        int64_t *nnz_out, int64_t *payload_bytes_out);
+
+/*
+ * pack_int4_activations -- host helper that writes int4 activations in the
+ * layout the SpMM reads: X (values in [-8, 7], HOST [N][K] int8, row stride
+ * ldx >= K) -> Xp (HOST, N * ceil(K/2) bytes). Returns BSP_E_RANGE for a
+ * value outside [-8, 7] (Xp then undefined).
+ */
+int pack_int4_activations(const int8_t *X, int64_t N, int64_t K, int64_t ldx, uint8_t *Xp);
+
+/*
+ * spmm_bitmap_w4a4 -- Y = W * X with int4 W (BT64 stream) and int4 X, exact
+ * int32 result (UnionSparse Sec. VI; W4A4 decode shapes of Sec. VII-A).
+ *
+ *   bitmaps, offsets, payload   DEVICE, the encoded W (M*T, M*T+1 entries and
+ *                               payload_bytes bytes); payload may be NULL only
+ *                               if payload_bytes == 0.
+ *   payload_bytes               size of the payload allocation: a multiple of
+ *                               BSP_PAYLOAD_ALIGN, >= ceil(nnz/2), bytes past the
+ *                               encoded payload zero. No byte at or past it is read.
+ *   M, K                        0 <= M < 2^31, 0 <= K < 2^25, M*ceil(K/64) < 2^31.
+ *   X                           DEVICE, [N][ceil(K/2)] packed int4.
+ *   N                           0..32. N == 0 or M == 0: nothing is launched.
+ *   Y                           DEVICE, [N][M] int32, fully overwritten (K == 0 gives zeros).
+ *   stream                      HIP stream (NULL = null stream).
+ * Exact: int32 sums are associative and cannot overflow under the K bound,
+ * so every kernel gives the same bits.
+ */
+int spmm_bitmap_w4a4(const uint64_t *bitmaps, const uint32_t *offsets, const uint8_t *payload,
+                     int64_t payload_bytes, int64_t M, int64_t K,
+                     const uint8_t *X, int64_t N, int32_t *Y, hipStream_t stream);
+
+/* As spmm_bitmap_w4a4 with an explicit kernel choice (bsp_algo). */
+int spmm_bitmap_w4a4_algo(const uint64_t *bitmaps, const uint32_t *offsets, const uint8_t *payload,
+                          int64_t payload_bytes, int64_t M, int64_t K,
+                          const uint8_t *X, int64_t N, int32_t *Y, int algo, hipStream_t stream);
+
+/*
+ * spmm_bitmap_f16 -- fp16 variant (SPDP Sec. 4: FP16 values in a bitmap
+ * format, decoded with a masked-popcount rank): payload is uint16[nnz]
+ * (payload_bytes >= 2*nnz, a multiple of BSP_PAYLOAD_ALIGN), X is fp16 [N][K],
+ * Y is fp16 [N][M]. Products and
+ * sums in fp32 (any order), one round-to-nearest-even to fp16 at the end.
+ * Other arguments as spmm_bitmap_w4a4.
+ */
+int spmm_bitmap_f16(const uint64_t *bitmaps, const uint32_t *offsets, const uint16_t *payload,
+                    int64_t payload_bytes, int64_t M, int64_t K,
+                    const uint16_t *X, int64_t N, uint16_t *Y, hipStream_t stream);
+
+int spmm_bitmap_f16_algo(const uint64_t *bitmaps, const uint32_t *offsets, const uint16_t *payload,
+                         int64_t payload_bytes, int64_t M, int64_t K,
+                         const uint16_t *X, int64_t N, uint16_t *Y, int algo, hipStream_t stream);
+
+/*
+ * bsp_select -- the kernel BSP_ALGO_AUTO picks for a problem (shape-aware
+ * selection; UnionSparse Sec. I names it, without a rule). nnz may be -1 when
+ * unknown. Returns a bsp_algo value, or -1 for invalid arguments. Host only.
+ */
+int bsp_select(int dtype, int64_t M, int64_t K, int64_t N, int64_t nnz);
+
+/* Human-readable description of bsp_select's choice and launch shape, written
+ * NUL-terminated into buf (at most n bytes). Returns bsp_status. Host only. */
+int bsp_describe_selection(int dtype, int64_t M, int64_t K, int64_t N, int64_t nnz, char *buf, size_t n);
+
+/* Static string for a bsp_status code. */
+const char *bsp_status_string(int status);
+
+/* Library version as "major.minor.patch". */
+const char *bsp_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BITMAP_SPMM_H */

@@ -1,0 +1,193 @@
+"""GPU parity: every kernel of the library against the CPU oracle.
+
+int4 results must match bit for bit; fp16 results must meet the documented
+tolerance (max floored relative error <= 1e-2 against the fp64 reference).
+Inputs are the seeded workloads; expected values come only from ``oracle``.
+Every call goes through the C ABI (``libbitmap_spmm.so``) via the binding.
+"""
+import functools
+
+import numpy as np
+import pytest
+
+import bit_unstructured_sparse_amd as bsp
+import oracle
+import workloads
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+INT4_ALGOS = [bsp.ALGO_AUTO, bsp.ALGO_ROWWAVE, bsp.ALGO_VALU, bsp.ALGO_MFMA]
+F16_ALGOS = [bsp.ALGO_AUTO, bsp.ALGO_ROWWAVE, bsp.ALGO_VALU, bsp.ALGO_MFMA]
+SENTINEL = -0x21524111   # 0xDEADBEEF as int32
+F16_TOL = 1e-2
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    return torch.device("cuda:0")
+
+
+def _y_with_canary(N, M, dtype, dev):
+    """Output buffer followed by 256 sentinel elements (out-of-bounds write check)."""
+    big = torch.full((N * M + 256,), SENTINEL if dtype == torch.int32 else -1, dtype=torch.int32, device=dev)
+    if dtype == torch.int32:
+        return big, big[: N * M].view(N, M)
+    raw = big.view(torch.int16)
+    return raw, raw[: N * M].view(torch.float16).view(N, M)
+
+
+def _canary_ok(big, N, M, dtype):
+    if dtype == torch.int32:
+        return bool((big[N * M:] == SENTINEL).all().item())
+    return bool((big[N * M:] == -1).all().item())
+
+
+def run_w4a4(W_int8, X_int8, algo, dev, enc=None):
+    enc = enc or bsp.encode(W_int8)
+    dm = enc.to_device(dev)
+    N = X_int8.shape[0]
+    Xd = torch.from_numpy(bsp.pack_int4(X_int8)).to(dev)
+    big, Y = _y_with_canary(N, enc.M, torch.int32, dev)
+    bsp.spmm_w4a4(dm, Xd, N, Y=Y, algo=algo)
+    torch.cuda.synchronize()
+    assert _canary_ok(big, N, enc.M, torch.int32), "write past the end of Y"
+    return Y.cpu().numpy()
+
+
+def run_f16(W_f16, X_f16, algo, dev, enc=None):
+    enc = enc or bsp.encode(W_f16)
+    dm = enc.to_device(dev)
+    N = X_f16.shape[0]
+    Xd = torch.from_numpy(np.ascontiguousarray(X_f16)).to(dev)
+    big, Y = _y_with_canary(N, enc.M, torch.float16, dev)
+    bsp.spmm_f16(dm, Xd, Y=Y, algo=algo)
+    torch.cuda.synchronize()
+    assert _canary_ok(big.view(torch.int16), N, enc.M, torch.float16), "write past the end of Y"
+    return Y.cpu().numpy()
+
+
+def oracle_w4a4(W, X):
+    s = oracle.encode(W)
+    return oracle.spmm_w4a4(s, _pack_for_oracle(X), X.shape[0])
+
+
+def _pack_for_oracle(X):
+    # the oracle consumes the packed layout; pack with the test-side packer that the
+    # golden layout file pins (tests/pins.py), independent of the library's packer
+    import pins
+    return pins._pack_x_for_test(X)
+
+
+SMALL_INT4 = [  # (M, K, N, keep)
+    (1, 1, 1, 1.0), (1, 64, 1, 0.5), (3, 63, 2, 0.5), (5, 65, 3, 0.5), (64, 64, 8, 0.5),
+    (65, 130, 3, 0.5), (17, 127, 31, 0.5), (257, 1000, 16, 0.3), (129, 64 * 67 + 17, 32, 0.7),
+    (300, 64 * 40, 5, 0.5), (97, 4096, 8, 0.5), (1024, 512, 4, 0.5), (33, 777, 7, 1.0),
+    (40, 333, 9, 0.0), (2, 2048, 32, 0.05), (512, 64 * 172, 16, 0.3),
+]
+
+
+@pytest.mark.parametrize("algo", INT4_ALGOS)
+@pytest.mark.parametrize("M,K,N,keep", SMALL_INT4)
+def test_w4a4_small(dev, algo, M, K, N, keep):
+    p = workloads.random_int4_problem(M * 7 + K * 3 + N, M, K, N, keep=keep)
+    Y = run_w4a4(p.W, p.X, algo, dev)
+    assert np.array_equal(Y, oracle_w4a4(p.W, p.X))
+
+
+@pytest.mark.parametrize("algo", INT4_ALGOS)
+def test_w4a4_extremes(dev, algo):
+    # every weight and activation at -8: the largest magnitude products
+    M, K, N = 70, 64 * 33 + 5, 32
+    W = np.full((M, K), -8, np.int8)
+    W[::3, ::5] = 7
+    X = np.full((N, K), -8, np.int8)
+    X[1::2] = 7
+    assert np.array_equal(run_w4a4(W, X, algo, dev), oracle_w4a4(W, X))
+
+
+@pytest.mark.parametrize("algo", INT4_ALGOS)
+def test_w4a4_k_zero(dev, algo):
+    W = np.zeros((9, 0), np.int8)
+    X = np.zeros((3, 0), np.int8)
+    Y = run_w4a4(W, X, algo, dev)
+    assert Y.shape == (3, 9) and not Y.any()
+
+
+@pytest.mark.parametrize("algo", INT4_ALGOS)
+@pytest.mark.parametrize("N", list(range(1, 33)))
+def test_w4a4_every_n(dev, algo, N):
+    p = workloads.random_int4_problem(77, 200, 64 * 9 + 33, 32, keep=0.5)
+    Y = run_w4a4(p.W, p.X[:N], algo, dev)
+    assert np.array_equal(Y, oracle_w4a4(p.W, p.X[:N]))
+
+
+SMALL_F16 = [(1, 1, 1), (3, 63, 2), (65, 130, 32), (257, 1000, 1), (129, 64 * 67 + 17, 17), (64, 4096, 8),
+             (500, 64 * 20, 32)]
+
+
+def _assert_f16(y, r):
+    e = oracle.fp16_error(y, r)
+    assert e["nonfinite"] == 0, e
+    assert e["max_rel_floored"] <= F16_TOL, e
+
+
+@pytest.mark.parametrize("algo", F16_ALGOS)
+@pytest.mark.parametrize("M,K,N", SMALL_F16)
+def test_f16_small(dev, algo, M, K, N):
+    p = workloads.random_fp16_problem(M + K + N, M, K, N)
+    y = run_f16(p.W, p.X, algo, dev).astype(np.float64)
+    _assert_f16(y, oracle.spmm_f16(oracle.encode(p.W), p.X))
+
+
+@pytest.mark.parametrize("algo", F16_ALGOS)
+def test_f16_zero_and_dense(dev, algo):
+    W = np.zeros((33, 100), np.float16)
+    X = np.ones((2, 100), np.float16)
+    assert not run_f16(W, X, algo, dev).any()
+    p = workloads.random_fp16_problem(3, 40, 256, 4, sparsity=0.0)
+    _assert_f16(run_f16(p.W, p.X, algo, dev).astype(np.float64), oracle.spmm_f16(oracle.encode(p.W), p.X))
+
+
+# --- the named workloads at their full sizes -------------------------------------------------
+
+@functools.lru_cache(maxsize=None)
+def _full_int4(config, idx, nmax):
+    p = workloads.make(config)[idx]
+    X = p.meta.get("X_full", p.X)[:nmax] if nmax else p.X
+    s = oracle.encode(p.W)
+    return p, X, oracle.spmm_w4a4(s, _pack_for_oracle(X), X.shape[0])
+
+
+@functools.lru_cache(maxsize=None)
+def _full_f16(idx):
+    p = workloads.make("fp16")[idx]
+    return p, oracle.spmm_f16(oracle.encode(p.W), p.X)
+
+
+FULL_INT4 = [("tiny", 0), ("qkv", 0), ("ffn", 0), ("ffn", 1), ("lowsparse", 0)]
+
+
+@pytest.mark.parametrize("algo", INT4_ALGOS)
+@pytest.mark.parametrize("config,idx", FULL_INT4)
+def test_w4a4_full_workload(dev, algo, config, idx):
+    p, X, ref = _full_int4(config, idx, 0)
+    Y = run_w4a4(p.W, X, algo, dev)
+    assert np.array_equal(Y, ref)
+
+
+@pytest.mark.parametrize("algo", INT4_ALGOS)
+@pytest.mark.parametrize("N", [1, 2, 4, 8, 16, 32])
+def test_w4a4_qkv_n_sweep(dev, algo, N):
+    p, X, ref = _full_int4("qkv", 0, 32)
+    Y = run_w4a4(p.W, X[:N], algo, dev)
+    assert np.array_equal(Y, ref[:N])
+
+
+@pytest.mark.parametrize("algo", F16_ALGOS)
+@pytest.mark.parametrize("idx", [0, 1])
+def test_f16_full_workload(dev, algo, idx):
+    p, r = _full_f16(idx)
+    y = run_f16(p.W, p.X, algo, dev).astype(np.float64)
+    _assert_f16(y, r)

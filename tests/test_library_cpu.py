@@ -1,0 +1,151 @@
+"""Host-side checks of the product library (no GPU needed): it loads, exports
+every symbol the header declares, its encoder is byte-identical to the
+oracle's reference encoder, and bad SpMM arguments are rejected on the host
+before any HIP call."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import bit_unstructured_sparse_amd as bsp
+import oracle
+import pins
+import workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "bitmap_spmm.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?(?:int|char\s*\*|const char\s*\*)\s*\*?\s*(\w+)\s*\(", src, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = bsp.load_library()
+    names = _declared_functions()
+    assert len(names) >= 10, names
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in include/bitmap_spmm.h but not exported"
+    assert sorted(bsp.EXPORTS) == names
+    assert bsp.load_library().bsp_version().decode().count(".") == 2
+
+
+def _same(e, s):
+    return (e.nnz == s.nnz and np.array_equal(e.bitmaps, s.bitmaps) and np.array_equal(e.offsets, s.offsets)
+            and np.array_equal(e.payload, s.payload))
+
+
+@pytest.mark.parametrize("M,K,keep", [(1, 1, 1.0), (3, 63, 0.5), (2, 64, 0.5), (5, 65, 0.3), (7, 127, 0.7),
+                                      (64, 128, 0.5), (129, 300, 0.5), (1000, 77, 0.37), (517, 513, 0.5),
+                                      (300, 64, 0.0), (257, 1, 0.5), (0, 10, 0.5), (10, 0, 0.5)])
+def test_encoder_byte_identical_to_oracle(M, K, keep):
+    p = workloads.random_int4_problem(M * 131 + K, M, K, 1, keep=keep)
+    e = bsp.encode(p.W)
+    s = oracle.encode(p.W)
+    assert _same(e, s)
+    assert oracle.validate_arrays(0, e.bitmaps, e.offsets, e.payload, M, K) == 0
+
+
+def test_encoder_thread_boundaries_odd_rows():
+    # every row holds an odd count, so thread blocks start and end mid-byte
+    rng = np.random.default_rng(5)
+    for M in (128, 129, 640, 1031):
+        W = np.zeros((M, 200), np.int8)
+        for m in range(M):
+            cnt = 2 * int(rng.integers(0, 50)) + 1
+            cols = rng.choice(200, cnt, replace=False)
+            W[m, cols] = rng.integers(1, 8, cnt) * rng.choice([-1, 1], cnt)
+        assert _same(bsp.encode(W), oracle.encode(W))
+
+
+def test_encoder_fp16_byte_identical():
+    for i, (M, K) in enumerate([(33, 200), (200, 64), (5, 1)]):
+        p = workloads.random_fp16_problem(50 + i, M, K, 1)
+        W = p.W.copy()
+        W[0, 0] = np.float16(-0.0)
+        e, s = bsp.encode(W), oracle.encode(W)
+        assert _same(e, s)
+
+
+def test_encoder_strided_input():
+    p = workloads.random_int4_problem(3, 40, 300, 1)
+    big = np.zeros((40, 333), np.int8)
+    big[:, :300] = p.W
+    assert _same(bsp.encode(big[:, :300]), oracle.encode(p.W))
+
+
+def test_encoder_errors():
+    L = bsp.load_library()
+    W = np.zeros((2, 10), np.int8); W[1, 3] = 8
+    with pytest.raises(bsp.BspError) as ei:
+        bsp.encode(W)
+    assert ei.value.status == bsp.E_RANGE
+    W = np.ones((2, 10), np.int8)
+    nnz, nb = ctypes.c_int64(-1), ctypes.c_int64(-1)
+    bm = np.zeros(2, np.uint64); off = np.zeros(3, np.uint32); pl = np.zeros(16, np.uint8)
+    P = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    rc = L.encode_bitmap_tiles(0, P(W), 2, 10, 10, P(bm), P(off), P(pl), 9, ctypes.byref(nnz), ctypes.byref(nb))
+    assert rc == bsp.E_CAPACITY and nnz.value == 20 and nb.value == 10
+    assert L.encode_bitmap_tiles(0, P(W), 2, 10, 9, None, None, None, 0, None, None) == bsp.E_ARG   # ldw < K
+    assert L.encode_bitmap_tiles(7, P(W), 2, 10, 10, None, None, None, 0, None, None) == bsp.E_ARG  # dtype
+    assert L.encode_bitmap_tiles(0, None, 2, 10, 10, None, None, None, 0, None, None) == bsp.E_ARG  # W null
+    assert L.encode_bitmap_tiles(0, P(W), 2, 10, 10, P(bm), None, None, 0, None, None) == bsp.E_ARG
+
+
+def test_pack_int4_golden():
+    g = pins._golden("x_int4_packing.json")
+    out = bsp.pack_int4(np.array(g["X_rows"], np.int8)).reshape(-1)
+    assert [f"{int(b):02X}" for b in out] == g["packed_hex"]
+    # round trip through the oracle's unpacker on a ragged K
+    p = workloads.random_int4_problem(4, 1, 77, 5)
+    assert np.array_equal(oracle.unpack_x4(bsp.pack_int4(p.X), 5, 77), p.X)
+    with pytest.raises(bsp.BspError):
+        bsp.pack_int4(np.full((1, 3), 9, np.int8))
+
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every case below fails on the host
+
+
+@pytest.mark.parametrize("fn", ["spmm_bitmap_w4a4_algo", "spmm_bitmap_f16_algo"])
+def test_spmm_argument_errors_on_host(fn):
+    f = getattr(bsp.load_library(), fn)
+    ok = dict(bm=FAKE, off=FAKE, pl=FAKE, pb=64, M=4, K=64, X=FAKE, N=1, Y=FAKE, algo=0)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["bm"], a["off"], a["pl"], a["pb"], a["M"], a["K"], a["X"], a["N"], a["Y"], a["algo"], None)
+
+    assert call(N=33) == bsp.E_ARG
+    assert call(N=-1) == bsp.E_ARG
+    assert call(M=-1) == bsp.E_ARG
+    assert call(K=-5) == bsp.E_ARG
+    assert call(K=1 << 25) == bsp.E_OVERFLOW
+    assert call(M=1 << 31) == bsp.E_OVERFLOW
+    assert call(M=1 << 30, K=1 << 20) == bsp.E_OVERFLOW       # M*T beyond 2^31
+    assert call(pb=17) == bsp.E_ARG                            # not a multiple of 16
+    assert call(pb=-16) == bsp.E_ARG
+    assert call(Y=None) == bsp.E_ARG
+    assert call(off=None) == bsp.E_ARG
+    assert call(bm=None) == bsp.E_ARG
+    assert call(X=None) == bsp.E_ARG
+    assert call(pl=None) == bsp.E_ARG
+    assert call(algo=99) == bsp.E_ARG
+    assert call(algo=-1) == bsp.E_ARG
+    # empty problems succeed without launching anything
+    assert call(M=0) == bsp.OK
+    assert call(N=0) == bsp.OK
+    assert call(M=0, Y=None, X=None) == bsp.OK
+
+
+def test_selection_is_defined_for_every_shape():
+    for dt in (bsp.INT4, bsp.FP16):
+        for N in range(1, 33):
+            for (M, K) in [(512, 512), (12288, 4096), (11008, 4096), (4096, 11008), (8192, 8192), (1, 1), (7, 0)]:
+                a = bsp.select(dt, M, K, N)
+                assert a in (bsp.ALGO_ROWWAVE, bsp.ALGO_VALU, bsp.ALGO_MFMA)
+                assert bsp.describe(dt, M, K, N).startswith("dtype=")
+    assert bsp.select(bsp.INT4, 1, 1, 33) == -1
+    assert bsp.select(5, 1, 1, 1) == -1

@@ -15,10 +15,11 @@ weights are not available, so iid masks stand in for pruned real weights.
 Recipe (numpy ``default_rng(seed)``, PCG64), draw order inside a config is
 mask -> values -> X:
 
-* int4 nonzeros: ``rng.integers(0, 15)`` mapped d -> d-8 if d < 8 else d-7,
-  i.e. uniform over {-8..-1, 1..7};
-* int4 activations: ``rng.integers(-8, 8)``, uniform over [-8, 7];
-* masks: ``rng.random(dtype=float32) < keep`` per element;
+* int4 nonzeros: ``rng.integers(0, 15, dtype=int8)`` mapped d -> d-8 if
+  d < 8 else d-7, i.e. uniform over {-8..-1, 1..7};
+* int4 activations: ``rng.integers(-8, 8, dtype=int8)``, uniform over [-8, 7];
+* masks: ``rng.integers(0, 65536, dtype=uint16) < round(keep * 65536)`` per
+  element (keep probability quantised to 1/65536);
 * per-row density (low-sparsity case): ``rng.uniform(0.6, 0.8, M)`` drawn
   before the mask, then element kept with its row's probability;
 * fp16 case: W = N(0, 0.02) cast to fp16, then the round(0.6*M*K) entries of
@@ -69,26 +70,27 @@ class Problem:
 
 
 def int4_nonzero_values(rng: np.random.Generator, size) -> np.ndarray:
-    d = rng.integers(0, 15, size=size, dtype=np.int16)
-    return np.where(d < 8, d - 8, d - 7).astype(np.int8)
+    d = rng.integers(0, 15, size=size, dtype=np.int8)
+    return (d - np.int8(8) + (d >= 8).astype(np.int8)).astype(np.int8)
 
 
 def int4_activations(rng: np.random.Generator, size) -> np.ndarray:
-    return rng.integers(-8, 8, size=size, dtype=np.int16).astype(np.int8)
+    return rng.integers(-8, 8, size=size, dtype=np.int8)
 
 
 def int4_mask_matrix(rng: np.random.Generator, M: int, K: int, keep) -> np.ndarray:
-    """Bernoulli keep-mask. ``keep`` is a scalar or a per-row array of length M."""
-    keep = np.asarray(keep, dtype=np.float32)
-    if keep.ndim == 1:
-        keep = keep[:, None]
-    return rng.random((M, K), dtype=np.float32) < keep
+    """Bernoulli keep-mask. ``keep`` is a scalar or a per-row array of length M;
+    the probability is quantised to 1/65536."""
+    thresh = np.round(np.asarray(keep, dtype=np.float64) * 65536.0).astype(np.uint32)
+    if thresh.ndim == 1:
+        thresh = thresh[:, None]
+    return rng.integers(0, 65536, size=(M, K), dtype=np.uint16) < thresh
 
 
 def _int4_weights(rng, M, K, keep) -> np.ndarray:
     mask = int4_mask_matrix(rng, M, K, keep)
     vals = int4_nonzero_values(rng, (M, K))
-    return np.where(mask, vals, np.int8(0)).astype(np.int8)
+    return (vals * mask).astype(np.int8)
 
 
 def random_int4_problem(seed: int, M: int, K: int, N: int, keep: float = 0.5,

@@ -11,9 +11,12 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include "bitmap_spmm.h"
 #include "device_common.h"
 #include "kernels_rowwave.hip"
+#include "kernels_mfma.hip"
 
 namespace {
 
@@ -46,8 +49,18 @@ int launch_status() {
     return e == hipSuccess ? BSP_OK : BSP_E_HIP;
 }
 
+// Whether a kernel family can run a problem (layout constraints of the fast paths).
+bool algo_supported(int algo, int dtype, const Shape &s) {
+    switch (algo) {
+        case BSP_ALGO_ROWWAVE: return true;
+        case BSP_ALGO_MFMA: return dtype == BSP_INT4 && mfma_w4a4_supported(s.K);
+        default: return false;
+    }
+}
+
 int select_algo(int dtype, const Shape &s, int64_t nnz) {
-    (void)dtype; (void)s; (void)nnz;
+    (void)nnz;
+    if (algo_supported(BSP_ALGO_MFMA, dtype, s)) return BSP_ALGO_MFMA;
     return BSP_ALGO_ROWWAVE;
 }
 
@@ -78,7 +91,11 @@ extern "C" int spmm_bitmap_w4a4_algo(const uint64_t *bitmaps, const uint32_t *of
     int rc = check_args(bitmaps, offsets, payload, payload_bytes, M, K, X, N, Y, algo, &s);
     if (rc != BSP_OK || M == 0 || N == 0) return rc;
     if (algo == BSP_ALGO_AUTO) algo = select_algo(BSP_INT4, s, -1);
+    if (!algo_supported(algo, BSP_INT4, s)) algo = BSP_ALGO_ROWWAVE;   // layout outside a fast path's range
     switch (algo) {
+        case BSP_ALGO_MFMA:
+            launch_mfma_w4a4(bitmaps, offsets, payload, (uint32_t)payload_bytes, (int)M, (int)K, X, (int)N, Y, stream);
+            break;
         default:
         case BSP_ALGO_ROWWAVE:
             launch_rowwave_w4a4(bitmaps, offsets, payload, (uint32_t)payload_bytes, (int)M, (int)K,
@@ -101,6 +118,7 @@ extern "C" int spmm_bitmap_f16_algo(const uint64_t *bitmaps, const uint32_t *off
     int rc = check_args(bitmaps, offsets, payload, payload_bytes, M, K, X, N, Y, algo, &s);
     if (rc != BSP_OK || M == 0 || N == 0) return rc;
     if (algo == BSP_ALGO_AUTO) algo = select_algo(BSP_FP16, s, -1);
+    if (!algo_supported(algo, BSP_FP16, s)) algo = BSP_ALGO_ROWWAVE;
     switch (algo) {
         default:
         case BSP_ALGO_ROWWAVE:

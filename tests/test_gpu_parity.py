@@ -17,8 +17,9 @@ import workloads
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
-INT4_ALGOS = [bsp.ALGO_AUTO, bsp.ALGO_ROWWAVE, bsp.ALGO_VALU, bsp.ALGO_MFMA]
-F16_ALGOS = [bsp.ALGO_AUTO, bsp.ALGO_ROWWAVE, bsp.ALGO_VALU, bsp.ALGO_MFMA]
+INT4_ALGOS = [bsp.ALGO_AUTO, bsp.ALGO_ROWWAVE, bsp.ALGO_MFMA]
+F16_ALGOS = [bsp.ALGO_AUTO, bsp.ALGO_ROWWAVE]
+_NAMES = {bsp.ALGO_AUTO: "auto", bsp.ALGO_ROWWAVE: "rowwave", bsp.ALGO_VALU: "valu", bsp.ALGO_MFMA: "mfma"}
 SENTINEL = -0x21524111   # 0xDEADBEEF as int32
 F16_TOL = 1e-2
 
@@ -84,11 +85,12 @@ SMALL_INT4 = [  # (M, K, N, keep)
     (1, 1, 1, 1.0), (1, 64, 1, 0.5), (3, 63, 2, 0.5), (5, 65, 3, 0.5), (64, 64, 8, 0.5),
     (65, 130, 3, 0.5), (17, 127, 31, 0.5), (257, 1000, 16, 0.3), (129, 64 * 67 + 17, 32, 0.7),
     (300, 64 * 40, 5, 0.5), (97, 4096, 8, 0.5), (1024, 512, 4, 0.5), (33, 777, 7, 1.0),
+    (48, 64 * 67 + 24, 20, 0.5), (31, 64 * 33 + 8, 16, 1.0), (16, 64 * 65, 32, 0.5), (250, 64 * 5 + 56, 13, 0.6),
     (40, 333, 9, 0.0), (2, 2048, 32, 0.05), (512, 64 * 172, 16, 0.3),
 ]
 
 
-@pytest.mark.parametrize("algo", INT4_ALGOS)
+@pytest.mark.parametrize("algo", INT4_ALGOS, ids=lambda a: _NAMES[a])
 @pytest.mark.parametrize("M,K,N,keep", SMALL_INT4)
 def test_w4a4_small(dev, algo, M, K, N, keep):
     p = workloads.random_int4_problem(M * 7 + K * 3 + N, M, K, N, keep=keep)
@@ -96,7 +98,7 @@ def test_w4a4_small(dev, algo, M, K, N, keep):
     assert np.array_equal(Y, oracle_w4a4(p.W, p.X))
 
 
-@pytest.mark.parametrize("algo", INT4_ALGOS)
+@pytest.mark.parametrize("algo", INT4_ALGOS, ids=lambda a: _NAMES[a])
 def test_w4a4_extremes(dev, algo):
     # every weight and activation at -8: the largest magnitude products
     M, K, N = 70, 64 * 33 + 5, 32
@@ -107,7 +109,7 @@ def test_w4a4_extremes(dev, algo):
     assert np.array_equal(run_w4a4(W, X, algo, dev), oracle_w4a4(W, X))
 
 
-@pytest.mark.parametrize("algo", INT4_ALGOS)
+@pytest.mark.parametrize("algo", INT4_ALGOS, ids=lambda a: _NAMES[a])
 def test_w4a4_k_zero(dev, algo):
     W = np.zeros((9, 0), np.int8)
     X = np.zeros((3, 0), np.int8)
@@ -115,7 +117,7 @@ def test_w4a4_k_zero(dev, algo):
     assert Y.shape == (3, 9) and not Y.any()
 
 
-@pytest.mark.parametrize("algo", INT4_ALGOS)
+@pytest.mark.parametrize("algo", INT4_ALGOS, ids=lambda a: _NAMES[a])
 @pytest.mark.parametrize("N", list(range(1, 33)))
 def test_w4a4_every_n(dev, algo, N):
     p = workloads.random_int4_problem(77, 200, 64 * 9 + 33, 32, keep=0.5)
@@ -133,7 +135,7 @@ def _assert_f16(y, r):
     assert e["max_rel_floored"] <= F16_TOL, e
 
 
-@pytest.mark.parametrize("algo", F16_ALGOS)
+@pytest.mark.parametrize("algo", F16_ALGOS, ids=lambda a: _NAMES[a])
 @pytest.mark.parametrize("M,K,N", SMALL_F16)
 def test_f16_small(dev, algo, M, K, N):
     p = workloads.random_fp16_problem(M + K + N, M, K, N)
@@ -141,7 +143,7 @@ def test_f16_small(dev, algo, M, K, N):
     _assert_f16(y, oracle.spmm_f16(oracle.encode(p.W), p.X))
 
 
-@pytest.mark.parametrize("algo", F16_ALGOS)
+@pytest.mark.parametrize("algo", F16_ALGOS, ids=lambda a: _NAMES[a])
 def test_f16_zero_and_dense(dev, algo):
     W = np.zeros((33, 100), np.float16)
     X = np.ones((2, 100), np.float16)
@@ -169,7 +171,7 @@ def _full_f16(idx):
 FULL_INT4 = [("tiny", 0), ("qkv", 0), ("ffn", 0), ("ffn", 1), ("lowsparse", 0)]
 
 
-@pytest.mark.parametrize("algo", INT4_ALGOS)
+@pytest.mark.parametrize("algo", INT4_ALGOS, ids=lambda a: _NAMES[a])
 @pytest.mark.parametrize("config,idx", FULL_INT4)
 def test_w4a4_full_workload(dev, algo, config, idx):
     p, X, ref = _full_int4(config, idx, 0)
@@ -177,7 +179,7 @@ def test_w4a4_full_workload(dev, algo, config, idx):
     assert np.array_equal(Y, ref)
 
 
-@pytest.mark.parametrize("algo", INT4_ALGOS)
+@pytest.mark.parametrize("algo", INT4_ALGOS, ids=lambda a: _NAMES[a])
 @pytest.mark.parametrize("N", [1, 2, 4, 8, 16, 32])
 def test_w4a4_qkv_n_sweep(dev, algo, N):
     p, X, ref = _full_int4("qkv", 0, 32)
@@ -185,7 +187,7 @@ def test_w4a4_qkv_n_sweep(dev, algo, N):
     assert np.array_equal(Y, ref[:N])
 
 
-@pytest.mark.parametrize("algo", F16_ALGOS)
+@pytest.mark.parametrize("algo", F16_ALGOS, ids=lambda a: _NAMES[a])
 @pytest.mark.parametrize("idx", [0, 1])
 def test_f16_full_workload(dev, algo, idx):
     p, r = _full_f16(idx)

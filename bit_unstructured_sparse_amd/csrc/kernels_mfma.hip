@@ -35,7 +35,9 @@
 
 #define BSP_MF_ROWS 16                 // rows per workgroup (one MFMA row block)
 #define BSP_MF_WAVES 4                 // wavefronts per workgroup (K quarters)
+#ifndef BSP_MF_CHUNK
 #define BSP_MF_CHUNK 16                // tiles per staged chunk of a wavefront
+#endif
 #define BSP_MF_TPL (BSP_MF_CHUNK / 4)  // tiles per lane per chunk
 // LDS slot per row per chunk, in 16-byte units: up to 16 tiles x 32 bytes of
 // payload, one unit for the start misalignment and one for the window that
@@ -96,25 +98,46 @@ constexpr BspMfLut bsp_mf_make_lut() {
 
 __device__ __attribute__((aligned(16))) const BspMfLut bsp_mf_lut_global = bsp_mf_make_lut();
 
-// Decode one tile (word, running nibble position q inside this wavefront's
-// LDS payload area) into 16 dwords of x16 int8: for byte group g, A[2g] holds
-// positions 8g+{0,2,4,6} and A[2g+1] positions 8g+{1,3,5,7}.
-__device__ __forceinline__ void bsp_mf_decode_tile(uint64_t word, uint32_t q, const uint2 *__restrict__ lut,
-                                                   uint32_t A[16]) {
+// Decode of one tile, split in two so that all of a tile's LDS reads are in
+// flight together before any of them is used:
+//   fetch: for every byte group g, the selector pair of its byte b_g and the
+//          two payload dwords holding nibbles q_g .. q_g+7, where q_g is the
+//          tile's start position plus the popcount of the bytes before g;
+//   build: funnel-shift the 8-nibble window, split it into even and odd
+//          nibbles in the high half of each byte (x16, so no sign extension),
+//          and place the bytes with two v_perm_b32. Output A[2g] holds
+//          positions 8g+{0,2,4,6}, A[2g+1] positions 8g+{1,3,5,7}.
+// q counts nibbles from the start of LDS.
+struct BspMfFetch {
+    uint2 sel[8];
+    uint32_t w0[8], w1[8];
+    uint32_t q[8];
+};
+
+__device__ __forceinline__ void bsp_mf_fetch(uint64_t word, uint32_t q, const uint2 *__restrict__ lut,
+                                             BspMfFetch &f) {
     const uint32_t lo = (uint32_t)word, hi = (uint32_t)(word >> 32);
 #pragma unroll
     for (int g = 0; g < 8; ++g) {
         const uint32_t b = __builtin_amdgcn_ubfe(g < 4 ? lo : hi, 8 * (g & 3), 8);
-        const uint2 sel = lut[b];
-        // the two dwords holding nibbles q .. q+7 (q counts nibbles from the LDS base)
+        f.q[g] = q;
+        f.sel[g] = lut[b];
         const bsp_lds_u32 *w = (const bsp_lds_u32 *)(uintptr_t)((q >> 1) & ~3u);
+        f.w0[g] = w[0];
+        f.w1[g] = w[1];
+        q += __builtin_popcount(b);
+    }
+}
+
+__device__ __forceinline__ void bsp_mf_build(const BspMfFetch &f, uint32_t A[16]) {
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
         // v_alignbit_b32 uses only the low five bits of the shift: 4 * (q % 8)
-        const uint32_t x = __builtin_amdgcn_alignbit(w[1], w[0], q << 2);
+        const uint32_t x = __builtin_amdgcn_alignbit(f.w1[g], f.w0[g], f.q[g] << 2);
         const uint32_t s_odd = x & 0xF0F0F0F0u;
         const uint32_t s_even = (x << 4) & 0xF0F0F0F0u;
-        A[2 * g] = __builtin_amdgcn_perm(s_odd, s_even, sel.x);
-        A[2 * g + 1] = __builtin_amdgcn_perm(s_odd, s_even, sel.y);
-        q += __builtin_popcount(b);
+        A[2 * g] = __builtin_amdgcn_perm(s_odd, s_even, f.sel[g].x);
+        A[2 * g + 1] = __builtin_amdgcn_perm(s_odd, s_even, f.sel[g].y);
     }
 }
 
@@ -130,7 +153,9 @@ __device__ __forceinline__ void bsp_mf_convert_x(const uint32_t d[8], uint32_t B
 
 // Maximum wavefronts per workgroup: the workgroup splits K in chunks of
 // BSP_MF_CHUNK tiles, one chunk per wavefront (more chunks loop).
+#ifndef BSP_MF_MAX_WAVES
 #define BSP_MF_MAX_WAVES 12
+#endif
 
 template <int NBLK>
 __global__ __launch_bounds__(BSP_WAVE * BSP_MF_MAX_WAVES) void k_mfma_w4a4(
@@ -240,9 +265,11 @@ __global__ __launch_bounds__(BSP_WAVE * BSP_MF_MAX_WAVES) void k_mfma_w4a4(
         if (!row_ok) q = slot_base * 2u;
 #pragma unroll
         for (int i = 0; i < BSP_MF_TPL; ++i) {
-            uint32_t A[16];
-            bsp_mf_decode_tile(words[i], q, lut, A);
+            BspMfFetch f;                  // all 24 LDS reads of the tile in flight together
+            bsp_mf_fetch(words[i], q, lut, f);
             q += __builtin_popcountll(words[i]);
+            uint32_t A[16];
+            bsp_mf_build(f, A);
 #pragma unroll
             for (int nb = 0; nb < NBLK; ++nb) {
                 uint32_t B[16];

@@ -17,6 +17,7 @@
 #include "device_common.h"
 #include "kernels_rowwave.hip"
 #include "kernels_mfma.hip"
+#include "kernels_mfma_wg.hip"
 
 namespace {
 
@@ -93,9 +94,21 @@ extern "C" int spmm_bitmap_w4a4_algo(const uint64_t *bitmaps, const uint32_t *of
     if (algo == BSP_ALGO_AUTO) algo = select_algo(BSP_INT4, s, -1);
     if (!algo_supported(algo, BSP_INT4, s)) algo = BSP_ALGO_ROWWAVE;   // layout outside a fast path's range
     switch (algo) {
-        case BSP_ALGO_MFMA:
-            launch_mfma_w4a4(bitmaps, offsets, payload, (uint32_t)payload_bytes, (int)M, (int)K, X, (int)N, Y, stream);
+        case BSP_ALGO_MFMA: {
+            BspMfWgPlan plan;
+            if (mfma_wg_plan((int)M, (int)K, (int)N, &plan)) {
+                if (N <= 16)
+                    launch_mfma_wg_nb<1>(plan, bitmaps, offsets, payload, (uint32_t)payload_bytes, (int)M, (int)K, X,
+                                         (int)N, Y, stream);
+                else
+                    launch_mfma_wg_nb<2>(plan, bitmaps, offsets, payload, (uint32_t)payload_bytes, (int)M, (int)K, X,
+                                         (int)N, Y, stream);
+            } else {
+                launch_mfma_w4a4(bitmaps, offsets, payload, (uint32_t)payload_bytes, (int)M, (int)K, X, (int)N, Y,
+                                 stream);
+            }
             break;
+        }
         default:
         case BSP_ALGO_ROWWAVE:
             launch_rowwave_w4a4(bitmaps, offsets, payload, (uint32_t)payload_bytes, (int)M, (int)K,

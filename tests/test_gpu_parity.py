@@ -86,6 +86,7 @@ SMALL_INT4 = [  # (M, K, N, keep)
     (65, 130, 3, 0.5), (17, 127, 31, 0.5), (257, 1000, 16, 0.3), (129, 64 * 67 + 17, 32, 0.7),
     (300, 64 * 40, 5, 0.5), (97, 4096, 8, 0.5), (1024, 512, 4, 0.5), (33, 777, 7, 1.0),
     (48, 64 * 67 + 24, 20, 0.5), (31, 64 * 33 + 8, 16, 1.0), (16, 64 * 65, 32, 0.5), (250, 64 * 5 + 56, 13, 0.6),
+    (40, 64 * 320, 5, 0.5), (17, 64 * 330 + 32, 24, 0.9),   # K beyond one block's LDS: per-chunk staging
     (40, 333, 9, 0.0), (2, 2048, 32, 0.05), (512, 64 * 172, 16, 0.3),
 ]
 

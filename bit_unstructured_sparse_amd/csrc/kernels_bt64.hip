@@ -1,0 +1,562 @@
+// kernels_bt64.hip -- block-staged bitmap decode + int8 MFMA contraction for
+// the int4 x int4 -> int32 SpMM on gfx950 (CDNA4).
+//
+// Y = W_sparse * X with W in the BT64 stream (UnionSparse, Sec. V-A, one area
+// per 1 x 64 tile: occupancy word, prefix offsets, packed nonzeros) and X a
+// skinny K x N int4 matrix. The pages decode position-per-thread with a masked
+// popcount (UnionSparse Sec. VI-B, SPDP Sec. 4.2.1) into tensor-core
+// fragments; here the same arithmetic is reorganised for gfx950:
+//
+// Work split. Rows are cut into blocks of 16 (the A-row count of
+// v_mfma_i32_16x16x64_i8). A workgroup is resident on one CU for the whole
+// kernel and owns a contiguous run of at most BT_NBLK(TPL) blocks. Its
+// wavefront w owns the tile range [4*TPL*w, 4*TPL*(w+1)) of every block, and
+// inside it lane l = r + 16 q owns row r and the TPL consecutive tiles
+// 4*TPL*w + TPL*q ... A step decodes one whole 1 x 64 tile per lane and issues
+// four MFMAs; MFMA j contracts positions 16j .. 16j+15 of every lane's tile
+// against the matching X slice (the K order inside one MFMA is free as long as
+// A and B use the same one).
+//
+// Loads. Everything is requested up front: the block-boundary offsets (scalar
+// loads), every block's bitmap words for this lane, X (once per workgroup,
+// coalesced, into LDS rows) and the payload of the first blocks. A block's
+// payload is one contiguous range (the stream is in row-major tile order), so
+// it needs only its two boundary offsets; each lane's start inside it is the
+// block start plus bitmap popcounts (the offset definition of Sec. V-A),
+// exchanged across wavefronts through LDS. Blocks are decoded in order while
+// the later ones are still in flight; a ring of LDS buffers is refilled as
+// blocks are finished.
+//
+// Payload layout in LDS. Random 8-byte LDS reads are fast on gfx950 only when
+// 8-byte aligned (a dword-aligned ds_read_b64 costs ~9x more), and a window of
+// 8 nibbles starting at an arbitrary nibble spans two arbitrary consecutive
+// dwords. A block is therefore staged as "pair slots": slot s (8 bytes,
+// 8-byte aligned) holds payload dwords s and s+1, so the window for nibble p is
+// the aligned read of slot p >> 3 and a funnel shift by 4 * (p & 7). The
+// staging is LDS DMA of 4-byte elements whose source offsets duplicate every
+// dword (lanes 2i and 2i+1 read dwords i and i+1): no VGPRs, no vector ALU.
+// It takes twice the payload's bytes; a block whose payload does not fit the
+// buffer sized at launch reads its windows from global memory instead
+// (slower, same result).
+//
+// Decode of 8 positions (one byte b of the word). The window is split into
+// even and odd nibbles placed in the high half of each byte (so a byte holds
+// 16 * value and needs no sign extension) and two v_perm_b32 place them; the
+// selector pair comes from a 256-entry LDS table indexed by b: for each of the
+// byte's positions, the rank of its nonzero among the byte's set bits, or
+// "zero". Output dword 2k holds positions 8k+{0,2,4,6}, dword 2k+1 positions
+// 8k+{1,3,5,7}: the order a packed X dword splits into with one AND (odd k)
+// or a shift and an AND (even k), which is the B operand order.
+//
+// Products are 256 * w * x; each wavefront's partial sum is shifted right by 8
+// (exact) before the wavefronts' partials are added, so no int32 sum can
+// overflow under the API's K bound.
+
+#define BT_ROWS 16                      // rows per block (MFMA A rows)
+#define BT_MAX_WAVES 8
+#define BT_LUT_COPIES 16               // selector-table copies in LDS (lane l reads copy l % 16)
+#define BT_LUT_BYTES (2048 * BT_LUT_COPIES)   // 256 entries x 8 bytes per copy
+#define BT_SLACK_BYTES 512              // windows a corrupt stream could run past a buffer
+#define BT_LDS_MAX (160 * 1024)
+#define BT_CUS 256
+
+// Blocks one workgroup can own: every block's words stay in VGPRs (TPL words per lane).
+#define BT_NBLK(TPL) ((TPL) == 1 ? 4 : 8 / (TPL))
+// Threads per workgroup at most: 16 wavefronts with one tile per lane (<= 128
+// VGPRs each), else 8 wavefronts (<= 256 VGPRs each).
+#define BT_WG_THREADS(TPL) ((TPL) == 1 ? 1024 : 512)
+
+typedef int bt_v4i __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void bt_lds_void;
+typedef __attribute__((address_space(3))) const uint64_t bt_lds_u64;
+typedef __attribute__((address_space(3))) const bt_v4i bt_lds_v4i;
+
+// Selector table: entry b (a bitmap byte) is the v_perm_b32 selector pair that
+// scatters the byte's nonzeros to their positions. The perm's sources are
+// S0 = odd-rank nibbles (selector 4..7) and S1 = even-rank nibbles (0..3);
+// selector 0x0C yields a zero byte.
+struct BtLut {
+    uint32_t w[512];
+};
+
+constexpr BtLut bt_make_lut() {
+    BtLut t{};
+    for (uint32_t b = 0; b < 256; ++b) {
+        uint32_t sel[2] = {0x0C0C0C0Cu, 0x0C0C0C0Cu};
+        uint32_t rank = 0;
+        for (int p = 0; p < 8; ++p) {
+            if ((b >> p) & 1u) {
+                const uint32_t src = (rank & 1u) ? 4u + (rank >> 1) : (rank >> 1);
+                const int half = p & 1, byte = p >> 1;
+                sel[half] = (sel[half] & ~(0xFFu << (8 * byte))) | (src << (8 * byte));
+                ++rank;
+            }
+        }
+        t.w[2 * b] = sel[0];
+        t.w[2 * b + 1] = sel[1];
+    }
+    return t;
+}
+
+__device__ __attribute__((aligned(16))) const BtLut bt_lut_global = bt_make_lut();
+
+// LDS byte address of a pointer into dynamic shared memory.
+__device__ __forceinline__ uint32_t bt_lds_addr(const void *p) {
+    return (uint32_t)(uintptr_t)(const bt_lds_void *)p;
+}
+
+// One aligned 8-byte LDS read (ds_read_b64) at byte address a, as (lo, hi).
+__device__ __forceinline__ uint2 bt_lds_pair(uint32_t a) {
+    const uint64_t v = *(bt_lds_u64 *)(uintptr_t)a;
+    return uint2{(uint32_t)v, (uint32_t)(v >> 32)};
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t bt_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// s_waitcnt vmcnt(n) for a run-time n (the instruction takes an immediate):
+// waits until at most n vector-memory operations of this wavefront are
+// outstanding. n above the counter's range (63) waits for n = 63.
+__device__ __forceinline__ void bt_wait_vm(uint32_t n) {
+#define BT_W(c) case c: __builtin_amdgcn_s_waitcnt(((c) & 15) | (((c) >> 4) << 14) | (7 << 4) | (15 << 8)); break;
+#define BT_W8(c) BT_W(c) BT_W(c + 1) BT_W(c + 2) BT_W(c + 3) BT_W(c + 4) BT_W(c + 5) BT_W(c + 6) BT_W(c + 7)
+    switch (n < 63u ? n : 63u) {
+        BT_W8(0) BT_W8(8) BT_W8(16) BT_W8(24) BT_W8(32) BT_W8(40) BT_W8(48) BT_W8(56)
+    }
+#undef BT_W8
+#undef BT_W
+}
+
+// Decode of one tile word into 16 dwords of x16 int8 (A operand of 4 MFMAs).
+// win(p) returns the two payload dwords holding nibbles p .. p+7 as (lo, hi).
+// lut_base is the LDS address of this lane's copy of the selector table: the
+// copies are interleaved entry by entry (entry b of copy c at (16 b + c) * 8),
+// so the 16 lanes that read one copy each cannot conflict with one another.
+template <class Win>
+__device__ __forceinline__ void bt_decode_tile(uint64_t word, uint32_t p, const Win &win, uint32_t lut_base,
+                                               uint32_t A[16]) {
+    const uint32_t lo = (uint32_t)word, hi = (uint32_t)(word >> 32);
+    uint2 sel[8];
+    uint2 d[8];
+    uint32_t pk[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const uint32_t b = __builtin_amdgcn_ubfe(k < 4 ? lo : hi, 8 * (k & 3), 8);
+        sel[k] = bt_lds_pair(lut_base + b * (8u * BT_LUT_COPIES));
+        pk[k] = p;
+        d[k] = win(p);
+        p = (uint32_t)__builtin_popcount(b) + p;   // v_bcnt_u32_b32 with accumulate
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const uint32_t x = __builtin_amdgcn_alignbit(d[k].y, d[k].x, pk[k] << 2);
+        const uint32_t s_odd = x & 0xF0F0F0F0u;
+        const uint32_t s_even = (x << 4) & 0xF0F0F0F0u;
+        A[2 * k] = __builtin_amdgcn_perm(s_odd, s_even, sel[k].x);
+        A[2 * k + 1] = __builtin_amdgcn_perm(s_odd, s_even, sel[k].y);
+    }
+}
+
+// Window source: pair slots in LDS. p already includes the LDS byte address of
+// slot 0 (a multiple of 8), so p & ~7 is the slot's address and p & 7 the
+// nibble offset inside it.
+struct BtWinLds {
+    __device__ __forceinline__ uint2 operator()(uint32_t p) const { return bt_lds_pair(p & ~7u); }
+};
+
+// Window source: global memory through a range-checked buffer resource
+// (p counts nibbles from payload dword d0).
+struct BtWinGlobal {
+    __amdgpu_buffer_rsrc_t rs;
+    uint32_t d0;
+    __device__ __forceinline__ uint2 operator()(uint32_t p) const {
+        const uint32_t off = (d0 + (p >> 3)) * 4u;
+        return uint2{(uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0),
+                     (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, off + 4u, 0, 0)};
+    }
+};
+
+// X slice of one tile for one MFMA j: packed dwords x0 (k 0..7) and x1
+// (k 8..15) -> B dwords {even k of x0, odd k of x0, even k of x1, odd k of x1}
+// in the same x16 form as A.
+__device__ __forceinline__ bt_v4i bt_b_operand(uint32_t x0, uint32_t x1) {
+    return bt_v4i{(int)((x0 << 4) & 0xF0F0F0F0u), (int)(x0 & 0xF0F0F0F0u), (int)((x1 << 4) & 0xF0F0F0F0u),
+                  (int)(x1 & 0xF0F0F0F0u)};
+}
+
+// Decode + contract the lane's TPL tiles of one block. xb holds the lane's
+// B operands (column r + 16 nb, tiles t0 .. t0+TPL-1, MFMA j), built once.
+template <int NB, int TPL, class Win>
+__device__ __forceinline__ void bt_contract(const uint64_t (&words)[TPL], uint32_t p, const Win &win,
+                                            uint32_t lut_base, const bt_v4i (&xb)[NB][TPL][4],
+                                            bt_v4i (&acc)[NB]) {
+#pragma unroll
+    for (int i = 0; i < TPL; ++i) {
+        uint32_t A[16];
+        bt_decode_tile(words[i], p, win, lut_base, A);
+        p += (uint32_t)__builtin_popcountll(words[i]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const bt_v4i a = {(int)A[4 * j], (int)A[4 * j + 1], (int)A[4 * j + 2], (int)A[4 * j + 3]};
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+                acc[nb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, xb[nb][i][j], acc[nb], 0, 0, 0);
+        }
+    }
+}
+
+// Payload range of a block in 16-byte granules: [g0, g0 + n) covers its
+// nibbles plus one granule for the windows that read past the last nonzero.
+struct BtRange {
+    uint32_t g0, n;
+};
+__device__ __forceinline__ BtRange bt_range(uint32_t nibA, uint32_t nibB) {
+    const uint32_t g0 = nibA >> 5;
+    const uint32_t g1 = (nibB >= nibA ? (nibB + 31u) >> 5 : g0) + 1u;
+    return BtRange{g0, g1 - g0};
+}
+
+// LDS layout (bytes):
+//   [selector table copies][row totals 2 x 16 x 8 ints][sums 2 x NB x 256 ints]
+//   [pair-slot buffer, pair_bytes][nbuf staging buffers of stage_bytes]
+// Workgroup g owns blocks [g*bq + min(g, br), ...): bq or bq + 1 of them.
+template <int NB, int TPL>
+__global__ __launch_bounds__(BT_WG_THREADS(TPL)) void k_bt64_w4a4(
+        const uint64_t *__restrict__ bitmaps, const uint32_t *__restrict__ offsets,
+        const uint8_t *__restrict__ payload, uint32_t payload_bytes, int M, int K,
+        const uint8_t *__restrict__ X, int N, int32_t *__restrict__ Y, uint32_t stage_bytes, uint32_t nbuf,
+        uint32_t pair_bytes, int bq, int br) {
+    constexpr int NBLK = BT_NBLK(TPL);
+    extern __shared__ __attribute__((aligned(16))) uint8_t bt_smem[];
+    const int nwaves = blockDim.x >> 6;
+    // the wavefront index is uniform: keep it (and the loops over it) scalar
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int r = lane & 15, q = lane >> 4;
+    const int T = (K + 63) >> 6;
+    const int gid = (int)blockIdx.x;
+    const int b_begin = gid * bq + min(gid, br);
+    const int nblk = bq + (gid < br ? 1 : 0);           // 1 .. NBLK
+    const int t0 = (wave * 4 + q) * TPL;                 // first tile of this lane
+    const uint32_t xs = (uint32_t)K >> 1;               // X row stride in bytes (K % 32 == 0 here)
+
+    const uint32_t lut_base = bt_lds_addr(bt_smem) + (uint32_t)(lane % BT_LUT_COPIES) * 8u;
+    int32_t *wt = reinterpret_cast<int32_t *>(bt_smem + BT_LUT_BYTES);                  // [2][16][8]
+    int32_t *sums = wt + 2 * BT_ROWS * 8;                                                // [2][NB*256]
+    uint8_t *pairs = reinterpret_cast<uint8_t *>(sums + 2 * NB * 256);
+    uint8_t *stage = pairs + pair_bytes;
+    const uint32_t pair_base = bt_lds_addr(pairs);
+    const __amdgpu_buffer_rsrc_t prs = bt_rsrc(payload, payload_bytes);
+
+    // (1) block boundaries (wave-uniform scalar loads), before anything else:
+    // the payload DMA waits for them
+    uint32_t nib[NBLK + 1];
+#pragma unroll
+    for (int i = 0; i <= NBLK; ++i) {
+        const int b = b_begin + (i < nblk ? i : nblk);
+        nib[i] = offsets[(int64_t)min(b * BT_ROWS, M) * T];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // (2) per block, in block order: this lane's words, then the payload DMA
+    // of the block into staging buffer i % nbuf (its granules in stream
+    // order, 1 KB = 64 lanes x 16 bytes per instruction; range checks of raw
+    // buffer loads cover the per-lane offset only, so every offset is in the
+    // per-lane operand). A block that does not fit is not staged: it reads
+    // its windows from global memory.
+    const int m_first = b_begin * BT_ROWS;
+    const int wg_rows = min(nblk * BT_ROWS, M - m_first);
+    const __amdgpu_buffer_rsrc_t brs = bt_rsrc(bitmaps + (int64_t)m_first * T, (uint32_t)wg_rows * (uint32_t)T * 8u);
+    uint64_t words[NBLK][TPL];
+    auto load_words = [&](int i) -> void {
+        const int rr = i * BT_ROWS + r;   // row inside the workgroup's range
+#pragma unroll
+        for (int k = 0; k < TPL; ++k) {
+            const uint32_t off = (rr < wg_rows && t0 + k < T) ? ((uint32_t)rr * (uint32_t)T + (uint32_t)(t0 + k)) * 8u
+                                                              : 0xFFFFFFF0u;
+            words[i][k] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(brs, off, 0, 0));
+        }
+    };
+    uint32_t vm_issued = 0;           // vector-memory operations issued so far by this wavefront
+    uint32_t vm_mark[NBLK];
+    auto fits = [&](int i) -> bool {
+        const BtRange g = bt_range(nib[i], nib[i + 1]);
+        return (g.n + 1u) * 16u <= stage_bytes && g.n * 32u + BT_SLACK_BYTES <= pair_bytes;
+    };
+    auto issue_block = [&](int i) -> void {
+        if (fits(i)) {
+            const BtRange g = bt_range(nib[i], nib[i + 1]);
+            uint8_t *buf = stage + (uint32_t)(i % (int)nbuf) * stage_bytes;
+            const uint32_t n_ins = (g.n + 63u) >> 6;
+            for (uint32_t j = (uint32_t)wave; j < n_ins; j += (uint32_t)nwaves) {
+                const uint32_t u = j * 64u + (uint32_t)lane;
+                if (u < g.n)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(prs, (bt_lds_void *)(buf + j * 1024u), 16,
+                                                             (g.g0 + u) * 16u, 0, 0, 0);
+                ++vm_issued;
+            }
+        }
+        vm_mark[i] = vm_issued;
+    };
+#pragma unroll
+    for (int i = 0; i < NBLK; ++i) {
+        if (i < nblk) {
+            load_words(i);
+            vm_issued += TPL;
+            if (i < (int)nbuf) issue_block(i);
+        }
+        if (i == 0) __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // (3) this lane's X slices, once for all blocks (column n >= N or tile >= T: zeros)
+    uint32_t xw[NB][TPL][8];
+    {
+        const __amdgpu_buffer_rsrc_t xrs = bt_rsrc(X, (uint32_t)N * xs);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int k = 0; k < TPL; ++k) {
+                const int n = r + 16 * nb;
+                const uint32_t off = (n < N && t0 + k < T) ? (uint32_t)n * xs + (uint32_t)(t0 + k) * 32u : 0xFFFFFFE0u;
+                const bt_v4i v0 = __builtin_bit_cast(bt_v4i, __builtin_amdgcn_raw_buffer_load_b128(xrs, off, 0, 0));
+                const bt_v4i v1 = __builtin_bit_cast(bt_v4i, __builtin_amdgcn_raw_buffer_load_b128(xrs, off + 16u, 0, 0));
+                xw[nb][k][0] = v0.x; xw[nb][k][1] = v0.y; xw[nb][k][2] = v0.z; xw[nb][k][3] = v0.w;
+                xw[nb][k][4] = v1.x; xw[nb][k][5] = v1.y; xw[nb][k][6] = v1.z; xw[nb][k][7] = v1.w;
+            }
+        vm_issued += 2 * NB * TPL;
+    }
+    // (4) the selector table for its 16 interleaved LDS copies: LDS slot v
+    // (8 bytes) holds entry v / 16; wavefront w fills slots 64 (w + 8 e) .. +63
+    // (consecutive addresses, so the writes cannot conflict)
+    constexpr int LUT_ROUNDS = 256 * BT_LUT_COPIES / 64 / 8;
+    uint2 lut_entry[LUT_ROUNDS];
+    {
+        const __amdgpu_buffer_rsrc_t lrs = bt_rsrc(&bt_lut_global, (uint32_t)sizeof(BtLut));
+#pragma unroll
+        for (int e = 0; e < LUT_ROUNDS; ++e) {
+            const uint32_t v = (uint32_t)((wave + 8 * e) * 64 + lane);
+            lut_entry[e] = __builtin_bit_cast(
+                    uint2, __builtin_amdgcn_raw_buffer_load_b64(lrs, wave < 8 ? (v / BT_LUT_COPIES) * 8u : 0xFFFFFFF0u,
+                                                                0, 0));
+        }
+        vm_issued += LUT_ROUNDS;
+    }
+
+    // zero both sum buffers (first added to after the first block's barriers)
+    for (int o = threadIdx.x; o < 2 * NB * 256; o += blockDim.x) sums[o] = 0;
+    {
+        __attribute__((address_space(3))) uint64_t *lut_lds =
+                (__attribute__((address_space(3))) uint64_t *)(uintptr_t)bt_lds_addr(bt_smem);
+        if (wave < 8) {
+#pragma unroll
+            for (int e = 0; e < LUT_ROUNDS; ++e)
+                lut_lds[(wave + 8 * e) * 64 + lane] = ((uint64_t)lut_entry[e].y << 32) | lut_entry[e].x;
+        }
+        if (nwaves < 8) {   // small workgroups: the remaining slots, straight from the table
+            const uint64_t *tab = reinterpret_cast<const uint64_t *>(&bt_lut_global);
+            for (int v = nwaves * 64 + (int)threadIdx.x; v < 256 * BT_LUT_COPIES; v += (int)blockDim.x)
+                if ((v / 64) % 8 >= nwaves) lut_lds[v] = tab[v / BT_LUT_COPIES];
+        }
+    }
+    // B operands of this lane's tiles, in the even/odd x16 order of the decode;
+    // pinned so that they are built once, not rebuilt in every block
+    bt_v4i xb[NB][TPL][4];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int k = 0; k < TPL; ++k)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                xb[nb][k][j] = bt_b_operand(xw[nb][k][2 * j], xw[nb][k][2 * j + 1]);
+                asm volatile("" : "+v"(xb[nb][k][j]));
+            }
+
+    // (5) blocks in order. Before the first barrier of block i each
+    // wavefront posts its row totals for block i; after it, each lane knows
+    // its start. Y of block i is written after the first barrier of block i+1
+    // (or after the loop), when every wavefront's partial is in.
+    auto write_y = [&](int i) -> void {
+        const int m0 = (b_begin + i) * BT_ROWS;
+        const int rows = min(BT_ROWS, M - m0);
+        const int32_t *s = sums + (i & 1) * NB * 256;
+        // D layout of v_mfma_i32_16x16x64_i8: lane l, register k -> row 4*(l/16)+k, column l%16
+        for (int o = threadIdx.x; o < NB * 256; o += blockDim.x) {
+            const int nb = o >> 8, col = (o >> 4) & 15, rl = o & 15;
+            const int ln = (rl >> 2) * 16 + col, k = rl & 3;
+            const int n = col + 16 * nb;
+            if (n < N && rl < rows) Y[(int64_t)n * M + m0 + rl] = s[(nb * 4 + k) * 64 + ln];
+        }
+    };
+#pragma unroll
+    for (int i = 0; i < NBLK; ++i) {
+        if (i >= nblk) break;
+        const bool in_lds = fits(i);
+        const BtRange g = bt_range(nib[i], nib[i + 1]);
+        const int rows = min(BT_ROWS, M - (b_begin + i) * BT_ROWS);
+
+        // this lane's segment popcount, inclusive prefix over q (lanes r, r+16, r+32, r+48)
+        uint32_t seg = 0;
+#pragma unroll
+        for (int k = 0; k < TPL; ++k) seg += (uint32_t)__builtin_popcountll(words[i][k]);
+        uint32_t incl = seg;
+        {
+            const uint32_t u16 = (uint32_t)__shfl_up((int)incl, 16, 64);
+            incl += q >= 1 ? u16 : 0u;
+            const uint32_t u32 = (uint32_t)__shfl_up((int)incl, 32, 64);
+            incl += q >= 2 ? u32 : 0u;
+        }
+        int32_t *wti = wt + (i & 1) * BT_ROWS * 8;
+        if (q == 3) wti[r * 8 + wave] = (int32_t)incl;   // this wavefront's total for row r
+
+        bt_wait_vm(vm_issued - vm_mark[i]);   // this wavefront's share of block i landed
+        __syncthreads();                      // ... everyone's; block i-1 is decoded and summed
+        if (i > 0) write_y(i - 1);
+
+        // lane start: rows before r, wavefronts before this one, lane groups before q
+        uint32_t pstart;
+        {
+            const bt_v4i t_lo = *(bt_lds_v4i *)(uintptr_t)bt_lds_addr(wti + r * 8);
+            const bt_v4i t_hi = *(bt_lds_v4i *)(uintptr_t)bt_lds_addr(wti + r * 8 + 4);
+            const uint32_t t[8] = {(uint32_t)t_lo.x, (uint32_t)t_lo.y, (uint32_t)t_lo.z, (uint32_t)t_lo.w,
+                                   (uint32_t)t_hi.x, (uint32_t)t_hi.y, (uint32_t)t_hi.z, (uint32_t)t_hi.w};
+            uint32_t row_total = 0, before_w = 0;
+#pragma unroll
+            for (int w = 0; w < 8; ++w) {
+                const uint32_t v = w < nwaves ? t[w] : 0u;
+                row_total += v;
+                if (w < wave) before_w += v;   // wave-uniform condition
+            }
+            // exclusive prefix of row totals over r inside each 16-lane DPP row
+            uint32_t s = row_total;
+            s += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)s, 0x111, 0xF, 0xF, true);   // row_shr:1
+            s += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)s, 0x112, 0xF, 0xF, true);   // row_shr:2
+            s += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)s, 0x114, 0xF, 0xF, true);   // row_shr:4
+            s += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)s, 0x118, 0xF, 0xF, true);   // row_shr:8
+            // nibble index of the lane's first nonzero, counted from the block's first granule
+            pstart = r < rows ? (nib[i] & 31u) + (s - row_total) + before_w + (incl - seg) : 0u;
+        }
+
+        if (in_lds) {
+            // staging -> pair slots: slot 4u+k = stream dwords 4u+k, 4u+k+1
+            const uint32_t sb = bt_lds_addr(stage + (uint32_t)(i % (int)nbuf) * stage_bytes);
+            for (uint32_t u0 = (uint32_t)wave * 64u; u0 < g.n; u0 += blockDim.x) {
+                const uint32_t u = u0 + (uint32_t)lane;     // consecutive granules across the lanes
+                const uint32_t uc = min(u, g.n);             // granule g.n is the last one staged
+                const bt_v4i d = *(bt_lds_v4i *)(uintptr_t)(sb + uc * 16u);
+                // dword 4u+4 is the next lane's first dword; lane 63 reads it
+                int d4 = __builtin_amdgcn_update_dpp(0, d.x, 0x130, 0xF, 0xF, false);   // wave_shl:1
+                if (lane == 63 && u < g.n) d4 = *(const __attribute__((address_space(3))) int *)(uintptr_t)(sb + u * 16u + 16u);
+                if (u < g.n) {
+                    // the two 16-byte halves in an order that spreads each half-wave over all banks
+                    const bt_v4i h0 = {d.x, d.y, d.y, d.z}, h1 = {d.z, d.w, d.w, d4};
+                    const bool swap = (u >> 3) & 1u;
+                    const uint32_t o = pair_base + u * 32u + (swap ? 16u : 0u);
+                    *(__attribute__((address_space(3))) bt_v4i *)(uintptr_t)o = swap ? h1 : h0;
+                    *(__attribute__((address_space(3))) bt_v4i *)(uintptr_t)(o ^ 16u) = swap ? h0 : h1;
+                }
+            }
+        }
+        __syncthreads();                      // pair slots complete; staging buffer i % nbuf free
+        if (i + (int)nbuf < nblk) issue_block(i + (int)nbuf);
+        // block i-1's sums were read by write_y before the barrier above: clear
+        // them for block i+1, which adds only after its own first barrier
+        if (i > 0)
+            for (int o = threadIdx.x; o < NB * 256; o += blockDim.x) sums[((i + 1) & 1) * NB * 256 + o] = 0;
+
+        bt_v4i acc[NB];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[nb] = bt_v4i{0, 0, 0, 0};
+        uint32_t p = pstart;
+        if (in_lds) {
+            p = min(p, 8u * (4u * g.n - 1u));   // a corrupt stream stays inside the buffer (+ slack)
+            // the buffer base is a multiple of 8: adding it keeps p & 7 and
+            // makes p & ~7 the slot's LDS address
+            p += pair_base;
+            bt_contract<NB, TPL>(words[i], p, BtWinLds{}, lut_base, xb, acc);
+        } else {
+            bt_contract<NB, TPL>(words[i], p, BtWinGlobal{prs, 4u * g.g0}, lut_base, xb, acc);
+        }
+        // the wavefronts' partials (each exact after >> 8) meet in LDS
+        int32_t *s = sums + (i & 1) * NB * 256;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) atomicAdd(&s[(nb * 4 + k) * 64 + lane], acc[nb][k] >> 8);
+    }
+    __syncthreads();
+    write_y(nblk - 1);
+}
+
+// Launch plan.
+struct BtPlan {
+    int nwaves, nb, tpl;
+    unsigned grid;
+    int bq, br;             // blocks per workgroup: bq, plus one for the first br workgroups
+    uint32_t stage_bytes;   // one staging buffer
+    uint32_t nbuf;          // staging buffers in the ring
+    uint32_t pair_bytes;    // the pair-slot buffer
+    size_t lds;             // total dynamic LDS
+};
+
+// Fast-path constraints: X rows 16-byte aligned (K % 32 == 0), K within
+// 8 wavefronts x 4 lane groups x 8 tiles, N <= 32.
+static bool bt64_supported(int64_t K, int64_t N) {
+    return K > 0 && K % 32 == 0 && (K + 63) / 64 <= 8 * 4 * 8 && N >= 1 && N <= 32;
+}
+
+static bool bt64_plan(int64_t M, int64_t K, int64_t N, int64_t payload_bytes, BtPlan *p) {
+    if (!bt64_supported(K, N) || M <= 0) return false;
+    const int64_t T = (K + 63) / 64;
+    p->tpl = T <= 64 ? 2 : T <= 128 ? 4 : 8;
+    p->nwaves = (int)((T + 4 * p->tpl - 1) / (4 * p->tpl));
+    p->nb = N <= 16 ? 1 : 2;
+    const int64_t nblk_max = BT_NBLK(p->tpl);
+    const int64_t blocks = (M + BT_ROWS - 1) / BT_ROWS;
+    // one workgroup per CU when that leaves each at most nblk_max blocks
+    const int64_t grid = std::max<int64_t>(std::min<int64_t>(blocks, BT_CUS), (blocks + nblk_max - 1) / nblk_max);
+    p->grid = (unsigned)grid;
+    p->bq = (int)(blocks / grid);
+    p->br = (int)(blocks % grid);
+    const int64_t per_wg = (blocks + grid - 1) / grid;                  // blocks of the busiest workgroup
+    const int64_t wg_per_cu = (grid + BT_CUS - 1) / BT_CUS;
+    const int64_t budget = BT_LDS_MAX / wg_per_cu;
+    // Staging: 1.2x the average block plus 2 KB (a denser block falls back
+    // to global-memory windows), capped at the densest block; the pair-slot
+    // buffer holds twice that.
+    const int64_t avg = payload_bytes / std::max<int64_t>(blocks, 1);
+    const int64_t worst = (int64_t)BT_ROWS * T * 32 + 64;
+    int64_t stage = std::min<int64_t>(worst, avg + avg / 5 + 2048) + 32;
+    stage = (stage + 1023) / 1024 * 1024;
+    const int64_t pair = 2 * stage + BT_SLACK_BYTES;
+    const int64_t fixed = BT_LUT_BYTES + 2 * BT_ROWS * 8 * 4 + 2 * p->nb * 256 * 4;
+    int64_t nbuf = (budget - fixed - pair) / stage;
+    if (nbuf < 1) return false;
+    nbuf = std::min(nbuf, per_wg);
+    p->stage_bytes = (uint32_t)stage;
+    p->nbuf = (uint32_t)nbuf;
+    p->pair_bytes = (uint32_t)pair;
+    p->lds = (size_t)(fixed + pair + nbuf * stage);
+    return true;
+}
+
+template <int NB, int TPL>
+static void launch_bt64_t(const BtPlan &p, const uint64_t *bitmaps, const uint32_t *offsets,
+                          const uint8_t *payload, uint32_t payload_bytes, int M, int K, const uint8_t *X, int N,
+                          int32_t *Y, hipStream_t stream) {
+    (void)hipFuncSetAttribute((const void *)k_bt64_w4a4<NB, TPL>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)p.lds);
+    hipLaunchKernelGGL((k_bt64_w4a4<NB, TPL>), dim3(p.grid), dim3(64 * p.nwaves), p.lds, stream, bitmaps, offsets,
+                       payload, payload_bytes, M, K, X, N, Y, p.stage_bytes, p.nbuf, p.pair_bytes, p.bq, p.br);
+}
+
+static void launch_bt64_w4a4(const BtPlan &p, const uint64_t *bitmaps, const uint32_t *offsets,
+                             const uint8_t *payload, uint32_t payload_bytes, int M, int K, const uint8_t *X, int N,
+                             int32_t *Y, hipStream_t stream) {
+#define BT_LAUNCH(NB, TPL) launch_bt64_t<NB, TPL>(p, bitmaps, offsets, payload, payload_bytes, M, K, X, N, Y, stream)
+    if (p.nb == 1) {
+        if (p.tpl == 2) BT_LAUNCH(1, 2); else if (p.tpl == 4) BT_LAUNCH(1, 4); else BT_LAUNCH(1, 8);
+    } else {
+        if (p.tpl == 2) BT_LAUNCH(2, 2); else if (p.tpl == 4) BT_LAUNCH(2, 4); else BT_LAUNCH(2, 8);
+    }
+#undef BT_LAUNCH
+}

@@ -16,8 +16,7 @@
 #include "bitmap_spmm.h"
 #include "device_common.h"
 #include "kernels_rowwave.hip"
-#include "kernels_mfma.hip"
-#include "kernels_mfma_wg.hip"
+#include "kernels_bt64.hip"
 
 namespace {
 
@@ -54,7 +53,7 @@ int launch_status() {
 bool algo_supported(int algo, int dtype, const Shape &s) {
     switch (algo) {
         case BSP_ALGO_ROWWAVE: return true;
-        case BSP_ALGO_MFMA: return dtype == BSP_INT4 && mfma_w4a4_supported(s.K);
+        case BSP_ALGO_MFMA: return dtype == BSP_INT4 && bt64_supported(s.K, s.N);
         default: return false;
     }
 }
@@ -95,18 +94,14 @@ extern "C" int spmm_bitmap_w4a4_algo(const uint64_t *bitmaps, const uint32_t *of
     if (!algo_supported(algo, BSP_INT4, s)) algo = BSP_ALGO_ROWWAVE;   // layout outside a fast path's range
     switch (algo) {
         case BSP_ALGO_MFMA: {
-            BspMfWgPlan plan;
-            if (mfma_wg_plan((int)M, (int)K, (int)N, &plan)) {
-                if (N <= 16)
-                    launch_mfma_wg_nb<1>(plan, bitmaps, offsets, payload, (uint32_t)payload_bytes, (int)M, (int)K, X,
-                                         (int)N, Y, stream);
-                else
-                    launch_mfma_wg_nb<2>(plan, bitmaps, offsets, payload, (uint32_t)payload_bytes, (int)M, (int)K, X,
-                                         (int)N, Y, stream);
-            } else {
-                launch_mfma_w4a4(bitmaps, offsets, payload, (uint32_t)payload_bytes, (int)M, (int)K, X, (int)N, Y,
-                                 stream);
+            BtPlan plan;
+            if (bt64_plan(M, K, N, payload_bytes, &plan)) {
+                launch_bt64_w4a4(plan, bitmaps, offsets, payload, (uint32_t)payload_bytes, (int)M, (int)K, X, (int)N,
+                                 Y, stream);
+                break;
             }
+            launch_rowwave_w4a4(bitmaps, offsets, payload, (uint32_t)payload_bytes, (int)M, (int)K, X, (int)N, Y,
+                                stream);
             break;
         }
         default:

@@ -111,6 +111,21 @@ def test_w4a4_extremes(dev, algo):
 
 
 @pytest.mark.parametrize("algo", INT4_ALGOS, ids=lambda a: _NAMES[a])
+@pytest.mark.parametrize("dense_block", [0, 3, 9])
+def test_w4a4_uneven_block_density(dev, algo, dense_block):
+    # One 16-row block at full density among blocks at 2 %: its payload is far
+    # larger than the average block the staging area is sized for, so the MFMA
+    # kernel must take its global-memory window path for that block only.
+    rng = np.random.default_rng(100 + dense_block)
+    M, K, N = 160, 64 * 40, 8
+    keep = np.full((M, 1), 0.02)
+    keep[16 * dense_block:16 * dense_block + 16] = 1.0
+    W = workloads._int4_weights(rng, M, K, keep)
+    X = workloads.int4_activations(rng, (N, K))
+    assert np.array_equal(run_w4a4(W, X, algo, dev), oracle_w4a4(W, X))
+
+
+@pytest.mark.parametrize("algo", INT4_ALGOS, ids=lambda a: _NAMES[a])
 def test_w4a4_k_zero(dev, algo):
     W = np.zeros((9, 0), np.int8)
     X = np.zeros((3, 0), np.int8)

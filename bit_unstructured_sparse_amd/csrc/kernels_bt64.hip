@@ -530,12 +530,19 @@ static bool bt64_plan(int64_t M, int64_t K, int64_t N, int64_t payload_bytes, Bt
     const int64_t pair = 2 * stage + BT_SLACK_BYTES;
     const int64_t fixed = BT_LUT_BYTES + 2 * BT_ROWS * 8 * 4 + 2 * p->nb * 256 * 4;
     int64_t nbuf = (budget - fixed - pair) / stage;
-    if (nbuf < 1) return false;
-    nbuf = std::min(nbuf, per_wg);
+    if (nbuf < 1) {
+        // blocks too dense to stage even once: every block reads its windows
+        // from global memory (a zero-byte staging buffer fits no block)
+        stage = 0;
+        nbuf = 1;
+    } else {
+        nbuf = std::min(nbuf, per_wg);
+    }
+    const int64_t pair_used = stage ? pair : 0;
     p->stage_bytes = (uint32_t)stage;
     p->nbuf = (uint32_t)nbuf;
-    p->pair_bytes = (uint32_t)pair;
-    p->lds = (size_t)(fixed + pair + nbuf * stage);
+    p->pair_bytes = (uint32_t)pair_used;
+    p->lds = (size_t)(fixed + pair_used + nbuf * stage);
     return true;
 }
 

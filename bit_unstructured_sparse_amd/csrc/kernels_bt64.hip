@@ -18,26 +18,21 @@
 // A and B use the same one).
 //
 // Loads. Everything is requested up front: the block-boundary offsets (scalar
-// loads), every block's bitmap words for this lane, X (once per workgroup,
-// coalesced, into LDS rows) and the payload of the first blocks. A block's
-// payload is one contiguous range (the stream is in row-major tile order), so
-// it needs only its two boundary offsets; each lane's start inside it is the
-// block start plus bitmap popcounts (the offset definition of Sec. V-A),
-// exchanged across wavefronts through LDS. Blocks are decoded in order while
-// the later ones are still in flight; a ring of LDS buffers is refilled as
-// blocks are finished.
-//
-// Payload layout in LDS. Random 8-byte LDS reads are fast on gfx950 only when
-// 8-byte aligned (a dword-aligned ds_read_b64 costs ~9x more), and a window of
-// 8 nibbles starting at an arbitrary nibble spans two arbitrary consecutive
-// dwords. A block is therefore staged as "pair slots": slot s (8 bytes,
-// 8-byte aligned) holds payload dwords s and s+1, so the window for nibble p is
-// the aligned read of slot p >> 3 and a funnel shift by 4 * (p & 7). The
-// staging is LDS DMA of 4-byte elements whose source offsets duplicate every
-// dword (lanes 2i and 2i+1 read dwords i and i+1): no VGPRs, no vector ALU.
-// It takes twice the payload's bytes; a block whose payload does not fit the
-// buffer sized at launch reads its windows from global memory instead
+// loads), every block's bitmap words for this lane, this lane's X slices (kept
+// in VGPRs for the whole launch) and the payload of as many blocks as the LDS
+// ring holds. A block's payload is one contiguous range of the stream (tiles
+// are in row-major order), so it needs only its two boundary offsets; it is
+// moved by LDS DMA (16-byte granules, no VGPRs). Each lane's start inside it
+// is the block start plus bitmap popcounts (the offset definition of
+// Sec. V-A), exchanged across wavefronts through LDS at the block's barrier.
+// Blocks are decoded in order while later ones are still in flight; a
+// buffer is refilled once the block in it has been decoded. A block whose
+// payload does not fit a buffer reads its windows from global memory instead
 // (slower, same result).
+//
+// Windows. The 8 nibbles a step needs start at an arbitrary nibble p of the
+// block's stream and span the two dwords p >> 3 and (p >> 3) + 1; one
+// ds_read2_b32 fetches both and a funnel shift by 4 * (p & 7) aligns them.
 //
 // Decode of 8 positions (one byte b of the word). The window is split into
 // even and odd nibbles placed in the high half of each byte (so a byte holds
@@ -56,7 +51,6 @@
 #define BT_MAX_WAVES 8
 #define BT_LUT_COPIES 16               // selector-table copies in LDS (lane l reads copy l % 16)
 #define BT_LUT_BYTES (2048 * BT_LUT_COPIES)   // 256 entries x 8 bytes per copy
-#define BT_SLACK_BYTES 512              // windows a corrupt stream could run past a buffer
 #define BT_LDS_MAX (160 * 1024)
 #define BT_CUS 256
 
@@ -69,6 +63,7 @@
 typedef int bt_v4i __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void bt_lds_void;
 typedef __attribute__((address_space(3))) const uint64_t bt_lds_u64;
+typedef __attribute__((address_space(3))) const uint32_t bt_lds_u32;
 typedef __attribute__((address_space(3))) const bt_v4i bt_lds_v4i;
 
 // Selector table: entry b (a bitmap byte) is the v_perm_b32 selector pair that
@@ -158,11 +153,15 @@ __device__ __forceinline__ void bt_decode_tile(uint64_t word, uint32_t p, const 
     }
 }
 
-// Window source: pair slots in LDS. p already includes the LDS byte address of
-// slot 0 (a multiple of 8), so p & ~7 is the slot's address and p & 7 the
-// nibble offset inside it.
+// Window source: the staged stream in LDS.
 struct BtWinLds {
-    __device__ __forceinline__ uint2 operator()(uint32_t p) const { return bt_lds_pair(p & ~7u); }
+    // p counts nibbles from twice the staging buffer's LDS address (a
+    // multiple of 16 bytes), so dword p >> 3 of the stream sits at LDS byte
+    // address (p >> 1) & ~3; the two dwords come from one ds_read2_b32
+    __device__ __forceinline__ uint2 operator()(uint32_t p) const {
+        const bt_lds_u32 *q = (const bt_lds_u32 *)(uintptr_t)((p >> 1) & ~3u);
+        return uint2{q[0], q[1]};
+    }
 };
 
 // Window source: global memory through a range-checked buffer resource
@@ -218,15 +217,15 @@ __device__ __forceinline__ BtRange bt_range(uint32_t nibA, uint32_t nibB) {
 }
 
 // LDS layout (bytes):
-//   [selector table copies][row totals 2 x 16 x 8 ints][sums 2 x NB x 256 ints]
-//   [pair-slot buffer, pair_bytes][nbuf staging buffers of stage_bytes]
+//   [selector table copies][row totals 2 x 16 x 8 ints][sums 3 x NB x 256 ints]
+//   [nbuf staging buffers of stage_bytes]
 // Workgroup g owns blocks [g*bq + min(g, br), ...): bq or bq + 1 of them.
 template <int NB, int TPL>
 __global__ __launch_bounds__(BT_WG_THREADS(TPL)) void k_bt64_w4a4(
         const uint64_t *__restrict__ bitmaps, const uint32_t *__restrict__ offsets,
         const uint8_t *__restrict__ payload, uint32_t payload_bytes, int M, int K,
         const uint8_t *__restrict__ X, int N, int32_t *__restrict__ Y, uint32_t stage_bytes, uint32_t nbuf,
-        uint32_t pair_bytes, int bq, int br) {
+        int bq, int br) {
     constexpr int NBLK = BT_NBLK(TPL);
     extern __shared__ __attribute__((aligned(16))) uint8_t bt_smem[];
     const int nwaves = blockDim.x >> 6;
@@ -242,10 +241,8 @@ __global__ __launch_bounds__(BT_WG_THREADS(TPL)) void k_bt64_w4a4(
 
     const uint32_t lut_base = bt_lds_addr(bt_smem) + (uint32_t)(lane % BT_LUT_COPIES) * 8u;
     int32_t *wt = reinterpret_cast<int32_t *>(bt_smem + BT_LUT_BYTES);                  // [2][16][8]
-    int32_t *sums = wt + 2 * BT_ROWS * 8;                                                // [2][NB*256]
-    uint8_t *pairs = reinterpret_cast<uint8_t *>(sums + 2 * NB * 256);
-    uint8_t *stage = pairs + pair_bytes;
-    const uint32_t pair_base = bt_lds_addr(pairs);
+    int32_t *sums = wt + 2 * BT_ROWS * 8;                                                // [3][NB*256]
+    uint8_t *stage = reinterpret_cast<uint8_t *>(sums + 3 * NB * 256);
     const __amdgpu_buffer_rsrc_t prs = bt_rsrc(payload, payload_bytes);
 
     // (1) block boundaries (wave-uniform scalar loads), before anything else:
@@ -268,20 +265,30 @@ __global__ __launch_bounds__(BT_WG_THREADS(TPL)) void k_bt64_w4a4(
     const int wg_rows = min(nblk * BT_ROWS, M - m_first);
     const __amdgpu_buffer_rsrc_t brs = bt_rsrc(bitmaps + (int64_t)m_first * T, (uint32_t)wg_rows * (uint32_t)T * 8u);
     uint64_t words[NBLK][TPL];
+    // two consecutive tiles per 16-byte load (one per 8-byte load at TPL 8,
+    // where the wider form costs registers); a tile at or past T reads as 0
+    constexpr int WPL = TPL >= 8 ? 1 : 2;   // words per load
     auto load_words = [&](int i) -> void {
         const int rr = i * BT_ROWS + r;   // row inside the workgroup's range
 #pragma unroll
-        for (int k = 0; k < TPL; ++k) {
+        for (int k = 0; k < TPL; k += WPL) {
             const uint32_t off = (rr < wg_rows && t0 + k < T) ? ((uint32_t)rr * (uint32_t)T + (uint32_t)(t0 + k)) * 8u
-                                                              : 0xFFFFFFF0u;
-            words[i][k] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(brs, off, 0, 0));
+                                                              : 0xFFFFFFE0u;
+            if constexpr (WPL == 2) {
+                const bt_v4i v = __builtin_bit_cast(bt_v4i, __builtin_amdgcn_raw_buffer_load_b128(brs, off, 0, 0));
+                words[i][k] = ((uint64_t)(uint32_t)v.y << 32) | (uint32_t)v.x;
+                words[i][k + 1] = t0 + k + 1 < T ? ((uint64_t)(uint32_t)v.w << 32) | (uint32_t)v.z : 0ull;
+            } else {
+                words[i][k] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(brs, off, 0, 0));
+            }
         }
     };
+
     uint32_t vm_issued = 0;           // vector-memory operations issued so far by this wavefront
     uint32_t vm_mark[NBLK];
     auto fits = [&](int i) -> bool {
         const BtRange g = bt_range(nib[i], nib[i + 1]);
-        return (g.n + 1u) * 16u <= stage_bytes && g.n * 32u + BT_SLACK_BYTES <= pair_bytes;
+        return g.n * 16u <= stage_bytes;
     };
     auto issue_block = [&](int i) -> void {
         if (fits(i)) {
@@ -302,7 +309,8 @@ __global__ __launch_bounds__(BT_WG_THREADS(TPL)) void k_bt64_w4a4(
     for (int i = 0; i < NBLK; ++i) {
         if (i < nblk) {
             load_words(i);
-            vm_issued += TPL;
+            vm_issued += TPL / WPL;
+            vm_mark[i] = vm_issued;   // the words; staging the block raises it
             if (i < (int)nbuf) issue_block(i);
         }
         if (i == 0) __builtin_amdgcn_sched_barrier(0);
@@ -342,8 +350,8 @@ __global__ __launch_bounds__(BT_WG_THREADS(TPL)) void k_bt64_w4a4(
         vm_issued += LUT_ROUNDS;
     }
 
-    // zero both sum buffers (first added to after the first block's barriers)
-    for (int o = threadIdx.x; o < 2 * NB * 256; o += blockDim.x) sums[o] = 0;
+    // zero the sum buffers (first added to after the first block's barrier)
+    for (int o = threadIdx.x; o < 3 * NB * 256; o += blockDim.x) sums[o] = 0;
     {
         __attribute__((address_space(3))) uint64_t *lut_lds =
                 (__attribute__((address_space(3))) uint64_t *)(uintptr_t)bt_lds_addr(bt_smem);
@@ -368,17 +376,20 @@ __global__ __launch_bounds__(BT_WG_THREADS(TPL)) void k_bt64_w4a4(
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 xb[nb][k][j] = bt_b_operand(xw[nb][k][2 * j], xw[nb][k][2 * j + 1]);
-                asm volatile("" : "+v"(xb[nb][k][j]));
+                if constexpr (NBLK > 1) asm volatile("" : "+v"(xb[nb][k][j]));
             }
 
-    // (5) blocks in order. Before the first barrier of block i each
-    // wavefront posts its row totals for block i; after it, each lane knows
-    // its start. Y of block i is written after the first barrier of block i+1
-    // (or after the loop), when every wavefront's partial is in.
+    // (5) blocks in order, one barrier each. Before the barrier of block i
+    // each wavefront posts its row totals for block i; after it, each lane
+    // knows its start, Y of block i-1 is complete (every wavefront's partial
+    // is in) and staging buffer (i-1) % nbuf is free for the next payload.
+    // Sums rotate over three buffers: block i adds into i % 3 after barrier
+    // i, block i-1's are read after barrier i, and i+1 % 3 (last read before
+    // barrier i) is cleared after barrier i for block i+1.
     auto write_y = [&](int i) -> void {
         const int m0 = (b_begin + i) * BT_ROWS;
         const int rows = min(BT_ROWS, M - m0);
-        const int32_t *s = sums + (i & 1) * NB * 256;
+        const int32_t *s = sums + (i % 3) * NB * 256;
         // D layout of v_mfma_i32_16x16x64_i8: lane l, register k -> row 4*(l/16)+k, column l%16
         for (int o = threadIdx.x; o < NB * 256; o += blockDim.x) {
             const int nb = o >> 8, col = (o >> 4) & 15, rl = o & 15;
@@ -410,7 +421,12 @@ __global__ __launch_bounds__(BT_WG_THREADS(TPL)) void k_bt64_w4a4(
 
         bt_wait_vm(vm_issued - vm_mark[i]);   // this wavefront's share of block i landed
         __syncthreads();                      // ... everyone's; block i-1 is decoded and summed
-        if (i > 0) write_y(i - 1);
+        if (i > 0) {
+            write_y(i - 1);
+            if (i - 1 + (int)nbuf < nblk) issue_block(i - 1 + (int)nbuf);
+        }
+        if (i >= 2)
+            for (int o = threadIdx.x; o < NB * 256; o += blockDim.x) sums[((i + 1) % 3) * NB * 256 + o] = 0;
 
         // lane start: rows before r, wavefronts before this one, lane groups before q
         uint32_t pstart;
@@ -436,48 +452,21 @@ __global__ __launch_bounds__(BT_WG_THREADS(TPL)) void k_bt64_w4a4(
             pstart = r < rows ? (nib[i] & 31u) + (s - row_total) + before_w + (incl - seg) : 0u;
         }
 
-        if (in_lds) {
-            // staging -> pair slots: slot 4u+k = stream dwords 4u+k, 4u+k+1
-            const uint32_t sb = bt_lds_addr(stage + (uint32_t)(i % (int)nbuf) * stage_bytes);
-            for (uint32_t u0 = (uint32_t)wave * 64u; u0 < g.n; u0 += blockDim.x) {
-                const uint32_t u = u0 + (uint32_t)lane;     // consecutive granules across the lanes
-                const uint32_t uc = min(u, g.n);             // granule g.n is the last one staged
-                const bt_v4i d = *(bt_lds_v4i *)(uintptr_t)(sb + uc * 16u);
-                // dword 4u+4 is the next lane's first dword; lane 63 reads it
-                int d4 = __builtin_amdgcn_update_dpp(0, d.x, 0x130, 0xF, 0xF, false);   // wave_shl:1
-                if (lane == 63 && u < g.n) d4 = *(const __attribute__((address_space(3))) int *)(uintptr_t)(sb + u * 16u + 16u);
-                if (u < g.n) {
-                    // the two 16-byte halves in an order that spreads each half-wave over all banks
-                    const bt_v4i h0 = {d.x, d.y, d.y, d.z}, h1 = {d.z, d.w, d.w, d4};
-                    const bool swap = (u >> 3) & 1u;
-                    const uint32_t o = pair_base + u * 32u + (swap ? 16u : 0u);
-                    *(__attribute__((address_space(3))) bt_v4i *)(uintptr_t)o = swap ? h1 : h0;
-                    *(__attribute__((address_space(3))) bt_v4i *)(uintptr_t)(o ^ 16u) = swap ? h0 : h1;
-                }
-            }
-        }
-        __syncthreads();                      // pair slots complete; staging buffer i % nbuf free
-        if (i + (int)nbuf < nblk) issue_block(i + (int)nbuf);
-        // block i-1's sums were read by write_y before the barrier above: clear
-        // them for block i+1, which adds only after its own first barrier
-        if (i > 0)
-            for (int o = threadIdx.x; o < NB * 256; o += blockDim.x) sums[((i + 1) & 1) * NB * 256 + o] = 0;
-
         bt_v4i acc[NB];
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) acc[nb] = bt_v4i{0, 0, 0, 0};
         uint32_t p = pstart;
         if (in_lds) {
-            p = min(p, 8u * (4u * g.n - 1u));   // a corrupt stream stays inside the buffer (+ slack)
-            // the buffer base is a multiple of 8: adding it keeps p & 7 and
-            // makes p & ~7 the slot's LDS address
-            p += pair_base;
+            // a corrupt stream stays inside the staged granules
+            p = min(p, 8u * (4u * g.n - 2u));
+            // twice the buffer's address (a multiple of 32) keeps p & 7
+            p += 2u * bt_lds_addr(stage + (uint32_t)(i % (int)nbuf) * stage_bytes);
             bt_contract<NB, TPL>(words[i], p, BtWinLds{}, lut_base, xb, acc);
         } else {
             bt_contract<NB, TPL>(words[i], p, BtWinGlobal{prs, 4u * g.g0}, lut_base, xb, acc);
         }
         // the wavefronts' partials (each exact after >> 8) meet in LDS
-        int32_t *s = sums + (i & 1) * NB * 256;
+        int32_t *s = sums + (i % 3) * NB * 256;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -494,7 +483,6 @@ struct BtPlan {
     int bq, br;             // blocks per workgroup: bq, plus one for the first br workgroups
     uint32_t stage_bytes;   // one staging buffer
     uint32_t nbuf;          // staging buffers in the ring
-    uint32_t pair_bytes;    // the pair-slot buffer
     size_t lds;             // total dynamic LDS
 };
 
@@ -521,28 +509,25 @@ static bool bt64_plan(int64_t M, int64_t K, int64_t N, int64_t payload_bytes, Bt
     const int64_t wg_per_cu = (grid + BT_CUS - 1) / BT_CUS;
     const int64_t budget = BT_LDS_MAX / wg_per_cu;
     // Staging: 1.2x the average block plus 2 KB (a denser block falls back
-    // to global-memory windows), capped at the densest block; the pair-slot
-    // buffer holds twice that.
+    // to global-memory windows), capped at the densest block.
     const int64_t avg = payload_bytes / std::max<int64_t>(blocks, 1);
     const int64_t worst = (int64_t)BT_ROWS * T * 32 + 64;
     int64_t stage = std::min<int64_t>(worst, avg + avg / 5 + 2048) + 32;
     stage = (stage + 1023) / 1024 * 1024;
-    const int64_t pair = 2 * stage + BT_SLACK_BYTES;
-    const int64_t fixed = BT_LUT_BYTES + 2 * BT_ROWS * 8 * 4 + 2 * p->nb * 256 * 4;
-    int64_t nbuf = (budget - fixed - pair) / stage;
-    if (nbuf < 1) {
-        // blocks too dense to stage even once: every block reads its windows
-        // from global memory (a zero-byte staging buffer fits no block)
+    const int64_t fixed = BT_LUT_BYTES + 2 * BT_ROWS * 8 * 4 + 3 * p->nb * 256 * 4;
+    int64_t nbuf = (budget - fixed) / stage;
+    nbuf = std::min(nbuf, per_wg);
+    // a buffer is refilled one block after it was decoded, so a ring of one
+    // works only when it never refills
+    if (nbuf < std::min<int64_t>(2, per_wg)) {
+        // blocks too dense to stage: every block reads its windows from
+        // global memory (a zero-byte staging buffer fits no block)
         stage = 0;
         nbuf = 1;
-    } else {
-        nbuf = std::min(nbuf, per_wg);
     }
-    const int64_t pair_used = stage ? pair : 0;
     p->stage_bytes = (uint32_t)stage;
     p->nbuf = (uint32_t)nbuf;
-    p->pair_bytes = (uint32_t)pair_used;
-    p->lds = (size_t)(fixed + pair_used + nbuf * stage);
+    p->lds = (size_t)(fixed + nbuf * stage);
     return true;
 }
 
@@ -553,7 +538,7 @@ static void launch_bt64_t(const BtPlan &p, const uint64_t *bitmaps, const uint32
     (void)hipFuncSetAttribute((const void *)k_bt64_w4a4<NB, TPL>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               (int)p.lds);
     hipLaunchKernelGGL((k_bt64_w4a4<NB, TPL>), dim3(p.grid), dim3(64 * p.nwaves), p.lds, stream, bitmaps, offsets,
-                       payload, payload_bytes, M, K, X, N, Y, p.stage_bytes, p.nbuf, p.pair_bytes, p.bq, p.br);
+                       payload, payload_bytes, M, K, X, N, Y, p.stage_bytes, p.nbuf, p.bq, p.br);
 }
 
 static void launch_bt64_w4a4(const BtPlan &p, const uint64_t *bitmaps, const uint32_t *offsets,

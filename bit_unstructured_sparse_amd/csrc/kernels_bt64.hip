@@ -255,12 +255,49 @@ __global__ __launch_bounds__(BT_WG_THREADS(TPL)) void k_bt64_w4a4(
     }
     __builtin_amdgcn_sched_barrier(0);
 
-    // (2) per block, in block order: this lane's words, then the payload DMA
-    // of the block into staging buffer i % nbuf (its granules in stream
-    // order, 1 KB = 64 lanes x 16 bytes per instruction; range checks of raw
-    // buffer loads cover the per-lane offset only, so every offset is in the
-    // per-lane operand). A block that does not fit is not staged: it reads
-    // its windows from global memory.
+    // (2) loads that need no offsets, so that waiting for them never waits
+    // for a payload DMA: the selector table, this lane's X slices, every
+    // block's bitmap words. Then (after the offsets land) the payload DMA of
+    // the first nbuf blocks, each into staging buffer i % nbuf (its granules
+    // in stream order, 1 KB = 64 lanes x 16 bytes per instruction; range
+    // checks of raw buffer loads cover the per-lane offset only, so every
+    // offset is in the per-lane operand). A block that does not fit is not
+    // staged: it reads its windows from global memory.
+    uint32_t vm_issued = 0;           // vector-memory operations issued so far by this wavefront
+    // the selector table for its 16 interleaved LDS copies: LDS slot v
+    // (8 bytes) holds entry v / 16; wavefront w fills slots 64 (w + 8 e) .. +63
+    // (consecutive addresses, so the writes cannot conflict)
+    constexpr int LUT_ROUNDS = 256 * BT_LUT_COPIES / 64 / 8;
+    uint2 lut_entry[LUT_ROUNDS];
+    {
+        const __amdgpu_buffer_rsrc_t lrs = bt_rsrc(&bt_lut_global, (uint32_t)sizeof(BtLut));
+#pragma unroll
+        for (int e = 0; e < LUT_ROUNDS; ++e) {
+            const uint32_t v = (uint32_t)((wave + 8 * e) * 64 + lane);
+            lut_entry[e] = __builtin_bit_cast(
+                    uint2, __builtin_amdgcn_raw_buffer_load_b64(lrs, wave < 8 ? (v / BT_LUT_COPIES) * 8u : 0xFFFFFFF0u,
+                                                                0, 0));
+        }
+        vm_issued += LUT_ROUNDS;
+    }
+
+    // this lane's X slices, once for all blocks (column n >= N or tile >= T: zeros)
+    uint32_t xw[NB][TPL][8];
+    {
+        const __amdgpu_buffer_rsrc_t xrs = bt_rsrc(X, (uint32_t)N * xs);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int k = 0; k < TPL; ++k) {
+                const int n = r + 16 * nb;
+                const uint32_t off = (n < N && t0 + k < T) ? (uint32_t)n * xs + (uint32_t)(t0 + k) * 32u : 0xFFFFFFE0u;
+                const bt_v4i v0 = __builtin_bit_cast(bt_v4i, __builtin_amdgcn_raw_buffer_load_b128(xrs, off, 0, 0));
+                const bt_v4i v1 = __builtin_bit_cast(bt_v4i, __builtin_amdgcn_raw_buffer_load_b128(xrs, off + 16u, 0, 0));
+                xw[nb][k][0] = v0.x; xw[nb][k][1] = v0.y; xw[nb][k][2] = v0.z; xw[nb][k][3] = v0.w;
+                xw[nb][k][4] = v1.x; xw[nb][k][5] = v1.y; xw[nb][k][6] = v1.z; xw[nb][k][7] = v1.w;
+            }
+        vm_issued += 2 * NB * TPL;
+    }
     const int m_first = b_begin * BT_ROWS;
     const int wg_rows = min(nblk * BT_ROWS, M - m_first);
     const __amdgpu_buffer_rsrc_t brs = bt_rsrc(bitmaps + (int64_t)m_first * T, (uint32_t)wg_rows * (uint32_t)T * 8u);
@@ -284,72 +321,12 @@ __global__ __launch_bounds__(BT_WG_THREADS(TPL)) void k_bt64_w4a4(
         }
     };
 
-    uint32_t vm_issued = 0;           // vector-memory operations issued so far by this wavefront
-    uint32_t vm_mark[NBLK];
-    auto fits = [&](int i) -> bool {
-        const BtRange g = bt_range(nib[i], nib[i + 1]);
-        return g.n * 16u <= stage_bytes;
-    };
-    auto issue_block = [&](int i) -> void {
-        if (fits(i)) {
-            const BtRange g = bt_range(nib[i], nib[i + 1]);
-            uint8_t *buf = stage + (uint32_t)(i % (int)nbuf) * stage_bytes;
-            const uint32_t n_ins = (g.n + 63u) >> 6;
-            for (uint32_t j = (uint32_t)wave; j < n_ins; j += (uint32_t)nwaves) {
-                const uint32_t u = j * 64u + (uint32_t)lane;
-                if (u < g.n)
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(prs, (bt_lds_void *)(buf + j * 1024u), 16,
-                                                             (g.g0 + u) * 16u, 0, 0, 0);
-                ++vm_issued;
-            }
-        }
-        vm_mark[i] = vm_issued;
-    };
 #pragma unroll
-    for (int i = 0; i < NBLK; ++i) {
+    for (int i = 0; i < NBLK; ++i)
         if (i < nblk) {
             load_words(i);
             vm_issued += TPL / WPL;
-            vm_mark[i] = vm_issued;   // the words; staging the block raises it
-            if (i < (int)nbuf) issue_block(i);
         }
-        if (i == 0) __builtin_amdgcn_sched_barrier(0);
-    }
-
-    // (3) this lane's X slices, once for all blocks (column n >= N or tile >= T: zeros)
-    uint32_t xw[NB][TPL][8];
-    {
-        const __amdgpu_buffer_rsrc_t xrs = bt_rsrc(X, (uint32_t)N * xs);
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-            for (int k = 0; k < TPL; ++k) {
-                const int n = r + 16 * nb;
-                const uint32_t off = (n < N && t0 + k < T) ? (uint32_t)n * xs + (uint32_t)(t0 + k) * 32u : 0xFFFFFFE0u;
-                const bt_v4i v0 = __builtin_bit_cast(bt_v4i, __builtin_amdgcn_raw_buffer_load_b128(xrs, off, 0, 0));
-                const bt_v4i v1 = __builtin_bit_cast(bt_v4i, __builtin_amdgcn_raw_buffer_load_b128(xrs, off + 16u, 0, 0));
-                xw[nb][k][0] = v0.x; xw[nb][k][1] = v0.y; xw[nb][k][2] = v0.z; xw[nb][k][3] = v0.w;
-                xw[nb][k][4] = v1.x; xw[nb][k][5] = v1.y; xw[nb][k][6] = v1.z; xw[nb][k][7] = v1.w;
-            }
-        vm_issued += 2 * NB * TPL;
-    }
-    // (4) the selector table for its 16 interleaved LDS copies: LDS slot v
-    // (8 bytes) holds entry v / 16; wavefront w fills slots 64 (w + 8 e) .. +63
-    // (consecutive addresses, so the writes cannot conflict)
-    constexpr int LUT_ROUNDS = 256 * BT_LUT_COPIES / 64 / 8;
-    uint2 lut_entry[LUT_ROUNDS];
-    {
-        const __amdgpu_buffer_rsrc_t lrs = bt_rsrc(&bt_lut_global, (uint32_t)sizeof(BtLut));
-#pragma unroll
-        for (int e = 0; e < LUT_ROUNDS; ++e) {
-            const uint32_t v = (uint32_t)((wave + 8 * e) * 64 + lane);
-            lut_entry[e] = __builtin_bit_cast(
-                    uint2, __builtin_amdgcn_raw_buffer_load_b64(lrs, wave < 8 ? (v / BT_LUT_COPIES) * 8u : 0xFFFFFFF0u,
-                                                                0, 0));
-        }
-        vm_issued += LUT_ROUNDS;
-    }
-
     // zero the sum buffers (first added to after the first block's barrier)
     for (int o = threadIdx.x; o < 3 * NB * 256; o += blockDim.x) sums[o] = 0;
     {
@@ -378,6 +355,32 @@ __global__ __launch_bounds__(BT_WG_THREADS(TPL)) void k_bt64_w4a4(
                 xb[nb][k][j] = bt_b_operand(xw[nb][k][2 * j], xw[nb][k][2 * j + 1]);
                 if constexpr (NBLK > 1) asm volatile("" : "+v"(xb[nb][k][j]));
             }
+
+    uint32_t vm_mark[NBLK];
+    auto fits = [&](int i) -> bool {
+        const BtRange g = bt_range(nib[i], nib[i + 1]);
+        return g.n * 16u <= stage_bytes;
+    };
+    auto issue_block = [&](int i) -> void {
+        if (fits(i)) {
+            const BtRange g = bt_range(nib[i], nib[i + 1]);
+            uint8_t *buf = stage + (uint32_t)(i % (int)nbuf) * stage_bytes;
+            const uint32_t n_ins = (g.n + 63u) >> 6;
+            for (uint32_t j = (uint32_t)wave; j < n_ins; j += (uint32_t)nwaves) {
+                const uint32_t u = j * 64u + (uint32_t)lane;
+                if (u < g.n)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(prs, (bt_lds_void *)(buf + j * 1024u), 16,
+                                                             (g.g0 + u) * 16u, 0, 0, 0);
+                ++vm_issued;
+            }
+        }
+        vm_mark[i] = vm_issued;
+    };
+#pragma unroll
+    for (int i = 0; i < NBLK; ++i) {
+        vm_mark[i] = vm_issued;   // the words; staging the block raises it
+        if (i < nblk && i < (int)nbuf) issue_block(i);
+    }
 
     // (5) blocks in order, one barrier each. Before the barrier of block i
     // each wavefront posts its row totals for block i; after it, each lane

@@ -1,0 +1,381 @@
+// kernels_bt64_f16.hip -- block-staged bitmap decode + fp16 MFMA contraction
+// for the fp16 SpMM (u16 payload, fp16 X, fp32 accumulation, fp16 Y) on
+// gfx950. Included after kernels_bt64.hip, whose helpers it uses.
+//
+// The stream is the same BT64 format with 2-byte values (the column-bitmap
+// kernel of SPDP, Sec. 4.2, stores FP16 values the same way: one bit per
+// position, values packed in position order). The skeleton is the int4
+// kernel's: 16-row blocks, a workgroup per CU owning a contiguous run of
+// blocks, each block's payload staged into LDS by DMA from its two boundary
+// offsets, lane starts from bitmap popcounts, one barrier per block.
+//
+// Work split. One tile per lane: lane l = r + 16 q of wavefront w owns row r
+// and tile 4 w + q, so a block of T <= 64 tiles takes ceil(T / 4) <= 16
+// wavefronts. A lane keeps its tile's X (64 halves per column) in VGPRs.
+//
+// Decode of 4 positions (one nibble m of the word). The 4 values they can
+// need start at the lane's element p: the two dwords holding halves p .. p+3
+// come from three staged dwords and one funnel shift by 16 * (p & 1). Two
+// v_perm_b32 then place the nibble's nonzeros (in rank order in the window)
+// at their positions and zero the rest; the selector pair comes from a
+// 16-entry table indexed by m. Two nibbles make the 8 halves a lane feeds to
+// one v_mfma_f32_16x16x32_f16; MFMA j of a tile contracts positions
+// 8j .. 8j+7 of every lane's tile with the matching X slice (the K order
+// inside one MFMA is free as long as A and B use the same one).
+//
+// Sums. Each wavefront stores its fp32 partial of a block to its own LDS
+// slice; after the next barrier the slices are added in wavefront order and
+// rounded once to fp16 (round to nearest even), so a result does not depend
+// on timing.
+
+#define BF_ROWS 16
+#define BF_MAX_WAVES 16
+#define BF_NBLK 4                        // blocks per workgroup, at most
+#define BF_LDS_MAX (160 * 1024)
+#define BF_CUS 256
+
+typedef _Float16 bf_h8 __attribute__((ext_vector_type(8)));
+typedef float bf_f4 __attribute__((ext_vector_type(4)));
+
+// Selector table: entry m (a 4-bit group of the word) is the v_perm_b32
+// selector pair for output dwords {positions 0,1} and {positions 2,3}; the
+// perm's sources are S0 = window halves 2,3 (selector bytes 4..7) and
+// S1 = window halves 0,1 (0..3), and selector 0x0C yields a zero byte.
+struct BfLut {
+    uint32_t w[32];
+};
+
+constexpr BfLut bf_make_lut() {
+    BfLut t{};
+    for (uint32_t m = 0; m < 16; ++m) {
+        uint32_t sel[2] = {0x0C0C0C0Cu, 0x0C0C0C0Cu};
+        uint32_t rank = 0;
+        for (int pos = 0; pos < 4; ++pos) {
+            if ((m >> pos) & 1u) {
+                const uint32_t lo = 2u * rank, hi = 2u * rank + 1u;   // bytes of half `rank`
+                const int d = pos >> 1, sh = 16 * (pos & 1);
+                sel[d] = (sel[d] & ~(0xFFFFu << sh)) | ((lo | (hi << 8)) << sh);
+                ++rank;
+            }
+        }
+        t.w[2 * m] = sel[0];
+        t.w[2 * m + 1] = sel[1];
+    }
+    return t;
+}
+
+__device__ __attribute__((aligned(16))) const BfLut bf_lut_global = bf_make_lut();
+
+// Payload range of a block in 16-byte granules: [g0, g0 + n) covers halves
+// [eA, eB) plus one granule for the windows that read past the last value.
+__device__ __forceinline__ BtRange bf_range(uint32_t eA, uint32_t eB) {
+    const uint32_t g0 = eA >> 3;
+    const uint32_t g1 = (eB >= eA ? (eB + 7u) >> 3 : g0) + 1u;
+    return BtRange{g0, g1 - g0};
+}
+
+// Window source: the staged stream in LDS; p counts halves from half the
+// buffer's LDS address (a multiple of 16), so dword p >> 1 of the stream sits
+// at byte address (p << 1) & ~3 and p & 1 is the half inside it.
+struct BfWinLds {
+    __device__ __forceinline__ uint2 operator()(uint32_t p) const {
+        const bt_lds_u32 *q = (const bt_lds_u32 *)(uintptr_t)((p << 1) & ~3u);
+        const uint32_t d0 = q[0], d1 = q[1], d2 = q[2];
+        const uint32_t s = p << 4;   // funnel shift by 16 * (p & 1)
+        return uint2{__builtin_amdgcn_alignbit(d1, d0, s), __builtin_amdgcn_alignbit(d2, d1, s)};
+    }
+};
+
+// Window source: global memory (p counts halves from payload dword d0).
+struct BfWinGlobal {
+    __amdgpu_buffer_rsrc_t rs;
+    uint32_t d0;
+    __device__ __forceinline__ uint2 operator()(uint32_t p) const {
+        const uint32_t off = (d0 + (p >> 1)) * 4u;
+        const uint32_t a = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0);
+        const uint32_t b = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, off + 4u, 0, 0);
+        const uint32_t c = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, off + 8u, 0, 0);
+        const uint32_t s = p << 4;
+        return uint2{__builtin_amdgcn_alignbit(b, a, s), __builtin_amdgcn_alignbit(c, b, s)};
+    }
+};
+
+// Decode + contract one tile: 8 MFMAs of 8 positions each.
+template <int NB, class Win>
+__device__ __forceinline__ void bf_contract(uint64_t word, uint32_t p, const Win &win, uint32_t lut,
+                                            const bf_h8 (&xb)[NB][8], bf_f4 (&acc)[NB]) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        uint32_t A[4];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const uint32_t m = (uint32_t)(word >> (8 * j + 4 * h)) & 15u;
+            const uint2 sel = bt_lds_pair(lut + m * 8u);
+            const uint2 w = win(p);
+            A[2 * h] = __builtin_amdgcn_perm(w.y, w.x, sel.x);
+            A[2 * h + 1] = __builtin_amdgcn_perm(w.y, w.x, sel.y);
+            p = (uint32_t)__builtin_popcount(m) + p;
+        }
+        const bf_h8 a = __builtin_bit_cast(bf_h8, bt_v4i{(int)A[0], (int)A[1], (int)A[2], (int)A[3]});
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, xb[nb][j], acc[nb], 0, 0, 0);
+    }
+}
+
+// LDS layout (bytes): [selector table 128][row totals 2 x 16 x 16 ints]
+//   [partials 2 x nwaves x NB x 256 floats][nbuf staging buffers of stage_bytes]
+// Workgroup g owns blocks [g*bq + min(g, br), ...): bq or bq + 1 of them.
+template <int NB>
+__global__ __launch_bounds__(1024) void k_bt64_f16(
+        const uint64_t *__restrict__ bitmaps, const uint32_t *__restrict__ offsets,
+        const uint16_t *__restrict__ payload, uint32_t payload_bytes, int M, int K,
+        const uint16_t *__restrict__ X, int N, uint16_t *__restrict__ Y, uint32_t stage_bytes, uint32_t nbuf,
+        int bq, int br) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t bf_smem[];
+    const int nwaves = blockDim.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int r = lane & 15, q = lane >> 4;
+    const int T = (K + 63) >> 6;
+    const int gid = (int)blockIdx.x;
+    const int b_begin = gid * bq + min(gid, br);
+    const int nblk = bq + (gid < br ? 1 : 0);           // 1 .. BF_NBLK
+    const int t = wave * 4 + q;                          // this lane's tile
+
+    uint32_t *lut_lds = reinterpret_cast<uint32_t *>(bf_smem);
+    int32_t *wt = reinterpret_cast<int32_t *>(bf_smem + 128);                           // [2][16][16]
+    float *part = reinterpret_cast<float *>(wt + 2 * BF_ROWS * BF_MAX_WAVES);            // [2][nwaves][NB*256]
+    uint8_t *stage = reinterpret_cast<uint8_t *>(part + 2 * nwaves * NB * 256);
+    const uint32_t lut = bt_lds_addr(lut_lds);
+    const __amdgpu_buffer_rsrc_t prs = bt_rsrc(payload, payload_bytes);
+
+    // (1) block boundaries (wave-uniform scalar loads)
+    uint32_t eb[BF_NBLK + 1];
+#pragma unroll
+    for (int i = 0; i <= BF_NBLK; ++i) {
+        const int b = b_begin + (i < nblk ? i : nblk);
+        eb[i] = offsets[(int64_t)min(b * BF_ROWS, M) * T];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // (2) loads that need no offsets first (waiting for them then never
+    // waits for a payload DMA): the selector table, this lane's X, every
+    // block's bitmap word; after the offsets land, the payload DMA of the
+    // first nbuf blocks (16-byte granules in stream order into staging buffer
+    // i % nbuf). A block that does not fit is not staged: it reads its
+    // windows from global memory.
+    uint32_t vm_issued = 0, vm_mark[BF_NBLK];
+    uint32_t lut_word = 0;
+    if (wave == 0) {
+        const __amdgpu_buffer_rsrc_t lrs = bt_rsrc(&bf_lut_global, (uint32_t)sizeof(BfLut));
+        lut_word = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(lrs, lane < 32 ? lane * 4u : 0xFFFFFFF0u, 0, 0);
+        ++vm_issued;
+    }
+    // this lane's X: column r + 16 nb, positions 64 t .. 64 t + 63, as the
+    // B operands of the tile's 8 MFMAs (column n >= N or tile >= T: zeros)
+    bf_h8 xb[NB][8];
+    {
+        const __amdgpu_buffer_rsrc_t xrs = bt_rsrc(X, (uint32_t)N * (uint32_t)K * 2u);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const int n = r + 16 * nb;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                // positions past K read as zeros too: a finite weight of 0 times
+                // a non-finite X from the next row would give NaN
+                const uint32_t k0 = (uint32_t)t * 64u + 8u * j;
+                const uint32_t off = (n < N && t < T && k0 < (uint32_t)K) ? ((uint32_t)n * (uint32_t)K + k0) * 2u
+                                                                          : 0xFFFFFFF0u;
+                xb[nb][j] = __builtin_bit_cast(bf_h8, __builtin_amdgcn_raw_buffer_load_b128(xrs, off, 0, 0));
+            }
+        }
+        vm_issued += NB * 8;
+    }
+    const int m_first = b_begin * BF_ROWS;
+    const int wg_rows = min(nblk * BF_ROWS, M - m_first);
+    const __amdgpu_buffer_rsrc_t brs = bt_rsrc(bitmaps + (int64_t)m_first * T, (uint32_t)wg_rows * (uint32_t)T * 8u);
+    uint64_t words[BF_NBLK];
+#pragma unroll
+    for (int i = 0; i < BF_NBLK; ++i) {
+        if (i < nblk) {
+            const int rr = i * BF_ROWS + r;
+            const uint32_t off = (rr < wg_rows && t < T) ? ((uint32_t)rr * (uint32_t)T + (uint32_t)t) * 8u : 0xFFFFFFF0u;
+            words[i] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(brs, off, 0, 0));
+            ++vm_issued;
+        }
+    }
+    if (wave == 0 && lane < 32) lut_lds[lane] = lut_word;
+
+    auto fits = [&](int i) -> bool { return bf_range(eb[i], eb[i + 1]).n * 16u <= stage_bytes; };
+    auto issue_block = [&](int i) -> void {
+        if (fits(i)) {
+            const BtRange g = bf_range(eb[i], eb[i + 1]);
+            uint8_t *buf = stage + (uint32_t)(i % (int)nbuf) * stage_bytes;
+            const uint32_t n_ins = (g.n + 63u) >> 6;
+            for (uint32_t j = (uint32_t)wave; j < n_ins; j += (uint32_t)nwaves) {
+                const uint32_t u = j * 64u + (uint32_t)lane;
+                if (u < g.n)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(prs, (bt_lds_void *)(buf + j * 1024u), 16,
+                                                             (g.g0 + u) * 16u, 0, 0, 0);
+                ++vm_issued;
+            }
+        }
+        vm_mark[i] = vm_issued;
+    };
+#pragma unroll
+    for (int i = 0; i < BF_NBLK; ++i) {
+        vm_mark[i] = vm_issued;   // the words; staging the block raises it
+        if (i < nblk && i < (int)nbuf) issue_block(i);
+    }
+
+    // (4) blocks in order, one barrier each (as in the int4 kernel): before
+    // the barrier of block i each wavefront posts its row totals; after it,
+    // lane starts are known, block i-1's partials are complete and its
+    // staging buffer is free. Partials alternate between two buffers.
+    auto write_y = [&](int i) -> void {
+        const int m0 = (b_begin + i) * BF_ROWS;
+        const int rows = min(BF_ROWS, M - m0);
+        const float *pb = part + (i & 1) * nwaves * NB * 256;
+        // D layout of the 16x16 MFMAs: lane l, register k -> row 4*(l/16)+k, column l%16
+        for (int o = threadIdx.x; o < NB * 256; o += blockDim.x) {
+            const int nb = o >> 8, col = (o >> 4) & 15, rl = o & 15;
+            const int ln = (rl >> 2) * 16 + col, k = rl & 3;
+            const int n = col + 16 * nb;
+            if (n < N && rl < rows) {
+                float s = 0.f;
+                for (int w = 0; w < nwaves; ++w) s += pb[(w * NB + nb) * 256 + k * 64 + ln];
+                Y[(int64_t)n * M + m0 + rl] = __builtin_bit_cast(uint16_t, (_Float16)s);
+            }
+        }
+    };
+#pragma unroll
+    for (int i = 0; i < BF_NBLK; ++i) {
+        if (i >= nblk) break;
+        const bool in_lds = fits(i);
+        const BtRange g = bf_range(eb[i], eb[i + 1]);
+        const int rows = min(BF_ROWS, M - (b_begin + i) * BF_ROWS);
+
+        // this lane's tile popcount, inclusive prefix over q
+        const uint32_t seg = (uint32_t)__builtin_popcountll(words[i]);
+        uint32_t incl = seg;
+        {
+            const uint32_t u16 = (uint32_t)__shfl_up((int)incl, 16, 64);
+            incl += q >= 1 ? u16 : 0u;
+            const uint32_t u32 = (uint32_t)__shfl_up((int)incl, 32, 64);
+            incl += q >= 2 ? u32 : 0u;
+        }
+        int32_t *wti = wt + (i & 1) * BF_ROWS * BF_MAX_WAVES;
+        if (q == 3) wti[r * BF_MAX_WAVES + wave] = (int32_t)incl;   // this wavefront's total for row r
+
+        bt_wait_vm(vm_issued - vm_mark[i]);
+        __syncthreads();
+        if (i > 0) {
+            write_y(i - 1);
+            if (i - 1 + (int)nbuf < nblk) issue_block(i - 1 + (int)nbuf);
+        }
+
+        // lane start: rows before r, wavefronts before this one, lane groups before q
+        uint32_t pstart;
+        {
+            uint32_t row_total = 0, before_w = 0;
+            const bt_lds_v4i *tv = (const bt_lds_v4i *)(uintptr_t)bt_lds_addr(wti + r * BF_MAX_WAVES);
+#pragma unroll
+            for (int v = 0; v < BF_MAX_WAVES / 4; ++v) {
+                const bt_v4i t4 = tv[v];
+                const uint32_t tw[4] = {(uint32_t)t4.x, (uint32_t)t4.y, (uint32_t)t4.z, (uint32_t)t4.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int w = 4 * v + e;
+                    const uint32_t val = w < nwaves ? tw[e] : 0u;
+                    row_total += val;
+                    if (w < wave) before_w += val;
+                }
+            }
+            uint32_t s = row_total;
+            s += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)s, 0x111, 0xF, 0xF, true);   // row_shr:1
+            s += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)s, 0x112, 0xF, 0xF, true);   // row_shr:2
+            s += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)s, 0x114, 0xF, 0xF, true);   // row_shr:4
+            s += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)s, 0x118, 0xF, 0xF, true);   // row_shr:8
+            // element index of the lane's first nonzero, counted from the block's first granule
+            pstart = r < rows ? (eb[i] & 7u) + (s - row_total) + before_w + (incl - seg) : 0u;
+        }
+
+        bf_f4 acc[NB];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[nb] = bf_f4{0.f, 0.f, 0.f, 0.f};
+        uint32_t p = pstart;
+        if (in_lds) {
+            p = min(p, 2u * (4u * g.n - 3u));   // a corrupt stream stays inside the staged granules
+            p += bt_lds_addr(stage + (uint32_t)(i % (int)nbuf) * stage_bytes) >> 1;
+            bf_contract<NB>(words[i], p, BfWinLds{}, lut, xb, acc);
+        } else {
+            bf_contract<NB>(words[i], p, BfWinGlobal{prs, 4u * g.g0}, lut, xb, acc);
+        }
+        float *pw = part + (i & 1) * nwaves * NB * 256 + wave * NB * 256;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) pw[nb * 256 + k * 64 + lane] = acc[nb][k];
+    }
+    __syncthreads();
+    write_y(nblk - 1);
+}
+
+struct BfPlan {
+    int nwaves, nb;
+    unsigned grid;
+    int bq, br;
+    uint32_t stage_bytes, nbuf;
+    size_t lds;
+};
+
+// Fast-path constraints: one tile per lane (K <= 4096) and N <= 32.
+static bool bf_supported(int64_t K, int64_t N) {
+    return K > 0 && K % 8 == 0 && (K + 63) / 64 <= 4 * BF_MAX_WAVES && N >= 1 && N <= 32;
+}
+
+static bool bf_plan(int64_t M, int64_t K, int64_t N, int64_t payload_bytes, BfPlan *p) {
+    if (!bf_supported(K, N) || M <= 0) return false;
+    const int64_t T = (K + 63) / 64;
+    p->nwaves = (int)((T + 3) / 4);
+    p->nb = N <= 16 ? 1 : 2;
+    const int64_t blocks = (M + BF_ROWS - 1) / BF_ROWS;
+    const int64_t grid = std::max<int64_t>(std::min<int64_t>(blocks, BF_CUS), (blocks + BF_NBLK - 1) / BF_NBLK);
+    p->grid = (unsigned)grid;
+    p->bq = (int)(blocks / grid);
+    p->br = (int)(blocks % grid);
+    const int64_t per_wg = (blocks + grid - 1) / grid;
+    const int64_t wg_per_cu = (grid + BF_CUS - 1) / BF_CUS;
+    const int64_t budget = BF_LDS_MAX / wg_per_cu;
+    const int64_t avg = payload_bytes / std::max<int64_t>(blocks, 1);
+    const int64_t worst = (int64_t)BF_ROWS * T * 128 + 64;
+    int64_t stage = std::min<int64_t>(worst, avg + avg / 5 + 2048) + 32;
+    stage = (stage + 1023) / 1024 * 1024;
+    const int64_t fixed = 128 + 2 * BF_ROWS * BF_MAX_WAVES * 4 + 2 * (int64_t)p->nwaves * p->nb * 256 * 4;
+    int64_t nbuf = std::min<int64_t>((budget - fixed) / stage, per_wg);
+    if (nbuf < std::min<int64_t>(2, per_wg)) {   // see the int4 plan
+        stage = 0;
+        nbuf = 1;
+    }
+    p->stage_bytes = (uint32_t)stage;
+    p->nbuf = (uint32_t)nbuf;
+    p->lds = (size_t)(fixed + nbuf * stage);
+    return p->lds <= (size_t)budget;
+}
+
+template <int NB>
+static void launch_bf_t(const BfPlan &p, const uint64_t *bitmaps, const uint32_t *offsets, const uint16_t *payload,
+                        uint32_t payload_bytes, int M, int K, const uint16_t *X, int N, uint16_t *Y,
+                        hipStream_t stream) {
+    (void)hipFuncSetAttribute((const void *)k_bt64_f16<NB>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds);
+    hipLaunchKernelGGL((k_bt64_f16<NB>), dim3(p.grid), dim3(64 * p.nwaves), p.lds, stream, bitmaps, offsets, payload,
+                       payload_bytes, M, K, X, N, Y, p.stage_bytes, p.nbuf, p.bq, p.br);
+}
+
+static void launch_bt64_f16(const BfPlan &p, const uint64_t *bitmaps, const uint32_t *offsets,
+                            const uint16_t *payload, uint32_t payload_bytes, int M, int K, const uint16_t *X, int N,
+                            uint16_t *Y, hipStream_t stream) {
+    if (p.nb == 1)
+        launch_bf_t<1>(p, bitmaps, offsets, payload, payload_bytes, M, K, X, N, Y, stream);
+    else
+        launch_bf_t<2>(p, bitmaps, offsets, payload, payload_bytes, M, K, X, N, Y, stream);
+}

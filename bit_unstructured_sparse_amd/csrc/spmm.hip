@@ -17,6 +17,7 @@
 #include "device_common.h"
 #include "kernels_rowwave.hip"
 #include "kernels_bt64.hip"
+#include "kernels_bt64_f16.hip"
 
 namespace {
 
@@ -53,7 +54,7 @@ int launch_status() {
 bool algo_supported(int algo, int dtype, const Shape &s) {
     switch (algo) {
         case BSP_ALGO_ROWWAVE: return true;
-        case BSP_ALGO_MFMA: return dtype == BSP_INT4 && bt64_supported(s.K, s.N);
+        case BSP_ALGO_MFMA: return dtype == BSP_INT4 ? bt64_supported(s.K, s.N) : bf_supported(s.K, s.N);
         default: return false;
     }
 }
@@ -128,6 +129,17 @@ extern "C" int spmm_bitmap_f16_algo(const uint64_t *bitmaps, const uint32_t *off
     if (algo == BSP_ALGO_AUTO) algo = select_algo(BSP_FP16, s, -1);
     if (!algo_supported(algo, BSP_FP16, s)) algo = BSP_ALGO_ROWWAVE;
     switch (algo) {
+        case BSP_ALGO_MFMA: {
+            BfPlan plan;
+            if (bf_plan(M, K, N, payload_bytes, &plan)) {
+                launch_bt64_f16(plan, bitmaps, offsets, payload, (uint32_t)payload_bytes, (int)M, (int)K, X, (int)N,
+                                Y, stream);
+                break;
+            }
+            launch_rowwave_f16(bitmaps, offsets, payload, (uint32_t)payload_bytes, (int)M, (int)K, X, (int)N, Y,
+                               stream);
+            break;
+        }
         default:
         case BSP_ALGO_ROWWAVE:
             launch_rowwave_f16(bitmaps, offsets, payload, (uint32_t)payload_bytes, (int)M, (int)K,

@@ -18,7 +18,7 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 INT4_ALGOS = [bsp.ALGO_AUTO, bsp.ALGO_ROWWAVE, bsp.ALGO_MFMA]
-F16_ALGOS = [bsp.ALGO_AUTO, bsp.ALGO_ROWWAVE]
+F16_ALGOS = [bsp.ALGO_AUTO, bsp.ALGO_ROWWAVE, bsp.ALGO_MFMA]
 _NAMES = {bsp.ALGO_AUTO: "auto", bsp.ALGO_ROWWAVE: "rowwave", bsp.ALGO_VALU: "valu", bsp.ALGO_MFMA: "mfma"}
 SENTINEL = -0x21524111   # 0xDEADBEEF as int32
 F16_TOL = 1e-2
@@ -142,7 +142,9 @@ def test_w4a4_every_n(dev, algo, N):
 
 
 SMALL_F16 = [(1, 1, 1), (3, 63, 2), (65, 130, 32), (257, 1000, 1), (129, 64 * 67 + 17, 17), (64, 4096, 8),
-             (500, 64 * 20, 32)]
+             (500, 64 * 20, 32), (16, 8, 1), (33, 4088, 16), (48, 4096, 32), (20, 64 * 65, 4),
+             (5000, 256, 3),    # several 16-row blocks per workgroup
+             (4100, 64, 17)]    # ragged last block, two column blocks
 
 
 def _assert_f16(y, r):
@@ -157,6 +159,22 @@ def test_f16_small(dev, algo, M, K, N):
     p = workloads.random_fp16_problem(M + K + N, M, K, N)
     y = run_f16(p.W, p.X, algo, dev).astype(np.float64)
     _assert_f16(y, oracle.spmm_f16(oracle.encode(p.W), p.X))
+
+
+@pytest.mark.parametrize("algo", F16_ALGOS, ids=lambda a: _NAMES[a])
+@pytest.mark.parametrize("dense_block", [0, 5])
+def test_f16_uneven_block_density(dev, algo, dense_block):
+    # one dense 16-row block among sparse ones: it overflows the staging
+    # buffer sized from the average block and takes the global-window path
+    rng = np.random.default_rng(11 + dense_block)
+    M, K, N = 128, 2048, 8
+    W = rng.normal(0, 0.02, size=(M, K)).astype(np.float16)
+    keep = rng.random((M, K)) < 0.03
+    keep[16 * dense_block: 16 * dense_block + 16] = True
+    W = np.where(keep, W, np.float16(0))
+    X = rng.normal(0, 1, size=(N, K)).astype(np.float16)
+    y = run_f16(W, X, algo, dev).astype(np.float64)
+    _assert_f16(y, oracle.spmm_f16(oracle.encode(W), X))
 
 
 @pytest.mark.parametrize("algo", F16_ALGOS, ids=lambda a: _NAMES[a])

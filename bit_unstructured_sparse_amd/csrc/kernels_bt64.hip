@@ -253,7 +253,9 @@ __global__ __launch_bounds__(BT_WG_THREADS(TPL)) void k_bt64_w4a4(
         const int b = b_begin + (i < nblk ? i : nblk);
         nib[i] = offsets[(int64_t)min(b * BT_ROWS, M) * T];
     }
-    __builtin_amdgcn_sched_barrier(0);
+    // keep these loads issued here, ahead of the vector loads below (without
+    // this the compiler sinks them to their first use, behind every wait)
+    asm volatile("" ::: "memory");
 
     // (2) loads that need no offsets, so that waiting for them never waits
     // for a payload DMA: the selector table, this lane's X slices, every
@@ -303,7 +305,7 @@ __global__ __launch_bounds__(BT_WG_THREADS(TPL)) void k_bt64_w4a4(
     const __amdgpu_buffer_rsrc_t brs = bt_rsrc(bitmaps + (int64_t)m_first * T, (uint32_t)wg_rows * (uint32_t)T * 8u);
     uint64_t words[NBLK][TPL];
     // two consecutive tiles per 16-byte load (one per 8-byte load at TPL 8,
-    // where the wider form costs registers); a tile at or past T reads as 0
+    // where the wider form costs registers)
     constexpr int WPL = TPL >= 8 ? 1 : 2;   // words per load
     auto load_words = [&](int i) -> void {
         const int rr = i * BT_ROWS + r;   // row inside the workgroup's range
@@ -313,8 +315,10 @@ __global__ __launch_bounds__(BT_WG_THREADS(TPL)) void k_bt64_w4a4(
                                                               : 0xFFFFFFE0u;
             if constexpr (WPL == 2) {
                 const bt_v4i v = __builtin_bit_cast(bt_v4i, __builtin_amdgcn_raw_buffer_load_b128(brs, off, 0, 0));
+                // a tile past T is cleared where the block is decoded: a select
+                // here would wait for the load right away
                 words[i][k] = ((uint64_t)(uint32_t)v.y << 32) | (uint32_t)v.x;
-                words[i][k + 1] = t0 + k + 1 < T ? ((uint64_t)(uint32_t)v.w << 32) | (uint32_t)v.z : 0ull;
+                words[i][k + 1] = ((uint64_t)(uint32_t)v.w << 32) | (uint32_t)v.z;
             } else {
                 words[i][k] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(brs, off, 0, 0));
             }
@@ -356,6 +360,10 @@ __global__ __launch_bounds__(BT_WG_THREADS(TPL)) void k_bt64_w4a4(
                 if constexpr (NBLK > 1) asm volatile("" : "+v"(xb[nb][k][j]));
             }
 
+    // the payload DMA of the first blocks. It comes after every use of the
+    // earlier loads: a wait for one of those after a loop of DMA issues would
+    // have to wait for the DMAs too (the counter is in order, the loop's
+    // length unknown to the compiler)
     uint32_t vm_mark[NBLK];
     auto fits = [&](int i) -> bool {
         const BtRange g = bt_range(nib[i], nib[i + 1]);
@@ -407,6 +415,9 @@ __global__ __launch_bounds__(BT_WG_THREADS(TPL)) void k_bt64_w4a4(
         const bool in_lds = fits(i);
         const BtRange g = bt_range(nib[i], nib[i + 1]);
         const int rows = min(BT_ROWS, M - (b_begin + i) * BT_ROWS);
+#pragma unroll
+        for (int k = 0; k < TPL; ++k)
+            if (t0 + k >= T) words[i][k] = 0;   // tiles past the row's end
 
         // this lane's segment popcount, inclusive prefix over q (lanes r, r+16, r+32, r+48)
         uint32_t seg = 0;

@@ -12,6 +12,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <cmath>
 
 #include "bitmap_spmm.h"
 #include "device_common.h"

@@ -69,31 +69,21 @@ typedef __attribute__((address_space(3))) const bt_v4i bt_lds_v4i;
 // Selector table: entry b (a bitmap byte) is the v_perm_b32 selector pair that
 // scatters the byte's nonzeros to their positions. The perm's sources are
 // S0 = odd-rank nibbles (selector 4..7) and S1 = even-rank nibbles (0..3);
-// selector 0x0C yields a zero byte.
-struct BtLut {
-    uint32_t w[512];
-};
-
-constexpr BtLut bt_make_lut() {
-    BtLut t{};
-    for (uint32_t b = 0; b < 256; ++b) {
-        uint32_t sel[2] = {0x0C0C0C0Cu, 0x0C0C0C0Cu};
-        uint32_t rank = 0;
-        for (int p = 0; p < 8; ++p) {
-            if ((b >> p) & 1u) {
-                const uint32_t src = (rank & 1u) ? 4u + (rank >> 1) : (rank >> 1);
-                const int half = p & 1, byte = p >> 1;
-                sel[half] = (sel[half] & ~(0xFFu << (8 * byte))) | (src << (8 * byte));
-                ++rank;
-            }
-        }
-        t.w[2 * b] = sel[0];
-        t.w[2 * b + 1] = sel[1];
+// selector 0x0C yields a zero byte. Position p of the byte goes to byte p >> 1
+// of selector p & 1; its source is the rank of its nonzero among the byte's
+// set bits. Computed in registers (no table in memory to wait for).
+__device__ __forceinline__ uint2 bt_lut_entry(uint32_t b) {
+    uint32_t sel[2] = {0x0C0C0C0Cu, 0x0C0C0C0Cu};
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+        const uint32_t rank = (uint32_t)__builtin_popcount(b & ((1u << p) - 1u));
+        const uint32_t src = (rank >> 1) | ((rank & 1u) << 2);
+        const uint32_t sh = 8u * (uint32_t)(p >> 1);
+        const uint32_t upd = (sel[p & 1] & ~(0xFFu << sh)) | (src << sh);
+        sel[p & 1] = ((b >> p) & 1u) ? upd : sel[p & 1];
     }
-    return t;
+    return uint2{sel[0], sel[1]};
 }
-
-__device__ __attribute__((aligned(16))) const BtLut bt_lut_global = bt_make_lut();
 
 // LDS byte address of a pointer into dynamic shared memory.
 __device__ __forceinline__ uint32_t bt_lds_addr(const void *p) {
@@ -217,7 +207,7 @@ __device__ __forceinline__ BtRange bt_range(uint32_t nibA, uint32_t nibB) {
 }
 
 // LDS layout (bytes):
-//   [selector table copies][row totals 2 x 16 x 8 ints][sums 3 x NB x 256 ints]
+//   [selector table copies][row totals NBLK x 16 x 8 ints][sums 3 x NB x 256 ints]
 //   [nbuf staging buffers of stage_bytes]
 // Workgroup g owns blocks [g*bq + min(g, br), ...): bq or bq + 1 of them.
 template <int NB, int TPL>
@@ -240,8 +230,8 @@ __global__ __launch_bounds__(BT_WG_THREADS(TPL)) void k_bt64_w4a4(
     const uint32_t xs = (uint32_t)K >> 1;               // X row stride in bytes (K % 32 == 0 here)
 
     const uint32_t lut_base = bt_lds_addr(bt_smem) + (uint32_t)(lane % BT_LUT_COPIES) * 8u;
-    int32_t *wt = reinterpret_cast<int32_t *>(bt_smem + BT_LUT_BYTES);                  // [2][16][8]
-    int32_t *sums = wt + 2 * BT_ROWS * 8;                                                // [3][NB*256]
+    int32_t *wt = reinterpret_cast<int32_t *>(bt_smem + BT_LUT_BYTES);                  // [NBLK][16][8]
+    int32_t *sums = wt + NBLK * BT_ROWS * 8;                                             // [3][NB*256]
     uint8_t *stage = reinterpret_cast<uint8_t *>(sums + 3 * NB * 256);
     const __amdgpu_buffer_rsrc_t prs = bt_rsrc(payload, payload_bytes);
 
@@ -257,32 +247,15 @@ __global__ __launch_bounds__(BT_WG_THREADS(TPL)) void k_bt64_w4a4(
     // this the compiler sinks them to their first use, behind every wait)
     asm volatile("" ::: "memory");
 
-    // (2) loads that need no offsets, so that waiting for them never waits
-    // for a payload DMA: the selector table, this lane's X slices, every
-    // block's bitmap words. Then (after the offsets land) the payload DMA of
-    // the first nbuf blocks, each into staging buffer i % nbuf (its granules
-    // in stream order, 1 KB = 64 lanes x 16 bytes per instruction; range
-    // checks of raw buffer loads cover the per-lane offset only, so every
-    // offset is in the per-lane operand). A block that does not fit is not
-    // staged: it reads its windows from global memory.
+    // (2) loads that need no offsets: this lane's X slices and every
+    // block's bitmap words. Then the B operands are built (waiting for X
+    // only), and then, once the offsets are in, the payload DMA of the first
+    // nbuf blocks, each into staging buffer i % nbuf (its granules in stream
+    // order, 1 KB = 64 lanes x 16 bytes per instruction; range checks of raw
+    // buffer loads cover the per-lane offset only, so every offset is in the
+    // per-lane operand). A block that does not fit is not staged: it reads
+    // its windows from global memory.
     uint32_t vm_issued = 0;           // vector-memory operations issued so far by this wavefront
-    // the selector table for its 16 interleaved LDS copies: LDS slot v
-    // (8 bytes) holds entry v / 16; wavefront w fills slots 64 (w + 8 e) .. +63
-    // (consecutive addresses, so the writes cannot conflict)
-    constexpr int LUT_ROUNDS = 256 * BT_LUT_COPIES / 64 / 8;
-    uint2 lut_entry[LUT_ROUNDS];
-    {
-        const __amdgpu_buffer_rsrc_t lrs = bt_rsrc(&bt_lut_global, (uint32_t)sizeof(BtLut));
-#pragma unroll
-        for (int e = 0; e < LUT_ROUNDS; ++e) {
-            const uint32_t v = (uint32_t)((wave + 8 * e) * 64 + lane);
-            lut_entry[e] = __builtin_bit_cast(
-                    uint2, __builtin_amdgcn_raw_buffer_load_b64(lrs, wave < 8 ? (v / BT_LUT_COPIES) * 8u : 0xFFFFFFF0u,
-                                                                0, 0));
-        }
-        vm_issued += LUT_ROUNDS;
-    }
-
     // this lane's X slices, once for all blocks (column n >= N or tile >= T: zeros)
     uint32_t xw[NB][TPL][8];
     {
@@ -325,28 +298,15 @@ __global__ __launch_bounds__(BT_WG_THREADS(TPL)) void k_bt64_w4a4(
         }
     };
 
+    // every block slot is loaded, used or not (a slot past nblk reads
+    // zeros): the compiler can then count the loads still in flight
 #pragma unroll
-    for (int i = 0; i < NBLK; ++i)
-        if (i < nblk) {
-            load_words(i);
-            vm_issued += TPL / WPL;
-        }
+    for (int i = 0; i < NBLK; ++i) {
+        load_words(i);
+        vm_issued += TPL / WPL;
+    }
     // zero the sum buffers (first added to after the first block's barrier)
     for (int o = threadIdx.x; o < 3 * NB * 256; o += blockDim.x) sums[o] = 0;
-    {
-        __attribute__((address_space(3))) uint64_t *lut_lds =
-                (__attribute__((address_space(3))) uint64_t *)(uintptr_t)bt_lds_addr(bt_smem);
-        if (wave < 8) {
-#pragma unroll
-            for (int e = 0; e < LUT_ROUNDS; ++e)
-                lut_lds[(wave + 8 * e) * 64 + lane] = ((uint64_t)lut_entry[e].y << 32) | lut_entry[e].x;
-        }
-        if (nwaves < 8) {   // small workgroups: the remaining slots, straight from the table
-            const uint64_t *tab = reinterpret_cast<const uint64_t *>(&bt_lut_global);
-            for (int v = nwaves * 64 + (int)threadIdx.x; v < 256 * BT_LUT_COPIES; v += (int)blockDim.x)
-                if ((v / 64) % 8 >= nwaves) lut_lds[v] = tab[v / BT_LUT_COPIES];
-        }
-    }
     // B operands of this lane's tiles, in the even/odd x16 order of the decode;
     // pinned so that they are built once, not rebuilt in every block
     bt_v4i xb[NB][TPL][4];
@@ -359,6 +319,26 @@ __global__ __launch_bounds__(BT_WG_THREADS(TPL)) void k_bt64_w4a4(
                 xb[nb][k][j] = bt_b_operand(xw[nb][k][2 * j], xw[nb][k][2 * j + 1]);
                 if constexpr (NBLK > 1) asm volatile("" : "+v"(xb[nb][k][j]));
             }
+
+    // every block's segment popcounts (inclusive prefix over the lane groups
+    // q of a row: lanes r, r+16, r+32, r+48) and this wavefront's row totals
+    uint32_t seg[NBLK], incl[NBLK];
+#pragma unroll
+    for (int i = 0; i < NBLK; ++i) {
+#pragma unroll
+        for (int k = 0; k < TPL; ++k)
+            if (t0 + k >= T) words[i][k] = 0;   // tiles past the row's end
+        seg[i] = 0;
+#pragma unroll
+        for (int k = 0; k < TPL; ++k) seg[i] += (uint32_t)__builtin_popcountll(words[i][k]);
+        uint32_t c = seg[i];
+        const uint32_t u16 = (uint32_t)__shfl_up((int)c, 16, 64);
+        c += q >= 1 ? u16 : 0u;
+        const uint32_t u32 = (uint32_t)__shfl_up((int)c, 32, 64);
+        c += q >= 2 ? u32 : 0u;
+        incl[i] = c;
+        if (q == 3) wt[(i * BT_ROWS + r) * 8 + wave] = (int32_t)c;   // this wavefront's total for row r
+    }
 
     // the payload DMA of the first blocks. It comes after every use of the
     // earlier loads: a wait for one of those after a loop of DMA issues would
@@ -390,10 +370,26 @@ __global__ __launch_bounds__(BT_WG_THREADS(TPL)) void k_bt64_w4a4(
         if (i < nblk && i < (int)nbuf) issue_block(i);
     }
 
-    // (5) blocks in order, one barrier each. Before the barrier of block i
-    // each wavefront posts its row totals for block i; after it, each lane
-    // knows its start, Y of block i-1 is complete (every wavefront's partial
-    // is in) and staging buffer (i-1) % nbuf is free for the next payload.
+    // the selector table's copies, computed while the payload is in flight:
+    // entry b of copy c at LDS slot 16 b + c (8 bytes); item v covers entry
+    // v % 256, copies 8 (v / 256) .. +7, written in an order rotated by v so
+    // that neighbouring lanes hit different banks
+    {
+        __attribute__((address_space(3))) uint64_t *lut_lds =
+                (__attribute__((address_space(3))) uint64_t *)(uintptr_t)bt_lds_addr(bt_smem);
+        for (uint32_t v = threadIdx.x; v < 256u * BT_LUT_COPIES / 8u; v += blockDim.x) {
+            const uint32_t b = v & 255u, c0 = 8u * (v >> 8);
+            const uint2 e = bt_lut_entry(b);
+            const uint64_t e64 = ((uint64_t)e.y << 32) | e.x;
+#pragma unroll
+            for (uint32_t k = 0; k < 8; ++k) lut_lds[b * BT_LUT_COPIES + c0 + ((k + v) & 7u)] = e64;
+        }
+    }
+
+    // (5) blocks in order, one barrier each. After the barrier of block i
+    // each lane can take its start from the row totals posted above, Y of
+    // block i-1 is complete (every wavefront's partial is in) and staging
+    // buffer (i-1) % nbuf is free for the next payload.
     // Sums rotate over three buffers: block i adds into i % 3 after barrier
     // i, block i-1's are read after barrier i, and i+1 % 3 (last read before
     // barrier i) is cleared after barrier i for block i+1.
@@ -415,24 +411,7 @@ __global__ __launch_bounds__(BT_WG_THREADS(TPL)) void k_bt64_w4a4(
         const bool in_lds = fits(i);
         const BtRange g = bt_range(nib[i], nib[i + 1]);
         const int rows = min(BT_ROWS, M - (b_begin + i) * BT_ROWS);
-#pragma unroll
-        for (int k = 0; k < TPL; ++k)
-            if (t0 + k >= T) words[i][k] = 0;   // tiles past the row's end
-
-        // this lane's segment popcount, inclusive prefix over q (lanes r, r+16, r+32, r+48)
-        uint32_t seg = 0;
-#pragma unroll
-        for (int k = 0; k < TPL; ++k) seg += (uint32_t)__builtin_popcountll(words[i][k]);
-        uint32_t incl = seg;
-        {
-            const uint32_t u16 = (uint32_t)__shfl_up((int)incl, 16, 64);
-            incl += q >= 1 ? u16 : 0u;
-            const uint32_t u32 = (uint32_t)__shfl_up((int)incl, 32, 64);
-            incl += q >= 2 ? u32 : 0u;
-        }
-        int32_t *wti = wt + (i & 1) * BT_ROWS * 8;
-        if (q == 3) wti[r * 8 + wave] = (int32_t)incl;   // this wavefront's total for row r
-
+        const int32_t *wti = wt + i * BT_ROWS * 8;
         bt_wait_vm(vm_issued - vm_mark[i]);   // this wavefront's share of block i landed
         __syncthreads();                      // ... everyone's; block i-1 is decoded and summed
         if (i > 0) {
@@ -463,7 +442,7 @@ __global__ __launch_bounds__(BT_WG_THREADS(TPL)) void k_bt64_w4a4(
             s += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)s, 0x114, 0xF, 0xF, true);   // row_shr:4
             s += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)s, 0x118, 0xF, 0xF, true);   // row_shr:8
             // nibble index of the lane's first nonzero, counted from the block's first granule
-            pstart = r < rows ? (nib[i] & 31u) + (s - row_total) + before_w + (incl - seg) : 0u;
+            pstart = r < rows ? (nib[i] & 31u) + (s - row_total) + before_w + (incl[i] - seg[i]) : 0u;
         }
 
         bt_v4i acc[NB];
@@ -528,7 +507,7 @@ static bool bt64_plan(int64_t M, int64_t K, int64_t N, int64_t payload_bytes, Bt
     const int64_t worst = (int64_t)BT_ROWS * T * 32 + 64;
     int64_t stage = std::min<int64_t>(worst, avg + avg / 5 + 2048) + 32;
     stage = (stage + 1023) / 1024 * 1024;
-    const int64_t fixed = BT_LUT_BYTES + 2 * BT_ROWS * 8 * 4 + 3 * p->nb * 256 * 4;
+    const int64_t fixed = BT_LUT_BYTES + nblk_max * BT_ROWS * 8 * 4 + 3 * p->nb * 256 * 4;
     int64_t nbuf = (budget - fixed) / stage;
     nbuf = std::min(nbuf, per_wg);
     // a buffer is refilled one block after it was decoded, so a ring of one

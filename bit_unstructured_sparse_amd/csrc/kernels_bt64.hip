@@ -48,7 +48,6 @@
 // overflow under the API's K bound.
 
 #define BT_ROWS 16                      // rows per block (MFMA A rows)
-#define BT_MAX_WAVES 8
 #define BT_LUT_COPIES 16               // selector-table copies in LDS (lane l reads copy l % 16)
 #define BT_LUT_BYTES (2048 * BT_LUT_COPIES)   // 256 entries x 8 bytes per copy
 #define BT_LDS_MAX (160 * 1024)
@@ -217,6 +216,7 @@ __global__ __launch_bounds__(BT_WG_THREADS(TPL)) void k_bt64_w4a4(
         const uint8_t *__restrict__ X, int N, int32_t *__restrict__ Y, uint32_t stage_bytes, uint32_t nbuf,
         int bq, int br) {
     constexpr int NBLK = BT_NBLK(TPL);
+    constexpr int WC = BT_WG_THREADS(TPL) / 64;          // row-total columns: wavefronts, at most
     extern __shared__ __attribute__((aligned(16))) uint8_t bt_smem[];
     const int nwaves = blockDim.x >> 6;
     // the wavefront index is uniform: keep it (and the loops over it) scalar
@@ -231,7 +231,7 @@ __global__ __launch_bounds__(BT_WG_THREADS(TPL)) void k_bt64_w4a4(
 
     const uint32_t lut_base = bt_lds_addr(bt_smem) + (uint32_t)(lane % BT_LUT_COPIES) * 8u;
     int32_t *wt = reinterpret_cast<int32_t *>(bt_smem + BT_LUT_BYTES);                  // [NBLK][16][8]
-    int32_t *sums = wt + NBLK * BT_ROWS * 8;                                             // [3][NB*256]
+    int32_t *sums = wt + NBLK * BT_ROWS * WC;                                            // [3][NB*256]
     uint8_t *stage = reinterpret_cast<uint8_t *>(sums + 3 * NB * 256);
     const __amdgpu_buffer_rsrc_t prs = bt_rsrc(payload, payload_bytes);
 
@@ -279,7 +279,7 @@ __global__ __launch_bounds__(BT_WG_THREADS(TPL)) void k_bt64_w4a4(
     uint64_t words[NBLK][TPL];
     // two consecutive tiles per 16-byte load (one per 8-byte load at TPL 8,
     // where the wider form costs registers)
-    constexpr int WPL = TPL >= 8 ? 1 : 2;   // words per load
+    constexpr int WPL = (TPL == 1 || TPL >= 8) ? 1 : 2;   // words per load
     auto load_words = [&](int i) -> void {
         const int rr = i * BT_ROWS + r;   // row inside the workgroup's range
 #pragma unroll
@@ -337,7 +337,7 @@ __global__ __launch_bounds__(BT_WG_THREADS(TPL)) void k_bt64_w4a4(
         const uint32_t u32 = (uint32_t)__shfl_up((int)c, 32, 64);
         c += q >= 2 ? u32 : 0u;
         incl[i] = c;
-        if (q == 3) wt[(i * BT_ROWS + r) * 8 + wave] = (int32_t)c;   // this wavefront's total for row r
+        if (q == 3) wt[(i * BT_ROWS + r) * WC + wave] = (int32_t)c;   // this wavefront's total for row r
     }
 
     // the payload DMA of the first blocks. It comes after every use of the
@@ -411,7 +411,7 @@ __global__ __launch_bounds__(BT_WG_THREADS(TPL)) void k_bt64_w4a4(
         const bool in_lds = fits(i);
         const BtRange g = bt_range(nib[i], nib[i + 1]);
         const int rows = min(BT_ROWS, M - (b_begin + i) * BT_ROWS);
-        const int32_t *wti = wt + i * BT_ROWS * 8;
+        const int32_t *wti = wt + i * BT_ROWS * WC;
         bt_wait_vm(vm_issued - vm_mark[i]);   // this wavefront's share of block i landed
         __syncthreads();                      // ... everyone's; block i-1 is decoded and summed
         if (i > 0) {
@@ -424,16 +424,18 @@ __global__ __launch_bounds__(BT_WG_THREADS(TPL)) void k_bt64_w4a4(
         // lane start: rows before r, wavefronts before this one, lane groups before q
         uint32_t pstart;
         {
-            const bt_v4i t_lo = *(bt_lds_v4i *)(uintptr_t)bt_lds_addr(wti + r * 8);
-            const bt_v4i t_hi = *(bt_lds_v4i *)(uintptr_t)bt_lds_addr(wti + r * 8 + 4);
-            const uint32_t t[8] = {(uint32_t)t_lo.x, (uint32_t)t_lo.y, (uint32_t)t_lo.z, (uint32_t)t_lo.w,
-                                   (uint32_t)t_hi.x, (uint32_t)t_hi.y, (uint32_t)t_hi.z, (uint32_t)t_hi.w};
             uint32_t row_total = 0, before_w = 0;
 #pragma unroll
-            for (int w = 0; w < 8; ++w) {
-                const uint32_t v = w < nwaves ? t[w] : 0u;
-                row_total += v;
-                if (w < wave) before_w += v;   // wave-uniform condition
+            for (int w4 = 0; w4 < WC; w4 += 4) {
+                const bt_v4i t4 = *(bt_lds_v4i *)(uintptr_t)bt_lds_addr(wti + r * WC + w4);
+                const uint32_t t[4] = {(uint32_t)t4.x, (uint32_t)t4.y, (uint32_t)t4.z, (uint32_t)t4.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int w = w4 + e;
+                    const uint32_t v = w < nwaves ? t[e] : 0u;
+                    row_total += v;
+                    if (w < wave) before_w += v;   // wave-uniform condition
+                }
             }
             // exclusive prefix of row totals over r inside each 16-lane DPP row
             uint32_t s = row_total;
@@ -507,7 +509,7 @@ static bool bt64_plan(int64_t M, int64_t K, int64_t N, int64_t payload_bytes, Bt
     const int64_t worst = (int64_t)BT_ROWS * T * 32 + 64;
     int64_t stage = std::min<int64_t>(worst, avg + avg / 5 + 2048) + 32;
     stage = (stage + 1023) / 1024 * 1024;
-    const int64_t fixed = BT_LUT_BYTES + nblk_max * BT_ROWS * 8 * 4 + 3 * p->nb * 256 * 4;
+    const int64_t fixed = BT_LUT_BYTES + nblk_max * BT_ROWS * (BT_WG_THREADS(p->tpl) / 64) * 4 + 3 * p->nb * 256 * 4;
     int64_t nbuf = (budget - fixed) / stage;
     nbuf = std::min(nbuf, per_wg);
     // a buffer is refilled one block after it was decoded, so a ring of one
@@ -539,9 +541,11 @@ static void launch_bt64_w4a4(const BtPlan &p, const uint64_t *bitmaps, const uin
                              int32_t *Y, hipStream_t stream) {
 #define BT_LAUNCH(NB, TPL) launch_bt64_t<NB, TPL>(p, bitmaps, offsets, payload, payload_bytes, M, K, X, N, Y, stream)
     if (p.nb == 1) {
-        if (p.tpl == 2) BT_LAUNCH(1, 2); else if (p.tpl == 4) BT_LAUNCH(1, 4); else BT_LAUNCH(1, 8);
+        if (p.tpl == 1) BT_LAUNCH(1, 1); else if (p.tpl == 2) BT_LAUNCH(1, 2);
+        else if (p.tpl == 4) BT_LAUNCH(1, 4); else BT_LAUNCH(1, 8);
     } else {
-        if (p.tpl == 2) BT_LAUNCH(2, 2); else if (p.tpl == 4) BT_LAUNCH(2, 4); else BT_LAUNCH(2, 8);
+        if (p.tpl == 1) BT_LAUNCH(2, 1); else if (p.tpl == 2) BT_LAUNCH(2, 2);
+        else if (p.tpl == 4) BT_LAUNCH(2, 4); else BT_LAUNCH(2, 8);
     }
 #undef BT_LAUNCH
 }

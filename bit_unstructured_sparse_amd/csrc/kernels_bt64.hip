@@ -214,7 +214,7 @@ __global__ __launch_bounds__(BT_WG_THREADS(TPL)) void k_bt64_w4a4(
         const uint64_t *__restrict__ bitmaps, const uint32_t *__restrict__ offsets,
         const uint8_t *__restrict__ payload, uint32_t payload_bytes, int M, int K,
         const uint8_t *__restrict__ X, int N, int32_t *__restrict__ Y, uint32_t stage_bytes, uint32_t nbuf,
-        int bq, int br) {
+        int bq, int br, int one_pass) {
     constexpr int NBLK = BT_NBLK(TPL);
     constexpr int WC = BT_WG_THREADS(TPL) / 64;          // row-total columns: wavefronts, at most
     extern __shared__ __attribute__((aligned(16))) uint8_t bt_smem[];
@@ -234,6 +234,12 @@ __global__ __launch_bounds__(BT_WG_THREADS(TPL)) void k_bt64_w4a4(
     int32_t *sums = wt + NBLK * BT_ROWS * WC;                                            // [3][NB*256]
     uint8_t *stage = reinterpret_cast<uint8_t *>(sums + 3 * NB * 256);
     const __amdgpu_buffer_rsrc_t prs = bt_rsrc(payload, payload_bytes);
+
+    // every kernel argument into SGPRs now, in the first batch of argument
+    // loads: one loaded after the boundary offsets below would make its first
+    // use wait for those too (scalar loads complete out of order)
+    asm volatile("" ::"s"(bitmaps), "s"(payload), "s"(X), "s"(Y), "s"(N), "s"(stage_bytes), "s"(nbuf),
+                 "s"(payload_bytes));
 
     // (1) block boundaries (wave-uniform scalar loads), before anything else:
     // the payload DMA waits for them
@@ -405,22 +411,12 @@ __global__ __launch_bounds__(BT_WG_THREADS(TPL)) void k_bt64_w4a4(
             if (n < N && rl < rows) Y[(int64_t)n * M + m0 + rl] = s[(nb * 4 + k) * 64 + ln];
         }
     };
-#pragma unroll
-    for (int i = 0; i < NBLK; ++i) {
-        if (i >= nblk) break;
+    // decode + contract block i into acc (after its barrier)
+    auto decode_block = [&](int i, bt_v4i (&acc)[NB]) -> void {
         const bool in_lds = fits(i);
         const BtRange g = bt_range(nib[i], nib[i + 1]);
         const int rows = min(BT_ROWS, M - (b_begin + i) * BT_ROWS);
         const int32_t *wti = wt + i * BT_ROWS * WC;
-        bt_wait_vm(vm_issued - vm_mark[i]);   // this wavefront's share of block i landed
-        __syncthreads();                      // ... everyone's; block i-1 is decoded and summed
-        if (i > 0) {
-            write_y(i - 1);
-            if (i - 1 + (int)nbuf < nblk) issue_block(i - 1 + (int)nbuf);
-        }
-        if (i >= 2)
-            for (int o = threadIdx.x; o < NB * 256; o += blockDim.x) sums[((i + 1) % 3) * NB * 256 + o] = 0;
-
         // lane start: rows before r, wavefronts before this one, lane groups before q
         uint32_t pstart;
         {
@@ -438,16 +434,14 @@ __global__ __launch_bounds__(BT_WG_THREADS(TPL)) void k_bt64_w4a4(
                 }
             }
             // exclusive prefix of row totals over r inside each 16-lane DPP row
-            uint32_t s = row_total;
-            s += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)s, 0x111, 0xF, 0xF, true);   // row_shr:1
-            s += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)s, 0x112, 0xF, 0xF, true);   // row_shr:2
-            s += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)s, 0x114, 0xF, 0xF, true);   // row_shr:4
-            s += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)s, 0x118, 0xF, 0xF, true);   // row_shr:8
+            uint32_t sc = row_total;
+            sc += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)sc, 0x111, 0xF, 0xF, true);   // row_shr:1
+            sc += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)sc, 0x112, 0xF, 0xF, true);   // row_shr:2
+            sc += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)sc, 0x114, 0xF, 0xF, true);   // row_shr:4
+            sc += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)sc, 0x118, 0xF, 0xF, true);   // row_shr:8
             // nibble index of the lane's first nonzero, counted from the block's first granule
-            pstart = r < rows ? (nib[i] & 31u) + (s - row_total) + before_w + (incl[i] - seg[i]) : 0u;
+            pstart = r < rows ? (nib[i] & 31u) + (sc - row_total) + before_w + (incl[i] - seg[i]) : 0u;
         }
-
-        bt_v4i acc[NB];
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) acc[nb] = bt_v4i{0, 0, 0, 0};
         uint32_t p = pstart;
@@ -460,12 +454,61 @@ __global__ __launch_bounds__(BT_WG_THREADS(TPL)) void k_bt64_w4a4(
         } else {
             bt_contract<NB, TPL>(words[i], p, BtWinGlobal{prs, 4u * g.g0}, lut_base, xb, acc);
         }
+    };
+
+    if (NBLK > 1 && one_pass) {
+        // every block is staged at once: one barrier for all of them, each
+        // wavefront's partials to its own LDS slice, one barrier, then Y
+        int32_t *part = reinterpret_cast<int32_t *>(stage + nbuf * stage_bytes);   // [nblk][nwaves][NB*256]
+        bt_wait_vm(0);
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < NBLK; ++i) {
+            if (i >= nblk) break;
+            bt_v4i acc[NB];
+            decode_block(i, acc);
+            int32_t *pw = part + (i * nwaves + wave) * NB * 256;
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int k = 0; k < 4; ++k) pw[nb * 256 + k * 64 + lane] = acc[nb][k] >> 8;
+        }
+        __syncthreads();
+        for (int o = threadIdx.x; o < nblk * NB * 256; o += blockDim.x) {
+            const int i = o / (NB * 256), oo = o % (NB * 256);
+            const int nb = oo >> 8, col = (oo >> 4) & 15, rl = oo & 15;
+            const int ln = (rl >> 2) * 16 + col, k = rl & 3;
+            const int n = col + 16 * nb;
+            const int m0 = (b_begin + i) * BT_ROWS;
+            if (n < N && rl < min(BT_ROWS, M - m0)) {
+                const int32_t *pb = part + i * nwaves * NB * 256 + nb * 256 + k * 64 + ln;
+                int32_t v = 0;
+                for (int w = 0; w < nwaves; ++w) v += pb[w * NB * 256];
+                Y[(int64_t)n * M + m0 + rl] = v;
+            }
+        }
+        return;
+    }
+
+#pragma unroll
+    for (int i = 0; i < NBLK; ++i) {
+        if (i >= nblk) break;
+        bt_wait_vm(vm_issued - vm_mark[i]);   // this wavefront's share of block i landed
+        __syncthreads();                      // ... everyone's; block i-1 is decoded and summed
+        if (i > 0) {
+            write_y(i - 1);
+            if (i - 1 + (int)nbuf < nblk) issue_block(i - 1 + (int)nbuf);
+        }
+        if (i >= 2)
+            for (int o = threadIdx.x; o < NB * 256; o += blockDim.x) sums[((i + 1) % 3) * NB * 256 + o] = 0;
+        bt_v4i acc[NB];
+        decode_block(i, acc);
         // the wavefronts' partials (each exact after >> 8) meet in LDS
-        int32_t *s = sums + (i % 3) * NB * 256;
+        int32_t *sp = sums + (i % 3) * NB * 256;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-            for (int k = 0; k < 4; ++k) atomicAdd(&s[(nb * 4 + k) * 64 + lane], acc[nb][k] >> 8);
+            for (int k = 0; k < 4; ++k) atomicAdd(&sp[(nb * 4 + k) * 64 + lane], acc[nb][k] >> 8);
     }
     __syncthreads();
     write_y(nblk - 1);
@@ -478,6 +521,7 @@ struct BtPlan {
     int bq, br;             // blocks per workgroup: bq, plus one for the first br workgroups
     uint32_t stage_bytes;   // one staging buffer
     uint32_t nbuf;          // staging buffers in the ring
+    int one_pass;           // every block staged at once: one barrier before and one after the decode
     size_t lds;             // total dynamic LDS
 };
 
@@ -520,9 +564,13 @@ static bool bt64_plan(int64_t M, int64_t K, int64_t N, int64_t payload_bytes, Bt
         stage = 0;
         nbuf = 1;
     }
+    // all of a workgroup's blocks staged at once, with room for per-wavefront
+    // partials: decode without a barrier between blocks
+    const int64_t part = per_wg * p->nwaves * p->nb * 256 * 4;
+    p->one_pass = nblk_max > 1 && (stage == 0 || nbuf >= per_wg) && fixed + nbuf * stage + part <= budget;
     p->stage_bytes = (uint32_t)stage;
     p->nbuf = (uint32_t)nbuf;
-    p->lds = (size_t)(fixed + nbuf * stage);
+    p->lds = (size_t)(fixed + nbuf * stage + (p->one_pass ? part : 0));
     return true;
 }
 
@@ -533,7 +581,7 @@ static void launch_bt64_t(const BtPlan &p, const uint64_t *bitmaps, const uint32
     (void)hipFuncSetAttribute((const void *)k_bt64_w4a4<NB, TPL>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               (int)p.lds);
     hipLaunchKernelGGL((k_bt64_w4a4<NB, TPL>), dim3(p.grid), dim3(64 * p.nwaves), p.lds, stream, bitmaps, offsets,
-                       payload, payload_bytes, M, K, X, N, Y, p.stage_bytes, p.nbuf, p.bq, p.br);
+                       payload, payload_bytes, M, K, X, N, Y, p.stage_bytes, p.nbuf, p.bq, p.br, p.one_pass);
 }
 
 static void launch_bt64_w4a4(const BtPlan &p, const uint64_t *bitmaps, const uint32_t *offsets,

@@ -40,31 +40,8 @@ typedef float bf_f4 __attribute__((ext_vector_type(4)));
 // Selector table: entry m (a 4-bit group of the word) is the v_perm_b32
 // selector pair for output dwords {positions 0,1} and {positions 2,3}; the
 // perm's sources are S0 = window halves 2,3 (selector bytes 4..7) and
-// S1 = window halves 0,1 (0..3), and selector 0x0C yields a zero byte.
-struct BfLut {
-    uint32_t w[32];
-};
-
-constexpr BfLut bf_make_lut() {
-    BfLut t{};
-    for (uint32_t m = 0; m < 16; ++m) {
-        uint32_t sel[2] = {0x0C0C0C0Cu, 0x0C0C0C0Cu};
-        uint32_t rank = 0;
-        for (int pos = 0; pos < 4; ++pos) {
-            if ((m >> pos) & 1u) {
-                const uint32_t lo = 2u * rank, hi = 2u * rank + 1u;   // bytes of half `rank`
-                const int d = pos >> 1, sh = 16 * (pos & 1);
-                sel[d] = (sel[d] & ~(0xFFFFu << sh)) | ((lo | (hi << 8)) << sh);
-                ++rank;
-            }
-        }
-        t.w[2 * m] = sel[0];
-        t.w[2 * m + 1] = sel[1];
-    }
-    return t;
-}
-
-__device__ __attribute__((aligned(16))) const BfLut bf_lut_global = bf_make_lut();
+// S1 = window halves 0,1 (0..3), and selector 0x0C yields a zero byte. Built
+// in LDS by the kernel itself.
 
 // Payload range of a block in 16-byte granules: [g0, g0 + n) covers halves
 // [eA, eB) plus one granule for the windows that read past the last value.
@@ -148,6 +125,11 @@ __global__ __launch_bounds__(1024) void k_bt64_f16(
     const uint32_t lut = bt_lds_addr(lut_lds);
     const __amdgpu_buffer_rsrc_t prs = bt_rsrc(payload, payload_bytes);
 
+    // every kernel argument into SGPRs in the first batch of argument loads
+    // (one loaded after the offsets below would wait for those too)
+    asm volatile("" ::"s"(bitmaps), "s"(payload), "s"(X), "s"(Y), "s"(N), "s"(stage_bytes), "s"(nbuf),
+                 "s"(payload_bytes));
+
     // (1) block boundaries (wave-uniform scalar loads)
     uint32_t eb[BF_NBLK + 1];
 #pragma unroll
@@ -155,7 +137,9 @@ __global__ __launch_bounds__(1024) void k_bt64_f16(
         const int b = b_begin + (i < nblk ? i : nblk);
         eb[i] = offsets[(int64_t)min(b * BF_ROWS, M) * T];
     }
-    __builtin_amdgcn_sched_barrier(0);
+    // keep these loads issued here, ahead of the vector loads (the compiler
+    // would otherwise sink them to their first use, behind every wait)
+    asm volatile("" ::: "memory");
 
     // (2) loads that need no offsets first (waiting for them then never
     // waits for a payload DMA): the selector table, this lane's X, every
@@ -164,12 +148,6 @@ __global__ __launch_bounds__(1024) void k_bt64_f16(
     // i % nbuf). A block that does not fit is not staged: it reads its
     // windows from global memory.
     uint32_t vm_issued = 0, vm_mark[BF_NBLK];
-    uint32_t lut_word = 0;
-    if (wave == 0) {
-        const __amdgpu_buffer_rsrc_t lrs = bt_rsrc(&bf_lut_global, (uint32_t)sizeof(BfLut));
-        lut_word = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(lrs, lane < 32 ? lane * 4u : 0xFFFFFFF0u, 0, 0);
-        ++vm_issued;
-    }
     // this lane's X: column r + 16 nb, positions 64 t .. 64 t + 63, as the
     // B operands of the tile's 8 MFMAs (column n >= N or tile >= T: zeros)
     bf_h8 xb[NB][8];
@@ -196,14 +174,27 @@ __global__ __launch_bounds__(1024) void k_bt64_f16(
     uint64_t words[BF_NBLK];
 #pragma unroll
     for (int i = 0; i < BF_NBLK; ++i) {
-        if (i < nblk) {
-            const int rr = i * BF_ROWS + r;
-            const uint32_t off = (rr < wg_rows && t < T) ? ((uint32_t)rr * (uint32_t)T + (uint32_t)t) * 8u : 0xFFFFFFF0u;
-            words[i] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(brs, off, 0, 0));
-            ++vm_issued;
-        }
+        // every slot is loaded (past nblk: zeros), so the loads in flight can be counted
+        const int rr = i * BF_ROWS + r;
+        const uint32_t off = (rr < wg_rows && t < T) ? ((uint32_t)rr * (uint32_t)T + (uint32_t)t) * 8u : 0xFFFFFFF0u;
+        words[i] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(brs, off, 0, 0));
+        ++vm_issued;
     }
-    if (wave == 0 && lane < 32) lut_lds[lane] = lut_word;
+    // the 16-entry selector table, computed in registers (lane m: entry m)
+    if (threadIdx.x < 16) {
+        const uint32_t m = threadIdx.x;
+        uint32_t sel[2] = {0x0C0C0C0Cu, 0x0C0C0C0Cu};
+#pragma unroll
+        for (int pos = 0; pos < 4; ++pos) {
+            const uint32_t rank = (uint32_t)__builtin_popcount(m & ((1u << pos) - 1u));
+            const uint32_t v = (2u * rank) | ((2u * rank + 1u) << 8);   // bytes of half `rank`
+            const uint32_t sh = 16u * (uint32_t)(pos & 1);
+            const uint32_t upd = (sel[pos >> 1] & ~(0xFFFFu << sh)) | (v << sh);
+            sel[pos >> 1] = ((m >> pos) & 1u) ? upd : sel[pos >> 1];
+        }
+        lut_lds[2 * m] = sel[0];
+        lut_lds[2 * m + 1] = sel[1];
+    }
 
     auto fits = [&](int i) -> bool { return bf_range(eb[i], eb[i + 1]).n * 16u <= stage_bytes; };
     auto issue_block = [&](int i) -> void {

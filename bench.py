@@ -194,10 +194,10 @@ def summarize_traffic(out, fetch, write, copy_fetch, copy_write, fragment, heade
     cf = _counter_per_kernel(copy_fetch, "FETCH_SIZE")
     cw = _counter_per_kernel(copy_write, "WRITE_SIZE")
     kf, kw = _pick(f_k, fragment), _pick(w_k, fragment)
-    ck = _pick(cf, "elementwise")
+    ck = _pick(cf, "bitwise_not")
     # counters read KiB per dispatch; the copy reads and writes COPY_BYTES
     fetch_factor = COPY_BYTES / (cf[ck][0] * 1024.0)
-    write_factor = COPY_BYTES / (cw[_pick(cw, "elementwise")][0] * 1024.0)
+    write_factor = COPY_BYTES / (cw[_pick(cw, "bitwise_not")][0] * 1024.0)
     fetch_b = f_k[kf][0] * 1024.0 * fetch_factor
     write_b = w_k[kw][0] * 1024.0 * write_factor
     lines = [f"# {h}" for h in header] + [
@@ -207,7 +207,7 @@ def summarize_traffic(out, fetch, write, copy_fetch, copy_write, fragment, heade
         f"write_kib_per_dispatch: {w_k[kw][0]:.1f}",
         f"copy_kernel: {ck}",
         f"copy_fetch_kib_per_dispatch: {cf[ck][0]:.1f}  (copy of {COPY_BYTES} bytes)",
-        f"copy_write_kib_per_dispatch: {cw[_pick(cw, 'elementwise')][0]:.1f}",
+        f"copy_write_kib_per_dispatch: {cw[_pick(cw, 'bitwise_not')][0]:.1f}",
         f"fetch_factor: {fetch_factor:.4f}",
         f"write_factor: {write_factor:.4f}",
         f"traffic_bytes_per_launch: {fetch_b + write_b:.0f}",
@@ -241,7 +241,13 @@ def copy_calibration():
     dst = torch.empty_like(src)
     for _ in range(5):
         torch.bitwise_not(src, out=dst)
+    # a read-only pass of the same bytes (a reduction): the fetch counter's
+    # factor for a kernel that streams loads without stores
+    total = None
+    for _ in range(5):
+        total = torch.sum(src, dtype=torch.int64)
     torch.cuda.synchronize()
+    assert int(total.item()) == n * (n - 1) // 2
     ok = bool(torch.equal(dst[:1024], ~src[:1024]))
     print(json.dumps({"copy_calibration_bytes": COPY_BYTES, "dispatches": 5, "ok": ok}), flush=True)
 

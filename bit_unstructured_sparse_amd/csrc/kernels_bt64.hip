@@ -210,11 +210,12 @@ __device__ __forceinline__ BtRange bt_range(uint32_t nibA, uint32_t nibB) {
 //   [nbuf staging buffers of stage_bytes]
 // Workgroup g owns blocks [g*bq + min(g, br), ...): bq or bq + 1 of them.
 template <int NB, int TPL>
+// (The arguments the first loads need come first: they are the ones a
+// kernel-argument preload would place in registers.)
 __global__ __launch_bounds__(BT_WG_THREADS(TPL)) void k_bt64_w4a4(
-        const uint64_t *__restrict__ bitmaps, const uint32_t *__restrict__ offsets,
-        const uint8_t *__restrict__ payload, uint32_t payload_bytes, int M, int K,
-        const uint8_t *__restrict__ X, int N, int32_t *__restrict__ Y, uint32_t stage_bytes, uint32_t nbuf,
-        int bq, int br, int one_pass) {
+        const uint32_t *__restrict__ offsets, int M, int K, int bq, int br, const uint64_t *__restrict__ bitmaps,
+        const uint8_t *__restrict__ X, int N, const uint8_t *__restrict__ payload, uint32_t payload_bytes,
+        int32_t *__restrict__ Y, uint32_t stage_bytes, uint32_t nbuf, int one_pass) {
     constexpr int NBLK = BT_NBLK(TPL);
     constexpr int WC = BT_WG_THREADS(TPL) / 64;          // row-total columns: wavefronts, at most
     extern __shared__ __attribute__((aligned(16))) uint8_t bt_smem[];
@@ -467,24 +468,31 @@ __global__ __launch_bounds__(BT_WG_THREADS(TPL)) void k_bt64_w4a4(
             if (i >= nblk) break;
             bt_v4i acc[NB];
             decode_block(i, acc);
+            // this wavefront's partial of block i, lane-major: the 4
+            // accumulators of a lane side by side (one 16-byte store)
             int32_t *pw = part + (i * nwaves + wave) * NB * 256;
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-                for (int k = 0; k < 4; ++k) pw[nb * 256 + k * 64 + lane] = acc[nb][k] >> 8;
+                *(__attribute__((address_space(3))) bt_v4i *)(uintptr_t)bt_lds_addr(pw + nb * 256 + lane * 4) =
+                        bt_v4i{acc[nb][0] >> 8, acc[nb][1] >> 8, acc[nb][2] >> 8, acc[nb][3] >> 8};
         }
         __syncthreads();
-        for (int o = threadIdx.x; o < nblk * NB * 256; o += blockDim.x) {
-            const int i = o / (NB * 256), oo = o % (NB * 256);
-            const int nb = oo >> 8, col = (oo >> 4) & 15, rl = oo & 15;
-            const int ln = (rl >> 2) * 16 + col, k = rl & 3;
-            const int n = col + 16 * nb;
-            const int m0 = (b_begin + i) * BT_ROWS;
-            if (n < N && rl < min(BT_ROWS, M - m0)) {
-                const int32_t *pb = part + i * nwaves * NB * 256 + nb * 256 + k * 64 + ln;
-                int32_t v = 0;
-                for (int w = 0; w < nwaves; ++w) v += pb[w * NB * 256];
-                Y[(int64_t)n * M + m0 + rl] = v;
+        // Y: item (block i, column block nb, lane l) sums the wavefronts'
+        // partials of lane l, i.e. rows 4 (l / 16) .. +3 of column l % 16
+        // (the D layout of the 16x16 MFMAs), four consecutive rows of Y
+        for (int o = threadIdx.x; o < nblk * NB * 64; o += blockDim.x) {
+            const int i = o / (NB * 64), nb = (o / 64) % NB, ln = o % 64;
+            const int n = (ln & 15) + 16 * nb;
+            const int m = (b_begin + i) * BT_ROWS + 4 * (ln >> 4);
+            if (n >= N || m >= M) continue;
+            bt_v4i v = {0, 0, 0, 0};
+            for (int w = 0; w < nwaves; ++w)
+                v += *(bt_lds_v4i *)(uintptr_t)bt_lds_addr(part + ((i * nwaves + w) * NB + nb) * 256 + ln * 4);
+            int32_t *y = Y + (int64_t)n * M + m;
+            if (((uintptr_t)Y & 15u) == 0 && (M & 3) == 0 && m + 4 <= M) {
+                *reinterpret_cast<bt_v4i *>(y) = v;   // 16-byte aligned: Y, M and m are
+            } else {
+                for (int k = 0; k < 4 && m + k < M; ++k) y[k] = v[k];
             }
         }
         return;
@@ -580,8 +588,8 @@ static void launch_bt64_t(const BtPlan &p, const uint64_t *bitmaps, const uint32
                           int32_t *Y, hipStream_t stream) {
     (void)hipFuncSetAttribute((const void *)k_bt64_w4a4<NB, TPL>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               (int)p.lds);
-    hipLaunchKernelGGL((k_bt64_w4a4<NB, TPL>), dim3(p.grid), dim3(64 * p.nwaves), p.lds, stream, bitmaps, offsets,
-                       payload, payload_bytes, M, K, X, N, Y, p.stage_bytes, p.nbuf, p.bq, p.br, p.one_pass);
+    hipLaunchKernelGGL((k_bt64_w4a4<NB, TPL>), dim3(p.grid), dim3(64 * p.nwaves), p.lds, stream, offsets, M, K, p.bq,
+                       p.br, bitmaps, X, N, payload, payload_bytes, Y, p.stage_bytes, p.nbuf, p.one_pass);
 }
 
 static void launch_bt64_w4a4(const BtPlan &p, const uint64_t *bitmaps, const uint32_t *offsets,

@@ -126,6 +126,25 @@ def test_w4a4_uneven_block_density(dev, algo, dense_block):
 
 
 @pytest.mark.parametrize("algo", INT4_ALGOS, ids=lambda a: _NAMES[a])
+@pytest.mark.parametrize("M,K,N", [(4100, 512, 8), (4098, 1024, 3), (8200, 4096, 20), (5000, 64 * 130, 5)])
+@pytest.mark.parametrize("y_shift", [0, 1])
+def test_w4a4_many_blocks_ragged_y(dev, algo, M, K, N, y_shift):
+    # several 16-row blocks per workgroup (the all-blocks-staged path and the
+    # ring), M not a multiple of 4 or 16, and Y placed 4 bytes off a 16-byte
+    # boundary: the 16-byte stores of Y must fall back to single stores
+    p = workloads.random_int4_problem(M + K + N, M, K, N, keep=0.5)
+    enc = bsp.encode(p.W)
+    dm = enc.to_device(dev)
+    Xd = torch.from_numpy(bsp.pack_int4(p.X)).to(dev)
+    big = torch.full((N * M + 8 + y_shift,), SENTINEL, dtype=torch.int32, device=dev)
+    Y = big[y_shift: y_shift + N * M].view(N, M)
+    bsp.spmm_w4a4(dm, Xd, N, Y=Y, algo=algo)
+    torch.cuda.synchronize()
+    assert bool((big[:y_shift] == SENTINEL).all()) and bool((big[y_shift + N * M:] == SENTINEL).all())
+    assert np.array_equal(Y.cpu().numpy(), oracle_w4a4(p.W, p.X))
+
+
+@pytest.mark.parametrize("algo", INT4_ALGOS, ids=lambda a: _NAMES[a])
 def test_w4a4_k_zero(dev, algo):
     W = np.zeros((9, 0), np.int8)
     X = np.zeros((3, 0), np.int8)

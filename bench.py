@@ -38,6 +38,7 @@ import glob
 import hashlib
 import json
 import os
+import re
 import platform
 import statistics
 import sys
@@ -62,12 +63,15 @@ def algo_name(bsp, a):
     return {bsp.ALGO_ROWWAVE: "rowwave", bsp.ALGO_VALU: "valu", bsp.ALGO_MFMA: "mfma"}[a]
 
 
-def kernel_symbol(name, dtype):
-    if name == "mfma" and dtype == "fp16":
-        return "k_bt64_f16"
-    if name == "mfma":
-        return "k_bt64_w4a4"
-    return KERNEL_SYMBOL[name]
+def kernel_symbol(bsp, chosen, dt, M, K, N, nnz):
+    """Name of the kernel a launch runs: the library's own description of its
+    plan when the automatic choice is the one timed, else the algorithm's
+    kernel family."""
+    if chosen == bsp.select(dt, M, K, N, nnz):
+        m = re.search(r"kernel=(\S+)", bsp.describe(dt, M, K, N, nnz))
+        if m:
+            return m.group(1)
+    return KERNEL_SYMBOL[algo_name(bsp, chosen)]
 
 
 def source_digest():
@@ -269,7 +273,7 @@ def main():
     ap.add_argument("--summarize-traffic", metavar="OUT")
     ap.add_argument("--fetch"), ap.add_argument("--write")
     ap.add_argument("--copy-fetch"), ap.add_argument("--copy-write")
-    ap.add_argument("--kernel", default="k_bt64_w4a4", help="kernel name fragment for --summarize-traffic")
+    ap.add_argument("--kernel", default="w4a4", help="kernel name fragment for --summarize-traffic")
     ap.add_argument("--note", action="append", default=[], help="header line for a summary")
     args = ap.parse_args()
 
@@ -409,7 +413,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None if traffic is None else int(traffic),
-                     "kernel": kernel_symbol(name, problem.dtype), "bytes_per_launch": nbytes},
+                     "kernel": kernel_symbol(bsp, chosen, dt, M, K, N, enc.nnz), "bytes_per_launch": nbytes},
         "parity_sample_ok": parity,
     }
     if not args.no_cpu_baseline:

@@ -522,6 +522,229 @@ __global__ __launch_bounds__(BT_WG_THREADS(TPL)) void k_bt64_w4a4(
     write_y(nblk - 1);
 }
 
+// Streaming variant for TPL = 2 (K <= 4096) and at most BTS_NBLK blocks per
+// workgroup. Each wavefront issues D payload DMA instructions (1 KB each) per
+// block, a fixed count, so the vector-memory counter tells exactly when block
+// i has landed; granules past the block read as zeros. A block with more
+// granules than the D KB per wavefront hold is decoded from global memory
+// instead. Only BTS_AHEAD blocks are in flight at a time: block i + BTS_AHEAD
+// is issued once block i has landed, so the memory system delivers the blocks
+// in order (with every block in flight at once they all land together) and
+// block i is decoded while the next one streams in. Per block: words -> row
+// totals -> wait for its payload -> barrier -> decode into a per-wavefront
+// partial slice. The barrier is an LDS-only one, so it never waits for the
+// later blocks' transfers.
+#define BTS_NBLK 3
+#define BTS_AHEAD 1   // blocks whose payload is in flight at once
+
+// Workgroup barrier for LDS traffic only: waits for this wavefront's LDS
+// operations, not for its outstanding global loads and payload DMAs (whose
+// completion the caller establishes with bt_wait_vm where it needs it).
+__device__ __forceinline__ void bt_barrier_lds() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt unconstrained
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+template <int NB, int D>
+__global__ __launch_bounds__(512) void k_bt64s_w4a4(
+        const uint32_t *__restrict__ offsets, int M, int K, int bq, int br, const uint64_t *__restrict__ bitmaps,
+        const uint8_t *__restrict__ X, int N, const uint8_t *__restrict__ payload, uint32_t payload_bytes,
+        int32_t *__restrict__ Y) {
+    constexpr int TPL = 2, NBLK = BTS_NBLK, WC = 8;
+    extern __shared__ __attribute__((aligned(16))) uint8_t bt_smem[];
+    const int nwaves = blockDim.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int r = lane & 15, q = lane >> 4;
+    const int T = (K + 63) >> 6;
+    const int gid = (int)blockIdx.x;
+    const int b_begin = gid * bq + min(gid, br);
+    const int nblk = bq + (gid < br ? 1 : 0);           // 1 .. NBLK
+    const int t0 = (wave * 4 + q) * TPL;
+    const uint32_t xs = (uint32_t)K >> 1;
+    asm volatile("" ::"s"(bitmaps), "s"(payload), "s"(X), "s"(Y), "s"(N), "s"(payload_bytes));
+
+    // LDS: selector table | row totals [NBLK][16][WC] | partials
+    // [NBLK][nwaves][NB*256] | staging [NBLK][nwaves*D KB]
+    const uint32_t lut_base = bt_lds_addr(bt_smem) + (uint32_t)(lane % BT_LUT_COPIES) * 8u;
+    int32_t *wt = reinterpret_cast<int32_t *>(bt_smem + BT_LUT_BYTES);
+    int32_t *part = wt + NBLK * BT_ROWS * WC;
+    uint8_t *stage = reinterpret_cast<uint8_t *>(part + NBLK * nwaves * NB * 256);
+    const uint32_t area = (uint32_t)nwaves * D * 1024u;
+    const uint32_t cap = (uint32_t)nwaves * D * 64u;   // granules one block's area holds
+    const __amdgpu_buffer_rsrc_t prs = bt_rsrc(payload, payload_bytes);
+
+    uint32_t nib[NBLK + 1];
+#pragma unroll
+    for (int i = 0; i <= NBLK; ++i) {
+        const int b = b_begin + (i < nblk ? i : nblk);
+        nib[i] = offsets[(int64_t)min(b * BT_ROWS, M) * T];
+    }
+    asm volatile("" ::: "memory");
+
+    // X slices of the lane's tiles (zeros past N or T)
+    uint32_t xw[NB][TPL][8];
+    {
+        const __amdgpu_buffer_rsrc_t xrs = bt_rsrc(X, (uint32_t)N * xs);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int k = 0; k < TPL; ++k) {
+                const int n = r + 16 * nb;
+                const uint32_t off = (n < N && t0 + k < T) ? (uint32_t)n * xs + (uint32_t)(t0 + k) * 32u : 0xFFFFFFE0u;
+                const bt_v4i v0 = __builtin_bit_cast(bt_v4i, __builtin_amdgcn_raw_buffer_load_b128(xrs, off, 0, 0));
+                const bt_v4i v1 = __builtin_bit_cast(bt_v4i, __builtin_amdgcn_raw_buffer_load_b128(xrs, off + 16u, 0, 0));
+                xw[nb][k][0] = v0.x; xw[nb][k][1] = v0.y; xw[nb][k][2] = v0.z; xw[nb][k][3] = v0.w;
+                xw[nb][k][4] = v1.x; xw[nb][k][5] = v1.y; xw[nb][k][6] = v1.z; xw[nb][k][7] = v1.w;
+            }
+    }
+    // every block's words (a slot past nblk, a row past M or a tile past T reads zeros)
+    const int m_first = b_begin * BT_ROWS;
+    const int wg_rows = min(nblk * BT_ROWS, M - m_first);
+    const __amdgpu_buffer_rsrc_t brs = bt_rsrc(bitmaps + (int64_t)m_first * T, (uint32_t)wg_rows * (uint32_t)T * 8u);
+    uint64_t words[NBLK][TPL];
+#pragma unroll
+    for (int i = 0; i < NBLK; ++i) {
+        const int rr = i * BT_ROWS + r;
+        const uint32_t off = (rr < wg_rows && t0 < T) ? ((uint32_t)rr * (uint32_t)T + (uint32_t)t0) * 8u : 0xFFFFFFE0u;
+        const bt_v4i v = __builtin_bit_cast(bt_v4i, __builtin_amdgcn_raw_buffer_load_b128(brs, off, 0, 0));
+        words[i][0] = ((uint64_t)(uint32_t)v.y << 32) | (uint32_t)v.x;
+        words[i][1] = ((uint64_t)(uint32_t)v.w << 32) | (uint32_t)v.z;
+    }
+    // B operands (waits for X only: the words were issued after it)
+    bt_v4i xb[NB][TPL][4];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int k = 0; k < TPL; ++k)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                xb[nb][k][j] = bt_b_operand(xw[nb][k][2 * j], xw[nb][k][2 * j + 1]);
+                asm volatile("" : "+v"(xb[nb][k][j]));
+            }
+    // payload of block i: D instructions per wavefront (a slot past nblk
+    // issues them too, out of range, so every count stays static)
+    auto issue = [&](int i) -> void {
+        const BtRange g = bt_range(nib[i], nib[i + 1]);
+        const uint32_t n = i < nblk ? min(g.n, cap) : 0u;
+        uint8_t *buf = stage + (uint32_t)i * area;
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            const uint32_t j = (uint32_t)(wave + nwaves * d);
+            const uint32_t u = j * 64u + (uint32_t)lane;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(prs, (bt_lds_void *)(buf + j * 1024u), 16,
+                                                     u < n ? (g.g0 + u) * 16u : 0xFFFFFFF0u, 0, 0, 0);
+        }
+    };
+    // BTS_AHEAD blocks in flight: the memory system serves them before any
+    // later block, which is issued only once block i has landed
+#pragma unroll
+    for (int i = 0; i < BTS_AHEAD && i < NBLK; ++i) issue(i);
+    {
+        __attribute__((address_space(3))) uint64_t *lut_lds =
+                (__attribute__((address_space(3))) uint64_t *)(uintptr_t)bt_lds_addr(bt_smem);
+        for (uint32_t v = threadIdx.x; v < 256u * BT_LUT_COPIES / 8u; v += blockDim.x) {
+            const uint32_t b = v & 255u, c0 = 8u * (v >> 8);
+            const uint2 e = bt_lut_entry(b);
+            const uint64_t e64 = ((uint64_t)e.y << 32) | e.x;
+#pragma unroll
+            for (uint32_t k = 0; k < 8; ++k) lut_lds[b * BT_LUT_COPIES + c0 + ((k + v) & 7u)] = e64;
+        }
+    }
+
+#pragma unroll
+    for (int i = 0; i < NBLK; ++i) {
+        if (i >= nblk) break;
+        // words of block i -> segment popcounts, lane-group prefix, row totals
+#pragma unroll
+        for (int k = 0; k < TPL; ++k)
+            if (t0 + k >= T) words[i][k] = 0;
+        uint32_t seg = 0;
+#pragma unroll
+        for (int k = 0; k < TPL; ++k) seg += (uint32_t)__builtin_popcountll(words[i][k]);
+        uint32_t incl = seg;
+        {
+            const uint32_t u16 = (uint32_t)__shfl_up((int)incl, 16, 64);
+            incl += q >= 1 ? u16 : 0u;
+            const uint32_t u32 = (uint32_t)__shfl_up((int)incl, 32, 64);
+            incl += q >= 2 ? u32 : 0u;
+        }
+        int32_t *wti = wt + i * BT_ROWS * WC;
+        if (q == 3) wti[r * WC + wave] = (int32_t)incl;
+        // this wavefront's share of block i landed (the blocks issued after it may not have)
+        bt_wait_vm((uint32_t)D * (uint32_t)(min(i + BTS_AHEAD, NBLK) - i - 1));
+        if (i + BTS_AHEAD < NBLK) issue(i + BTS_AHEAD);
+        bt_barrier_lds();                     // ... everyone's, and every row total of block i
+        const BtRange g = bt_range(nib[i], nib[i + 1]);
+        const int rows = min(BT_ROWS, M - (b_begin + i) * BT_ROWS);
+        uint32_t pstart;
+        {
+            uint32_t row_total = 0, before_w = 0;
+#pragma unroll
+            for (int w4 = 0; w4 < WC; w4 += 4) {
+                const bt_v4i t4 = *(bt_lds_v4i *)(uintptr_t)bt_lds_addr(wti + r * WC + w4);
+                const uint32_t t[4] = {(uint32_t)t4.x, (uint32_t)t4.y, (uint32_t)t4.z, (uint32_t)t4.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int w = w4 + e;
+                    const uint32_t v = w < nwaves ? t[e] : 0u;
+                    row_total += v;
+                    if (w < wave) before_w += v;
+                }
+            }
+            uint32_t sc = row_total;
+            sc += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)sc, 0x111, 0xF, 0xF, true);   // row_shr:1
+            sc += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)sc, 0x112, 0xF, 0xF, true);   // row_shr:2
+            sc += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)sc, 0x114, 0xF, 0xF, true);   // row_shr:4
+            sc += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)sc, 0x118, 0xF, 0xF, true);   // row_shr:8
+            pstart = r < rows ? (nib[i] & 31u) + (sc - row_total) + before_w + (incl - seg) : 0u;
+        }
+        bt_v4i acc[NB];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[nb] = bt_v4i{0, 0, 0, 0};
+        if (g.n <= cap) {
+            // a corrupt stream stays inside the staged granules
+            uint32_t p = min(pstart, 8u * (4u * g.n - 2u));
+            p += 2u * bt_lds_addr(stage + (uint32_t)i * area);
+            bt_contract<NB, TPL>(words[i], p, BtWinLds{}, lut_base, xb, acc);
+        } else {
+            bt_contract<NB, TPL>(words[i], pstart, BtWinGlobal{prs, 4u * g.g0}, lut_base, xb, acc);
+        }
+        int32_t *pw = part + (i * nwaves + wave) * NB * 256;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+            *(__attribute__((address_space(3))) bt_v4i *)(uintptr_t)bt_lds_addr(pw + nb * 256 + lane * 4) =
+                    bt_v4i{acc[nb][0] >> 8, acc[nb][1] >> 8, acc[nb][2] >> 8, acc[nb][3] >> 8};
+    }
+    bt_barrier_lds();
+    // Y: item (block i, column block nb, lane l) sums the wavefronts' partials
+    // of lane l: rows 4 (l / 16) .. +3 of column l % 16 (the MFMA D layout)
+    const bool vec = ((uintptr_t)Y & 15) == 0 && (M & 3) == 0;
+    for (int o = threadIdx.x; o < nblk * NB * 64; o += blockDim.x) {
+        const int i = o / (NB * 64), nb = (o / 64) % NB, ln = o % 64;
+        const int n = (ln & 15) + 16 * nb;
+        const int m = (b_begin + i) * BT_ROWS + 4 * (ln >> 4);
+        if (n >= N || m >= M) continue;
+        bt_v4i s = bt_v4i{0, 0, 0, 0};
+        for (int w = 0; w < nwaves; ++w)
+            s += *(bt_lds_v4i *)(uintptr_t)bt_lds_addr(part + ((i * nwaves + w) * NB + nb) * 256 + ln * 4);
+        int32_t *yp = Y + (int64_t)n * M + m;
+        if (vec && m + 4 <= M) {
+            *(bt_v4i *)yp = s;
+        } else {
+            const int32_t v[4] = {s.x, s.y, s.z, s.w};
+            for (int k = 0; k < 4 && m + k < M; ++k) yp[k] = v[k];
+        }
+    }
+}
+
+// LDS of the streaming variant with D KB of staging per wavefront and block
+static size_t bts_lds(int nwaves, int nb, int d) {
+    return (size_t)BT_LUT_BYTES + (size_t)BTS_NBLK * BT_ROWS * 8 * 4 + (size_t)BTS_NBLK * nwaves * nb * 256 * 4 +
+           (size_t)BTS_NBLK * nwaves * d * 1024;
+}
+
 // Launch plan.
 struct BtPlan {
     int nwaves, nb, tpl;
@@ -529,6 +752,7 @@ struct BtPlan {
     int bq, br;             // blocks per workgroup: bq, plus one for the first br workgroups
     uint32_t stage_bytes;   // one staging buffer
     uint32_t nbuf;          // staging buffers in the ring
+    int streaming;          // > 0: the streaming variant k_bt64s_w4a4 with this many KB per wavefront and block
     int one_pass;           // every block staged at once: one barrier before and one after the decode
     size_t lds;             // total dynamic LDS
 };
@@ -579,6 +803,18 @@ static bool bt64_plan(int64_t M, int64_t K, int64_t N, int64_t payload_bytes, Bt
     p->stage_bytes = (uint32_t)stage;
     p->nbuf = (uint32_t)nbuf;
     p->lds = (size_t)(fixed + nbuf * stage + (p->one_pass ? part : 0));
+    // streaming variant: D KB per wavefront and block covers the same
+    // estimate as the staging buffer above
+    p->streaming = 0;
+    if (p->tpl == 2 && per_wg <= BTS_NBLK) {
+        const int64_t est = std::min<int64_t>(worst, avg + avg / 5 + 2048) + 32;
+        const int64_t d = std::min<int64_t>(4, std::max<int64_t>(2, (est + p->nwaves * 1024 - 1) / (p->nwaves * 1024)));
+        const size_t s_lds = bts_lds(p->nwaves, p->nb, (int)d);
+        if ((int64_t)s_lds <= budget) {
+            p->streaming = (int)d;
+            p->lds = s_lds;
+        }
+    }
     return true;
 }
 
@@ -595,6 +831,22 @@ static void launch_bt64_t(const BtPlan &p, const uint64_t *bitmaps, const uint32
 static void launch_bt64_w4a4(const BtPlan &p, const uint64_t *bitmaps, const uint32_t *offsets,
                              const uint8_t *payload, uint32_t payload_bytes, int M, int K, const uint8_t *X, int N,
                              int32_t *Y, hipStream_t stream) {
+    if (p.streaming) {
+#define BTS_LAUNCH(NB, D)                                                                                         \
+    do {                                                                                                          \
+        (void)hipFuncSetAttribute((const void *)k_bt64s_w4a4<NB, D>, hipFuncAttributeMaxDynamicSharedMemorySize, \
+                                  (int)p.lds);                                                                    \
+        hipLaunchKernelGGL((k_bt64s_w4a4<NB, D>), dim3(p.grid), dim3(64 * p.nwaves), p.lds, stream, offsets, M, K, \
+                           p.bq, p.br, bitmaps, X, N, payload, payload_bytes, Y);                                 \
+    } while (0)
+        if (p.nb == 1) {
+            if (p.streaming == 2) BTS_LAUNCH(1, 2); else if (p.streaming == 3) BTS_LAUNCH(1, 3); else BTS_LAUNCH(1, 4);
+        } else {
+            if (p.streaming == 2) BTS_LAUNCH(2, 2); else if (p.streaming == 3) BTS_LAUNCH(2, 3); else BTS_LAUNCH(2, 4);
+        }
+#undef BTS_LAUNCH
+        return;
+    }
 #define BT_LAUNCH(NB, TPL) launch_bt64_t<NB, TPL>(p, bitmaps, offsets, payload, payload_bytes, M, K, X, N, Y, stream)
     if (p.nb == 1) {
         if (p.tpl == 1) BT_LAUNCH(1, 1); else if (p.tpl == 2) BT_LAUNCH(1, 2);

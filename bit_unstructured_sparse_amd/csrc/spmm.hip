@@ -80,9 +80,33 @@ extern "C" int bsp_describe_selection(int dtype, int64_t M, int64_t K, int64_t N
     int a = bsp_select(dtype, M, K, N, nnz);
     if (a < 0 || buf == nullptr || n == 0) return BSP_E_ARG;
     const char *name = a == BSP_ALGO_ROWWAVE ? "rowwave" : a == BSP_ALGO_VALU ? "valu" : "mfma";
-    snprintf(buf, n, "dtype=%s M=%lld K=%lld N=%lld nnz=%lld -> %s",
-             dtype == BSP_INT4 ? "int4" : "fp16", (long long)M, (long long)K, (long long)N,
-             (long long)nnz, name);
+    const char *ty = dtype == BSP_INT4 ? "int4" : "fp16";
+    // payload bytes the encoder writes for nnz nonzeros (all of W when unknown)
+    const int64_t nz = nnz >= 0 ? nnz : M * K;
+    const int64_t pbytes = dtype == BSP_INT4 ? (nz + 1) / 2 : 2 * nz;
+    char launch[160] = "";
+    if (a == BSP_ALGO_MFMA && M > 0 && N > 0) {
+        if (dtype == BSP_INT4) {
+            BtPlan p;
+            if (bt64_plan(M, K, N, pbytes, &p)) {
+                if (p.streaming)
+                    snprintf(launch, sizeof launch, " kernel=k_bt64s_w4a4 grid=%u block=%d lds=%zu stage_kb_per_wave=%d",
+                             p.grid, 64 * p.nwaves, p.lds, p.streaming);
+                else
+                    snprintf(launch, sizeof launch, " kernel=k_bt64_w4a4 grid=%u block=%d lds=%zu tiles_per_lane=%d one_pass=%d",
+                             p.grid, 64 * p.nwaves, p.lds, p.tpl, p.one_pass);
+            }
+        } else {
+            BfPlan p;
+            if (bf_plan(M, K, N, pbytes, &p))
+                snprintf(launch, sizeof launch, " kernel=k_bt64_f16 grid=%u block=%d lds=%zu", p.grid, 64 * p.nwaves,
+                         p.lds);
+        }
+    }
+    if (launch[0] == 0 && a != BSP_ALGO_VALU && M > 0 && N > 0)
+        snprintf(launch, sizeof launch, " kernel=k_rowwave_%s", dtype == BSP_INT4 ? "w4a4" : "f16");
+    snprintf(buf, n, "dtype=%s M=%lld K=%lld N=%lld nnz=%lld -> %s%s", ty, (long long)M, (long long)K, (long long)N,
+             (long long)nnz, name, launch);
     return BSP_OK;
 }
 

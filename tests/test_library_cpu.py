@@ -149,3 +149,17 @@ def test_selection_is_defined_for_every_shape():
                 assert bsp.describe(dt, M, K, N).startswith("dtype=")
     assert bsp.select(bsp.INT4, 1, 1, 33) == -1
     assert bsp.select(5, 1, 1, 1) == -1
+
+
+def test_description_names_the_launched_kernel():
+    # the plan's kernel for each family of shapes (host-only planning, no launch)
+    d = bsp.describe(bsp.INT4, 12288, 4096, 8, 12288 * 4096 // 2)
+    assert "-> mfma kernel=k_bt64s_w4a4 " in d and "grid=256 block=512" in d
+    d = bsp.describe(bsp.INT4, 4096, 11008, 16, 4096 * 11008 * 3 // 10)
+    assert "-> mfma kernel=k_bt64_w4a4 " in d and "tiles_per_lane=8" in d
+    d = bsp.describe(bsp.FP16, 4096, 4096, 1, 4096 * 4096 * 4 // 10)
+    assert "-> mfma kernel=k_bt64_f16 " in d and "block=1024" in d
+    # K not a multiple of 32: outside the fast path
+    assert bsp.describe(bsp.INT4, 64, 100, 4).endswith("-> rowwave kernel=k_rowwave_w4a4")
+    # nothing to launch
+    assert "kernel=" not in bsp.describe(bsp.INT4, 0, 4096, 8)

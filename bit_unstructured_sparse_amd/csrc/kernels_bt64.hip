@@ -173,16 +173,23 @@ __device__ __forceinline__ bt_v4i bt_b_operand(uint32_t x0, uint32_t x1) {
                   (int)(x1 & 0xF0F0F0F0u)};
 }
 
+// Window positions of a tile as counted: p unchanged.
+struct BtTileSame {
+    __device__ __forceinline__ uint32_t operator()(uint32_t p) const { return p; }
+};
+
 // Decode + contract the lane's TPL tiles of one block. xb holds the lane's
 // B operands (column r + 16 nb, tiles t0 .. t0+TPL-1, MFMA j), built once.
-template <int NB, int TPL, class Win>
+// tile(p) maps the stream position of a tile's first nonzero to the position
+// its windows are read from.
+template <int NB, int TPL, class Win, class Tile = BtTileSame>
 __device__ __forceinline__ void bt_contract(const uint64_t (&words)[TPL], uint32_t p, const Win &win,
                                             uint32_t lut_base, const bt_v4i (&xb)[NB][TPL][4],
-                                            bt_v4i (&acc)[NB]) {
+                                            bt_v4i (&acc)[NB], const Tile &tile = Tile{}) {
 #pragma unroll
     for (int i = 0; i < TPL; ++i) {
         uint32_t A[16];
-        bt_decode_tile(words[i], p, win, lut_base, A);
+        bt_decode_tile(words[i], tile(p), win, lut_base, A);
         p += (uint32_t)__builtin_popcountll(words[i]);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -535,6 +542,10 @@ __global__ __launch_bounds__(BT_WG_THREADS(TPL)) void k_bt64_w4a4(
 // partial slice. The barrier is an LDS-only one, so it never waits for the
 // later blocks' transfers.
 #define BTS_NBLK 3
+#define BTS_RUN 64u              // granules per run of the staggered staging (1 KB)
+#define BTS_RUN_NIB_LOG2 11      // log2 of the nibbles in a run
+#define BTS_OVL 3u               // granules stored again after each run: a tile's windows reach < 48 B past its start
+#define BTS_DIVMAG 15651u        // ceil(2^20 / (BTS_RUN + BTS_OVL)): exact quotient for slots < 2^14
 #define BTS_AHEAD 1   // blocks whose payload is in flight at once
 
 // Workgroup barrier for LDS traffic only: waits for this wavefront's LDS
@@ -551,7 +562,7 @@ template <int NB, int D>
 __global__ __launch_bounds__(512) void k_bt64s_w4a4(
         const uint32_t *__restrict__ offsets, int M, int K, int bq, int br, const uint64_t *__restrict__ bitmaps,
         const uint8_t *__restrict__ X, int N, const uint8_t *__restrict__ payload, uint32_t payload_bytes,
-        int32_t *__restrict__ Y) {
+        int32_t *__restrict__ Y, uint32_t stagger) {
     constexpr int TPL = 2, NBLK = BTS_NBLK, WC = 8;
     extern __shared__ __attribute__((aligned(16))) uint8_t bt_smem[];
     const int nwaves = blockDim.x >> 6;
@@ -572,7 +583,17 @@ __global__ __launch_bounds__(512) void k_bt64s_w4a4(
     int32_t *part = wt + NBLK * BT_ROWS * WC;
     uint8_t *stage = reinterpret_cast<uint8_t *>(part + NBLK * nwaves * NB * 256);
     const uint32_t area = (uint32_t)nwaves * D * 1024u;
-    const uint32_t cap = (uint32_t)nwaves * D * 64u;   // granules one block's area holds
+    // Staggered staging (stagger = 1): the stream is cut in runs of
+    // BTS_RUN granules, each stored with the next BTS_OVL granules after it,
+    // so every run starts BTS_OVL granules (48 B) further round the LDS banks
+    // than the stream would put it. Rows whose length is close to a multiple
+    // of 256 B otherwise put the same tile of every row on the same banks.
+    // Granule u of the stream sits in slot u + BTS_OVL * (u / BTS_RUN); slot s
+    // holds granule s - BTS_OVL * (s / (BTS_RUN + BTS_OVL)).
+    const uint32_t slots = (uint32_t)nwaves * D * 64u;
+    const uint32_t cap = stagger ? BTS_RUN * (slots / (BTS_RUN + BTS_OVL)) : slots;   // granules a block's area holds
+    const uint32_t kmag = stagger ? BTS_DIVMAG : 0u;             // s * kmag >> 20 = s / (BTS_RUN + BTS_OVL)
+    const uint32_t tmul = stagger ? 2u * 16u * BTS_OVL : 0u;     // nibbles added per run
     const __amdgpu_buffer_rsrc_t prs = bt_rsrc(payload, payload_bytes);
 
     uint32_t nib[NBLK + 1];
@@ -632,7 +653,8 @@ __global__ __launch_bounds__(512) void k_bt64s_w4a4(
 #pragma unroll
         for (int d = 0; d < D; ++d) {
             const uint32_t j = (uint32_t)(wave + nwaves * d);
-            const uint32_t u = j * 64u + (uint32_t)lane;
+            const uint32_t sl = j * 64u + (uint32_t)lane;
+            const uint32_t u = sl - BTS_OVL * ((sl * kmag) >> 20);   // stream granule of slot sl
             __builtin_amdgcn_raw_ptr_buffer_load_lds(prs, (bt_lds_void *)(buf + j * 1024u), 16,
                                                      u < n ? (g.g0 + u) * 16u : 0xFFFFFFF0u, 0, 0, 0);
         }
@@ -705,9 +727,12 @@ __global__ __launch_bounds__(512) void k_bt64s_w4a4(
         for (int nb = 0; nb < NB; ++nb) acc[nb] = bt_v4i{0, 0, 0, 0};
         if (g.n <= cap) {
             // a corrupt stream stays inside the staged granules
-            uint32_t p = min(pstart, 8u * (4u * g.n - 2u));
-            p += 2u * bt_lds_addr(stage + (uint32_t)i * area);
-            bt_contract<NB, TPL>(words[i], p, BtWinLds{}, lut_base, xb, acc);
+            // (a tile's windows stay inside the run of its first nonzero plus
+            // the BTS_OVL granules stored after it)
+            const uint32_t p = min(pstart, 8u * (4u * g.n - 2u));
+            const uint32_t base2 = 2u * bt_lds_addr(stage + (uint32_t)i * area);
+            bt_contract<NB, TPL>(words[i], p, BtWinLds{}, lut_base, xb, acc,
+                                 [=](uint32_t pt) { return pt + base2 + (pt >> BTS_RUN_NIB_LOG2) * tmul; });
         } else {
             bt_contract<NB, TPL>(words[i], pstart, BtWinGlobal{prs, 4u * g.g0}, lut_base, xb, acc);
         }
@@ -753,6 +778,7 @@ struct BtPlan {
     uint32_t stage_bytes;   // one staging buffer
     uint32_t nbuf;          // staging buffers in the ring
     int streaming;          // > 0: the streaming variant k_bt64s_w4a4 with this many KB per wavefront and block
+    int stagger;            // streaming variant: staggered staging (rows near a multiple of 256 B long)
     int one_pass;           // every block staged at once: one barrier before and one after the decode
     size_t lds;             // total dynamic LDS
 };
@@ -806,6 +832,7 @@ static bool bt64_plan(int64_t M, int64_t K, int64_t N, int64_t payload_bytes, Bt
     // streaming variant: D KB per wavefront and block covers the same
     // estimate as the staging buffer above
     p->streaming = 0;
+    p->stagger = 0;
     if (p->tpl == 2 && per_wg <= BTS_NBLK) {
         const int64_t est = std::min<int64_t>(worst, avg + avg / 5 + 2048) + 32;
         const int64_t d = std::min<int64_t>(4, std::max<int64_t>(2, (est + p->nwaves * 1024 - 1) / (p->nwaves * 1024)));
@@ -813,6 +840,12 @@ static bool bt64_plan(int64_t M, int64_t K, int64_t N, int64_t payload_bytes, Bt
         if ((int64_t)s_lds <= budget) {
             p->streaming = (int)d;
             p->lds = s_lds;
+            // average payload bytes per row, modulo the 256 B the LDS banks
+            // span: within 28 B of a multiple, the same tile of consecutive
+            // rows falls on the same banks (elsewhere the plain layout does as
+            // well or better)
+            const int64_t rb = (payload_bytes / std::max<int64_t>(M, 1)) % 256;
+            p->stagger = std::min<int64_t>(rb, 256 - rb) < 28;
         }
     }
     return true;
@@ -837,7 +870,7 @@ static void launch_bt64_w4a4(const BtPlan &p, const uint64_t *bitmaps, const uin
         (void)hipFuncSetAttribute((const void *)k_bt64s_w4a4<NB, D>, hipFuncAttributeMaxDynamicSharedMemorySize, \
                                   (int)p.lds);                                                                    \
         hipLaunchKernelGGL((k_bt64s_w4a4<NB, D>), dim3(p.grid), dim3(64 * p.nwaves), p.lds, stream, offsets, M, K, \
-                           p.bq, p.br, bitmaps, X, N, payload, payload_bytes, Y);                                 \
+                           p.bq, p.br, bitmaps, X, N, payload, payload_bytes, Y, (uint32_t)p.stagger);            \
     } while (0)
         if (p.nb == 1) {
             if (p.streaming == 2) BTS_LAUNCH(1, 2); else if (p.streaming == 3) BTS_LAUNCH(1, 3); else BTS_LAUNCH(1, 4);

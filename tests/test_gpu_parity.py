@@ -145,6 +145,27 @@ def test_w4a4_many_blocks_ragged_y(dev, algo, M, K, N, y_shift):
 
 
 @pytest.mark.parametrize("algo", INT4_ALGOS, ids=lambda a: _NAMES[a])
+@pytest.mark.parametrize("M,K,N,dense_block", [(4100, 2048, 8, -1), (3000, 1024, 5, -1), (2048, 4096, 20, -1),
+                                               (1600, 4096, 8, -1), (1600, 4096, 8, 7), (1600, 4096, 8, 99)])
+def test_w4a4_staggered_staging(dev, algo, M, K, N, dense_block):
+    # rows whose payload is close to a multiple of 256 bytes (half density at
+    # K = 1024, 2048 and 4096, quarter density at 4096): the plan stages them
+    # in staggered runs; one fully dense block (or the last, ragged one) is
+    # too large for the staggered area and reads its windows from global memory
+    rng = np.random.default_rng(M + K + N + dense_block)
+    keep = np.full((M, 1), 0.25 if N == 20 else 0.5)
+    if dense_block >= 0:
+        b = min(dense_block, (M - 1) // 16)
+        keep[16 * b:16 * b + 16] = 1.0
+    W = workloads._int4_weights(rng, M, K, keep)
+    X = workloads.int4_activations(rng, (N, K))
+    enc = bsp.encode(W)
+    if algo == bsp.ALGO_MFMA:
+        assert "stagger=1" in bsp.describe(bsp.INT4, M, K, N, enc.nnz)
+    assert np.array_equal(run_w4a4(W, X, algo, dev, enc=enc), oracle_w4a4(W, X))
+
+
+@pytest.mark.parametrize("algo", INT4_ALGOS, ids=lambda a: _NAMES[a])
 def test_w4a4_k_zero(dev, algo):
     W = np.zeros((9, 0), np.int8)
     X = np.zeros((3, 0), np.int8)

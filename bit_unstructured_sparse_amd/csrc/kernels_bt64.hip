@@ -54,10 +54,9 @@
 #define BT_CUS 256
 
 // Blocks one workgroup can own: every block's words stay in VGPRs (TPL words per lane).
-#define BT_NBLK(TPL) ((TPL) == 1 ? 4 : 8 / (TPL))
-// Threads per workgroup at most: 16 wavefronts with one tile per lane (<= 128
-// VGPRs each), else 8 wavefronts (<= 256 VGPRs each).
-#define BT_WG_THREADS(TPL) ((TPL) == 1 ? 1024 : 512)
+#define BT_NBLK(TPL) (8 / (TPL))
+// Threads per workgroup at most: 8 wavefronts (<= 256 VGPRs each).
+#define BT_WG_THREADS(TPL) 512
 
 typedef int bt_v4i __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void bt_lds_void;
@@ -293,7 +292,7 @@ __global__ __launch_bounds__(BT_WG_THREADS(TPL)) void k_bt64_w4a4(
     uint64_t words[NBLK][TPL];
     // two consecutive tiles per 16-byte load (one per 8-byte load at TPL 8,
     // where the wider form costs registers)
-    constexpr int WPL = (TPL == 1 || TPL >= 8) ? 1 : 2;   // words per load
+    constexpr int WPL = TPL >= 8 ? 1 : 2;   // words per load
     auto load_words = [&](int i) -> void {
         const int rr = i * BT_ROWS + r;   // row inside the workgroup's range
 #pragma unroll
@@ -428,19 +427,19 @@ __global__ __launch_bounds__(BT_WG_THREADS(TPL)) void k_bt64_w4a4(
         // lane start: rows before r, wavefronts before this one, lane groups before q
         uint32_t pstart;
         {
-            uint32_t row_total = 0, before_w = 0;
+            // prefix over the wavefronts' totals; the wave-uniform indices
+            // become one indexed register read each
+            uint32_t pre[WC + 1];
+            pre[0] = 0;
 #pragma unroll
             for (int w4 = 0; w4 < WC; w4 += 4) {
                 const bt_v4i t4 = *(bt_lds_v4i *)(uintptr_t)bt_lds_addr(wti + r * WC + w4);
-                const uint32_t t[4] = {(uint32_t)t4.x, (uint32_t)t4.y, (uint32_t)t4.z, (uint32_t)t4.w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int w = w4 + e;
-                    const uint32_t v = w < nwaves ? t[e] : 0u;
-                    row_total += v;
-                    if (w < wave) before_w += v;   // wave-uniform condition
-                }
+                pre[w4 + 1] = pre[w4] + (uint32_t)t4.x;
+                pre[w4 + 2] = pre[w4 + 1] + (uint32_t)t4.y;
+                pre[w4 + 3] = pre[w4 + 2] + (uint32_t)t4.z;
+                pre[w4 + 4] = pre[w4 + 3] + (uint32_t)t4.w;
             }
+            const uint32_t row_total = pre[nwaves], before_w = pre[wave];
             // exclusive prefix of row totals over r inside each 16-lane DPP row
             uint32_t sc = row_total;
             sc += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)sc, 0x111, 0xF, 0xF, true);   // row_shr:1
@@ -702,19 +701,19 @@ __global__ __launch_bounds__(512) void k_bt64s_w4a4(
         const int rows = min(BT_ROWS, M - (b_begin + i) * BT_ROWS);
         uint32_t pstart;
         {
-            uint32_t row_total = 0, before_w = 0;
+            // prefix over the wavefronts' totals; the wave-uniform indices
+            // become one indexed register read each
+            uint32_t pre[WC + 1];
+            pre[0] = 0;
 #pragma unroll
             for (int w4 = 0; w4 < WC; w4 += 4) {
                 const bt_v4i t4 = *(bt_lds_v4i *)(uintptr_t)bt_lds_addr(wti + r * WC + w4);
-                const uint32_t t[4] = {(uint32_t)t4.x, (uint32_t)t4.y, (uint32_t)t4.z, (uint32_t)t4.w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int w = w4 + e;
-                    const uint32_t v = w < nwaves ? t[e] : 0u;
-                    row_total += v;
-                    if (w < wave) before_w += v;
-                }
+                pre[w4 + 1] = pre[w4] + (uint32_t)t4.x;
+                pre[w4 + 2] = pre[w4 + 1] + (uint32_t)t4.y;
+                pre[w4 + 3] = pre[w4 + 2] + (uint32_t)t4.z;
+                pre[w4 + 4] = pre[w4 + 3] + (uint32_t)t4.w;
             }
+            const uint32_t row_total = pre[nwaves], before_w = pre[wave];
             uint32_t sc = row_total;
             sc += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)sc, 0x111, 0xF, 0xF, true);   // row_shr:1
             sc += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)sc, 0x112, 0xF, 0xF, true);   // row_shr:2
@@ -882,11 +881,9 @@ static void launch_bt64_w4a4(const BtPlan &p, const uint64_t *bitmaps, const uin
     }
 #define BT_LAUNCH(NB, TPL) launch_bt64_t<NB, TPL>(p, bitmaps, offsets, payload, payload_bytes, M, K, X, N, Y, stream)
     if (p.nb == 1) {
-        if (p.tpl == 1) BT_LAUNCH(1, 1); else if (p.tpl == 2) BT_LAUNCH(1, 2);
-        else if (p.tpl == 4) BT_LAUNCH(1, 4); else BT_LAUNCH(1, 8);
+        if (p.tpl == 2) BT_LAUNCH(1, 2); else if (p.tpl == 4) BT_LAUNCH(1, 4); else BT_LAUNCH(1, 8);
     } else {
-        if (p.tpl == 1) BT_LAUNCH(2, 1); else if (p.tpl == 2) BT_LAUNCH(2, 2);
-        else if (p.tpl == 4) BT_LAUNCH(2, 4); else BT_LAUNCH(2, 8);
+        if (p.tpl == 2) BT_LAUNCH(2, 2); else if (p.tpl == 4) BT_LAUNCH(2, 4); else BT_LAUNCH(2, 8);
     }
 #undef BT_LAUNCH
 }

@@ -293,12 +293,15 @@ __global__ __launch_bounds__(BT_WG_THREADS(TPL)) void k_bt64_w4a4(
     // two consecutive tiles per 16-byte load (one per 8-byte load at TPL 8,
     // where the wider form costs registers)
     constexpr int WPL = TPL >= 8 ? 1 : 2;   // words per load
+    // No select on the offsets (the compiler turns one into branches with a
+    // wait in each): a row past the workgroup's range is past the end of the
+    // buffer and reads zeros, and a tile past the row's end is cleared before
+    // use.
     auto load_words = [&](int i) -> void {
         const int rr = i * BT_ROWS + r;   // row inside the workgroup's range
 #pragma unroll
         for (int k = 0; k < TPL; k += WPL) {
-            const uint32_t off = (rr < wg_rows && t0 + k < T) ? ((uint32_t)rr * (uint32_t)T + (uint32_t)(t0 + k)) * 8u
-                                                              : 0xFFFFFFE0u;
+            const uint32_t off = ((uint32_t)rr * (uint32_t)T + (uint32_t)(t0 + k)) * 8u;
             if constexpr (WPL == 2) {
                 const bt_v4i v = __builtin_bit_cast(bt_v4i, __builtin_amdgcn_raw_buffer_load_b128(brs, off, 0, 0));
                 // a tile past T is cleared where the block is decoded: a select
@@ -545,7 +548,6 @@ __global__ __launch_bounds__(BT_WG_THREADS(TPL)) void k_bt64_w4a4(
 #define BTS_RUN_NIB_LOG2 11      // log2 of the nibbles in a run
 #define BTS_OVL 3u               // granules stored again after each run: a tile's windows reach < 48 B past its start
 #define BTS_DIVMAG 15651u        // ceil(2^20 / (BTS_RUN + BTS_OVL)): exact quotient for slots < 2^14
-#define BTS_AHEAD 1   // blocks whose payload is in flight at once
 
 // Workgroup barrier for LDS traffic only: waits for this wavefront's LDS
 // operations, not for its outstanding global loads and payload DMAs (whose
@@ -561,7 +563,7 @@ template <int NB, int D>
 __global__ __launch_bounds__(512) void k_bt64s_w4a4(
         const uint32_t *__restrict__ offsets, int M, int K, int bq, int br, const uint64_t *__restrict__ bitmaps,
         const uint8_t *__restrict__ X, int N, const uint8_t *__restrict__ payload, uint32_t payload_bytes,
-        int32_t *__restrict__ Y, uint32_t stagger) {
+        int32_t *__restrict__ Y, uint32_t stagger, uint32_t area_kb) {
     constexpr int TPL = 2, NBLK = BTS_NBLK, WC = 8;
     extern __shared__ __attribute__((aligned(16))) uint8_t bt_smem[];
     const int nwaves = blockDim.x >> 6;
@@ -576,12 +578,15 @@ __global__ __launch_bounds__(512) void k_bt64s_w4a4(
     asm volatile("" ::"s"(bitmaps), "s"(payload), "s"(X), "s"(Y), "s"(N), "s"(payload_bytes));
 
     // LDS: selector table | row totals [NBLK][16][WC] | partials
-    // [NBLK][nwaves][NB*256] | staging [NBLK][nwaves*D KB]
+    // [nblk_max][nwaves][NB*256] | staging [nblk_max][area_kb KB]; staging
+    // area i holds block i's payload, 1 KB per DMA instruction, dealt round
+    // robin to the wavefronts (at most D each)
     const uint32_t lut_base = bt_lds_addr(bt_smem) + (uint32_t)(lane % BT_LUT_COPIES) * 8u;
     int32_t *wt = reinterpret_cast<int32_t *>(bt_smem + BT_LUT_BYTES);
     int32_t *part = wt + NBLK * BT_ROWS * WC;
-    uint8_t *stage = reinterpret_cast<uint8_t *>(part + NBLK * nwaves * NB * 256);
-    const uint32_t area = (uint32_t)nwaves * D * 1024u;
+    const int nblk_max = bq + (br > 0 ? 1 : 0);
+    uint8_t *stage = reinterpret_cast<uint8_t *>(part + nblk_max * nwaves * NB * 256);
+    const uint32_t area = area_kb * 1024u;
     // Staggered staging (stagger = 1): the stream is cut in runs of
     // BTS_RUN granules, each stored with the next BTS_OVL granules after it,
     // so every run starts BTS_OVL granules (48 B) further round the LDS banks
@@ -589,7 +594,7 @@ __global__ __launch_bounds__(512) void k_bt64s_w4a4(
     // of 256 B otherwise put the same tile of every row on the same banks.
     // Granule u of the stream sits in slot u + BTS_OVL * (u / BTS_RUN); slot s
     // holds granule s - BTS_OVL * (s / (BTS_RUN + BTS_OVL)).
-    const uint32_t slots = (uint32_t)nwaves * D * 64u;
+    const uint32_t slots = area_kb * 64u;
     const uint32_t cap = stagger ? BTS_RUN * (slots / (BTS_RUN + BTS_OVL)) : slots;   // granules a block's area holds
     const uint32_t kmag = stagger ? BTS_DIVMAG : 0u;             // s * kmag >> 20 = s / (BTS_RUN + BTS_OVL)
     const uint32_t tmul = stagger ? 2u * 16u * BTS_OVL : 0u;     // nibbles added per run
@@ -623,11 +628,13 @@ __global__ __launch_bounds__(512) void k_bt64s_w4a4(
     const int m_first = b_begin * BT_ROWS;
     const int wg_rows = min(nblk * BT_ROWS, M - m_first);
     const __amdgpu_buffer_rsrc_t brs = bt_rsrc(bitmaps + (int64_t)m_first * T, (uint32_t)wg_rows * (uint32_t)T * 8u);
+    // (a row past the workgroup's range is past the end of the buffer and
+    // reads zeros; a tile past the row's end is cleared before use)
     uint64_t words[NBLK][TPL];
 #pragma unroll
     for (int i = 0; i < NBLK; ++i) {
         const int rr = i * BT_ROWS + r;
-        const uint32_t off = (rr < wg_rows && t0 < T) ? ((uint32_t)rr * (uint32_t)T + (uint32_t)t0) * 8u : 0xFFFFFFE0u;
+        const uint32_t off = ((uint32_t)rr * (uint32_t)T + (uint32_t)t0) * 8u;
         const bt_v4i v = __builtin_bit_cast(bt_v4i, __builtin_amdgcn_raw_buffer_load_b128(brs, off, 0, 0));
         words[i][0] = ((uint64_t)(uint32_t)v.y << 32) | (uint32_t)v.x;
         words[i][1] = ((uint64_t)(uint32_t)v.w << 32) | (uint32_t)v.z;
@@ -643,25 +650,24 @@ __global__ __launch_bounds__(512) void k_bt64s_w4a4(
                 xb[nb][k][j] = bt_b_operand(xw[nb][k][2 * j], xw[nb][k][2 * j + 1]);
                 asm volatile("" : "+v"(xb[nb][k][j]));
             }
-    // payload of block i: D instructions per wavefront (a slot past nblk
-    // issues them too, out of range, so every count stays static)
+    // payload of block i < nblk: D instructions per wavefront
     auto issue = [&](int i) -> void {
         const BtRange g = bt_range(nib[i], nib[i + 1]);
-        const uint32_t n = i < nblk ? min(g.n, cap) : 0u;
+        const uint32_t n = min(g.n, cap);
         uint8_t *buf = stage + (uint32_t)i * area;
 #pragma unroll
         for (int d = 0; d < D; ++d) {
             const uint32_t j = (uint32_t)(wave + nwaves * d);
+            if (j >= area_kb) break;   // wave-uniform
             const uint32_t sl = j * 64u + (uint32_t)lane;
             const uint32_t u = sl - BTS_OVL * ((sl * kmag) >> 20);   // stream granule of slot sl
             __builtin_amdgcn_raw_ptr_buffer_load_lds(prs, (bt_lds_void *)(buf + j * 1024u), 16,
                                                      u < n ? (g.g0 + u) * 16u : 0xFFFFFFF0u, 0, 0, 0);
         }
     };
-    // BTS_AHEAD blocks in flight: the memory system serves them before any
-    // later block, which is issued only once block i has landed
-#pragma unroll
-    for (int i = 0; i < BTS_AHEAD && i < NBLK; ++i) issue(i);
+    // one block in flight: the memory system serves it before any later
+    // block, which is issued only once block i has landed
+    issue(0);
     {
         __attribute__((address_space(3))) uint64_t *lut_lds =
                 (__attribute__((address_space(3))) uint64_t *)(uintptr_t)bt_lds_addr(bt_smem);
@@ -693,9 +699,8 @@ __global__ __launch_bounds__(512) void k_bt64s_w4a4(
         }
         int32_t *wti = wt + i * BT_ROWS * WC;
         if (q == 3) wti[r * WC + wave] = (int32_t)incl;
-        // this wavefront's share of block i landed (the blocks issued after it may not have)
-        bt_wait_vm((uint32_t)D * (uint32_t)(min(i + BTS_AHEAD, NBLK) - i - 1));
-        if (i + BTS_AHEAD < NBLK) issue(i + BTS_AHEAD);
+        bt_wait_vm(0);   // this wavefront's share of block i landed (nothing later is in flight)
+        if (i + 1 < nblk) issue(i + 1);
         bt_barrier_lds();                     // ... everyone's, and every row total of block i
         const BtRange g = bt_range(nib[i], nib[i + 1]);
         const int rows = min(BT_ROWS, M - (b_begin + i) * BT_ROWS);
@@ -763,10 +768,11 @@ __global__ __launch_bounds__(512) void k_bt64s_w4a4(
     }
 }
 
-// LDS of the streaming variant with D KB of staging per wavefront and block
-static size_t bts_lds(int nwaves, int nb, int d) {
-    return (size_t)BT_LUT_BYTES + (size_t)BTS_NBLK * BT_ROWS * 8 * 4 + (size_t)BTS_NBLK * nwaves * nb * 256 * 4 +
-           (size_t)BTS_NBLK * nwaves * d * 1024;
+// LDS of the streaming variant: the selector table, and for each of a
+// workgroup's nblk blocks the wavefronts' partials and area_kb KB of staging
+static size_t bts_lds(int nwaves, int nb, int64_t area_kb, int64_t nblk) {
+    return (size_t)BT_LUT_BYTES + (size_t)BTS_NBLK * BT_ROWS * 8 * 4 +
+           (size_t)nblk * ((size_t)nwaves * nb * 256 * 4 + (size_t)area_kb * 1024);
 }
 
 // Launch plan.
@@ -776,8 +782,9 @@ struct BtPlan {
     int bq, br;             // blocks per workgroup: bq, plus one for the first br workgroups
     uint32_t stage_bytes;   // one staging buffer
     uint32_t nbuf;          // staging buffers in the ring
-    int streaming;          // > 0: the streaming variant k_bt64s_w4a4 with this many KB per wavefront and block
+    int streaming;          // > 0: the streaming variant k_bt64s_w4a4, at most this many DMA instructions per wavefront and block
     int stagger;            // streaming variant: staggered staging (rows near a multiple of 256 B long)
+    int area_kb;            // streaming variant: KB of staging per block
     int one_pass;           // every block staged at once: one barrier before and one after the decode
     size_t lds;             // total dynamic LDS
 };
@@ -832,19 +839,24 @@ static bool bt64_plan(int64_t M, int64_t K, int64_t N, int64_t payload_bytes, Bt
     // estimate as the staging buffer above
     p->streaming = 0;
     p->stagger = 0;
-    if (p->tpl == 2 && per_wg <= BTS_NBLK) {
+    if (p->tpl == 2) {
+        // staging per block: the estimate above in whole KB (with 3 extra
+        // granules per 64 when staggered), at least 2 KB per wavefront
         const int64_t est = std::min<int64_t>(worst, avg + avg / 5 + 2048) + 32;
-        const int64_t d = std::min<int64_t>(4, std::max<int64_t>(2, (est + p->nwaves * 1024 - 1) / (p->nwaves * 1024)));
-        const size_t s_lds = bts_lds(p->nwaves, p->nb, (int)d);
-        if ((int64_t)s_lds <= budget) {
-            p->streaming = (int)d;
-            p->lds = s_lds;
-            // average payload bytes per row, modulo the 256 B the LDS banks
-            // span: within 28 B of a multiple, the same tile of consecutive
-            // rows falls on the same banks (elsewhere the plain layout does as
-            // well or better)
-            const int64_t rb = (payload_bytes / std::max<int64_t>(M, 1)) % 256;
-            p->stagger = std::min<int64_t>(rb, 256 - rb) < 28;
+        // average payload bytes per row, modulo the 256 B the LDS banks
+        // span: within 28 B of a multiple, the same tile of consecutive rows
+        // falls on the same banks (elsewhere the plain layout does as well or
+        // better)
+        const int64_t rb = (payload_bytes / std::max<int64_t>(M, 1)) % 256;
+        const int stagger = std::min<int64_t>(rb, 256 - rb) < 28;
+        const int64_t need = (stagger ? est * (BTS_RUN + BTS_OVL) / BTS_RUN : est) + 1023;
+        const int64_t area_kb = std::min<int64_t>(4 * p->nwaves, std::max<int64_t>(2 * p->nwaves, need / 1024));
+        const int d = (int)((area_kb + p->nwaves - 1) / p->nwaves);   // DMA instructions per wavefront at most
+        if (per_wg <= BTS_NBLK && (int64_t)bts_lds(p->nwaves, p->nb, area_kb, per_wg) <= budget) {
+            p->streaming = d;
+            p->area_kb = (int)area_kb;
+            p->stagger = stagger;
+            p->lds = bts_lds(p->nwaves, p->nb, area_kb, per_wg);
         }
     }
     return true;
@@ -869,7 +881,8 @@ static void launch_bt64_w4a4(const BtPlan &p, const uint64_t *bitmaps, const uin
         (void)hipFuncSetAttribute((const void *)k_bt64s_w4a4<NB, D>, hipFuncAttributeMaxDynamicSharedMemorySize, \
                                   (int)p.lds);                                                                    \
         hipLaunchKernelGGL((k_bt64s_w4a4<NB, D>), dim3(p.grid), dim3(64 * p.nwaves), p.lds, stream, offsets, M, K, \
-                           p.bq, p.br, bitmaps, X, N, payload, payload_bytes, Y, (uint32_t)p.stagger);            \
+                           p.bq, p.br, bitmaps, X, N, payload, payload_bytes, Y, (uint32_t)p.stagger,             \
+                           (uint32_t)p.area_kb);                                                                  \
     } while (0)
         if (p.nb == 1) {
             if (p.streaming == 2) BTS_LAUNCH(1, 2); else if (p.streaming == 3) BTS_LAUNCH(1, 3); else BTS_LAUNCH(1, 4);

@@ -90,8 +90,8 @@ extern "C" int bsp_describe_selection(int dtype, int64_t M, int64_t K, int64_t N
             BtPlan p;
             if (bt64_plan(M, K, N, pbytes, &p)) {
                 if (p.streaming)
-                    snprintf(launch, sizeof launch, " kernel=k_bt64s_w4a4 grid=%u block=%d lds=%zu stage_kb_per_wave=%d stagger=%d",
-                             p.grid, 64 * p.nwaves, p.lds, p.streaming, p.stagger);
+                    snprintf(launch, sizeof launch, " kernel=k_bt64s_w4a4 grid=%u block=%d lds=%zu stage_kb=%d stagger=%d",
+                             p.grid, 64 * p.nwaves, p.lds, p.area_kb, p.stagger);
                 else
                     snprintf(launch, sizeof launch, " kernel=k_bt64_w4a4 grid=%u block=%d lds=%zu tiles_per_lane=%d one_pass=%d",
                              p.grid, 64 * p.nwaves, p.lds, p.tpl, p.one_pass);

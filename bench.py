@@ -26,9 +26,11 @@ CPU oracle (plain C, one thread) on a bounded sample of the same workload.
 
 Helper modes used to produce the ``profiles/`` summaries:
 
+    python bench.py --sweep                     # N = 1..32 on the qkv weights, N = 16, 32 at 70 % density
     python bench.py --copy-calibration          # a plain copy of known size
     python bench.py --summarize-trace DIR OUT   # rocprofv3 --kernel-trace --stats csv -> text
     python bench.py --summarize-traffic OUT --fetch DIR --write DIR --copy-fetch DIR --copy-write DIR
+    python bench.py --summarize-counters DIR OUT --kernel FRAGMENT   # rocprofv3 --pmc csv -> text
 """
 from __future__ import annotations
 
@@ -55,6 +57,7 @@ METRIC = "achieved HBM GB/s (frac of peak) + dense-equiv TOPS, bitmap SpMM at N=
 
 # kernel symbol fragment per algorithm, and whether it reads one 4-byte
 # offset per tile (else one per 16-row block)
+SWEEP = [("qkv", 0, n) for n in (1, 2, 4, 8, 16, 32)] + [("lowsparse", 0, 16), ("lowsparse", 0, 32)]
 KERNEL_SYMBOL = {"rowwave": "k_rowwave", "valu": "k_valu", "mfma": "k_bt64"}
 READS_TILE_OFFSETS = {"rowwave": True, "valu": False, "mfma": False}
 
@@ -181,12 +184,19 @@ def _pick(table, fragment):
 
 def summarize_trace(d, out, header):
     rows = _csv_rows(d, "kernel_stats.csv")
+    # per-dispatch durations (end - start) for the percentiles
+    durs = {}
+    for r in _csv_rows(d, "kernel_trace.csv"):
+        durs.setdefault(r["Kernel_Name"], []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
     lines = [f"# {h}" for h in header]
-    lines.append(f"{'kernel':72s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s} {'share%':>7s}")
+    lines.append(f"{'kernel':72s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'p10_us':>9s} {'p50_us':>9s} "
+                 f"{'p90_us':>9s} {'max_us':>9s} {'share%':>7s}")
     for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        v = sorted(durs.get(r["Name"], [float("nan")]))
+        pct = lambda q: v[min(len(v) - 1, int(q * (len(v) - 1) + 0.5))]
         lines.append(f"{r['Name'][:72]:72s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:9.3f} "
-                     f"{float(r['MinNs']) / 1e3:9.3f} {float(r['MaxNs']) / 1e3:9.3f} "
-                     f"{float(r['Percentage']):7.2f}")
+                     f"{float(r['MinNs']) / 1e3:9.3f} {pct(0.1):9.3f} {pct(0.5):9.3f} {pct(0.9):9.3f} "
+                     f"{float(r['MaxNs']) / 1e3:9.3f} {float(r['Percentage']):7.2f}")
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -217,6 +227,24 @@ def summarize_traffic(out, fetch, write, copy_fetch, copy_write, fragment, heade
         f"traffic_bytes_per_launch: {fetch_b + write_b:.0f}",
         f"source_digest: {source_digest()}",
     ]
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def summarize_counters(d, out, fragment, header):
+    """Mean per dispatch of every counter in a rocprofv3 --pmc csv, for the
+    kernel whose name holds `fragment`."""
+    per = {}
+    name = None
+    for r in _csv_rows(d, "counter_collection.csv"):
+        if fragment in r["Kernel_Name"]:
+            name = r["Kernel_Name"]
+            per.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    if name is None:
+        raise SystemExit(f"no dispatch of a kernel matching {fragment!r} under {d}")
+    lines = [f"# {h}" for h in header] + [f"kernel: {name}"]
+    lines += [f"{k}: {sum(v) / len(v):.0f}  (mean of {len(v)} dispatches)" for k, v in sorted(per.items())]
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -258,37 +286,9 @@ def copy_calibration():
 
 # ---------------------------------------------------------------- main
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="qkv", help="tiny | qkv | ffn | lowsparse | fp16")
-    ap.add_argument("--index", type=int, default=0, help="matrix index inside the workload (ffn: 0 up, 1 down)")
-    ap.add_argument("--n", type=int, default=0, help="override N (slices the workload's widest X)")
-    ap.add_argument("--algo", default="auto", choices=["auto", "rowwave", "valu", "mfma"])
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--copy-calibration", action="store_true")
-    ap.add_argument("--summarize-trace", nargs=2, metavar=("DIR", "OUT"))
-    ap.add_argument("--summarize-traffic", metavar="OUT")
-    ap.add_argument("--fetch"), ap.add_argument("--write")
-    ap.add_argument("--copy-fetch"), ap.add_argument("--copy-write")
-    ap.add_argument("--kernel", default="w4a4", help="kernel name fragment for --summarize-traffic")
-    ap.add_argument("--note", action="append", default=[], help="header line for a summary")
-    args = ap.parse_args()
-
-    if args.summarize_trace:
-        return summarize_trace(args.summarize_trace[0], args.summarize_trace[1], args.note)
-    if args.summarize_traffic:
-        return summarize_traffic(args.summarize_traffic, args.fetch, args.write, args.copy_fetch,
-                                 args.copy_write, args.kernel, args.note)
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the path has no "
-              f"multi-GPU code; how it would shard is described with the design.", file=sys.stderr)
-        sys.exit(2)
-    if args.copy_calibration:
-        return copy_calibration()
-
+def measure(args, workload, index, n):
+    """Time one workload (n > 0 slices its widest X to N = n); returns the
+    bench record without the CPU baseline."""
     import numpy as np
     import torch
     import bit_unstructured_sparse_amd as bsp
@@ -296,13 +296,13 @@ def main():
 
     dev = torch.device("cuda:0")
     bsp.load_library()
-    problems = workloads.make(args.workload)
-    problem = problems[args.index]
-    if args.n:
+    problems = workloads.make(workload)
+    problem = problems[index]
+    if n:
         widest = max(problems, key=lambda p: p.N) if problem.dtype == "fp16" else problem
         X = problem.meta.get("X_full", widest.X)
         problem = workloads.Problem(problem.name.rsplit("_n", 1)[0] if problem.dtype == "fp16" else problem.name,
-                                    problem.dtype, problem.W, X[: args.n], dict(problem.meta, N=args.n))
+                                    problem.dtype, problem.W, X[:n], dict(problem.meta, N=n))
     fp16 = problem.dtype == "fp16"
     N, M, K = problem.N, problem.M, problem.K
 
@@ -416,8 +416,59 @@ def main():
                      "kernel": kernel_symbol(bsp, chosen, dt, M, K, N, enc.nnz), "bytes_per_launch": nbytes},
         "parity_sample_ok": parity,
     }
+    args._problem = problem
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="qkv", help="tiny | qkv | ffn | lowsparse | fp16")
+    ap.add_argument("--index", type=int, default=0, help="matrix index inside the workload (ffn: 0 up, 1 down)")
+    ap.add_argument("--n", type=int, default=0, help="override N (slices the workload's widest X)")
+    ap.add_argument("--algo", default="auto", choices=["auto", "rowwave", "valu", "mfma"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep", action="store_true", help="one line per (workload, N) of the N sweep")
+    ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("DIR", "OUT"))
+    ap.add_argument("--summarize-traffic", metavar="OUT")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("DIR", "OUT"))
+    ap.add_argument("--fetch"), ap.add_argument("--write")
+    ap.add_argument("--copy-fetch"), ap.add_argument("--copy-write")
+    ap.add_argument("--kernel", default="w4a4", help="kernel name fragment for --summarize-traffic")
+    ap.add_argument("--note", action="append", default=[], help="header line for a summary")
+    args = ap.parse_args()
+
+    if args.summarize_trace:
+        return summarize_trace(args.summarize_trace[0], args.summarize_trace[1], args.note)
+    if args.summarize_counters:
+        return summarize_counters(args.summarize_counters[0], args.summarize_counters[1], args.kernel, args.note)
+    if args.summarize_traffic:
+        return summarize_traffic(args.summarize_traffic, args.fetch, args.write, args.copy_fetch,
+                                 args.copy_write, args.kernel, args.note)
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the path has no "
+              f"multi-GPU code; how it would shard is described with the design.", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        return copy_calibration()
+
+    if args.sweep:
+        # the N sweep on the qkv weights and the 70 %-dense matrix at N = 16, 32
+        for wl, idx, n in SWEEP:
+            out = measure(args, wl, idx, n)
+            print(json.dumps({"sweep": out["config"]["workload"].split(":")[0], "N": out["config"]["N"],
+                              "kernel": out["roofline"]["kernel"], "kernel_us_avg": out["kernel_us_avg"],
+                              "GB/s (events)": out["roofline"]["achieved"], "GB/s (wall)": out["value"],
+                              "frac_of_peak": out["roofline"]["frac"], "tops_dense_equiv": out["tops_dense_equiv"],
+                              "tops_useful": out["tops_useful"], "parity_sample_ok": out["parity_sample_ok"]}),
+                  flush=True)
+        return
+    out = measure(args, args.workload, args.index, args.n)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(problem, nbytes / M)
+        out["cpu_baseline"] = cpu_baseline(args._problem, out["config"]["bytes_per_step"] / out["config"]["M"])
     print(json.dumps(out), flush=True)
 
 

@@ -311,6 +311,238 @@ __global__ __launch_bounds__(1024) void k_bt64_f16(
     write_y(nblk - 1);
 }
 
+// ---------------------------------------------------------------------------
+// Eight-row steps (N <= 8, K <= 4096). A workgroup walks its rows eight at a
+// time; the payload of eight consecutive rows is one contiguous piece of the
+// stream, so a step's payload can be in flight while the previous step is
+// decoded, also when a workgroup owns a single 16-row block (the fp16
+// configuration here: 4096 rows over 256 CUs). The 16 A rows of an MFMA hold
+// the step's 8 rows twice: lanes r < 8 take row r over the first half of the
+// tiles, lanes r >= 8 row r - 8 over the second half. B column n < 8 carries
+// X column n over the first half, column 8 + n the same X column over the
+// second half, so D[i][n] and D[8 + i][8 + n] are the two halves of row i,
+// column n (the other entries mix halves and are dropped): one MFMA per 8
+// positions, as in the 16-row kernel, with one accumulator. A lane's X tile is
+// the same tile as its A tile.
+//
+// Lane starts: a lane loads the start of its half row from the offsets (one
+// 4-byte load per lane and step) and adds the popcounts of the tiles before
+// its own in that half row: earlier wavefronts through the row totals posted
+// to LDS before the step's barrier, earlier lane groups by lane shuffles.
+//
+// Payload: 1 KB DMA instructions into a staging area of area_kb KB, dealt
+// round robin to the wavefronts; one step in flight (step s + 1 is issued
+// once step s has landed), areas used in a ring of three so that the area a
+// DMA fills was last read two barriers earlier. A step larger than the area
+// reads its windows from global memory.
+#define BF8_NSTEP 4                      // steps per workgroup, at most
+#define BF8_WAVES 8
+
+__global__ __launch_bounds__(512) void k_bt8_f16(
+        const uint32_t *__restrict__ offsets, int M, int K, int sq, int sr, const uint64_t *__restrict__ bitmaps,
+        const uint16_t *__restrict__ X, int N, const uint16_t *__restrict__ payload, uint32_t payload_bytes,
+        uint16_t *__restrict__ Y, uint32_t area_kb) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t bf_smem[];
+    const int nwaves = blockDim.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int r = lane & 15, q = lane >> 4;
+    const int row8 = r & 7, kh = r >> 3;
+    const int T = (K + 63) >> 6, T2 = (T + 1) >> 1;
+    const int tw = wave * 4 + q;                 // tile inside the half row
+    const int t = kh * T2 + tw;                  // this lane's tile (A and X)
+    const bool tile_ok = tw < T2 && t < T;
+    const int gid = (int)blockIdx.x;
+    const int s_begin = gid * sq + min(gid, sr);   // first step (8-row unit) of this workgroup
+    const int nstep = sq + (gid < sr ? 1 : 0);     // 1 .. BF8_NSTEP
+    const int nstep_max = sq + (sr > 0 ? 1 : 0);
+    asm volatile("" ::"s"(bitmaps), "s"(payload), "s"(X), "s"(Y), "s"(N), "s"(payload_bytes), "s"(area_kb));
+
+    // LDS: selector table (128 B) | row totals [BF8_NSTEP][16][8] | partials
+    // [nstep_max][nwaves][256] floats | staging [min(nstep_max, 3)][area_kb KB]
+    uint32_t *lut_lds = reinterpret_cast<uint32_t *>(bf_smem);
+    int32_t *wt = reinterpret_cast<int32_t *>(bf_smem + 128);
+    float *part = reinterpret_cast<float *>(wt + BF8_NSTEP * BF_ROWS * BF8_WAVES);
+    uint8_t *stage = reinterpret_cast<uint8_t *>(part + nstep_max * nwaves * 256);
+    const uint32_t area = area_kb * 1024u;
+    const uint32_t cap = area_kb * 64u;           // granules an area holds
+    const uint32_t lut = bt_lds_addr(lut_lds);
+    const __amdgpu_buffer_rsrc_t prs = bt_rsrc(payload, payload_bytes);
+
+    // step boundaries (wave-uniform scalar loads), ahead of everything
+    uint32_t eb[BF8_NSTEP + 1];
+#pragma unroll
+    for (int i = 0; i <= BF8_NSTEP; ++i) {
+        const int s = s_begin + (i < nstep ? i : nstep);
+        eb[i] = offsets[(int64_t)min(s * 8, M) * T];
+    }
+    asm volatile("" ::: "memory");
+
+    // every step's word and half-row start (rows past M read zeros: past the
+    // end of the buffers; a tile past its half is cleared before use)
+    const int m_first = s_begin * 8;
+    const int wg_rows = max(0, min(nstep * 8, M - m_first));
+    const __amdgpu_buffer_rsrc_t brs = bt_rsrc(bitmaps + (int64_t)m_first * T, (uint32_t)wg_rows * (uint32_t)T * 8u);
+    const __amdgpu_buffer_rsrc_t ors = bt_rsrc(offsets + (int64_t)m_first * T, (uint32_t)wg_rows * (uint32_t)T * 4u);
+    uint64_t words[BF8_NSTEP];
+    uint32_t hs[BF8_NSTEP];
+#pragma unroll
+    for (int i = 0; i < BF8_NSTEP; ++i) {
+        const uint32_t row = (uint32_t)(i * 8 + row8);   // inside the workgroup's range
+        words[i] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(
+                                                        brs, (row * (uint32_t)T + (uint32_t)t) * 8u, 0, 0));
+        hs[i] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(ors, (row * (uint32_t)T + (uint32_t)(kh * T2)) * 4u,
+                                                               0, 0);
+    }
+    // the 16-entry selector table (as in the 16-row kernel)
+    if (threadIdx.x < 16) {
+        const uint32_t m = threadIdx.x;
+        uint32_t sel[2] = {0x0C0C0C0Cu, 0x0C0C0C0Cu};
+#pragma unroll
+        for (int pos = 0; pos < 4; ++pos) {
+            const uint32_t rank = (uint32_t)__builtin_popcount(m & ((1u << pos) - 1u));
+            const uint32_t v = (2u * rank) | ((2u * rank + 1u) << 8);
+            const uint32_t sh = 16u * (uint32_t)(pos & 1);
+            const uint32_t upd = (sel[pos >> 1] & ~(0xFFFFu << sh)) | (v << sh);
+            sel[pos >> 1] = ((m >> pos) & 1u) ? upd : sel[pos >> 1];
+        }
+        lut_lds[2 * m] = sel[0];
+        lut_lds[2 * m + 1] = sel[1];
+    }
+
+    const uint32_t dmax = (area_kb + (uint32_t)nwaves - 1u) / (uint32_t)nwaves;   // DMA instructions per wavefront
+    auto issue = [&](int i) -> void {
+        const BtRange g = bf_range(eb[i], eb[i + 1]);
+        const uint32_t n = min(g.n, cap);
+        uint8_t *buf = stage + (uint32_t)(i % 3) * area;
+        for (uint32_t d = 0; d < dmax; ++d) {
+            const uint32_t j = (uint32_t)wave + (uint32_t)nwaves * d;
+            if (j >= area_kb) break;   // wave-uniform
+            const uint32_t u = j * 64u + (uint32_t)lane;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(prs, (bt_lds_void *)(buf + j * 1024u), 16,
+                                                     u < n ? (g.g0 + u) * 16u : 0xFFFFFFF0u, 0, 0, 0);
+        }
+    };
+    issue(0);
+    bf_h8 xb[1][8];   // X of this lane's tile, loaded behind the first DMA (below)
+
+#pragma unroll
+    for (int i = 0; i < BF8_NSTEP; ++i) {
+        if (i >= nstep) break;
+        const uint64_t word = tile_ok ? words[i] : 0ull;
+        const uint32_t seg = (uint32_t)__builtin_popcountll(word);
+        uint32_t incl = seg;
+        {
+            const uint32_t u16 = (uint32_t)__shfl_up((int)incl, 16, 64);
+            incl += q >= 1 ? u16 : 0u;
+            const uint32_t u32 = (uint32_t)__shfl_up((int)incl, 32, 64);
+            incl += q >= 2 ? u32 : 0u;
+        }
+        int32_t *wti = wt + i * BF_ROWS * BF8_WAVES;
+        if (q == 3) wti[r * BF8_WAVES + wave] = (int32_t)incl;   // this wavefront's total for half row r
+        if (i == 0) {
+            // X of this lane's tile: column r & 7, as the B operands of the
+            // tile's 8 MFMAs (column >= N, a tile past the half or past K:
+            // zeros). Issued after the words and the first DMA so that neither
+            // waits behind it; the decode is the first use.
+            const __amdgpu_buffer_rsrc_t xrs = bt_rsrc(X, (uint32_t)N * (uint32_t)K * 2u);
+            const int n = row8;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const uint32_t k0 = (uint32_t)t * 64u + 8u * j;
+                const uint32_t off = (n < N && tile_ok && k0 < (uint32_t)K) ? ((uint32_t)n * (uint32_t)K + k0) * 2u
+                                                                            : 0xFFFFFFF0u;
+                xb[0][j] = __builtin_bit_cast(bf_h8, __builtin_amdgcn_raw_buffer_load_b128(xrs, off, 0, 0));
+            }
+        }
+        bt_wait_vm(0);   // this wavefront's share of step i landed (nothing later in flight)
+        if (i + 1 < nstep) issue(i + 1);
+        bt_barrier_lds();   // everyone's share, every half-row total of step i
+
+        const BtRange g = bf_range(eb[i], eb[i + 1]);
+        // element index of the lane's first nonzero, counted from the step's first granule
+        uint32_t pstart;
+        {
+            uint32_t pre[BF8_WAVES + 1];
+            pre[0] = 0;
+            const bt_v4i t0v = *(bt_lds_v4i *)(uintptr_t)bt_lds_addr(wti + r * BF8_WAVES);
+            const bt_v4i t1v = *(bt_lds_v4i *)(uintptr_t)bt_lds_addr(wti + r * BF8_WAVES + 4);
+            pre[1] = (uint32_t)t0v.x; pre[2] = pre[1] + (uint32_t)t0v.y;
+            pre[3] = pre[2] + (uint32_t)t0v.z; pre[4] = pre[3] + (uint32_t)t0v.w;
+            pre[5] = pre[4] + (uint32_t)t1v.x; pre[6] = pre[5] + (uint32_t)t1v.y;
+            pre[7] = pre[6] + (uint32_t)t1v.z; pre[8] = pre[7] + (uint32_t)t1v.w;
+            pstart = (hs[i] - (eb[i] & ~7u)) + pre[wave] + (incl - seg);
+        }
+        bf_f4 acc[1] = {bf_f4{0.f, 0.f, 0.f, 0.f}};
+        if (g.n <= cap) {
+            uint32_t p = min(pstart, 2u * (4u * g.n - 3u));   // a corrupt stream stays inside the staged granules
+            p += bt_lds_addr(stage + (uint32_t)(i % 3) * area) >> 1;
+            bf_contract<1>(word, p, BfWinLds{}, lut, xb, acc);
+        } else {
+            bf_contract<1>(word, pstart, BfWinGlobal{prs, 4u * g.g0}, lut, xb, acc);
+        }
+        float *pw = part + (i * nwaves + wave) * 256;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) pw[k * 64 + lane] = acc[0][k];
+    }
+    bt_barrier_lds();
+    // Y: item (step i, row j, column n) adds D[j][n] and D[8 + j][8 + n] of
+    // every wavefront (lanes (j/4)*16 + n and 32 + (j/4)*16 + 8 + n, register
+    // j % 4 in the 16x16 D layout), in wavefront order; one rounding to fp16
+    for (int o = threadIdx.x; o < nstep * 64; o += blockDim.x) {
+        const int i = o >> 6, j = (o >> 3) & 7, n = o & 7;
+        const int m = (s_begin + i) * 8 + j;
+        if (n >= N || m >= M) continue;
+        const int k = j & 3, l1 = (j >> 2) * 16 + n, l2 = 32 + (j >> 2) * 16 + 8 + n;
+        float sum = 0.f;
+        for (int w = 0; w < nwaves; ++w) {
+            const float *pw = part + (i * nwaves + w) * 256 + k * 64;
+            sum += pw[l1];
+            sum += pw[l2];
+        }
+        Y[(int64_t)n * M + m] = __builtin_bit_cast(uint16_t, (_Float16)sum);
+    }
+}
+
+// Plan of the eight-row kernel, or false when it does not apply.
+struct Bf8Plan {
+    int nwaves;
+    unsigned grid;
+    int sq, sr;
+    uint32_t area_kb;
+    size_t lds;
+};
+
+static bool bf8_plan(int64_t M, int64_t K, int64_t N, int64_t payload_bytes, Bf8Plan *p) {
+    if (K <= 0 || K % 8 != 0 || (K + 63) / 64 > 64 || N < 1 || N > 8 || M <= 0) return false;
+    const int64_t T = (K + 63) / 64, T2 = (T + 1) / 2;
+    p->nwaves = (int)((T2 + 3) / 4);
+    const int64_t steps = (M + 7) / 8;
+    // two steps per workgroup at least (the second streams in while the
+    // first decodes), one workgroup per CU, at most BF8_NSTEP steps each
+    const int64_t grid = std::max<int64_t>(std::min<int64_t>((steps + 1) / 2, BF_CUS), (steps + BF8_NSTEP - 1) / BF8_NSTEP);
+    p->grid = (unsigned)grid;
+    p->sq = (int)(steps / grid);
+    p->sr = (int)(steps % grid);
+    const int64_t per_wg = (steps + grid - 1) / grid;
+    // staging per step: 1.2x the average step plus 2 KB, in KB (a larger
+    // step reads its windows from global memory), capped at a dense step
+    const int64_t avg = payload_bytes / std::max<int64_t>(steps, 1);
+    const int64_t worst = 8 * T * 128 + 64;
+    const int64_t est = std::min<int64_t>(worst, avg + avg / 5 + 2048) + 32;
+    p->area_kb = (uint32_t)std::max<int64_t>(1, (est + 1023) / 1024);
+    p->lds = 128 + (size_t)BF8_NSTEP * BF_ROWS * BF8_WAVES * 4 + (size_t)per_wg * p->nwaves * 256 * 4 +
+             (size_t)std::min<int64_t>(per_wg, 3) * p->area_kb * 1024;
+    return p->lds <= (size_t)BF_LDS_MAX;
+}
+
+static void launch_bt8_f16(const Bf8Plan &p, const uint64_t *bitmaps, const uint32_t *offsets,
+                           const uint16_t *payload, uint32_t payload_bytes, int M, int K, const uint16_t *X, int N,
+                           uint16_t *Y, hipStream_t stream) {
+    (void)hipFuncSetAttribute((const void *)k_bt8_f16, hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds);
+    hipLaunchKernelGGL(k_bt8_f16, dim3(p.grid), dim3(64 * p.nwaves), p.lds, stream, offsets, M, K, p.sq, p.sr,
+                       bitmaps, X, N, payload, payload_bytes, Y, p.area_kb);
+}
+
 struct BfPlan {
     int nwaves, nb;
     unsigned grid;

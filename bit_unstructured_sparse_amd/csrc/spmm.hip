@@ -97,8 +97,12 @@ extern "C" int bsp_describe_selection(int dtype, int64_t M, int64_t K, int64_t N
                              p.grid, 64 * p.nwaves, p.lds, p.tpl, p.one_pass);
             }
         } else {
+            Bf8Plan p8;
             BfPlan p;
-            if (bf_plan(M, K, N, pbytes, &p))
+            if (bf8_plan(M, K, N, pbytes, &p8))
+                snprintf(launch, sizeof launch, " kernel=k_bt8_f16 grid=%u block=%d lds=%zu stage_kb=%u", p8.grid,
+                         64 * p8.nwaves, p8.lds, p8.area_kb);
+            else if (bf_plan(M, K, N, pbytes, &p))
                 snprintf(launch, sizeof launch, " kernel=k_bt64_f16 grid=%u block=%d lds=%zu", p.grid, 64 * p.nwaves,
                          p.lds);
         }
@@ -155,6 +159,12 @@ extern "C" int spmm_bitmap_f16_algo(const uint64_t *bitmaps, const uint32_t *off
     if (!algo_supported(algo, BSP_FP16, s)) algo = BSP_ALGO_ROWWAVE;
     switch (algo) {
         case BSP_ALGO_MFMA: {
+            Bf8Plan plan8;
+            if (bf8_plan(M, K, N, payload_bytes, &plan8)) {
+                launch_bt8_f16(plan8, bitmaps, offsets, payload, (uint32_t)payload_bytes, (int)M, (int)K, X, (int)N, Y,
+                               stream);
+                break;
+            }
             BfPlan plan;
             if (bf_plan(M, K, N, payload_bytes, &plan)) {
                 launch_bt64_f16(plan, bitmaps, offsets, payload, (uint32_t)payload_bytes, (int)M, (int)K, X, (int)N,

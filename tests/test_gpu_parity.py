@@ -218,6 +218,29 @@ def test_f16_uneven_block_density(dev, algo, dense_block):
 
 
 @pytest.mark.parametrize("algo", F16_ALGOS, ids=lambda a: _NAMES[a])
+@pytest.mark.parametrize("M,K,N,dense_rows", [(8003, 1000, 5, -1),   # 4 steps per workgroup: the ring wraps
+                                              (4096, 4096, 1, -1), (4099, 4088, 8, -1), (1000, 2048, 7, 3),
+                                              (77, 520, 2, 9), (9, 4096, 1, 0), (2048, 64, 6, -1)])
+def test_f16_eight_row_steps(dev, algo, M, K, N, dense_rows):
+    # N <= 8 and K <= 4096: the kernel that walks rows eight at a time (one
+    # step in flight, MFMA rows 8-15 holding the second half of K); ragged M
+    # and K, every step count per workgroup up to four, and an optional dense
+    # group of 8 rows that overflows its staging area (global-window path)
+    rng = np.random.default_rng(M + K + N)
+    W = rng.normal(0, 0.02, size=(M, K)).astype(np.float16)
+    keep = rng.random((M, K)) < 0.4
+    if dense_rows >= 0:
+        keep[8 * dense_rows: 8 * dense_rows + 8] = True
+    W = np.where(keep, W, np.float16(0))
+    X = rng.normal(0, 1, size=(N, K)).astype(np.float16)
+    enc = bsp.encode(W)
+    if algo == bsp.ALGO_MFMA:
+        assert "kernel=k_bt8_f16" in bsp.describe(bsp.FP16, M, K, N, enc.nnz)
+    y = run_f16(W, X, algo, dev, enc=enc).astype(np.float64)
+    _assert_f16(y, oracle.spmm_f16(oracle.encode(W), X))
+
+
+@pytest.mark.parametrize("algo", F16_ALGOS, ids=lambda a: _NAMES[a])
 def test_f16_zero_and_dense(dev, algo):
     W = np.zeros((33, 100), np.float16)
     X = np.ones((2, 100), np.float16)

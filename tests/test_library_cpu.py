@@ -158,6 +158,8 @@ def test_description_names_the_launched_kernel():
     d = bsp.describe(bsp.INT4, 4096, 11008, 16, 4096 * 11008 * 3 // 10)
     assert "-> mfma kernel=k_bt64_w4a4 " in d and "tiles_per_lane=8" in d
     d = bsp.describe(bsp.FP16, 4096, 4096, 1, 4096 * 4096 * 4 // 10)
+    assert "-> mfma kernel=k_bt8_f16 " in d and "grid=256 block=512" in d
+    d = bsp.describe(bsp.FP16, 4096, 4096, 32, 4096 * 4096 * 4 // 10)
     assert "-> mfma kernel=k_bt64_f16 " in d and "block=1024" in d
     # K not a multiple of 32: outside the fast path
     assert bsp.describe(bsp.INT4, 64, 100, 4).endswith("-> rowwave kernel=k_rowwave_w4a4")

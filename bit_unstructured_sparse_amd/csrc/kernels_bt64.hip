@@ -536,13 +536,13 @@ __global__ __launch_bounds__(BT_WG_THREADS(TPL)) void k_bt64_w4a4(
 // block, a fixed count, so the vector-memory counter tells exactly when block
 // i has landed; granules past the block read as zeros. A block with more
 // granules than the D KB per wavefront hold is decoded from global memory
-// instead. Only BTS_AHEAD blocks are in flight at a time: block i + BTS_AHEAD
-// is issued once block i has landed, so the memory system delivers the blocks
-// in order (with every block in flight at once they all land together) and
-// block i is decoded while the next one streams in. Per block: words -> row
-// totals -> wait for its payload -> barrier -> decode into a per-wavefront
-// partial slice. The barrier is an LDS-only one, so it never waits for the
-// later blocks' transfers.
+// instead. One block is in flight at a time: block i + 1 (its payload, then
+// its bitmap words) is issued once block i has landed, so the memory system
+// delivers the blocks in order (with two or more in flight each lands later)
+// and block i is decoded while the next one streams in. Per block: words ->
+// row totals -> wait for its payload -> barrier -> decode into a
+// per-wavefront partial slice. The barrier is an LDS-only one, so it never
+// waits for the later blocks' transfers.
 #define BTS_NBLK 3
 #define BTS_RUN 64u              // granules per run of the staggered staging (1 KB)
 #define BTS_RUN_NIB_LOG2 11      // log2 of the nibbles in a run
@@ -664,21 +664,23 @@ __global__ __launch_bounds__(512) void k_bt64s_w4a4(
                 xw[nb][k][4] = v1.x; xw[nb][k][5] = v1.y; xw[nb][k][6] = v1.z; xw[nb][k][7] = v1.w;
             }
     }
-    // every block's words (a slot past nblk, a row past M or a tile past T reads zeros)
+    // bitmap words: block 0's now; block i + 1's are issued behind its DMA
+    // (below), so that the first payload does not queue behind every
+    // block's words (a row past M or past the workgroup's range is past the
+    // end of the buffer and reads zeros; a tile past the row's end is
+    // cleared before use)
     const int m_first = b_begin * BT_ROWS;
     const int wg_rows = min(nblk * BT_ROWS, M - m_first);
     const __amdgpu_buffer_rsrc_t brs = bt_rsrc(bitmaps + (int64_t)m_first * T, (uint32_t)wg_rows * (uint32_t)T * 8u);
-    // (a row past the workgroup's range is past the end of the buffer and
-    // reads zeros; a tile past the row's end is cleared before use)
     uint64_t words[NBLK][TPL];
-#pragma unroll
-    for (int i = 0; i < NBLK; ++i) {
+    auto load_words = [&](int i) -> void {
         const int rr = i * BT_ROWS + r;
         const uint32_t off = ((uint32_t)rr * (uint32_t)T + (uint32_t)t0) * 8u;
         const bt_v4i v = __builtin_bit_cast(bt_v4i, __builtin_amdgcn_raw_buffer_load_b128(brs, off, 0, 0));
         words[i][0] = ((uint64_t)(uint32_t)v.y << 32) | (uint32_t)v.x;
         words[i][1] = ((uint64_t)(uint32_t)v.w << 32) | (uint32_t)v.z;
-    }
+    };
+    load_words(0);
     // B operands (waits for X only: the words were issued after it)
     bt_v4i xb[NB][TPL][4];
     if constexpr (!x_late)
@@ -743,7 +745,10 @@ __global__ __launch_bounds__(512) void k_bt64s_w4a4(
         int32_t *wti = wt + i * BT_ROWS * WC;
         if (q == 3) wti[r * WC + wave] = (int32_t)incl;
         bt_wait_vm(0);   // this wavefront's share of block i landed (nothing later is in flight)
-        if (i + 1 < nblk) issue(i + 1);
+        if (i + 1 < nblk) {
+            issue(i + 1);
+            if (i + 1 < NBLK) load_words(i + 1);   // needed after block i + 1 lands
+        }
         if constexpr (x_late)
             if (i == 0) bt_make_b<NB, TPL>(xw, xb);
         bt_barrier_lds();                     // ... everyone's, and every row total of block i

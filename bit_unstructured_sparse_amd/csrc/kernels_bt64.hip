@@ -559,25 +559,6 @@ __device__ __forceinline__ void bt_barrier_lds() {
     asm volatile("" ::: "memory");
 }
 
-// X slices of a lane's TPL tiles for NB column blocks of 16 (zeros past N or
-// the row's T tiles): 32 bytes of column r + 16 nb at tile t0 + k
-template <int NB, int TPL>
-__device__ __forceinline__ void bt_load_x(const uint8_t *X, int N, uint32_t xs, int r, int t0, int T,
-                                          uint32_t (&xw)[NB][TPL][8]) {
-    const __amdgpu_buffer_rsrc_t xrs = bt_rsrc(X, (uint32_t)N * xs);
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int k = 0; k < TPL; ++k) {
-            const int n = r + 16 * nb;
-            const uint32_t off = (n < N && t0 + k < T) ? (uint32_t)n * xs + (uint32_t)(t0 + k) * 32u : 0xFFFFFFE0u;
-            const bt_v4i v0 = __builtin_bit_cast(bt_v4i, __builtin_amdgcn_raw_buffer_load_b128(xrs, off, 0, 0));
-            const bt_v4i v1 = __builtin_bit_cast(bt_v4i, __builtin_amdgcn_raw_buffer_load_b128(xrs, off + 16u, 0, 0));
-            xw[nb][k][0] = v0.x; xw[nb][k][1] = v0.y; xw[nb][k][2] = v0.z; xw[nb][k][3] = v0.w;
-            xw[nb][k][4] = v1.x; xw[nb][k][5] = v1.y; xw[nb][k][6] = v1.z; xw[nb][k][7] = v1.w;
-        }
-}
-
 // B operands of the lane's tiles from their X slices
 template <int NB, int TPL>
 __device__ __forceinline__ void bt_make_b(const uint32_t (&xw)[NB][TPL][8], bt_v4i (&xb)[NB][TPL][4]) {
@@ -641,16 +622,12 @@ __global__ __launch_bounds__(512) void k_bt64s_w4a4(
     }
     asm volatile("" ::: "memory");
 
-    // X slices of the lane's tiles (zeros past N or T) and the B operands
-    // made from them. One column block of X is small and is loaded here,
-    // ahead of the words; two (64 KB a workgroup at K = 4096) are issued
-    // behind the first payload DMA, which would otherwise wait for them, and
-    // become B operands once block 0 has landed. (The one-block path keeps
-    // its loads written out in place: through the helpers the compiler
-    // schedules that kernel differently, and it measured slower.)
-    constexpr bool x_late = NB >= 2;
+    // X slices of the lane's tiles (zeros past N or T), loaded first; they
+    // become B operands only once block 0 has landed, so that the first
+    // payload DMA goes out as soon as the block offsets are in (waiting for
+    // X first held it back by about half a microsecond)
     uint32_t xw[NB][TPL][8];
-    if constexpr (!x_late) {
+    {
         const __amdgpu_buffer_rsrc_t xrs = bt_rsrc(X, (uint32_t)N * xs);
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
@@ -681,18 +658,7 @@ __global__ __launch_bounds__(512) void k_bt64s_w4a4(
         words[i][1] = ((uint64_t)(uint32_t)v.w << 32) | (uint32_t)v.z;
     };
     load_words(0);
-    // B operands (waits for X only: the words were issued after it)
-    bt_v4i xb[NB][TPL][4];
-    if constexpr (!x_late)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-            for (int k = 0; k < TPL; ++k)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    xb[nb][k][j] = bt_b_operand(xw[nb][k][2 * j], xw[nb][k][2 * j + 1]);
-                    asm volatile("" : "+v"(xb[nb][k][j]));
-                }
+    bt_v4i xb[NB][TPL][4];   // B operands, made from xw once block 0 has landed
     // payload of block i < nblk: D instructions per wavefront
     auto issue = [&](int i) -> void {
         const BtRange g = bt_range(nib[i], nib[i + 1]);
@@ -723,8 +689,6 @@ __global__ __launch_bounds__(512) void k_bt64s_w4a4(
         }
     }
 
-    if constexpr (x_late) bt_load_x<NB, TPL>(X, N, xs, r, t0, T, xw);
-
 #pragma unroll
     for (int i = 0; i < NBLK; ++i) {
         if (i >= nblk) break;
@@ -749,8 +713,7 @@ __global__ __launch_bounds__(512) void k_bt64s_w4a4(
             issue(i + 1);
             if (i + 1 < NBLK) load_words(i + 1);   // needed after block i + 1 lands
         }
-        if constexpr (x_late)
-            if (i == 0) bt_make_b<NB, TPL>(xw, xb);
+        if (i == 0) bt_make_b<NB, TPL>(xw, xb);   // X landed with block 0 (waited above)
         bt_barrier_lds();                     // ... everyone's, and every row total of block i
         const BtRange g = bt_range(nib[i], nib[i + 1]);
         const int rows = min(BT_ROWS, M - (b_begin + i) * BT_ROWS);

@@ -592,9 +592,9 @@ __global__ __launch_bounds__(512) void k_bt64s_w4a4(
     asm volatile("" ::"s"(bitmaps), "s"(payload), "s"(X), "s"(Y), "s"(N), "s"(payload_bytes));
 
     // LDS: selector table | row totals [NBLK][16][WC] | partials
-    // [nblk_max][nwaves][NB*256] | staging [nblk_max][area_kb KB]; staging
-    // area i holds block i's payload, 1 KB per DMA instruction, dealt round
-    // robin to the wavefronts (at most D each)
+    // [nblk_max][nwaves][NB*256] | staging [nblk_max][area_kb KB] | 1 KB
+    // dummy; staging area i holds block i's payload, 1 KB per DMA
+    // instruction, dealt round robin to the wavefronts (D each)
     const uint32_t lut_base = bt_lds_addr(bt_smem) + (uint32_t)(lane % BT_LUT_COPIES) * 8u;
     int32_t *wt = reinterpret_cast<int32_t *>(bt_smem + BT_LUT_BYTES);
     int32_t *part = wt + NBLK * BT_ROWS * WC;
@@ -660,18 +660,26 @@ __global__ __launch_bounds__(512) void k_bt64s_w4a4(
     load_words(0);
     bt_v4i xb[NB][TPL][4];   // B operands, made from xw once block 0 has landed
     // payload of block i < nblk: D instructions per wavefront
+    // Every wavefront issues exactly D instructions per block, also for KB
+    // past the area: those write zeros into a 1 KB dummy slot behind the
+    // staging areas. With a fixed count in straight-line code the compiler's
+    // own waits are exact (block 0's words are used before its payload has
+    // landed); with a count that depends on the wavefront it waits for
+    // everything in flight.
+    uint8_t *dummy = stage + (uint32_t)nblk_max * area;
     auto issue = [&](int i) -> void {
+        const bool blk = i < nblk;
         const BtRange g = bt_range(nib[i], nib[i + 1]);
-        const uint32_t n = min(g.n, cap);
+        const uint32_t n = blk ? min(g.n, cap) : 0u;
         uint8_t *buf = stage + (uint32_t)i * area;
 #pragma unroll
         for (int d = 0; d < D; ++d) {
             const uint32_t j = (uint32_t)(wave + nwaves * d);
-            if (j >= area_kb) break;   // wave-uniform
+            const bool real = blk && j < area_kb;   // wave-uniform
             const uint32_t sl = j * 64u + (uint32_t)lane;
             const uint32_t u = sl - BTS_OVL * ((sl * kmag) >> 20);   // stream granule of slot sl
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(prs, (bt_lds_void *)(buf + j * 1024u), 16,
-                                                     u < n ? (g.g0 + u) * 16u : 0xFFFFFFF0u, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(prs, (bt_lds_void *)(real ? buf + j * 1024u : dummy), 16,
+                                                     (real && u < n) ? (g.g0 + u) * 16u : 0xFFFFFFF0u, 0, 0, 0);
         }
     };
     // one block in flight: the memory system serves it before any later
@@ -711,7 +719,7 @@ __global__ __launch_bounds__(512) void k_bt64s_w4a4(
         bt_wait_vm(0);   // this wavefront's share of block i landed (nothing later is in flight)
         if (i + 1 < nblk) {
             issue(i + 1);
-            if (i + 1 < NBLK) load_words(i + 1);   // needed after block i + 1 lands
+            load_words(i + 1);   // needed after block i + 1 lands
         }
         if (i == 0) bt_make_b<NB, TPL>(xw, xb);   // X landed with block 0 (waited above)
         bt_barrier_lds();                     // ... everyone's, and every row total of block i
@@ -781,11 +789,12 @@ __global__ __launch_bounds__(512) void k_bt64s_w4a4(
     }
 }
 
-// LDS of the streaming variant: the selector table, and for each of a
-// workgroup's nblk blocks the wavefronts' partials and area_kb KB of staging
+// LDS of the streaming variant: the selector table, the row totals, for each
+// of a workgroup's nblk blocks the wavefronts' partials and area_kb KB of
+// staging, and the 1 KB dummy slot of the unused DMA instructions
 static size_t bts_lds(int nwaves, int nb, int64_t area_kb, int64_t nblk) {
     return (size_t)BT_LUT_BYTES + (size_t)BTS_NBLK * BT_ROWS * 8 * 4 +
-           (size_t)nblk * ((size_t)nwaves * nb * 256 * 4 + (size_t)area_kb * 1024);
+           (size_t)nblk * ((size_t)nwaves * nb * 256 * 4 + (size_t)area_kb * 1024) + 1024;
 }
 
 // Launch plan.

@@ -536,8 +536,8 @@ __global__ __launch_bounds__(BT_WG_THREADS(TPL)) void k_bt64_w4a4(
 // block, a fixed count, so the vector-memory counter tells exactly when block
 // i has landed; granules past the block read as zeros. A block with more
 // granules than the D KB per wavefront hold is decoded from global memory
-// instead. One block is in flight at a time: block i + 1 (its payload, then
-// its bitmap words) is issued once block i has landed, so the memory system
+// instead. One block is in flight at a time: block i + 1 (its bitmap words,
+// then its payload) is issued once block i has landed, so the memory system
 // delivers the blocks in order (with two or more in flight each lands later)
 // and block i is decoded while the next one streams in. Per block: words ->
 // row totals -> wait for its payload -> barrier -> decode into a
@@ -641,9 +641,8 @@ __global__ __launch_bounds__(512) void k_bt64s_w4a4(
                 xw[nb][k][4] = v1.x; xw[nb][k][5] = v1.y; xw[nb][k][6] = v1.z; xw[nb][k][7] = v1.w;
             }
     }
-    // bitmap words: block 0's now; block i + 1's are issued behind its DMA
-    // (below), so that the first payload does not queue behind every
-    // block's words (a row past M or past the workgroup's range is past the
+    // bitmap words: block 0's now, block i + 1's with its DMA (below), so
+    // that the first payload does not queue behind every block's words (a row past M or past the workgroup's range is past the
     // end of the buffer and reads zeros; a tile past the row's end is
     // cleared before use)
     const int m_first = b_begin * BT_ROWS;
@@ -718,8 +717,8 @@ __global__ __launch_bounds__(512) void k_bt64s_w4a4(
         if (q == 3) wti[r * WC + wave] = (int32_t)incl;
         bt_wait_vm(0);   // this wavefront's share of block i landed (nothing later is in flight)
         if (i + 1 < nblk) {
+            load_words(i + 1);   // ahead of its payload: block i + 1's row totals need no wait for it
             issue(i + 1);
-            load_words(i + 1);   // needed after block i + 1 lands
         }
         if (i == 0) bt_make_b<NB, TPL>(xw, xb);   // X landed with block 0 (waited above)
         bt_barrier_lds();                     // ... everyone's, and every row total of block i

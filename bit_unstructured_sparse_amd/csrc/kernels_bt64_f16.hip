@@ -335,9 +335,10 @@ __global__ __launch_bounds__(1024) void k_bt64_f16(
 // once step s has landed), areas used in a ring of three so that the area a
 // DMA fills was last read two barriers earlier. A step larger than the area
 // reads its windows from global memory.
-#define BF8_NSTEP 4                      // steps per workgroup, at most
+#define BF8_NSTEP_MAX 4                  // steps per workgroup, at most (NSTEP 2 or 4)
 #define BF8_WAVES 8
 
+template <int NSTEP>
 __global__ __launch_bounds__(512) void k_bt8_f16(
         const uint32_t *__restrict__ offsets, int M, int K, int sq, int sr, const uint64_t *__restrict__ bitmaps,
         const uint16_t *__restrict__ X, int N, const uint16_t *__restrict__ payload, uint32_t payload_bytes,
@@ -353,15 +354,15 @@ __global__ __launch_bounds__(512) void k_bt8_f16(
     const bool tile_ok = tw < T2 && t < T;
     const int gid = (int)blockIdx.x;
     const int s_begin = gid * sq + min(gid, sr);   // first step (8-row unit) of this workgroup
-    const int nstep = sq + (gid < sr ? 1 : 0);     // 1 .. BF8_NSTEP
+    const int nstep = sq + (gid < sr ? 1 : 0);     // 1 .. NSTEP
     const int nstep_max = sq + (sr > 0 ? 1 : 0);
     asm volatile("" ::"s"(bitmaps), "s"(payload), "s"(X), "s"(Y), "s"(N), "s"(payload_bytes), "s"(area_kb));
 
-    // LDS: selector table (128 B) | row totals [BF8_NSTEP][16][8] | partials
+    // LDS: selector table (128 B) | row totals [NSTEP][16][8] | partials
     // [nstep_max][nwaves][256] floats | staging [min(nstep_max, 3)][area_kb KB]
     uint32_t *lut_lds = reinterpret_cast<uint32_t *>(bf_smem);
     int32_t *wt = reinterpret_cast<int32_t *>(bf_smem + 128);
-    float *part = reinterpret_cast<float *>(wt + BF8_NSTEP * BF_ROWS * BF8_WAVES);
+    float *part = reinterpret_cast<float *>(wt + NSTEP * BF_ROWS * BF8_WAVES);
     uint8_t *stage = reinterpret_cast<uint8_t *>(part + nstep_max * nwaves * 256);
     const uint32_t area = area_kb * 1024u;
     const uint32_t cap = area_kb * 64u;           // granules an area holds
@@ -369,9 +370,9 @@ __global__ __launch_bounds__(512) void k_bt8_f16(
     const __amdgpu_buffer_rsrc_t prs = bt_rsrc(payload, payload_bytes);
 
     // step boundaries (wave-uniform scalar loads), ahead of everything
-    uint32_t eb[BF8_NSTEP + 1];
+    uint32_t eb[NSTEP + 1];
 #pragma unroll
-    for (int i = 0; i <= BF8_NSTEP; ++i) {
+    for (int i = 0; i <= NSTEP; ++i) {
         const int s = s_begin + (i < nstep ? i : nstep);
         eb[i] = offsets[(int64_t)min(s * 8, M) * T];
     }
@@ -383,10 +384,10 @@ __global__ __launch_bounds__(512) void k_bt8_f16(
     const int wg_rows = max(0, min(nstep * 8, M - m_first));
     const __amdgpu_buffer_rsrc_t brs = bt_rsrc(bitmaps + (int64_t)m_first * T, (uint32_t)wg_rows * (uint32_t)T * 8u);
     const __amdgpu_buffer_rsrc_t ors = bt_rsrc(offsets + (int64_t)m_first * T, (uint32_t)wg_rows * (uint32_t)T * 4u);
-    uint64_t words[BF8_NSTEP];
-    uint32_t hs[BF8_NSTEP];
+    uint64_t words[NSTEP];
+    uint32_t hs[NSTEP];
 #pragma unroll
-    for (int i = 0; i < BF8_NSTEP; ++i) {
+    for (int i = 0; i < NSTEP; ++i) {
         const uint32_t row = (uint32_t)(i * 8 + row8);   // inside the workgroup's range
         words[i] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(
                                                         brs, (row * (uint32_t)T + (uint32_t)t) * 8u, 0, 0));
@@ -426,7 +427,7 @@ __global__ __launch_bounds__(512) void k_bt8_f16(
     bf_h8 xb[1][8];   // X of this lane's tile, loaded behind the first DMA (below)
 
 #pragma unroll
-    for (int i = 0; i < BF8_NSTEP; ++i) {
+    for (int i = 0; i < NSTEP; ++i) {
         if (i >= nstep) break;
         const uint64_t word = tile_ok ? words[i] : 0ull;
         const uint32_t seg = (uint32_t)__builtin_popcountll(word);
@@ -506,6 +507,7 @@ __global__ __launch_bounds__(512) void k_bt8_f16(
 // Plan of the eight-row kernel, or false when it does not apply.
 struct Bf8Plan {
     int nwaves;
+    int nstep;   // step slots per workgroup (2 or 4), a template argument
     unsigned grid;
     int sq, sr;
     uint32_t area_kb;
@@ -518,8 +520,11 @@ static bool bf8_plan(int64_t M, int64_t K, int64_t N, int64_t payload_bytes, Bf8
     p->nwaves = (int)((T2 + 3) / 4);
     const int64_t steps = (M + 7) / 8;
     // two steps per workgroup at least (the second streams in while the
-    // first decodes), one workgroup per CU, at most BF8_NSTEP steps each
-    const int64_t grid = std::max<int64_t>(std::min<int64_t>((steps + 1) / 2, BF_CUS), (steps + BF8_NSTEP - 1) / BF8_NSTEP);
+    // first decodes), one workgroup per CU, at most BF8_NSTEP_MAX steps each;
+    // two step slots when that suffices (the prologue loads every slot's
+    // words: fewer loads ahead of the first DMA)
+    const int64_t grid = std::max<int64_t>(std::min<int64_t>((steps + 1) / 2, BF_CUS), (steps + BF8_NSTEP_MAX - 1) / BF8_NSTEP_MAX);
+    p->nstep = (steps + grid - 1) / grid <= 2 ? 2 : BF8_NSTEP_MAX;
     p->grid = (unsigned)grid;
     p->sq = (int)(steps / grid);
     p->sr = (int)(steps % grid);
@@ -530,7 +535,7 @@ static bool bf8_plan(int64_t M, int64_t K, int64_t N, int64_t payload_bytes, Bf8
     const int64_t worst = 8 * T * 128 + 64;
     const int64_t est = std::min<int64_t>(worst, avg + avg / 5 + 2048) + 32;
     p->area_kb = (uint32_t)std::max<int64_t>(1, (est + 1023) / 1024);
-    p->lds = 128 + (size_t)BF8_NSTEP * BF_ROWS * BF8_WAVES * 4 + (size_t)per_wg * p->nwaves * 256 * 4 +
+    p->lds = 128 + (size_t)p->nstep * BF_ROWS * BF8_WAVES * 4 + (size_t)per_wg * p->nwaves * 256 * 4 +
              (size_t)std::min<int64_t>(per_wg, 3) * p->area_kb * 1024;
     return p->lds <= (size_t)BF_LDS_MAX;
 }
@@ -538,9 +543,14 @@ static bool bf8_plan(int64_t M, int64_t K, int64_t N, int64_t payload_bytes, Bf8
 static void launch_bt8_f16(const Bf8Plan &p, const uint64_t *bitmaps, const uint32_t *offsets,
                            const uint16_t *payload, uint32_t payload_bytes, int M, int K, const uint16_t *X, int N,
                            uint16_t *Y, hipStream_t stream) {
-    (void)hipFuncSetAttribute((const void *)k_bt8_f16, hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds);
-    hipLaunchKernelGGL(k_bt8_f16, dim3(p.grid), dim3(64 * p.nwaves), p.lds, stream, offsets, M, K, p.sq, p.sr,
-                       bitmaps, X, N, payload, payload_bytes, Y, p.area_kb);
+    const void *fn = p.nstep == 2 ? (const void *)k_bt8_f16<2> : (const void *)k_bt8_f16<BF8_NSTEP_MAX>;
+    (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds);
+    if (p.nstep == 2)
+        hipLaunchKernelGGL(k_bt8_f16<2>, dim3(p.grid), dim3(64 * p.nwaves), p.lds, stream, offsets, M, K, p.sq, p.sr,
+                           bitmaps, X, N, payload, payload_bytes, Y, p.area_kb);
+    else
+        hipLaunchKernelGGL(k_bt8_f16<BF8_NSTEP_MAX>, dim3(p.grid), dim3(64 * p.nwaves), p.lds, stream, offsets, M, K,
+                           p.sq, p.sr, bitmaps, X, N, payload, payload_bytes, Y, p.area_kb);
 }
 
 struct BfPlan {

@@ -100,8 +100,8 @@ extern "C" int bsp_describe_selection(int dtype, int64_t M, int64_t K, int64_t N
             Bf8Plan p8;
             BfPlan p;
             if (bf8_plan(M, K, N, pbytes, &p8))
-                snprintf(launch, sizeof launch, " kernel=k_bt8_f16 grid=%u block=%d lds=%zu stage_kb=%u", p8.grid,
-                         64 * p8.nwaves, p8.lds, p8.area_kb);
+                snprintf(launch, sizeof launch, " kernel=k_bt8_f16 grid=%u block=%d lds=%zu stage_kb=%u step_slots=%d",
+                         p8.grid, 64 * p8.nwaves, p8.lds, p8.area_kb, p8.nstep);
             else if (bf_plan(M, K, N, pbytes, &p))
                 snprintf(launch, sizeof launch, " kernel=k_bt64_f16 grid=%u block=%d lds=%zu", p.grid, 64 * p.nwaves,
                          p.lds);

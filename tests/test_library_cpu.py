@@ -158,7 +158,9 @@ def test_description_names_the_launched_kernel():
     d = bsp.describe(bsp.INT4, 4096, 11008, 16, 4096 * 11008 * 3 // 10)
     assert "-> mfma kernel=k_bt64_w4a4 " in d and "tiles_per_lane=8" in d
     d = bsp.describe(bsp.FP16, 4096, 4096, 1, 4096 * 4096 * 4 // 10)
-    assert "-> mfma kernel=k_bt8_f16 " in d and "grid=256 block=512" in d
+    assert "-> mfma kernel=k_bt8_f16 " in d and "grid=256 block=512" in d and "step_slots=2" in d
+    d = bsp.describe(bsp.FP16, 8003, 1000, 5, 8003 * 1000 // 10)   # four steps per workgroup
+    assert "-> mfma kernel=k_bt8_f16 " in d and "step_slots=4" in d
     d = bsp.describe(bsp.FP16, 4096, 4096, 32, 4096 * 4096 * 4 // 10)
     assert "-> mfma kernel=k_bt64_f16 " in d and "block=1024" in d
     # K not a multiple of 32: outside the fast path

@@ -77,6 +77,56 @@ struct BfWinGlobal {
     }
 };
 
+// The same for a staged stream, software-pipelined: the stream positions of
+// all 16 groups first, then each byte's window and selector reads are issued
+// one byte ahead of the placement that uses them (scheduling fences keep the
+// compiler from sinking the reads back to their use; one byte of lookahead
+// keeps about 8 LDS reads in flight at 20 more registers).
+template <int NB>
+__device__ __forceinline__ void bf_contract_lds_ahead(uint64_t word, uint32_t p, uint32_t lut,
+                                                      const bf_h8 (&xb)[NB][8], bf_f4 (&acc)[NB]) {
+    uint32_t pp[16], mm[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        mm[k] = (uint32_t)(word >> (4 * k)) & 15u;
+        pp[k] = p;
+        p = (uint32_t)__builtin_popcount(mm[k]) + p;
+    }
+    uint32_t d0[16], d1[16], d2[16];
+    uint2 ss[16];
+    auto rd = [&](int j) -> void {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int k = 2 * j + h;
+            ss[k] = bt_lds_pair(lut + mm[k] * 8u);
+            const bt_lds_u32 *q = (const bt_lds_u32 *)(uintptr_t)((pp[k] << 1) & ~3u);
+            d0[k] = q[0];
+            d1[k] = q[1];
+            d2[k] = q[2];
+        }
+    };
+    rd(0);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        if (j + 1 < 8) rd(j + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        uint32_t A[4];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int k = 2 * j + h;
+            const uint32_t s = pp[k] << 4;   // funnel shift by 16 * (p & 1)
+            const uint32_t wx = __builtin_amdgcn_alignbit(d1[k], d0[k], s);
+            const uint32_t wy = __builtin_amdgcn_alignbit(d2[k], d1[k], s);
+            A[2 * h] = __builtin_amdgcn_perm(wy, wx, ss[k].x);
+            A[2 * h + 1] = __builtin_amdgcn_perm(wy, wx, ss[k].y);
+        }
+        const bf_h8 a = __builtin_bit_cast(bf_h8, bt_v4i{(int)A[0], (int)A[1], (int)A[2], (int)A[3]});
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, xb[nb][j], acc[nb], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
 // Decode + contract one tile: 8 MFMAs of 8 positions each.
 template <int NB, class Win>
 __device__ __forceinline__ void bf_contract(uint64_t word, uint32_t p, const Win &win, uint32_t lut,
@@ -477,7 +527,7 @@ __global__ __launch_bounds__(512) void k_bt8_f16(
         if (g.n <= cap) {
             uint32_t p = min(pstart, 2u * (4u * g.n - 3u));   // a corrupt stream stays inside the staged granules
             p += bt_lds_addr(stage + (uint32_t)(i % 3) * area) >> 1;
-            bf_contract<1>(word, p, BfWinLds{}, lut, xb, acc);
+            bf_contract_lds_ahead<1>(word, p, lut, xb, acc);
         } else {
             bf_contract<1>(word, pstart, BfWinGlobal{prs, 4u * g.g0}, lut, xb, acc);
         }

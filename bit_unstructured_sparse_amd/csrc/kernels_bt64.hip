@@ -52,6 +52,14 @@
 #define BT_LUT_BYTES (2048 * BT_LUT_COPIES)   // 256 entries x 8 bytes per copy
 #define BT_LDS_MAX (160 * 1024)
 #define BT_CUS 256
+// Cache policy of the payload DMAs (and of the streaming kernel's bitmap
+// words): non-temporal. Each of these bytes is read once per launch, by one
+// workgroup, in whole 64-byte lines; the hint keeps them from displacing X and
+// the other lines the launch reuses. Loads whose lines are shared between
+// wavefronts or instructions (X, the ring kernel's 8-byte words, the fp16
+// half-row starts) keep the default policy: marked non-temporal they were
+// re-fetched and measured slower.
+#define BT_NT 2
 
 // Blocks one workgroup can own: every block's words stay in VGPRs (TPL words per lane).
 #define BT_NBLK(TPL) (8 / (TPL))
@@ -374,7 +382,7 @@ __global__ __launch_bounds__(BT_WG_THREADS(TPL)) void k_bt64_w4a4(
                 const uint32_t u = j * 64u + (uint32_t)lane;
                 if (u < g.n)
                     __builtin_amdgcn_raw_ptr_buffer_load_lds(prs, (bt_lds_void *)(buf + j * 1024u), 16,
-                                                             (g.g0 + u) * 16u, 0, 0, 0);
+                                                             (g.g0 + u) * 16u, 0, 0, BT_NT);
                 ++vm_issued;
             }
         }
@@ -652,7 +660,7 @@ __global__ __launch_bounds__(512) void k_bt64s_w4a4(
     auto load_words = [&](int i) -> void {
         const int rr = i * BT_ROWS + r;
         const uint32_t off = ((uint32_t)rr * (uint32_t)T + (uint32_t)t0) * 8u;
-        const bt_v4i v = __builtin_bit_cast(bt_v4i, __builtin_amdgcn_raw_buffer_load_b128(brs, off, 0, 0));
+        const bt_v4i v = __builtin_bit_cast(bt_v4i, __builtin_amdgcn_raw_buffer_load_b128(brs, off, 0, BT_NT));
         words[i][0] = ((uint64_t)(uint32_t)v.y << 32) | (uint32_t)v.x;
         words[i][1] = ((uint64_t)(uint32_t)v.w << 32) | (uint32_t)v.z;
     };
@@ -678,7 +686,7 @@ __global__ __launch_bounds__(512) void k_bt64s_w4a4(
             const uint32_t sl = j * 64u + (uint32_t)lane;
             const uint32_t u = sl - BTS_OVL * ((sl * kmag) >> 20);   // stream granule of slot sl
             __builtin_amdgcn_raw_ptr_buffer_load_lds(prs, (bt_lds_void *)(real ? buf + j * 1024u : dummy), 16,
-                                                     (real && u < n) ? (g.g0 + u) * 16u : 0xFFFFFFF0u, 0, 0, 0);
+                                                     (real && u < n) ? (g.g0 + u) * 16u : 0xFFFFFFF0u, 0, 0, BT_NT);
         }
     };
     // one block in flight: the memory system serves it before any later

@@ -256,7 +256,7 @@ __global__ __launch_bounds__(1024) void k_bt64_f16(
                 const uint32_t u = j * 64u + (uint32_t)lane;
                 if (u < g.n)
                     __builtin_amdgcn_raw_ptr_buffer_load_lds(prs, (bt_lds_void *)(buf + j * 1024u), 16,
-                                                             (g.g0 + u) * 16u, 0, 0, 0);
+                                                             (g.g0 + u) * 16u, 0, 0, BT_NT);
                 ++vm_issued;
             }
         }
@@ -470,7 +470,7 @@ __global__ __launch_bounds__(512) void k_bt8_f16(
             if (j >= area_kb) break;   // wave-uniform
             const uint32_t u = j * 64u + (uint32_t)lane;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(prs, (bt_lds_void *)(buf + j * 1024u), 16,
-                                                     u < n ? (g.g0 + u) * 16u : 0xFFFFFFF0u, 0, 0, 0);
+                                                     u < n ? (g.g0 + u) * 16u : 0xFFFFFFF0u, 0, 0, BT_NT);
         }
     };
     issue(0);

@@ -650,9 +650,9 @@ __global__ __launch_bounds__(512) void k_bt64s_w4a4(
             }
     }
     // bitmap words: block 0's now, block i + 1's with its DMA (below), so
-    // that the first payload does not queue behind every block's words (a row past M or past the workgroup's range is past the
-    // end of the buffer and reads zeros; a tile past the row's end is
-    // cleared before use)
+    // that the first payload does not queue behind every block's words (a
+    // row past M or past the workgroup's range is past the end of the buffer
+    // and reads zeros; a tile past the row's end is cleared before use)
     const int m_first = b_begin * BT_ROWS;
     const int wg_rows = min(nblk * BT_ROWS, M - m_first);
     const __amdgpu_buffer_rsrc_t brs = bt_rsrc(bitmaps + (int64_t)m_first * T, (uint32_t)wg_rows * (uint32_t)T * 8u);
@@ -666,10 +666,9 @@ __global__ __launch_bounds__(512) void k_bt64s_w4a4(
     };
     load_words(0);
     bt_v4i xb[NB][TPL][4];   // B operands, made from xw once block 0 has landed
-    // payload of block i < nblk: D instructions per wavefront
-    // Every wavefront issues exactly D instructions per block, also for KB
-    // past the area: those write zeros into a 1 KB dummy slot behind the
-    // staging areas. With a fixed count in straight-line code the compiler's
+    // payload of block i < nblk: every wavefront issues exactly D
+    // instructions per block, also for KB past the area, which write zeros
+    // into a 1 KB dummy slot behind the staging areas. With a fixed count in straight-line code the compiler's
     // own waits are exact (block 0's words are used before its payload has
     // landed); with a count that depends on the wavefront it waits for
     // everything in flight.

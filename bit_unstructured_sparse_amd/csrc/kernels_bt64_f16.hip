@@ -127,6 +127,49 @@ __device__ __forceinline__ void bf_contract_lds_ahead(uint64_t word, uint32_t p,
     }
 }
 
+// X granules loaded with lane group q holding granules 4 i + q (i = 0..7) of
+// its wavefront's four tiles -> each lane's own tile q, granule j in xb[.][j].
+// Element E[q][s] = (xg[2s], xg[2s+1]) = granules 8s + q and 8s + 4 + q; the
+// 4 x 4 transpose over (q, s) leaves E[s][q] in slot s of group q, i.e.
+// granules 8q + s and 8q + 4 + s: j = s and j = 4 + s of tile q. Two stages
+// of swaps between lane groups: q ^ 2 (32-lane swap: the upper half of its
+// first operand with the lower half of its second) on slots s and s + 2, then
+// q ^ 1 (16-lane swap: the odd rows of the first with the even rows of the
+// second) on slots 2u and 2u + 1. Every lane must be active.
+template <int NB>
+__device__ __forceinline__ void bf_x_transpose(bt_v4i (&xg)[NB][8], bf_h8 (&xb)[NB][8]) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int e = 0; e < 2; ++e)
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    const auto w = __builtin_amdgcn_permlane32_swap((unsigned)xg[nb][2 * s + e][d],
+                                                                    (unsigned)xg[nb][2 * (s + 2) + e][d], false, false);
+                    xg[nb][2 * s + e][d] = (int)w[0];
+                    xg[nb][2 * (s + 2) + e][d] = (int)w[1];
+                }
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int e = 0; e < 2; ++e)
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    const auto w = __builtin_amdgcn_permlane16_swap((unsigned)xg[nb][2 * (2 * u) + e][d],
+                                                                    (unsigned)xg[nb][2 * (2 * u + 1) + e][d], false, false);
+                    xg[nb][2 * (2 * u) + e][d] = (int)w[0];
+                    xg[nb][2 * (2 * u + 1) + e][d] = (int)w[1];
+                }
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            xb[nb][s] = __builtin_bit_cast(bf_h8, xg[nb][2 * s]);
+            xb[nb][4 + s] = __builtin_bit_cast(bf_h8, xg[nb][2 * s + 1]);
+        }
+    }
+}
+
 // Decode + contract one tile: 8 MFMAs of 8 positions each.
 template <int NB, class Win>
 __device__ __forceinline__ void bf_contract(uint64_t word, uint32_t p, const Win &win, uint32_t lut,
@@ -199,25 +242,34 @@ __global__ __launch_bounds__(1024) void k_bt64_f16(
     // windows from global memory.
     uint32_t vm_issued = 0, vm_mark[BF_NBLK];
     // this lane's X: column r + 16 nb, positions 64 t .. 64 t + 63, as the
-    // B operands of the tile's 8 MFMAs (column n >= N or tile >= T: zeros)
-    bf_h8 xb[NB][8];
+    // B operands of the tile's 8 MFMAs (column n >= N or tile >= T: zeros).
+    // The wavefront's four tiles are 512 contiguous bytes of each X row. Load
+    // i gives lane group q the 16-byte granule 4 i + q of them, so one load
+    // covers 64-byte runs of 16 rows instead of one line per lane (the line
+    // requests, not the bytes, bound this prologue); a transpose across the
+    // lane groups (bf_x_transpose, in block 0) then hands each lane its own
+    // tile's granules.
+    bt_v4i xg[NB][8];
     {
         const __amdgpu_buffer_rsrc_t xrs = bt_rsrc(X, (uint32_t)N * (uint32_t)K * 2u);
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
             const int n = r + 16 * nb;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
+            for (int i = 0; i < 8; ++i) {
+                const uint32_t gi = 4u * (uint32_t)i + (uint32_t)q;       // granule of the wavefront's 512 bytes
+                const uint32_t tt = (uint32_t)(wave * 4) + (gi >> 3);       // its tile
                 // positions past K read as zeros too: a finite weight of 0 times
                 // a non-finite X from the next row would give NaN
-                const uint32_t k0 = (uint32_t)t * 64u + 8u * j;
-                const uint32_t off = (n < N && t < T && k0 < (uint32_t)K) ? ((uint32_t)n * (uint32_t)K + k0) * 2u
-                                                                          : 0xFFFFFFF0u;
-                xb[nb][j] = __builtin_bit_cast(bf_h8, __builtin_amdgcn_raw_buffer_load_b128(xrs, off, 0, 0));
+                const uint32_t k0 = tt * 64u + 8u * (gi & 7u);
+                const uint32_t off = (n < N && tt < (uint32_t)T && k0 < (uint32_t)K)
+                                             ? ((uint32_t)n * (uint32_t)K + k0) * 2u : 0xFFFFFFF0u;
+                xg[nb][i] = __builtin_bit_cast(bt_v4i, __builtin_amdgcn_raw_buffer_load_b128(xrs, off, 0, 0));
             }
         }
         vm_issued += NB * 8;
     }
+    bf_h8 xb[NB][8];
     const int m_first = b_begin * BF_ROWS;
     const int wg_rows = min(nblk * BF_ROWS, M - m_first);
     const __amdgpu_buffer_rsrc_t brs = bt_rsrc(bitmaps + (int64_t)m_first * T, (uint32_t)wg_rows * (uint32_t)T * 8u);
@@ -340,6 +392,7 @@ __global__ __launch_bounds__(1024) void k_bt64_f16(
             pstart = r < rows ? (eb[i] & 7u) + (s - row_total) + before_w + (incl - seg) : 0u;
         }
 
+        if (i == 0) bf_x_transpose<NB>(xg, xb);
         bf_f4 acc[NB];
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) acc[nb] = bf_f4{0.f, 0.f, 0.f, 0.f};

@@ -129,6 +129,74 @@ __device__ __forceinline__ void bt_barrier_lds() {
     asm volatile("" ::: "memory");
 }
 
+// X of a wavefront's 4 TPL consecutive tiles (lane group q owns tiles
+// q TPL .. q TPL + TPL - 1 of them) is 8 TPL contiguous 16-byte granules of
+// each X row. Load i (i < 2 TPL) gives lane group q granule 4 i + q, so one
+// load covers 64-byte runs of 16 rows; slices loaded lane by lane touch one
+// line per lane instead, and the line requests, not the bytes, bound how
+// fast X comes in. Columns n >= N and tiles >= T read zeros.
+template <int NB, int TPL>
+__device__ __forceinline__ void bt_load_x_runs(__amdgpu_buffer_rsrc_t xrs, int r, int q, int wave, int T, int N,
+                                               uint32_t xs, bt_v4i (&xg)[NB][2 * TPL]) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        const int n = r + 16 * nb;
+#pragma unroll
+        for (int i = 0; i < 2 * TPL; ++i) {
+            const uint32_t gi = 4u * (uint32_t)i + (uint32_t)q;
+            const uint32_t tt = (uint32_t)(wave * 4 * TPL) + (gi >> 1);
+            const uint32_t off = (n < N && tt < (uint32_t)T) ? (uint32_t)n * xs + tt * 32u + (gi & 1u) * 16u : 0xFFFFFFE0u;
+            xg[nb][i] = __builtin_bit_cast(bt_v4i, __builtin_amdgcn_raw_buffer_load_b128(xrs, off, 0, 0));
+        }
+    }
+}
+
+// The granules of bt_load_x_runs -> each lane's own slices. With G = 2 TPL
+// granules per lane and E = G / 4, element (q, s) = loads s E .. s E + E - 1
+// of lane group q = the granules of group s taken by group q. A 4 x 4
+// transpose over (q, s) gives group q the elements (s, q): its granule j is
+// load (j / 4) of element j % 4. Two stages of swaps between lane groups:
+// q ^ 2 (the 32-lane swap exchanges the upper half of its first operand with
+// the lower half of its second) on elements s and s + 2, then q ^ 1 (the
+// 16-lane swap exchanges the odd rows of the first with the even rows of the
+// second) on elements 2u and 2u + 1. Every lane must be active.
+template <int NB, int TPL>
+__device__ __forceinline__ void bt_x_runs_to_slices(bt_v4i (&xg)[NB][2 * TPL], uint32_t (&xw)[NB][TPL][8]) {
+    constexpr int E = TPL / 2;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    const auto w = __builtin_amdgcn_permlane32_swap((unsigned)xg[nb][s * E + e][d],
+                                                                    (unsigned)xg[nb][(s + 2) * E + e][d], false, false);
+                    xg[nb][s * E + e][d] = (int)w[0];
+                    xg[nb][(s + 2) * E + e][d] = (int)w[1];
+                }
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    const auto w = __builtin_amdgcn_permlane16_swap((unsigned)xg[nb][2 * u * E + e][d],
+                                                                    (unsigned)xg[nb][(2 * u + 1) * E + e][d], false, false);
+                    xg[nb][2 * u * E + e][d] = (int)w[0];
+                    xg[nb][(2 * u + 1) * E + e][d] = (int)w[1];
+                }
+#pragma unroll
+        for (int k = 0; k < TPL; ++k) {
+            const bt_v4i v0 = xg[nb][((2 * k) % 4) * E + (2 * k) / 4];
+            const bt_v4i v1 = xg[nb][((2 * k + 1) % 4) * E + (2 * k + 1) / 4];
+            xw[nb][k][0] = v0.x; xw[nb][k][1] = v0.y; xw[nb][k][2] = v0.z; xw[nb][k][3] = v0.w;
+            xw[nb][k][4] = v1.x; xw[nb][k][5] = v1.y; xw[nb][k][6] = v1.z; xw[nb][k][7] = v1.w;
+        }
+    }
+}
+
 // Decode of one tile word into 16 dwords of x16 int8 (A operand of 4 MFMAs).
 // win(p) returns the two payload dwords holding nibbles p .. p+7 as (lo, hi).
 // lut_base is the LDS address of this lane's copy of the selector table: the
@@ -291,6 +359,7 @@ __global__ __launch_bounds__(BT_WG_THREADS(TPL)) void k_bt64_w4a4(
     uint32_t vm_issued = 0;           // vector-memory operations issued so far by this wavefront
     // this lane's X slices, once for all blocks (column n >= N or tile >= T: zeros)
     uint32_t xw[NB][TPL][8];
+    bt_v4i xg[NB][2 * TPL];           // X granules as loaded (global-memory path)
     const __amdgpu_buffer_rsrc_t xrs = bt_rsrc(X, (uint32_t)N * xs);
     const uint32_t xgr = xs >> 4;     // 16-byte granules per X row
     if (x_lds) {
@@ -313,17 +382,7 @@ __global__ __launch_bounds__(BT_WG_THREADS(TPL)) void k_bt64_w4a4(
             ++vm_issued;
         }
     } else {
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-            for (int k = 0; k < TPL; ++k) {
-                const int n = r + 16 * nb;
-                const uint32_t off = (n < N && t0 + k < T) ? (uint32_t)n * xs + (uint32_t)(t0 + k) * 32u : 0xFFFFFFE0u;
-                const bt_v4i v0 = __builtin_bit_cast(bt_v4i, __builtin_amdgcn_raw_buffer_load_b128(xrs, off, 0, 0));
-                const bt_v4i v1 = __builtin_bit_cast(bt_v4i, __builtin_amdgcn_raw_buffer_load_b128(xrs, off + 16u, 0, 0));
-                xw[nb][k][0] = v0.x; xw[nb][k][1] = v0.y; xw[nb][k][2] = v0.z; xw[nb][k][3] = v0.w;
-                xw[nb][k][4] = v1.x; xw[nb][k][5] = v1.y; xw[nb][k][6] = v1.z; xw[nb][k][7] = v1.w;
-            }
+        bt_load_x_runs<NB, TPL>(xrs, r, q, wave, T, N, xs, xg);
         vm_issued += 2 * NB * TPL;
     }
     const int m_first = b_begin * BT_ROWS;
@@ -382,6 +441,8 @@ __global__ __launch_bounds__(BT_WG_THREADS(TPL)) void k_bt64_w4a4(
                 xw[nb][k][0] = v0.x; xw[nb][k][1] = v0.y; xw[nb][k][2] = v0.z; xw[nb][k][3] = v0.w;
                 xw[nb][k][4] = v1.x; xw[nb][k][5] = v1.y; xw[nb][k][6] = v1.z; xw[nb][k][7] = v1.w;
             }
+    } else {
+        bt_x_runs_to_slices<NB, TPL>(xg, xw);
     }
     // B operands of this lane's tiles, in the even/odd x16 order of the decode;
     // pinned so that they are built once, not rebuilt in every block
@@ -678,20 +739,25 @@ __global__ __launch_bounds__(512) void k_bt64s_w4a4(
     // become B operands only once block 0 has landed, so that the first
     // payload DMA goes out as soon as the block offsets are in (waiting for
     // X first held it back by about half a microsecond)
+    // (in runs of 16 rows at N > 16, where that gains 0.35 us at qkv N = 32;
+    // at N <= 16 per-lane slices, which were 0.05 us faster at qkv N = 8)
+    bt_v4i xg[NB][2 * TPL];
     uint32_t xw[NB][TPL][8];
     {
         const __amdgpu_buffer_rsrc_t xrs = bt_rsrc(X, (uint32_t)N * xs);
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
+        if constexpr (NB == 2) {
+            bt_load_x_runs<NB, TPL>(xrs, r, q, wave, T, N, xs, xg);
+        } else {
 #pragma unroll
             for (int k = 0; k < TPL; ++k) {
-                const int n = r + 16 * nb;
+                const int n = r;
                 const uint32_t off = (n < N && t0 + k < T) ? (uint32_t)n * xs + (uint32_t)(t0 + k) * 32u : 0xFFFFFFE0u;
                 const bt_v4i v0 = __builtin_bit_cast(bt_v4i, __builtin_amdgcn_raw_buffer_load_b128(xrs, off, 0, 0));
                 const bt_v4i v1 = __builtin_bit_cast(bt_v4i, __builtin_amdgcn_raw_buffer_load_b128(xrs, off + 16u, 0, 0));
-                xw[nb][k][0] = v0.x; xw[nb][k][1] = v0.y; xw[nb][k][2] = v0.z; xw[nb][k][3] = v0.w;
-                xw[nb][k][4] = v1.x; xw[nb][k][5] = v1.y; xw[nb][k][6] = v1.z; xw[nb][k][7] = v1.w;
+                xw[0][k][0] = v0.x; xw[0][k][1] = v0.y; xw[0][k][2] = v0.z; xw[0][k][3] = v0.w;
+                xw[0][k][4] = v1.x; xw[0][k][5] = v1.y; xw[0][k][6] = v1.z; xw[0][k][7] = v1.w;
             }
+        }
     }
     // bitmap words: block 0's now, block i + 1's with its DMA (below), so
     // that the first payload does not queue behind every block's words (a
@@ -771,7 +837,11 @@ __global__ __launch_bounds__(512) void k_bt64s_w4a4(
             load_words(i + 1);   // ahead of its payload: block i + 1's row totals need no wait for it
             issue(i + 1);
         }
-        if (i == 0) bt_make_b<NB, TPL>(xw, xb);   // X landed with block 0 (waited above)
+        if (i == 0) {
+            // X landed with block 0 (waited above)
+            if constexpr (NB == 2) bt_x_runs_to_slices<NB, TPL>(xg, xw);
+            bt_make_b<NB, TPL>(xw, xb);
+        }
         bt_barrier_lds();                     // ... everyone's, and every row total of block i
         const BtRange g = bt_range(nib[i], nib[i + 1]);
         const int rows = min(BT_ROWS, M - (b_begin + i) * BT_ROWS);

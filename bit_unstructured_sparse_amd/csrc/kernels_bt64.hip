@@ -300,7 +300,6 @@ __device__ __forceinline__ BtRange bt_range(uint32_t nibA, uint32_t nibB) {
 // LDS layout (bytes):
 //   [row totals NBLK x 16 x 8 ints][sums 3 x NB x 256 ints][selector table copies]
 //   [nbuf staging buffers of stage_bytes]
-// With x_lds, X (N x K/2 bytes) is first staged from the table's start on.
 // Workgroup g owns blocks [g*bq + min(g, br), ...): bq or bq + 1 of them.
 template <int NB, int TPL>
 // (The arguments the first loads need come first: they are the ones a
@@ -308,7 +307,7 @@ template <int NB, int TPL>
 __global__ __launch_bounds__(BT_WG_THREADS(TPL)) void k_bt64_w4a4(
         const uint32_t *__restrict__ offsets, int M, int K, int bq, int br, const uint64_t *__restrict__ bitmaps,
         const uint8_t *__restrict__ X, int N, const uint8_t *__restrict__ payload, uint32_t payload_bytes,
-        int32_t *__restrict__ Y, uint32_t stage_bytes, uint32_t nbuf, int one_pass, int x_lds) {
+        int32_t *__restrict__ Y, uint32_t stage_bytes, uint32_t nbuf, int one_pass) {
     constexpr int NBLK = BT_NBLK(TPL);
     constexpr int WC = BT_WG_THREADS(TPL) / 64;          // row-total columns: wavefronts, at most
     extern __shared__ __attribute__((aligned(16))) uint8_t bt_smem[];
@@ -359,32 +358,9 @@ __global__ __launch_bounds__(BT_WG_THREADS(TPL)) void k_bt64_w4a4(
     uint32_t vm_issued = 0;           // vector-memory operations issued so far by this wavefront
     // this lane's X slices, once for all blocks (column n >= N or tile >= T: zeros)
     uint32_t xw[NB][TPL][8];
-    bt_v4i xg[NB][2 * TPL];           // X granules as loaded (global-memory path)
-    const __amdgpu_buffer_rsrc_t xrs = bt_rsrc(X, (uint32_t)N * xs);
-    const uint32_t xgr = xs >> 4;     // 16-byte granules per X row
-    if (x_lds) {
-        // X through LDS, over the selector table and the staging (both
-        // written only after every lane has read its slices): granule c of
-        // row n to slot c * N + n. The DMA instructions then read whole
-        // lines (consecutive slots are the same granule of consecutive rows,
-        // then the next granule), and the 16 lanes of a slice read take 16
-        // consecutive slots (conflict-free). Per-lane slice loads straight
-        // from global memory touch one line per lane and instruction, which
-        // is what bounded this prologue.
-        const uint32_t S = (uint32_t)N * xgr;
-        const uint32_t n_ins = (S + 63u) >> 6;
-        for (uint32_t j = (uint32_t)wave; j < n_ins; j += (uint32_t)nwaves) {
-            const uint32_t sl = j * 64u + (uint32_t)lane;
-            const uint32_t c = sl / (uint32_t)N, n = sl - c * (uint32_t)N;
-            if (sl < S)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, (bt_lds_void *)(lut_lds8 + j * 1024u), 16,
-                                                         n * xs + c * 16u, 0, 0, 0);
-            ++vm_issued;
-        }
-    } else {
-        bt_load_x_runs<NB, TPL>(xrs, r, q, wave, T, N, xs, xg);
-        vm_issued += 2 * NB * TPL;
-    }
+    bt_v4i xg[NB][2 * TPL];           // X granules as loaded, in runs of 16 rows
+    bt_load_x_runs<NB, TPL>(bt_rsrc(X, (uint32_t)N * xs), r, q, wave, T, N, xs, xg);
+    vm_issued += 2 * NB * TPL;
     const int m_first = b_begin * BT_ROWS;
     const int wg_rows = min(nblk * BT_ROWS, M - m_first);
     const __amdgpu_buffer_rsrc_t brs = bt_rsrc(bitmaps + (int64_t)m_first * T, (uint32_t)wg_rows * (uint32_t)T * 8u);
@@ -422,28 +398,7 @@ __global__ __launch_bounds__(BT_WG_THREADS(TPL)) void k_bt64_w4a4(
     }
     // zero the sum buffers (first added to after the first block's barrier)
     for (int o = threadIdx.x; o < 3 * NB * 256; o += blockDim.x) sums[o] = 0;
-    if (x_lds) {
-        // every wavefront's share of X has landed: the slices from LDS
-        bt_wait_vm(0);
-        __syncthreads();
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-            for (int k = 0; k < TPL; ++k) {
-                const uint32_t n = (uint32_t)(r + 16 * nb), t = (uint32_t)(t0 + k);
-                bt_v4i v0 = {0, 0, 0, 0}, v1 = {0, 0, 0, 0};
-                if (n < (uint32_t)N && t < (uint32_t)T) {
-                    const uint32_t s0 = 2u * t * (uint32_t)N + n;
-                    v0 = *(bt_lds_v4i *)(uintptr_t)bt_lds_addr(lut_lds8 + s0 * 16u);
-                    // the second half of a tile past K (K % 64 == 32) stays zero
-                    if (2u * t + 1u < xgr) v1 = *(bt_lds_v4i *)(uintptr_t)bt_lds_addr(lut_lds8 + (s0 + (uint32_t)N) * 16u);
-                }
-                xw[nb][k][0] = v0.x; xw[nb][k][1] = v0.y; xw[nb][k][2] = v0.z; xw[nb][k][3] = v0.w;
-                xw[nb][k][4] = v1.x; xw[nb][k][5] = v1.y; xw[nb][k][6] = v1.z; xw[nb][k][7] = v1.w;
-            }
-    } else {
-        bt_x_runs_to_slices<NB, TPL>(xg, xw);
-    }
+    bt_x_runs_to_slices<NB, TPL>(xg, xw);
     // B operands of this lane's tiles, in the even/odd x16 order of the decode;
     // pinned so that they are built once, not rebuilt in every block
     bt_v4i xb[NB][TPL][4];
@@ -481,8 +436,6 @@ __global__ __launch_bounds__(BT_WG_THREADS(TPL)) void k_bt64_w4a4(
     // earlier loads: a wait for one of those after a loop of DMA issues would
     // have to wait for the DMAs too (the counter is in order, the loop's
     // length unknown to the compiler)
-    // X's LDS copy is about to be overwritten: every lane has read its slices
-    if (x_lds) bt_barrier_lds();
     uint32_t vm_mark[NBLK];
     auto fits = [&](int i) -> bool {
         const BtRange g = bt_range(nib[i], nib[i + 1]);
@@ -928,7 +881,6 @@ struct BtPlan {
     int stagger;            // streaming variant: staggered staging (rows near a multiple of 256 B long)
     int area_kb;            // streaming variant: KB of staging per block
     int one_pass;           // every block staged at once: one barrier before and one after the decode
-    int x_lds;              // ring variant: X staged through LDS by coalesced DMA
     size_t lds;             // total dynamic LDS
 };
 
@@ -978,16 +930,6 @@ static bool bt64_plan(int64_t M, int64_t K, int64_t N, int64_t payload_bytes, Bt
     p->stage_bytes = (uint32_t)stage;
     p->nbuf = (uint32_t)nbuf;
     p->lds = (size_t)(fixed + nbuf * stage + (p->one_pass ? part : 0));
-    // X staged through LDS (over the table and the staging) at N > 16, when
-    // it fits. There X is twice the bytes and per-lane slice loads are twice
-    // the line requests, and the coalesced staging gains more than its two
-    // barriers cost: 8192 x 8192 at N = 32 measured 19.1 -> 18.5 us. At
-    // N <= 16 it lost (4096 x 11008: 11.7 -> 12.1 us; 8192 x 8192: 15.2 ->
-    // 15.5 us), so the slices are loaded straight from global memory there.
-    const int64_t xbytes = N * (K / 2);
-    const int64_t x_end = fixed - BT_LUT_BYTES + xbytes;
-    p->x_lds = N > 16 && x_end <= budget;
-    if (p->x_lds) p->lds = std::max<size_t>(p->lds, (size_t)x_end);
     // streaming variant: D KB per wavefront and block covers the same
     // estimate as the staging buffer above
     p->streaming = 0;
@@ -1022,7 +964,7 @@ static void launch_bt64_t(const BtPlan &p, const uint64_t *bitmaps, const uint32
     (void)hipFuncSetAttribute((const void *)k_bt64_w4a4<NB, TPL>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               (int)p.lds);
     hipLaunchKernelGGL((k_bt64_w4a4<NB, TPL>), dim3(p.grid), dim3(64 * p.nwaves), p.lds, stream, offsets, M, K, p.bq,
-                       p.br, bitmaps, X, N, payload, payload_bytes, Y, p.stage_bytes, p.nbuf, p.one_pass, p.x_lds);
+                       p.br, bitmaps, X, N, payload, payload_bytes, Y, p.stage_bytes, p.nbuf, p.one_pass);
 }
 
 static void launch_bt64_w4a4(const BtPlan &p, const uint64_t *bitmaps, const uint32_t *offsets,

@@ -93,8 +93,8 @@ extern "C" int bsp_describe_selection(int dtype, int64_t M, int64_t K, int64_t N
                     snprintf(launch, sizeof launch, " kernel=k_bt64s_w4a4 grid=%u block=%d lds=%zu stage_kb=%d stagger=%d",
                              p.grid, 64 * p.nwaves, p.lds, p.area_kb, p.stagger);
                 else
-                    snprintf(launch, sizeof launch, " kernel=k_bt64_w4a4 grid=%u block=%d lds=%zu tiles_per_lane=%d one_pass=%d x_lds=%d",
-                             p.grid, 64 * p.nwaves, p.lds, p.tpl, p.one_pass, p.x_lds);
+                    snprintf(launch, sizeof launch, " kernel=k_bt64_w4a4 grid=%u block=%d lds=%zu tiles_per_lane=%d one_pass=%d",
+                             p.grid, 64 * p.nwaves, p.lds, p.tpl, p.one_pass);
             }
         } else {
             Bf8Plan p8;

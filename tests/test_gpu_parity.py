@@ -144,14 +144,14 @@ def test_w4a4_many_blocks_ragged_y(dev, algo, M, K, N, y_shift):
     assert np.array_equal(Y.cpu().numpy(), oracle_w4a4(p.W, p.X))
 
 
-@pytest.mark.parametrize("M,K,N,x_lds", [(1000, 64 * 100 + 32, 17, 1), (2050, 8192, 32, 1), (300, 11008, 20, 1),
-                                         (70, 8256, 24, 1), (200, 16384, 32, 0)])
-def test_w4a4_ring_x_staging(dev, M, K, N, x_lds):
-    # the ring kernel at N > 16 stages X through LDS (granule c of row n in
-    # slot c * N + n) when it fits, and loads the slices straight from global
-    # memory when it does not; K % 64 == 32 leaves the last tile half in X
+@pytest.mark.parametrize("M,K,N", [(1000, 64 * 100 + 32, 17), (2050, 8192, 32), (300, 11008, 20), (70, 8256, 24),
+                                   (200, 16384, 32), (333, 64 * 70 + 32, 3)])
+def test_w4a4_ring_x_runs(dev, M, K, N):
+    # the ring kernel loads X in 64-byte runs of 16 rows and hands each lane
+    # its slices by a transpose across lane groups; K % 64 == 32 leaves the
+    # last tile half in X, and rows n >= N read zeros
     p = workloads.random_int4_problem(M + K + N, M, K, N, keep=0.4)
-    assert f"x_lds={x_lds}" in bsp.describe(bsp.INT4, M, K, N, int(np.count_nonzero(p.W)))
+    assert "kernel=k_bt64_w4a4 " in bsp.describe(bsp.INT4, M, K, N, int(np.count_nonzero(p.W)))
     Y = run_w4a4(p.W, p.X, bsp.ALGO_MFMA, dev)
     assert np.array_equal(Y, oracle_w4a4(p.W, p.X))
 

@@ -156,9 +156,7 @@ def test_description_names_the_launched_kernel():
     d = bsp.describe(bsp.INT4, 12288, 4096, 8, 12288 * 4096 // 2)
     assert "-> mfma kernel=k_bt64s_w4a4 " in d and "grid=256 block=512" in d
     d = bsp.describe(bsp.INT4, 4096, 11008, 16, 4096 * 11008 * 3 // 10)
-    assert "-> mfma kernel=k_bt64_w4a4 " in d and "tiles_per_lane=8" in d and "x_lds=0" in d
-    d = bsp.describe(bsp.INT4, 8192, 8192, 32, 8192 * 8192 * 7 // 10)   # X staged through LDS at N > 16
-    assert "-> mfma kernel=k_bt64_w4a4 " in d and "x_lds=1" in d
+    assert "-> mfma kernel=k_bt64_w4a4 " in d and "tiles_per_lane=8" in d
     d = bsp.describe(bsp.FP16, 4096, 4096, 1, 4096 * 4096 * 4 // 10)
     assert "-> mfma kernel=k_bt8_f16 " in d and "grid=256 block=512" in d and "step_slots=2" in d
     d = bsp.describe(bsp.FP16, 8003, 1000, 5, 8003 * 1000 // 10)   # four steps per workgroup

@@ -441,7 +441,7 @@ __global__ __launch_bounds__(1024) void k_bt64_f16(
 #define BF8_NSTEP_MAX 4                  // steps per workgroup, at most (NSTEP 2 or 4)
 #define BF8_WAVES 8
 
-template <int NSTEP>
+template <int NSTEP, bool XR>
 __global__ __launch_bounds__(512) void k_bt8_f16(
         const uint32_t *__restrict__ offsets, int M, int K, int sq, int sr, const uint64_t *__restrict__ bitmaps,
         const uint16_t *__restrict__ X, int N, const uint16_t *__restrict__ payload, uint32_t payload_bytes,
@@ -528,6 +528,8 @@ __global__ __launch_bounds__(512) void k_bt8_f16(
     };
     issue(0);
     bf_h8 xb[1][8];   // X of this lane's tile, loaded behind the first DMA (below)
+    bt_v4i xg[1][8];  // the same in runs of the rows, before the transpose (XR: N > 4)
+    constexpr bool x_runs = XR;
 
 #pragma unroll
     for (int i = 0; i < NSTEP; ++i) {
@@ -550,12 +552,29 @@ __global__ __launch_bounds__(512) void k_bt8_f16(
             // waits behind it; the decode is the first use.
             const __amdgpu_buffer_rsrc_t xrs = bt_rsrc(X, (uint32_t)N * (uint32_t)K * 2u);
             const int n = row8;
+            if constexpr (x_runs) {
+                // at N > 4, in 64-byte runs of the rows (load j gives lane
+                // group q granule 4 j + q of the wavefront's four tiles of
+                // this half), handed out by the lane-group transpose before
+                // the decode
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const uint32_t k0 = (uint32_t)t * 64u + 8u * j;
-                const uint32_t off = (n < N && tile_ok && k0 < (uint32_t)K) ? ((uint32_t)n * (uint32_t)K + k0) * 2u
-                                                                            : 0xFFFFFFF0u;
-                xb[0][j] = __builtin_bit_cast(bf_h8, __builtin_amdgcn_raw_buffer_load_b128(xrs, off, 0, 0));
+                for (int j = 0; j < 8; ++j) {
+                    const uint32_t gi = 4u * (uint32_t)j + (uint32_t)q;
+                    const uint32_t tw2 = (uint32_t)(wave * 4) + (gi >> 3);
+                    const uint32_t tt = (uint32_t)(kh * T2) + tw2;
+                    const uint32_t k0 = tt * 64u + 8u * (gi & 7u);
+                    const bool ok = n < N && tw2 < (uint32_t)T2 && tt < (uint32_t)T && k0 < (uint32_t)K;
+                    xg[0][j] = __builtin_bit_cast(bt_v4i, __builtin_amdgcn_raw_buffer_load_b128(
+                                                                  xrs, ok ? ((uint32_t)n * (uint32_t)K + k0) * 2u : 0xFFFFFFF0u, 0, 0));
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const uint32_t k0 = (uint32_t)t * 64u + 8u * j;
+                    const uint32_t off = (n < N && tile_ok && k0 < (uint32_t)K) ? ((uint32_t)n * (uint32_t)K + k0) * 2u
+                                                                                : 0xFFFFFFF0u;
+                    xb[0][j] = __builtin_bit_cast(bf_h8, __builtin_amdgcn_raw_buffer_load_b128(xrs, off, 0, 0));
+                }
             }
         }
         bt_wait_vm(0);   // this wavefront's share of step i landed (nothing later in flight)
@@ -576,6 +595,8 @@ __global__ __launch_bounds__(512) void k_bt8_f16(
             pre[7] = pre[6] + (uint32_t)t1v.z; pre[8] = pre[7] + (uint32_t)t1v.w;
             pstart = (hs[i] - (eb[i] & ~7u)) + pre[wave] + (incl - seg);
         }
+        if constexpr (x_runs)
+            if (i == 0) bf_x_transpose<1>(xg, xb);
         bf_f4 acc[1] = {bf_f4{0.f, 0.f, 0.f, 0.f}};
         if (g.n <= cap) {
             uint32_t p = min(pstart, 2u * (4u * g.n - 3u));   // a corrupt stream stays inside the staged granules
@@ -646,14 +667,21 @@ static bool bf8_plan(int64_t M, int64_t K, int64_t N, int64_t payload_bytes, Bf8
 static void launch_bt8_f16(const Bf8Plan &p, const uint64_t *bitmaps, const uint32_t *offsets,
                            const uint16_t *payload, uint32_t payload_bytes, int M, int K, const uint16_t *X, int N,
                            uint16_t *Y, hipStream_t stream) {
-    const void *fn = p.nstep == 2 ? (const void *)k_bt8_f16<2> : (const void *)k_bt8_f16<BF8_NSTEP_MAX>;
-    (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds);
-    if (p.nstep == 2)
-        hipLaunchKernelGGL(k_bt8_f16<2>, dim3(p.grid), dim3(64 * p.nwaves), p.lds, stream, offsets, M, K, p.sq, p.sr,
-                           bitmaps, X, N, payload, payload_bytes, Y, p.area_kb);
-    else
-        hipLaunchKernelGGL(k_bt8_f16<BF8_NSTEP_MAX>, dim3(p.grid), dim3(64 * p.nwaves), p.lds, stream, offsets, M, K,
-                           p.sq, p.sr, bitmaps, X, N, payload, payload_bytes, Y, p.area_kb);
+    // X in runs of the rows at N > 4 (N = 8: 10.5 -> 9.6 us); per-lane loads
+    // below (N = 1 and 4 measured 0.05 us faster that way)
+#define BF8_LAUNCH(S, XR)                                                                                       \
+    do {                                                                                                        \
+        (void)hipFuncSetAttribute((const void *)k_bt8_f16<S, XR>, hipFuncAttributeMaxDynamicSharedMemorySize,  \
+                                  (int)p.lds);                                                                  \
+        hipLaunchKernelGGL((k_bt8_f16<S, XR>), dim3(p.grid), dim3(64 * p.nwaves), p.lds, stream, offsets, M, K, \
+                           p.sq, p.sr, bitmaps, X, N, payload, payload_bytes, Y, p.area_kb);                    \
+    } while (0)
+    if (p.nstep == 2) {
+        if (N > 4) BF8_LAUNCH(2, true); else BF8_LAUNCH(2, false);
+    } else {
+        if (N > 4) BF8_LAUNCH(BF8_NSTEP_MAX, true); else BF8_LAUNCH(BF8_NSTEP_MAX, false);
+    }
+#undef BF8_LAUNCH
 }
 
 struct BfPlan {

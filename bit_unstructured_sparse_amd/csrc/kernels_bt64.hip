@@ -692,8 +692,8 @@ __global__ __launch_bounds__(512) void k_bt64s_w4a4(
     // become B operands only once block 0 has landed, so that the first
     // payload DMA goes out as soon as the block offsets are in (waiting for
     // X first held it back by about half a microsecond)
-    // (in runs of 16 rows at N > 16, where that gains 0.35 us at qkv N = 32;
-    // at N <= 16 per-lane slices, which were 0.05 us faster at qkv N = 8)
+    // (in runs of 16 rows at N > 16, where that gains 0.35 us on 12288 x 4096
+    // at N = 32; at N <= 16 per-lane slices, 0.05 us faster there at N = 8)
     bt_v4i xg[NB][2 * TPL];
     uint32_t xw[NB][TPL][8];
     {

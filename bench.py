@@ -7,9 +7,11 @@ A step is one call of the SpMM entry point (``spmm_bitmap_w4a4``, or
 kernel selection, then the kernel that streams the compressed tiles, stages
 X, decodes, contracts and stores Y) on one batch of synthetic input already
 resident in HBM. Encoding is the offline step of the method and runs once,
-before timing. The inputs are rotated through enough identical device copies
-(>= 1 GiB in total, four times the 256 MB Infinity Cache) that each step reads
-its operands from HBM, not from cache.
+before timing. Every timed step reads its own device copy of the inputs, and
+between a copy's last use and its timed use the GPU reads at least 1 GiB of
+other copies (four times the 256 MB Infinity Cache), whatever --steps is: the
+K steps use copies 0..K-1, and after the graph's warm-up replay the copies
+K..R-1 (>= 1 GiB) are run eagerly before the timed replay.
 
 The K timed steps are captured once in a HIP graph (one kernel node per SpMM
 call) and replayed back to back: these kernels last a few microseconds, less
@@ -19,17 +21,23 @@ Prints ONE JSON line. ``value`` is achieved GB/s over the algorithmic bytes of
 a step (bitmaps, the offsets the kernel reads, payload, X, Y) divided by the
 host wall time per step around the replay; the ``roofline`` object divides the
 same bytes by the average launch duration from HIP events recorded on the
-replay stream. ``traffic`` is the HBM byte count of one launch from the
-FETCH_SIZE / WRITE_SIZE counter summary in ``profiles/`` when that summary was
-taken from the current kernel sources (else null). ``cpu_baseline`` times the
-CPU oracle (plain C, one thread) on a bounded sample of the same workload.
+replay stream, and ``roofline.achievable`` gives what a plain streaming read
+of the same byte count reaches in one launch on this GPU (the best of a few
+launch shapes and load forms of ``libbsp_probe.so``), and a read of 1 GiB.
+``traffic`` is the HBM byte count of one launch from the counter summary in
+``profiles/`` (TCC read/write requests to DRAM, checked against a read-only
+probe and a copy of known size) when that summary was taken from the current
+kernel sources (else null). ``cpu_baseline`` times the CPU oracle (plain C)
+on every host core the process may use, and on one core, on a bounded sample
+of the same workload.
 
 Helper modes used to produce the ``profiles/`` summaries:
 
     python bench.py --sweep                     # N = 1..32 on the qkv weights, N = 16, 32 at 70 % density
-    python bench.py --copy-calibration          # a plain copy of known size
+    python bench.py --peak-read                 # the read probe alone, at this workload's byte count
+    python bench.py --counter-run               # read probe + copy of known size + the SpMM steps (for --pmc)
     python bench.py --summarize-trace DIR OUT   # rocprofv3 --kernel-trace --stats csv -> text
-    python bench.py --summarize-traffic OUT --fetch DIR --write DIR --copy-fetch DIR --copy-write DIR
+    python bench.py --summarize-traffic OUT --reads DIR --writes DIR --kernel FRAGMENT
     python bench.py --summarize-counters DIR OUT --kernel FRAGMENT   # rocprofv3 --pmc csv -> text
 """
 from __future__ import annotations
@@ -51,19 +59,23 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
-ROTATE_TARGET = 1 << 30
-COPY_BYTES = 256 << 20         # calibration copy: reads and writes this many bytes
+FLUSH_BYTES = 1 << 30          # other traffic between a copy's last use and its timed use
+COPY_BYTES = 256 << 20         # calibration kernels: the copy reads and writes this many bytes, the probe reads it
+PROBE_SHAPES = [(256, 512), (512, 512), (1024, 256), (2048, 256)]   # (grid, block) of the read probe
+PROBE_MODES = {0: "registers", 1: "registers, non-temporal", 2: "direct-to-LDS, non-temporal"}
+# TCC counters of the traffic passes (each pass within the 4-TCC-counter limit)
+READ_COUNTERS = ["TCC_EA0_RDREQ_32B_sum", "TCC_EA0_RDREQ_64B_sum", "TCC_EA0_RDREQ_128B_sum",
+                 "TCC_EA0_RDREQ_DRAM_32B_sum"]
+WRITE_COUNTERS = ["TCC_EA0_WRREQ_sum", "TCC_EA0_WRREQ_64B_sum", "TCC_EA0_WRREQ_WRITE_DRAM_32B_sum",
+                  "TCC_BUBBLE_sum"]
 METRIC = "achieved HBM GB/s (frac of peak) + dense-equiv TOPS, bitmap SpMM at N=1..32"
 
-# kernel symbol fragment per algorithm, and whether it reads one 4-byte
-# offset per tile (else one per 16-row block)
 SWEEP = [("qkv", 0, n) for n in (1, 2, 4, 8, 16, 32)] + [("lowsparse", 0, 16), ("lowsparse", 0, 32)]
-KERNEL_SYMBOL = {"rowwave": "k_rowwave", "valu": "k_valu", "mfma": "k_bt64"}
-READS_TILE_OFFSETS = {"rowwave": True, "valu": False, "mfma": False}
+KERNEL_SYMBOL = {"rowwave": "k_rowwave", "mfma": "k_bt64"}
 
 
 def algo_name(bsp, a):
-    return {bsp.ALGO_ROWWAVE: "rowwave", bsp.ALGO_VALU: "valu", bsp.ALGO_MFMA: "mfma"}[a]
+    return {bsp.ALGO_ROWWAVE: "rowwave", bsp.ALGO_MFMA: "mfma"}[a]
 
 
 def kernel_symbol(bsp, chosen, dt, M, K, N, nnz):
@@ -91,12 +103,22 @@ def source_digest():
     return h.hexdigest()[:16]
 
 
-def step_bytes(dm, N, algo, fp16):
-    """Algorithmic bytes of one SpMM call: stream (+ offsets read) + X + Y."""
-    tile_offsets = READS_TILE_OFFSETS[algo]
-    stream = dm.stream_bytes(with_offsets=tile_offsets)
-    if not tile_offsets:
-        stream += 4 * ((dm.M + 15) // 16 + 1)      # one offset per 16-row block
+def offsets_read(kernel, M, T):
+    """4-byte offsets one launch of `kernel` reads: every tile's (the plain
+    row-wave kernel), one per 16-row block plus the end (the 16-row MFMA
+    kernels), or one per 8-row step plus the end and one half-row start per
+    row (the eight-row fp16 kernel)."""
+    if kernel.startswith("k_rowwave"):
+        return M * T
+    if kernel.startswith("k_bt8_f16"):
+        return (M + 7) // 8 + 1 + M
+    return (M + 15) // 16 + 1
+
+
+def step_bytes(dm, N, kernel, fp16):
+    """Algorithmic bytes of one SpMM call: words, the offsets the kernel
+    reads, payload, X and Y."""
+    stream = dm.stream_bytes(with_offsets=False) + 4 * offsets_read(kernel, dm.M, dm.T)
     if fp16:
         return stream + 2 * N * dm.K + 2 * dm.M * N
     return stream + N * ((dm.K + 1) // 2) + 4 * dm.M * N
@@ -109,24 +131,44 @@ def _pack(X):
     return pins._pack_x_for_test(X)
 
 
-def cpu_baseline(problem, bytes_per_row, max_seconds=20.0):
-    """The oracle as it stands (plain C, one thread): decode the stream to
-    dense, then the exact int64 (fp64 for fp16) triple loop, on a bounded
-    sample of the same workload: the first rows of W, grown until one run
-    takes at least a second (or W is whole), then up to three runs within the
-    time budget. Encoding is not timed. GB/s scales the GPU step's bytes by
-    the share of rows in the sample."""
+def host_threads():
+    """Threads the CPU baseline may use: the process's CPU share (the
+    OMP_NUM_THREADS the host sets for it, else the CPUs it may run on)."""
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        return int(env)
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+def _time_oracle(problem, Xin, threads, max_seconds):
+    """Rows sampled and median seconds of the oracle on the first rows of W:
+    the sample grows until one run takes at least a second (or W is whole),
+    then runs repeat until three are taken or the budget is spent (at least
+    one second of runs when W is whole)."""
     import numpy as np
     import oracle
     M = problem.M
-    Xin = problem.X if problem.dtype == "fp16" else _pack(problem.X)
 
     def run(s):
         t0 = time.perf_counter()
         if problem.dtype == "fp16":
-            oracle.spmm_f16(s, Xin)
+            oracle.spmm_f16(s, Xin, threads=threads)
         else:
-            oracle.spmm_w4a4(s, Xin, problem.N)
+            oracle.spmm_w4a4(s, Xin, problem.N, threads=threads)
         return time.perf_counter() - t0
 
     rows = min(M, 64)
@@ -137,15 +179,121 @@ def cpu_baseline(problem, bytes_per_row, max_seconds=20.0):
             break
         rows = min(M, rows * max(2, int(1.5 / max(t, 1e-3))))
     times = [t]
-    while len(times) < 3 and sum(times) + t < max_seconds:
+    while (len(times) < 3 or sum(times) < 1.0) and sum(times) + t < max_seconds and len(times) < 50:
         times.append(run(s))
-    t_run = statistics.median(times)
-    gbs = bytes_per_row * rows / t_run / 1e9
-    return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {rows} of {M} rows of {problem.name} (K={problem.K}, N={problem.N}): "
-                      f"decode + exact triple loop, median of {len(times)} runs of {t_run:.2f} s; "
-                      f"bytes scaled per row from the GPU step",
-            "cpu": platform.processor() or platform.machine()}
+    return rows, statistics.median(times), len(times)
+
+
+def cpu_baseline(problem, bytes_per_row, max_seconds=12.0):
+    """The oracle as it stands (plain C: decode the stream to dense, then the
+    exact int64 -- fp64 for fp16 -- triple loop), its rows split over every
+    thread the process may use, and again on one thread, on a bounded sample
+    of the same workload. Encoding is not timed. GB/s scales the GPU step's
+    bytes by the share of rows in the sample."""
+    Xin = problem.X if problem.dtype == "fp16" else _pack(problem.X)
+    nthr = host_threads()
+    rows, t_all, n_all = _time_oracle(problem, Xin, nthr, max_seconds)
+    rows1, t_one, n_one = _time_oracle(problem, Xin, 1, max_seconds)
+    sample = (f"{{rows}} of {problem.M} rows of {problem.name} (K={problem.K}, N={problem.N}): decode + exact "
+              f"triple loop, median of {{n}} runs of {{t:.3f}} s; bytes scaled per row from the GPU step")
+    return {"value": round(bytes_per_row * rows / t_all / 1e9, 4), "unit": "GB/s", "cores": nthr, "kind": "oracle",
+            "sample": sample.format(rows=rows, n=n_all, t=t_all) + f"; rows split over {nthr} threads",
+            "cpu": cpu_model(), "nproc": os.cpu_count(),
+            "one_core": {"value": round(bytes_per_row * rows1 / t_one / 1e9, 4), "unit": "GB/s", "cores": 1,
+                         "sample": sample.format(rows=rows1, n=n_one, t=t_one)}}
+
+
+# ---------------------------------------------------------------- read probe
+
+def _probe_lib():
+    import ctypes
+    path = os.path.join(ROOT, "bit_unstructured_sparse_amd", "libbsp_probe.so")
+    if not os.path.exists(path):
+        raise SystemExit(f"{path} is missing; build it with `python -m bit_unstructured_sparse_amd.build`")
+    L = ctypes.CDLL(path)
+    P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    L.bsp_probe_read.argtypes, L.bsp_probe_read.restype = [P, I64, P, I32, I32, I32, P], I32
+    L.bsp_probe_sink_words.argtypes, L.bsp_probe_sink_words.restype = [I32, I32], I64
+    return L
+
+
+def _probe_launch(L, buf_ptr, nbytes, sink, mode, grid, block):
+    import ctypes
+    import torch
+    rc = L.bsp_probe_read(ctypes.c_void_p(buf_ptr), nbytes, ctypes.c_void_p(sink.data_ptr()), mode, grid, block,
+                          ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    if rc != 0:
+        raise RuntimeError(f"bsp_probe_read failed: {rc}")
+
+
+def probe_achievable(nbytes, steps):
+    """What a plain streaming read reaches on this GPU: per launch for
+    `nbytes` (each of `steps` launches in a graph reads its own slice, with
+    >= 1 GiB of other slices read between a slice's warm-up and timed use,
+    as the SpMM steps are timed), best over launch shapes and load forms;
+    and one launch over 1 GiB."""
+    import torch
+    L = _probe_lib()
+    dev = torch.device("cuda:0")
+    nb = (nbytes + 15) // 16 * 16
+    slot = (nb + 4095) // 4096 * 4096
+    nflush = -(-FLUSH_BYTES // slot)
+    nslots = steps + nflush
+    buf = torch.empty(nslots * slot, dtype=torch.uint8, device=dev)
+    buf.fill_(0x5A)
+    big = max(g * (b // 64) for g, b in PROBE_SHAPES)
+    sink = torch.zeros(big, dtype=torch.int32, device=dev)
+    base = buf.data_ptr()
+    best = None
+    for mode in PROBE_MODES:
+        for grid, block in PROBE_SHAPES:
+            g = torch.cuda.CUDAGraph()
+            cs = torch.cuda.Stream()
+            cs.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(cs):
+                with torch.cuda.graph(g, stream=cs):
+                    for i in range(steps):
+                        _probe_launch(L, base + i * slot, nb, sink, mode, grid, block)
+            torch.cuda.synchronize()
+            g.replay()
+            for i in range(steps, nslots):
+                _probe_launch(L, base + i * slot, nb, sink, mode, grid, block)
+            torch.cuda.synchronize()
+            stream = torch.cuda.current_stream()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / steps
+            if best is None or us < best[0]:
+                best = (us, mode, grid, block)
+            del g
+    # one launch over 1 GiB, alternating between two halves of a 2 GiB buffer
+    del buf
+    torch.cuda.empty_cache()
+    gib = 1 << 30
+    buf2 = torch.empty(2 * gib, dtype=torch.uint8, device=dev)
+    buf2.fill_(0x33)
+    us_big = []
+    for rep in range(6):
+        stream = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        _probe_launch(L, buf2.data_ptr() + (rep % 2) * gib, gib, sink, best[1], best[2], best[3])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if rep >= 2:
+            us_big.append(e0.elapsed_time(e1) * 1e3)
+    del buf2
+    torch.cuda.empty_cache()
+    us, mode, grid, block = best
+    t_big = statistics.median(us_big)
+    return {"unit": "GB/s", "bytes_per_launch": nb, "one_launch": round(nb / (us * 1e-6) / 1e9, 2),
+            "one_launch_us": round(us, 3), "large_read": round(gib / (t_big * 1e-6) / 1e9, 2),
+            "large_read_bytes": gib,
+            "probe": f"bsp_probe_read mode {mode} ({PROBE_MODES[mode]}), grid {grid} x {block} threads, "
+                     f"best of {len(PROBE_MODES) * len(PROBE_SHAPES)} forms; {steps} launches in a graph"}
 
 
 # ---------------------------------------------------------------- profiles
@@ -159,20 +307,6 @@ def _csv_rows(d, suffix):
         with open(f, newline="") as fh:
             rows.extend(csv.DictReader(fh))
     return rows
-
-
-def _counter_per_kernel(d, counter):
-    """Mean counter value per dispatch, per kernel name (rocprofv3 csv)."""
-    per = {}
-    for r in _csv_rows(d, "counter_collection.csv"):
-        if r.get("Counter_Name") != counter:
-            continue
-        key = (r.get("Kernel_Name", "?"), r.get("Dispatch_Id", r.get("Correlation_Id")))
-        per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
-    by_kernel = {}
-    for (k, _), v in per.items():
-        by_kernel.setdefault(k, []).append(v)
-    return {k: (statistics.mean(v), len(v)) for k, v in by_kernel.items()}
 
 
 def _pick(table, fragment):
@@ -202,31 +336,71 @@ def summarize_trace(d, out, header):
     print("\n".join(lines))
 
 
-def summarize_traffic(out, fetch, write, copy_fetch, copy_write, fragment, header):
-    f_k = _counter_per_kernel(fetch, "FETCH_SIZE")
-    w_k = _counter_per_kernel(write, "WRITE_SIZE")
-    cf = _counter_per_kernel(copy_fetch, "FETCH_SIZE")
-    cw = _counter_per_kernel(copy_write, "WRITE_SIZE")
-    kf, kw = _pick(f_k, fragment), _pick(w_k, fragment)
-    ck = _pick(cf, "bitwise_not")
-    # counters read KiB per dispatch; the copy reads and writes COPY_BYTES
-    fetch_factor = COPY_BYTES / (cf[ck][0] * 1024.0)
-    write_factor = COPY_BYTES / (cw[_pick(cw, "bitwise_not")][0] * 1024.0)
-    fetch_b = f_k[kf][0] * 1024.0 * fetch_factor
-    write_b = w_k[kw][0] * 1024.0 * write_factor
-    lines = [f"# {h}" for h in header] + [
-        f"kernel: {kf}",
-        f"dispatches: fetch {f_k[kf][1]}, write {w_k[kw][1]}",
-        f"fetch_kib_per_dispatch: {f_k[kf][0]:.1f}",
-        f"write_kib_per_dispatch: {w_k[kw][0]:.1f}",
-        f"copy_kernel: {ck}",
-        f"copy_fetch_kib_per_dispatch: {cf[ck][0]:.1f}  (copy of {COPY_BYTES} bytes)",
-        f"copy_write_kib_per_dispatch: {cw[_pick(cw, 'bitwise_not')][0]:.1f}",
-        f"fetch_factor: {fetch_factor:.4f}",
-        f"write_factor: {write_factor:.4f}",
-        f"traffic_bytes_per_launch: {fetch_b + write_b:.0f}",
-        f"source_digest: {source_digest()}",
-    ]
+def _counters_by_kernel(d, names):
+    """{kernel: {counter: mean per dispatch}} over a rocprofv3 --pmc csv."""
+    per = {}
+    for r in _csv_rows(d, "counter_collection.csv"):
+        c = r.get("Counter_Name")
+        if c not in names:
+            continue
+        key = (r.get("Kernel_Name", "?"), r.get("Dispatch_Id", r.get("Correlation_Id")), c)
+        per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    out = {}
+    for (k, _, c), v in per.items():
+        out.setdefault(k, {}).setdefault(c, []).append(v)
+    return {k: {c: (statistics.mean(v), len(v)) for c, v in cs.items()} for k, cs in out.items()}
+
+
+def traffic_estimators(rd, wr):
+    """HBM bytes of one dispatch from the TCC counters, two ways:
+    'by_size' -- read requests by size (32/64/128 B) and write requests by
+    size (32/64 B) leaving the L2 for memory; 'dram_32b' -- the counts of
+    32-byte DRAM units (a 64-byte request counts 2, a 128-byte one 4)."""
+    g = lambda t, c: t.get(c, (0.0, 0))[0]
+    by_size_r = 32 * g(rd, "TCC_EA0_RDREQ_32B_sum") + 64 * g(rd, "TCC_EA0_RDREQ_64B_sum") \
+        + 128 * g(rd, "TCC_EA0_RDREQ_128B_sum")
+    by_size_w = 32 * (g(wr, "TCC_EA0_WRREQ_sum") - g(wr, "TCC_EA0_WRREQ_64B_sum")) + 64 * g(wr, "TCC_EA0_WRREQ_64B_sum")
+    return {"by_size": (by_size_r, by_size_w),
+            "dram_32b": (32 * g(rd, "TCC_EA0_RDREQ_DRAM_32B_sum"), 32 * g(wr, "TCC_EA0_WRREQ_WRITE_DRAM_32B_sum"))}
+
+
+def summarize_traffic(out, reads, writes, fragment, header):
+    """Traffic of one launch of the kernel matching `fragment`, with the
+    estimator that reproduces the known bytes of both calibration kernels of
+    the same run (the read probe: COPY_BYTES read; the copy: COPY_BYTES read
+    and written) within 5 %."""
+    R = _counters_by_kernel(reads, set(READ_COUNTERS))
+    W = _counters_by_kernel(writes, set(WRITE_COUNTERS))
+    kr, kw = _pick({k: (0, v[READ_COUNTERS[0]][1]) for k, v in R.items()}, fragment), \
+        _pick({k: (0, v[WRITE_COUNTERS[0]][1]) for k, v in W.items()}, fragment)
+    pr = _pick({k: (0, 1) for k in R}, "k_probe_read")
+    cr = _pick({k: (0, 1) for k in R}, "bitwise_not")
+    pw = _pick({k: (0, 1) for k in W}, "k_probe_read")
+    cw = _pick({k: (0, 1) for k in W}, "bitwise_not")
+    lines = [f"# {h}" for h in header] + [f"kernel: {kr}", f"dispatches: reads {R[kr][READ_COUNTERS[0]][1]}, "
+                                                           f"writes {W[kw][WRITE_COUNTERS[0]][1]}"]
+    for c in READ_COUNTERS:
+        lines.append(f"{c}: {R[kr].get(c, (0.0, 0))[0]:.0f}")
+    for c in WRITE_COUNTERS:
+        lines.append(f"{c}: {W[kw].get(c, (0.0, 0))[0]:.0f}")
+    chosen = None
+    for name in ("dram_32b", "by_size"):
+        p_r, p_w = traffic_estimators(R[pr], W[pw])[name]
+        c_r, c_w = traffic_estimators(R[cr], W[cw])[name]
+        ratios = (p_r / COPY_BYTES, c_r / COPY_BYTES, c_w / COPY_BYTES)
+        ok = all(abs(x - 1.0) <= 0.05 for x in ratios)
+        lines.append(f"estimator {name}: read probe reads {p_r:.0f} of {COPY_BYTES} B ({ratios[0]:.4f}); copy reads "
+                     f"{c_r:.0f} ({ratios[1]:.4f}) and writes {c_w:.0f} ({ratios[2]:.4f}) of {COPY_BYTES} B: "
+                     f"{'within' if ok else 'outside'} 5 %")
+        if ok and chosen is None:
+            chosen = name
+    if chosen is not None:
+        k_r, k_w = traffic_estimators(R[kr], W[kw])[chosen]
+        lines += [f"estimator: {chosen}", f"read_bytes_per_launch: {k_r:.0f}", f"write_bytes_per_launch: {k_w:.0f}",
+                  f"traffic_bytes_per_launch: {k_r + k_w:.0f}"]
+    else:
+        lines += ["estimator: none (no estimator reproduces both calibration kernels within 5 %)"]
+    lines.append(f"source_digest: {source_digest()}")
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -252,7 +426,8 @@ def summarize_counters(d, out, fragment, header):
 
 def read_traffic(path):
     """Bytes per launch from a traffic summary, or None when the summary is
-    missing or was taken from other kernel sources."""
+    missing, has no calibrated estimator, or was taken from other kernel
+    sources."""
     if not os.path.exists(path):
         return None
     kv = {}
@@ -261,35 +436,38 @@ def read_traffic(path):
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 kv[k.strip()] = v.strip()
-    if kv.get("source_digest") != source_digest():
+    if kv.get("source_digest") != source_digest() or "traffic_bytes_per_launch" not in kv:
         return None
     return float(kv["traffic_bytes_per_launch"])
 
 
-def copy_calibration():
+def calibration_kernels():
+    """The two kernels of known traffic the counter passes are checked on: the
+    read probe over COPY_BYTES (reads them) and an int32 bitwise_not over
+    COPY_BYTES (reads and writes them), five launches each, on buffers far
+    larger than the Infinity Cache."""
     import torch
     n = COPY_BYTES // 4
     src = torch.arange(n, dtype=torch.int32, device="cuda:0")
     dst = torch.empty_like(src)
+    other = torch.empty(4 * COPY_BYTES // 4, dtype=torch.int32, device="cuda:0")
+    L = _probe_lib()
+    sink = torch.zeros(L.bsp_probe_sink_words(1024, 256), dtype=torch.int32, device="cuda:0")
     for _ in range(5):
+        other.fill_(1)          # evicts src from the Infinity Cache between launches
+        _probe_launch(L, src.data_ptr(), COPY_BYTES, sink, 0, 1024, 256)
+    for _ in range(5):
+        other.fill_(2)
         torch.bitwise_not(src, out=dst)
-    # a read-only pass of the same bytes (a reduction): the fetch counter's
-    # factor for a kernel that streams loads without stores
-    total = None
-    for _ in range(5):
-        total = torch.sum(src, dtype=torch.int64)
     torch.cuda.synchronize()
-    assert int(total.item()) == n * (n - 1) // 2
     ok = bool(torch.equal(dst[:1024], ~src[:1024]))
-    print(json.dumps({"copy_calibration_bytes": COPY_BYTES, "dispatches": 5, "ok": ok}), flush=True)
+    print(json.dumps({"calibration_bytes": COPY_BYTES, "dispatches": 5, "ok": ok}), flush=True)
 
 
 # ---------------------------------------------------------------- main
 
-def measure(args, workload, index, n):
-    """Time one workload (n > 0 slices its widest X to N = n); returns the
-    bench record without the CPU baseline."""
-    import numpy as np
+def prepare(args, workload, index, n):
+    """The problem, its encoding and device copies, and a step function."""
     import torch
     import bit_unstructured_sparse_amd as bsp
     import workloads
@@ -305,12 +483,10 @@ def measure(args, workload, index, n):
                                     problem.dtype, problem.W, X[:n], dict(problem.meta, N=n))
     fp16 = problem.dtype == "fp16"
     N, M, K = problem.N, problem.M, problem.K
-
     enc = bsp.encode(problem.W)
-    algo = {"auto": bsp.ALGO_AUTO, "rowwave": bsp.ALGO_ROWWAVE, "valu": bsp.ALGO_VALU, "mfma": bsp.ALGO_MFMA}[args.algo]
+    algo = {"auto": bsp.ALGO_AUTO, "rowwave": bsp.ALGO_ROWWAVE, "mfma": bsp.ALGO_MFMA}[args.algo]
     dt = bsp.FP16 if fp16 else bsp.INT4
     chosen = algo if algo != bsp.ALGO_AUTO else bsp.select(dt, M, K, N, enc.nnz)
-    name = algo_name(bsp, chosen)
     dm0 = enc.to_device(dev)
     if fp16:
         Xd = torch.from_numpy(problem.X.copy()).to(dev)
@@ -321,7 +497,9 @@ def measure(args, workload, index, n):
     esize = 2 if fp16 else 4
     ws = (dm0.bitmaps.numel() * 8 + dm0.offsets.numel() * 4 + dm0.payload.numel() * dm0.payload.element_size()
           + Xd.numel() * Xd.element_size() + esize * M * N)
-    R = max(1, -(-ROTATE_TARGET // ws))
+    # copies 0..steps-1 are the timed steps'; the rest (>= FLUSH_BYTES) are
+    # run between the graph's warm-up replay and its timed replay
+    R = args.steps + max(1, -(-FLUSH_BYTES // ws))
     copies = [(dm0, Xd, torch.empty((N, M), dtype=y_dtype, device=dev))]
     for _ in range(R - 1):
         dm = bsp.DeviceMatrix(enc.dtype, M, K, enc.nnz, dm0.bitmaps.clone(), dm0.offsets.clone(), dm0.payload.clone())
@@ -335,15 +513,30 @@ def measure(args, workload, index, n):
         else:
             bsp.spmm_w4a4(dm, x, N, Y=y, algo=chosen)
 
+    kernel = kernel_symbol(bsp, chosen, dt, M, K, N, enc.nnz)
+    return dict(problem=problem, fp16=fp16, enc=enc, dm0=dm0, copies=copies, R=R, step=step, chosen=chosen,
+                name=algo_name(bsp, chosen), kernel=kernel, dt=dt)
+
+
+def measure(args, workload, index, n, with_probe=True):
+    """Time one workload (n > 0 slices its widest X to N = n); returns the
+    bench record without the CPU baseline."""
+    import numpy as np
+    import torch
+
+    ctx = prepare(args, workload, index, n)
+    problem, fp16, enc, dm0, copies, R, step = (ctx[k] for k in ("problem", "fp16", "enc", "dm0", "copies", "R",
+                                                                   "step"))
+    N, M, K = problem.N, problem.M, problem.K
     for i in range(args.warmup):
-        step(i)
+        step(args.steps + i % (R - args.steps))
     torch.cuda.synchronize()
     # spot check of the timed configuration against an independent dense
     # product on a sample of rows (exact integers; fp16 within the 1e-2 bound)
     rows = np.random.default_rng(0).choice(M, size=min(M, 256), replace=False)
 
-    def spot_ok():
-        got = copies[0][2].cpu().numpy()[:, rows]
+    def spot_ok(i):
+        got = copies[i][2].cpu().numpy()[:, rows]
         if fp16:
             ref = (problem.W[rows].astype(np.float64) @ problem.X.astype(np.float64).T).T
             floor = 0.01 * np.sqrt(np.mean(ref ** 2))
@@ -352,10 +545,10 @@ def measure(args, workload, index, n):
         ref = (problem.W[rows].astype(np.int64) @ problem.X.astype(np.int64).T).T
         return bool(np.array_equal(got, ref))
 
-    parity = spot_ok()
+    parity = spot_ok(args.steps)
 
     # timed region: exactly K steps, captured once in a HIP graph (one node
-    # per SpMM call, cycling through the rotated copies) and replayed
+    # per SpMM call, step i on copy i) and replayed
     capture_stream = torch.cuda.Stream()
     capture_stream.wait_stream(torch.cuda.current_stream())
     graph = torch.cuda.CUDAGraph()
@@ -365,6 +558,8 @@ def measure(args, workload, index, n):
                 step(i)
     torch.cuda.synchronize()
     graph.replay()                  # first replay is warm-up
+    for i in range(args.steps, R):  # >= 1 GiB of other copies: the timed steps' copies leave the caches
+        step(i)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()     # graph.replay() launches on this stream
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -376,17 +571,29 @@ def measure(args, workload, index, n):
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
     kern_ms = ev0.elapsed_time(ev1) / args.steps     # average launch duration (HIP events)
-    parity = parity and spot_ok()
+    parity = parity and spot_ok(0) and spot_ok(args.steps - 1)
+    del graph
 
-    nbytes = step_bytes(dm0, N, name, fp16)
+    kernel = ctx["kernel"]
+    nbytes = step_bytes(dm0, N, kernel, fp16)
     value = nbytes / (ms_per_step * 1e-3) / 1e9
     achieved = nbytes / (kern_ms * 1e-3) / 1e9
     dense_ops = 2.0 * M * K * N
     useful_ops = 2.0 * enc.nnz * N
     wl = f"{problem.name}_n{N}" if not problem.name.endswith(f"_n{N}") else problem.name
-    traffic = read_traffic(os.path.join(ROOT, "profiles", f"traffic_{name}_{wl}.txt"))
+    traffic = read_traffic(os.path.join(ROOT, "profiles", f"traffic_{ctx['name']}_{wl}.txt"))
+    del copies, ctx
+    torch.cuda.empty_cache()
+    achievable = probe_achievable(nbytes, args.steps) if with_probe else None
 
     density = enc.nnz / (M * K)
+    roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None if traffic is None else int(traffic),
+            "kernel": kernel, "bytes_per_launch": nbytes}
+    if achievable is not None:
+        roof["achievable"] = achievable
+        roof["frac_of_achievable_one_launch"] = round(achieved / achievable["one_launch"], 4)
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -402,22 +609,36 @@ def measure(args, workload, index, n):
         "data": "synthetic (seeded iid unstructured mask / magnitude pruning; the pages' model weights "
                 "are not available)",
         "config": {"workload": f"{wl}: W {M}x{K} {'fp16' if fp16 else 'int4'}, density {density:.3f}, N={N}",
-                   "M": M, "K": K, "N": N, "nnz": enc.nnz, "kernel": name,
+                   "M": M, "K": K, "N": N, "nnz": enc.nnz, "kernel": algo_label(kernel),
                    "rotated_copies": R, "bytes_per_step": nbytes},
         "frac_of_peak": round(value / HBM_PEAK_GBS, 4),
         "tops_dense_equiv": round(dense_ops / (ms_per_step * 1e-3) / 1e12, 3),
         "tops_useful": round(useful_ops / (ms_per_step * 1e-3) / 1e12, 3),
         "kernel_us_avg": round(kern_ms * 1e3, 3),
-        "timing": "K steps captured in one HIP graph and replayed back to back; value uses host wall time "
-                  "around the replay, roofline uses HIP events on the replay stream",
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None if traffic is None else int(traffic),
-                     "kernel": kernel_symbol(bsp, chosen, dt, M, K, N, enc.nnz), "bytes_per_launch": nbytes},
+        "timing": "K steps captured in one HIP graph (step i on its own copy i) and replayed back to back after "
+                  ">= 1 GiB of other copies; value uses host wall time around the replay, roofline uses HIP "
+                  "events on the replay stream",
+        "roofline": roof,
         "parity_sample_ok": parity,
     }
     args._problem = problem
     return out
+
+
+def algo_label(kernel):
+    return "rowwave" if kernel.startswith("k_rowwave") else "mfma"
+
+
+def counter_run(args):
+    """One process for the --pmc passes: the two calibration kernels, then
+    the workload's SpMM steps (eager, each on its own copy)."""
+    import torch
+    calibration_kernels()
+    ctx = prepare(args, args.workload, args.index, args.n)
+    for i in range(args.steps):
+        ctx["step"](i)
+    torch.cuda.synchronize()
+    print(json.dumps({"counter_run": ctx["problem"].name, "steps": args.steps, "kernel": ctx["kernel"]}), flush=True)
 
 
 def main():
@@ -428,16 +649,17 @@ def main():
     ap.add_argument("--workload", default="qkv", help="tiny | qkv | ffn | lowsparse | fp16")
     ap.add_argument("--index", type=int, default=0, help="matrix index inside the workload (ffn: 0 up, 1 down)")
     ap.add_argument("--n", type=int, default=0, help="override N (slices the workload's widest X)")
-    ap.add_argument("--algo", default="auto", choices=["auto", "rowwave", "valu", "mfma"])
+    ap.add_argument("--algo", default="auto", choices=["auto", "rowwave", "mfma"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-probe", action="store_true", help="leave out the read probe (roofline.achievable)")
     ap.add_argument("--sweep", action="store_true", help="one line per (workload, N) of the N sweep")
-    ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--peak-read", action="store_true", help="the read probe alone at this workload's byte count")
+    ap.add_argument("--counter-run", action="store_true", help="calibration kernels + SpMM steps, for --pmc passes")
     ap.add_argument("--summarize-trace", nargs=2, metavar=("DIR", "OUT"))
     ap.add_argument("--summarize-traffic", metavar="OUT")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("DIR", "OUT"))
-    ap.add_argument("--fetch"), ap.add_argument("--write")
-    ap.add_argument("--copy-fetch"), ap.add_argument("--copy-write")
-    ap.add_argument("--kernel", default="w4a4", help="kernel name fragment for --summarize-traffic")
+    ap.add_argument("--reads"), ap.add_argument("--writes")
+    ap.add_argument("--kernel", default="w4a4", help="kernel name fragment for the summaries")
     ap.add_argument("--note", action="append", default=[], help="header line for a summary")
     args = ap.parse_args()
 
@@ -446,19 +668,26 @@ def main():
     if args.summarize_counters:
         return summarize_counters(args.summarize_counters[0], args.summarize_counters[1], args.kernel, args.note)
     if args.summarize_traffic:
-        return summarize_traffic(args.summarize_traffic, args.fetch, args.write, args.copy_fetch,
-                                 args.copy_write, args.kernel, args.note)
+        return summarize_traffic(args.summarize_traffic, args.reads, args.writes, args.kernel, args.note)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the path has no "
               f"multi-GPU code; how it would shard is described with the design.", file=sys.stderr)
         sys.exit(2)
-    if args.copy_calibration:
-        return copy_calibration()
+    if args.counter_run:
+        return counter_run(args)
+    if args.peak_read:
+        import torch
+        ctx = prepare(args, args.workload, args.index, args.n)
+        nbytes = step_bytes(ctx["dm0"], ctx["problem"].N, ctx["kernel"], ctx["fp16"])
+        del ctx
+        torch.cuda.empty_cache()
+        print(json.dumps({"peak_read": probe_achievable(nbytes, args.steps)}), flush=True)
+        return
 
     if args.sweep:
         # the N sweep on the qkv weights and the 70 %-dense matrix at N = 16, 32
         for wl, idx, n in SWEEP:
-            out = measure(args, wl, idx, n)
+            out = measure(args, wl, idx, n, with_probe=False)
             print(json.dumps({"sweep": out["config"]["workload"].split(":")[0], "N": out["config"]["N"],
                               "kernel": out["roofline"]["kernel"], "kernel_us_avg": out["kernel_us_avg"],
                               "GB/s (events)": out["roofline"]["achieved"], "GB/s (wall)": out["value"],
@@ -466,7 +695,7 @@ def main():
                               "tops_useful": out["tops_useful"], "parity_sample_ok": out["parity_sample_ok"]}),
                   flush=True)
         return
-    out = measure(args, args.workload, args.index, args.n)
+    out = measure(args, args.workload, args.index, args.n, with_probe=not args.no_probe)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args._problem, out["config"]["bytes_per_step"] / out["config"]["M"])
     print(json.dumps(out), flush=True)

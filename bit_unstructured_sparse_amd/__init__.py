@@ -22,15 +22,15 @@ from typing import Optional
 import numpy as np
 
 __all__ = ["load_library", "encode", "pack_int4", "Encoded", "DeviceMatrix", "spmm_w4a4", "spmm_f16",
-           "select", "describe", "BspError", "ALGO_AUTO", "ALGO_ROWWAVE", "ALGO_VALU", "ALGO_MFMA",
+           "select", "describe", "BspError", "ALGO_AUTO", "ALGO_ROWWAVE", "ALGO_MFMA",
            "INT4", "FP16", "PAYLOAD_ALIGN", "MAX_N", "library_path"]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(HERE, "libbitmap_spmm.so")
 
-OK, E_ARG, E_RANGE, E_CAPACITY, E_OVERFLOW, E_HIP = 0, 1, 2, 3, 4, 5
+OK, E_ARG, E_RANGE, E_CAPACITY, E_OVERFLOW, E_HIP, E_UNSUPPORTED = 0, 1, 2, 3, 4, 5, 6
 INT4, FP16 = 0, 1
-ALGO_AUTO, ALGO_ROWWAVE, ALGO_VALU, ALGO_MFMA = 0, 1, 2, 3
+ALGO_AUTO, ALGO_ROWWAVE, ALGO_MFMA = 0, 1, 2
 PAYLOAD_ALIGN = 16
 MAX_N = 32
 

@@ -217,6 +217,7 @@ extern "C" const char *bsp_status_string(int status) {
         case BSP_E_CAPACITY: return "payload buffer too small";
         case BSP_E_OVERFLOW: return "size beyond the supported range";
         case BSP_E_HIP: return "HIP launch error";
+        case BSP_E_UNSUPPORTED: return "the forced kernel cannot run this shape";
         default: return "unknown status";
     }
 }

@@ -129,13 +129,42 @@ __device__ __forceinline__ void bt_barrier_lds() {
     asm volatile("" ::: "memory");
 }
 
+// Range of the X buffer resource: its N rows of xs bytes, rounded up to a
+// whole dword. The hardware checks the range per dword, so a last dword only
+// partly inside N * xs would read as zero; the dword holding the buffer's last
+// byte lies in the same page as that byte, and its bytes past the end meet
+// zero bits of the last tile (columns >= K).
+__device__ __forceinline__ uint32_t bt_x_range(int N, uint32_t xs) {
+    return ((uint32_t)N * xs + 3u) & ~3u;
+}
+
+// 16 bytes of X at byte offset off. X rows start on a 4-byte boundary when
+// K % 8 == 0 (XU false): one 16-byte load. Otherwise (XU true) the dwords
+// around the bytes are loaded from the 4-byte boundary below off and the
+// bytes are funnel-shifted into place (v_alignbyte_b32). An offset past the
+// buffer reads zeros either way.
+template <bool XU>
+__device__ __forceinline__ bt_v4i bt_load_x16(__amdgpu_buffer_rsrc_t xrs, uint32_t off) {
+    if constexpr (!XU) {
+        return __builtin_bit_cast(bt_v4i, __builtin_amdgcn_raw_buffer_load_b128(xrs, off, 0, 0));
+    } else {
+        const uint32_t a = off & ~3u, sh = off & 3u;
+        const bt_v4i d = __builtin_bit_cast(bt_v4i, __builtin_amdgcn_raw_buffer_load_b128(xrs, a, 0, 0));
+        const uint32_t e = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(xrs, a + 16u, 0, 0);
+        return bt_v4i{(int)__builtin_amdgcn_alignbyte((uint32_t)d.y, (uint32_t)d.x, sh),
+                      (int)__builtin_amdgcn_alignbyte((uint32_t)d.z, (uint32_t)d.y, sh),
+                      (int)__builtin_amdgcn_alignbyte((uint32_t)d.w, (uint32_t)d.z, sh),
+                      (int)__builtin_amdgcn_alignbyte(e, (uint32_t)d.w, sh)};
+    }
+}
+
 // X of a wavefront's 4 TPL consecutive tiles (lane group q owns tiles
 // q TPL .. q TPL + TPL - 1 of them) is 8 TPL contiguous 16-byte granules of
 // each X row. Load i (i < 2 TPL) gives lane group q granule 4 i + q, so one
 // load covers 64-byte runs of 16 rows; slices loaded lane by lane touch one
 // line per lane instead, and the line requests, not the bytes, bound how
 // fast X comes in. Columns n >= N and tiles >= T read zeros.
-template <int NB, int TPL>
+template <int NB, int TPL, bool XU>
 __device__ __forceinline__ void bt_load_x_runs(__amdgpu_buffer_rsrc_t xrs, int r, int q, int wave, int T, int N,
                                                uint32_t xs, bt_v4i (&xg)[NB][2 * TPL]) {
 #pragma unroll
@@ -146,7 +175,7 @@ __device__ __forceinline__ void bt_load_x_runs(__amdgpu_buffer_rsrc_t xrs, int r
             const uint32_t gi = 4u * (uint32_t)i + (uint32_t)q;
             const uint32_t tt = (uint32_t)(wave * 4 * TPL) + (gi >> 1);
             const uint32_t off = (n < N && tt < (uint32_t)T) ? (uint32_t)n * xs + tt * 32u + (gi & 1u) * 16u : 0xFFFFFFE0u;
-            xg[nb][i] = __builtin_bit_cast(bt_v4i, __builtin_amdgcn_raw_buffer_load_b128(xrs, off, 0, 0));
+            xg[nb][i] = bt_load_x16<XU>(xrs, off);
         }
     }
 }
@@ -301,7 +330,8 @@ __device__ __forceinline__ BtRange bt_range(uint32_t nibA, uint32_t nibB) {
 //   [row totals NBLK x 16 x 8 ints][sums 3 x NB x 256 ints][selector table copies]
 //   [nbuf staging buffers of stage_bytes]
 // Workgroup g owns blocks [g*bq + min(g, br), ...): bq or bq + 1 of them.
-template <int NB, int TPL>
+// XU: X rows are not on a 4-byte boundary (K % 8 != 0).
+template <int NB, int TPL, bool XU>
 // (The arguments the first loads need come first: they are the ones a
 // kernel-argument preload would place in registers.)
 __global__ __launch_bounds__(BT_WG_THREADS(TPL)) void k_bt64_w4a4(
@@ -320,7 +350,7 @@ __global__ __launch_bounds__(BT_WG_THREADS(TPL)) void k_bt64_w4a4(
     const int b_begin = gid * bq + min(gid, br);
     const int nblk = bq + (gid < br ? 1 : 0);           // 1 .. NBLK
     const int t0 = (wave * 4 + q) * TPL;                 // first tile of this lane
-    const uint32_t xs = (uint32_t)K >> 1;               // X row stride in bytes (K % 32 == 0 here)
+    const uint32_t xs = ((uint32_t)K + 1u) >> 1;        // X row stride in bytes
 
     int32_t *wt = reinterpret_cast<int32_t *>(bt_smem);                                 // [NBLK][16][8]
     int32_t *sums = wt + NBLK * BT_ROWS * WC;                                            // [3][NB*256]
@@ -359,7 +389,7 @@ __global__ __launch_bounds__(BT_WG_THREADS(TPL)) void k_bt64_w4a4(
     // this lane's X slices, once for all blocks (column n >= N or tile >= T: zeros)
     uint32_t xw[NB][TPL][8];
     bt_v4i xg[NB][2 * TPL];           // X granules as loaded, in runs of 16 rows
-    bt_load_x_runs<NB, TPL>(bt_rsrc(X, (uint32_t)N * xs), r, q, wave, T, N, xs, xg);
+    bt_load_x_runs<NB, TPL, XU>(bt_rsrc(X, bt_x_range(N, xs)), r, q, wave, T, N, xs, xg);
     vm_issued += 2 * NB * TPL;
     const int m_first = b_begin * BT_ROWS;
     const int wg_rows = min(nblk * BT_ROWS, M - m_first);
@@ -639,7 +669,7 @@ __device__ __forceinline__ void bt_make_b(const uint32_t (&xw)[NB][TPL][8], bt_v
             }
 }
 
-template <int NB, int D>
+template <int NB, int D, bool XU>
 __global__ __launch_bounds__(512) void k_bt64s_w4a4(
         const uint32_t *__restrict__ offsets, int M, int K, int bq, int br, const uint64_t *__restrict__ bitmaps,
         const uint8_t *__restrict__ X, int N, const uint8_t *__restrict__ payload, uint32_t payload_bytes,
@@ -654,7 +684,7 @@ __global__ __launch_bounds__(512) void k_bt64s_w4a4(
     const int b_begin = gid * bq + min(gid, br);
     const int nblk = bq + (gid < br ? 1 : 0);           // 1 .. NBLK
     const int t0 = (wave * 4 + q) * TPL;
-    const uint32_t xs = (uint32_t)K >> 1;
+    const uint32_t xs = ((uint32_t)K + 1u) >> 1;
     asm volatile("" ::"s"(bitmaps), "s"(payload), "s"(X), "s"(Y), "s"(N), "s"(payload_bytes));
 
     // LDS: selector table | row totals [NBLK][16][WC] | partials
@@ -697,16 +727,16 @@ __global__ __launch_bounds__(512) void k_bt64s_w4a4(
     bt_v4i xg[NB][2 * TPL];
     uint32_t xw[NB][TPL][8];
     {
-        const __amdgpu_buffer_rsrc_t xrs = bt_rsrc(X, (uint32_t)N * xs);
+        const __amdgpu_buffer_rsrc_t xrs = bt_rsrc(X, bt_x_range(N, xs));
         if constexpr (NB == 2) {
-            bt_load_x_runs<NB, TPL>(xrs, r, q, wave, T, N, xs, xg);
+            bt_load_x_runs<NB, TPL, XU>(xrs, r, q, wave, T, N, xs, xg);
         } else {
 #pragma unroll
             for (int k = 0; k < TPL; ++k) {
                 const int n = r;
                 const uint32_t off = (n < N && t0 + k < T) ? (uint32_t)n * xs + (uint32_t)(t0 + k) * 32u : 0xFFFFFFE0u;
-                const bt_v4i v0 = __builtin_bit_cast(bt_v4i, __builtin_amdgcn_raw_buffer_load_b128(xrs, off, 0, 0));
-                const bt_v4i v1 = __builtin_bit_cast(bt_v4i, __builtin_amdgcn_raw_buffer_load_b128(xrs, off + 16u, 0, 0));
+                const bt_v4i v0 = bt_load_x16<XU>(xrs, off);
+                const bt_v4i v1 = bt_load_x16<XU>(xrs, off + 16u);
                 xw[0][k][0] = v0.x; xw[0][k][1] = v0.y; xw[0][k][2] = v0.z; xw[0][k][3] = v0.w;
                 xw[0][k][4] = v1.x; xw[0][k][5] = v1.y; xw[0][k][6] = v1.z; xw[0][k][7] = v1.w;
             }
@@ -884,10 +914,11 @@ struct BtPlan {
     size_t lds;             // total dynamic LDS
 };
 
-// Fast-path constraints: X rows 16-byte aligned (K % 32 == 0), K within
-// 8 wavefronts x 4 lane groups x 8 tiles, N <= 32.
+// Fast-path constraints: K within 8 wavefronts x 4 lane groups x 8 tiles
+// (K <= 16384), N <= 32. Any K % 64: the tail of the last tile has zero bits,
+// and X rows off a 4-byte boundary take the funnel-shifted loads.
 static bool bt64_supported(int64_t K, int64_t N) {
-    return K > 0 && K % 32 == 0 && (K + 63) / 64 <= 8 * 4 * 8 && N >= 1 && N <= 32;
+    return K > 0 && (K + 63) / 64 <= 8 * 4 * 8 && N >= 1 && N <= 32;
 }
 
 static bool bt64_plan(int64_t M, int64_t K, int64_t N, int64_t payload_bytes, BtPlan *p) {
@@ -957,27 +988,28 @@ static bool bt64_plan(int64_t M, int64_t K, int64_t N, int64_t payload_bytes, Bt
     return true;
 }
 
-template <int NB, int TPL>
+template <int NB, int TPL, bool XU>
 static void launch_bt64_t(const BtPlan &p, const uint64_t *bitmaps, const uint32_t *offsets,
                           const uint8_t *payload, uint32_t payload_bytes, int M, int K, const uint8_t *X, int N,
                           int32_t *Y, hipStream_t stream) {
-    (void)hipFuncSetAttribute((const void *)k_bt64_w4a4<NB, TPL>, hipFuncAttributeMaxDynamicSharedMemorySize,
+    (void)hipFuncSetAttribute((const void *)k_bt64_w4a4<NB, TPL, XU>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               (int)p.lds);
-    hipLaunchKernelGGL((k_bt64_w4a4<NB, TPL>), dim3(p.grid), dim3(64 * p.nwaves), p.lds, stream, offsets, M, K, p.bq,
+    hipLaunchKernelGGL((k_bt64_w4a4<NB, TPL, XU>), dim3(p.grid), dim3(64 * p.nwaves), p.lds, stream, offsets, M, K, p.bq,
                        p.br, bitmaps, X, N, payload, payload_bytes, Y, p.stage_bytes, p.nbuf, p.one_pass);
 }
 
-static void launch_bt64_w4a4(const BtPlan &p, const uint64_t *bitmaps, const uint32_t *offsets,
-                             const uint8_t *payload, uint32_t payload_bytes, int M, int K, const uint8_t *X, int N,
-                             int32_t *Y, hipStream_t stream) {
+template <bool XU>
+static void launch_bt64_w4a4_x(const BtPlan &p, const uint64_t *bitmaps, const uint32_t *offsets,
+                               const uint8_t *payload, uint32_t payload_bytes, int M, int K, const uint8_t *X, int N,
+                               int32_t *Y, hipStream_t stream) {
     if (p.streaming) {
-#define BTS_LAUNCH(NB, D)                                                                                         \
-    do {                                                                                                          \
-        (void)hipFuncSetAttribute((const void *)k_bt64s_w4a4<NB, D>, hipFuncAttributeMaxDynamicSharedMemorySize, \
-                                  (int)p.lds);                                                                    \
-        hipLaunchKernelGGL((k_bt64s_w4a4<NB, D>), dim3(p.grid), dim3(64 * p.nwaves), p.lds, stream, offsets, M, K, \
-                           p.bq, p.br, bitmaps, X, N, payload, payload_bytes, Y, (uint32_t)p.stagger,             \
-                           (uint32_t)p.area_kb);                                                                  \
+#define BTS_LAUNCH(NB, D)                                                                                             \
+    do {                                                                                                              \
+        (void)hipFuncSetAttribute((const void *)k_bt64s_w4a4<NB, D, XU>, hipFuncAttributeMaxDynamicSharedMemorySize, \
+                                  (int)p.lds);                                                                        \
+        hipLaunchKernelGGL((k_bt64s_w4a4<NB, D, XU>), dim3(p.grid), dim3(64 * p.nwaves), p.lds, stream, offsets, M, K, \
+                           p.bq, p.br, bitmaps, X, N, payload, payload_bytes, Y, (uint32_t)p.stagger,                 \
+                           (uint32_t)p.area_kb);                                                                      \
     } while (0)
         if (p.nb == 1) {
             if (p.streaming == 2) BTS_LAUNCH(1, 2); else if (p.streaming == 3) BTS_LAUNCH(1, 3); else BTS_LAUNCH(1, 4);
@@ -987,11 +1019,21 @@ static void launch_bt64_w4a4(const BtPlan &p, const uint64_t *bitmaps, const uin
 #undef BTS_LAUNCH
         return;
     }
-#define BT_LAUNCH(NB, TPL) launch_bt64_t<NB, TPL>(p, bitmaps, offsets, payload, payload_bytes, M, K, X, N, Y, stream)
+#define BT_LAUNCH(NB, TPL) launch_bt64_t<NB, TPL, XU>(p, bitmaps, offsets, payload, payload_bytes, M, K, X, N, Y, stream)
     if (p.nb == 1) {
         if (p.tpl == 2) BT_LAUNCH(1, 2); else if (p.tpl == 4) BT_LAUNCH(1, 4); else BT_LAUNCH(1, 8);
     } else {
         if (p.tpl == 2) BT_LAUNCH(2, 2); else if (p.tpl == 4) BT_LAUNCH(2, 4); else BT_LAUNCH(2, 8);
     }
 #undef BT_LAUNCH
+}
+
+// X rows of ceil(K/2) bytes sit on a 4-byte boundary when K % 8 == 0
+static void launch_bt64_w4a4(const BtPlan &p, const uint64_t *bitmaps, const uint32_t *offsets,
+                             const uint8_t *payload, uint32_t payload_bytes, int M, int K, const uint8_t *X, int N,
+                             int32_t *Y, hipStream_t stream) {
+    if (K % 8 == 0)
+        launch_bt64_w4a4_x<false>(p, bitmaps, offsets, payload, payload_bytes, M, K, X, N, Y, stream);
+    else
+        launch_bt64_w4a4_x<true>(p, bitmaps, offsets, payload, payload_bytes, M, K, X, N, Y, stream);
 }

@@ -79,7 +79,7 @@ extern "C" int bsp_describe_selection(int dtype, int64_t M, int64_t K, int64_t N
                                       char *buf, size_t n) {
     int a = bsp_select(dtype, M, K, N, nnz);
     if (a < 0 || buf == nullptr || n == 0) return BSP_E_ARG;
-    const char *name = a == BSP_ALGO_ROWWAVE ? "rowwave" : a == BSP_ALGO_VALU ? "valu" : "mfma";
+    const char *name = a == BSP_ALGO_ROWWAVE ? "rowwave" : "mfma";
     const char *ty = dtype == BSP_INT4 ? "int4" : "fp16";
     // payload bytes the encoder writes for nnz nonzeros (all of W when unknown)
     const int64_t nz = nnz >= 0 ? nnz : M * K;
@@ -107,7 +107,7 @@ extern "C" int bsp_describe_selection(int dtype, int64_t M, int64_t K, int64_t N
                          p.lds);
         }
     }
-    if (launch[0] == 0 && a != BSP_ALGO_VALU && M > 0 && N > 0)
+    if (launch[0] == 0 && M > 0 && N > 0)
         snprintf(launch, sizeof launch, " kernel=k_rowwave_%s", dtype == BSP_INT4 ? "w4a4" : "f16");
     snprintf(buf, n, "dtype=%s M=%lld K=%lld N=%lld nnz=%lld -> %s%s", ty, (long long)M, (long long)K, (long long)N,
              (long long)nnz, name, launch);
@@ -120,18 +120,23 @@ extern "C" int spmm_bitmap_w4a4_algo(const uint64_t *bitmaps, const uint32_t *of
     Shape s;
     int rc = check_args(bitmaps, offsets, payload, payload_bytes, M, K, X, N, Y, algo, &s);
     if (rc != BSP_OK || M == 0 || N == 0) return rc;
-    if (algo == BSP_ALGO_AUTO) algo = select_algo(BSP_INT4, s, -1);
-    if (!algo_supported(algo, BSP_INT4, s)) algo = BSP_ALGO_ROWWAVE;   // layout outside a fast path's range
+    // The MFMA kernels read X in whole dwords from its start (the last one
+    // may reach up to 3 bytes past N * ceil(K/2), inside the same page only
+    // when X starts on a 4-byte boundary): an X off that boundary takes the
+    // plain kernel.
+    const bool x_aligned = ((uintptr_t)X & 3u) == 0;
+    if (algo == BSP_ALGO_AUTO) {
+        algo = select_algo(BSP_INT4, s, -1);
+        if (algo == BSP_ALGO_MFMA && !x_aligned) algo = BSP_ALGO_ROWWAVE;
+    }
+    if (!algo_supported(algo, BSP_INT4, s) || (algo == BSP_ALGO_MFMA && !x_aligned))
+        return BSP_E_UNSUPPORTED;   // a forced kernel never falls back
     switch (algo) {
         case BSP_ALGO_MFMA: {
             BtPlan plan;
-            if (bt64_plan(M, K, N, payload_bytes, &plan)) {
-                launch_bt64_w4a4(plan, bitmaps, offsets, payload, (uint32_t)payload_bytes, (int)M, (int)K, X, (int)N,
-                                 Y, stream);
-                break;
-            }
-            launch_rowwave_w4a4(bitmaps, offsets, payload, (uint32_t)payload_bytes, (int)M, (int)K, X, (int)N, Y,
-                                stream);
+            if (!bt64_plan(M, K, N, payload_bytes, &plan)) return BSP_E_UNSUPPORTED;
+            launch_bt64_w4a4(plan, bitmaps, offsets, payload, (uint32_t)payload_bytes, (int)M, (int)K, X, (int)N,
+                             Y, stream);
             break;
         }
         default:
@@ -156,7 +161,7 @@ extern "C" int spmm_bitmap_f16_algo(const uint64_t *bitmaps, const uint32_t *off
     int rc = check_args(bitmaps, offsets, payload, payload_bytes, M, K, X, N, Y, algo, &s);
     if (rc != BSP_OK || M == 0 || N == 0) return rc;
     if (algo == BSP_ALGO_AUTO) algo = select_algo(BSP_FP16, s, -1);
-    if (!algo_supported(algo, BSP_FP16, s)) algo = BSP_ALGO_ROWWAVE;
+    if (!algo_supported(algo, BSP_FP16, s)) return BSP_E_UNSUPPORTED;   // a forced kernel never falls back
     switch (algo) {
         case BSP_ALGO_MFMA: {
             Bf8Plan plan8;
@@ -166,13 +171,9 @@ extern "C" int spmm_bitmap_f16_algo(const uint64_t *bitmaps, const uint32_t *off
                 break;
             }
             BfPlan plan;
-            if (bf_plan(M, K, N, payload_bytes, &plan)) {
-                launch_bt64_f16(plan, bitmaps, offsets, payload, (uint32_t)payload_bytes, (int)M, (int)K, X, (int)N,
-                                Y, stream);
-                break;
-            }
-            launch_rowwave_f16(bitmaps, offsets, payload, (uint32_t)payload_bytes, (int)M, (int)K, X, (int)N, Y,
-                               stream);
+            if (!bf_plan(M, K, N, payload_bytes, &plan)) return BSP_E_UNSUPPORTED;
+            launch_bt64_f16(plan, bitmaps, offsets, payload, (uint32_t)payload_bytes, (int)M, (int)K, X, (int)N,
+                            Y, stream);
             break;
         }
         default:

@@ -63,18 +63,20 @@ typedef enum bsp_status {
     BSP_E_RANGE = 2,     /* an int4 weight outside [-8, 7] */
     BSP_E_CAPACITY = 3,  /* payload buffer smaller than the encoded payload */
     BSP_E_OVERFLOW = 4,  /* nnz >= 2^32, K >= 2^25 (int32 sums could overflow), or an index beyond 2^31 */
-    BSP_E_HIP = 5        /* a HIP launch error (hipGetLastError after the launch) */
+    BSP_E_HIP = 5,       /* a HIP launch error (hipGetLastError after the launch) */
+    BSP_E_UNSUPPORTED = 6 /* a kernel forced through an *_algo entry point cannot run this shape */
 } bsp_status;
 
 typedef enum bsp_dtype { BSP_INT4 = 0, BSP_FP16 = 1 } bsp_dtype;
 
 /* Kernel choice for the *_algo entry points. BSP_ALGO_AUTO applies the
- * library's shape-aware selection (by N, density, M, K). */
+ * library's shape-aware selection (by N, density, M, K). A forced choice
+ * that cannot run the shape returns BSP_E_UNSUPPORTED and launches nothing;
+ * it never falls back to another kernel. */
 typedef enum bsp_algo {
     BSP_ALGO_AUTO = 0,
-    BSP_ALGO_ROWWAVE = 1,   /* one wavefront per output row; plain per-nonzero decode */
-    BSP_ALGO_VALU = 2,      /* lane-per-tile SWAR decode + dot8 / fp32 FMA contraction */
-    BSP_ALGO_MFMA = 3       /* lane-per-tile SWAR decode + int8 / fp16 MFMA contraction */
+    BSP_ALGO_ROWWAVE = 1,   /* one wavefront per output row; plain per-nonzero decode (any shape) */
+    BSP_ALGO_MFMA = 2       /* lane-per-tile decode from LDS-staged tiles + int8 / fp16 MFMA */
 } bsp_algo;
 
 /* The device payload allocation handed to the SpMM calls is a whole number
@@ -130,7 +132,10 @@ int pack_int4_activations(const int8_t *X, int64_t N, int64_t K, int64_t ldx, ui
  *                               BSP_PAYLOAD_ALIGN, >= ceil(nnz/2), bytes past the
  *                               encoded payload zero. No byte at or past it is read.
  *   M, K                        0 <= M < 2^31, 0 <= K < 2^25, M*ceil(K/64) < 2^31.
- *   X                           DEVICE, [N][ceil(K/2)] packed int4.
+ *   X                           DEVICE, [N][ceil(K/2)] packed int4. The MFMA kernels
+ *                               need X on a 4-byte boundary (any allocation is); an X
+ *                               off it runs the plain kernel (BSP_ALGO_AUTO) or is
+ *                               refused with BSP_E_UNSUPPORTED (BSP_ALGO_MFMA).
  *   N                           0..32. N == 0 or M == 0: nothing is launched.
  *   Y                           DEVICE, [N][M] int32, fully overwritten (K == 0 gives zeros).
  *   stream                      HIP stream (NULL = null stream).

@@ -31,7 +31,7 @@ def build(force: bool = True) -> str:
     """Compile bsp_oracle.c with gcc. Returns the library path."""
     if force or not os.path.exists(_LIB):
         tmp = _LIB + f".tmp{os.getpid()}"
-        subprocess.check_call(["gcc", "-O2", "-std=c99", "-shared", "-fPIC", _SRC, "-o", tmp, "-lm"])
+        subprocess.check_call(["gcc", "-O2", "-std=c99", "-shared", "-fPIC", "-pthread", _SRC, "-o", tmp, "-lm"])
         os.replace(tmp, _LIB)
     return _LIB
 
@@ -73,6 +73,8 @@ def _configure(L):
     L.or_matmul_f64.argtypes, L.or_matmul_f64.restype = [P, I64, I64, P, I64, P], None
     L.or_spmm_w4a4.argtypes, L.or_spmm_w4a4.restype = [P, P, P, I64, I64, P, I64, P], I32
     L.or_spmm_f16.argtypes, L.or_spmm_f16.restype = [P, P, P, I64, I64, P, I64, P], I32
+    L.or_spmm_w4a4_mt.argtypes, L.or_spmm_w4a4_mt.restype = [P, P, P, I64, I64, P, I64, P, I32], I32
+    L.or_spmm_f16_mt.argtypes, L.or_spmm_f16_mt.restype = [P, P, P, I64, I64, P, I64, P, I32], I32
     L.or_spmm_w4a4_one.argtypes, L.or_spmm_w4a4_one.restype = [P, P, P, I64, P, I64, I64], I64
     L.or_spmm_f16_one.argtypes, L.or_spmm_f16_one.restype = [P, P, P, I64, P, I64, I64], ctypes.c_double
     return L
@@ -205,22 +207,30 @@ def matmul_f64(Wd: np.ndarray, Xh: np.ndarray) -> np.ndarray:
     return Y
 
 
-def spmm_w4a4(s: Stream, Xp: np.ndarray, N: int) -> np.ndarray:
-    """Y int32 [N][M] from the stream and packed int4 X ([N][ceil(K/2)] bytes)."""
+def spmm_w4a4(s: Stream, Xp: np.ndarray, N: int, threads: int = 0) -> np.ndarray:
+    """Y int32 [N][M] from the stream and packed int4 X ([N][ceil(K/2)] bytes).
+    threads > 0 splits the rows of Y over that many threads (same result)."""
     Xp = np.ascontiguousarray(Xp, dtype=np.uint8)
     Y = np.zeros((N, s.M), np.int32)
-    rc = lib().or_spmm_w4a4(_p(s.bitmaps), _p(s.offsets), _p(s.payload), s.M, s.K, _p(Xp), N, _p(Y))
+    if threads > 0:
+        rc = lib().or_spmm_w4a4_mt(_p(s.bitmaps), _p(s.offsets), _p(s.payload), s.M, s.K, _p(Xp), N, _p(Y), threads)
+    else:
+        rc = lib().or_spmm_w4a4(_p(s.bitmaps), _p(s.offsets), _p(s.payload), s.M, s.K, _p(Xp), N, _p(Y))
     if rc != OK:
         raise ValueError(f"oracle spmm_w4a4 failed: code {rc}")
     return Y
 
 
-def spmm_f16(s: Stream, Xh: np.ndarray) -> np.ndarray:
-    """fp64 reference r[N][M] for an fp16 stream and fp16 X [N][K]."""
+def spmm_f16(s: Stream, Xh: np.ndarray, threads: int = 0) -> np.ndarray:
+    """fp64 reference r[N][M] for an fp16 stream and fp16 X [N][K].
+    threads > 0 splits the rows over that many threads (same result)."""
     Xh = np.ascontiguousarray(Xh, np.float16).view(np.uint16)
     N = Xh.shape[0]
     Y = np.zeros((N, s.M), np.float64)
-    rc = lib().or_spmm_f16(_p(s.bitmaps), _p(s.offsets), _p(s.payload), s.M, s.K, _p(Xh), N, _p(Y))
+    if threads > 0:
+        rc = lib().or_spmm_f16_mt(_p(s.bitmaps), _p(s.offsets), _p(s.payload), s.M, s.K, _p(Xh), N, _p(Y), threads)
+    else:
+        rc = lib().or_spmm_f16(_p(s.bitmaps), _p(s.offsets), _p(s.payload), s.M, s.K, _p(Xh), N, _p(Y))
     if rc != OK:
         raise ValueError(f"oracle spmm_f16 failed: code {rc}")
     return Y

@@ -45,6 +45,7 @@
 #include <string.h>
 #include <stdlib.h>
 #include <math.h>
+#include <pthread.h>
 
 #define OR_OK 0
 #define OR_E_ARG 1
@@ -315,4 +316,104 @@ double or_spmm_f16_one(const uint64_t *bitmaps, const uint32_t *offsets, const u
         acc += or_f16_to_f64(w) * or_f16_to_f64(Xh[n * K + k]);
     }
     return acc;
+}
+
+/*
+ * The same whole paths with the rows of Y split into contiguous ranges, one
+ * per thread (for timing the oracle on every core of a host). Each thread
+ * runs the definitions above on its own rows only: decode of those rows of W
+ * (their tiles are a contiguous part of the stream; the stream's offsets are
+ * absolute, so no rebasing is needed), the unpacked X, the exact product.
+ * The result does not depend on the thread count.
+ */
+typedef struct {
+    int dtype;
+    const uint64_t *bitmaps;
+    const uint32_t *offsets;
+    const void *payload;
+    int64_t M, K, N, m0, m1;
+    const int8_t *Xd;        /* int4: unpacked X [N][K] */
+    const uint16_t *Xh;      /* fp16: X [N][K] */
+    int32_t *Y32;            /* int4 result [N][M] */
+    double *Yf;              /* fp16 result [N][M] */
+    int rc;
+} or_rows_job;
+
+static void *or_rows_worker(void *arg) {
+    or_rows_job *j = (or_rows_job *)arg;
+    int64_t T = or_tiles_per_row(j->K);
+    int64_t rows = j->m1 - j->m0;
+    j->rc = OR_OK;
+    if (rows <= 0) return NULL;
+    /* the job's rows as a stream of their own: same words and offsets, the
+     * payload pointer unchanged (offsets index it absolutely) */
+    const uint64_t *bm = j->bitmaps + j->m0 * T;
+    const uint32_t *off = j->offsets + j->m0 * T;
+    if (j->dtype == 0) {
+        int8_t *Wd = (int8_t *)malloc((size_t)(rows * j->K > 0 ? rows * j->K : 1));
+        int64_t *Y64 = (int64_t *)malloc((size_t)(rows * j->N > 0 ? rows * j->N : 1) * sizeof(int64_t));
+        if (!Wd || !Y64) { free(Wd); free(Y64); j->rc = OR_E_ARG; return NULL; }
+        or_decode(0, bm, off, j->payload, rows, j->K, Wd);
+        or_matmul_i64(Wd, rows, j->K, j->Xd, j->N, Y64);    /* Y64[n][r] for the job's rows */
+        for (int64_t n = 0; n < j->N; ++n)
+            for (int64_t r = 0; r < rows; ++r) {
+                int64_t v = Y64[n * rows + r];
+                if (v > INT32_MAX || v < INT32_MIN) j->rc = OR_E_OVERFLOW;
+                j->Y32[n * j->M + j->m0 + r] = (int32_t)v;
+            }
+        free(Wd); free(Y64);
+    } else {
+        uint16_t *Wd = (uint16_t *)malloc((size_t)(rows * j->K > 0 ? rows * j->K : 1) * sizeof(uint16_t));
+        double *Yr = (double *)malloc((size_t)(rows * j->N > 0 ? rows * j->N : 1) * sizeof(double));
+        if (!Wd || !Yr) { free(Wd); free(Yr); j->rc = OR_E_ARG; return NULL; }
+        or_decode(1, bm, off, j->payload, rows, j->K, Wd);
+        or_matmul_f64(Wd, rows, j->K, j->Xh, j->N, Yr);
+        for (int64_t n = 0; n < j->N; ++n)
+            for (int64_t r = 0; r < rows; ++r) j->Yf[n * j->M + j->m0 + r] = Yr[n * rows + r];
+        free(Wd); free(Yr);
+    }
+    return NULL;
+}
+
+static int or_spmm_threads(int dtype, const uint64_t *bitmaps, const uint32_t *offsets, const void *payload,
+                           int64_t M, int64_t K, const void *X, int64_t N, void *Y, int nthreads) {
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 1024) nthreads = 1024;
+    int8_t *Xd = NULL;
+    if (dtype == 0) {
+        Xd = (int8_t *)malloc((size_t)(N * K > 0 ? N * K : 1));
+        if (!Xd) return OR_E_ARG;
+        or_unpack_x4((const uint8_t *)X, N, K, Xd);
+    }
+    or_rows_job *jobs = (or_rows_job *)calloc((size_t)nthreads, sizeof(or_rows_job));
+    pthread_t *th = (pthread_t *)calloc((size_t)nthreads, sizeof(pthread_t));
+    int *started = (int *)calloc((size_t)nthreads, sizeof(int));
+    if (!jobs || !th || !started) { free(Xd); free(jobs); free(th); free(started); return OR_E_ARG; }
+    for (int i = 0; i < nthreads; ++i) {
+        or_rows_job *j = &jobs[i];
+        j->dtype = dtype; j->bitmaps = bitmaps; j->offsets = offsets; j->payload = payload;
+        j->M = M; j->K = K; j->N = N;
+        j->m0 = M * i / nthreads; j->m1 = M * (i + 1) / nthreads;
+        j->Xd = Xd; j->Xh = (const uint16_t *)X;
+        j->Y32 = (int32_t *)Y; j->Yf = (double *)Y;
+        started[i] = pthread_create(&th[i], NULL, or_rows_worker, j) == 0;
+        if (!started[i]) or_rows_worker(j);
+    }
+    int rc = OR_OK;
+    for (int i = 0; i < nthreads; ++i) {
+        if (started[i]) pthread_join(th[i], NULL);
+        if (jobs[i].rc != OR_OK) rc = jobs[i].rc;
+    }
+    free(Xd); free(jobs); free(th); free(started);
+    return rc;
+}
+
+int or_spmm_w4a4_mt(const uint64_t *bitmaps, const uint32_t *offsets, const uint8_t *payload,
+                    int64_t M, int64_t K, const uint8_t *Xp, int64_t N, int32_t *Y, int nthreads) {
+    return or_spmm_threads(0, bitmaps, offsets, payload, M, K, Xp, N, Y, nthreads);
+}
+
+int or_spmm_f16_mt(const uint64_t *bitmaps, const uint32_t *offsets, const uint16_t *payload,
+                   int64_t M, int64_t K, const uint16_t *Xh, int64_t N, double *Y, int nthreads) {
+    return or_spmm_threads(1, bitmaps, offsets, payload, M, K, Xh, N, Y, nthreads);
 }

@@ -272,4 +272,37 @@ def pin_f16_matmul_numpy():
             assert abs(oracle.spmm_f16_one(s, p.X, m, n) - ref[n, m]) <= 1e-12 * (abs(ref[n, m]) + 1e-3)
 
 
+
+def pin_fp16_error():
+    """The fp16 pass/fail metric (floored elementwise relative error, its
+    unfloored maximum, the normwise error and the non-finite count) on vectors
+    whose values are worked out by hand here."""
+    import math
+    fn = oracle.fp16_error
+    # the floor decides: rms(r) = sqrt(84 / 4) = sqrt(21), floor = 0.01 sqrt(21);
+    # the zero reference with |y - r| = 0.01 gives 0.01 / (0.01 sqrt(21)) = 1 / sqrt(21)
+    e = fn(np.array([2.02, -4.0, 0.01, 7.9]), np.array([2.0, -4.0, 0.0, 8.0]))
+    assert math.isclose(e["max_rel_floored"], 1.0 / math.sqrt(21.0), rel_tol=1e-12), e
+    assert e["max_rel_unfloored"] == math.inf, e           # a zero reference with a nonzero error
+    assert math.isclose(e["normwise"], 0.1 / 8.0, rel_tol=1e-9), e
+    assert e["nonfinite"] == 0, e
+    # signs: the largest error is y below a negative r (|-2.5 - (-2)| / |-2| = 0.25);
+    # rms(r) = sqrt(7) puts the floor (0.026) below every |r|, so floored = unfloored
+    e = fn(np.array([0.9, -2.5, 4.0]), np.array([1.0, -2.0, 4.0]))
+    assert math.isclose(e["max_rel_floored"], 0.25, rel_tol=1e-12), e
+    assert math.isclose(e["max_rel_unfloored"], 0.25, rel_tol=1e-12), e
+    assert math.isclose(e["normwise"], 0.5 / 4.0, rel_tol=1e-12), e
+    # non-finite outputs are counted (and never pass as small errors)
+    e = fn(np.array([np.inf, np.nan, 1.0]), np.array([1.0, 1.0, 1.0]))
+    assert e["nonfinite"] == 2, e
+    # exact results, and the empty case
+    e = fn(np.array([0.0, 0.0]), np.array([0.0, 0.0]))
+    assert e == dict(max_rel_floored=0.0, max_rel_unfloored=0.0, normwise=0.0, nonfinite=0), e
+    e = fn(np.zeros(0), np.zeros(0))
+    assert e == dict(max_rel_floored=0.0, max_rel_unfloored=0.0, normwise=0.0, nonfinite=0), e
+    # a 2-D result is judged over all its elements
+    e = fn(np.array([[1.0, 2.0], [3.0, 4.4]]), np.array([[1.0, 2.0], [3.0, 4.0]]))
+    assert math.isclose(e["max_rel_floored"], 0.1, rel_tol=1e-12), e
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

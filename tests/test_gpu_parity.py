@@ -4,8 +4,12 @@ int4 results must match bit for bit; fp16 results must meet the documented
 tolerance (max floored relative error <= 1e-2 against the fp64 reference).
 Inputs are the seeded workloads; expected values come only from ``oracle``.
 Every call goes through the C ABI (``libbitmap_spmm.so``) via the binding.
+A call that forces the MFMA kernels first checks, from the library's own
+launch plan, which kernel runs; a shape outside them must be refused with
+BSP_E_UNSUPPORTED (a forced kernel never falls back to another one).
 """
 import functools
+import re
 
 import numpy as np
 import pytest
@@ -19,15 +23,28 @@ pytestmark = pytest.mark.gpu
 
 INT4_ALGOS = [bsp.ALGO_AUTO, bsp.ALGO_ROWWAVE, bsp.ALGO_MFMA]
 F16_ALGOS = [bsp.ALGO_AUTO, bsp.ALGO_ROWWAVE, bsp.ALGO_MFMA]
-_NAMES = {bsp.ALGO_AUTO: "auto", bsp.ALGO_ROWWAVE: "rowwave", bsp.ALGO_VALU: "valu", bsp.ALGO_MFMA: "mfma"}
+_NAMES = {bsp.ALGO_AUTO: "auto", bsp.ALGO_ROWWAVE: "rowwave", bsp.ALGO_MFMA: "mfma"}
 SENTINEL = -0x21524111   # 0xDEADBEEF as int32
 F16_TOL = 1e-2
+MFMA_KERNELS = {bsp.INT4: ("k_bt64s_w4a4", "k_bt64_w4a4"), bsp.FP16: ("k_bt8_f16", "k_bt64_f16")}
 
 
 @pytest.fixture(scope="module")
 def dev():
     assert torch.cuda.is_available(), "GPU tests need a HIP device"
     return torch.device("cuda:0")
+
+
+def mfma_kernel(dtype, M, K, N, nnz):
+    """The MFMA kernel a forced-MFMA call launches, from the library's plan
+    (the automatic choice is the MFMA path for every shape inside it), or
+    None for a shape outside the MFMA path."""
+    d = bsp.describe(dtype, M, K, N, nnz)
+    if "-> mfma" not in d:
+        return None
+    k = re.search(r"kernel=(\w+)", d).group(1)
+    assert k in MFMA_KERNELS[dtype], d
+    return k
 
 
 def _y_with_canary(N, M, dtype, dev):
@@ -45,28 +62,60 @@ def _canary_ok(big, N, M, dtype):
     return bool((big[N * M:] == -1).all().item())
 
 
-def run_w4a4(W_int8, X_int8, algo, dev, enc=None):
+def run_w4a4(W_int8, X_int8, algo, dev, enc=None, expect_kernel=None):
+    """Y from the library, or None when a forced MFMA call is refused as
+    unsupported (which is then asserted). expect_kernel: the MFMA kernel the
+    caller intends to exercise (asserted when forcing MFMA)."""
     enc = enc or bsp.encode(W_int8)
-    dm = enc.to_device(dev)
     N = X_int8.shape[0]
+    k = None
+    if algo == bsp.ALGO_MFMA and N > 0 and enc.M > 0:
+        k = mfma_kernel(bsp.INT4, enc.M, enc.K, N, enc.nnz)
+        if expect_kernel is not None:
+            assert k == expect_kernel, (k, expect_kernel)
+    dm = enc.to_device(dev)
     Xd = torch.from_numpy(bsp.pack_int4(X_int8)).to(dev)
     big, Y = _y_with_canary(N, enc.M, torch.int32, dev)
+    if algo == bsp.ALGO_MFMA and N > 0 and enc.M > 0 and k is None:
+        with pytest.raises(bsp.BspError) as ei:
+            bsp.spmm_w4a4(dm, Xd, N, Y=Y, algo=algo)
+        assert ei.value.status == bsp.E_UNSUPPORTED
+        torch.cuda.synchronize()
+        assert bool((big == SENTINEL).all()), "a refused call wrote Y"
+        return None
     bsp.spmm_w4a4(dm, Xd, N, Y=Y, algo=algo)
     torch.cuda.synchronize()
     assert _canary_ok(big, N, enc.M, torch.int32), "write past the end of Y"
     return Y.cpu().numpy()
 
 
-def run_f16(W_f16, X_f16, algo, dev, enc=None):
+def run_f16(W_f16, X_f16, algo, dev, enc=None, expect_kernel=None):
     enc = enc or bsp.encode(W_f16)
-    dm = enc.to_device(dev)
     N = X_f16.shape[0]
+    k = None
+    if algo == bsp.ALGO_MFMA:
+        k = mfma_kernel(bsp.FP16, enc.M, enc.K, N, enc.nnz)
+        if expect_kernel is not None:
+            assert k == expect_kernel, (k, expect_kernel)
+    dm = enc.to_device(dev)
     Xd = torch.from_numpy(np.ascontiguousarray(X_f16)).to(dev)
     big, Y = _y_with_canary(N, enc.M, torch.float16, dev)
+    if algo == bsp.ALGO_MFMA and k is None:
+        with pytest.raises(bsp.BspError) as ei:
+            bsp.spmm_f16(dm, Xd, Y=Y, algo=algo)
+        assert ei.value.status == bsp.E_UNSUPPORTED
+        return None
     bsp.spmm_f16(dm, Xd, Y=Y, algo=algo)
     torch.cuda.synchronize()
     assert _canary_ok(big.view(torch.int16), N, enc.M, torch.float16), "write past the end of Y"
     return Y.cpu().numpy()
+
+
+def assert_w4a4(Y, W, X, ref=None):
+    """Bit-exact against the oracle (nothing to compare for a refused call)."""
+    if Y is None:
+        return
+    assert np.array_equal(Y, oracle_w4a4(W, X) if ref is None else ref)
 
 
 def oracle_w4a4(W, X):
@@ -86,8 +135,9 @@ SMALL_INT4 = [  # (M, K, N, keep)
     (65, 130, 3, 0.5), (17, 127, 31, 0.5), (257, 1000, 16, 0.3), (129, 64 * 67 + 17, 32, 0.7),
     (300, 64 * 40, 5, 0.5), (97, 4096, 8, 0.5), (1024, 512, 4, 0.5), (33, 777, 7, 1.0),
     (48, 64 * 67 + 24, 20, 0.5), (31, 64 * 33 + 8, 16, 1.0), (16, 64 * 65, 32, 0.5), (250, 64 * 5 + 56, 13, 0.6),
-    (40, 64 * 320, 5, 0.5), (17, 64 * 330 + 32, 24, 0.9),   # K beyond one block's LDS: per-chunk staging
+    (40, 64 * 320, 5, 0.5), (17, 64 * 330 + 32, 24, 0.9),   # K beyond the MFMA kernels' 16384: refused there
     (40, 333, 9, 0.0), (2, 2048, 32, 0.05), (512, 64 * 172, 16, 0.3),
+    (70, 64 * 256, 8, 0.5), (33, 64 * 255 + 7, 17, 0.5),   # the largest K of the MFMA kernels, and an odd one
 ]
 
 
@@ -95,19 +145,22 @@ SMALL_INT4 = [  # (M, K, N, keep)
 @pytest.mark.parametrize("M,K,N,keep", SMALL_INT4)
 def test_w4a4_small(dev, algo, M, K, N, keep):
     p = workloads.random_int4_problem(M * 7 + K * 3 + N, M, K, N, keep=keep)
-    Y = run_w4a4(p.W, p.X, algo, dev)
-    assert np.array_equal(Y, oracle_w4a4(p.W, p.X))
+    assert_w4a4(run_w4a4(p.W, p.X, algo, dev), p.W, p.X)
 
 
+# every weight and activation at -8 or +7: the largest-magnitude products,
+# through the x16 int8 form and the >> 8 of the MFMA kernels (K = 64 * 33:
+# rows on a 4-byte boundary; K = 2117: odd K, rows off any boundary)
 @pytest.mark.parametrize("algo", INT4_ALGOS, ids=lambda a: _NAMES[a])
-def test_w4a4_extremes(dev, algo):
-    # every weight and activation at -8: the largest magnitude products
-    M, K, N = 70, 64 * 33 + 5, 32
+@pytest.mark.parametrize("K", [64 * 33, 2117, 64 * 256])
+def test_w4a4_extremes(dev, algo, K):
+    M, N = 70, 32
     W = np.full((M, K), -8, np.int8)
     W[::3, ::5] = 7
     X = np.full((N, K), -8, np.int8)
     X[1::2] = 7
-    assert np.array_equal(run_w4a4(W, X, algo, dev), oracle_w4a4(W, X))
+    kern = "k_bt64s_w4a4" if K <= 4096 else "k_bt64_w4a4"
+    assert_w4a4(run_w4a4(W, X, algo, dev, expect_kernel=kern if algo == bsp.ALGO_MFMA else None), W, X)
 
 
 @pytest.mark.parametrize("algo", INT4_ALGOS, ids=lambda a: _NAMES[a])
@@ -122,7 +175,7 @@ def test_w4a4_uneven_block_density(dev, algo, dense_block):
     keep[16 * dense_block:16 * dense_block + 16] = 1.0
     W = workloads._int4_weights(rng, M, K, keep)
     X = workloads.int4_activations(rng, (N, K))
-    assert np.array_equal(run_w4a4(W, X, algo, dev), oracle_w4a4(W, X))
+    assert_w4a4(run_w4a4(W, X, algo, dev), W, X)
 
 
 @pytest.mark.parametrize("algo", INT4_ALGOS, ids=lambda a: _NAMES[a])
@@ -134,6 +187,8 @@ def test_w4a4_many_blocks_ragged_y(dev, algo, M, K, N, y_shift):
     # boundary: the 16-byte stores of Y must fall back to single stores
     p = workloads.random_int4_problem(M + K + N, M, K, N, keep=0.5)
     enc = bsp.encode(p.W)
+    if algo == bsp.ALGO_MFMA:
+        assert mfma_kernel(bsp.INT4, M, K, N, enc.nnz) is not None
     dm = enc.to_device(dev)
     Xd = torch.from_numpy(bsp.pack_int4(p.X)).to(dev)
     big = torch.full((N * M + 8 + y_shift,), SENTINEL, dtype=torch.int32, device=dev)
@@ -145,15 +200,15 @@ def test_w4a4_many_blocks_ragged_y(dev, algo, M, K, N, y_shift):
 
 
 @pytest.mark.parametrize("M,K,N", [(1000, 64 * 100 + 32, 17), (2050, 8192, 32), (300, 11008, 20), (70, 8256, 24),
-                                   (200, 16384, 32), (333, 64 * 70 + 32, 3)])
+                                   (200, 16384, 32), (333, 64 * 70 + 32, 3), (301, 64 * 90 + 13, 20),
+                                   (77, 64 * 150 + 40, 7)])
 def test_w4a4_ring_x_runs(dev, M, K, N):
     # the ring kernel loads X in 64-byte runs of 16 rows and hands each lane
     # its slices by a transpose across lane groups; K % 64 == 32 leaves the
-    # last tile half in X, and rows n >= N read zeros
+    # last tile half in X, K % 8 != 0 puts X rows off a 4-byte boundary
+    # (funnel-shifted loads), and rows n >= N read zeros
     p = workloads.random_int4_problem(M + K + N, M, K, N, keep=0.4)
-    assert "kernel=k_bt64_w4a4 " in bsp.describe(bsp.INT4, M, K, N, int(np.count_nonzero(p.W)))
-    Y = run_w4a4(p.W, p.X, bsp.ALGO_MFMA, dev)
-    assert np.array_equal(Y, oracle_w4a4(p.W, p.X))
+    assert_w4a4(run_w4a4(p.W, p.X, bsp.ALGO_MFMA, dev, expect_kernel="k_bt64_w4a4"), p.W, p.X)
 
 
 @pytest.mark.parametrize("algo", INT4_ALGOS, ids=lambda a: _NAMES[a])
@@ -174,23 +229,41 @@ def test_w4a4_staggered_staging(dev, algo, M, K, N, dense_block):
     enc = bsp.encode(W)
     if algo == bsp.ALGO_MFMA:
         assert "stagger=1" in bsp.describe(bsp.INT4, M, K, N, enc.nnz)
-    assert np.array_equal(run_w4a4(W, X, algo, dev, enc=enc), oracle_w4a4(W, X))
+    assert_w4a4(run_w4a4(W, X, algo, dev, enc=enc, expect_kernel="k_bt64s_w4a4" if algo == bsp.ALGO_MFMA else None),
+                W, X)
 
 
 @pytest.mark.parametrize("algo", INT4_ALGOS, ids=lambda a: _NAMES[a])
 def test_w4a4_k_zero(dev, algo):
     W = np.zeros((9, 0), np.int8)
     X = np.zeros((3, 0), np.int8)
-    Y = run_w4a4(W, X, algo, dev)
-    assert Y.shape == (3, 9) and not Y.any()
+    enc = bsp.encode(W)
+    dm = enc.to_device(dev)
+    Xd = torch.zeros(0, dtype=torch.uint8, device=dev)
+    Y = torch.full((3, 9), SENTINEL, dtype=torch.int32, device=dev)
+    if algo == bsp.ALGO_MFMA:
+        # K = 0 has no tile to decode: only the plain kernel writes its zeros
+        with pytest.raises(bsp.BspError) as ei:
+            bsp.spmm_w4a4(dm, Xd, 3, Y=Y, algo=algo)
+        assert ei.value.status == bsp.E_UNSUPPORTED
+        return
+    bsp.spmm_w4a4(dm, Xd, 3, Y=Y, algo=algo)
+    torch.cuda.synchronize()
+    assert not Y.cpu().numpy().any()
 
 
+# every N in 1..32 through the MFMA kernels: the streaming kernel (K = 608,
+# rows on a 4-byte boundary; K = 609, odd) and the ring kernel (K = 6432)
 @pytest.mark.parametrize("algo", INT4_ALGOS, ids=lambda a: _NAMES[a])
+@pytest.mark.parametrize("K", [64 * 9 + 32, 64 * 9 + 33, 64 * 100 + 32])
 @pytest.mark.parametrize("N", list(range(1, 33)))
-def test_w4a4_every_n(dev, algo, N):
-    p = workloads.random_int4_problem(77, 200, 64 * 9 + 33, 32, keep=0.5)
-    Y = run_w4a4(p.W, p.X[:N], algo, dev)
-    assert np.array_equal(Y, oracle_w4a4(p.W, p.X[:N]))
+def test_w4a4_every_n(dev, algo, K, N):
+    if K > 4096 and algo != bsp.ALGO_MFMA:
+        pytest.skip("the ring-kernel shape is checked through the forced MFMA path only")
+    p = workloads.random_int4_problem(77 + K, 200, K, 32, keep=0.5)
+    kern = ("k_bt64s_w4a4" if K <= 4096 else "k_bt64_w4a4") if algo == bsp.ALGO_MFMA else None
+    Y = run_w4a4(p.W, p.X[:N], algo, dev, expect_kernel=kern)
+    assert_w4a4(Y, p.W, p.X[:N])
 
 
 SMALL_F16 = [(1, 1, 1), (3, 63, 2), (65, 130, 32), (257, 1000, 1), (129, 64 * 67 + 17, 17), (64, 4096, 8),
@@ -200,7 +273,9 @@ SMALL_F16 = [(1, 1, 1), (3, 63, 2), (65, 130, 32), (257, 1000, 1), (129, 64 * 67
 
 
 def _assert_f16(y, r):
-    e = oracle.fp16_error(y, r)
+    if y is None:
+        return
+    e = oracle.fp16_error(y.astype(np.float64), r)
     assert e["nonfinite"] == 0, e
     assert e["max_rel_floored"] <= F16_TOL, e
 
@@ -209,8 +284,7 @@ def _assert_f16(y, r):
 @pytest.mark.parametrize("M,K,N", SMALL_F16)
 def test_f16_small(dev, algo, M, K, N):
     p = workloads.random_fp16_problem(M + K + N, M, K, N)
-    y = run_f16(p.W, p.X, algo, dev).astype(np.float64)
-    _assert_f16(y, oracle.spmm_f16(oracle.encode(p.W), p.X))
+    _assert_f16(run_f16(p.W, p.X, algo, dev), oracle.spmm_f16(oracle.encode(p.W), p.X))
 
 
 @pytest.mark.parametrize("algo", F16_ALGOS, ids=lambda a: _NAMES[a])
@@ -225,8 +299,7 @@ def test_f16_uneven_block_density(dev, algo, dense_block):
     keep[16 * dense_block: 16 * dense_block + 16] = True
     W = np.where(keep, W, np.float16(0))
     X = rng.normal(0, 1, size=(N, K)).astype(np.float16)
-    y = run_f16(W, X, algo, dev).astype(np.float64)
-    _assert_f16(y, oracle.spmm_f16(oracle.encode(W), X))
+    _assert_f16(run_f16(W, X, algo, dev), oracle.spmm_f16(oracle.encode(W), X))
 
 
 @pytest.mark.parametrize("algo", F16_ALGOS, ids=lambda a: _NAMES[a])
@@ -246,9 +319,7 @@ def test_f16_eight_row_steps(dev, algo, M, K, N, dense_rows):
     W = np.where(keep, W, np.float16(0))
     X = rng.normal(0, 1, size=(N, K)).astype(np.float16)
     enc = bsp.encode(W)
-    if algo == bsp.ALGO_MFMA:
-        assert "kernel=k_bt8_f16" in bsp.describe(bsp.FP16, M, K, N, enc.nnz)
-    y = run_f16(W, X, algo, dev, enc=enc).astype(np.float64)
+    y = run_f16(W, X, algo, dev, enc=enc, expect_kernel="k_bt8_f16" if algo == bsp.ALGO_MFMA else None)
     _assert_f16(y, oracle.spmm_f16(oracle.encode(W), X))
 
 
@@ -256,9 +327,10 @@ def test_f16_eight_row_steps(dev, algo, M, K, N, dense_rows):
 def test_f16_zero_and_dense(dev, algo):
     W = np.zeros((33, 100), np.float16)
     X = np.ones((2, 100), np.float16)
-    assert not run_f16(W, X, algo, dev).any()
+    y = run_f16(W, X, algo, dev)
+    assert y is None or not y.any()
     p = workloads.random_fp16_problem(3, 40, 256, 4, sparsity=0.0)
-    _assert_f16(run_f16(p.W, p.X, algo, dev).astype(np.float64), oracle.spmm_f16(oracle.encode(p.W), p.X))
+    _assert_f16(run_f16(p.W, p.X, algo, dev), oracle.spmm_f16(oracle.encode(p.W), p.X))
 
 
 # --- the named workloads at their full sizes -------------------------------------------------
@@ -284,21 +356,48 @@ FULL_INT4 = [("tiny", 0), ("qkv", 0), ("ffn", 0), ("ffn", 1), ("lowsparse", 0)]
 @pytest.mark.parametrize("config,idx", FULL_INT4)
 def test_w4a4_full_workload(dev, algo, config, idx):
     p, X, ref = _full_int4(config, idx, 0)
-    Y = run_w4a4(p.W, X, algo, dev)
-    assert np.array_equal(Y, ref)
+    assert_w4a4(run_w4a4(p.W, X, algo, dev), p.W, X, ref=ref)
 
 
 @pytest.mark.parametrize("algo", INT4_ALGOS, ids=lambda a: _NAMES[a])
 @pytest.mark.parametrize("N", [1, 2, 4, 8, 16, 32])
 def test_w4a4_qkv_n_sweep(dev, algo, N):
     p, X, ref = _full_int4("qkv", 0, 32)
-    Y = run_w4a4(p.W, X[:N], algo, dev)
-    assert np.array_equal(Y, ref[:N])
+    assert_w4a4(run_w4a4(p.W, X[:N], algo, dev), p.W, X[:N], ref=ref[:N])
+
+
+@pytest.mark.parametrize("algo", INT4_ALGOS, ids=lambda a: _NAMES[a])
+def test_w4a4_lowsparse_n16(dev, algo):
+    # the 70 %-dense 8192 x 8192 workload at N = 16 (the N sweep's other point)
+    p, X, ref = _full_int4("lowsparse", 0, 32)
+    assert_w4a4(run_w4a4(p.W, X[:16], algo, dev), p.W, X[:16], ref=ref[:16])
 
 
 @pytest.mark.parametrize("algo", F16_ALGOS, ids=lambda a: _NAMES[a])
 @pytest.mark.parametrize("idx", [0, 1])
 def test_f16_full_workload(dev, algo, idx):
     p, r = _full_f16(idx)
-    y = run_f16(p.W, p.X, algo, dev).astype(np.float64)
-    _assert_f16(y, r)
+    _assert_f16(run_f16(p.W, p.X, algo, dev), r)
+
+
+@pytest.mark.parametrize("algo", INT4_ALGOS, ids=lambda a: _NAMES[a])
+def test_w4a4_x_off_a_dword_boundary(dev, algo):
+    # X one byte into an allocation: the MFMA kernels read X in whole dwords
+    # from its start, so such an X runs the plain kernel (automatic choice) or
+    # is refused (forced MFMA)
+    p = workloads.random_int4_problem(4242, 300, 777, 5, keep=0.5)
+    enc = bsp.encode(p.W)
+    dm = enc.to_device(dev)
+    Xp = bsp.pack_int4(p.X).reshape(-1)
+    raw = torch.zeros(Xp.size + 1, dtype=torch.uint8, device=dev)
+    raw[1:] = torch.from_numpy(Xp).to(dev)
+    Xd = raw[1:]
+    Y = torch.full((5, 300), SENTINEL, dtype=torch.int32, device=dev)
+    if algo == bsp.ALGO_MFMA:
+        with pytest.raises(bsp.BspError) as ei:
+            bsp.spmm_w4a4(dm, Xd, 5, Y=Y, algo=algo)
+        assert ei.value.status == bsp.E_UNSUPPORTED
+        return
+    bsp.spmm_w4a4(dm, Xd, 5, Y=Y, algo=algo)
+    torch.cuda.synchronize()
+    assert np.array_equal(Y.cpu().numpy(), oracle_w4a4(p.W, p.X))

@@ -17,10 +17,11 @@ import workloads
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def _declared_functions():
-    src = open(os.path.join(ROOT, "include", "bitmap_spmm.h")).read()
+def _declared_functions(header="bitmap_spmm.h"):
+    src = open(os.path.join(ROOT, "include", header)).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?(?:int|char\s*\*|const char\s*\*)\s*\*?\s*(\w+)\s*\(", src, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?(?:int|int64_t|char\s*\*|const char\s*\*)\s*\*?\s*(\w+)\s*\(",
+                                src, re.M)))
 
 
 def test_library_exports_every_declared_symbol():
@@ -31,6 +32,24 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(L, n), f"{n} declared in include/bitmap_spmm.h but not exported"
     assert sorted(bsp.EXPORTS) == names
     assert bsp.load_library().bsp_version().decode().count(".") == 2
+
+
+def test_probe_library_exports_every_declared_symbol():
+    # the streaming-read probe the benchmark loads (include/bsp_probe.h)
+    L = ctypes.CDLL(os.path.join(ROOT, "bit_unstructured_sparse_amd", "libbsp_probe.so"))
+    names = _declared_functions("bsp_probe.h")
+    assert names == ["bsp_probe_read", "bsp_probe_sink_words"]
+    for n in names:
+        assert hasattr(L, n)
+    L.bsp_probe_sink_words.restype = ctypes.c_int64
+    assert L.bsp_probe_sink_words(256, 512) == 2048
+    # invalid arguments are refused before any launch
+    L.bsp_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                 ctypes.c_int, ctypes.c_void_p]
+    assert L.bsp_probe_read(None, 1024, FAKE, 0, 256, 512, None) == 1
+    assert L.bsp_probe_read(FAKE, 1000, FAKE, 0, 256, 512, None) == 1     # not a multiple of 16
+    assert L.bsp_probe_read(FAKE, 1024, FAKE, 3, 256, 512, None) == 1     # unknown mode
+    assert L.bsp_probe_read(FAKE, 1024, FAKE, 0, 256, 100, None) == 1     # block not a multiple of 64
 
 
 def _same(e, s):
@@ -134,6 +153,11 @@ def test_spmm_argument_errors_on_host(fn):
     assert call(pl=None) == bsp.E_ARG
     assert call(algo=99) == bsp.E_ARG
     assert call(algo=-1) == bsp.E_ARG
+    assert call(algo=3) == bsp.E_ARG                           # no third kernel family
+    # a forced kernel that cannot run the shape is an error, never a silent
+    # fallback to another kernel (the shape is far past the fast path's K range)
+    assert call(algo=bsp.ALGO_MFMA, K=1 << 20, pb=1 << 20) == bsp.E_UNSUPPORTED
+    assert bsp.status_string(bsp.E_UNSUPPORTED) == "the forced kernel cannot run this shape"
     # empty problems succeed without launching anything
     assert call(M=0) == bsp.OK
     assert call(N=0) == bsp.OK
@@ -145,7 +169,7 @@ def test_selection_is_defined_for_every_shape():
         for N in range(1, 33):
             for (M, K) in [(512, 512), (12288, 4096), (11008, 4096), (4096, 11008), (8192, 8192), (1, 1), (7, 0)]:
                 a = bsp.select(dt, M, K, N)
-                assert a in (bsp.ALGO_ROWWAVE, bsp.ALGO_VALU, bsp.ALGO_MFMA)
+                assert a in (bsp.ALGO_ROWWAVE, bsp.ALGO_MFMA)
                 assert bsp.describe(dt, M, K, N).startswith("dtype=")
     assert bsp.select(bsp.INT4, 1, 1, 33) == -1
     assert bsp.select(5, 1, 1, 1) == -1
@@ -163,7 +187,9 @@ def test_description_names_the_launched_kernel():
     assert "-> mfma kernel=k_bt8_f16 " in d and "step_slots=4" in d
     d = bsp.describe(bsp.FP16, 4096, 4096, 32, 4096 * 4096 * 4 // 10)
     assert "-> mfma kernel=k_bt64_f16 " in d and "block=1024" in d
-    # K not a multiple of 32: outside the fast path
-    assert bsp.describe(bsp.INT4, 64, 100, 4).endswith("-> rowwave kernel=k_rowwave_w4a4")
+    # any K up to 16384 takes the MFMA kernels (odd K too); beyond, the plain kernel
+    assert "-> mfma kernel=k_bt64s_w4a4 " in bsp.describe(bsp.INT4, 64, 100, 4)
+    assert "-> mfma kernel=k_bt64_w4a4 " in bsp.describe(bsp.INT4, 64, 64 * 255 + 7, 4)
+    assert bsp.describe(bsp.INT4, 64, 16385, 4).endswith("-> rowwave kernel=k_rowwave_w4a4")
     # nothing to launch
     assert "kernel=" not in bsp.describe(bsp.INT4, 0, 4096, 8)

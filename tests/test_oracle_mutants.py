@@ -67,3 +67,35 @@ def test_pins_catch_mutant(name, edits, tmp_path):
         oracle.swap_library(None)
         oracle._lib = prev
     assert caught, f"no pin catches mutant {name}"
+
+
+# Planted mistakes in the fp16 tolerance metric (a Python function of the
+# oracle): each must make at least one pin fail.
+F16_METRIC_MUTANTS = [
+    ("rms_of_y", "np.mean(r * r)", "np.mean(y * y)"),
+    ("floor_on_numerator", "floored = d / np.maximum(np.abs(r), floor)",
+     "floored = np.maximum(d, floor) / np.maximum(np.abs(r), floor)"),
+    ("abs_dropped_from_difference", "d = np.abs(y - r)", "d = (y - r)"),
+    ("abs_dropped_from_reference", "floored = d / np.maximum(np.abs(r), floor)",
+     "floored = d / np.maximum(r, floor)"),
+    ("floor_factor", "0.01 * rms", "0.1 * rms"),
+    ("normwise_over_y", "rn = float(np.max(np.abs(r)))", "rn = float(np.max(np.abs(y)))"),
+    ("nonfinite_not_counted", "np.count_nonzero(~np.isfinite(y))", "np.count_nonzero(np.isnan(y))"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", F16_METRIC_MUTANTS, ids=[m[0] for m in F16_METRIC_MUTANTS])
+def test_pins_catch_fp16_metric_mutant(name, old, new):
+    import inspect
+    import textwrap
+    src = textwrap.dedent(inspect.getsource(oracle.fp16_error))
+    assert old in src, f"mutation anchor not found: {old!r}"
+    ns = dict(oracle.__dict__)
+    exec(compile(src.replace(old, new), "<mutant>", "exec"), ns)
+    real = oracle.fp16_error
+    oracle.fp16_error = ns["fp16_error"]
+    try:
+        with pytest.raises(AssertionError):
+            pins.pin_fp16_error()
+    finally:
+        oracle.fp16_error = real

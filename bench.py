@@ -71,19 +71,19 @@ WRITE_COUNTERS = ["TCC_EA0_WRREQ_sum", "TCC_EA0_WRREQ_64B_sum", "TCC_EA0_WRREQ_W
 METRIC = "achieved HBM GB/s (frac of peak) + dense-equiv TOPS, bitmap SpMM at N=1..32"
 
 SWEEP = [("qkv", 0, n) for n in (1, 2, 4, 8, 16, 32)] + [("lowsparse", 0, 16), ("lowsparse", 0, 32)]
-KERNEL_SYMBOL = {"rowwave": "k_rowwave", "mfma": "k_bt64"}
+KERNEL_SYMBOL = {"rowwave": "k_rowwave", "mfma": "k_bt64", "splitk": "k_bsk"}
 
 
 def algo_name(bsp, a):
-    return {bsp.ALGO_ROWWAVE: "rowwave", bsp.ALGO_MFMA: "mfma"}[a]
+    return {bsp.ALGO_AUTO: "auto", bsp.ALGO_ROWWAVE: "rowwave", bsp.ALGO_MFMA: "mfma", bsp.ALGO_SPLITK: "splitk"}[a]
 
 
-def kernel_symbol(bsp, chosen, dt, M, K, N, nnz):
+def kernel_symbol(bsp, chosen, dt, M, K, N, nnz, workspace=False):
     """Name of the kernel a launch runs: the library's own description of its
     plan when the automatic choice is the one timed, else the algorithm's
     kernel family."""
-    if chosen == bsp.select(dt, M, K, N, nnz):
-        m = re.search(r"kernel=(\S+)", bsp.describe(dt, M, K, N, nnz))
+    if chosen == bsp.ALGO_AUTO:
+        m = re.search(r"kernel=(\S+)", bsp.describe(dt, M, K, N, nnz, workspace=workspace))
         if m:
             return m.group(1)
     return KERNEL_SYMBOL[algo_name(bsp, chosen)]
@@ -103,22 +103,36 @@ def source_digest():
     return h.hexdigest()[:16]
 
 
-def offsets_read(kernel, M, T):
+def offsets_read(kernel, M, T, plan=""):
     """4-byte offsets one launch of `kernel` reads: every tile's (the plain
     row-wave kernel), one per 16-row block plus the end (the 16-row MFMA
-    kernels), or one per 8-row step plus the end and one half-row start per
-    row (the eight-row fp16 kernel)."""
+    kernels), one per 8-row step plus the end and one half-row start per row
+    (the eight-row fp16 kernel), or the bounds of every row's chunks (the
+    split-K kernels: chunks of `chunk_tiles` tiles inside K ranges of
+    `tiles_per_split`, from the plan's description)."""
     if kernel.startswith("k_rowwave"):
         return M * T
     if kernel.startswith("k_bt8_f16"):
         return (M + 7) // 8 + 1 + M
+    if kernel.startswith("k_bsk"):
+        m_tps, m_ct = re.search(r"tiles_per_split=(\d+)", plan), re.search(r"chunk_tiles=(\d+)", plan)
+        if not (m_tps and m_ct):
+            return M * T          # plan not described (a forced choice): at most every tile's
+        tps, ct = int(m_tps.group(1)), int(m_ct.group(1))
+        bounds = 1   # the row's start
+        t = 0
+        while t < T:
+            te = min(T, t + tps)
+            bounds += -(-(te - t) // ct)
+            t = te
+        return M * bounds
     return (M + 15) // 16 + 1
 
 
-def step_bytes(dm, N, kernel, fp16):
+def step_bytes(dm, N, kernel, fp16, plan=""):
     """Algorithmic bytes of one SpMM call: words, the offsets the kernel
     reads, payload, X and Y."""
-    stream = dm.stream_bytes(with_offsets=False) + 4 * offsets_read(kernel, dm.M, dm.T)
+    stream = dm.stream_bytes(with_offsets=False) + 4 * offsets_read(kernel, dm.M, dm.T, plan)
     if fp16:
         return stream + 2 * N * dm.K + 2 * dm.M * N
     return stream + N * ((dm.K + 1) // 2) + 4 * dm.M * N
@@ -446,6 +460,7 @@ def calibration_kernels():
     read probe over COPY_BYTES (reads them) and an int32 bitwise_not over
     COPY_BYTES (reads and writes them), five launches each, on buffers far
     larger than the Infinity Cache."""
+    import numpy as np
     import torch
     n = COPY_BYTES // 4
     src = torch.arange(n, dtype=torch.int32, device="cuda:0")
@@ -460,7 +475,9 @@ def calibration_kernels():
         other.fill_(2)
         torch.bitwise_not(src, out=dst)
     torch.cuda.synchronize()
-    ok = bool(torch.equal(dst[:1024], ~src[:1024]))
+    # checked on the host: a device-side check would launch a small kernel
+    # of the same name, and the summary averages over that name's dispatches
+    ok = bool(np.array_equal(dst[:1024].cpu().numpy(), ~src[:1024].cpu().numpy()))
     print(json.dumps({"calibration_bytes": COPY_BYTES, "dispatches": 5, "ok": ok}), flush=True)
 
 
@@ -474,7 +491,20 @@ def prepare(args, workload, index, n):
 
     dev = torch.device("cuda:0")
     bsp.load_library()
-    problems = workloads.make(workload)
+    if workload.startswith("custom:"):
+        # custom:DTYPE:M:K:N:DENSITY[:SEED] -- a seeded random problem of any
+        # shape (selection A/B runs on shapes outside the named workloads)
+        parts = workload.split(":")
+        dty, Mc, Kc, Nc, dens = parts[1], int(parts[2]), int(parts[3]), int(parts[4]), float(parts[5])
+        seed = int(parts[6]) if len(parts) > 6 else 12345
+        if dty == "int4":
+            problems = [workloads.random_int4_problem(seed, Mc, Kc, Nc, keep=dens,
+                                                      name=f"custom_int4_{Mc}x{Kc}_d{dens:g}")]
+        else:
+            problems = [workloads.random_fp16_problem(seed, Mc, Kc, Nc, sparsity=1.0 - dens,
+                                                      name=f"custom_fp16_{Mc}x{Kc}_d{dens:g}")]
+    else:
+        problems = workloads.make(workload)
     problem = problems[index]
     if n:
         widest = max(problems, key=lambda p: p.N) if problem.dtype == "fp16" else problem
@@ -484,9 +514,9 @@ def prepare(args, workload, index, n):
     fp16 = problem.dtype == "fp16"
     N, M, K = problem.N, problem.M, problem.K
     enc = bsp.encode(problem.W)
-    algo = {"auto": bsp.ALGO_AUTO, "rowwave": bsp.ALGO_ROWWAVE, "mfma": bsp.ALGO_MFMA}[args.algo]
+    algo = {"auto": bsp.ALGO_AUTO, "rowwave": bsp.ALGO_ROWWAVE, "mfma": bsp.ALGO_MFMA, "splitk": bsp.ALGO_SPLITK}[args.algo]
     dt = bsp.FP16 if fp16 else bsp.INT4
-    chosen = algo if algo != bsp.ALGO_AUTO else bsp.select(dt, M, K, N, enc.nnz)
+    chosen = algo
     dm0 = enc.to_device(dev)
     if fp16:
         Xd = torch.from_numpy(problem.X.copy()).to(dev)
@@ -506,16 +536,20 @@ def prepare(args, workload, index, n):
         copies.append((dm, Xd.clone(), torch.empty((N, M), dtype=y_dtype, device=dev)))
     torch.cuda.synchronize()
 
+    # the split plans' workspace (calls on one stream share it in order)
+    ws = bsp.new_workspace(dt, M, K, N, enc.nnz, device=dev) if args.workspace else None
+
     def step(i):
         dm, x, y = copies[i % R]
         if fp16:
-            bsp.spmm_f16(dm, x, Y=y, algo=chosen)
+            bsp.spmm_f16(dm, x, Y=y, algo=chosen, workspace=ws)
         else:
-            bsp.spmm_w4a4(dm, x, N, Y=y, algo=chosen)
+            bsp.spmm_w4a4(dm, x, N, Y=y, algo=chosen, workspace=ws)
 
-    kernel = kernel_symbol(bsp, chosen, dt, M, K, N, enc.nnz)
+    kernel = kernel_symbol(bsp, chosen, dt, M, K, N, enc.nnz, workspace=ws is not None)
+    plan = bsp.describe(dt, M, K, N, enc.nnz, workspace=ws is not None)
     return dict(problem=problem, fp16=fp16, enc=enc, dm0=dm0, copies=copies, R=R, step=step, chosen=chosen,
-                name=algo_name(bsp, chosen), kernel=kernel, dt=dt)
+                name=algo_label(kernel), kernel=kernel, dt=dt, plan=plan)
 
 
 def measure(args, workload, index, n, with_probe=True):
@@ -575,7 +609,7 @@ def measure(args, workload, index, n, with_probe=True):
     del graph
 
     kernel = ctx["kernel"]
-    nbytes = step_bytes(dm0, N, kernel, fp16)
+    nbytes = step_bytes(dm0, N, kernel, fp16, ctx["plan"])
     value = nbytes / (ms_per_step * 1e-3) / 1e9
     achieved = nbytes / (kern_ms * 1e-3) / 1e9
     dense_ops = 2.0 * M * K * N
@@ -626,7 +660,7 @@ def measure(args, workload, index, n, with_probe=True):
 
 
 def algo_label(kernel):
-    return "rowwave" if kernel.startswith("k_rowwave") else "mfma"
+    return "rowwave" if kernel.startswith("k_rowwave") else "splitk" if kernel.startswith("k_bsk") else "mfma"
 
 
 def counter_run(args):
@@ -646,10 +680,12 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="qkv", help="tiny | qkv | ffn | lowsparse | fp16")
+    ap.add_argument("--workload", default="qkv",
+                    help="tiny | qkv | ffn | lowsparse | fp16 | custom:DTYPE:M:K:N:DENSITY[:SEED]")
     ap.add_argument("--index", type=int, default=0, help="matrix index inside the workload (ffn: 0 up, 1 down)")
     ap.add_argument("--n", type=int, default=0, help="override N (slices the workload's widest X)")
-    ap.add_argument("--algo", default="auto", choices=["auto", "rowwave", "mfma"])
+    ap.add_argument("--algo", default="auto", choices=["auto", "rowwave", "mfma", "splitk"])
+    ap.add_argument("--workspace", action="store_true", help="call the *_ws entry point with a workspace")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probe", action="store_true", help="leave out the read probe (roofline.achievable)")
     ap.add_argument("--sweep", action="store_true", help="one line per (workload, N) of the N sweep")
@@ -678,7 +714,7 @@ def main():
     if args.peak_read:
         import torch
         ctx = prepare(args, args.workload, args.index, args.n)
-        nbytes = step_bytes(ctx["dm0"], ctx["problem"].N, ctx["kernel"], ctx["fp16"])
+        nbytes = step_bytes(ctx["dm0"], ctx["problem"].N, ctx["kernel"], ctx["fp16"], ctx["plan"])
         del ctx
         torch.cuda.empty_cache()
         print(json.dumps({"peak_read": probe_achievable(nbytes, args.steps)}), flush=True)

@@ -22,7 +22,8 @@ from typing import Optional
 import numpy as np
 
 __all__ = ["load_library", "encode", "pack_int4", "Encoded", "DeviceMatrix", "spmm_w4a4", "spmm_f16",
-           "select", "describe", "BspError", "ALGO_AUTO", "ALGO_ROWWAVE", "ALGO_MFMA",
+           "select", "describe", "workspace_bytes", "BspError", "ALGO_AUTO", "ALGO_ROWWAVE", "ALGO_MFMA",
+           "ALGO_SPLITK",
            "INT4", "FP16", "PAYLOAD_ALIGN", "MAX_N", "library_path"]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -30,13 +31,14 @@ library_path = os.path.join(HERE, "libbitmap_spmm.so")
 
 OK, E_ARG, E_RANGE, E_CAPACITY, E_OVERFLOW, E_HIP, E_UNSUPPORTED = 0, 1, 2, 3, 4, 5, 6
 INT4, FP16 = 0, 1
-ALGO_AUTO, ALGO_ROWWAVE, ALGO_MFMA = 0, 1, 2
+ALGO_AUTO, ALGO_ROWWAVE, ALGO_MFMA, ALGO_SPLITK = 0, 1, 2, 3
 PAYLOAD_ALIGN = 16
 MAX_N = 32
 
 # Every symbol include/bitmap_spmm.h declares.
 EXPORTS = ["encode_bitmap_tiles", "pack_int4_activations", "spmm_bitmap_w4a4", "spmm_bitmap_w4a4_algo",
-           "spmm_bitmap_f16", "spmm_bitmap_f16_algo", "bsp_select", "bsp_describe_selection",
+           "spmm_bitmap_w4a4_ws", "spmm_bitmap_f16", "spmm_bitmap_f16_algo", "spmm_bitmap_f16_ws",
+           "bsp_workspace_bytes", "bsp_select", "bsp_describe_selection", "bsp_describe_selection_ws",
            "bsp_status_string", "bsp_version"]
 
 
@@ -69,6 +71,13 @@ def load_library():
         L.spmm_bitmap_f16.restype = I32
         L.spmm_bitmap_f16_algo.argtypes = [P, P, P, I64, I64, I64, P, I64, P, I32, P]
         L.spmm_bitmap_f16_algo.restype = I32
+        L.spmm_bitmap_w4a4_ws.argtypes = [P, P, P, I64, I64, I64, P, I64, P, P, I64, I32, P]
+        L.spmm_bitmap_w4a4_ws.restype = I32
+        L.spmm_bitmap_f16_ws.argtypes = [P, P, P, I64, I64, I64, P, I64, P, P, I64, I32, P]
+        L.spmm_bitmap_f16_ws.restype = I32
+        L.bsp_workspace_bytes.argtypes, L.bsp_workspace_bytes.restype = [I32, I64, I64, I64, I64, P], I32
+        L.bsp_describe_selection_ws.argtypes = [I32, I64, I64, I64, I64, ctypes.c_char_p, ctypes.c_size_t]
+        L.bsp_describe_selection_ws.restype = I32
         L.bsp_select.argtypes, L.bsp_select.restype = [I32, I64, I64, I64, I64], I32
         L.bsp_describe_selection.argtypes = [I32, I64, I64, I64, I64, ctypes.c_char_p, ctypes.c_size_t]
         L.bsp_describe_selection.restype = I32
@@ -214,8 +223,19 @@ def _check_dev(t, name, dtype, numel=None):
         raise ValueError(f"{name} has {t.numel()} elements, expected {numel}")
 
 
-def spmm_w4a4(W: DeviceMatrix, X, N: int, Y=None, algo: int = ALGO_AUTO, stream=None):
-    """Y[n][m] = sum_k W[m][k] X[k][n] (int32) on the GPU. X: uint8 [N][ceil(K/2)]."""
+def _ws_args(workspace):
+    if workspace is None:
+        return None, 0
+    import torch
+    if not isinstance(workspace, torch.Tensor) or not workspace.is_cuda or not workspace.is_contiguous():
+        raise TypeError("workspace must be a contiguous CUDA (HIP) tensor")
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+
+
+def spmm_w4a4(W: DeviceMatrix, X, N: int, Y=None, algo: int = ALGO_AUTO, stream=None, workspace=None):
+    """Y[n][m] = sum_k W[m][k] X[k][n] (int32) on the GPU. X: uint8 [N][ceil(K/2)].
+    workspace: an optional zero-initialised device tensor of at least
+    workspace_bytes(...) bytes, 256-byte aligned (enables the split plans)."""
     import torch
     if W.dtype != INT4:
         raise TypeError("spmm_w4a4 needs an int4 DeviceMatrix")
@@ -223,14 +243,15 @@ def spmm_w4a4(W: DeviceMatrix, X, N: int, Y=None, algo: int = ALGO_AUTO, stream=
     if Y is None:
         Y = torch.empty((N, W.M), dtype=torch.int32, device=X.device)
     _check_dev(Y, "Y", torch.int32, N * W.M)
-    rc = load_library().spmm_bitmap_w4a4_algo(
+    wp, wb = _ws_args(workspace)
+    rc = load_library().spmm_bitmap_w4a4_ws(
         _dptr(W.bitmaps), _dptr(W.offsets), _dptr(W.payload), W.payload.numel(), W.M, W.K,
-        _dptr(X), N, _dptr(Y), algo, _stream_handle(stream))
+        _dptr(X), N, _dptr(Y), wp, wb, algo, _stream_handle(stream))
     _check(rc, "spmm_bitmap_w4a4")
     return Y
 
 
-def spmm_f16(W: DeviceMatrix, X, Y=None, algo: int = ALGO_AUTO, stream=None):
+def spmm_f16(W: DeviceMatrix, X, Y=None, algo: int = ALGO_AUTO, stream=None, workspace=None):
     """fp16 Y [N][M] = W X with fp32 accumulation. X: float16 [N][K]."""
     import torch
     if W.dtype != FP16:
@@ -242,9 +263,10 @@ def spmm_f16(W: DeviceMatrix, X, Y=None, algo: int = ALGO_AUTO, stream=None):
     if Y is None:
         Y = torch.empty((N, W.M), dtype=torch.float16, device=X.device)
     _check_dev(Y, "Y", torch.float16, N * W.M)
-    rc = load_library().spmm_bitmap_f16_algo(
+    wp, wb = _ws_args(workspace)
+    rc = load_library().spmm_bitmap_f16_ws(
         _dptr(W.bitmaps), _dptr(W.offsets), _dptr(W.payload), W.payload.numel(), W.M, W.K,
-        _dptr(X), N, _dptr(Y), algo, _stream_handle(stream))
+        _dptr(X), N, _dptr(Y), wp, wb, algo, _stream_handle(stream))
     _check(rc, "spmm_bitmap_f16")
     return Y
 
@@ -253,7 +275,26 @@ def select(dtype: int, M: int, K: int, N: int, nnz: int = -1) -> int:
     return int(load_library().bsp_select(dtype, M, K, N, nnz))
 
 
-def describe(dtype: int, M: int, K: int, N: int, nnz: int = -1) -> str:
-    buf = ctypes.create_string_buffer(256)
-    _check(load_library().bsp_describe_selection(dtype, M, K, N, nnz, buf, 256), "bsp_describe_selection")
+def describe(dtype: int, M: int, K: int, N: int, nnz: int = -1, workspace: bool = False) -> str:
+    """The plan (kernel and launch shape) of the plain entry points, or with
+    workspace=True of the *_ws entry points given a workspace."""
+    buf = ctypes.create_string_buffer(384)
+    fn = load_library().bsp_describe_selection_ws if workspace else load_library().bsp_describe_selection
+    _check(fn(dtype, M, K, N, nnz, buf, 384), "bsp_describe_selection")
     return buf.value.decode()
+
+
+def workspace_bytes(dtype: int, M: int, K: int, N: int, nnz: int = -1) -> int:
+    """Bytes of workspace the *_ws entry points want for a problem (0: none)."""
+    out = ctypes.c_int64(0)
+    _check(load_library().bsp_workspace_bytes(dtype, M, K, N, nnz, ctypes.byref(out)), "bsp_workspace_bytes")
+    return int(out.value)
+
+
+def new_workspace(dtype: int, M: int, K: int, N: int, nnz: int = -1, device="cuda"):
+    """A zero-filled device workspace for the split plans (None if none is needed)."""
+    import torch
+    n = workspace_bytes(dtype, M, K, N, nnz)
+    if n == 0:
+        return None
+    return torch.zeros(n, dtype=torch.uint8, device=device)

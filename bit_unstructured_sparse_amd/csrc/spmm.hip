@@ -19,6 +19,7 @@
 #include "kernels_rowwave.hip"
 #include "kernels_bt64.hip"
 #include "kernels_bt64_f16.hip"
+#include "kernels_splitk.hip"
 
 namespace {
 
@@ -31,7 +32,7 @@ int check_args(const void *bitmaps, const void *offsets, const void *payload, in
                int64_t M, int64_t K, const void *X, int64_t N, const void *Y, int algo, Shape *s) {
     if (M < 0 || K < 0 || N < 0 || payload_bytes < 0) return BSP_E_ARG;
     if (N > BSP_MAX_N) return BSP_E_ARG;
-    if (algo < BSP_ALGO_AUTO || algo > BSP_ALGO_MFMA) return BSP_E_ARG;
+    if (algo < BSP_ALGO_AUTO || algo > BSP_ALGO_SPLITK) return BSP_E_ARG;
     if (K >= BSP_MAX_K) return BSP_E_OVERFLOW;
     if (M > INT32_MAX) return BSP_E_OVERFLOW;
     const int64_t T = (K + 63) / 64;
@@ -51,19 +52,198 @@ int launch_status() {
     return e == hipSuccess ? BSP_OK : BSP_E_HIP;
 }
 
-// Whether a kernel family can run a problem (layout constraints of the fast paths).
-bool algo_supported(int algo, int dtype, const Shape &s) {
+// A chosen kernel and its launch shape.
+enum PlanKind { PK_ROWWAVE = 0, PK_BT64, PK_BT8F16, PK_BT64F16, PK_BSK };
+struct Plan {
+    int kind = PK_ROWWAVE;
+    int algo = BSP_ALGO_ROWWAVE;
+    BtPlan bt;
+    Bf8Plan bf8;
+    BfPlan bf;
+    SkPlan sk;
+    int64_t ws_bytes() const { return kind == PK_BSK ? sk.ws_bytes : 0; }
+};
+
+// K ranges per block set the automatic plan gives the split-K kernels when
+// a workspace is given: 2 for fp16 past K = 4096 (4096 x 11008: 28.1 us
+// against 31.0 at N = 8, 26.0 against 27.2 at N = 1); 1 for int4 (4096 x
+// 20000 at N = 8: 23.6 us with 2 against 22.2 with 1).
+int preferred_splits(int dtype, const Shape &s) {
+    return dtype == BSP_FP16 && s.T > 64 ? 2 : 1;
+}
+
+// The MFMA family: the 16-row block kernels (int4: streaming up to K = 4096,
+// ring above, up to K = 16384; fp16: eight-row steps at N <= 8, 16-row
+// blocks above, K <= 4096 and K % 8 == 0).
+bool plan_mfma(int dtype, const Shape &s, int64_t pbytes, Plan *p) {
+    p->algo = BSP_ALGO_MFMA;
+    if (dtype == BSP_INT4) {
+        if (!bt64_plan(s.M, s.K, s.N, pbytes, &p->bt)) return false;
+        p->kind = PK_BT64;
+        return true;
+    }
+    if (bf8_plan(s.M, s.K, s.N, pbytes, &p->bf8)) {
+        p->kind = PK_BT8F16;
+        return true;
+    }
+    if (!bf_plan(s.M, s.K, s.N, pbytes, &p->bf)) return false;
+    p->kind = PK_BT64F16;
+    return true;
+}
+
+// The split-K family: any K (fp16: K % 8 == 0), `splits` K ranges per block
+// set (fewer if the shape cannot take them; 1 without a workspace).
+bool plan_splitk(int dtype, const Shape &s, int64_t pbytes, int splits, Plan *p) {
+    p->algo = BSP_ALGO_SPLITK;
+    if (dtype == BSP_FP16 && s.K % 8 != 0) return false;
+    for (; splits >= 1; splits /= 2)
+        if (sk_plan(dtype, s.M, s.K, s.N, pbytes, splits, &p->sk)) {
+            p->kind = PK_BSK;
+            return true;
+        }
+    return false;
+}
+
+// Shape-aware selection (UnionSparse, Sec. I, names it without a rule; the
+// thresholds are the measured ones recorded with the design). The MFMA block
+// kernels wherever they run (int4: K <= 16384; fp16: K <= 4096, K % 8 == 0):
+// on every shape both can run they measured faster than the split-K kernel
+// (4096 x 11008 int4 N = 16: 11.2 us against 14.9 / 16.9 with 1 / 2 K
+// ranges; 8192 x 8192 N = 32: 16.7 against 28.0; fp16 4096 x 4096 N = 32:
+// 16.2 against 25.3). Beyond them the split-K kernel (8-24 times faster than
+// the plain kernel there), with the K ranges above; fp16 with K % 8 != 0:
+// the plain kernel. A forced BSP_ALGO_SPLITK takes 2 K ranges per 2-block set
+// when given a workspace. Forced algorithms run their own family or return
+// BSP_E_UNSUPPORTED.
+int choose_plan(int dtype, const Shape &s, int64_t pbytes, int algo, bool have_ws, Plan *p) {
+    *p = Plan{};
     switch (algo) {
-        case BSP_ALGO_ROWWAVE: return true;
-        case BSP_ALGO_MFMA: return dtype == BSP_INT4 ? bt64_supported(s.K, s.N) : bf_supported(s.K, s.N);
-        default: return false;
+        case BSP_ALGO_ROWWAVE:
+            p->kind = PK_ROWWAVE;
+            p->algo = BSP_ALGO_ROWWAVE;
+            return BSP_OK;
+        case BSP_ALGO_MFMA:
+            return plan_mfma(dtype, s, pbytes, p) ? BSP_OK : BSP_E_UNSUPPORTED;
+        case BSP_ALGO_SPLITK:
+            return plan_splitk(dtype, s, pbytes, have_ws ? 2 : 1, p) ? BSP_OK : BSP_E_UNSUPPORTED;
+        default:
+            break;
+    }
+    if (s.M == 0 || s.N == 0 || s.K == 0) {
+        p->kind = PK_ROWWAVE;
+        return BSP_OK;
+    }
+    if (plan_mfma(dtype, s, pbytes, p)) return BSP_OK;
+    if (plan_splitk(dtype, s, pbytes, have_ws ? preferred_splits(dtype, s) : 1, p)) return BSP_OK;
+    p->kind = PK_ROWWAVE;
+    p->algo = BSP_ALGO_ROWWAVE;
+    return BSP_OK;
+}
+
+void describe_plan(int dtype, const Plan &p, char *launch, size_t n) {
+    launch[0] = 0;
+    switch (p.kind) {
+        case PK_BT64:
+            if (p.bt.streaming)
+                snprintf(launch, n, " kernel=k_bt64s_w4a4 grid=%u block=%d lds=%zu stage_kb=%d stagger=%d", p.bt.grid,
+                         64 * p.bt.nwaves, p.bt.lds, p.bt.area_kb, p.bt.stagger);
+            else
+                snprintf(launch, n, " kernel=k_bt64_w4a4 grid=%u block=%d lds=%zu tiles_per_lane=%d one_pass=%d",
+                         p.bt.grid, 64 * p.bt.nwaves, p.bt.lds, p.bt.tpl, p.bt.one_pass);
+            break;
+        case PK_BT8F16:
+            snprintf(launch, n, " kernel=k_bt8_f16 grid=%u block=%d lds=%zu stage_kb=%u step_slots=%d", p.bf8.grid,
+                     64 * p.bf8.nwaves, p.bf8.lds, p.bf8.area_kb, p.bf8.nstep);
+            break;
+        case PK_BT64F16:
+            snprintf(launch, n, " kernel=k_bt64_f16 grid=%u block=%d lds=%zu", p.bf.grid, 64 * p.bf.nwaves, p.bf.lds);
+            break;
+        case PK_BSK:
+            snprintf(launch, n, " kernel=k_bsk_%s grid=%u block=%d lds=%zu blocks_per_set=%d splits=%d "
+                     "tiles_per_split=%d chunk_tiles=%d slot_kb=%d workspace=%lld",
+                     dtype == BSP_INT4 ? "w4a4" : "f16", p.sk.grid, 64 * p.sk.nwaves, p.sk.lds, p.sk.nbs, p.sk.S,
+                     p.sk.tps, (dtype == BSP_INT4 ? 8 : 4) * p.sk.nwaves, p.sk.iseg, (long long)p.sk.ws_bytes);
+            break;
+        default:
+            snprintf(launch, n, " kernel=k_rowwave_%s", dtype == BSP_INT4 ? "w4a4" : "f16");
+            break;
     }
 }
 
-int select_algo(int dtype, const Shape &s, int64_t nnz) {
-    (void)nnz;
-    if (algo_supported(BSP_ALGO_MFMA, dtype, s)) return BSP_ALGO_MFMA;
-    return BSP_ALGO_ROWWAVE;
+int describe(int dtype, int64_t M, int64_t K, int64_t N, int64_t nnz, bool have_ws, char *buf, size_t n) {
+    if (dtype != BSP_INT4 && dtype != BSP_FP16) return BSP_E_ARG;
+    if (M < 0 || K < 0 || N < 0 || N > BSP_MAX_N || buf == nullptr || n == 0) return BSP_E_ARG;
+    const Shape s{M, K, N, (K + 63) / 64, M * ((K + 63) / 64)};
+    // payload bytes the encoder writes for nnz nonzeros (all of W when unknown)
+    const int64_t nz = nnz >= 0 ? nnz : M * K;
+    const int64_t pbytes = dtype == BSP_INT4 ? (nz + 1) / 2 : 2 * nz;
+    Plan p;
+    choose_plan(dtype, s, pbytes, BSP_ALGO_AUTO, have_ws, &p);
+    const char *name = p.algo == BSP_ALGO_ROWWAVE ? "rowwave" : p.algo == BSP_ALGO_MFMA ? "mfma" : "splitk";
+    char launch[256] = "";
+    if (M > 0 && N > 0) describe_plan(dtype, p, launch, sizeof launch);
+    snprintf(buf, n, "dtype=%s M=%lld K=%lld N=%lld nnz=%lld -> %s%s", dtype == BSP_INT4 ? "int4" : "fp16",
+             (long long)M, (long long)K, (long long)N, (long long)nnz, name, launch);
+    return BSP_OK;
+}
+
+// The workspace an SpMM call gets: non-null, 256-byte aligned, and at least
+// what the plan needs (checked by the caller of this helper).
+bool workspace_usable(const void *ws, int64_t bytes) {
+    return ws != nullptr && bytes > 0 && ((uintptr_t)ws & 255u) == 0;
+}
+
+int spmm_common(int dtype, const uint64_t *bitmaps, const uint32_t *offsets, const void *payload,
+                int64_t payload_bytes, int64_t M, int64_t K, const void *X, int64_t N, void *Y, void *workspace,
+                int64_t workspace_bytes, int algo, hipStream_t stream) {
+    Shape s;
+    int rc = check_args(bitmaps, offsets, payload, payload_bytes, M, K, X, N, Y, algo, &s);
+    if (rc != BSP_OK || M == 0 || N == 0) return rc;
+    if (workspace_bytes < 0 || (workspace == nullptr && workspace_bytes != 0)) return BSP_E_ARG;
+    if (workspace != nullptr && ((uintptr_t)workspace & 255u) != 0) return BSP_E_ARG;
+    const bool have_ws = workspace_usable(workspace, workspace_bytes);
+    Plan p;
+    rc = choose_plan(dtype, s, payload_bytes, algo, have_ws, &p);
+    if (rc != BSP_OK) return rc;
+    // The int4 MFMA and split-K kernels read X in whole dwords from its start
+    // (the last one may reach up to 3 bytes past N * ceil(K/2), inside the
+    // same page only when X starts on a 4-byte boundary); fp16 ones read
+    // 16-byte pieces. An X off the boundary takes the plain kernel (automatic
+    // choice) or is refused (forced).
+    const bool x_aligned = ((uintptr_t)X & (dtype == BSP_INT4 ? 3u : 15u)) == 0;
+    if (p.kind != PK_ROWWAVE && !x_aligned) {
+        if (algo != BSP_ALGO_AUTO) return BSP_E_UNSUPPORTED;
+        p = Plan{};
+    }
+    if (p.ws_bytes() > workspace_bytes) return BSP_E_CAPACITY;
+    const uint32_t pb = (uint32_t)payload_bytes;
+    switch (p.kind) {
+        case PK_BT64:
+            launch_bt64_w4a4(p.bt, bitmaps, offsets, (const uint8_t *)payload, pb, (int)M, (int)K, (const uint8_t *)X,
+                             (int)N, (int32_t *)Y, stream);
+            break;
+        case PK_BT8F16:
+            launch_bt8_f16(p.bf8, bitmaps, offsets, (const uint16_t *)payload, pb, (int)M, (int)K, (const uint16_t *)X,
+                           (int)N, (uint16_t *)Y, stream);
+            break;
+        case PK_BT64F16:
+            launch_bt64_f16(p.bf, bitmaps, offsets, (const uint16_t *)payload, pb, (int)M, (int)K, (const uint16_t *)X,
+                            (int)N, (uint16_t *)Y, stream);
+            break;
+        case PK_BSK:
+            launch_bsk(p.sk, sk_args(p.sk, bitmaps, offsets, payload, pb, (int)M, (int)K, X, (int)N, Y, workspace),
+                       stream);
+            break;
+        default:
+            if (dtype == BSP_INT4)
+                launch_rowwave_w4a4(bitmaps, offsets, (const uint8_t *)payload, pb, (int)M, (int)K, (const uint8_t *)X,
+                                    (int)N, (int32_t *)Y, stream);
+            else
+                launch_rowwave_f16(bitmaps, offsets, (const uint16_t *)payload, pb, (int)M, (int)K,
+                                   (const uint16_t *)X, (int)N, (uint16_t *)Y, stream);
+            break;
+    }
+    return launch_status();
 }
 
 }  // namespace
@@ -71,122 +251,77 @@ int select_algo(int dtype, const Shape &s, int64_t nnz) {
 extern "C" int bsp_select(int dtype, int64_t M, int64_t K, int64_t N, int64_t nnz) {
     if (dtype != BSP_INT4 && dtype != BSP_FP16) return -1;
     if (M < 0 || K < 0 || N < 0 || N > BSP_MAX_N) return -1;
-    Shape s{M, K, N, (K + 63) / 64, M * ((K + 63) / 64)};
-    return select_algo(dtype, s, nnz);
+    const Shape s{M, K, N, (K + 63) / 64, M * ((K + 63) / 64)};
+    const int64_t nz = nnz >= 0 ? nnz : M * K;
+    Plan p;
+    choose_plan(dtype, s, dtype == BSP_INT4 ? (nz + 1) / 2 : 2 * nz, BSP_ALGO_AUTO, false, &p);
+    return p.algo;
 }
 
-extern "C" int bsp_describe_selection(int dtype, int64_t M, int64_t K, int64_t N, int64_t nnz,
-                                      char *buf, size_t n) {
-    int a = bsp_select(dtype, M, K, N, nnz);
-    if (a < 0 || buf == nullptr || n == 0) return BSP_E_ARG;
-    const char *name = a == BSP_ALGO_ROWWAVE ? "rowwave" : "mfma";
-    const char *ty = dtype == BSP_INT4 ? "int4" : "fp16";
-    // payload bytes the encoder writes for nnz nonzeros (all of W when unknown)
+extern "C" int bsp_describe_selection(int dtype, int64_t M, int64_t K, int64_t N, int64_t nnz, char *buf, size_t n) {
+    return describe(dtype, M, K, N, nnz, false, buf, n);
+}
+
+extern "C" int bsp_describe_selection_ws(int dtype, int64_t M, int64_t K, int64_t N, int64_t nnz, char *buf,
+                                         size_t n) {
+    return describe(dtype, M, K, N, nnz, true, buf, n);
+}
+
+extern "C" int bsp_workspace_bytes(int dtype, int64_t M, int64_t K, int64_t N, int64_t nnz, int64_t *bytes) {
+    if (dtype != BSP_INT4 && dtype != BSP_FP16) return BSP_E_ARG;
+    if (M < 0 || K < 0 || N < 0 || N > BSP_MAX_N || bytes == nullptr) return BSP_E_ARG;
+    if (K >= BSP_MAX_K || M > INT32_MAX || M * ((K + 63) / 64) >= INT32_MAX) return BSP_E_OVERFLOW;
+    const Shape s{M, K, N, (K + 63) / 64, M * ((K + 63) / 64)};
     const int64_t nz = nnz >= 0 ? nnz : M * K;
-    const int64_t pbytes = dtype == BSP_INT4 ? (nz + 1) / 2 : 2 * nz;
-    char launch[160] = "";
-    if (a == BSP_ALGO_MFMA && M > 0 && N > 0) {
-        if (dtype == BSP_INT4) {
-            BtPlan p;
-            if (bt64_plan(M, K, N, pbytes, &p)) {
-                if (p.streaming)
-                    snprintf(launch, sizeof launch, " kernel=k_bt64s_w4a4 grid=%u block=%d lds=%zu stage_kb=%d stagger=%d",
-                             p.grid, 64 * p.nwaves, p.lds, p.area_kb, p.stagger);
-                else
-                    snprintf(launch, sizeof launch, " kernel=k_bt64_w4a4 grid=%u block=%d lds=%zu tiles_per_lane=%d one_pass=%d",
-                             p.grid, 64 * p.nwaves, p.lds, p.tpl, p.one_pass);
-            }
-        } else {
-            Bf8Plan p8;
-            BfPlan p;
-            if (bf8_plan(M, K, N, pbytes, &p8))
-                snprintf(launch, sizeof launch, " kernel=k_bt8_f16 grid=%u block=%d lds=%zu stage_kb=%u step_slots=%d",
-                         p8.grid, 64 * p8.nwaves, p8.lds, p8.area_kb, p8.nstep);
-            else if (bf_plan(M, K, N, pbytes, &p))
-                snprintf(launch, sizeof launch, " kernel=k_bt64_f16 grid=%u block=%d lds=%zu", p.grid, 64 * p.nwaves,
-                         p.lds);
-        }
-    }
-    if (launch[0] == 0 && M > 0 && N > 0)
-        snprintf(launch, sizeof launch, " kernel=k_rowwave_%s", dtype == BSP_INT4 ? "w4a4" : "f16");
-    snprintf(buf, n, "dtype=%s M=%lld K=%lld N=%lld nnz=%lld -> %s%s", ty, (long long)M, (long long)K, (long long)N,
-             (long long)nnz, name, launch);
+    Plan p;
+    choose_plan(dtype, s, dtype == BSP_INT4 ? (nz + 1) / 2 : 2 * nz, BSP_ALGO_AUTO, true, &p);
+    // the forced split-K plan may want more than the automatic one
+    Plan q;
+    int64_t need = p.ws_bytes();
+    if (choose_plan(dtype, s, dtype == BSP_INT4 ? (nz + 1) / 2 : 2 * nz, BSP_ALGO_SPLITK, true, &q) == BSP_OK)
+        need = std::max(need, q.ws_bytes());
+    *bytes = need;
     return BSP_OK;
+}
+
+extern "C" int spmm_bitmap_w4a4_ws(const uint64_t *bitmaps, const uint32_t *offsets, const uint8_t *payload,
+                                   int64_t payload_bytes, int64_t M, int64_t K, const uint8_t *X, int64_t N,
+                                   int32_t *Y, void *workspace, int64_t workspace_bytes, int algo,
+                                   hipStream_t stream) {
+    return spmm_common(BSP_INT4, bitmaps, offsets, payload, payload_bytes, M, K, X, N, Y, workspace, workspace_bytes,
+                       algo, stream);
 }
 
 extern "C" int spmm_bitmap_w4a4_algo(const uint64_t *bitmaps, const uint32_t *offsets, const uint8_t *payload,
                                      int64_t payload_bytes, int64_t M, int64_t K,
                                      const uint8_t *X, int64_t N, int32_t *Y, int algo, hipStream_t stream) {
-    Shape s;
-    int rc = check_args(bitmaps, offsets, payload, payload_bytes, M, K, X, N, Y, algo, &s);
-    if (rc != BSP_OK || M == 0 || N == 0) return rc;
-    // The MFMA kernels read X in whole dwords from its start (the last one
-    // may reach up to 3 bytes past N * ceil(K/2), inside the same page only
-    // when X starts on a 4-byte boundary): an X off that boundary takes the
-    // plain kernel.
-    const bool x_aligned = ((uintptr_t)X & 3u) == 0;
-    if (algo == BSP_ALGO_AUTO) {
-        algo = select_algo(BSP_INT4, s, -1);
-        if (algo == BSP_ALGO_MFMA && !x_aligned) algo = BSP_ALGO_ROWWAVE;
-    }
-    if (!algo_supported(algo, BSP_INT4, s) || (algo == BSP_ALGO_MFMA && !x_aligned))
-        return BSP_E_UNSUPPORTED;   // a forced kernel never falls back
-    switch (algo) {
-        case BSP_ALGO_MFMA: {
-            BtPlan plan;
-            if (!bt64_plan(M, K, N, payload_bytes, &plan)) return BSP_E_UNSUPPORTED;
-            launch_bt64_w4a4(plan, bitmaps, offsets, payload, (uint32_t)payload_bytes, (int)M, (int)K, X, (int)N,
-                             Y, stream);
-            break;
-        }
-        default:
-        case BSP_ALGO_ROWWAVE:
-            launch_rowwave_w4a4(bitmaps, offsets, payload, (uint32_t)payload_bytes, (int)M, (int)K,
-                                X, (int)N, Y, stream);
-            break;
-    }
-    return launch_status();
+    return spmm_common(BSP_INT4, bitmaps, offsets, payload, payload_bytes, M, K, X, N, Y, nullptr, 0, algo, stream);
 }
 
 extern "C" int spmm_bitmap_w4a4(const uint64_t *bitmaps, const uint32_t *offsets, const uint8_t *payload,
                                 int64_t payload_bytes, int64_t M, int64_t K,
                                 const uint8_t *X, int64_t N, int32_t *Y, hipStream_t stream) {
-    return spmm_bitmap_w4a4_algo(bitmaps, offsets, payload, payload_bytes, M, K, X, N, Y, BSP_ALGO_AUTO, stream);
+    return spmm_common(BSP_INT4, bitmaps, offsets, payload, payload_bytes, M, K, X, N, Y, nullptr, 0,
+                       BSP_ALGO_AUTO, stream);
+}
+
+extern "C" int spmm_bitmap_f16_ws(const uint64_t *bitmaps, const uint32_t *offsets, const uint16_t *payload,
+                                  int64_t payload_bytes, int64_t M, int64_t K, const uint16_t *X, int64_t N,
+                                  uint16_t *Y, void *workspace, int64_t workspace_bytes, int algo,
+                                  hipStream_t stream) {
+    return spmm_common(BSP_FP16, bitmaps, offsets, payload, payload_bytes, M, K, X, N, Y, workspace, workspace_bytes,
+                       algo, stream);
 }
 
 extern "C" int spmm_bitmap_f16_algo(const uint64_t *bitmaps, const uint32_t *offsets, const uint16_t *payload,
                                     int64_t payload_bytes, int64_t M, int64_t K,
                                     const uint16_t *X, int64_t N, uint16_t *Y, int algo, hipStream_t stream) {
-    Shape s;
-    int rc = check_args(bitmaps, offsets, payload, payload_bytes, M, K, X, N, Y, algo, &s);
-    if (rc != BSP_OK || M == 0 || N == 0) return rc;
-    if (algo == BSP_ALGO_AUTO) algo = select_algo(BSP_FP16, s, -1);
-    if (!algo_supported(algo, BSP_FP16, s)) return BSP_E_UNSUPPORTED;   // a forced kernel never falls back
-    switch (algo) {
-        case BSP_ALGO_MFMA: {
-            Bf8Plan plan8;
-            if (bf8_plan(M, K, N, payload_bytes, &plan8)) {
-                launch_bt8_f16(plan8, bitmaps, offsets, payload, (uint32_t)payload_bytes, (int)M, (int)K, X, (int)N, Y,
-                               stream);
-                break;
-            }
-            BfPlan plan;
-            if (!bf_plan(M, K, N, payload_bytes, &plan)) return BSP_E_UNSUPPORTED;
-            launch_bt64_f16(plan, bitmaps, offsets, payload, (uint32_t)payload_bytes, (int)M, (int)K, X, (int)N,
-                            Y, stream);
-            break;
-        }
-        default:
-        case BSP_ALGO_ROWWAVE:
-            launch_rowwave_f16(bitmaps, offsets, payload, (uint32_t)payload_bytes, (int)M, (int)K,
-                               X, (int)N, Y, stream);
-            break;
-    }
-    return launch_status();
+    return spmm_common(BSP_FP16, bitmaps, offsets, payload, payload_bytes, M, K, X, N, Y, nullptr, 0, algo, stream);
 }
 
 extern "C" int spmm_bitmap_f16(const uint64_t *bitmaps, const uint32_t *offsets, const uint16_t *payload,
                                int64_t payload_bytes, int64_t M, int64_t K,
                                const uint16_t *X, int64_t N, uint16_t *Y, hipStream_t stream) {
-    return spmm_bitmap_f16_algo(bitmaps, offsets, payload, payload_bytes, M, K, X, N, Y, BSP_ALGO_AUTO, stream);
+    return spmm_common(BSP_FP16, bitmaps, offsets, payload, payload_bytes, M, K, X, N, Y, nullptr, 0, BSP_ALGO_AUTO,
+                       stream);
 }

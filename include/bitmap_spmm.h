@@ -76,7 +76,12 @@ typedef enum bsp_dtype { BSP_INT4 = 0, BSP_FP16 = 1 } bsp_dtype;
 typedef enum bsp_algo {
     BSP_ALGO_AUTO = 0,
     BSP_ALGO_ROWWAVE = 1,   /* one wavefront per output row; plain per-nonzero decode (any shape) */
-    BSP_ALGO_MFMA = 2       /* lane-per-tile decode from LDS-staged tiles + int8 / fp16 MFMA */
+    BSP_ALGO_MFMA = 2,      /* lane-per-tile decode from LDS-staged 16-row blocks over all of K + int8 / fp16
+                               MFMA (int4: K <= 16384; fp16: K <= 4096, K % 8 == 0) */
+    BSP_ALGO_SPLITK = 3     /* the same decode and MFMA over K ranges of block sets (UnionSparse Sec. VI-C,
+                               Alg. 2: partial tiles, then a reduction): any K (fp16: K % 8 == 0); with a
+                               workspace (the *_ws entry points) a block set's K ranges run on several
+                               workgroups and meet in it */
 } bsp_algo;
 
 /* The device payload allocation handed to the SpMM calls is a whole number
@@ -132,10 +137,10 @@ int pack_int4_activations(const int8_t *X, int64_t N, int64_t K, int64_t ldx, ui
  *                               BSP_PAYLOAD_ALIGN, >= ceil(nnz/2), bytes past the
  *                               encoded payload zero. No byte at or past it is read.
  *   M, K                        0 <= M < 2^31, 0 <= K < 2^25, M*ceil(K/64) < 2^31.
- *   X                           DEVICE, [N][ceil(K/2)] packed int4. The MFMA kernels
- *                               need X on a 4-byte boundary (any allocation is); an X
- *                               off it runs the plain kernel (BSP_ALGO_AUTO) or is
- *                               refused with BSP_E_UNSUPPORTED (BSP_ALGO_MFMA).
+ *   X                           DEVICE, [N][ceil(K/2)] packed int4. The MFMA and split-K
+ *                               kernels need X on a 4-byte boundary (any allocation is;
+ *                               fp16: 16 bytes); an X off it runs the plain kernel
+ *                               (BSP_ALGO_AUTO) or is refused with BSP_E_UNSUPPORTED.
  *   N                           0..32. N == 0 or M == 0: nothing is launched.
  *   Y                           DEVICE, [N][M] int32, fully overwritten (K == 0 gives zeros).
  *   stream                      HIP stream (NULL = null stream).
@@ -168,15 +173,52 @@ int spmm_bitmap_f16_algo(const uint64_t *bitmaps, const uint32_t *offsets, const
                          const uint16_t *X, int64_t N, uint16_t *Y, int algo, hipStream_t stream);
 
 /*
+ * Split-K with a workspace (UnionSparse Sec. VI-C, Alg. 2: each workgroup
+ * stores its partial tile, a reduction adds them; the N:M co-design page,
+ * Sec. 4.3, bounds the split count). The library allocates nothing; callers
+ * that want the split plans pass a workspace:
+ *
+ *   bsp_workspace_bytes -- bytes of workspace the *_ws entry points want for
+ *     a problem (their automatic plan and the forced BSP_ALGO_SPLITK plan),
+ *     0 when no plan of the shape uses one. nnz may be -1 when unknown.
+ *     Returns BSP_E_ARG / BSP_E_OVERFLOW for invalid shapes. Host only.
+ *
+ *   spmm_bitmap_w4a4_ws / spmm_bitmap_f16_ws -- as the *_algo entry points
+ *     with a workspace: DEVICE memory, 256-byte aligned, workspace_bytes long,
+ *     owned by the caller, ZERO-FILLED before its first use (it holds arrival
+ *     counters; every call leaves them at zero again). workspace may be NULL
+ *     with workspace_bytes 0 (then no plan needs one). A plan that needs more
+ *     than workspace_bytes returns BSP_E_CAPACITY and launches nothing; a
+ *     workspace off a 256-byte boundary returns BSP_E_ARG. Calls that share a
+ *     workspace must be ordered (one stream, or events): concurrent calls on
+ *     one workspace race. fp16 results do not depend on timing (partials are
+ *     added in a fixed order).
+ */
+int bsp_workspace_bytes(int dtype, int64_t M, int64_t K, int64_t N, int64_t nnz, int64_t *bytes);
+
+int spmm_bitmap_w4a4_ws(const uint64_t *bitmaps, const uint32_t *offsets, const uint8_t *payload,
+                        int64_t payload_bytes, int64_t M, int64_t K, const uint8_t *X, int64_t N, int32_t *Y,
+                        void *workspace, int64_t workspace_bytes, int algo, hipStream_t stream);
+
+int spmm_bitmap_f16_ws(const uint64_t *bitmaps, const uint32_t *offsets, const uint16_t *payload,
+                       int64_t payload_bytes, int64_t M, int64_t K, const uint16_t *X, int64_t N, uint16_t *Y,
+                       void *workspace, int64_t workspace_bytes, int algo, hipStream_t stream);
+
+/*
  * bsp_select -- the kernel BSP_ALGO_AUTO picks for a problem (shape-aware
  * selection; UnionSparse Sec. I names it, without a rule). nnz may be -1 when
  * unknown. Returns a bsp_algo value, or -1 for invalid arguments. Host only.
  */
 int bsp_select(int dtype, int64_t M, int64_t K, int64_t N, int64_t nnz);
 
-/* Human-readable description of bsp_select's choice and launch shape, written
- * NUL-terminated into buf (at most n bytes). Returns bsp_status. Host only. */
+/* Human-readable description of bsp_select's choice and launch shape (the
+ * plain and *_algo entry points, no workspace), written NUL-terminated into
+ * buf (at most n bytes). Returns bsp_status. Host only. */
 int bsp_describe_selection(int dtype, int64_t M, int64_t K, int64_t N, int64_t nnz, char *buf, size_t n);
+
+/* The same for the automatic plan of the *_ws entry points given a
+ * workspace of bsp_workspace_bytes. */
+int bsp_describe_selection_ws(int dtype, int64_t M, int64_t K, int64_t N, int64_t nnz, char *buf, size_t n);
 
 /* Static string for a bsp_status code. */
 const char *bsp_status_string(int status);

@@ -29,6 +29,13 @@ F16_TOL = 1e-2
 MFMA_KERNELS = {bsp.INT4: ("k_bt64s_w4a4", "k_bt64_w4a4"), bsp.FP16: ("k_bt8_f16", "k_bt64_f16")}
 
 
+def int4_kernel_for(K, N):
+    """The int4 MFMA kernel the plan picks for the small shapes below (at
+    most three 16-row blocks per workgroup): the streaming kernel up to
+    K = 4096, the ring kernel past it."""
+    return "k_bt64s_w4a4" if K <= 4096 else "k_bt64_w4a4"
+
+
 @pytest.fixture(scope="module")
 def dev():
     assert torch.cuda.is_available(), "GPU tests need a HIP device"
@@ -159,7 +166,7 @@ def test_w4a4_extremes(dev, algo, K):
     W[::3, ::5] = 7
     X = np.full((N, K), -8, np.int8)
     X[1::2] = 7
-    kern = "k_bt64s_w4a4" if K <= 4096 else "k_bt64_w4a4"
+    kern = int4_kernel_for(K, N)
     assert_w4a4(run_w4a4(W, X, algo, dev, expect_kernel=kern if algo == bsp.ALGO_MFMA else None), W, X)
 
 
@@ -212,15 +219,17 @@ def test_w4a4_ring_x_runs(dev, M, K, N):
 
 
 @pytest.mark.parametrize("algo", INT4_ALGOS, ids=lambda a: _NAMES[a])
-@pytest.mark.parametrize("M,K,N,dense_block", [(4100, 2048, 8, -1), (3000, 1024, 5, -1), (2048, 4096, 20, -1),
-                                               (1600, 4096, 8, -1), (1600, 4096, 8, 7), (1600, 4096, 8, 99)])
-def test_w4a4_staggered_staging(dev, algo, M, K, N, dense_block):
-    # rows whose payload is close to a multiple of 256 bytes (half density at
-    # K = 1024, 2048 and 4096, quarter density at 4096): the plan stages them
-    # in staggered runs; one fully dense block (or the last, ragged one) is
-    # too large for the staggered area and reads its windows from global memory
+@pytest.mark.parametrize("M,K,N,keep,dense_block", [(4100, 2048, 20, 0.5, -1), (3000, 1024, 24, 0.5, -1),
+                                                    (2048, 4096, 20, 0.25, -1), (1600, 4096, 17, 0.5, -1),
+                                                    (1600, 4096, 17, 0.5, 7), (1600, 4096, 17, 0.5, 99)])
+def test_w4a4_staggered_staging(dev, algo, M, K, N, keep, dense_block):
+    # the streaming kernel (N > 16) with rows whose payload is close to a
+    # multiple of 256 bytes (half density at K = 1024, 2048 and 4096, quarter
+    # density at 4096): the plan stages them in staggered runs; one fully
+    # dense block (or the last, ragged one) is too large for the staggered
+    # area and reads its windows from global memory
     rng = np.random.default_rng(M + K + N + dense_block)
-    keep = np.full((M, 1), 0.25 if N == 20 else 0.5)
+    keep = np.full((M, 1), keep)
     if dense_block >= 0:
         b = min(dense_block, (M - 1) // 16)
         keep[16 * b:16 * b + 16] = 1.0
@@ -231,6 +240,28 @@ def test_w4a4_staggered_staging(dev, algo, M, K, N, dense_block):
         assert "stagger=1" in bsp.describe(bsp.INT4, M, K, N, enc.nnz)
     assert_w4a4(run_w4a4(W, X, algo, dev, enc=enc, expect_kernel="k_bt64s_w4a4" if algo == bsp.ALGO_MFMA else None),
                 W, X)
+
+
+@pytest.mark.parametrize("algo", INT4_ALGOS, ids=lambda a: _NAMES[a])
+@pytest.mark.parametrize("M,K,N,pattern", [(64, 4096, 8, "alternate"), (4100, 4096, 16, "alternate"),
+                                           (300, 2048, 5, "every_fifth"), (48, 512, 1, "one_row"),
+                                           (16 * 768, 4096, 8, "alternate")])
+def test_w4a4_mixed_dense_rows(dev, algo, M, K, N, pattern):
+    # nearly dense rows beside sparse ones in the same 16-row blocks: blocks
+    # larger than the staging area sized from the average read their windows
+    # from global memory, the others from LDS
+    rng = np.random.default_rng(M + K + N)
+    keep = np.full((M, 1), 0.3)
+    if pattern == "alternate":
+        keep[::2] = 0.97
+    elif pattern == "every_fifth":
+        keep[::5] = 1.0
+    else:
+        keep[7] = 1.0
+    W = workloads._int4_weights(rng, M, K, keep)
+    X = workloads.int4_activations(rng, (N, K))
+    Y = run_w4a4(W, X, algo, dev, expect_kernel="k_bt64s_w4a4" if algo == bsp.ALGO_MFMA else None)
+    assert_w4a4(Y, W, X)
 
 
 @pytest.mark.parametrize("algo", INT4_ALGOS, ids=lambda a: _NAMES[a])
@@ -252,8 +283,8 @@ def test_w4a4_k_zero(dev, algo):
     assert not Y.cpu().numpy().any()
 
 
-# every N in 1..32 through the MFMA kernels: the streaming kernel (K = 608,
-# rows on a 4-byte boundary; K = 609, odd) and the ring kernel (K = 6432)
+# every N in 1..32 through the MFMA kernels: the streaming kernel at K = 608
+# (rows on a 4-byte boundary) and K = 609 (odd), the ring kernel at K = 6432
 @pytest.mark.parametrize("algo", INT4_ALGOS, ids=lambda a: _NAMES[a])
 @pytest.mark.parametrize("K", [64 * 9 + 32, 64 * 9 + 33, 64 * 100 + 32])
 @pytest.mark.parametrize("N", list(range(1, 33)))
@@ -261,7 +292,7 @@ def test_w4a4_every_n(dev, algo, K, N):
     if K > 4096 and algo != bsp.ALGO_MFMA:
         pytest.skip("the ring-kernel shape is checked through the forced MFMA path only")
     p = workloads.random_int4_problem(77 + K, 200, K, 32, keep=0.5)
-    kern = ("k_bt64s_w4a4" if K <= 4096 else "k_bt64_w4a4") if algo == bsp.ALGO_MFMA else None
+    kern = int4_kernel_for(K, N) if algo == bsp.ALGO_MFMA else None
     Y = run_w4a4(p.W, p.X[:N], algo, dev, expect_kernel=kern)
     assert_w4a4(Y, p.W, p.X[:N])
 
@@ -401,3 +432,131 @@ def test_w4a4_x_off_a_dword_boundary(dev, algo):
     bsp.spmm_w4a4(dm, Xd, 5, Y=Y, algo=algo)
     torch.cuda.synchronize()
     assert np.array_equal(Y.cpu().numpy(), oracle_w4a4(p.W, p.X))
+
+
+# --- the split-K kernels (K ranges of block sets; partials meet in a workspace) --------------
+
+def _ws(dtype, M, K, N, nnz, dev, extra=0):
+    n = bsp.workspace_bytes(dtype, M, K, N, nnz)
+    return torch.zeros(max(n, 256) + extra, dtype=torch.uint8, device=dev) if n else None
+
+
+SPLITK_INT4 = [  # (M, K, N, keep)
+    (48, 20000, 5, 0.5),         # K past the MFMA block kernels
+    (100, 64 * 300 + 17, 16, 0.3),
+    (4100, 11008, 16, 0.3),      # ragged last block, last set of one block
+    (33, 8192, 32, 0.7), (257, 64 * 130 + 32, 8, 0.5), (16, 128, 1, 0.5), (70, 300, 17, 0.9),
+    (200, 64 * 140, 24, 0.05),
+]
+
+
+@pytest.mark.parametrize("with_ws", [False, True], ids=["plain", "workspace"])
+@pytest.mark.parametrize("M,K,N,keep", SPLITK_INT4)
+def test_splitk_w4a4(dev, M, K, N, keep, with_ws):
+    p = workloads.random_int4_problem(M * 5 + K + N, M, K, N, keep=keep)
+    enc = bsp.encode(p.W)
+    dm = enc.to_device(dev)
+    Xd = torch.from_numpy(bsp.pack_int4(p.X)).to(dev)
+    ws = _ws(bsp.INT4, M, K, N, enc.nnz, dev) if with_ws else None
+    ref = oracle_w4a4(p.W, p.X)
+    for rep in range(2):   # the second call reuses the workspace (its counters were reset)
+        big, Y = _y_with_canary(N, M, torch.int32, dev)
+        bsp.spmm_w4a4(dm, Xd, N, Y=Y, algo=bsp.ALGO_SPLITK, workspace=ws)
+        torch.cuda.synchronize()
+        assert _canary_ok(big, N, M, torch.int32), "write past the end of Y"
+        assert np.array_equal(Y.cpu().numpy(), ref), f"call {rep}"
+    if ws is not None:
+        assert not ws[:256].any(), "arrival counters left nonzero"
+
+
+SPLITK_F16 = [(4096, 11008, 8), (100, 5000, 1), (257, 64 * 130 + 8, 16), (33, 8192, 32), (64, 4096, 32),
+              (4100, 4096, 17), (17, 64 * 65, 3)]
+
+
+@pytest.mark.parametrize("with_ws", [False, True], ids=["plain", "workspace"])
+@pytest.mark.parametrize("M,K,N", SPLITK_F16)
+def test_splitk_f16(dev, M, K, N, with_ws):
+    p = workloads.random_fp16_problem(M + 3 * K + N, M, K, N)
+    enc = bsp.encode(p.W)
+    dm = enc.to_device(dev)
+    Xd = torch.from_numpy(p.X).to(dev)
+    ws = _ws(bsp.FP16, M, K, N, enc.nnz, dev) if with_ws else None
+    r = oracle.spmm_f16(oracle.encode(p.W), p.X)
+    first = None
+    for rep in range(2):
+        big, Y = _y_with_canary(N, M, torch.float16, dev)
+        bsp.spmm_f16(dm, Xd, Y=Y, algo=bsp.ALGO_SPLITK, workspace=ws)
+        torch.cuda.synchronize()
+        assert _canary_ok(big.view(torch.int16), N, M, torch.float16), "write past the end of Y"
+        y = Y.cpu().numpy()
+        _assert_f16(y, r)
+        if first is None:
+            first = y.view(np.uint16).copy()
+        else:   # partials are added in a fixed order: the same bits every call
+            assert np.array_equal(first, y.view(np.uint16))
+
+
+@pytest.mark.parametrize("dtype", ["int4", "fp16"])
+def test_splitk_dense_block_global_windows(dev, dtype):
+    # one fully dense 16-row block among sparse ones: its segments exceed the
+    # slots sized from the average, and that block reads its windows from
+    # global memory (with and without a workspace)
+    rng = np.random.default_rng(7)
+    M, K, N = 96, 64 * 150, 8
+    keep = np.full((M, 1), 0.05)
+    keep[32:48] = 1.0
+    for with_ws in (False, True):
+        if dtype == "int4":
+            W = workloads._int4_weights(rng, M, K, keep)
+            X = workloads.int4_activations(rng, (N, K))
+            enc = bsp.encode(W)
+            ws = _ws(bsp.INT4, M, K, N, enc.nnz, dev) if with_ws else None
+            Y = bsp.spmm_w4a4(enc.to_device(dev), torch.from_numpy(bsp.pack_int4(X)).to(dev), N,
+                              algo=bsp.ALGO_SPLITK, workspace=ws)
+            torch.cuda.synchronize()
+            assert np.array_equal(Y.cpu().numpy(), oracle_w4a4(W, X))
+        else:
+            W = np.where(rng.random((M, K)) < keep, rng.normal(0, 0.02, (M, K)), 0).astype(np.float16)
+            X = rng.normal(0, 1, (N, K)).astype(np.float16)
+            enc = bsp.encode(W)
+            ws = _ws(bsp.FP16, M, K, N, enc.nnz, dev) if with_ws else None
+            Y = bsp.spmm_f16(enc.to_device(dev), torch.from_numpy(X).to(dev), algo=bsp.ALGO_SPLITK, workspace=ws)
+            torch.cuda.synchronize()
+            _assert_f16(Y.cpu().numpy(), oracle.spmm_f16(oracle.encode(W), X))
+
+
+@pytest.mark.parametrize("config,idx,N", [("ffn", 1, 16), ("lowsparse", 0, 32)])
+def test_splitk_full_workloads_forced_with_workspace(dev, config, idx, N):
+    # the split-K kernel with 2 K ranges per 2-block set on the named workloads
+    p, X, ref = _full_int4(config, idx, 32 if config == "lowsparse" else 0)
+    X = X[:N]
+    enc = bsp.encode(p.W)
+    ws = _ws(bsp.INT4, p.M, p.K, N, enc.nnz, dev)
+    Y = bsp.spmm_w4a4(enc.to_device(dev), torch.from_numpy(bsp.pack_int4(X)).to(dev), N, algo=bsp.ALGO_SPLITK,
+                      workspace=ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(Y.cpu().numpy(), ref[:N])
+
+
+def test_splitk_f16_full_workload_n32_with_workspace(dev):
+    p, r = _full_f16(1)
+    enc = bsp.encode(p.W)
+    ws = _ws(bsp.FP16, p.M, p.K, p.N, enc.nnz, dev)
+    Y = bsp.spmm_f16(enc.to_device(dev), torch.from_numpy(p.X).to(dev), algo=bsp.ALGO_SPLITK, workspace=ws)
+    torch.cuda.synchronize()
+    _assert_f16(Y.cpu().numpy(), r)
+
+
+@pytest.mark.parametrize("M,K,N", [(4096, 11008, 8), (300, 64 * 100, 1)])
+def test_f16_past_k4096_auto(dev, M, K, N):
+    # fp16 past K = 4096: the automatic plan is the split-K kernel (2 K ranges
+    # with a workspace, 1 without), never the plain kernel
+    p = workloads.random_fp16_problem(M + K + N, M, K, N)
+    enc = bsp.encode(p.W)
+    r = oracle.spmm_f16(oracle.encode(p.W), p.X)
+    for ws in (None, _ws(bsp.FP16, M, K, N, enc.nnz, dev)):
+        d = bsp.describe(bsp.FP16, M, K, N, enc.nnz, workspace=ws is not None)
+        assert "-> splitk kernel=k_bsk_f16" in d and ("splits=2 " in d) == (ws is not None), d
+        Y = bsp.spmm_f16(enc.to_device(dev), torch.from_numpy(p.X).to(dev), workspace=ws)
+        torch.cuda.synchronize()
+        _assert_f16(Y.cpu().numpy(), r)

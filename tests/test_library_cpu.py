@@ -153,7 +153,7 @@ def test_spmm_argument_errors_on_host(fn):
     assert call(pl=None) == bsp.E_ARG
     assert call(algo=99) == bsp.E_ARG
     assert call(algo=-1) == bsp.E_ARG
-    assert call(algo=3) == bsp.E_ARG                           # no third kernel family
+    assert call(algo=4) == bsp.E_ARG                           # no fourth kernel family
     # a forced kernel that cannot run the shape is an error, never a silent
     # fallback to another kernel (the shape is far past the fast path's K range)
     assert call(algo=bsp.ALGO_MFMA, K=1 << 20, pb=1 << 20) == bsp.E_UNSUPPORTED
@@ -164,12 +164,48 @@ def test_spmm_argument_errors_on_host(fn):
     assert call(M=0, Y=None, X=None) == bsp.OK
 
 
+def test_workspace_api_on_host():
+    # sizes: no workspace below the split thresholds; the split plans' counters
+    # and partials above (independent of nnz); errors before any launch
+    # (the size covers the forced split-K plan: 2 K ranges per 2-block set)
+    n = bsp.workspace_bytes(bsp.INT4, 4096, 11008, 16)
+    # 128 sets of 2 blocks, 2 K ranges: 512-byte counter area + 128 * 2 * 2 * 16 columns * 16 rows * 4 B
+    assert n == 512 + 128 * 2 * 2 * 16 * 16 * 4
+    assert bsp.workspace_bytes(bsp.INT4, 12288, 4096, 8) > 0
+    assert bsp.workspace_bytes(bsp.FP16, 4096, 11008, 8) > 0
+    assert bsp.workspace_bytes(bsp.FP16, 4096, 11008, 8, 1000) == bsp.workspace_bytes(bsp.FP16, 4096, 11008, 8)
+    L = bsp.load_library()
+    out = ctypes.c_int64(-1)
+    assert L.bsp_workspace_bytes(7, 1, 1, 1, -1, ctypes.byref(out)) == bsp.E_ARG
+    assert L.bsp_workspace_bytes(0, 1, 1, 33, -1, ctypes.byref(out)) == bsp.E_ARG
+    assert L.bsp_workspace_bytes(0, 1, 1 << 25, 1, -1, ctypes.byref(out)) == bsp.E_OVERFLOW
+    assert L.bsp_workspace_bytes(0, 1, 1, 1, -1, None) == bsp.E_ARG
+    # the _ws entry points: a workspace off a 256-byte boundary, NULL with a
+    # size, or smaller than the plan needs is refused on the host
+    f = L.spmm_bitmap_w4a4_ws
+    M, K, N = 4096, 11008, 16
+    base = dict(bm=FAKE, off=FAKE, pl=FAKE, pb=16 * (M * K // 32), X=FAKE, Y=FAKE)
+
+    def call(ws, wsb, algo=bsp.ALGO_AUTO):
+        return f(base["bm"], base["off"], base["pl"], base["pb"], M, K, base["X"], N, base["Y"], ws, wsb, algo, None)
+
+    assert call(ctypes.c_void_p(0x1010), n) == bsp.E_ARG          # not 256-byte aligned
+    assert call(None, 256) == bsp.E_ARG                            # size without a workspace
+    assert call(FAKE, -256) == bsp.E_ARG
+    # (every call here fails on the host: the pointers are fake, a launch would fault)
+    assert call(FAKE, 256, bsp.ALGO_SPLITK) == bsp.E_CAPACITY      # the forced split plan needs more
+    g = L.spmm_bitmap_f16_ws
+    assert g(FAKE, FAKE, FAKE, 16 * 1000, 4096, 11008, FAKE, 8, FAKE, FAKE, 256, bsp.ALGO_AUTO, None) == bsp.E_CAPACITY
+    # fp16 with K % 8 != 0 has no split-K plan
+    assert g(FAKE, FAKE, FAKE, 16, 16, 100, FAKE, 8, FAKE, None, 0, bsp.ALGO_SPLITK, None) == bsp.E_UNSUPPORTED
+
+
 def test_selection_is_defined_for_every_shape():
     for dt in (bsp.INT4, bsp.FP16):
         for N in range(1, 33):
             for (M, K) in [(512, 512), (12288, 4096), (11008, 4096), (4096, 11008), (8192, 8192), (1, 1), (7, 0)]:
                 a = bsp.select(dt, M, K, N)
-                assert a in (bsp.ALGO_ROWWAVE, bsp.ALGO_MFMA)
+                assert a in (bsp.ALGO_ROWWAVE, bsp.ALGO_MFMA, bsp.ALGO_SPLITK)
                 assert bsp.describe(dt, M, K, N).startswith("dtype=")
     assert bsp.select(bsp.INT4, 1, 1, 33) == -1
     assert bsp.select(5, 1, 1, 1) == -1
@@ -187,9 +223,22 @@ def test_description_names_the_launched_kernel():
     assert "-> mfma kernel=k_bt8_f16 " in d and "step_slots=4" in d
     d = bsp.describe(bsp.FP16, 4096, 4096, 32, 4096 * 4096 * 4 // 10)
     assert "-> mfma kernel=k_bt64_f16 " in d and "block=1024" in d
-    # any K up to 16384 takes the MFMA kernels (odd K too); beyond, the plain kernel
+    # any K up to 16384 takes the MFMA kernels (odd K too); beyond, the split-K
+    # kernel walking all of K per workgroup
     assert "-> mfma kernel=k_bt64s_w4a4 " in bsp.describe(bsp.INT4, 64, 100, 4)
     assert "-> mfma kernel=k_bt64_w4a4 " in bsp.describe(bsp.INT4, 64, 64 * 255 + 7, 4)
-    assert bsp.describe(bsp.INT4, 64, 16385, 4).endswith("-> rowwave kernel=k_rowwave_w4a4")
+    d = bsp.describe(bsp.INT4, 64, 16385, 4)
+    assert "-> splitk kernel=k_bsk_w4a4 " in d and "splits=1 " in d
+    # fp16 beyond K = 4096: the split-K kernel (2 K ranges with a workspace)
+    d = bsp.describe(bsp.FP16, 4096, 11008, 8)
+    assert "-> splitk kernel=k_bsk_f16 " in d and "splits=1 " in d
+    d = bsp.describe(bsp.FP16, 4096, 11008, 8, workspace=True)
+    assert "-> splitk kernel=k_bsk_f16 " in d and "splits=2 " in d and "blocks_per_set=2 " in d
+    # int4 with a workspace: the block kernels up to K = 16384, one K range beyond
+    assert "-> mfma kernel=k_bt64_w4a4 " in bsp.describe(bsp.INT4, 4096, 11008, 16, workspace=True)
+    d = bsp.describe(bsp.INT4, 4096, 20000, 8, workspace=True)
+    assert "-> splitk kernel=k_bsk_w4a4 " in d and "splits=1 " in d
+    # fp16 with K % 8 != 0: the plain kernel
+    assert bsp.describe(bsp.FP16, 64, 100, 4).endswith("-> rowwave kernel=k_rowwave_f16")
     # nothing to launch
     assert "kernel=" not in bsp.describe(bsp.INT4, 0, 4096, 8)

@@ -531,9 +531,12 @@ struct SkPlan {
     int64_t ws_bytes;   // workspace the plan needs (0 for S == 1)
 };
 
-// Workspace layout: the arrival counters (one uint32 per set, zero between
-// calls) first, then the partial sums at the next 256-byte boundary.
-static int64_t sk_ws_counters_bytes(int64_t nsets) { return (nsets * 4 + 255) / 256 * 256; }
+// Workspace layout: a fixed area of arrival counters (one uint32 per set,
+// zero between calls) first, then the partial sums. The counter area's size
+// does not depend on the problem, so the partials of one call never land on
+// counters another call of a different shape uses on the same workspace.
+#define SK_WS_COUNTERS 16384
+static int64_t sk_ws_counters_bytes() { return (int64_t)SK_WS_COUNTERS * 4; }
 
 // Plan for the K-range kernels. splits: 1 (no workspace: one workgroup walks
 // all of K of a block in chunks) or the number of K ranges per block set (2
@@ -544,6 +547,7 @@ static bool sk_plan(int dtype, int64_t M, int64_t K, int64_t N, int64_t payload_
     if (M <= 0 || K <= 0 || N < 1 || N > 32 || splits < 1 || splits > SK_NBS_MAX) return false;
     const int64_t T = (K + 63) / 64, blocks = (M + 15) / 16;
     if (splits > 1 && T < 2 * splits) return false;               // at least two tiles per split
+    if (splits > 1 && (blocks + splits - 1) / splits > SK_WS_COUNTERS) return false;   // one counter per set
     if (M * T + 1 > (int64_t)UINT32_MAX / 8) return false;        // 32-bit buffer ranges of words and offsets
     p->dtype = dtype;
     p->nb = N <= 16 ? 1 : 2;
@@ -575,7 +579,7 @@ static bool sk_plan(int dtype, int64_t M, int64_t K, int64_t N, int64_t payload_
     }
     p->grid = (unsigned)(p->nsets * p->S);
     const int64_t esize = 4;                                          // int32 or fp32 partials
-    p->ws_bytes = splits > 1 ? sk_ws_counters_bytes(p->nsets) + (int64_t)p->nsets * p->nbs * p->S * N * 16 * esize : 0;
+    p->ws_bytes = splits > 1 ? sk_ws_counters_bytes() + (int64_t)p->nsets * p->nbs * p->S * N * 16 * esize : 0;
     return true;
 }
 
@@ -586,7 +590,7 @@ static SkArgs sk_args(const SkPlan &p, const uint64_t *bitmaps, const uint32_t *
     a.M = M; a.K = K; a.N = N; a.T = (K + 63) / 64; a.X = X; a.Y = Y;
     a.nbs = p.nbs; a.nsets = p.nsets; a.S = p.S; a.tps = p.tps; a.iseg = p.iseg;
     a.ws_cnt = reinterpret_cast<uint32_t *>(workspace);
-    a.ws_part = workspace ? reinterpret_cast<uint8_t *>(workspace) + sk_ws_counters_bytes(p.nsets) : nullptr;
+    a.ws_part = workspace ? reinterpret_cast<uint8_t *>(workspace) + sk_ws_counters_bytes() : nullptr;
     return a;
 }
 

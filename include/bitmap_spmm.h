@@ -185,8 +185,9 @@ int spmm_bitmap_f16_algo(const uint64_t *bitmaps, const uint32_t *offsets, const
  *
  *   spmm_bitmap_w4a4_ws / spmm_bitmap_f16_ws -- as the *_algo entry points
  *     with a workspace: DEVICE memory, 256-byte aligned, workspace_bytes long,
- *     owned by the caller, ZERO-FILLED before its first use (it holds arrival
- *     counters; every call leaves them at zero again). workspace may be NULL
+ *     owned by the caller, ZERO-FILLED before its first use (its first 64 KiB
+ *     hold arrival counters; every call leaves them at zero again, so one
+ *     workspace serves calls of any shapes in turn). workspace may be NULL
  *     with workspace_bytes 0 (then no plan needs one). A plan that needs more
  *     than workspace_bytes returns BSP_E_CAPACITY and launches nothing; a
  *     workspace off a 256-byte boundary returns BSP_E_ARG. Calls that share a

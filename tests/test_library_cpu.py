@@ -169,8 +169,8 @@ def test_workspace_api_on_host():
     # and partials above (independent of nnz); errors before any launch
     # (the size covers the forced split-K plan: 2 K ranges per 2-block set)
     n = bsp.workspace_bytes(bsp.INT4, 4096, 11008, 16)
-    # 128 sets of 2 blocks, 2 K ranges: 512-byte counter area + 128 * 2 * 2 * 16 columns * 16 rows * 4 B
-    assert n == 512 + 128 * 2 * 2 * 16 * 16 * 4
+    # 128 sets of 2 blocks, 2 K ranges: the fixed 64 KiB counter area + 128 * 2 * 2 * 16 columns * 16 rows * 4 B
+    assert n == 65536 + 128 * 2 * 2 * 16 * 16 * 4
     assert bsp.workspace_bytes(bsp.INT4, 12288, 4096, 8) > 0
     assert bsp.workspace_bytes(bsp.FP16, 4096, 11008, 8) > 0
     assert bsp.workspace_bytes(bsp.FP16, 4096, 11008, 8, 1000) == bsp.workspace_bytes(bsp.FP16, 4096, 11008, 8)

@@ -39,7 +39,7 @@ MAX_N = 32
 EXPORTS = ["encode_bitmap_tiles", "pack_int4_activations", "spmm_bitmap_w4a4", "spmm_bitmap_w4a4_algo",
            "spmm_bitmap_w4a4_ws", "spmm_bitmap_f16", "spmm_bitmap_f16_algo", "spmm_bitmap_f16_ws",
            "bsp_workspace_bytes", "bsp_select", "bsp_describe_selection", "bsp_describe_selection_ws",
-           "bsp_status_string", "bsp_version"]
+           "bsp_status_string", "bsp_version", "spmm_bitmap_f16_noalloc", "bsp_noalloc_scratch_bytes"]
 
 
 class BspError(RuntimeError):
@@ -76,6 +76,9 @@ def load_library():
         L.spmm_bitmap_f16_ws.argtypes = [P, P, P, I64, I64, I64, P, I64, P, P, I64, I32, P]
         L.spmm_bitmap_f16_ws.restype = I32
         L.bsp_workspace_bytes.argtypes, L.bsp_workspace_bytes.restype = [I32, I64, I64, I64, I64, P], I32
+        L.spmm_bitmap_f16_noalloc.argtypes = [P, P, P, I64, I64, I64, P, I64, P, I32, P]
+        L.spmm_bitmap_f16_noalloc.restype = I32
+        L.bsp_noalloc_scratch_bytes.argtypes, L.bsp_noalloc_scratch_bytes.restype = [], I64
         L.bsp_describe_selection_ws.argtypes = [I32, I64, I64, I64, I64, ctypes.c_char_p, ctypes.c_size_t]
         L.bsp_describe_selection_ws.restype = I32
         L.bsp_select.argtypes, L.bsp_select.restype = [I32, I64, I64, I64, I64], I32

@@ -13,6 +13,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 
 #include "bitmap_spmm.h"
 #include "device_common.h"
@@ -247,6 +248,70 @@ int spmm_common(int dtype, const uint64_t *bitmaps, const uint32_t *offsets, con
 }
 
 }  // namespace
+
+// ---------------------------------------------------------------------------
+// Scratch of the allocation-free entry point: the workspace of the split-K
+// plans in a static device array, one copy per GPU, held until the process
+// ends. In host code `scratch` names a host-side stand-in, not device memory:
+// the device address comes from hipGetSymbolAddress, once per device, with
+// that device current, and only that address is handed to kernels.
+#define BSP_NOALLOC_SCRATCH_BYTES ((int64_t)8 << 20)
+#define BSP_NOALLOC_MAX_DEVICES 64
+static __device__ __align__(256) uint8_t scratch[BSP_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+std::mutex scratch_mu;
+void *scratch_ptr[BSP_NOALLOC_MAX_DEVICES];   // device address of `scratch` per GPU (null: not set up)
+
+__global__ void k_zero_scratch(uint32_t *p, int64_t words) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < words; i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = 0u;
+}
+
+// The current device's scratch address, set up on its first use: the address
+// of the array on that device, and the array cleared once by a fill kernel on
+// `stream` (the split-K kernels need zero arrival counters; every call leaves
+// them at zero again). No allocation happens.
+int scratch_for_current_device(hipStream_t stream, void **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= BSP_NOALLOC_MAX_DEVICES) return BSP_E_HIP;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (scratch_ptr[dev] == nullptr) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return BSP_E_HIP;
+        hipLaunchKernelGGL(k_zero_scratch, dim3(256), dim3(256), 0, stream, reinterpret_cast<uint32_t *>(ptr),
+                           BSP_NOALLOC_SCRATCH_BYTES / 4);
+        if (hipGetLastError() != hipSuccess) return BSP_E_HIP;
+        scratch_ptr[dev] = ptr;
+    }
+    *out = scratch_ptr[dev];
+    return BSP_OK;
+}
+
+}  // namespace
+
+extern "C" int spmm_bitmap_f16_noalloc(const uint64_t *bitmaps, const uint32_t *offsets, const uint16_t *payload,
+                                       int64_t payload_bytes, int64_t M, int64_t K, const uint16_t *X, int64_t N,
+                                       uint16_t *Y, int algo, hipStream_t stream) {
+    // the plan spmm_bitmap_f16_ws takes with a workspace of the scratch's size
+    Shape s;
+    int rc = check_args(bitmaps, offsets, payload, payload_bytes, M, K, X, N, Y, algo, &s);
+    if (rc != BSP_OK || M == 0 || N == 0) return rc;
+    Plan p;
+    rc = choose_plan(BSP_FP16, s, payload_bytes, algo, true, &p);
+    if (rc != BSP_OK) return rc;
+    if (p.ws_bytes() > BSP_NOALLOC_SCRATCH_BYTES) return BSP_E_CAPACITY;
+    void *ws = nullptr;
+    if (p.ws_bytes() > 0) {
+        rc = scratch_for_current_device(stream, &ws);
+        if (rc != BSP_OK) return rc;
+    }
+    return spmm_common(BSP_FP16, bitmaps, offsets, payload, payload_bytes, M, K, X, N, Y, ws,
+                       ws ? BSP_NOALLOC_SCRATCH_BYTES : 0, algo, stream);
+}
+
+extern "C" int64_t bsp_noalloc_scratch_bytes(void) { return BSP_NOALLOC_SCRATCH_BYTES; }
 
 extern "C" int bsp_select(int dtype, int64_t M, int64_t K, int64_t N, int64_t nnz) {
     if (dtype != BSP_INT4 && dtype != BSP_FP16) return -1;

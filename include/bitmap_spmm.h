@@ -206,6 +206,27 @@ int spmm_bitmap_f16_ws(const uint64_t *bitmaps, const uint32_t *offsets, const u
                        void *workspace, int64_t workspace_bytes, int algo, hipStream_t stream);
 
 /*
+ * spmm_bitmap_f16_noalloc -- for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): spmm_bitmap_f16_ws with the library's own scratch as the
+ * workspace instead of a caller's. The scratch is a static device array of
+ * bsp_noalloc_scratch_bytes() bytes (8 MiB), one per GPU, held until the
+ * process ends; its device address is looked up on a device's first call
+ * (which also clears it with a fill kernel on `stream`). No call allocates.
+ * A plan that needs more scratch returns BSP_E_CAPACITY (a 4096-row fp16
+ * problem needs at most 1 MiB; the need grows with M and N). Every call on a
+ * GPU shares that GPU's scratch: calls that overlap on one GPU (different
+ * streams without ordering) race, and must not be made. Other arguments,
+ * results and errors as spmm_bitmap_f16_ws.
+ */
+int spmm_bitmap_f16_noalloc(const uint64_t *bitmaps, const uint32_t *offsets, const uint16_t *payload,
+                            int64_t payload_bytes, int64_t M, int64_t K, const uint16_t *X, int64_t N,
+                            uint16_t *Y, int algo, hipStream_t stream);
+
+/* Size in bytes of the per-GPU scratch of spmm_bitmap_f16_noalloc. */
+int64_t bsp_noalloc_scratch_bytes(void);
+
+/*
  * bsp_select -- the kernel BSP_ALGO_AUTO picks for a problem (shape-aware
  * selection; UnionSparse Sec. I names it, without a rule). nnz may be -1 when
  * unknown. Returns a bsp_algo value, or -1 for invalid arguments. Host only.

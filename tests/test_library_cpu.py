@@ -200,6 +200,19 @@ def test_workspace_api_on_host():
     assert g(FAKE, FAKE, FAKE, 16, 16, 100, FAKE, 8, FAKE, None, 0, bsp.ALGO_SPLITK, None) == bsp.E_UNSUPPORTED
 
 
+def test_noalloc_entry_point_limits_on_host():
+    # a plan needing more than the static scratch is refused before any
+    # device call (fake pointers: a launch would fault)
+    L = bsp.load_library()
+    assert L.bsp_noalloc_scratch_bytes() == 8 << 20
+    M, K, N = 1 << 19, 8192, 32          # 16384 sets of 2 blocks (the most the counter area holds)
+    assert bsp.workspace_bytes(bsp.FP16, M, K, N) > L.bsp_noalloc_scratch_bytes()
+    f = L.spmm_bitmap_f16_noalloc
+    assert f(FAKE, FAKE, FAKE, 16 << 20, M, K, FAKE, N, FAKE, bsp.ALGO_AUTO, None) == bsp.E_CAPACITY
+    assert f(FAKE, FAKE, FAKE, 16, 4, 64, FAKE, 33, FAKE, bsp.ALGO_AUTO, None) == bsp.E_ARG
+    assert f(FAKE, FAKE, FAKE, 16, 4, 100, FAKE, 8, FAKE, bsp.ALGO_SPLITK, None) == bsp.E_UNSUPPORTED
+
+
 def test_selection_is_defined_for_every_shape():
     for dt in (bsp.INT4, bsp.FP16):
         for N in range(1, 33):

@@ -39,7 +39,8 @@ MAX_N = 32
 EXPORTS = ["encode_bitmap_tiles", "pack_int4_activations", "spmm_bitmap_w4a4", "spmm_bitmap_w4a4_algo",
            "spmm_bitmap_w4a4_ws", "spmm_bitmap_f16", "spmm_bitmap_f16_algo", "spmm_bitmap_f16_ws",
            "bsp_workspace_bytes", "bsp_select", "bsp_describe_selection", "bsp_describe_selection_ws",
-           "bsp_status_string", "bsp_version", "spmm_bitmap_f16_noalloc", "bsp_noalloc_scratch_bytes"]
+           "bsp_status_string", "bsp_version", "spmm_bitmap_f16_noalloc", "bsp_noalloc_scratch_bytes",
+           "union_tile_count", "union_mask_words", "encode_union_tiles", "spmm_union_w4a4"]
 
 
 class BspError(RuntimeError):
@@ -86,6 +87,12 @@ def load_library():
         L.bsp_describe_selection.restype = I32
         L.bsp_status_string.argtypes, L.bsp_status_string.restype = [I32], ctypes.c_char_p
         L.bsp_version.argtypes, L.bsp_version.restype = [], ctypes.c_char_p
+        L.union_tile_count.argtypes, L.union_tile_count.restype = [I64, I64], I64
+        L.union_mask_words.argtypes, L.union_mask_words.restype = [I32, I32], I32
+        L.encode_union_tiles.argtypes = [P, I64, I64, I64, I32, I32, I32, P, P, P, P, I64, P, P]
+        L.encode_union_tiles.restype = I32
+        L.spmm_union_w4a4.argtypes = [P, P, P, P, I64, I32, I32, I64, I64, P, I64, P, P]
+        L.spmm_union_w4a4.restype = I32
         _lib = L
     return _lib
 
@@ -271,6 +278,104 @@ def spmm_f16(W: DeviceMatrix, X, Y=None, algo: int = ALGO_AUTO, stream=None, wor
         _dptr(W.bitmaps), _dptr(W.offsets), _dptr(W.payload), W.payload.numel(), W.M, W.K,
         _dptr(X), N, _dptr(Y), wp, wb, algo, _stream_handle(stream))
     _check(rc, "spmm_bitmap_f16")
+    return Y
+
+
+# ---- union-mask (IE-BME) format: 16 x 64 local tiles, ra x ca areas ----
+
+UNION_MAX_K = 32768
+
+
+@dataclass
+class UnionEncoded:
+    """Host-side union-mask stream: ubitmaps uint64[nlt * words], offsets
+    uint32[nlt + 1], rowpos uint64[nlt], payload uint8[ceil(nvals / 2)]."""
+    M: int
+    K: int
+    ra: int
+    ca: int
+    nvals: int
+    ubitmaps: np.ndarray
+    offsets: np.ndarray
+    rowpos: np.ndarray
+    payload: np.ndarray
+
+    @property
+    def nlt(self) -> int:
+        return int(self.rowpos.size)
+
+    def stream_bytes(self) -> int:
+        """Bytes of the encoded stream proper: mask words, offsets, rowpos, payload."""
+        return int(self.ubitmaps.nbytes + self.offsets.nbytes + self.rowpos.nbytes + self.payload.nbytes)
+
+    def to_device(self, device="cuda") -> "UnionDevice":
+        import torch
+        pb = self.payload.nbytes
+        raw = np.zeros(max(PAYLOAD_ALIGN, pb + (-pb) % PAYLOAD_ALIGN), np.uint8)
+        raw[:pb] = self.payload
+        return UnionDevice(self.M, self.K, self.ra, self.ca, self.nvals,
+                           torch.from_numpy(self.ubitmaps.view(np.int64)).to(device),
+                           torch.from_numpy(self.offsets.view(np.int32)).to(device),
+                           torch.from_numpy(self.rowpos.view(np.int64)).to(device),
+                           torch.from_numpy(raw).to(device))
+
+
+@dataclass
+class UnionDevice:
+    """The union-mask stream in device memory; payload padded with zeros to a
+    whole number of PAYLOAD_ALIGN bytes."""
+    M: int
+    K: int
+    ra: int
+    ca: int
+    nvals: int
+    ubitmaps: "object"
+    offsets: "object"
+    rowpos: "object"
+    payload: "object"
+
+
+def union_tile_count(M: int, K: int) -> int:
+    return int(load_library().union_tile_count(M, K))
+
+
+def union_mask_words(ra: int, ca: int) -> int:
+    return int(load_library().union_mask_words(ra, ca))
+
+
+def encode_union_tiles(W: np.ndarray, ra: int = 2, ca: int = 2, reorder: bool = True) -> UnionEncoded:
+    """Union-mask encoding of an int8 (int4 values) host matrix, with
+    bitmap-aware row reordering of every local tile when ``reorder``."""
+    L = load_library()
+    if W.dtype != np.int8 or W.ndim != 2:
+        raise TypeError("W must be a 2-D int8 array of int4 values")
+    W = np.ascontiguousarray(W)
+    M, K = W.shape
+    nv, nb = ctypes.c_int64(0), ctypes.c_int64(0)
+    _check(L.encode_union_tiles(_np_ptr(W), M, K, K, ra, ca, int(reorder), None, None, None, None, 0,
+                                ctypes.byref(nv), ctypes.byref(nb)), "encode_union_tiles (size)")
+    nlt, words = union_tile_count(M, K), union_mask_words(ra, ca)
+    ub = np.zeros(nlt * words, np.uint64)
+    off = np.zeros(nlt + 1, np.uint32)
+    rp = np.zeros(nlt, np.uint64)
+    pl = np.zeros(nb.value, np.uint8)
+    _check(L.encode_union_tiles(_np_ptr(W), M, K, K, ra, ca, int(reorder), _np_ptr(ub), _np_ptr(off), _np_ptr(rp),
+                                _np_ptr(pl), pl.nbytes, ctypes.byref(nv), ctypes.byref(nb)), "encode_union_tiles")
+    return UnionEncoded(M, K, ra, ca, int(nv.value), ub, off, rp, pl)
+
+
+def spmm_union_w4a4(U: UnionDevice, X, N: int, Y=None, stream=None):
+    """Y[n][m] = sum_k W[m][k] X[k][n] (int32) with W in the union-mask
+    format. X: uint8 [N][ceil(K/2)] packed int4."""
+    import torch
+    _check_dev(X, "X", torch.uint8, N * ((U.K + 1) // 2))
+    if Y is None:
+        Y = torch.empty((N, U.M), dtype=torch.int32, device=X.device)
+    _check_dev(Y, "Y", torch.int32, N * U.M)
+    rc = load_library().spmm_union_w4a4(
+        _dptr(U.ubitmaps), _dptr(U.offsets), _dptr(U.rowpos), _dptr(U.payload), U.payload.numel(), U.ra, U.ca,
+        U.M, U.K, _dptr(X), N, _dptr(Y), _stream_handle(stream))
+    _check(rc, "spmm_union_w4a4")
     return Y
 
 

@@ -21,6 +21,7 @@
 #include "kernels_bt64.hip"
 #include "kernels_bt64_f16.hip"
 #include "kernels_splitk.hip"
+#include "kernels_union.hip"
 
 namespace {
 
@@ -389,4 +390,35 @@ extern "C" int spmm_bitmap_f16(const uint64_t *bitmaps, const uint32_t *offsets,
                                const uint16_t *X, int64_t N, uint16_t *Y, hipStream_t stream) {
     return spmm_common(BSP_FP16, bitmaps, offsets, payload, payload_bytes, M, K, X, N, Y, nullptr, 0, BSP_ALGO_AUTO,
                        stream);
+}
+
+// ---------------------------------------------------------------------------
+// Union-mask format (UnionSparse Sec. V-A, 2 x 2 areas of 16 x 64 tiles).
+extern "C" int spmm_union_w4a4(const uint64_t *ubitmaps, const uint32_t *offsets, const uint64_t *rowpos,
+                               const uint8_t *payload, int64_t payload_bytes, int ra, int ca, int64_t M,
+                               int64_t K, const uint8_t *X, int64_t N, int32_t *Y, hipStream_t stream) {
+    if (union_mask_words(ra, ca) == 0) return BSP_E_ARG;
+    if (M < 0 || K < 0 || N < 0 || N > BSP_MAX_N || payload_bytes < 0) return BSP_E_ARG;
+    if (payload_bytes % BSP_PAYLOAD_ALIGN != 0) return BSP_E_ARG;
+    if (payload_bytes > UINT32_MAX || M > INT32_MAX) return BSP_E_OVERFLOW;
+    const int64_t nlt = union_tile_count(M, K);
+    if (nlt * 32 > (int64_t)UINT32_MAX) return BSP_E_OVERFLOW;    // buffer-resource ranges are 32-bit
+    if (M == 0 || N == 0) return BSP_OK;
+    if (Y == nullptr || offsets == nullptr) return BSP_E_ARG;
+    if (K > 0 && (ubitmaps == nullptr || rowpos == nullptr || X == nullptr)) return BSP_E_ARG;
+    if (payload == nullptr && payload_bytes != 0) return BSP_E_ARG;
+    if (ra != 2 || ca != 2) return BSP_E_UNSUPPORTED;
+    if (K > BSP_UNION_MAX_K) return BSP_E_UNSUPPORTED;
+    if (K == 0) {
+        const int64_t n = M * N;
+        hipLaunchKernelGGL(k_ie_zero, dim3((unsigned)std::min<int64_t>((n + 255) / 256, 1024)), dim3(256), 0, stream,
+                           Y, n);
+        return launch_status();
+    }
+    if (((uintptr_t)X & 3u) != 0) return BSP_E_UNSUPPORTED;
+    IePlan p;
+    if (!ie_plan(M, K, N, &p)) return BSP_E_UNSUPPORTED;
+    launch_ie_w4a4(p, offsets, ubitmaps, rowpos, payload, (uint32_t)payload_bytes, (int)M, (int)K, X, (int)N, Y,
+                   stream);
+    return launch_status();
 }

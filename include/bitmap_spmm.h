@@ -242,6 +242,86 @@ int bsp_describe_selection(int dtype, int64_t M, int64_t K, int64_t N, int64_t n
  * workspace of bsp_workspace_bytes. */
 int bsp_describe_selection_ws(int dtype, int64_t M, int64_t K, int64_t N, int64_t nnz, char *buf, size_t n);
 
+/* ---------------------------------------------------------------------------
+ * Union-mask format ("IE-BME"): UnionSparse Sec. V-A, Fig. 7, with 16 x 64
+ * local tiles (LTs) and bitmap-aware row reordering (Sec. V-B, Eq. 3-5,
+ * Algorithm 1).
+ *   bands = ceil(M/16), T = ceil(K/64), nlt = bands*T LTs in row-major order
+ *   (LT t = band*T + column covers rows 16*band .. +15, columns 64*column ..
+ *   +63; past M or K the tile is padded with zeros).
+ *   An LT is cut into ra x ca areas of (16/ra) x (64/ca); area q = a*ca + c
+ *   holds tile rows a*16/ra .. and columns c*64/ca ... Logical position (i, j)
+ *   of the (16/ra) x (64/ca) union mask is set iff any area has a nonzero at
+ *   (i, j) (after the LT's row permutation).
+ *   ubitmaps[t*W .. t*W+W-1]  uint64, W = 16/(ra*ca) words: the mask scanned
+ *                row-major, position f in bit f%64 of word f/64 (leftmost
+ *                position of a row in the lowest bit, as in Fig. 7).
+ *   offsets[t]   uint32, number of values before LT t ("Union Value Offsets":
+ *                the sum of Q*P over earlier LTs, Q = ra*ca, P = set mask
+ *                bits); offsets[nlt] = nvals. nlt+1 entries.
+ *   rowpos[t]    uint64, nibble r = position of tile row r in the LT's
+ *                reordered row order (identity without reordering). The
+ *                reordered tile lists, area row by area row, row p of every
+ *                row group found by the reordering.
+ *   payload      int4 values ("Compressed Values"): for each set position of
+ *                rank rho (set positions before it, row-major), area q's value
+ *                (zero or not) is element offsets[t] + q*P + rho. Element e is
+ *                byte e>>1, low nibble when e is even. ceil(nvals/2) bytes.
+ * Row reordering, per LT: rows are grouped into 16/ra groups of ra rows so
+ * that the number of set mask positions is minimal (subset DP over row sets,
+ * each step taking a group with the smallest remaining row); among equal
+ * costs the first group in ascending lexicographic order is kept.
+ * --------------------------------------------------------------------------- */
+#define BSP_LT_ROWS 16
+#define BSP_LT_COLS 64
+
+/* Number of LTs of an M x K matrix (ceil(M/16)*ceil(K/64)); -1 for negative sizes. */
+int64_t union_tile_count(int64_t M, int64_t K);
+
+/* 64-bit mask words per LT for an ra x ca partition: 16/(ra*ca). 0 when the
+ * partition is not supported (ra, ca powers of two with ra*ca <= 16). */
+int union_mask_words(int ra, int ca);
+
+/*
+ * encode_union_tiles -- host-side encoder of the union-mask format.
+ *   W          HOST int8 [M][ldw], values in [-8, 7] (BSP_E_RANGE otherwise).
+ *   ra, ca     area partition (union_mask_words(ra, ca) > 0, else BSP_E_ARG).
+ *   reorder    nonzero: bitmap-aware row reordering of every LT; 0: identity.
+ *   ubitmaps, offsets, rowpos   HOST, caller-allocated: nlt*W, nlt+1 and nlt
+ *              entries; all three NULL for a size query.
+ *   payload    HOST, payload_capacity_bytes >= ceil(nvals/2), or NULL (size
+ *              query, or words/offsets/rowpos only).
+ *   nvals_out, payload_bytes_out  written on BSP_OK, BSP_E_CAPACITY and
+ *              BSP_E_OVERFLOW (either may be NULL).
+ * Returns BSP_E_OVERFLOW when nvals >= 2^32. Deterministic for a given input.
+ */
+int encode_union_tiles(const int8_t *W, int64_t M, int64_t K, int64_t ldw, int ra, int ca, int reorder,
+                       uint64_t *ubitmaps, uint32_t *offsets, uint64_t *rowpos,
+                       uint8_t *payload, int64_t payload_capacity_bytes,
+                       int64_t *nvals_out, int64_t *payload_bytes_out);
+
+/* K bound of the union-mask SpMM. */
+#define BSP_UNION_MAX_K 32768
+
+/*
+ * spmm_union_w4a4 -- Y = W * X with W in the union-mask format (int4 values,
+ * int32 Y), asynchronous on `stream`. All pointers are DEVICE memory.
+ *   ubitmaps, offsets, rowpos, payload   as encode_union_tiles wrote them;
+ *              payload_bytes is the payload allocation (a multiple of
+ *              BSP_PAYLOAD_ALIGN, zero past the encoded bytes).
+ *   ra, ca     the encoding's partition. The kernel runs ra = ca = 2 (the
+ *              pages' 2 x 2 areas); another valid partition returns
+ *              BSP_E_UNSUPPORTED, an invalid one BSP_E_ARG.
+ *   M, K       0 <= M < 2^31, 0 <= K <= BSP_UNION_MAX_K (larger K: BSP_E_UNSUPPORTED).
+ *   X          [N][ceil(K/2)] packed int4 as for spmm_bitmap_w4a4, on a 4-byte
+ *              boundary (BSP_E_UNSUPPORTED otherwise).
+ *   N          0..32; N == 0 or M == 0 launches nothing.
+ *   Y          [N][M] int32, fully overwritten (K == 0 gives zeros).
+ */
+int spmm_union_w4a4(const uint64_t *ubitmaps, const uint32_t *offsets, const uint64_t *rowpos,
+                    const uint8_t *payload, int64_t payload_bytes, int ra, int ca, int64_t M, int64_t K,
+                    const uint8_t *X, int64_t N, int32_t *Y, hipStream_t stream);
+
 /* Static string for a bsp_status code. */
 const char *bsp_status_string(int status);
 

@@ -513,6 +513,8 @@ def prepare(args, workload, index, n):
                                     problem.dtype, problem.W, X[:n], dict(problem.meta, N=n))
     fp16 = problem.dtype == "fp16"
     N, M, K = problem.N, problem.M, problem.K
+    if getattr(args, "format", "bt64") == "union":
+        return _prepare_union(args, bsp, problem, dev)
     enc = bsp.encode(problem.W)
     algo = {"auto": bsp.ALGO_AUTO, "rowwave": bsp.ALGO_ROWWAVE, "mfma": bsp.ALGO_MFMA, "splitk": bsp.ALGO_SPLITK}[args.algo]
     dt = bsp.FP16 if fp16 else bsp.INT4
@@ -550,6 +552,51 @@ def prepare(args, workload, index, n):
     plan = bsp.describe(dt, M, K, N, enc.nnz, workspace=ws is not None)
     return dict(problem=problem, fp16=fp16, enc=enc, dm0=dm0, copies=copies, R=R, step=step, chosen=chosen,
                 name=algo_label(kernel), kernel=kernel, dt=dt, plan=plan)
+
+
+def union_step_bytes(ue, N):
+    """Algorithmic bytes of one union-mask SpMM call: every tile's four mask
+    words, rowpos word and offset (plus the end offset), the payload, X and Y."""
+    return ue.stream_bytes() + N * ((ue.K + 1) // 2) + 4 * ue.M * N
+
+
+def _prepare_union(args, bsp, problem, dev):
+    """prepare() for the union-mask format (int4 only): 2 x 2 areas, rows of
+    every tile reordered unless --no-reorder."""
+    import numpy as np
+    import torch
+    if problem.dtype != "int4":
+        raise SystemExit("the union-mask format is int4 only")
+    N, M, K = problem.N, problem.M, problem.K
+    t0 = time.perf_counter()
+    ue = bsp.encode_union_tiles(problem.W, 2, 2, reorder=not args.no_reorder)
+    enc_s = time.perf_counter() - t0
+    du0 = ue.to_device(dev)
+    Xd = torch.from_numpy(bsp.pack_int4(problem.X)).to(dev)
+    ws = ue.stream_bytes() + Xd.numel() + 4 * M * N
+    R = args.steps + max(1, -(-FLUSH_BYTES // ws))
+    copies = [(du0, Xd, torch.empty((N, M), dtype=torch.int32, device=dev))]
+    for _ in range(R - 1):
+        du = bsp.UnionDevice(M, K, 2, 2, ue.nvals, du0.ubitmaps.clone(), du0.offsets.clone(), du0.rowpos.clone(),
+                             du0.payload.clone())
+        copies.append((du, Xd.clone(), torch.empty((N, M), dtype=torch.int32, device=dev)))
+    torch.cuda.synchronize()
+
+    def step(i):
+        du, x, y = copies[i % R]
+        bsp.spmm_union_w4a4(du, x, N, Y=y)
+
+    nnz = int(np.count_nonzero(problem.W))
+
+    class _Enc:   # what measure() reads of an encoding
+        pass
+    enc = _Enc()
+    enc.nnz = nnz
+    return dict(problem=problem, fp16=False, enc=enc, dm0=None, copies=copies, R=R, step=step, chosen=None,
+                name="union", kernel="k_ie_w4a4", dt=bsp.INT4, plan="union 2x2", nbytes=union_step_bytes(ue, N),
+                union={"nvals": ue.nvals, "reorder": not args.no_reorder, "encode_seconds": round(enc_s, 3),
+                       "stream_bytes": ue.stream_bytes(), "payload_bytes": int(ue.payload.nbytes),
+                       "value_fill": round(ue.nvals / max(1, 4 * nnz), 4)})
 
 
 def measure(args, workload, index, n, with_probe=True):
@@ -609,7 +656,8 @@ def measure(args, workload, index, n, with_probe=True):
     del graph
 
     kernel = ctx["kernel"]
-    nbytes = step_bytes(dm0, N, kernel, fp16, ctx["plan"])
+    nbytes = ctx["nbytes"] if "nbytes" in ctx else step_bytes(dm0, N, kernel, fp16, ctx["plan"])
+    union_info = ctx.get("union")
     value = nbytes / (ms_per_step * 1e-3) / 1e9
     achieved = nbytes / (kern_ms * 1e-3) / 1e9
     dense_ops = 2.0 * M * K * N
@@ -655,11 +703,17 @@ def measure(args, workload, index, n, with_probe=True):
         "roofline": roof,
         "parity_sample_ok": parity,
     }
+    if union_info is not None:
+        out["config"]["format"] = "union-mask 2x2 areas of 16x64 tiles" + (", rows reordered" if union_info["reorder"]
+                                                                          else "")
+        out["union"] = union_info
     args._problem = problem
     return out
 
 
 def algo_label(kernel):
+    if kernel.startswith("k_ie"):
+        return "union"
     return "rowwave" if kernel.startswith("k_rowwave") else "splitk" if kernel.startswith("k_bsk") else "mfma"
 
 
@@ -686,6 +740,9 @@ def main():
     ap.add_argument("--n", type=int, default=0, help="override N (slices the workload's widest X)")
     ap.add_argument("--algo", default="auto", choices=["auto", "rowwave", "mfma", "splitk"])
     ap.add_argument("--workspace", action="store_true", help="call the *_ws entry point with a workspace")
+    ap.add_argument("--format", default="bt64", choices=["bt64", "union"],
+                    help="weight format: BT64 (1x64 tiles) or the union mask (2x2 areas of 16x64 tiles)")
+    ap.add_argument("--no-reorder", action="store_true", help="union format without row reordering")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probe", action="store_true", help="leave out the read probe (roofline.achievable)")
     ap.add_argument("--sweep", action="store_true", help="one line per (workload, N) of the N sweep")

@@ -15,8 +15,9 @@
 // of up to 8 consecutive LTs of one band: their masks, rowpos words and
 // offsets come in as one dword per lane, their payload (one contiguous
 // stretch of the value array, at most 8 x 512 bytes) by LDS DMA into one of
-// the wavefront's two slots, and their X columns as 16-byte granules, all
-// issued one step ahead. Slots, tables and X are private to the wavefront, so
+// the wavefront's slots (IE_NSLOT at N <= 16, two above), and their X columns
+// as 16-byte granules, all issued as many steps ahead as there are slots
+// after the first. Slots, tables and X are private to the wavefront, so
 // no step waits at a barrier; the per-band partial sums meet in LDS at the end
 // of each band (integer adds, exact in any order).
 //
@@ -42,16 +43,48 @@
 #define IE_SLOT_KB 5                  // DMA instructions (1 KB each) per slot: 8 x 512 B + alignment
 #define IE_SLOT_BYTES (IE_SLOT_KB * 1024)
 #define IE_META_BYTES 512             // per wavefront: 64 x (mask row, rows-before count)
+#define IE_NSLOT 3                    // payload slots per wavefront: steps in flight
+#define IE_LUT_COPIES 8               // selector-table copies (lane l reads copy l % 8)
+#define IE_LUT_BYTES (2048 * IE_LUT_COPIES)
 #define IE_SUMS_BYTES (IE_MAXB * 32 * 16 * 4)
-#define IE_LDS_BYTES (IE_SUMS_BYTES + BT_LUT_BYTES + IE_WAVES * IE_META_BYTES + IE_WAVES * 2 * IE_SLOT_BYTES)
+#define IE_LDS_BYTES (IE_SUMS_BYTES + IE_LUT_BYTES + IE_WAVES * IE_META_BYTES + IE_WAVES * IE_NSLOT * IE_SLOT_BYTES)
 #define IE_MAX_K BSP_UNION_MAX_K
 #define IE_OOR 0xFFFFFFF0u            // a buffer offset past every range: reads zeros
 
-// Two dwords of a slot holding nibbles pos .. pos + 7 (pos counted from the
-// slot's start), aligned by a funnel shift.
-__device__ __forceinline__ uint32_t ie_window(uint32_t slot_addr, uint32_t pos) {
-    const bt_lds_u32 *q = (const bt_lds_u32 *)(uintptr_t)(slot_addr + ((pos >> 1) & ~3u));
-    return __builtin_amdgcn_alignbit(q[1], q[0], (pos & 7u) << 2);
+// Eight payload-window reads (two dwords each, at LDS byte addresses a0[i]
+// and a1[i], i < 4), completed before the block ends: the outputs are
+// written when the block's own wait returns, never later.
+__device__ __forceinline__ void ie_read_windows(const uint32_t *a0, const uint32_t *a1, uint64_t *d0,
+                                                uint64_t *d1) {
+    asm volatile(
+            "ds_read2_b32 %0, %8 offset1:1\n\t"
+            "ds_read2_b32 %1, %9 offset1:1\n\t"
+            "ds_read2_b32 %2, %10 offset1:1\n\t"
+            "ds_read2_b32 %3, %11 offset1:1\n\t"
+            "ds_read2_b32 %4, %12 offset1:1\n\t"
+            "ds_read2_b32 %5, %13 offset1:1\n\t"
+            "ds_read2_b32 %6, %14 offset1:1\n\t"
+            "ds_read2_b32 %7, %15 offset1:1\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(d0[0]), "=&v"(d1[0]), "=&v"(d0[1]), "=&v"(d1[1]), "=&v"(d0[2]), "=&v"(d1[2]), "=&v"(d0[3]),
+              "=&v"(d1[3])
+            : "v"(a0[0]), "v"(a1[0]), "v"(a0[1]), "v"(a1[1]), "v"(a0[2]), "v"(a1[2]), "v"(a0[3]), "v"(a1[3])
+            : "memory");
+}
+
+// Four LDS integer adds at byte address a (a, a + 4, a + 8, a + 12). Issued
+// as LDS instructions the compiler would first wait for every LDS DMA in
+// flight; they have no outputs, and the kernel waits for them (lgkmcnt)
+// before its final barrier.
+__device__ __forceinline__ void ie_add4(uint32_t a, bt_v4i v) {
+    asm volatile(
+            "ds_add_u32 %0, %1\n\t"
+            "ds_add_u32 %0, %2 offset:4\n\t"
+            "ds_add_u32 %0, %3 offset:8\n\t"
+            "ds_add_u32 %0, %4 offset:12"
+            :
+            : "v"(a), "v"(v.x), "v"(v.y), "v"(v.z), "v"(v.w)
+            : "memory");
 }
 
 // A operand dwords of one window: {even ranks, odd ranks} placed by the
@@ -95,9 +128,9 @@ __global__ __launch_bounds__(IE_WAVES * 64) void k_ie_w4a4(
 
     int32_t *sums = reinterpret_cast<int32_t *>(ie_smem);   // [IE_MAXB][32 columns][16 rows]
     uint8_t *lut8 = ie_smem + IE_SUMS_BYTES;
-    uint8_t *meta8 = lut8 + BT_LUT_BYTES + wave * IE_META_BYTES;
-    uint8_t *slot8 = lut8 + BT_LUT_BYTES + IE_WAVES * IE_META_BYTES + wave * 2 * IE_SLOT_BYTES;
-    const uint32_t lut_base = bt_lds_addr(lut8) + (uint32_t)(lane % BT_LUT_COPIES) * 8u;
+    uint8_t *meta8 = lut8 + IE_LUT_BYTES + wave * IE_META_BYTES;
+    uint8_t *slot8 = lut8 + IE_LUT_BYTES + IE_WAVES * IE_META_BYTES + wave * IE_NSLOT * IE_SLOT_BYTES;
+    const uint32_t lut_base = bt_lds_addr(lut8) + (uint32_t)(lane % IE_LUT_COPIES) * 8u;
     const uint32_t meta_addr = bt_lds_addr(meta8);
     const uint32_t slot_addr0 = bt_lds_addr(slot8);
 
@@ -123,14 +156,18 @@ __global__ __launch_bounds__(IE_WAVES * 64) void k_ie_w4a4(
     uint32_t issued = 1;
 
     for (int o = threadIdx.x; o < IE_MAXB * 32 * 16; o += blockDim.x) sums[o] = 0;
-    for (int e = threadIdx.x; e < 256 * BT_LUT_COPIES; e += blockDim.x) {
-        const uint2 v = bt_lut_entry((uint32_t)e / BT_LUT_COPIES);
+    for (int e = threadIdx.x; e < 256 * IE_LUT_COPIES; e += blockDim.x) {
+        const uint2 v = bt_lut_entry((uint32_t)e / IE_LUT_COPIES);
         *reinterpret_cast<uint2 *>(lut8 + (size_t)e * 8) = v;
     }
     __syncthreads();
 
-    uint32_t maskv[2], rpv[2], offv[2], g0s[2], mark[2] = {0, 0};
-    bt_v4i xg[2][NCH][4];
+    // slots in use: all IE_NSLOT at N <= 16; two at N > 16, whose X granules
+    // take twice the registers
+    constexpr int NS = NCH == 1 ? IE_NSLOT : 2;
+    uint32_t maskv[NS], rpv[NS], offv[NS], g0s[NS], mark[NS] = {};
+    bt_v4i xg[NS][NCH][4];
+    uint32_t xe[NS][NCH][4];
 
     // Issue the loads of step s into slot k. A step past the last one issues
     // the same instructions with every offset out of range (they read zeros
@@ -138,7 +175,7 @@ __global__ __launch_bounds__(IE_WAVES * 64) void k_ie_w4a4(
     // below is exact.
     auto issue = [&](int s, int k) {
         const bool live = s < S;
-        const int bi = live ? s / nck : 0, ci = live ? s - bi * nck : 0;
+        const int ci = live ? s / nb : 0, bi = live ? s - ci * nb : 0;
         const int band = b0 + bi;
         const int cc0 = c0 + IE_CHUNK * ci;
         const int n_lt = live ? min(IE_CHUNK, c1 - cc0) : 0;
@@ -162,7 +199,12 @@ __global__ __launch_bounds__(IE_WAVES * 64) void k_ie_w4a4(
                 const bool ok = live && n < N && col < c1;
                 const uint32_t off = ok ? (uint32_t)n * xs + (uint32_t)(cc0 + 2 * j) * 32u + 16u * (uint32_t)kg
                                         : IE_OOR;
-                xg[k][nch][j] = bt_load_x16<XU>(xrs, off);
+                // K % 8 != 0: rows are not dword aligned; the 20 bytes from the
+                // dword boundary below are loaded now and shifted into place
+                // when used, so nothing waits for them here
+                const uint32_t a = XU ? (off & ~3u) : off;
+                xg[k][nch][j] = __builtin_bit_cast(bt_v4i, __builtin_amdgcn_raw_buffer_load_b128(xrs, a, 0, 0));
+                if constexpr (XU) xe[k][nch][j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(xrs, a + 16u, 0, 0);
             }
         }
         // payload of the chunk: granules [G0, G1), at most IE_SLOT_KB x 64 of them
@@ -179,20 +221,15 @@ __global__ __launch_bounds__(IE_WAVES * 64) void k_ie_w4a4(
         mark[k] = issued;
     };
 
-    bt_v4i acc[NCH], accb[IE_MAXB][NCH];
-#pragma unroll
-    for (int nch = 0; nch < NCH; ++nch) {
-        acc[nch] = bt_v4i{0, 0, 0, 0};
-#pragma unroll
-        for (int b = 0; b < IE_MAXB; ++b) accb[b][nch] = bt_v4i{0, 0, 0, 0};
-    }
+    bt_v4i xb[IE_CHUNK][NCH];              // B operands of the current chunk
 
     auto process = [&](int s, int k) {
-        const int bi = s / nck, ci = s - bi * nck;
+        const int ci = s / nb, bi = s - ci * nb;
         const int cc0 = c0 + IE_CHUNK * ci;
         const int n_lt = min(IE_CHUNK, c1 - cc0);
         bt_wait_vm(issued - mark[k]);
-        // per mask row: (row bits, set bits in the LT's earlier rows)
+        // per mask row: (row bits, set bits in the LT's earlier rows); the
+        // prefix runs over each LT's 8 rows (8 lanes)
         const uint32_t mv = maskv[k];
         const uint32_t cnt = (uint32_t)__builtin_popcount(mv);
         uint32_t incl = cnt;
@@ -203,84 +240,112 @@ __global__ __launch_bounds__(IE_WAVES * 64) void k_ie_w4a4(
         }
         *(__attribute__((address_space(3))) uint64_t *)(uintptr_t)(meta_addr + 8u * (uint32_t)lane) =
                 ((uint64_t)(incl - cnt) << 32) | mv;
-        // B operands of the chunk's LTs
-        bt_v4i xb[IE_CHUNK][NCH];
-#pragma unroll
-        for (int nch = 0; nch < NCH; ++nch)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const bt_v4i v = ie_transpose(xg[k][nch][j]);
-                xb[2 * j][nch] = bt_b_operand((uint32_t)v.x, (uint32_t)v.y);
-                xb[2 * j + 1][nch] = bt_b_operand((uint32_t)v.z, (uint32_t)v.w);
-            }
         const uint32_t slot_addr = slot_addr0 + (uint32_t)k * IE_SLOT_BYTES;
         const uint32_t org = g0s[k] << 5;                 // nibble index of the slot's first byte
         const uint32_t below = kg == 0 ? 0u : ((1u << (8 * kg)) - 1u);
+        // The step's LTs go through three phases, each over all IE_CHUNK of
+        // them with no branch, so each phase's LDS reads are in flight
+        // together: (1) the lane's mask row, (2) its selector pair and two
+        // payload windows, (3) decode and MFMA. An LT past the chunk's end has
+        // an empty mask (its mask dwords read as zeros): its selectors give
+        // zeros and its windows are read at the slot's start.
+        uint2 rb[IE_CHUNK];
+        uint32_t aP2[IE_CHUNK], Pl[IE_CHUNK], base[IE_CHUNK];
 #pragma unroll
         for (int lt = 0; lt < IE_CHUNK; ++lt) {
-            if (lt >= n_lt) break;
-            const uint32_t ot = (uint32_t)__builtin_amdgcn_readlane((int)offv[k], lt);
-            const uint32_t ot1 = (uint32_t)__builtin_amdgcn_readlane((int)offv[k], lt + 1);
-            const uint32_t P = (ot1 - ot) >> 2;
+            const bool in = lt < n_lt;
+            const uint32_t ot_l = (uint32_t)__builtin_amdgcn_readlane((int)offv[k], lt);
+            const uint32_t ot1_l = (uint32_t)__builtin_amdgcn_readlane((int)offv[k], lt + 1);
+            const uint32_t ot = in ? ot_l : org, ot1 = in ? ot1_l : org;
+            Pl[lt] = (ot1 - ot) >> 2;
+            base[lt] = ot - org;
             const uint32_t rlo = (uint32_t)__builtin_amdgcn_readlane((int)rpv[k], 2 * lt);
             const uint32_t rhi = (uint32_t)__builtin_amdgcn_readlane((int)rpv[k], 2 * lt + 1);
-            const uint32_t p = ((R < 8 ? rlo : rhi) >> (4 * (R & 7))) & 15u;
-            const uint32_t a = p >> 3, gi = p & 7u;
-            const uint2 rb = bt_lds_pair(meta_addr + 8u * (8u * (uint32_t)lt + gi));
-            const uint32_t byte = __builtin_amdgcn_ubfe(rb.x, 8u * (uint32_t)kg, 8u);
-            const uint32_t rank = (uint32_t)__builtin_popcount(rb.x & below) + rb.y;
-            const uint2 sel = bt_lds_pair(lut_base + byte * (8u * BT_LUT_COPIES));
-            const uint32_t pos0 = (ot - org) + 2u * a * P + rank;
-            const uint32_t w0 = ie_window(slot_addr, pos0);
-            const uint32_t w1 = ie_window(slot_addr, pos0 + P);
+            const uint32_t p = (uint32_t)((((uint64_t)rhi << 32) | rlo) >> (4 * R)) & 15u;
+            aP2[lt] = (p >> 3) ? 2u * Pl[lt] : 0u;       // stream 2a starts 2 a P values in
+            rb[lt] = bt_lds_pair(meta_addr + 8u * (8u * (uint32_t)lt + (p & 7u)));
+        }
+        uint2 sel[IE_CHUNK];
+        uint64_t d0[IE_CHUNK], d1[IE_CHUNK];
+        uint32_t sh0[IE_CHUNK], sh1[IE_CHUNK], wa0[IE_CHUNK], wa1[IE_CHUNK];
+#pragma unroll
+        for (int lt = 0; lt < IE_CHUNK; ++lt) {
+            const uint32_t byte = __builtin_amdgcn_ubfe(rb[lt].x, 8u * (uint32_t)kg, 8u);
+            const uint32_t rank = (uint32_t)__builtin_popcount(rb[lt].x & below) + rb[lt].y;
+            sel[lt] = bt_lds_pair(lut_base + byte * (8u * IE_LUT_COPIES));
+            const uint32_t pos0 = base[lt] + aP2[lt] + rank;
+            const uint32_t pos1 = pos0 + Pl[lt];
+            wa0[lt] = slot_addr + ((pos0 >> 3) << 2);
+            wa1[lt] = slot_addr + ((pos1 >> 3) << 2);
+            // the funnel shift reads the low 5 bits of its amount: 4 (pos & 7)
+            sh0[lt] = pos0 << 2;
+            sh1[lt] = pos1 << 2;
+        }
+        // The window reads of the slot. Written out as LDS instructions the
+        // compiler would precede them with a wait for every LDS DMA still in
+        // flight (the later steps' too): it cannot tell the slots apart. The
+        // step's own DMAs are complete (the counted wait above), so the reads
+        // are issued here, four LTs per block, and each block waits for its
+        // own reads before it ends.
+        ie_read_windows(&wa0[0], &wa1[0], &d0[0], &d1[0]);
+        ie_read_windows(&wa0[4], &wa1[4], &d0[4], &d1[4]);
+        // A chunk's first step (band 0) builds the B operands of its LTs from
+        // the X granules that came with it; the chunk's other bands reuse them
+        if (bi == 0) {
+#pragma unroll
+            for (int j = 0; j < IE_CHUNK / 2; ++j)
+#pragma unroll
+                for (int nch = 0; nch < NCH; ++nch) {
+                    bt_v4i g = xg[k][nch][j];
+                    if constexpr (XU) {
+                        const uint32_t sh = ((uint32_t)(R + 16 * nch) * xs) & 3u;
+                        const uint32_t e = xe[k][nch][j];
+                        g = bt_v4i{(int)__builtin_amdgcn_alignbyte((uint32_t)g.y, (uint32_t)g.x, sh),
+                                   (int)__builtin_amdgcn_alignbyte((uint32_t)g.z, (uint32_t)g.y, sh),
+                                   (int)__builtin_amdgcn_alignbyte((uint32_t)g.w, (uint32_t)g.z, sh),
+                                   (int)__builtin_amdgcn_alignbyte(e, (uint32_t)g.w, sh)};
+                    }
+                    const bt_v4i t = ie_transpose(g);
+                    xb[2 * j][nch] = bt_b_operand((uint32_t)t.x, (uint32_t)t.y);
+                    xb[2 * j + 1][nch] = bt_b_operand((uint32_t)t.z, (uint32_t)t.w);
+                }
+        }
+        bt_v4i acc[NCH];
+#pragma unroll
+        for (int lt = 0; lt < IE_CHUNK; ++lt) {
             uint32_t A0, A1, A2, A3;
-            ie_place(w0, sel, A0, A1);
-            ie_place(w1, sel, A2, A3);
+            ie_place(__builtin_amdgcn_alignbit((uint32_t)(d0[lt] >> 32), (uint32_t)d0[lt], sh0[lt]), sel[lt], A0, A1);
+            ie_place(__builtin_amdgcn_alignbit((uint32_t)(d1[lt] >> 32), (uint32_t)d1[lt], sh1[lt]), sel[lt], A2, A3);
             const bt_v4i av = {(int)A0, (int)A1, (int)A2, (int)A3};
 #pragma unroll
             for (int nch = 0; nch < NCH; ++nch)
-                acc[nch] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, xb[lt][nch], acc[nch], 0, 0, 0);
+                acc[nch] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, xb[lt][nch], lt == 0 ? bt_v4i{0, 0, 0, 0} : acc[nch],
+                                                                 0, 0, 0);
         }
+        // the step's partial (exact after >> 8) joins its band's sums in LDS
+#pragma unroll
+        for (int nch = 0; nch < NCH; ++nch)
+            ie_add4(bt_lds_addr(sums + (bi * 32 + R + 16 * nch) * 16 + 4 * kg), acc[nch] >> 8);
         // the slot and the tables are rewritten by the next issue into them
         __builtin_amdgcn_s_waitcnt(0xC07F);
         asm volatile("" ::: "memory");
-        if (ci == nck - 1) {
-            // a band is done: its partial moves to the band's registers (a
-            // select per register keeps the array statically indexed); the
-            // LDS adds wait for the end, where no DMA is left in flight
-#pragma unroll
-            for (int b = 0; b < IE_MAXB; ++b)
-#pragma unroll
-                for (int nch = 0; nch < NCH; ++nch)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) accb[b][nch][i] = b == bi ? acc[nch][i] : accb[b][nch][i];
-#pragma unroll
-            for (int nch = 0; nch < NCH; ++nch) acc[nch] = bt_v4i{0, 0, 0, 0};
-        }
     };
 
     if (S > 0) {
         bt_wait_vm(0);                                   // chunk boundaries
-        issue(0, 0);
-        issue(1, 1);
-        for (int s = 0; s < S; s += 2) {
-            process(s, 0);
-            issue(s + 2, 0);
-            if (s + 1 < S) process(s + 1, 1);
-            issue(s + 3, 1);
-        }
-        bt_wait_vm(0);
 #pragma unroll
-        for (int b = 0; b < IE_MAXB; ++b) {
-            if (b >= nb) break;
+        for (int k = 0; k < NS; ++k) issue(k, k);
+        for (int s = 0; s < S; s += NS) {
 #pragma unroll
-            for (int nch = 0; nch < NCH; ++nch) {
-                int32_t *sp = sums + (b * 32 + R + 16 * nch) * 16 + 4 * kg;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) atomicAdd(&sp[i], accb[b][nch][i] >> 8);
+            for (int k = 0; k < NS; ++k) {
+                if (k == 0 || s + k < S) process(s + k, k);
+                issue(s + k + NS, k);
             }
         }
+        bt_wait_vm(0);
     }
+    // the LDS adds above were issued outside the compiler's view: wait for them
+    __builtin_amdgcn_s_waitcnt(0xC07F);
     __syncthreads();
     for (int o = threadIdx.x; o < nb * 16 * N; o += blockDim.x) {
         const int bi = o / (16 * N), r2 = o - bi * 16 * N;

@@ -269,3 +269,28 @@ def fp16_error(y: np.ndarray, r: np.ndarray) -> dict:
     return dict(max_rel_floored=float(np.max(floored)), max_rel_unfloored=float(np.max(unf)),
                 normwise=float(np.max(d) / rn) if rn > 0 else float(np.max(d)),
                 nonfinite=int(np.count_nonzero(~np.isfinite(y))))
+
+
+def dequant_f16(Y: np.ndarray, scale_w: np.ndarray, scale_x: np.ndarray) -> np.ndarray:
+    """The Dequant step after the int4 SpMM (UnionSparse, Fig. 2: the int32
+    result goes back to fp16), with one fp32 scale per output channel (row m
+    of W) and one per token (column n of X), as the fused epilogue computes it:
+
+        Yh[n][m] = fp16( fp32( fp32(Y[n][m]) * scale_w[m] ) * scale_x[n] )
+
+    each operation rounded to nearest even, in this order. numpy's float32
+    arithmetic is IEEE binary32 with that rounding, and its float32 -> float16
+    conversion rounds to nearest even; overflow gives +-inf. Returns the fp16
+    array [N][M]."""
+    Y = np.asarray(Y)
+    sw = np.asarray(scale_w, np.float32)
+    sx = np.asarray(scale_x, np.float32)
+    N, M = Y.shape
+    assert sw.shape == (M,) and sx.shape == (N,)
+    out = np.empty((N, M), np.float16)
+    with np.errstate(over="ignore"):
+        for n in range(N):
+            a = Y[n].astype(np.float32) * sw          # fp32(y) * scale_w, rounded in fp32
+            b = a * sx[n]                             # ... * scale_x, rounded in fp32
+            out[n] = b.astype(np.float16)             # one rounding to fp16
+    return out

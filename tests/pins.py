@@ -305,4 +305,63 @@ def pin_fp16_error():
     assert math.isclose(e["max_rel_floored"], 0.1, rel_tol=1e-12), e
 
 
+# ---- dequant epilogue (int32 -> fp16 with per-channel and per-token scales) ----
+
+def _ulp16(x):
+    """Spacing of binary16 numbers at magnitude x (subnormal spacing 2^-24 below 2^-14)."""
+    x = abs(float(x))
+    if x < 2.0 ** -14:
+        return 2.0 ** -24
+    return 2.0 ** (np.floor(np.log2(x)) - 10)
+
+
+def pin_dequant_closed_form():
+    """Against the exact product y * scale_w * scale_x (fp64 holds it to 2^-53):
+    three roundings to fp32 (int -> fp32 and two products) and one to fp16
+    leave at most half an fp16 ulp plus 3 fp32 units in the last place."""
+    rng = np.random.default_rng(31)
+    N, M = 7, 300
+    Y = rng.integers(-(1 << 26), 1 << 26, size=(N, M)).astype(np.int32)
+    Y[:, :50] = rng.integers(-3000, 3000, size=(N, 50))
+    sw = np.exp(rng.uniform(np.log(1e-6), np.log(1e-2), size=M)).astype(np.float32)
+    sx = np.exp(rng.uniform(np.log(1e-3), np.log(1.0), size=N)).astype(np.float32)
+    out = oracle.dequant_f16(Y, sw, sx).astype(np.float64)
+    exact = Y.astype(np.float64) * sw.astype(np.float64)[None, :] * sx.astype(np.float64)[:, None]
+    checked = 0
+    for n in range(N):
+        for m in range(M):
+            e = exact[n, m]
+            if abs(e) > 65504.0:
+                assert np.isinf(out[n, m]) or abs(out[n, m]) == 65504.0
+                continue
+            tol = 0.5 * _ulp16(e) * (1 + 2.0 ** -10) + 3 * 2.0 ** -24 * abs(e)
+            assert abs(out[n, m] - e) <= tol, (n, m, out[n, m], e)
+            checked += 1
+    assert checked > N * M // 2
+
+
+# Hand-derived binary16 results (IEEE 754 round to nearest, ties to even):
+# (y, scale_w, scale_x, expected bits)
+DEQUANT_CASES = [
+    (1, 1.0, 1 + 2.0 ** -11, 0x3C00),        # halfway between 1 and 1 + 2^-10: even mantissa, 1.0
+    (1, 1.0, 1 + 3 * 2.0 ** -11, 0x3C02),    # halfway between 1 + 2^-10 and 1 + 2^-9: to 1 + 2^-9
+    (3, 1.0, 2.0 ** -26, 0x0001),            # 0.75 x 2^-24 rounds to the smallest subnormal
+    (1, 2.0 ** -25, 1.0, 0x0000),            # exactly half the smallest subnormal: ties to +0
+    (65504, 1.0, 1.0, 0x7BFF),               # largest finite fp16
+    (65519, 1.0, 1.0, 0x7BFF),               # below the halfway point to 2^16
+    (65520, 1.0, 1.0, 0x7C00),               # halfway: ties to even, 2^16, overflows to +inf
+    (-2, 0.5, -1.0, 0x3C00),                 # signs: (-2 * 0.5) * -1 = +1
+    (0, -1.0, 1.0, 0x8000),                  # 0 * -1 = -0.0
+    (7, -0.25, 2.0, 0xC300),                 # -3.5 = -1.75 x 2^1: sign 1, exponent 16, fraction 0b11 << 8
+    (1 << 30, 2.0 ** 100, 2.0 ** -120, 0x7C00),   # 2^130 overflows fp32 before the token scale: +inf
+]
+
+
+def pin_dequant_rounding_cases():
+    for (y, sw, sx, bits) in DEQUANT_CASES:
+        got = oracle.dequant_f16(np.array([[y]], np.int32), np.array([sw], np.float32),
+                                 np.array([sx], np.float32)).view(np.uint16)[0, 0]
+        assert int(got) == bits, (y, sw, sx, hex(int(got)), hex(bits))
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

@@ -99,3 +99,38 @@ def test_pins_catch_fp16_metric_mutant(name, old, new):
             pins.pin_fp16_error()
     finally:
         oracle.fp16_error = real
+
+
+# Planted mistakes in the dequant epilogue's oracle (a Python function).
+DEQUANT_MUTANTS = [
+    ("scales_applied_in_other_order", [("a = Y[n].astype(np.float32) * sw ", "a = Y[n].astype(np.float32) * sx[n] "),
+                                       ("b = a * sx[n] ", "b = a * sw ")]),
+    ("token_scale_dropped", [("b = a * sx[n] ", "b = a * 1 ")]),
+    ("channel_scale_reversed", [("a = Y[n].astype(np.float32) * sw ", "a = Y[n].astype(np.float32) * sw[::-1] ")]),
+    ("truncated_to_fp16", [("out[n] = b.astype(np.float16)", "out[n] = np.trunc(b * 1024) / 1024")]),
+    ("saturates_instead_of_inf", [("out[n] = b.astype(np.float16)", "out[n] = np.clip(b, -65504, 65504).astype(np.float16)")]),
+]
+
+
+@pytest.mark.parametrize("name,edits", DEQUANT_MUTANTS, ids=[m[0] for m in DEQUANT_MUTANTS])
+def test_pins_catch_dequant_mutant(name, edits):
+    import inspect
+    import textwrap
+    src = textwrap.dedent(inspect.getsource(oracle.dequant_f16))
+    for old, new in edits:
+        assert old in src, f"mutation anchor not found: {old!r}"
+        src = src.replace(old, new)
+    ns = dict(oracle.__dict__)
+    exec(compile(src, "<mutant>", "exec"), ns)
+    real = oracle.dequant_f16
+    oracle.dequant_f16 = ns["dequant_f16"]
+    caught = []
+    try:
+        for pin in (pins.pin_dequant_closed_form, pins.pin_dequant_rounding_cases):
+            try:
+                pin()
+            except (AssertionError, ValueError, IndexError):
+                caught.append(pin.__name__)
+    finally:
+        oracle.dequant_f16 = real
+    assert caught, f"no pin catches mutant {name}"

@@ -40,7 +40,8 @@ EXPORTS = ["encode_bitmap_tiles", "pack_int4_activations", "spmm_bitmap_w4a4", "
            "spmm_bitmap_w4a4_ws", "spmm_bitmap_f16", "spmm_bitmap_f16_algo", "spmm_bitmap_f16_ws",
            "bsp_workspace_bytes", "bsp_select", "bsp_describe_selection", "bsp_describe_selection_ws",
            "bsp_status_string", "bsp_version", "spmm_bitmap_f16_noalloc", "bsp_noalloc_scratch_bytes",
-           "union_tile_count", "union_mask_words", "encode_union_tiles", "spmm_union_w4a4"]
+           "union_tile_count", "union_mask_words", "encode_union_tiles", "spmm_union_w4a4",
+           "spmm_bitmap_w4a4_dq", "spmm_bitmap_w4a4_grouped"]
 
 
 class BspError(RuntimeError):
@@ -93,6 +94,10 @@ def load_library():
         L.encode_union_tiles.restype = I32
         L.spmm_union_w4a4.argtypes = [P, P, P, P, I64, I32, I32, I64, I64, P, I64, P, P]
         L.spmm_union_w4a4.restype = I32
+        L.spmm_bitmap_w4a4_dq.argtypes = [P, P, P, I64, I64, I64, P, I64, P, P, P, P]
+        L.spmm_bitmap_w4a4_dq.restype = I32
+        L.spmm_bitmap_w4a4_grouped.argtypes = [P, I32, I64, P]
+        L.spmm_bitmap_w4a4_grouped.restype = I32
         _lib = L
     return _lib
 
@@ -279,6 +284,78 @@ def spmm_f16(W: DeviceMatrix, X, Y=None, algo: int = ALGO_AUTO, stream=None, wor
         _dptr(X), N, _dptr(Y), wp, wb, algo, _stream_handle(stream))
     _check(rc, "spmm_bitmap_f16")
     return Y
+
+
+# ---- dequant epilogue and grouped launch ----
+
+GROUP_MAX = 8
+
+
+class W4A4Item(ctypes.Structure):
+    """bsp_w4a4_item of include/bitmap_spmm.h."""
+    _fields_ = [("bitmaps", ctypes.c_void_p), ("offsets", ctypes.c_void_p), ("payload", ctypes.c_void_p),
+                ("payload_bytes", ctypes.c_int64), ("M", ctypes.c_int64), ("X", ctypes.c_void_p),
+                ("N", ctypes.c_int64), ("Y", ctypes.c_void_p), ("Yh", ctypes.c_void_p),
+                ("scale_w", ctypes.c_void_p), ("scale_x", ctypes.c_void_p)]
+
+
+def spmm_bitmap_w4a4_dq(W: DeviceMatrix, X, N: int, scale_w, scale_x, Yh=None, stream=None):
+    """fp16 Yh [N][M] = fp16(fp32(fp32(W X) * scale_w[m]) * scale_x[n]), the
+    dequant step fused into the int4 SpMM. scale_w: float32 [M], scale_x:
+    float32 [N] (device)."""
+    import torch
+    if W.dtype != INT4:
+        raise TypeError("spmm_bitmap_w4a4_dq needs an int4 DeviceMatrix")
+    _check_dev(X, "X", torch.uint8, N * ((W.K + 1) // 2))
+    _check_dev(scale_w, "scale_w", torch.float32, W.M)
+    _check_dev(scale_x, "scale_x", torch.float32, N)
+    if Yh is None:
+        Yh = torch.empty((N, W.M), dtype=torch.float16, device=X.device)
+    _check_dev(Yh, "Yh", torch.float16, N * W.M)
+    rc = load_library().spmm_bitmap_w4a4_dq(
+        _dptr(W.bitmaps), _dptr(W.offsets), _dptr(W.payload), W.payload.numel(), W.M, W.K, _dptr(X), N,
+        _dptr(scale_w), _dptr(scale_x), _dptr(Yh), _stream_handle(stream))
+    _check(rc, "spmm_bitmap_w4a4_dq")
+    return Yh
+
+
+def spmm_bitmap_w4a4_grouped(items, stream=None):
+    """One launch for several int4 matrices of one K. items: a list of dicts
+    with W (DeviceMatrix), X (uint8 [N][ceil(K/2)]), N, and either Y (int32
+    [N][M]) or Yh (fp16 [N][M]) with scale_w (float32 [M]) and scale_x
+    (float32 [N]). Returns the list of outputs."""
+    import torch
+    if not items:
+        raise ValueError("no items")
+    K = items[0]["W"].K
+    arr = (W4A4Item * len(items))()
+    outs = []
+    for i, it in enumerate(items):
+        W, X, N = it["W"], it["X"], int(it["N"])
+        if W.K != K or W.dtype != INT4:
+            raise ValueError("grouped items must be int4 matrices of one K")
+        _check_dev(X, "X", torch.uint8, N * ((K + 1) // 2))
+        Y, Yh = it.get("Y"), it.get("Yh")
+        sw, sx = it.get("scale_w"), it.get("scale_x")
+        if sw is not None:
+            _check_dev(sw, "scale_w", torch.float32, W.M)
+            _check_dev(sx, "scale_x", torch.float32, N)
+            if Yh is None:
+                Yh = torch.empty((N, W.M), dtype=torch.float16, device=X.device)
+            _check_dev(Yh, "Yh", torch.float16, N * W.M)
+            outs.append(Yh)
+        else:
+            if Y is None:
+                Y = torch.empty((N, W.M), dtype=torch.int32, device=X.device)
+            _check_dev(Y, "Y", torch.int32, N * W.M)
+            outs.append(Y)
+        arr[i] = W4A4Item(_dptr(W.bitmaps), _dptr(W.offsets), _dptr(W.payload), W.payload.numel(), W.M, _dptr(X), N,
+                          _dptr(Y) if sw is None else None, _dptr(Yh) if sw is not None else None, _dptr(sw),
+                          _dptr(sx))
+    rc = load_library().spmm_bitmap_w4a4_grouped(ctypes.cast(arr, ctypes.c_void_p), len(items), K,
+                                                 _stream_handle(stream))
+    _check(rc, "spmm_bitmap_w4a4_grouped")
+    return outs
 
 
 # ---- union-mask (IE-BME) format: 16 x 64 local tiles, ra x ca areas ----

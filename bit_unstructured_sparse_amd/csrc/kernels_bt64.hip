@@ -138,6 +138,62 @@ __device__ __forceinline__ uint32_t bt_x_range(int N, uint32_t xs) {
     return ((uint32_t)N * xs + 3u) & ~3u;
 }
 
+// Output stage of the int4 MFMA kernels. Y receives the int32 sums; with
+// the dequant epilogue (Yh set) Yh receives instead, for output row m and
+// column n, fp16(fp32(fp32(y) * sw[m]) * sx[n]): the int32 sum converted to
+// fp32, times the output channel's scale, times the token's scale, each
+// product rounded to nearest even in fp32, then one round to nearest even to
+// fp16 (the Dequant step that follows the SpMM in UnionSparse, Fig. 2, fused
+// into the kernel's final write).
+struct BtEpi {
+    uint16_t *Yh;
+    const float *sw;
+    const float *sx;
+};
+
+__device__ __forceinline__ uint16_t bt_dequant(int32_t v, float sw, float sx) {
+    const float a = (float)v * sw;
+    float b = a * sx;
+    // b is rounded to fp32 and only then converted: left to itself the
+    // compiler turns the second product and the conversion into one
+    // mixed-precision multiply that rounds once, from the exact product
+    asm volatile("" : "+v"(b));
+    return bsp_f2h(b);
+}
+
+__device__ __forceinline__ void bt_store_y1(int32_t *Y, const BtEpi &e, int M, int n, int m, int32_t v) {
+    const int64_t at = (int64_t)n * M + m;
+    if (e.Yh != nullptr)
+        e.Yh[at] = bt_dequant(v, e.sw[m], e.sx[n]);
+    else
+        Y[at] = v;
+}
+
+// Rows m .. m+3 of column n (those below M).
+__device__ __forceinline__ void bt_store_y4(int32_t *Y, const BtEpi &e, int M, int n, int m, bt_v4i v) {
+    const int64_t at = (int64_t)n * M + m;
+    const bool whole = m + 4 <= M && (M & 3) == 0;
+    if (e.Yh != nullptr) {
+        const float sx = e.sx[n];
+        if (whole && ((uintptr_t)e.Yh & 7u) == 0 && ((uintptr_t)e.sw & 15u) == 0) {
+            const float4 w = *reinterpret_cast<const float4 *>(e.sw + m);
+            const uint32_t lo = (uint32_t)bt_dequant(v.x, w.x, sx) | ((uint32_t)bt_dequant(v.y, w.y, sx) << 16);
+            const uint32_t hi = (uint32_t)bt_dequant(v.z, w.z, sx) | ((uint32_t)bt_dequant(v.w, w.w, sx) << 16);
+            *reinterpret_cast<uint2 *>(e.Yh + at) = uint2{lo, hi};
+        } else {
+            const int32_t a[4] = {v.x, v.y, v.z, v.w};
+            for (int k = 0; k < 4 && m + k < M; ++k) e.Yh[at + k] = bt_dequant(a[k], e.sw[m + k], sx);
+        }
+        return;
+    }
+    if (whole && ((uintptr_t)Y & 15u) == 0) {
+        *reinterpret_cast<bt_v4i *>(Y + at) = v;
+    } else {
+        const int32_t a[4] = {v.x, v.y, v.z, v.w};
+        for (int k = 0; k < 4 && m + k < M; ++k) Y[at + k] = a[k];
+    }
+}
+
 // 16 bytes of X at byte offset off. X rows start on a 4-byte boundary when
 // K % 8 == 0 (XU false): one 16-byte load. Otherwise (XU true) the dwords
 // around the bytes are loaded from the 4-byte boundary below off and the
@@ -337,7 +393,9 @@ template <int NB, int TPL, bool XU>
 __global__ __launch_bounds__(BT_WG_THREADS(TPL)) void k_bt64_w4a4(
         const uint32_t *__restrict__ offsets, int M, int K, int bq, int br, const uint64_t *__restrict__ bitmaps,
         const uint8_t *__restrict__ X, int N, const uint8_t *__restrict__ payload, uint32_t payload_bytes,
-        int32_t *__restrict__ Y, uint32_t stage_bytes, uint32_t nbuf, int one_pass) {
+        int32_t *__restrict__ Y, uint32_t stage_bytes, uint32_t nbuf, int one_pass, uint16_t *Yh, const float *sw,
+        const float *sx) {
+    const BtEpi epi{Yh, sw, sx};
     constexpr int NBLK = BT_NBLK(TPL);
     constexpr int WC = BT_WG_THREADS(TPL) / 64;          // row-total columns: wavefronts, at most
     extern __shared__ __attribute__((aligned(16))) uint8_t bt_smem[];
@@ -524,7 +582,7 @@ __global__ __launch_bounds__(BT_WG_THREADS(TPL)) void k_bt64_w4a4(
             const int nb = o >> 8, col = (o >> 4) & 15, rl = o & 15;
             const int ln = (rl >> 2) * 16 + col, k = rl & 3;
             const int n = col + 16 * nb;
-            if (n < N && rl < rows) Y[(int64_t)n * M + m0 + rl] = s[(nb * 4 + k) * 64 + ln];
+            if (n < N && rl < rows) bt_store_y1(Y, epi, M, n, m0 + rl, s[(nb * 4 + k) * 64 + ln]);
         }
     };
     // decode + contract block i into acc (after its barrier)
@@ -603,12 +661,7 @@ __global__ __launch_bounds__(BT_WG_THREADS(TPL)) void k_bt64_w4a4(
             bt_v4i v = {0, 0, 0, 0};
             for (int w = 0; w < nwaves; ++w)
                 v += *(bt_lds_v4i *)(uintptr_t)bt_lds_addr(part + ((i * nwaves + w) * NB + nb) * 256 + ln * 4);
-            int32_t *y = Y + (int64_t)n * M + m;
-            if (((uintptr_t)Y & 15u) == 0 && (M & 3) == 0 && m + 4 <= M) {
-                *reinterpret_cast<bt_v4i *>(y) = v;   // 16-byte aligned: Y, M and m are
-            } else {
-                for (int k = 0; k < 4 && m + k < M; ++k) y[k] = v[k];
-            }
+            bt_store_y4(Y, epi, M, n, m, v);
         }
         return;
     }
@@ -669,18 +722,20 @@ __device__ __forceinline__ void bt_make_b(const uint32_t (&xw)[NB][TPL][8], bt_v
             }
 }
 
+// The work of one workgroup; gid is its index among the workgroups of its
+// matrix (the plain kernel's block index, or its place in a grouped launch).
 template <int NB, int D, bool XU>
-__global__ __launch_bounds__(512) void k_bt64s_w4a4(
-        const uint32_t *__restrict__ offsets, int M, int K, int bq, int br, const uint64_t *__restrict__ bitmaps,
-        const uint8_t *__restrict__ X, int N, const uint8_t *__restrict__ payload, uint32_t payload_bytes,
-        int32_t *__restrict__ Y, uint32_t stagger, uint32_t area_kb) {
+__device__ __forceinline__ void bts_body(
+        int gid, const uint32_t *__restrict__ offsets, int M, int K, int bq, int br,
+        const uint64_t *__restrict__ bitmaps, const uint8_t *__restrict__ X, int N,
+        const uint8_t *__restrict__ payload, uint32_t payload_bytes, int32_t *__restrict__ Y, uint32_t stagger,
+        uint32_t area_kb, const BtEpi epi) {
     constexpr int TPL = 2, NBLK = BTS_NBLK, WC = 8;
     extern __shared__ __attribute__((aligned(16))) uint8_t bt_smem[];
     const int nwaves = blockDim.x >> 6;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int r = lane & 15, q = lane >> 4;
     const int T = (K + 63) >> 6;
-    const int gid = (int)blockIdx.x;
     const int b_begin = gid * bq + min(gid, br);
     const int nblk = bq + (gid < br ? 1 : 0);           // 1 .. NBLK
     const int t0 = (wave * 4 + q) * TPL;
@@ -873,7 +928,6 @@ __global__ __launch_bounds__(512) void k_bt64s_w4a4(
     bt_barrier_lds();
     // Y: item (block i, column block nb, lane l) sums the wavefronts' partials
     // of lane l: rows 4 (l / 16) .. +3 of column l % 16 (the MFMA D layout)
-    const bool vec = ((uintptr_t)Y & 15) == 0 && (M & 3) == 0;
     for (int o = threadIdx.x; o < nblk * NB * 64; o += blockDim.x) {
         const int i = o / (NB * 64), nb = (o / 64) % NB, ln = o % 64;
         const int n = (ln & 15) + 16 * nb;
@@ -882,14 +936,50 @@ __global__ __launch_bounds__(512) void k_bt64s_w4a4(
         bt_v4i s = bt_v4i{0, 0, 0, 0};
         for (int w = 0; w < nwaves; ++w)
             s += *(bt_lds_v4i *)(uintptr_t)bt_lds_addr(part + ((i * nwaves + w) * NB + nb) * 256 + ln * 4);
-        int32_t *yp = Y + (int64_t)n * M + m;
-        if (vec && m + 4 <= M) {
-            *(bt_v4i *)yp = s;
-        } else {
-            const int32_t v[4] = {s.x, s.y, s.z, s.w};
-            for (int k = 0; k < 4 && m + k < M; ++k) yp[k] = v[k];
-        }
+        bt_store_y4(Y, epi, M, n, m, s);
     }
+}
+
+template <int NB, int D, bool XU>
+__global__ __launch_bounds__(512) void k_bt64s_w4a4(
+        const uint32_t *__restrict__ offsets, int M, int K, int bq, int br, const uint64_t *__restrict__ bitmaps,
+        const uint8_t *__restrict__ X, int N, const uint8_t *__restrict__ payload, uint32_t payload_bytes,
+        int32_t *__restrict__ Y, uint32_t stagger, uint32_t area_kb, uint16_t *Yh, const float *sw, const float *sx) {
+    bts_body<NB, D, XU>((int)blockIdx.x, offsets, M, K, bq, br, bitmaps, X, N, payload, payload_bytes, Y, stagger,
+                        area_kb, BtEpi{Yh, sw, sx});
+}
+
+// Grouped launch: up to BTS_GROUP_MAX matrices with one K, each with its own
+// stream, X, output and epilogue, in one dispatch; item i owns the
+// workgroups [wg_begin, next item's wg_begin).
+#define BTS_GROUP_MAX 8
+struct BtsItem {
+    const uint32_t *offsets;
+    const uint64_t *bitmaps;
+    const uint8_t *X;
+    const uint8_t *payload;
+    int32_t *Y;
+    uint16_t *Yh;
+    const float *sw;
+    const float *sx;
+    int M, N, bq, br, wg_begin;
+    uint32_t payload_bytes, stagger, area_kb;
+};
+struct BtsGroup {
+    int count, K;
+    BtsItem item[BTS_GROUP_MAX];
+};
+
+template <int NB, int D, bool XU>
+__global__ __launch_bounds__(512) void k_bt64s_group(const BtsGroup g) {
+    const int wg = (int)blockIdx.x;
+    // the item of this workgroup (uniform; every field read at a fixed offset)
+    BtsItem it = g.item[0];
+#pragma unroll
+    for (int j = 1; j < BTS_GROUP_MAX; ++j)
+        if (j < g.count && wg >= g.item[j].wg_begin) it = g.item[j];
+    bts_body<NB, D, XU>(wg - it.wg_begin, it.offsets, it.M, g.K, it.bq, it.br, it.bitmaps, it.X, it.N, it.payload,
+                        it.payload_bytes, it.Y, it.stagger, it.area_kb, BtEpi{it.Yh, it.sw, it.sx});
 }
 
 // LDS of the streaming variant: the selector table, the row totals, for each
@@ -991,17 +1081,18 @@ static bool bt64_plan(int64_t M, int64_t K, int64_t N, int64_t payload_bytes, Bt
 template <int NB, int TPL, bool XU>
 static void launch_bt64_t(const BtPlan &p, const uint64_t *bitmaps, const uint32_t *offsets,
                           const uint8_t *payload, uint32_t payload_bytes, int M, int K, const uint8_t *X, int N,
-                          int32_t *Y, hipStream_t stream) {
+                          int32_t *Y, const BtEpi &e, hipStream_t stream) {
     (void)hipFuncSetAttribute((const void *)k_bt64_w4a4<NB, TPL, XU>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               (int)p.lds);
     hipLaunchKernelGGL((k_bt64_w4a4<NB, TPL, XU>), dim3(p.grid), dim3(64 * p.nwaves), p.lds, stream, offsets, M, K, p.bq,
-                       p.br, bitmaps, X, N, payload, payload_bytes, Y, p.stage_bytes, p.nbuf, p.one_pass);
+                       p.br, bitmaps, X, N, payload, payload_bytes, Y, p.stage_bytes, p.nbuf, p.one_pass, e.Yh, e.sw,
+                       e.sx);
 }
 
 template <bool XU>
 static void launch_bt64_w4a4_x(const BtPlan &p, const uint64_t *bitmaps, const uint32_t *offsets,
                                const uint8_t *payload, uint32_t payload_bytes, int M, int K, const uint8_t *X, int N,
-                               int32_t *Y, hipStream_t stream) {
+                               int32_t *Y, const BtEpi &e, hipStream_t stream) {
     if (p.streaming) {
 #define BTS_LAUNCH(NB, D)                                                                                             \
     do {                                                                                                              \
@@ -1009,7 +1100,7 @@ static void launch_bt64_w4a4_x(const BtPlan &p, const uint64_t *bitmaps, const u
                                   (int)p.lds);                                                                        \
         hipLaunchKernelGGL((k_bt64s_w4a4<NB, D, XU>), dim3(p.grid), dim3(64 * p.nwaves), p.lds, stream, offsets, M, K, \
                            p.bq, p.br, bitmaps, X, N, payload, payload_bytes, Y, (uint32_t)p.stagger,                 \
-                           (uint32_t)p.area_kb);                                                                      \
+                           (uint32_t)p.area_kb, e.Yh, e.sw, e.sx);                                                    \
     } while (0)
         if (p.nb == 1) {
             if (p.streaming == 2) BTS_LAUNCH(1, 2); else if (p.streaming == 3) BTS_LAUNCH(1, 3); else BTS_LAUNCH(1, 4);
@@ -1019,7 +1110,7 @@ static void launch_bt64_w4a4_x(const BtPlan &p, const uint64_t *bitmaps, const u
 #undef BTS_LAUNCH
         return;
     }
-#define BT_LAUNCH(NB, TPL) launch_bt64_t<NB, TPL, XU>(p, bitmaps, offsets, payload, payload_bytes, M, K, X, N, Y, stream)
+#define BT_LAUNCH(NB, TPL) launch_bt64_t<NB, TPL, XU>(p, bitmaps, offsets, payload, payload_bytes, M, K, X, N, Y, e, stream)
     if (p.nb == 1) {
         if (p.tpl == 2) BT_LAUNCH(1, 2); else if (p.tpl == 4) BT_LAUNCH(1, 4); else BT_LAUNCH(1, 8);
     } else {
@@ -1031,9 +1122,28 @@ static void launch_bt64_w4a4_x(const BtPlan &p, const uint64_t *bitmaps, const u
 // X rows of ceil(K/2) bytes sit on a 4-byte boundary when K % 8 == 0
 static void launch_bt64_w4a4(const BtPlan &p, const uint64_t *bitmaps, const uint32_t *offsets,
                              const uint8_t *payload, uint32_t payload_bytes, int M, int K, const uint8_t *X, int N,
-                             int32_t *Y, hipStream_t stream) {
+                             int32_t *Y, hipStream_t stream, const BtEpi &e = BtEpi{nullptr, nullptr, nullptr}) {
     if (K % 8 == 0)
-        launch_bt64_w4a4_x<false>(p, bitmaps, offsets, payload, payload_bytes, M, K, X, N, Y, stream);
+        launch_bt64_w4a4_x<false>(p, bitmaps, offsets, payload, payload_bytes, M, K, X, N, Y, e, stream);
     else
-        launch_bt64_w4a4_x<true>(p, bitmaps, offsets, payload, payload_bytes, M, K, X, N, Y, stream);
+        launch_bt64_w4a4_x<true>(p, bitmaps, offsets, payload, payload_bytes, M, K, X, N, Y, e, stream);
+}
+
+// Grouped launch of the streaming kernel (items prepared by the caller:
+// plans with one nwaves, NB the widest item's, D the largest).
+template <bool XU>
+static void launch_bts_group_x(const BtsGroup &g, int nb, int d, unsigned grid, int nwaves, size_t lds,
+                               hipStream_t stream) {
+#define BTG_LAUNCH(NB, D)                                                                                             \
+    do {                                                                                                              \
+        (void)hipFuncSetAttribute((const void *)k_bt64s_group<NB, D, XU>, hipFuncAttributeMaxDynamicSharedMemorySize, \
+                                  (int)lds);                                                                          \
+        hipLaunchKernelGGL((k_bt64s_group<NB, D, XU>), dim3(grid), dim3(64 * nwaves), lds, stream, g);                \
+    } while (0)
+    if (nb == 1) {
+        if (d == 2) BTG_LAUNCH(1, 2); else if (d == 3) BTG_LAUNCH(1, 3); else BTG_LAUNCH(1, 4);
+    } else {
+        if (d == 2) BTG_LAUNCH(2, 2); else if (d == 3) BTG_LAUNCH(2, 3); else BTG_LAUNCH(2, 4);
+    }
+#undef BTG_LAUNCH
 }

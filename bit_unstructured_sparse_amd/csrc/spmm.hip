@@ -422,3 +422,121 @@ extern "C" int spmm_union_w4a4(const uint64_t *ubitmaps, const uint32_t *offsets
                    stream);
     return launch_status();
 }
+
+// ---------------------------------------------------------------------------
+// Dequant epilogue and grouped launch (int4 MFMA kernels).
+
+__global__ void k_dq_zero(uint16_t *__restrict__ Yh, const float *__restrict__ sw, const float *__restrict__ sx,
+                          int64_t M, int64_t N) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < M * N; i += (int64_t)gridDim.x * blockDim.x)
+        Yh[i] = bt_dequant(0, sw[i % M], sx[i / M]);
+}
+
+extern "C" int spmm_bitmap_w4a4_dq(const uint64_t *bitmaps, const uint32_t *offsets, const uint8_t *payload,
+                                   int64_t payload_bytes, int64_t M, int64_t K, const uint8_t *X, int64_t N,
+                                   const float *scale_w, const float *scale_x, uint16_t *Yh, hipStream_t stream) {
+    Shape s;
+    int rc = check_args(bitmaps, offsets, payload, payload_bytes, M, K, X, N, Yh, BSP_ALGO_AUTO, &s);
+    if (rc != BSP_OK || M == 0 || N == 0) return rc;
+    if (scale_w == nullptr || scale_x == nullptr) return BSP_E_ARG;
+    if (K == 0) {
+        const int64_t n = M * N;
+        hipLaunchKernelGGL(k_dq_zero, dim3((unsigned)std::min<int64_t>((n + 255) / 256, 1024)), dim3(256), 0, stream,
+                           Yh, scale_w, scale_x, M, N);
+        return launch_status();
+    }
+    Plan p;
+    rc = choose_plan(BSP_INT4, s, payload_bytes, BSP_ALGO_MFMA, false, &p);
+    if (rc != BSP_OK || p.kind != PK_BT64) return BSP_E_UNSUPPORTED;
+    if (((uintptr_t)X & 3u) != 0) return BSP_E_UNSUPPORTED;
+    launch_bt64_w4a4(p.bt, bitmaps, offsets, payload, (uint32_t)payload_bytes, (int)M, (int)K, X, (int)N, nullptr,
+                     stream, BtEpi{Yh, scale_w, scale_x});
+    return launch_status();
+}
+
+namespace {
+
+// The streaming plan of one item of a grouped launch with `grid` workgroups.
+bool bts_item_plan(int64_t M, int64_t K, int64_t N, int64_t pbytes, int64_t grid, BtPlan *p) {
+    if (!bt64_plan(M, K, N, pbytes, p) || !p->streaming) return false;
+    const int64_t blocks = (M + BT_ROWS - 1) / BT_ROWS;
+    grid = std::max<int64_t>(grid, (blocks + BTS_NBLK - 1) / BTS_NBLK);
+    grid = std::min<int64_t>(grid, blocks);
+    p->grid = (unsigned)grid;
+    p->bq = (int)(blocks / grid);
+    p->br = (int)(blocks % grid);
+    return true;
+}
+
+}  // namespace
+
+extern "C" int spmm_bitmap_w4a4_grouped(const bsp_w4a4_item *items, int count, int64_t K, hipStream_t stream) {
+    if (items == nullptr || count < 1 || count > BSP_GROUP_MAX) return BSP_E_ARG;
+    if (K < 0) return BSP_E_ARG;
+    int64_t total_blocks = 0;
+    for (int i = 0; i < count; ++i) {
+        const bsp_w4a4_item &it = items[i];
+        Shape s;
+        const void *y = it.Yh != nullptr ? (const void *)it.Yh : (const void *)it.Y;
+        int rc = check_args(it.bitmaps, it.offsets, it.payload, it.payload_bytes, it.M, K, it.X, it.N, y,
+                            BSP_ALGO_AUTO, &s);
+        if (rc != BSP_OK) return rc;
+        if (it.M == 0 || it.N == 0) continue;
+        if ((it.Y != nullptr) == (it.Yh != nullptr)) return BSP_E_ARG;   // exactly one output
+        if (it.Yh != nullptr && (it.scale_w == nullptr || it.scale_x == nullptr)) return BSP_E_ARG;
+        if (((uintptr_t)it.X & 3u) != 0) return BSP_E_UNSUPPORTED;
+        total_blocks += (it.M + BT_ROWS - 1) / BT_ROWS;
+    }
+    if (total_blocks == 0) return BSP_OK;
+    if (K == 0) return BSP_E_UNSUPPORTED;
+    BtsGroup g{};
+    g.K = (int)K;
+    int nb = 1, d = 2, nwaves = 0;
+    size_t lds = 0;
+    int64_t wg = 0;
+    BtPlan plans[BSP_GROUP_MAX];
+    int idx[BSP_GROUP_MAX], n_items = 0;
+    for (int i = 0; i < count; ++i) {
+        const bsp_w4a4_item &it = items[i];
+        if (it.M == 0 || it.N == 0) continue;
+        const int64_t blocks = (it.M + BT_ROWS - 1) / BT_ROWS;
+        // the CUs are shared out in proportion to the items' row blocks
+        const int64_t share = std::max<int64_t>(1, (BT_CUS * blocks + total_blocks - 1) / total_blocks);
+        if (!bts_item_plan(it.M, K, it.N, it.payload_bytes, share, &plans[n_items])) return BSP_E_UNSUPPORTED;
+        nb = std::max(nb, plans[n_items].nb);
+        d = std::max(d, plans[n_items].streaming);
+        nwaves = plans[n_items].nwaves;
+        idx[n_items++] = i;
+    }
+    for (int j = 0; j < n_items; ++j) {
+        const BtPlan &p = plans[j];
+        const bsp_w4a4_item &it = items[idx[j]];
+        const int64_t per_wg = p.bq + (p.br > 0 ? 1 : 0);
+        lds = std::max(lds, bts_lds(nwaves, nb, p.area_kb, per_wg));
+        BtsItem &b = g.item[j];
+        b.offsets = it.offsets;
+        b.bitmaps = it.bitmaps;
+        b.X = it.X;
+        b.payload = it.payload;
+        b.Y = it.Y;
+        b.Yh = it.Yh;
+        b.sw = it.scale_w;
+        b.sx = it.scale_x;
+        b.M = (int)it.M;
+        b.N = (int)it.N;
+        b.bq = p.bq;
+        b.br = p.br;
+        b.wg_begin = (int)wg;
+        b.payload_bytes = (uint32_t)it.payload_bytes;
+        b.stagger = (uint32_t)p.stagger;
+        b.area_kb = (uint32_t)p.area_kb;
+        wg += p.grid;
+    }
+    if (lds > (size_t)BT_LDS_MAX || wg > INT32_MAX) return BSP_E_UNSUPPORTED;
+    g.count = n_items;
+    if (K % 8 == 0)
+        launch_bts_group_x<false>(g, nb, d, (unsigned)wg, nwaves, lds, stream);
+    else
+        launch_bts_group_x<true>(g, nb, d, (unsigned)wg, nwaves, lds, stream);
+    return launch_status();
+}

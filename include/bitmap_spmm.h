@@ -243,6 +243,66 @@ int bsp_describe_selection(int dtype, int64_t M, int64_t K, int64_t N, int64_t n
 int bsp_describe_selection_ws(int dtype, int64_t M, int64_t K, int64_t N, int64_t nnz, char *buf, size_t n);
 
 /* ---------------------------------------------------------------------------
+ * Dequant epilogue and grouped launch (the Quant -> SpMM -> Dequant pipeline
+ * of UnionSparse Fig. 2, with the Dequant step fused into the SpMM's final
+ * write, and several matrices in one launch).
+ * With the epilogue, output element (n, m) is
+ *     Yh[n*M + m] = fp16( fp32( fp32(y) * scale_w[m] ) * scale_x[n] )
+ * y being the int32 sum of spmm_bitmap_w4a4: the sum converted to fp32
+ * (round to nearest even), multiplied by the output channel's scale, then by
+ * the token's scale, each product rounded to nearest even in fp32, and one
+ * round to nearest even to fp16 (overflow gives +-inf). Scales are fp32, in
+ * the normal range (no subnormal products).
+ * --------------------------------------------------------------------------- */
+
+/*
+ * spmm_bitmap_w4a4_dq -- spmm_bitmap_w4a4 with the dequant epilogue.
+ *   scale_w    DEVICE float[M], one scale per output row (channel).
+ *   scale_x    DEVICE float[N], one scale per activation column (token).
+ *   Yh         DEVICE uint16 [N][M] (fp16 bits), fully overwritten.
+ * Runs the int4 MFMA kernels (K <= 16384, X on a 4-byte boundary); other
+ * shapes return BSP_E_UNSUPPORTED. K == 0 gives fp16(0 * scale_w * scale_x)
+ * (signed zeros). Other arguments as spmm_bitmap_w4a4.
+ */
+int spmm_bitmap_w4a4_dq(const uint64_t *bitmaps, const uint32_t *offsets, const uint8_t *payload,
+                        int64_t payload_bytes, int64_t M, int64_t K, const uint8_t *X, int64_t N,
+                        const float *scale_w, const float *scale_x, uint16_t *Yh, hipStream_t stream);
+
+/* Most matrices in one grouped launch. */
+#define BSP_GROUP_MAX 8
+
+/* One matrix of a grouped launch: its BT64 stream, its X, and exactly one of
+ * Y (int32 [N][M]) or Yh (fp16 [N][M] through the dequant epilogue, with
+ * scale_w[M] and scale_x[N]). All pointers DEVICE; M, N, payload_bytes as for
+ * spmm_bitmap_w4a4. An item with M == 0 or N == 0 is skipped. */
+typedef struct bsp_w4a4_item {
+    const uint64_t *bitmaps;
+    const uint32_t *offsets;
+    const uint8_t *payload;
+    int64_t payload_bytes;
+    int64_t M;
+    const uint8_t *X;
+    int64_t N;
+    int32_t *Y;
+    uint16_t *Yh;
+    const float *scale_w;
+    const float *scale_x;
+} bsp_w4a4_item;
+
+/*
+ * spmm_bitmap_w4a4_grouped -- Y_i = W_i * X_i for `count` (1..BSP_GROUP_MAX)
+ * matrices sharing one K (e.g. the Q, K and V projections of a layer, or an
+ * FFN's gate and up projections) in ONE kernel launch on `stream`; the
+ * workgroups are shared out over the items in proportion to their rows.
+ *   items      HOST array of `count` descriptors (read during the call only).
+ * Results equal spmm_bitmap_w4a4 / spmm_bitmap_w4a4_dq per item, bit for bit.
+ * The items must all run the streaming int4 kernel (1 <= K <= 4096, X on a
+ * 4-byte boundary), else BSP_E_UNSUPPORTED and nothing is launched. Errors
+ * in any item are reported before anything is launched.
+ */
+int spmm_bitmap_w4a4_grouped(const bsp_w4a4_item *items, int count, int64_t K, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * Union-mask format ("IE-BME"): UnionSparse Sec. V-A, Fig. 7, with 16 x 64
  * local tiles (LTs) and bitmap-aware row reordering (Sec. V-B, Eq. 3-5,
  * Algorithm 1).

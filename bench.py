@@ -515,6 +515,8 @@ def prepare(args, workload, index, n):
     N, M, K = problem.N, problem.M, problem.K
     if getattr(args, "format", "bt64") == "union":
         return _prepare_union(args, bsp, problem, dev)
+    if getattr(args, "parts", 0) or getattr(args, "epilogue", "int32") == "dq":
+        return _prepare_parts(args, bsp, problem, dev)
     enc = bsp.encode(problem.W)
     algo = {"auto": bsp.ALGO_AUTO, "rowwave": bsp.ALGO_ROWWAVE, "mfma": bsp.ALGO_MFMA, "splitk": bsp.ALGO_SPLITK}[args.algo]
     dt = bsp.FP16 if fp16 else bsp.INT4
@@ -599,6 +601,86 @@ def _prepare_union(args, bsp, problem, dev):
                        "value_fill": round(ue.nvals / max(1, 4 * nnz), 4)})
 
 
+def _prepare_parts(args, bsp, problem, dev):
+    """prepare() for the grouped launch and the dequant epilogue (int4): W's
+    rows cut into --parts matrices sharing X, run as one grouped launch (or,
+    with --separate, one call each); --epilogue dq writes fp16 through the
+    dequant epilogue with seeded per-channel and per-token scales."""
+    import numpy as np
+    import torch
+    if problem.dtype != "int4":
+        raise SystemExit("the grouped launch and the dequant epilogue are int4 only")
+    N, M, K = problem.N, problem.M, problem.K
+    P = max(1, args.parts)
+    dq = args.epilogue == "dq"
+    separate = args.separate or not args.parts   # the epilogue alone: one plain call
+    cuts = [M * j // P for j in range(P + 1)]
+    encs = [bsp.encode(np.ascontiguousarray(problem.W[cuts[j]:cuts[j + 1]])) for j in range(P)]
+    rng = np.random.default_rng(0)
+    sx = torch.from_numpy(np.exp(rng.uniform(np.log(1e-2), np.log(2.0), N)).astype(np.float32)).to(dev)
+    sws = [torch.from_numpy(np.exp(rng.uniform(np.log(1e-4), np.log(5e-2), e.M)).astype(np.float32)).to(dev)
+           for e in encs]
+    Xd = torch.from_numpy(bsp.pack_int4(problem.X)).to(dev)
+    dms0 = [e.to_device(dev) for e in encs]
+    esize = 2 if dq else 4
+    per_copy = sum(d.stream_bytes() for d in dms0) + Xd.numel() + esize * M * N
+    R = args.steps + max(1, -(-FLUSH_BYTES // per_copy))
+    ydt = torch.float16 if dq else torch.int32
+
+    def fresh(dms, x):
+        return (dms, x, [torch.empty((N, e.M), dtype=ydt, device=dev) for e in encs])
+    copies = [fresh(dms0, Xd)]
+    for _ in range(R - 1):
+        copies.append(fresh([bsp.DeviceMatrix(e.dtype, e.M, K, e.nnz, d.bitmaps.clone(), d.offsets.clone(),
+                                              d.payload.clone()) for e, d in zip(encs, dms0)], Xd.clone()))
+    torch.cuda.synchronize()
+
+    def step(i):
+        dms, x, ys = copies[i % R]
+        if separate:
+            for j in range(P):
+                if dq:
+                    bsp.spmm_bitmap_w4a4_dq(dms[j], x, N, sws[j], sx, Yh=ys[j])
+                else:
+                    bsp.spmm_w4a4(dms[j], x, N, Y=ys[j])
+        else:
+            items = []
+            for j in range(P):
+                it = dict(W=dms[j], X=x, N=N)
+                if dq:
+                    it.update(scale_w=sws[j], scale_x=sx, Yh=ys[j])
+                else:
+                    it["Y"] = ys[j]
+                items.append(it)
+            bsp.spmm_bitmap_w4a4_grouped(items)
+
+    nnz = sum(e.nnz for e in encs)
+    # algorithmic bytes: every part's words, block offsets and payload, X once
+    # per part (each reads it), Y (fp16 with the epilogue, plus the scales)
+    nbytes = 0
+    for e, d in zip(encs, dms0):
+        nbytes += d.stream_bytes(with_offsets=False) + 4 * ((e.M + 15) // 16 + 1) + N * ((K + 1) // 2)
+        nbytes += esize * e.M * N + (4 * e.M + 4 * N if dq else 0)
+
+    class _Enc:
+        pass
+    enc = _Enc()
+    enc.nnz = nnz
+    separate = args.separate or not args.parts
+    kernel = kernel_symbol(bsp, bsp.ALGO_AUTO, bsp.INT4, encs[0].M, K, N, encs[0].nnz) if separate else "k_bt64s_group"
+
+    def gather(i):
+        # Y of copy i as one [N][M] array (int32), or the fp16 values
+        return torch.cat([ys.float() if dq else ys for ys in copies[i][2]], dim=1)
+    return dict(problem=problem, fp16=False, enc=enc, dm0=None, copies=copies, R=R, step=step, chosen=None,
+                name="separate" if separate else "grouped", kernel=kernel, dt=bsp.INT4,
+                plan=f"parts={P} {'separate calls' if separate else 'one grouped launch'}"
+                     f"{' dequant epilogue' if dq else ''}",
+                nbytes=nbytes, gather=gather, dq=(sws, sx) if dq else None,
+                parts={"parts": P, "separate": separate, "epilogue": args.epilogue,
+                       "launches_per_step": P if separate else 1})
+
+
 def measure(args, workload, index, n, with_probe=True):
     """Time one workload (n > 0 slices its widest X to N = n); returns the
     bench record without the CPU baseline."""
@@ -617,6 +699,15 @@ def measure(args, workload, index, n, with_probe=True):
     rows = np.random.default_rng(0).choice(M, size=min(M, 256), replace=False)
 
     def spot_ok(i):
+        if "gather" in ctx:
+            got = ctx["gather"](i).cpu().numpy()[:, rows]
+            ref = (problem.W[rows].astype(np.int64) @ problem.X.astype(np.int64).T).T
+            if ctx.get("dq") is not None:
+                sws, sx = ctx["dq"]
+                sw = torch.cat(sws).cpu().numpy()[rows]
+                want = ((ref.astype(np.float32) * sw[None, :]) * sx.cpu().numpy()[:, None]).astype(np.float16)
+                return bool(np.array_equal(got.astype(np.float16).view(np.uint16), want.view(np.uint16)))
+            return bool(np.array_equal(got, ref))
         got = copies[i][2].cpu().numpy()[:, rows]
         if fp16:
             ref = (problem.W[rows].astype(np.float64) @ problem.X.astype(np.float64).T).T
@@ -658,6 +749,7 @@ def measure(args, workload, index, n, with_probe=True):
     kernel = ctx["kernel"]
     nbytes = ctx["nbytes"] if "nbytes" in ctx else step_bytes(dm0, N, kernel, fp16, ctx["plan"])
     union_info = ctx.get("union")
+    ctx_parts = ctx.get("parts")
     value = nbytes / (ms_per_step * 1e-3) / 1e9
     achieved = nbytes / (kern_ms * 1e-3) / 1e9
     dense_ops = 2.0 * M * K * N
@@ -703,6 +795,8 @@ def measure(args, workload, index, n, with_probe=True):
         "roofline": roof,
         "parity_sample_ok": parity,
     }
+    if ctx_parts is not None:
+        out["config"]["grouping"] = ctx_parts
     if union_info is not None:
         out["config"]["format"] = "union-mask 2x2 areas of 16x64 tiles" + (", rows reordered" if union_info["reorder"]
                                                                           else "")
@@ -743,6 +837,10 @@ def main():
     ap.add_argument("--format", default="bt64", choices=["bt64", "union"],
                     help="weight format: BT64 (1x64 tiles) or the union mask (2x2 areas of 16x64 tiles)")
     ap.add_argument("--no-reorder", action="store_true", help="union format without row reordering")
+    ap.add_argument("--parts", type=int, default=0, help="cut W's rows into this many matrices: one grouped launch")
+    ap.add_argument("--separate", action="store_true", help="with --parts: one call per part instead")
+    ap.add_argument("--epilogue", default="int32", choices=["int32", "dq"],
+                    help="dq: fp16 output through the fused dequant epilogue")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probe", action="store_true", help="leave out the read probe (roofline.achievable)")
     ap.add_argument("--sweep", action="store_true", help="one line per (workload, N) of the N sweep")

@@ -724,13 +724,13 @@ __device__ __forceinline__ void bt_make_b(const uint32_t (&xw)[NB][TPL][8], bt_v
 
 // The work of one workgroup; gid is its index among the workgroups of its
 // matrix (the plain kernel's block index, or its place in a grouped launch).
-template <int NB, int D, bool XU>
+template <int NB, int D, bool XU, int NBLK = BTS_NBLK>
 __device__ __forceinline__ void bts_body(
         int gid, const uint32_t *__restrict__ offsets, int M, int K, int bq, int br,
         const uint64_t *__restrict__ bitmaps, const uint8_t *__restrict__ X, int N,
         const uint8_t *__restrict__ payload, uint32_t payload_bytes, int32_t *__restrict__ Y, uint32_t stagger,
         uint32_t area_kb, const BtEpi epi) {
-    constexpr int TPL = 2, NBLK = BTS_NBLK, WC = 8;
+    constexpr int TPL = 2, WC = 8;
     extern __shared__ __attribute__((aligned(16))) uint8_t bt_smem[];
     const int nwaves = blockDim.x >> 6;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -951,8 +951,11 @@ __global__ __launch_bounds__(512) void k_bt64s_w4a4(
 
 // Grouped launch: up to BTS_GROUP_MAX matrices with one K, each with its own
 // stream, X, output and epilogue, in one dispatch; item i owns the
-// workgroups [wg_begin, next item's wg_begin).
+// workgroups [wg_begin, next item's wg_begin). A workgroup takes up to
+// BTS_GROUP_NBLK blocks, one more than the plain kernel: items whose blocks
+// do not divide evenly into the CUs then fit in one round of workgroups.
 #define BTS_GROUP_MAX 8
+#define BTS_GROUP_NBLK 4
 struct BtsItem {
     const uint32_t *offsets;
     const uint64_t *bitmaps;
@@ -978,15 +981,16 @@ __global__ __launch_bounds__(512) void k_bt64s_group(const BtsGroup g) {
 #pragma unroll
     for (int j = 1; j < BTS_GROUP_MAX; ++j)
         if (j < g.count && wg >= g.item[j].wg_begin) it = g.item[j];
-    bts_body<NB, D, XU>(wg - it.wg_begin, it.offsets, it.M, g.K, it.bq, it.br, it.bitmaps, it.X, it.N, it.payload,
-                        it.payload_bytes, it.Y, it.stagger, it.area_kb, BtEpi{it.Yh, it.sw, it.sx});
+    bts_body<NB, D, XU, BTS_GROUP_NBLK>(wg - it.wg_begin, it.offsets, it.M, g.K, it.bq, it.br, it.bitmaps, it.X, it.N,
+                                        it.payload, it.payload_bytes, it.Y, it.stagger, it.area_kb,
+                                        BtEpi{it.Yh, it.sw, it.sx});
 }
 
 // LDS of the streaming variant: the selector table, the row totals, for each
 // of a workgroup's nblk blocks the wavefronts' partials and area_kb KB of
 // staging, and the 1 KB dummy slot of the unused DMA instructions
-static size_t bts_lds(int nwaves, int nb, int64_t area_kb, int64_t nblk) {
-    return (size_t)BT_LUT_BYTES + (size_t)BTS_NBLK * BT_ROWS * 8 * 4 +
+static size_t bts_lds(int nwaves, int nb, int64_t area_kb, int64_t nblk, int nblk_cap = BTS_NBLK) {
+    return (size_t)BT_LUT_BYTES + (size_t)nblk_cap * BT_ROWS * 8 * 4 +
            (size_t)nblk * ((size_t)nwaves * nb * 256 * 4 + (size_t)area_kb * 1024) + 1024;
 }
 

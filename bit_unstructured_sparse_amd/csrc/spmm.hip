@@ -456,11 +456,12 @@ extern "C" int spmm_bitmap_w4a4_dq(const uint64_t *bitmaps, const uint32_t *offs
 
 namespace {
 
-// The streaming plan of one item of a grouped launch with `grid` workgroups.
-bool bts_item_plan(int64_t M, int64_t K, int64_t N, int64_t pbytes, int64_t grid, BtPlan *p) {
+// The streaming plan of one item of a grouped launch with `grid` workgroups
+// (at most nblk_cap blocks each).
+bool bts_item_plan(int64_t M, int64_t K, int64_t N, int64_t pbytes, int64_t grid, int nblk_cap, BtPlan *p) {
     if (!bt64_plan(M, K, N, pbytes, p) || !p->streaming) return false;
     const int64_t blocks = (M + BT_ROWS - 1) / BT_ROWS;
-    grid = std::max<int64_t>(grid, (blocks + BTS_NBLK - 1) / BTS_NBLK);
+    grid = std::max<int64_t>(grid, (blocks + nblk_cap - 1) / nblk_cap);
     grid = std::min<int64_t>(grid, blocks);
     p->grid = (unsigned)grid;
     p->bq = (int)(blocks / grid);
@@ -496,23 +497,32 @@ extern "C" int spmm_bitmap_w4a4_grouped(const bsp_w4a4_item *items, int count, i
     int64_t wg = 0;
     BtPlan plans[BSP_GROUP_MAX];
     int idx[BSP_GROUP_MAX], n_items = 0;
-    for (int i = 0; i < count; ++i) {
-        const bsp_w4a4_item &it = items[i];
-        if (it.M == 0 || it.N == 0) continue;
-        const int64_t blocks = (it.M + BT_ROWS - 1) / BT_ROWS;
-        // the CUs are shared out in proportion to the items' row blocks
-        const int64_t share = std::max<int64_t>(1, (BT_CUS * blocks + total_blocks - 1) / total_blocks);
-        if (!bts_item_plan(it.M, K, it.N, it.payload_bytes, share, &plans[n_items])) return BSP_E_UNSUPPORTED;
-        nb = std::max(nb, plans[n_items].nb);
-        d = std::max(d, plans[n_items].streaming);
-        nwaves = plans[n_items].nwaves;
-        idx[n_items++] = i;
+    // up to BTS_GROUP_NBLK blocks per workgroup, so that the group fits in
+    // one round of workgroups; three (the plain kernel's) when four do not
+    // fit in LDS
+    for (int cap = BTS_GROUP_NBLK; cap >= BTS_NBLK; --cap) {
+        nb = 1, d = 2, nwaves = 0, lds = 0, wg = 0, n_items = 0;
+        for (int i = 0; i < count; ++i) {
+            const bsp_w4a4_item &it = items[i];
+            if (it.M == 0 || it.N == 0) continue;
+            const int64_t blocks = (it.M + BT_ROWS - 1) / BT_ROWS;
+            // the CUs are shared out in proportion to the items' row blocks
+            const int64_t share = std::max<int64_t>(1, BT_CUS * blocks / total_blocks);
+            if (!bts_item_plan(it.M, K, it.N, it.payload_bytes, share, cap, &plans[n_items])) return BSP_E_UNSUPPORTED;
+            nb = std::max(nb, plans[n_items].nb);
+            d = std::max(d, plans[n_items].streaming);
+            nwaves = plans[n_items].nwaves;
+            idx[n_items++] = i;
+        }
+        for (int j = 0; j < n_items; ++j) {
+            const BtPlan &p = plans[j];
+            lds = std::max(lds, bts_lds(nwaves, nb, p.area_kb, p.bq + (p.br > 0 ? 1 : 0), BTS_GROUP_NBLK));
+        }
+        if (lds <= (size_t)BT_LDS_MAX) break;
     }
     for (int j = 0; j < n_items; ++j) {
         const BtPlan &p = plans[j];
         const bsp_w4a4_item &it = items[idx[j]];
-        const int64_t per_wg = p.bq + (p.br > 0 ? 1 : 0);
-        lds = std::max(lds, bts_lds(nwaves, nb, p.area_kb, per_wg));
         BtsItem &b = g.item[j];
         b.offsets = it.offsets;
         b.bitmaps = it.bitmaps;

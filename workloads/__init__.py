@@ -38,7 +38,7 @@ from typing import Dict, List, Tuple
 import numpy as np
 
 __all__ = ["Problem", "CONFIGS", "make", "int4_nonzero_values", "int4_mask_matrix",
-           "random_int4_problem", "config_names"]
+           "random_int4_problem", "config_names", "int2_nonzero_values", "int2_like", "random_int2_problem"]
 
 
 @dataclass
@@ -91,6 +91,28 @@ def _int4_weights(rng, M, K, keep) -> np.ndarray:
     mask = int4_mask_matrix(rng, M, K, keep)
     vals = int4_nonzero_values(rng, (M, K))
     return (vals * mask).astype(np.int8)
+
+
+def int2_nonzero_values(rng: np.random.Generator, size) -> np.ndarray:
+    """Uniform over the nonzero 2-bit codes {-2, -1, 1}."""
+    d = rng.integers(0, 3, size=size, dtype=np.int8)
+    return (d - np.int8(2) + (d >= 2).astype(np.int8)).astype(np.int8)
+
+
+def int2_like(W: np.ndarray, seed: int = 0) -> np.ndarray:
+    """2-bit weights with the nonzero pattern of W (W2A4 runs on the same
+    masks as the int4 workloads): fresh values in {-2, -1, 1} where W != 0."""
+    rng = np.random.default_rng(seed)
+    return (int2_nonzero_values(rng, W.shape) * (W != 0)).astype(np.int8)
+
+
+def random_int2_problem(seed: int, M: int, K: int, N: int, keep: float = 0.5, name: str = "random_w2") -> Problem:
+    """Small seeded W2A4 case of any shape: 2-bit weights, int4 activations."""
+    rng = np.random.default_rng(seed)
+    mask = int4_mask_matrix(rng, M, K, keep)
+    W = (int2_nonzero_values(rng, (M, K)) * mask).astype(np.int8)
+    X = int4_activations(rng, (N, K))
+    return Problem(name, "int2", W, X, dict(seed=seed, keep=keep, N=N))
 
 
 def random_int4_problem(seed: int, M: int, K: int, N: int, keep: float = 0.5,

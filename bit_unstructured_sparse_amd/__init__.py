@@ -30,7 +30,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(HERE, "libbitmap_spmm.so")
 
 OK, E_ARG, E_RANGE, E_CAPACITY, E_OVERFLOW, E_HIP, E_UNSUPPORTED = 0, 1, 2, 3, 4, 5, 6
-INT4, FP16 = 0, 1
+INT4, FP16, INT2 = 0, 1, 2
 ALGO_AUTO, ALGO_ROWWAVE, ALGO_MFMA, ALGO_SPLITK = 0, 1, 2, 3
 PAYLOAD_ALIGN = 16
 MAX_N = 32
@@ -41,7 +41,7 @@ EXPORTS = ["encode_bitmap_tiles", "pack_int4_activations", "spmm_bitmap_w4a4", "
            "bsp_workspace_bytes", "bsp_select", "bsp_describe_selection", "bsp_describe_selection_ws",
            "bsp_status_string", "bsp_version", "spmm_bitmap_f16_noalloc", "bsp_noalloc_scratch_bytes",
            "union_tile_count", "union_mask_words", "encode_union_tiles", "spmm_union_w4a4",
-           "spmm_bitmap_w4a4_dq", "spmm_bitmap_w4a4_grouped"]
+           "spmm_bitmap_w4a4_dq", "spmm_bitmap_w4a4_grouped", "spmm_bitmap_w2a4", "spmm_bitmap_w2a4_algo"]
 
 
 class BspError(RuntimeError):
@@ -98,6 +98,10 @@ def load_library():
         L.spmm_bitmap_w4a4_dq.restype = I32
         L.spmm_bitmap_w4a4_grouped.argtypes = [P, I32, I64, P]
         L.spmm_bitmap_w4a4_grouped.restype = I32
+        L.spmm_bitmap_w2a4.argtypes = [P, P, P, I64, I64, I64, P, I64, P, P]
+        L.spmm_bitmap_w2a4.restype = I32
+        L.spmm_bitmap_w2a4_algo.argtypes = [P, P, P, I64, I64, I64, P, I64, P, I32, P]
+        L.spmm_bitmap_w2a4_algo.restype = I32
         _lib = L
     return _lib
 
@@ -168,15 +172,16 @@ class DeviceMatrix:
     def stream_bytes(self, with_offsets: bool = True) -> int:
         """Bytes of the encoded stream proper (unpadded payload)."""
         G = self.M * self.T
-        pb = (self.nnz + 1) // 2 if self.dtype == INT4 else 2 * self.nnz
+        pb = {INT4: (self.nnz + 1) // 2, INT2: (self.nnz + 3) // 4}.get(self.dtype, 2 * self.nnz)
         return 8 * G + (4 * (G + 1) if with_offsets else 0) + pb
 
 
-def encode(W: np.ndarray) -> Encoded:
-    """Encode a dense host matrix: int8 (int4 values in [-8, 7]) or float16."""
+def encode(W: np.ndarray, dtype: Optional[int] = None) -> Encoded:
+    """Encode a dense host matrix: int8 (int4 values in [-8, 7]; with
+    dtype=INT2, 2-bit values in [-2, 1]) or float16."""
     L = load_library()
     if W.dtype == np.int8:
-        dt = INT4
+        dt = INT2 if dtype == INT2 else INT4
     elif W.dtype == np.float16:
         dt = FP16
         W = W.view(np.uint16)
@@ -202,6 +207,23 @@ def encode(W: np.ndarray) -> Encoded:
                                  _np_ptr(payload), payload.nbytes, ctypes.byref(nnz), ctypes.byref(nbytes)),
            "encode_bitmap_tiles")
     return Encoded(dt, M, K, int(nnz.value), bitmaps, offsets, payload)
+
+
+def spmm_w2a4(W: DeviceMatrix, X, N: int, Y=None, algo: int = ALGO_AUTO, stream=None):
+    """Y[n][m] = sum_k W[m][k] X[k][n] (int32) with 2-bit weights (a stream
+    encoded with dtype=INT2). X: uint8 [N][ceil(K/2)] packed int4."""
+    import torch
+    if W.dtype != INT2:
+        raise TypeError("spmm_w2a4 needs an INT2 DeviceMatrix")
+    _check_dev(X, "X", torch.uint8, N * ((W.K + 1) // 2))
+    if Y is None:
+        Y = torch.empty((N, W.M), dtype=torch.int32, device=X.device)
+    _check_dev(Y, "Y", torch.int32, N * W.M)
+    rc = load_library().spmm_bitmap_w2a4_algo(
+        _dptr(W.bitmaps), _dptr(W.offsets), _dptr(W.payload), W.payload.numel(), W.M, W.K,
+        _dptr(X), N, _dptr(Y), algo, _stream_handle(stream))
+    _check(rc, "spmm_bitmap_w2a4")
+    return Y
 
 
 def pack_int4(X: np.ndarray) -> np.ndarray:

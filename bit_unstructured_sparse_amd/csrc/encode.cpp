@@ -71,7 +71,7 @@ extern "C" int encode_bitmap_tiles(int dtype, const void *W, int64_t M, int64_t 
                                    uint64_t *bitmaps, uint32_t *offsets,
                                    void *payload, int64_t payload_capacity_bytes,
                                    int64_t *nnz_out, int64_t *payload_bytes_out) {
-    if (dtype != BSP_INT4 && dtype != BSP_FP16) return BSP_E_ARG;
+    if (dtype != BSP_INT4 && dtype != BSP_FP16 && dtype != BSP_INT2) return BSP_E_ARG;
     if (M < 0 || K < 0 || ldw < K) return BSP_E_ARG;
     if (M > 0 && K > 0 && W == nullptr) return BSP_E_ARG;
     if (payload_capacity_bytes < 0) return BSP_E_ARG;
@@ -85,11 +85,12 @@ extern "C" int encode_bitmap_tiles(int dtype, const void *W, int64_t M, int64_t 
     parallel_rows(M, [&](int, int64_t r0, int64_t r1) {
         for (int64_t m = r0; m < r1; ++m) {
             int64_t c = 0;
-            if (dtype == BSP_INT4) {
+            if (dtype == BSP_INT4 || dtype == BSP_INT2) {
+                const int lo = dtype == BSP_INT4 ? -8 : -2, hi = dtype == BSP_INT4 ? 7 : 1;
                 const int8_t *row = (const int8_t *)W + m * ldw;
                 for (int64_t k = 0; k < K; ++k) {
                     int v = row[k];
-                    if (v < -8 || v > 7) { bad_range.store(true, std::memory_order_relaxed); }
+                    if (v < lo || v > hi) { bad_range.store(true, std::memory_order_relaxed); }
                     c += (v != 0);
                 }
             } else {
@@ -106,7 +107,7 @@ extern "C" int encode_bitmap_tiles(int dtype, const void *W, int64_t M, int64_t 
     for (int64_t m = 0; m < M; ++m) row_start[(size_t)m + 1] = row_start[(size_t)m] + row_nnz[(size_t)m];
     const int64_t nnz = row_start[(size_t)M];
     if (nnz > (int64_t)UINT32_MAX) return BSP_E_OVERFLOW;
-    const int64_t bytes = dtype == BSP_INT4 ? (nnz + 1) / 2 : 2 * nnz;
+    const int64_t bytes = dtype == BSP_INT4 ? (nnz + 1) / 2 : dtype == BSP_INT2 ? (nnz + 3) / 4 : 2 * nnz;
     if (nnz_out) *nnz_out = nnz;
     if (payload_bytes_out) *payload_bytes_out = bytes;
     if (payload == nullptr) {
@@ -151,6 +152,15 @@ extern "C" int encode_bitmap_tiles(int dtype, const void *W, int64_t M, int64_t 
                         }
                         ++e;
                     }
+                } else if (dtype == BSP_INT2) {
+                    // words only here; the 2-bit codes are packed after the
+                    // threads join (four to a byte, across thread boundaries)
+                    const int8_t *row = (const int8_t *)W + m * ldw + k0;
+                    for (int j = 0; j < jn; ++j)
+                        if (row[j] != 0) {
+                            word |= (uint64_t)1 << j;
+                            ++e;
+                        }
                 } else {
                     const uint16_t *row = (const uint16_t *)W + m * ldw + k0;
                     for (int j = 0; j < jn; ++j) {
@@ -186,6 +196,20 @@ extern "C" int encode_bitmap_tiles(int dtype, const void *W, int64_t M, int64_t 
         for (auto &x : lo) p8[x.first] = x.second;                 // high nibble zero for now
         for (auto &x : hi) p8[x.first] = (uint8_t)((p8[x.first] & 0x0F) | (x.second << 4));
     }
+    if (dtype == BSP_INT2 && payload && bytes > 0) {
+        // element e in byte e >> 2 at bits 2 (e & 3), the lowest first
+        uint8_t *p8 = (uint8_t *)payload;
+        memset(p8, 0, (size_t)bytes);
+        int64_t e = 0;
+        for (int64_t m = 0; m < M; ++m) {
+            const int8_t *row = (const int8_t *)W + m * ldw;
+            for (int64_t k = 0; k < K; ++k)
+                if (row[k] != 0) {
+                    p8[e >> 2] = (uint8_t)(p8[e >> 2] | ((row[k] & 3) << (2 * (e & 3))));
+                    ++e;
+                }
+        }
+    }
     return BSP_OK;
 }
 
@@ -213,7 +237,7 @@ extern "C" const char *bsp_status_string(int status) {
     switch (status) {
         case BSP_OK: return "ok";
         case BSP_E_ARG: return "invalid argument";
-        case BSP_E_RANGE: return "int4 value outside [-8, 7]";
+        case BSP_E_RANGE: return "weight outside its type's range (int4 [-8, 7], int2 [-2, 1])";
         case BSP_E_CAPACITY: return "payload buffer too small";
         case BSP_E_OVERFLOW: return "size beyond the supported range";
         case BSP_E_HIP: return "HIP launch error";

@@ -283,11 +283,14 @@ __device__ __forceinline__ void bt_x_runs_to_slices(bt_v4i (&xg)[NB][2 * TPL], u
 }
 
 // Decode of one tile word into 16 dwords of x16 int8 (A operand of 4 MFMAs).
-// win(p) returns the two payload dwords holding nibbles p .. p+7 as (lo, hi).
+// win(p) returns the two payload dwords holding values p .. p+7 as (lo, hi).
+// WB is the width of a stored value: 4 (int4 weights: each byte of the A
+// operand is 16 w) or 2 (int2 weights, W2A4: the 16 bits of the window are
+// spread to one 4-bit group per byte first, and each byte is 64 w).
 // lut_base is the LDS address of this lane's copy of the selector table: the
 // copies are interleaved entry by entry (entry b of copy c at (16 b + c) * 8),
 // so the 16 lanes that read one copy each cannot conflict with one another.
-template <class Win>
+template <class Win, int WB = 4>
 __device__ __forceinline__ void bt_decode_tile(uint64_t word, uint32_t p, const Win &win, uint32_t lut_base,
                                                uint32_t A[16]) {
     const uint32_t lo = (uint32_t)word, hi = (uint32_t)(word >> 32);
@@ -304,36 +307,51 @@ __device__ __forceinline__ void bt_decode_tile(uint64_t word, uint32_t p, const 
     }
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-        const uint32_t x = __builtin_amdgcn_alignbit(d[k].y, d[k].x, pk[k] << 2);
-        const uint32_t s_odd = x & 0xF0F0F0F0u;
-        const uint32_t s_even = (x << 4) & 0xF0F0F0F0u;
+        uint32_t s_odd, s_even;
+        if constexpr (WB == 4) {
+            const uint32_t x = __builtin_amdgcn_alignbit(d[k].y, d[k].x, pk[k] << 2);
+            s_odd = x & 0xF0F0F0F0u;
+            s_even = (x << 4) & 0xF0F0F0F0u;
+        } else {
+            uint32_t t = __builtin_amdgcn_alignbit(d[k].y, d[k].x, pk[k] << 1) & 0xFFFFu;
+            t = (t | (t << 8)) & 0x00FF00FFu;
+            t = (t | (t << 4)) & 0x0F0F0F0Fu;     // byte i: values 2i (bits 0-1) and 2i+1 (bits 2-3)
+            s_odd = (t << 4) & 0xC0C0C0C0u;
+            s_even = (t << 6) & 0xC0C0C0C0u;
+        }
         A[2 * k] = __builtin_amdgcn_perm(s_odd, s_even, sel[k].x);
         A[2 * k + 1] = __builtin_amdgcn_perm(s_odd, s_even, sel[k].y);
     }
 }
 
 // Window source: the staged stream in LDS.
-struct BtWinLds {
-    // p counts nibbles from twice the staging buffer's LDS address (a
-    // multiple of 16 bytes), so dword p >> 3 of the stream sits at LDS byte
-    // address (p >> 1) & ~3; the two dwords come from one ds_read2_b32
+template <int WB = 4>
+struct BtWinLdsT {
+    // p counts values from 8 / WB times the staging buffer's LDS address (a
+    // multiple of 16 bytes), so the dword holding value p sits at LDS byte
+    // address (p >> (WB == 4 ? 1 : 2)) & ~3; the two dwords come from one
+    // ds_read2_b32
     __device__ __forceinline__ uint2 operator()(uint32_t p) const {
-        const bt_lds_u32 *q = (const bt_lds_u32 *)(uintptr_t)((p >> 1) & ~3u);
+        const bt_lds_u32 *q = (const bt_lds_u32 *)(uintptr_t)((p >> (WB == 4 ? 1 : 2)) & ~3u);
         return uint2{q[0], q[1]};
     }
 };
+using BtWinLds = BtWinLdsT<4>;
 
 // Window source: global memory through a range-checked buffer resource
-// (p counts nibbles from payload dword d0).
-struct BtWinGlobal {
+// (p counts values from payload dword d0).
+template <int WB = 4>
+struct BtWinGlobalT {
     __amdgpu_buffer_rsrc_t rs;
     uint32_t d0;
     __device__ __forceinline__ uint2 operator()(uint32_t p) const {
-        const uint32_t off = (d0 + (p >> 3)) * 4u;
+        const uint32_t off = (d0 + (p >> (WB == 4 ? 3 : 4))) * 4u;
         return uint2{(uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0),
                      (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, off + 4u, 0, 0)};
     }
 };
+
+using BtWinGlobal = BtWinGlobalT<4>;
 
 // X slice of one tile for one MFMA j: packed dwords x0 (k 0..7) and x1
 // (k 8..15) -> B dwords {even k of x0, odd k of x0, even k of x1, odd k of x1}
@@ -352,14 +370,14 @@ struct BtTileSame {
 // B operands (column r + 16 nb, tiles t0 .. t0+TPL-1, MFMA j), built once.
 // tile(p) maps the stream position of a tile's first nonzero to the position
 // its windows are read from.
-template <int NB, int TPL, class Win, class Tile = BtTileSame>
+template <int NB, int TPL, class Win, class Tile = BtTileSame, int WB = 4>
 __device__ __forceinline__ void bt_contract(const uint64_t (&words)[TPL], uint32_t p, const Win &win,
                                             uint32_t lut_base, const bt_v4i (&xb)[NB][TPL][4],
                                             bt_v4i (&acc)[NB], const Tile &tile = Tile{}) {
 #pragma unroll
     for (int i = 0; i < TPL; ++i) {
         uint32_t A[16];
-        bt_decode_tile(words[i], tile(p), win, lut_base, A);
+        bt_decode_tile<Win, WB>(words[i], tile(p), win, lut_base, A);
         p += (uint32_t)__builtin_popcountll(words[i]);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -372,13 +390,16 @@ __device__ __forceinline__ void bt_contract(const uint64_t (&words)[TPL], uint32
 }
 
 // Payload range of a block in 16-byte granules: [g0, g0 + n) covers its
-// nibbles plus one granule for the windows that read past the last nonzero.
+// values (32 per granule for int4, 64 for int2) plus one granule for the
+// windows that read past the last nonzero.
 struct BtRange {
     uint32_t g0, n;
 };
+template <int WB = 4>
 __device__ __forceinline__ BtRange bt_range(uint32_t nibA, uint32_t nibB) {
-    const uint32_t g0 = nibA >> 5;
-    const uint32_t g1 = (nibB >= nibA ? (nibB + 31u) >> 5 : g0) + 1u;
+    constexpr uint32_t S = WB == 4 ? 5 : 6;
+    const uint32_t g0 = nibA >> S;
+    const uint32_t g1 = (nibB >= nibA ? (nibB + (1u << S) - 1u) >> S : g0) + 1u;
     return BtRange{g0, g1 - g0};
 }
 
@@ -724,7 +745,8 @@ __device__ __forceinline__ void bt_make_b(const uint32_t (&xw)[NB][TPL][8], bt_v
 
 // The work of one workgroup; gid is its index among the workgroups of its
 // matrix (the plain kernel's block index, or its place in a grouped launch).
-template <int NB, int D, bool XU, int NBLK = BTS_NBLK>
+// WB: width of a stored weight value (4: int4; 2: int2, the W2A4 variant).
+template <int NB, int D, bool XU, int NBLK = BTS_NBLK, int WB = 4>
 __device__ __forceinline__ void bts_body(
         int gid, const uint32_t *__restrict__ offsets, int M, int K, int bq, int br,
         const uint64_t *__restrict__ bitmaps, const uint8_t *__restrict__ X, int N,
@@ -762,7 +784,9 @@ __device__ __forceinline__ void bts_body(
     const uint32_t slots = area_kb * 64u;
     const uint32_t cap = stagger ? BTS_RUN * (slots / (BTS_RUN + BTS_OVL)) : slots;   // granules a block's area holds
     const uint32_t kmag = stagger ? BTS_DIVMAG : 0u;             // s * kmag >> 20 = s / (BTS_RUN + BTS_OVL)
-    const uint32_t tmul = stagger ? 2u * 16u * BTS_OVL : 0u;     // nibbles added per run
+    constexpr uint32_t VPB = 8 / WB;                               // values per payload byte
+    constexpr int PS = WB == 4 ? 8 : 10;                           // log2 of the A x B operand scale
+    const uint32_t tmul = stagger ? VPB * 16u * BTS_OVL : 0u;    // values added per run
     const __amdgpu_buffer_rsrc_t prs = bt_rsrc(payload, payload_bytes);
 
     uint32_t nib[NBLK + 1];
@@ -823,7 +847,7 @@ __device__ __forceinline__ void bts_body(
     uint8_t *dummy = stage + (uint32_t)nblk_max * area;
     auto issue = [&](int i) -> void {
         const bool blk = i < nblk;
-        const BtRange g = bt_range(nib[i], nib[i + 1]);
+        const BtRange g = bt_range<WB>(nib[i], nib[i + 1]);
         const uint32_t n = blk ? min(g.n, cap) : 0u;
         uint8_t *buf = stage + (uint32_t)i * area;
 #pragma unroll
@@ -881,7 +905,7 @@ __device__ __forceinline__ void bts_body(
             bt_make_b<NB, TPL>(xw, xb);
         }
         bt_barrier_lds();                     // ... everyone's, and every row total of block i
-        const BtRange g = bt_range(nib[i], nib[i + 1]);
+        const BtRange g = bt_range<WB>(nib[i], nib[i + 1]);
         const int rows = min(BT_ROWS, M - (b_begin + i) * BT_ROWS);
         uint32_t pstart;
         {
@@ -903,7 +927,7 @@ __device__ __forceinline__ void bts_body(
             sc += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)sc, 0x112, 0xF, 0xF, true);   // row_shr:2
             sc += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)sc, 0x114, 0xF, 0xF, true);   // row_shr:4
             sc += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)sc, 0x118, 0xF, 0xF, true);   // row_shr:8
-            pstart = r < rows ? (nib[i] & 31u) + (sc - row_total) + before_w + (incl - seg) : 0u;
+            pstart = r < rows ? (nib[i] & (16u * VPB - 1u)) + (sc - row_total) + before_w + (incl - seg) : 0u;
         }
         bt_v4i acc[NB];
 #pragma unroll
@@ -912,18 +936,20 @@ __device__ __forceinline__ void bts_body(
             // a corrupt stream stays inside the staged granules
             // (a tile's windows stay inside the run of its first nonzero plus
             // the BTS_OVL granules stored after it)
-            const uint32_t p = min(pstart, 8u * (4u * g.n - 2u));
-            const uint32_t base2 = 2u * bt_lds_addr(stage + (uint32_t)i * area);
-            bt_contract<NB, TPL>(words[i], p, BtWinLds{}, lut_base, xb, acc,
-                                 [=](uint32_t pt) { return pt + base2 + (pt >> BTS_RUN_NIB_LOG2) * tmul; });
+            const uint32_t p = min(pstart, 16u * VPB * g.n - 8u * VPB);
+            const uint32_t base2 = VPB * bt_lds_addr(stage + (uint32_t)i * area);
+            const auto tmap = [=](uint32_t pt) { return pt + base2 + (pt >> (BTS_RUN_NIB_LOG2 + (WB == 2))) * tmul; };
+            bt_contract<NB, TPL, BtWinLdsT<WB>, decltype(tmap), WB>(words[i], p, BtWinLdsT<WB>{}, lut_base, xb, acc,
+                                                                    tmap);
         } else {
-            bt_contract<NB, TPL>(words[i], pstart, BtWinGlobal{prs, 4u * g.g0}, lut_base, xb, acc);
+            bt_contract<NB, TPL, BtWinGlobalT<WB>, BtTileSame, WB>(words[i], pstart, BtWinGlobalT<WB>{prs, 4u * g.g0},
+                                                                  lut_base, xb, acc);
         }
         int32_t *pw = part + (i * nwaves + wave) * NB * 256;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
             *(__attribute__((address_space(3))) bt_v4i *)(uintptr_t)bt_lds_addr(pw + nb * 256 + lane * 4) =
-                    bt_v4i{acc[nb][0] >> 8, acc[nb][1] >> 8, acc[nb][2] >> 8, acc[nb][3] >> 8};
+                    bt_v4i{acc[nb][0] >> PS, acc[nb][1] >> PS, acc[nb][2] >> PS, acc[nb][3] >> PS};
     }
     bt_barrier_lds();
     // Y: item (block i, column block nb, lane l) sums the wavefronts' partials
@@ -947,6 +973,17 @@ __global__ __launch_bounds__(512) void k_bt64s_w4a4(
         int32_t *__restrict__ Y, uint32_t stagger, uint32_t area_kb, uint16_t *Yh, const float *sw, const float *sx) {
     bts_body<NB, D, XU>((int)blockIdx.x, offsets, M, K, bq, br, bitmaps, X, N, payload, payload_bytes, Y, stagger,
                         area_kb, BtEpi{Yh, sw, sx});
+}
+
+// W2A4: 2-bit weights (UnionSparse Sec. VII, Fig. 11) through the same
+// streaming kernel; int32 Y.
+template <int NB, int D, bool XU>
+__global__ __launch_bounds__(512) void k_bt64s_w2a4(
+        const uint32_t *__restrict__ offsets, int M, int K, int bq, int br, const uint64_t *__restrict__ bitmaps,
+        const uint8_t *__restrict__ X, int N, const uint8_t *__restrict__ payload, uint32_t payload_bytes,
+        int32_t *__restrict__ Y, uint32_t stagger, uint32_t area_kb) {
+    bts_body<NB, D, XU, BTS_NBLK, 2>((int)blockIdx.x, offsets, M, K, bq, br, bitmaps, X, N, payload, payload_bytes, Y,
+                                     stagger, area_kb, BtEpi{nullptr, nullptr, nullptr});
 }
 
 // Grouped launch: up to BTS_GROUP_MAX matrices with one K, each with its own
@@ -1015,7 +1052,7 @@ static bool bt64_supported(int64_t K, int64_t N) {
     return K > 0 && (K + 63) / 64 <= 8 * 4 * 8 && N >= 1 && N <= 32;
 }
 
-static bool bt64_plan(int64_t M, int64_t K, int64_t N, int64_t payload_bytes, BtPlan *p) {
+static bool bt64_plan(int64_t M, int64_t K, int64_t N, int64_t payload_bytes, BtPlan *p, int wb = 4) {
     if (!bt64_supported(K, N) || M <= 0) return false;
     const int64_t T = (K + 63) / 64;
     p->tpl = T <= 64 ? 2 : T <= 128 ? 4 : 8;
@@ -1034,7 +1071,7 @@ static bool bt64_plan(int64_t M, int64_t K, int64_t N, int64_t payload_bytes, Bt
     // Staging: 1.2x the average block plus 2 KB (a denser block falls back
     // to global-memory windows), capped at the densest block.
     const int64_t avg = payload_bytes / std::max<int64_t>(blocks, 1);
-    const int64_t worst = (int64_t)BT_ROWS * T * 32 + 64;
+    const int64_t worst = (int64_t)BT_ROWS * T * 8 * wb + 64;   // a fully dense block
     int64_t stage = std::min<int64_t>(worst, avg + avg / 5 + 2048) + 32;
     stage = (stage + 1023) / 1024 * 1024;
     const int64_t fixed = BT_LUT_BYTES + nblk_max * BT_ROWS * (BT_WG_THREADS(p->tpl) / 64) * 4 + 3 * p->nb * 256 * 4;
@@ -1131,6 +1168,36 @@ static void launch_bt64_w4a4(const BtPlan &p, const uint64_t *bitmaps, const uin
         launch_bt64_w4a4_x<false>(p, bitmaps, offsets, payload, payload_bytes, M, K, X, N, Y, e, stream);
     else
         launch_bt64_w4a4_x<true>(p, bitmaps, offsets, payload, payload_bytes, M, K, X, N, Y, e, stream);
+}
+
+// W2A4 through the streaming kernel (the plan must be a streaming one).
+template <bool XU>
+static void launch_bt64s_w2a4_x(const BtPlan &p, const uint64_t *bitmaps, const uint32_t *offsets,
+                                const uint8_t *payload, uint32_t payload_bytes, int M, int K, const uint8_t *X, int N,
+                                int32_t *Y, hipStream_t stream) {
+#define BTS2_LAUNCH(NB, D)                                                                                            \
+    do {                                                                                                              \
+        (void)hipFuncSetAttribute((const void *)k_bt64s_w2a4<NB, D, XU>, hipFuncAttributeMaxDynamicSharedMemorySize, \
+                                  (int)p.lds);                                                                        \
+        hipLaunchKernelGGL((k_bt64s_w2a4<NB, D, XU>), dim3(p.grid), dim3(64 * p.nwaves), p.lds, stream, offsets, M, K, \
+                           p.bq, p.br, bitmaps, X, N, payload, payload_bytes, Y, (uint32_t)p.stagger,                 \
+                           (uint32_t)p.area_kb);                                                                      \
+    } while (0)
+    if (p.nb == 1) {
+        if (p.streaming == 2) BTS2_LAUNCH(1, 2); else if (p.streaming == 3) BTS2_LAUNCH(1, 3); else BTS2_LAUNCH(1, 4);
+    } else {
+        if (p.streaming == 2) BTS2_LAUNCH(2, 2); else if (p.streaming == 3) BTS2_LAUNCH(2, 3); else BTS2_LAUNCH(2, 4);
+    }
+#undef BTS2_LAUNCH
+}
+
+static void launch_bt64s_w2a4(const BtPlan &p, const uint64_t *bitmaps, const uint32_t *offsets,
+                              const uint8_t *payload, uint32_t payload_bytes, int M, int K, const uint8_t *X, int N,
+                              int32_t *Y, hipStream_t stream) {
+    if (K % 8 == 0)
+        launch_bt64s_w2a4_x<false>(p, bitmaps, offsets, payload, payload_bytes, M, K, X, N, Y, stream);
+    else
+        launch_bt64s_w2a4_x<true>(p, bitmaps, offsets, payload, payload_bytes, M, K, X, N, Y, stream);
 }
 
 // Grouped launch of the streaming kernel (items prepared by the caller:

@@ -8,7 +8,9 @@
 // It reads every operand through the caches one element at a time, so it is
 // the simple baseline the faster kernels are measured against.
 
-template <int NB>
+// WB: width of a stored weight (4: int4 codes two per byte; 2: int2 codes
+// four per byte, the W2A4 variant), low bits first.
+template <int NB, int WB = 4>
 __global__ __launch_bounds__(256) void k_rowwave_w4a4(const uint64_t *__restrict__ bitmaps,
                                                       const uint32_t *__restrict__ offsets,
                                                       const uint8_t *__restrict__ payload, uint32_t payload_bytes,
@@ -33,8 +35,14 @@ __global__ __launch_bounds__(256) void k_rowwave_w4a4(const uint64_t *__restrict
         while (word) {
             const int j = __builtin_ctzll(word);
             word &= word - 1;
-            const uint32_t byte = __builtin_amdgcn_raw_buffer_load_b8(pr, e >> 1, 0, 0);
-            const int w = bsp_sext4(byte >> ((e & 1) * 4));
+            int w;
+            if constexpr (WB == 4) {
+                const uint32_t byte = __builtin_amdgcn_raw_buffer_load_b8(pr, e >> 1, 0, 0);
+                w = bsp_sext4(byte >> ((e & 1) * 4));
+            } else {
+                const uint32_t byte = __builtin_amdgcn_raw_buffer_load_b8(pr, e >> 2, 0, 0);
+                w = (int)((byte >> ((e & 3) * 2)) << 30) >> 30;
+            }
             ++e;
             const int k = 64 * t + j;
 #pragma unroll
@@ -98,14 +106,17 @@ __global__ __launch_bounds__(256) void k_rowwave_f16(const uint64_t *__restrict_
     }
 }
 
+template <int WB = 4>
 static void launch_rowwave_w4a4(const uint64_t *bitmaps, const uint32_t *offsets, const uint8_t *payload,
                                 uint32_t payload_bytes, int M, int K, const uint8_t *X, int N, int32_t *Y,
                                 hipStream_t stream) {
     const dim3 block(256), grid((unsigned)((M + 3) / 4));
     if (N <= 8)
-        hipLaunchKernelGGL(k_rowwave_w4a4<8>, grid, block, 0, stream, bitmaps, offsets, payload, payload_bytes, M, K, X, N, Y);
+        hipLaunchKernelGGL((k_rowwave_w4a4<8, WB>), grid, block, 0, stream, bitmaps, offsets, payload, payload_bytes, M, K,
+                           X, N, Y);
     else
-        hipLaunchKernelGGL(k_rowwave_w4a4<32>, grid, block, 0, stream, bitmaps, offsets, payload, payload_bytes, M, K, X, N, Y);
+        hipLaunchKernelGGL((k_rowwave_w4a4<32, WB>), grid, block, 0, stream, bitmaps, offsets, payload, payload_bytes, M,
+                           K, X, N, Y);
 }
 
 static void launch_rowwave_f16(const uint64_t *bitmaps, const uint32_t *offsets, const uint16_t *payload,

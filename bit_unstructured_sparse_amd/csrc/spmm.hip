@@ -550,3 +550,29 @@ extern "C" int spmm_bitmap_w4a4_grouped(const bsp_w4a4_item *items, int count, i
         launch_bts_group_x<true>(g, nb, d, (unsigned)wg, nwaves, lds, stream);
     return launch_status();
 }
+
+// ---------------------------------------------------------------------------
+// W2A4: 2-bit weights in the BT64 format, int4 activations, int32 Y.
+extern "C" int spmm_bitmap_w2a4_algo(const uint64_t *bitmaps, const uint32_t *offsets, const uint8_t *payload,
+                                     int64_t payload_bytes, int64_t M, int64_t K, const uint8_t *X, int64_t N,
+                                     int32_t *Y, int algo, hipStream_t stream) {
+    Shape s;
+    int rc = check_args(bitmaps, offsets, payload, payload_bytes, M, K, X, N, Y, algo, &s);
+    if (rc != BSP_OK || M == 0 || N == 0) return rc;
+    if (algo == BSP_ALGO_SPLITK) return BSP_E_UNSUPPORTED;
+    BtPlan bp;
+    const bool streaming = K > 0 && bt64_plan(M, K, N, payload_bytes, &bp, 2) && bp.streaming > 0 &&
+                           ((uintptr_t)X & 3u) == 0;
+    if (algo == BSP_ALGO_MFMA && !streaming) return BSP_E_UNSUPPORTED;
+    if (streaming && algo != BSP_ALGO_ROWWAVE)
+        launch_bt64s_w2a4(bp, bitmaps, offsets, payload, (uint32_t)payload_bytes, (int)M, (int)K, X, (int)N, Y, stream);
+    else
+        launch_rowwave_w4a4<2>(bitmaps, offsets, payload, (uint32_t)payload_bytes, (int)M, (int)K, X, (int)N, Y, stream);
+    return launch_status();
+}
+
+extern "C" int spmm_bitmap_w2a4(const uint64_t *bitmaps, const uint32_t *offsets, const uint8_t *payload,
+                                int64_t payload_bytes, int64_t M, int64_t K, const uint8_t *X, int64_t N, int32_t *Y,
+                                hipStream_t stream) {
+    return spmm_bitmap_w2a4_algo(bitmaps, offsets, payload, payload_bytes, M, K, X, N, Y, BSP_ALGO_AUTO, stream);
+}

@@ -60,14 +60,14 @@ extern "C" {
 typedef enum bsp_status {
     BSP_OK = 0,
     BSP_E_ARG = 1,       /* null pointer, negative size, N > 32, ldw < K, unknown dtype/algo */
-    BSP_E_RANGE = 2,     /* an int4 weight outside [-8, 7] */
+    BSP_E_RANGE = 2,     /* a weight outside its type's range: int4 [-8, 7], int2 [-2, 1] */
     BSP_E_CAPACITY = 3,  /* payload buffer smaller than the encoded payload */
     BSP_E_OVERFLOW = 4,  /* nnz >= 2^32, K >= 2^25 (int32 sums could overflow), or an index beyond 2^31 */
     BSP_E_HIP = 5,       /* a HIP launch error (hipGetLastError after the launch) */
     BSP_E_UNSUPPORTED = 6 /* a kernel forced through an *_algo entry point cannot run this shape */
 } bsp_status;
 
-typedef enum bsp_dtype { BSP_INT4 = 0, BSP_FP16 = 1 } bsp_dtype;
+typedef enum bsp_dtype { BSP_INT4 = 0, BSP_FP16 = 1, BSP_INT2 = 2 } bsp_dtype;
 
 /* Kernel choice for the *_algo entry points. BSP_ALGO_AUTO applies the
  * library's shape-aware selection (by N, density, M, K). A forced choice
@@ -99,6 +99,9 @@ typedef enum bsp_algo {
  * 1 x 64 tiles; the encoded form is produced offline and cached, Sec. V-B).
  *
  *   dtype    BSP_INT4: W is const int8_t*, values in [-8, 7];
+ *            BSP_INT2: W is const int8_t*, values in [-2, 1] (the W2A4 weights
+ *            of UnionSparse Sec. VII, Fig. 11): payload element e is the 2-bit
+ *            two's-complement code in byte e>>2 at bits 2*(e&3), lowest first;
  *            BSP_FP16: W is const uint16_t* holding IEEE binary16 bits
  *            (+0 and -0 are zero; every other pattern, NaN included, is stored).
  *   W        HOST memory, row-major M x K with leading dimension ldw >= K.
@@ -107,8 +110,8 @@ typedef enum bsp_algo {
  *   payload  HOST, caller-allocated, payload_capacity_bytes bytes, or NULL for
  *            a size query (then bitmaps/offsets may also be NULL).
  *   nnz_out, payload_bytes_out  written on BSP_OK and on BSP_E_CAPACITY
- *            (either may be NULL). payload_bytes = ceil(nnz/2) (int4) or
- *            2*nnz (fp16).
+ *            (either may be NULL). payload_bytes = ceil(nnz/2) (int4),
+ *            ceil(nnz/4) (int2) or 2*nnz (fp16).
  * Returns BSP_E_ARG, BSP_E_RANGE (nothing written), BSP_E_OVERFLOW
  * (nnz >= 2^32), BSP_E_CAPACITY (counts written, arrays untouched) or BSP_OK.
  * Multi-threaded over rows; the output does not depend on the thread count.
@@ -241,6 +244,22 @@ int bsp_describe_selection(int dtype, int64_t M, int64_t K, int64_t N, int64_t n
 /* The same for the automatic plan of the *_ws entry points given a
  * workspace of bsp_workspace_bytes. */
 int bsp_describe_selection_ws(int dtype, int64_t M, int64_t K, int64_t N, int64_t nnz, char *buf, size_t n);
+
+/*
+ * spmm_bitmap_w2a4 -- Y = W * X with W's values 2-bit (encoded with dtype
+ * BSP_INT2: the W2A4 setting of UnionSparse Sec. VII, Fig. 11) and X packed
+ * int4 as for spmm_bitmap_w4a4; Y int32 [N][M], exact. payload_bytes >=
+ * ceil(nnz/4), a multiple of BSP_PAYLOAD_ALIGN. The automatic choice runs the
+ * streaming MFMA kernel (K <= 4096, X on a 4-byte boundary) and the plain
+ * kernel elsewhere; _algo forces BSP_ALGO_MFMA (BSP_E_UNSUPPORTED outside it)
+ * or BSP_ALGO_ROWWAVE; BSP_ALGO_SPLITK returns BSP_E_UNSUPPORTED.
+ */
+int spmm_bitmap_w2a4(const uint64_t *bitmaps, const uint32_t *offsets, const uint8_t *payload,
+                     int64_t payload_bytes, int64_t M, int64_t K, const uint8_t *X, int64_t N,
+                     int32_t *Y, hipStream_t stream);
+int spmm_bitmap_w2a4_algo(const uint64_t *bitmaps, const uint32_t *offsets, const uint8_t *payload,
+                          int64_t payload_bytes, int64_t M, int64_t K, const uint8_t *X, int64_t N,
+                          int32_t *Y, int algo, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * Dequant epilogue and grouped launch (the Quant -> SpMM -> Dequant pipeline

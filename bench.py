@@ -517,6 +517,8 @@ def prepare(args, workload, index, n):
         return _prepare_union(args, bsp, problem, dev)
     if getattr(args, "parts", 0) or getattr(args, "epilogue", "int32") == "dq":
         return _prepare_parts(args, bsp, problem, dev)
+    if getattr(args, "wbits", 4) == 2:
+        return _prepare_w2(args, bsp, problem, dev)
     enc = bsp.encode(problem.W)
     algo = {"auto": bsp.ALGO_AUTO, "rowwave": bsp.ALGO_ROWWAVE, "mfma": bsp.ALGO_MFMA, "splitk": bsp.ALGO_SPLITK}[args.algo]
     dt = bsp.FP16 if fp16 else bsp.INT4
@@ -599,6 +601,39 @@ def _prepare_union(args, bsp, problem, dev):
                 union={"nvals": ue.nvals, "reorder": not args.no_reorder, "encode_seconds": round(enc_s, 3),
                        "stream_bytes": ue.stream_bytes(), "payload_bytes": int(ue.payload.nbytes),
                        "value_fill": round(ue.nvals / max(1, 4 * nnz), 4)})
+
+
+def _prepare_w2(args, bsp, problem, dev):
+    """prepare() for W2A4: the workload's nonzero pattern with fresh 2-bit
+    values in {-2, -1, 1} (workloads.int2_like), its int4 X."""
+    import numpy as np
+    import torch
+    import workloads
+    if problem.dtype != "int4":
+        raise SystemExit("W2A4 runs on the int4 workloads' shapes")
+    N, M, K = problem.N, problem.M, problem.K
+    W2 = workloads.int2_like(problem.W, seed=0)
+    problem = workloads.Problem(problem.name + "_w2", "int2", W2, problem.X, dict(problem.meta))
+    enc = bsp.encode(W2, dtype=bsp.INT2)
+    dm0 = enc.to_device(dev)
+    Xd = torch.from_numpy(bsp.pack_int4(problem.X)).to(dev)
+    algo = {"auto": bsp.ALGO_AUTO, "rowwave": bsp.ALGO_ROWWAVE, "mfma": bsp.ALGO_MFMA}[args.algo]
+    per_copy = dm0.stream_bytes() + Xd.numel() + 4 * M * N
+    R = args.steps + max(1, -(-FLUSH_BYTES // per_copy))
+    copies = [(dm0, Xd, torch.empty((N, M), dtype=torch.int32, device=dev))]
+    for _ in range(R - 1):
+        dm = bsp.DeviceMatrix(enc.dtype, M, K, enc.nnz, dm0.bitmaps.clone(), dm0.offsets.clone(), dm0.payload.clone())
+        copies.append((dm, Xd.clone(), torch.empty((N, M), dtype=torch.int32, device=dev)))
+    torch.cuda.synchronize()
+
+    def step(i):
+        dm, x, y = copies[i % R]
+        bsp.spmm_w2a4(dm, x, N, Y=y, algo=algo)
+
+    kernel = "k_rowwave_w4a4" if algo == bsp.ALGO_ROWWAVE or K > 4096 else "k_bt64s_w2a4"
+    nbytes = dm0.stream_bytes(with_offsets=False) + 4 * offsets_read(kernel, M, dm0.T) + N * ((K + 1) // 2) + 4 * M * N
+    return dict(problem=problem, fp16=False, enc=enc, dm0=dm0, copies=copies, R=R, step=step, chosen=algo,
+                name="w2a4", kernel=kernel, dt=bsp.INT2, plan="w2a4", nbytes=nbytes)
 
 
 def _prepare_parts(args, bsp, problem, dev):
@@ -779,10 +814,11 @@ def measure(args, workload, index, n, with_probe=True):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16 x f16 -> f32 acc -> f16" if fp16 else "int4 x int4 -> int32",
+        "dtype": "f16 x f16 -> f32 acc -> f16" if fp16 else
+                 ("int2 x int4 -> int32" if problem.dtype == "int2" else "int4 x int4 -> int32"),
         "data": "synthetic (seeded iid unstructured mask / magnitude pruning; the pages' model weights "
                 "are not available)",
-        "config": {"workload": f"{wl}: W {M}x{K} {'fp16' if fp16 else 'int4'}, density {density:.3f}, N={N}",
+        "config": {"workload": f"{wl}: W {M}x{K} {'fp16' if fp16 else problem.dtype}, density {density:.3f}, N={N}",
                    "M": M, "K": K, "N": N, "nnz": enc.nnz, "kernel": algo_label(kernel),
                    "rotated_copies": R, "bytes_per_step": nbytes},
         "frac_of_peak": round(value / HBM_PEAK_GBS, 4),
@@ -837,6 +873,7 @@ def main():
     ap.add_argument("--format", default="bt64", choices=["bt64", "union"],
                     help="weight format: BT64 (1x64 tiles) or the union mask (2x2 areas of 16x64 tiles)")
     ap.add_argument("--no-reorder", action="store_true", help="union format without row reordering")
+    ap.add_argument("--wbits", type=int, default=4, choices=[4, 2], help="2: W2A4 (2-bit weights) on the shape")
     ap.add_argument("--parts", type=int, default=0, help="cut W's rows into this many matrices: one grouped launch")
     ap.add_argument("--separate", action="store_true", help="with --parts: one call per part instead")
     ap.add_argument("--epilogue", default="int32", choices=["int32", "dq"],

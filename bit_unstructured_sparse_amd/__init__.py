@@ -41,7 +41,8 @@ EXPORTS = ["encode_bitmap_tiles", "pack_int4_activations", "spmm_bitmap_w4a4", "
            "bsp_workspace_bytes", "bsp_select", "bsp_describe_selection", "bsp_describe_selection_ws",
            "bsp_status_string", "bsp_version", "spmm_bitmap_f16_noalloc", "bsp_noalloc_scratch_bytes",
            "union_tile_count", "union_mask_words", "encode_union_tiles", "spmm_union_w4a4",
-           "spmm_bitmap_w4a4_dq", "spmm_bitmap_w4a4_grouped", "spmm_bitmap_w2a4", "spmm_bitmap_w2a4_algo"]
+           "spmm_bitmap_w4a4_dq", "spmm_bitmap_w4a4_grouped", "spmm_bitmap_w2a4", "spmm_bitmap_w2a4_algo",
+           "cbc_gtile_count", "encode_cbc_f16", "spmspv_cbc_workspace_bytes", "spmspv_cbc_f16"]
 
 
 class BspError(RuntimeError):
@@ -102,6 +103,12 @@ def load_library():
         L.spmm_bitmap_w2a4.restype = I32
         L.spmm_bitmap_w2a4_algo.argtypes = [P, P, P, I64, I64, I64, P, I64, P, I32, P]
         L.spmm_bitmap_w2a4_algo.restype = I32
+        L.cbc_gtile_count.argtypes, L.cbc_gtile_count.restype = [I64, I64], I64
+        L.encode_cbc_f16.argtypes = [P, I64, I64, I64, P, P, P, P, I64, P]
+        L.encode_cbc_f16.restype = I32
+        L.spmspv_cbc_workspace_bytes.argtypes, L.spmspv_cbc_workspace_bytes.restype = [I64, I64, I64, P], I32
+        L.spmspv_cbc_f16.argtypes = [P, P, P, P, I64, I64, I64, P, I64, ctypes.c_float, P, P, I64, P]
+        L.spmspv_cbc_f16.restype = I32
         _lib = L
     return _lib
 
@@ -378,6 +385,105 @@ def spmm_bitmap_w4a4_grouped(items, stream=None):
                                                  _stream_handle(stream))
     _check(rc, "spmm_bitmap_w4a4_grouped")
     return outs
+
+
+# ---- Tiled-CBC format with dynamic activation pruning (fp16) ----
+
+CBC_TILE = (256, 64)
+CBC_MAX_N = 8
+
+
+@dataclass
+class CbcEncoded:
+    """Host-side Tiled-CBC stream: tile_offsets uint32[n_gt + 1], colinfo
+    uint32[n_gt * 64], bitmaps uint64[n_gt * 256], values fp16 bits [nnz]."""
+    M: int
+    K: int
+    nnz: int
+    tile_offsets: np.ndarray
+    colinfo: np.ndarray
+    bitmaps: np.ndarray
+    values: np.ndarray
+
+    def storage_bytes(self) -> int:
+        return int(self.tile_offsets.nbytes + self.colinfo.nbytes + self.bitmaps.nbytes + self.values.nbytes)
+
+    def to_device(self, device="cuda") -> "CbcDevice":
+        import torch
+        vb = self.values.nbytes
+        raw = np.zeros(max(PAYLOAD_ALIGN, vb + (-vb) % PAYLOAD_ALIGN), np.uint8)
+        raw[:vb] = self.values.view(np.uint8)
+        return CbcDevice(self.M, self.K, self.nnz,
+                         torch.from_numpy(self.tile_offsets.view(np.int32)).to(device),
+                         torch.from_numpy(self.colinfo.view(np.int32)).to(device),
+                         torch.from_numpy(self.bitmaps.view(np.int64)).to(device),
+                         torch.from_numpy(raw).to(device))
+
+
+@dataclass
+class CbcDevice:
+    M: int
+    K: int
+    nnz: int
+    tile_offsets: "object"
+    colinfo: "object"
+    bitmaps: "object"
+    values: "object"       # uint8, padded to PAYLOAD_ALIGN
+
+
+def cbc_gtile_count(M: int, K: int) -> int:
+    return int(load_library().cbc_gtile_count(M, K))
+
+
+def encode_cbc_f16(W: np.ndarray) -> CbcEncoded:
+    L = load_library()
+    W = np.ascontiguousarray(W)
+    if W.dtype == np.float16:
+        W = W.view(np.uint16)
+    if W.dtype != np.uint16 or W.ndim != 2:
+        raise TypeError("W must be a 2-D float16 (or uint16 bits) array")
+    M, K = W.shape
+    nnz = ctypes.c_int64(0)
+    _check(L.encode_cbc_f16(_np_ptr(W), M, K, K, None, None, None, None, 0, ctypes.byref(nnz)), "encode_cbc_f16 (size)")
+    ngt = cbc_gtile_count(M, K)
+    to = np.zeros(ngt + 1, np.uint32)
+    ci = np.zeros(ngt * 64, np.uint32)
+    bm = np.zeros(ngt * 256, np.uint64)
+    vals = np.zeros(nnz.value, np.uint16)
+    _check(L.encode_cbc_f16(_np_ptr(W), M, K, K, _np_ptr(to), _np_ptr(ci), _np_ptr(bm), _np_ptr(vals), vals.size,
+                            ctypes.byref(nnz)), "encode_cbc_f16")
+    return CbcEncoded(M, K, int(nnz.value), to, ci, bm, vals)
+
+
+def spmspv_cbc_workspace_bytes(M: int, K: int, N: int) -> int:
+    b = ctypes.c_int64(0)
+    _check(load_library().spmspv_cbc_workspace_bytes(M, K, N, ctypes.byref(b)), "spmspv_cbc_workspace_bytes")
+    return int(b.value)
+
+
+def new_cbc_workspace(M: int, K: int, N: int, device="cuda"):
+    import torch
+    n = spmspv_cbc_workspace_bytes(M, K, N)
+    return torch.zeros(max(n, 256), dtype=torch.uint8, device=device) if n else None
+
+
+def spmspv_cbc_f16(D: CbcDevice, X, threshold: float, Y=None, workspace=None, stream=None):
+    """fp16 Y [N][M] = W X' with X' = X where |x| > threshold, else 0 (dynamic
+    activation pruning; the all-pruned columns of W are not read)."""
+    import torch
+    if X.dim() != 2 or X.shape[1] != D.K:
+        raise ValueError("X must be [N][K]")
+    N = int(X.shape[0])
+    _check_dev(X, "X", torch.float16)
+    if Y is None:
+        Y = torch.empty((N, D.M), dtype=torch.float16, device=X.device)
+    _check_dev(Y, "Y", torch.float16, N * D.M)
+    wp, wb = _ws_args(workspace)
+    rc = load_library().spmspv_cbc_f16(
+        _dptr(D.tile_offsets), _dptr(D.colinfo), _dptr(D.bitmaps), _dptr(D.values), D.values.numel(), D.M, D.K,
+        _dptr(X), N, ctypes.c_float(threshold), _dptr(Y), wp, wb, _stream_handle(stream))
+    _check(rc, "spmspv_cbc_f16")
+    return Y
 
 
 # ---- union-mask (IE-BME) format: 16 x 64 local tiles, ra x ca areas ----

@@ -3,7 +3,8 @@ in this directory with hipcc for gfx950.
 
     python -m bit_unstructured_sparse_amd.build
 
-One shared library holds the host encoders (encode.cpp, encode_union.cpp) and every HIP kernel
+One shared library holds the host encoders (encode.cpp, encode_union.cpp,
+encode_cbc.cpp) and every HIP kernel
 (spmm.hip with its kernels_*.hip includes). The probe (probe_read.hip) is a
 measurement aid the benchmark loads; the SpMM library does not contain it.
 Packed-fp32 VALU forms are switched off for the device pass; hipcc's host
@@ -23,7 +24,8 @@ PROBE_LIB = os.path.join(HERE, "libbsp_probe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = [os.path.join(CSRC, "spmm.hip"), os.path.join(CSRC, "encode.cpp"), os.path.join(CSRC, "encode_union.cpp")]
+SOURCES = [os.path.join(CSRC, "spmm.hip"), os.path.join(CSRC, "encode.cpp"), os.path.join(CSRC, "encode_union.cpp"),
+           os.path.join(CSRC, "encode_cbc.cpp")]
 PROBE_SOURCES = [os.path.join(CSRC, "probe_read.hip")]
 
 

@@ -22,6 +22,7 @@
 #include "kernels_bt64_f16.hip"
 #include "kernels_splitk.hip"
 #include "kernels_union.hip"
+#include "kernels_cbc.hip"
 
 namespace {
 
@@ -426,6 +427,10 @@ extern "C" int spmm_union_w4a4(const uint64_t *ubitmaps, const uint32_t *offsets
 // ---------------------------------------------------------------------------
 // Dequant epilogue and grouped launch (int4 MFMA kernels).
 
+__global__ void k_f16_zero(uint16_t *__restrict__ Y, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) Y[i] = 0;
+}
+
 __global__ void k_dq_zero(uint16_t *__restrict__ Yh, const float *__restrict__ sw, const float *__restrict__ sx,
                           int64_t M, int64_t N) {
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < M * N; i += (int64_t)gridDim.x * blockDim.x)
@@ -575,4 +580,49 @@ extern "C" int spmm_bitmap_w2a4(const uint64_t *bitmaps, const uint32_t *offsets
                                 int64_t payload_bytes, int64_t M, int64_t K, const uint8_t *X, int64_t N, int32_t *Y,
                                 hipStream_t stream) {
     return spmm_bitmap_w2a4_algo(bitmaps, offsets, payload, payload_bytes, M, K, X, N, Y, BSP_ALGO_AUTO, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Tiled-CBC product with dynamic activation pruning (fp16).
+extern "C" int spmspv_cbc_workspace_bytes(int64_t M, int64_t K, int64_t N, int64_t *bytes) {
+    if (bytes == nullptr || M < 0 || K < 0 || N < 0 || N > BSP_CBC_MAX_N) return BSP_E_ARG;
+    *bytes = (M == 0 || K == 0 || N == 0) ? 0 : cbc_plan(M, K, N, true).ws_bytes;
+    return BSP_OK;
+}
+
+extern "C" int spmspv_cbc_f16(const uint32_t *tile_offsets, const uint32_t *colinfo, const uint64_t *bitmaps,
+                              const uint16_t *values, int64_t values_bytes, int64_t M, int64_t K, const uint16_t *X,
+                              int64_t N, float threshold, uint16_t *Y, void *workspace, int64_t workspace_bytes,
+                              hipStream_t stream) {
+    if (M < 0 || K < 0 || N < 0 || N > BSP_CBC_MAX_N || values_bytes < 0 || workspace_bytes < 0) return BSP_E_ARG;
+    if (!(threshold >= 0.f) || std::isinf(threshold)) return BSP_E_ARG;     // NaN, negative or infinite
+    if (values_bytes % BSP_PAYLOAD_ALIGN != 0) return BSP_E_ARG;
+    if (values_bytes > UINT32_MAX || M > INT32_MAX || K > INT32_MAX) return BSP_E_OVERFLOW;
+    if (workspace == nullptr && workspace_bytes != 0) return BSP_E_ARG;
+    if (workspace != nullptr && ((uintptr_t)workspace & 255u) != 0) return BSP_E_ARG;
+    if (M == 0 || N == 0) return BSP_OK;
+    if (Y == nullptr || tile_offsets == nullptr) return BSP_E_ARG;
+    if (K > 0 && (colinfo == nullptr || bitmaps == nullptr || X == nullptr)) return BSP_E_ARG;
+    if (values == nullptr && values_bytes != 0) return BSP_E_ARG;
+    if (cbc_gtile_count(M, K) * BSP_CBC_TILE_K * (BSP_CBC_TILE_M / 64) * 8 > (int64_t)INT32_MAX * 4) return BSP_E_OVERFLOW;
+    if (K == 0) {
+        const int64_t n = M * N;
+        hipLaunchKernelGGL(k_f16_zero, dim3((unsigned)std::min<int64_t>((n + 255) / 256, 1024)), dim3(256), 0, stream,
+                           Y, n);
+        return launch_status();
+    }
+    const bool split = workspace != nullptr && workspace_bytes > 0;
+    const CbcPlan p = cbc_plan(M, K, N, split);
+    if (p.ws_bytes > workspace_bytes) return BSP_E_CAPACITY;
+    float *part = p.S > 1 ? (float *)((uint8_t *)workspace + CBC_WS_COUNTERS) : nullptr;
+    uint32_t *cnt = p.S > 1 ? (uint32_t *)workspace : nullptr;
+    const unsigned grid = (unsigned)((int64_t)p.bands * p.S);
+    if (N == 1)
+        hipLaunchKernelGGL(k_cbc_f16<1>, dim3(grid), dim3(256), 0, stream, tile_offsets, colinfo, bitmaps, values,
+                           (uint32_t)values_bytes, (int)M, (int)K, X, (int)N, threshold, Y, part, cnt, p.S, p.G);
+    else
+        hipLaunchKernelGGL(k_cbc_f16<CBC_NMAX>, dim3(grid), dim3(256), 0, stream, tile_offsets, colinfo, bitmaps,
+                           values, (uint32_t)values_bytes, (int)M, (int)K, X, (int)N, threshold, Y, part, cnt, p.S,
+                           p.G);
+    return launch_status();
 }

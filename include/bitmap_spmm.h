@@ -401,6 +401,62 @@ int spmm_union_w4a4(const uint64_t *ubitmaps, const uint32_t *offsets, const uin
                     const uint8_t *payload, int64_t payload_bytes, int ra, int ca, int64_t M, int64_t K,
                     const uint8_t *X, int64_t N, int32_t *Y, hipStream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * Tiled-CBC format and dynamic activation pruning (SPDP, Sec. 4.1 "Tiled-CBC",
+ * Fig. 4(a); Sec. 4.2, the decode-phase spMspV kernel).
+ *   GTiles of BSP_CBC_TILE_M x BSP_CBC_TILE_K (256 x 64) in row-major order
+ *   over the matrix (n_gt = cbc_gtile_count(M, K); zero-padded past M and K).
+ *   tile_offsets[g]   uint32, GTile g's first value; n_gt+1 entries, the last NNZ.
+ *   colinfo[g*64 + c] uint32, (first value of column c inside the GTile << 16)
+ *                     | (nonzeros of column c).
+ *   bitmaps[(g*64 + c)*4 + w]  uint64: bit j is row 64w+j of column c.
+ *   values            fp16 bits: GTile by GTile, column by column, rows ascending.
+ * Storage: 4(n_gt+1) + 4 n_gt 64 + 8 (n_gt 64 4) + 2 NNZ bytes.
+ * --------------------------------------------------------------------------- */
+#define BSP_CBC_TILE_M 256
+#define BSP_CBC_TILE_K 64
+/* Largest N of spmspv_cbc_f16 (decode widths). */
+#define BSP_CBC_MAX_N 8
+
+/* GTiles of an M x K matrix; -1 for negative sizes. */
+int64_t cbc_gtile_count(int64_t M, int64_t K);
+
+/*
+ * encode_cbc_f16 -- host-side Tiled-CBC encoder. W: HOST uint16 (fp16 bits)
+ * [M][ldw]; +0 and -0 are zero. tile_offsets/colinfo/bitmaps: HOST arrays of
+ * n_gt+1, n_gt*64 and n_gt*256 entries, all NULL for a size query; values:
+ * HOST, values_capacity elements (>= NNZ), or NULL. nnz_out written on BSP_OK,
+ * BSP_E_CAPACITY and BSP_E_OVERFLOW (NNZ >= 2^32).
+ */
+int encode_cbc_f16(const uint16_t *W, int64_t M, int64_t K, int64_t ldw, uint32_t *tile_offsets,
+                   uint32_t *colinfo, uint64_t *bitmaps, uint16_t *values, int64_t values_capacity,
+                   int64_t *nnz_out);
+
+/* Workspace bytes spmspv_cbc_f16 uses to split K over workgroups (0: none). */
+int spmspv_cbc_workspace_bytes(int64_t M, int64_t K, int64_t N, int64_t *bytes);
+
+/*
+ * spmspv_cbc_f16 -- Y = W * X' on `stream`, X' = X with every activation of
+ * magnitude <= threshold set to zero (dynamic pruning); the columns of W
+ * whose activations are all pruned are not read. fp32 products and sums, one
+ * round to nearest even to fp16.
+ *   tile_offsets, colinfo, bitmaps, values  DEVICE, as encode_cbc_f16 wrote
+ *            them; values_bytes: the values allocation, a multiple of
+ *            BSP_PAYLOAD_ALIGN, zero past the encoded values.
+ *   X        DEVICE fp16 [N][K]; N 0..BSP_CBC_MAX_N.
+ *   threshold  fp32, finite, >= 0 (0: the plain product); compared with |x| in fp32.
+ *   Y        DEVICE fp16 [N][M], fully overwritten (K == 0 gives zeros).
+ *   workspace  DEVICE, NULL (one workgroup per 256-row band) or
+ *            spmspv_cbc_workspace_bytes() bytes, 256-byte aligned, zero-filled
+ *            before its first use (its first 64 KiB are arrival counters,
+ *            left zero by every call); calls that share a workspace must be
+ *            ordered on one stream. Too small: BSP_E_CAPACITY.
+ */
+int spmspv_cbc_f16(const uint32_t *tile_offsets, const uint32_t *colinfo, const uint64_t *bitmaps,
+                   const uint16_t *values, int64_t values_bytes, int64_t M, int64_t K, const uint16_t *X,
+                   int64_t N, float threshold, uint16_t *Y, void *workspace, int64_t workspace_bytes,
+                   hipStream_t stream);
+
 /* Static string for a bsp_status code. */
 const char *bsp_status_string(int status);
 

@@ -515,6 +515,8 @@ def prepare(args, workload, index, n):
     N, M, K = problem.N, problem.M, problem.K
     if getattr(args, "format", "bt64") == "union":
         return _prepare_union(args, bsp, problem, dev)
+    if getattr(args, "format", "bt64") == "cbc":
+        return _prepare_cbc(args, bsp, problem, dev)
     if getattr(args, "parts", 0) or getattr(args, "epilogue", "int32") == "dq":
         return _prepare_parts(args, bsp, problem, dev)
     if getattr(args, "wbits", 4) == 2:
@@ -601,6 +603,54 @@ def _prepare_union(args, bsp, problem, dev):
                 union={"nvals": ue.nvals, "reorder": not args.no_reorder, "encode_seconds": round(enc_s, 3),
                        "stream_bytes": ue.stream_bytes(), "payload_bytes": int(ue.payload.nbytes),
                        "value_fill": round(ue.nvals / max(1, 4 * nnz), 4)})
+
+
+def _prepare_cbc(args, bsp, problem, dev):
+    """prepare() for the Tiled-CBC product with dynamic activation pruning
+    (fp16): the threshold is the --dyn-sparsity quantile of |x|, so that
+    fraction of the activations (and, at N = 1, of W's columns) is pruned."""
+    import numpy as np
+    import torch
+    if problem.dtype != "fp16":
+        raise SystemExit("the Tiled-CBC path is fp16")
+    N, M, K = problem.N, problem.M, problem.K
+    q = args.dyn_sparsity
+    tau = float(np.quantile(np.abs(problem.X.astype(np.float32)), q)) if q > 0 else 0.0
+    enc = bsp.encode_cbc_f16(problem.W)
+    d0 = enc.to_device(dev)
+    Xd = torch.from_numpy(problem.X.copy()).to(dev)
+    ws = bsp.new_cbc_workspace(M, K, N, device=dev)
+    per_copy = enc.storage_bytes() + Xd.numel() * 2 + 2 * M * N
+    R = args.steps + max(1, -(-FLUSH_BYTES // per_copy))
+    copies = [(d0, Xd, torch.empty((N, M), dtype=torch.float16, device=dev))]
+    for _ in range(R - 1):
+        d = bsp.CbcDevice(M, K, enc.nnz, d0.tile_offsets.clone(), d0.colinfo.clone(), d0.bitmaps.clone(),
+                          d0.values.clone())
+        copies.append((d, Xd.clone(), torch.empty((N, M), dtype=torch.float16, device=dev)))
+    torch.cuda.synchronize()
+
+    def step(i):
+        d, x, y = copies[i % R]
+        bsp.spmspv_cbc_f16(d, x, tau, Y=y, workspace=ws)
+
+    # algorithmic bytes: for every column with an activation kept, its bitmap
+    # words, ColInfo and values; every GTile offset; X and Y
+    kept = np.abs(problem.X.astype(np.float32)) > np.float32(tau)       # the kernel's rule: |x| > tau
+    active = kept.any(axis=0)
+    kept_nnz = int(np.count_nonzero(problem.W[:, active]))
+    bands = (M + 255) // 256
+    nbytes = (4 * (enc.tile_offsets.size) + bands * int(active.sum()) * (4 + 32) + 2 * kept_nnz +
+              2 * N * K + 2 * N * M)
+
+    class _Enc:
+        pass
+    e = _Enc()
+    e.nnz = enc.nnz
+    return dict(problem=problem, fp16=True, enc=e, dm0=None, copies=copies, R=R, step=step, chosen=None,
+                name="cbc", kernel="k_cbc_f16", dt=bsp.FP16, plan="tiled-cbc", nbytes=nbytes,
+                cbc={"threshold": tau, "dyn_sparsity": q, "active_columns": int(active.sum()),
+                     "kept_nnz": kept_nnz, "storage_bytes": enc.storage_bytes()},
+                ref_mask=kept)
 
 
 def _prepare_w2(args, bsp, problem, dev):
@@ -745,7 +795,10 @@ def measure(args, workload, index, n, with_probe=True):
             return bool(np.array_equal(got, ref))
         got = copies[i][2].cpu().numpy()[:, rows]
         if fp16:
-            ref = (problem.W[rows].astype(np.float64) @ problem.X.astype(np.float64).T).T
+            Xr = problem.X
+            if "ref_mask" in ctx:
+                Xr = np.where(ctx["ref_mask"], problem.X, np.float16(0))
+            ref = (problem.W[rows].astype(np.float64) @ Xr.astype(np.float64).T).T
             floor = 0.01 * np.sqrt(np.mean(ref ** 2))
             err = np.abs(got.astype(np.float64) - ref) / np.maximum(np.abs(ref), floor)
             return bool(np.max(err) <= 1e-2)
@@ -785,6 +838,7 @@ def measure(args, workload, index, n, with_probe=True):
     nbytes = ctx["nbytes"] if "nbytes" in ctx else step_bytes(dm0, N, kernel, fp16, ctx["plan"])
     union_info = ctx.get("union")
     ctx_parts = ctx.get("parts")
+    cbc_info = ctx.get("cbc")
     value = nbytes / (ms_per_step * 1e-3) / 1e9
     achieved = nbytes / (kern_ms * 1e-3) / 1e9
     dense_ops = 2.0 * M * K * N
@@ -831,6 +885,9 @@ def measure(args, workload, index, n, with_probe=True):
         "roofline": roof,
         "parity_sample_ok": parity,
     }
+    if cbc_info is not None:
+        out["config"]["format"] = "Tiled-CBC (256 x 64 GTiles), dynamic activation pruning"
+        out["cbc"] = cbc_info
     if ctx_parts is not None:
         out["config"]["grouping"] = ctx_parts
     if union_info is not None:
@@ -870,9 +927,12 @@ def main():
     ap.add_argument("--n", type=int, default=0, help="override N (slices the workload's widest X)")
     ap.add_argument("--algo", default="auto", choices=["auto", "rowwave", "mfma", "splitk"])
     ap.add_argument("--workspace", action="store_true", help="call the *_ws entry point with a workspace")
-    ap.add_argument("--format", default="bt64", choices=["bt64", "union"],
-                    help="weight format: BT64 (1x64 tiles) or the union mask (2x2 areas of 16x64 tiles)")
+    ap.add_argument("--format", default="bt64", choices=["bt64", "union", "cbc"],
+                    help="weight format: BT64 (1x64 tiles), the union mask (2x2 areas of 16x64 tiles) or Tiled-CBC "
+                         "(fp16, dynamic activation pruning)")
     ap.add_argument("--no-reorder", action="store_true", help="union format without row reordering")
+    ap.add_argument("--dyn-sparsity", type=float, default=0.5,
+                    help="--format cbc: fraction of activations pruned (the threshold is that quantile of |x|)")
     ap.add_argument("--wbits", type=int, default=4, choices=[4, 2], help="2: W2A4 (2-bit weights) on the shape")
     ap.add_argument("--parts", type=int, default=0, help="cut W's rows into this many matrices: one grouped launch")
     ap.add_argument("--separate", action="store_true", help="with --parts: one call per part instead")

@@ -3,53 +3,61 @@
 // and Sec. 4.2 (the spMspV kernel and its HAD-SMBD decoding).
 //
 // Y[n][m] = sum over k of W[m][k] * x'[n][k], x' = x where |x| > tau, else 0.
-// A column k whose activations are all pruned is skipped: its bitmap words
-// and values are never read, which is where dynamic pruning saves bytes.
+// A column k whose activations are all pruned is skipped: its values are
+// never read, which is where dynamic pruning saves bytes.
 //
 // Work split. Rows go in bands of 256 (one column tile of a GTile); a
-// workgroup of 4 wavefronts takes one band and a segment of G consecutive
-// GTiles (G x 64 columns); wavefront w owns rows 64 w .. 64 w + 63 of the
-// band, one per lane (the column-major, CUDA-core style register layout of
-// HAD-SMBD: one output row per thread, one column at a time).
+// workgroup of 16 wavefronts takes one band and a segment of G consecutive
+// GTiles: its 4 column groups of 4 wavefronts take GTiles of the segment in
+// turn, and wavefront r of a group owns rows 64 r .. 64 r + 63 of the band,
+// one per lane (the column-major, CUDA-core style register layout of
+// HAD-SMBD: one output row per thread, one column at a time). The groups'
+// partials are added in LDS, in group order.
 //
-// A workgroup first stages its segment of X, applies the threshold and
-// builds the list of active columns in LDS (ballot and prefix count). Then,
-// for each active column, every wavefront reads the column's four bitmap
-// words, its ColInfo and its GTile's offset with scalar loads (one address
-// for the whole wavefront), finds its lane's rank with a masked popcount
-// (v_mbcnt over its own word plus the set bits of the words of the lower
-// wavefronts) and gathers its value (lanes whose bit is clear read zero
-// through the buffer range check), and accumulates value x x' in fp32.
-// Eight columns are unrolled so that their loads are in flight together.
+// A wavefront takes its quarter of a GTile in two memory round trips, with
+// no LDS and no barrier: (1) lane c loads column c's ColInfo, its four
+// bitmap words and its N activations (the threshold applied), and the
+// wavefront keeps, in lane c, the column's word for its own 64 rows and the
+// position of that word's first value (GTile offset + column offset + the
+// set bits of the words above); a ballot marks the columns that are active
+// and hold a nonzero in these rows (the others are skipped, values unread);
+// (2) for up to 32 of those columns at a time the wavefront reads each
+// column's word and position out of its lane (readlane: uniform values), and
+// every lane finds its rank with v_mbcnt and gathers its value (a lane whose
+// bit is clear reads zero through the buffer range check); then it
+// accumulates value x x' in fp32.
 //
 // Segments of one band meet through a workspace: each workgroup posts its
 // fp32 partials, and the last of the band's workgroups to arrive (an
 // agent-scope counter) adds the segments in segment order (so the result
 // does not depend on timing) and writes Y in fp16 (round to nearest even).
-// Without a workspace one workgroup covers the whole band, CBC_SEG_MAX
+// Without a workspace one workgroup covers the whole band, CBC_GROUPS
 // GTiles at a time.
 
 #define CBC_TM BSP_CBC_TILE_M                 // 256
 #define CBC_TK BSP_CBC_TILE_K                 // 64
-#define CBC_SEG_MAX 4                         // GTiles per segment, at most
-#define CBC_UNROLL 8
+#define CBC_GROUPS 4                          // column groups per workgroup, one GTile each at a time
+#define CBC_UNROLL 32                         // columns whose gathers are in flight at once
 #define CBC_NMAX 8
 #define CBC_WS_COUNTERS 65536                 // bytes of arrival counters at the workspace's start
 #define CBC_OOR 0xFFFFFFF0u
 
+__device__ __forceinline__ float cbc_readlane_f(float v, int l) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
 template <int NMAX>
-__global__ __launch_bounds__(256) void k_cbc_f16(const uint32_t *__restrict__ tile_offsets,
-                                                 const uint32_t *__restrict__ colinfo,
-                                                 const uint64_t *__restrict__ bitmaps,
-                                                 const uint16_t *__restrict__ values, uint32_t values_bytes, int M,
-                                                 int K, const uint16_t *__restrict__ X, int N, float tau,
-                                                 uint16_t *__restrict__ Y, float *ws_part, uint32_t *ws_cnt, int S,
-                                                 int G) {
-    __shared__ float xs[NMAX][CBC_SEG_MAX * CBC_TK];
-    __shared__ uint16_t list[CBC_SEG_MAX * CBC_TK];
-    __shared__ int wcount[4];
+__global__ __launch_bounds__(1024) void k_cbc_f16(const uint32_t *__restrict__ tile_offsets,
+                                                  const uint32_t *__restrict__ colinfo,
+                                                  const uint64_t *__restrict__ bitmaps,
+                                                  const uint16_t *__restrict__ values, uint32_t values_bytes, int M,
+                                                  int K, const uint16_t *__restrict__ X, int N, float tau,
+                                                  uint16_t *__restrict__ Y, float *ws_part, uint32_t *ws_cnt, int S,
+                                                  int G) {
+    __shared__ float part[CBC_GROUPS][NMAX][CBC_TM];
     __shared__ int flag;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int rq = wave & 3, grp = wave >> 2;              // row quarter, column group
     const int gcols = (K + CBC_TK - 1) / CBC_TK;
     const int band = (int)blockIdx.x / S, seg = (int)blockIdx.x % S;
     const int gc0 = seg * G, gc1 = min(gcols, gc0 + G);
@@ -59,128 +67,145 @@ __global__ __launch_bounds__(256) void k_cbc_f16(const uint32_t *__restrict__ ti
 #pragma unroll
     for (int n = 0; n < NMAX; ++n) acc[n] = 0.f;
 
-    // the segment in chunks of up to CBC_SEG_MAX GTiles
-    for (int cg = gc0; cg < gc1; cg += CBC_SEG_MAX) {
-        const int k0 = cg * CBC_TK, k1 = min(K, min(gc1, cg + CBC_SEG_MAX) * CBC_TK);
-        const int ncols = max(0, k1 - k0);
-        if (cg > gc0) __syncthreads();              // the previous chunk's list and X are read
-
-        // (1) X of the chunk, thresholded; the active columns
-        const int t = threadIdx.x;
+    // group grp takes GTiles gc0 + grp, gc0 + grp + CBC_GROUPS, ...
+    for (int gcol = gc0 + grp; gcol < gc1; gcol += CBC_GROUPS) {
+        const int k = gcol * CBC_TK + lane;
+        const int64_t g = gbase + gcol;
+        // (1) lane = column of the GTile
+        uint64_t mine = 0;
+        uint32_t pos = 0;
+        float xv[NMAX];
         bool act = false;
-        if (t < ncols) {
 #pragma unroll
-            for (int n = 0; n < NMAX; ++n) {
-                float x = 0.f;
+        for (int n = 0; n < NMAX; ++n) xv[n] = 0.f;
+        if (k < K) {
+            const uint64_t *bw = bitmaps + (g * CBC_TK + lane) * (CBC_TM / 64);
+            const uint64_t w0 = bw[0], w1 = bw[1], w2 = bw[2], w3 = bw[3];
+            const uint32_t ci = colinfo[g * CBC_TK + lane];
+            const uint32_t to = tile_offsets[g];
+#pragma unroll
+            for (int n = 0; n < NMAX; ++n)
                 if (n < N) {
-                    x = bsp_h2f(X[(int64_t)n * K + k0 + t]);
-                    x = fabsf(x) > tau ? x : 0.f;
-                    act = act || x != 0.f;
+                    const float x = bsp_h2f(X[(int64_t)n * K + k]);
+                    xv[n] = fabsf(x) > tau ? x : 0.f;
+                    act = act || xv[n] != 0.f;
                 }
-                xs[n][t] = x;
-            }
+            mine = rq == 0 ? w0 : rq == 1 ? w1 : rq == 2 ? w2 : w3;
+            pos = to + (ci >> 16) + (rq > 0 ? (uint32_t)__builtin_popcountll(w0) : 0u) +
+                  (rq > 1 ? (uint32_t)__builtin_popcountll(w1) : 0u) +
+                  (rq > 2 ? (uint32_t)__builtin_popcountll(w2) : 0u);
         }
-        const uint64_t bal = __ballot(act);
-        if (lane == 0) wcount[wave] = __builtin_popcountll(bal);
-        __syncthreads();
-        int before = 0, nact = 0;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            before += w < wave ? wcount[w] : 0;
-            nact += wcount[w];
-        }
-        if (act) {
-            const uint32_t below =
-                    __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
-            list[before + (int)below] = (uint16_t)t;
-        }
-        __syncthreads();
+        uint64_t todo = __ballot(act && mine != 0);
+        const uint32_t mlo = (uint32_t)mine, mhi = (uint32_t)(mine >> 32);
 
-        // (2) the active columns, CBC_UNROLL at a time
-        for (int i0 = 0; i0 < nact; i0 += CBC_UNROLL) {
+        // (2) CBC_UNROLL columns' gathers in flight at a time
+        while (todo != 0) {
             uint32_t vpos[CBC_UNROLL];
-            int col[CBC_UNROLL];
+            int src[CBC_UNROLL];
+            bool ok[CBC_UNROLL];
 #pragma unroll
             for (int u = 0; u < CBC_UNROLL; ++u) {
-                const int i = min(i0 + u, nact - 1);
-                const int c = __builtin_amdgcn_readfirstlane(list[i]);
-                col[u] = c;
-                const int k = k0 + c;
-                const int64_t g = gbase + (k >> 6);
-                const int64_t cc = g * CBC_TK + (k & 63);
-                const uint64_t *bw = bitmaps + cc * (CBC_TM / 64);
-                const uint64_t w0 = bw[0], w1 = bw[1], w2 = bw[2], w3 = bw[3];
-                const uint32_t ci = colinfo[cc];
-                const uint32_t to = tile_offsets[g];
-                const uint64_t mine = wave == 0 ? w0 : wave == 1 ? w1 : wave == 2 ? w2 : w3;
-                const uint32_t prefix = (wave > 0 ? (uint32_t)__builtin_popcountll(w0) : 0u) +
-                                        (wave > 1 ? (uint32_t)__builtin_popcountll(w1) : 0u) +
-                                        (wave > 2 ? (uint32_t)__builtin_popcountll(w2) : 0u);
-                const uint32_t rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(mine >> 32),
-                                                                __builtin_amdgcn_mbcnt_lo((uint32_t)mine, 0u));
-                const bool bit = ((mine >> lane) & 1ull) != 0 && i0 + u < nact;
-                vpos[u] = bit ? (to + (ci >> 16) + prefix + rank) * 2u : CBC_OOR;
+                ok[u] = todo != 0;
+                const int c = ok[u] ? (int)__builtin_ctzll(todo) : 0;
+                todo &= todo - 1;
+                src[u] = c;
+                const uint64_t w = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)mhi, c) << 32) |
+                                   (uint32_t)__builtin_amdgcn_readlane((int)mlo, c);
+                const uint32_t p = (uint32_t)__builtin_amdgcn_readlane((int)pos, c);
+                const uint32_t rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(w >> 32),
+                                                                __builtin_amdgcn_mbcnt_lo((uint32_t)w, 0u));
+                const bool bit = ok[u] && ((w >> lane) & 1ull) != 0;
+                vpos[u] = bit ? (p + rank) * 2u : CBC_OOR;
             }
             uint32_t hv[CBC_UNROLL];
 #pragma unroll
             for (int u = 0; u < CBC_UNROLL; ++u) hv[u] = __builtin_amdgcn_raw_buffer_load_b16(vrs, vpos[u], 0, 0);
+            // xv is zero for n >= N, so no guard (a branch per column would
+            // wait for each gather in turn)
 #pragma unroll
             for (int u = 0; u < CBC_UNROLL; ++u) {
                 const float w = bsp_h2f((uint16_t)hv[u]);
 #pragma unroll
-                for (int n = 0; n < NMAX; ++n)
-                    if (n < N) acc[n] = fmaf(w, xs[n][col[u]], acc[n]);
+                for (int n = 0; n < NMAX; ++n) {
+                    const float x = cbc_readlane_f(xv[n], src[u]);
+                    acc[n] = fmaf(w, ok[u] ? x : 0.f, acc[n]);
+                }
             }
         }
     }
 
-    // (3) the band's rows
-    const int row = wave * 64 + lane;
+    // the column groups' partials, added in group order by column group 0's
+    // 256 threads (the other wavefronts only take part in the barriers)
+    const int row = rq * 64 + lane;
+    const bool lead = grp == 0;
+#pragma unroll
+    for (int n = 0; n < NMAX; ++n) part[grp][n][row] = acc[n];
+    __syncthreads();
+    if (lead) {
+#pragma unroll
+        for (int n = 0; n < NMAX; ++n) {
+            float v = 0.f;
+#pragma unroll
+            for (int q = 0; q < CBC_GROUPS; ++q) v += part[q][n][row];
+            acc[n] = v;
+        }
+    }
     const int m = band * CBC_TM + row;
     if (S == 1) {
-        if (m < M)
+        if (lead && m < M)
 #pragma unroll
             for (int n = 0; n < NMAX; ++n)
                 if (n < N) Y[(int64_t)n * M + m] = bsp_f2h(acc[n]);
         return;
     }
+    if (lead)
 #pragma unroll
-    for (int n = 0; n < NMAX; ++n)
-        if (n < N) sk_ws_store(ws_part + (((int64_t)band * S + seg) * N + n) * CBC_TM + row, acc[n]);
+        for (int n = 0; n < NMAX; ++n)
+            if (n < N) sk_ws_store(ws_part + (((int64_t)band * S + seg) * N + n) * CBC_TM + row, acc[n]);
     __builtin_amdgcn_s_waitcnt(0);           // this thread's partial stores completed
     __syncthreads();
     if (threadIdx.x == 0)
         flag = (int)__hip_atomic_fetch_add(&ws_cnt[band], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     if (flag != S - 1) return;
-    if (m < M)
+    // the segments' partials, added in segment order; 16 loads in flight at
+    // a time (one after the other, each would wait for the one before)
+    if (lead && m < M)
         for (int n = 0; n < N; ++n) {
+            const float *pp = ws_part + ((int64_t)band * S * N + n) * CBC_TM + row;
+            const int64_t stride = (int64_t)N * CBC_TM;
             float s = 0.f;
-            for (int sp = 0; sp < S; ++sp) s += sk_ws_load(ws_part + (((int64_t)band * S + sp) * N + n) * CBC_TM + row);
+            for (int s0 = 0; s0 < S; s0 += 16) {
+                float v[16];
+#pragma unroll
+                for (int u = 0; u < 16; ++u) v[u] = s0 + u < S ? sk_ws_load(pp + (s0 + u) * stride) : 0.f;
+#pragma unroll
+                for (int u = 0; u < 16; ++u) s += v[u];
+            }
             Y[(int64_t)n * M + m] = bsp_f2h(s);
         }
     if (threadIdx.x == 0) sk_ws_store(&ws_cnt[band], 0u);   // ready for the next call
 }
 
 struct CbcPlan {
-    int bands = 0, S = 1, G = CBC_SEG_MAX;
+    int bands = 0, S = 1, G = CBC_GROUPS;
     int64_t ws_bytes = 0;
 };
 
-// Segments per band: enough workgroups to give every CU four (G >= 1
-// GTile each), when a workspace is given.
+// With a workspace a workgroup takes CBC_GROUPS GTiles of its band (one per
+// column group) and the band's segments meet in the workspace; without one
+// it takes the whole band.
 static CbcPlan cbc_plan(int64_t M, int64_t K, int64_t N, bool split) {
     CbcPlan p;
     p.bands = (int)((M + CBC_TM - 1) / CBC_TM);
     const int64_t gcols = (K + CBC_TK - 1) / CBC_TK;
-    if (!split || gcols <= 1 || p.bands > CBC_WS_COUNTERS / 4) {
+    if (!split || gcols <= CBC_GROUPS || p.bands > CBC_WS_COUNTERS / 4) {
         p.S = 1;
         p.G = (int)std::max<int64_t>(1, gcols);
         return p;
     }
-    int64_t G = std::max<int64_t>(1, std::min<int64_t>(CBC_SEG_MAX, (int64_t)p.bands * gcols / (4 * BT_CUS)));
-    p.G = (int)G;
-    p.S = (int)((gcols + G - 1) / G);
+    p.G = CBC_GROUPS;
+    p.S = (int)((gcols + CBC_GROUPS - 1) / CBC_GROUPS);
     p.ws_bytes = CBC_WS_COUNTERS + (int64_t)p.bands * p.S * N * CBC_TM * 4;
     return p;
 }

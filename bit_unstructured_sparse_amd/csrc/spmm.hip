@@ -618,10 +618,10 @@ extern "C" int spmspv_cbc_f16(const uint32_t *tile_offsets, const uint32_t *coli
     uint32_t *cnt = p.S > 1 ? (uint32_t *)workspace : nullptr;
     const unsigned grid = (unsigned)((int64_t)p.bands * p.S);
     if (N == 1)
-        hipLaunchKernelGGL(k_cbc_f16<1>, dim3(grid), dim3(256), 0, stream, tile_offsets, colinfo, bitmaps, values,
+        hipLaunchKernelGGL(k_cbc_f16<1>, dim3(grid), dim3(1024), 0, stream, tile_offsets, colinfo, bitmaps, values,
                            (uint32_t)values_bytes, (int)M, (int)K, X, (int)N, threshold, Y, part, cnt, p.S, p.G);
     else
-        hipLaunchKernelGGL(k_cbc_f16<CBC_NMAX>, dim3(grid), dim3(256), 0, stream, tile_offsets, colinfo, bitmaps,
+        hipLaunchKernelGGL(k_cbc_f16<CBC_NMAX>, dim3(grid), dim3(1024), 0, stream, tile_offsets, colinfo, bitmaps,
                            values, (uint32_t)values_bytes, (int)M, (int)K, X, (int)N, threshold, Y, part, cnt, p.S,
                            p.G);
     return launch_status();

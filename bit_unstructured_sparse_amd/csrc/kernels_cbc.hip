@@ -23,9 +23,12 @@
 // and hold a nonzero in these rows (the others are skipped, values unread);
 // (2) for up to 32 of those columns at a time the wavefront reads each
 // column's word and position out of its lane (readlane: uniform values), and
-// every lane finds its rank with v_mbcnt and gathers its value (a lane whose
-// bit is clear reads zero through the buffer range check); then it
-// accumulates value x x' in fp32.
+// every lane finds its rank with v_mbcnt and gathers its value (the word
+// itself, as a lane mask, sends a lane whose bit is clear past the buffer's
+// range, where it reads zero); then it accumulates value x x' in fp32, x'
+// read from a per-wavefront LDS copy of the GTile's activations (a broadcast
+// read). A column costs a wavefront about eight vector instructions, which
+// is what bounds this kernel once the values are in flight.
 //
 // Segments of one band meet through a workspace: each workgroup posts its
 // fp32 partials, and the last of the band's workgroups to arrive (an
@@ -42,8 +45,11 @@
 #define CBC_WS_COUNTERS 65536                 // bytes of arrival counters at the workspace's start
 #define CBC_OOR 0xFFFFFFF0u
 
-__device__ __forceinline__ float cbc_readlane_f(float v, int l) {
-    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+// Lane l of the result is a where bit l of the uniform mask m is set, else b.
+__device__ __forceinline__ uint32_t cbc_lane_select(uint64_t m, uint32_t a, uint32_t b) {
+    uint32_t r;
+    asm volatile("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(r) : "v"(b), "v"(a), "s"(m));
+    return r;
 }
 
 template <int NMAX>
@@ -55,6 +61,7 @@ __global__ __launch_bounds__(1024) void k_cbc_f16(const uint32_t *__restrict__ t
                                                   uint16_t *__restrict__ Y, float *ws_part, uint32_t *ws_cnt, int S,
                                                   int G) {
     __shared__ float part[CBC_GROUPS][NMAX][CBC_TM];
+    __shared__ float xsw[CBC_GROUPS * 4][NMAX][CBC_TK + 1];   // per wavefront: x' of the GTile, then a zero
     __shared__ int flag;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int rq = wave & 3, grp = wave >> 2;              // row quarter, column group
@@ -97,41 +104,45 @@ __global__ __launch_bounds__(1024) void k_cbc_f16(const uint32_t *__restrict__ t
         }
         uint64_t todo = __ballot(act && mine != 0);
         const uint32_t mlo = (uint32_t)mine, mhi = (uint32_t)(mine >> 32);
+#pragma unroll
+        for (int n = 0; n < NMAX; ++n) {
+            xsw[wave][n][lane] = xv[n];
+            if (lane == 0) xsw[wave][n][CBC_TK] = 0.f;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-        // (2) CBC_UNROLL columns' gathers in flight at a time
+        // (2) CBC_UNROLL columns' gathers in flight at a time; past the last
+        // column, an empty word and the zero activation
         while (todo != 0) {
-            uint32_t vpos[CBC_UNROLL];
+            uint32_t hv[CBC_UNROLL];
             int src[CBC_UNROLL];
-            bool ok[CBC_UNROLL];
 #pragma unroll
             for (int u = 0; u < CBC_UNROLL; ++u) {
-                ok[u] = todo != 0;
-                const int c = ok[u] ? (int)__builtin_ctzll(todo) : 0;
+                // c == CBC_TK once the list is empty: the word is masked to
+                // zero and src names the zero activation
+                const int c = todo != 0 ? (int)__builtin_ctzll(todo) : CBC_TK;
                 todo &= todo - 1;
                 src[u] = c;
-                const uint64_t w = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)mhi, c) << 32) |
-                                   (uint32_t)__builtin_amdgcn_readlane((int)mlo, c);
-                const uint32_t p = (uint32_t)__builtin_amdgcn_readlane((int)pos, c);
+                const int l = c & (CBC_TK - 1);
+                const uint64_t wr = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)mhi, l) << 32) |
+                                    (uint32_t)__builtin_amdgcn_readlane((int)mlo, l);
+                const uint64_t w = c < CBC_TK ? wr : 0ull;
+                const uint32_t p = (uint32_t)__builtin_amdgcn_readlane((int)pos, l);
                 const uint32_t rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(w >> 32),
                                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)w, 0u));
-                const bool bit = ok[u] && ((w >> lane) & 1ull) != 0;
-                vpos[u] = bit ? (p + rank) * 2u : CBC_OOR;
+                const uint32_t vpos = cbc_lane_select(w, (p + rank) * 2u, CBC_OOR);
+                hv[u] = __builtin_amdgcn_raw_buffer_load_b16(vrs, vpos, 0, 0);
             }
-            uint32_t hv[CBC_UNROLL];
-#pragma unroll
-            for (int u = 0; u < CBC_UNROLL; ++u) hv[u] = __builtin_amdgcn_raw_buffer_load_b16(vrs, vpos[u], 0, 0);
-            // xv is zero for n >= N, so no guard (a branch per column would
-            // wait for each gather in turn)
 #pragma unroll
             for (int u = 0; u < CBC_UNROLL; ++u) {
                 const float w = bsp_h2f((uint16_t)hv[u]);
 #pragma unroll
-                for (int n = 0; n < NMAX; ++n) {
-                    const float x = cbc_readlane_f(xv[n], src[u]);
-                    acc[n] = fmaf(w, ok[u] ? x : 0.f, acc[n]);
-                }
+                for (int n = 0; n < NMAX; ++n) acc[n] = fmaf(w, xsw[wave][n][src[u]], acc[n]);
             }
         }
+        __builtin_amdgcn_wave_barrier();                    // xsw is read before the next GTile writes it
     }
 
     // the column groups' partials, added in group order by column group 0's

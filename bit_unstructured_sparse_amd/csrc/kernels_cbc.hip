@@ -21,14 +21,16 @@
 // position of that word's first value (GTile offset + column offset + the
 // set bits of the words above); a ballot marks the columns that are active
 // and hold a nonzero in these rows (the others are skipped, values unread);
-// (2) for up to 32 of those columns at a time the wavefront reads each
-// column's word and position out of its lane (readlane: uniform values), and
+// (2) the listed columns' words, positions and activations are moved to the
+// first lanes in column order (one ds_permute per field); for up to 32 of
+// them at a time the wavefront reads each column's word and position out of
+// its lane (readlane with a constant lane number: uniform values), and
 // every lane finds its rank with v_mbcnt and gathers its value (the word
 // itself, as a lane mask, sends a lane whose bit is clear past the buffer's
-// range, where it reads zero); then it accumulates value x x' in fp32, x'
-// read from a per-wavefront LDS copy of the GTile's activations (a broadcast
-// read). A column costs a wavefront about eight vector instructions, which
-// is what bounds this kernel once the values are in flight.
+// range, where it reads zero); then it accumulates value x x' in fp32 (x'
+// read out of its lane at N = 1, else from a per-wavefront LDS copy of the
+// GTile's activations, a broadcast read). A column costs a wavefront about
+// nine vector instructions and no scalar ones.
 //
 // Segments of one band meet through a workspace: each workgroup posts its
 // fp32 partials, and the last of the band's workgroups to arrive (an
@@ -102,34 +104,49 @@ __global__ __launch_bounds__(1024) void k_cbc_f16(const uint32_t *__restrict__ t
                   (rq > 1 ? (uint32_t)__builtin_popcountll(w1) : 0u) +
                   (rq > 2 ? (uint32_t)__builtin_popcountll(w2) : 0u);
         }
-        uint64_t todo = __ballot(act && mine != 0);
-        const uint32_t mlo = (uint32_t)mine, mhi = (uint32_t)(mine >> 32);
+        const bool listed = act && mine != 0;
+        const uint64_t todo = __ballot(listed);
+        const int cnt = __builtin_popcountll(todo);
 #pragma unroll
         for (int n = 0; n < NMAX; ++n) {
             xsw[wave][n][lane] = xv[n];
             if (lane == 0) xsw[wave][n][CBC_TK] = 0.f;
         }
+        // the listed columns' words, value positions and activations (or
+        // column numbers) to lanes 0 .. cnt - 1 in column order, the other
+        // columns after them: one forward permute per field, so that the
+        // column loop reads them with constant lane numbers
+        const uint32_t r1 = __builtin_amdgcn_mbcnt_hi((uint32_t)(todo >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)todo, 0u));
+        const uint32_t r0 = (uint32_t)lane - r1;
+        const int dst = (int)((listed ? r1 : (uint32_t)cnt + r0) * 4u);
+        // every lane takes part in each permute (a lane left out would not
+        // deliver its column): the results are pinned before the selects so
+        // that the compiler cannot move a permute under the selects' mask
+        uint32_t tlo = (uint32_t)__builtin_amdgcn_ds_permute(dst, (int)(uint32_t)mine);
+        uint32_t thi = (uint32_t)__builtin_amdgcn_ds_permute(dst, (int)(uint32_t)(mine >> 32));
+        uint32_t cpos = (uint32_t)__builtin_amdgcn_ds_permute(dst, (int)pos);
+        int tx = __builtin_amdgcn_ds_permute(dst, NMAX == 1 ? __float_as_int(xv[0]) : lane);
+        asm volatile("" : "+v"(tlo), "+v"(thi), "+v"(cpos), "+v"(tx));
+        const bool valid = lane < cnt;
+        const uint32_t cmlo = valid ? tlo : 0u, cmhi = valid ? thi : 0u;
+        const float cx = valid ? __int_as_float(tx) : 0.f;   // N = 1: the activation
+        const int ccol = valid ? tx : CBC_TK;                 // N > 1: the column
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-        // (2) CBC_UNROLL columns' gathers in flight at a time; past the last
-        // column, an empty word and the zero activation
-        while (todo != 0) {
+        // (2) CBC_UNROLL columns' gathers in flight at a time; a lane past
+        // cnt holds an empty word and a zero activation
+#pragma unroll
+        for (int bt = 0; bt < CBC_TK / CBC_UNROLL; ++bt) {
+            if (bt * CBC_UNROLL >= cnt) break;
             uint32_t hv[CBC_UNROLL];
-            int src[CBC_UNROLL];
 #pragma unroll
             for (int u = 0; u < CBC_UNROLL; ++u) {
-                // c == CBC_TK once the list is empty: the word is masked to
-                // zero and src names the zero activation
-                const int c = todo != 0 ? (int)__builtin_ctzll(todo) : CBC_TK;
-                todo &= todo - 1;
-                src[u] = c;
-                const int l = c & (CBC_TK - 1);
-                const uint64_t wr = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)mhi, l) << 32) |
-                                    (uint32_t)__builtin_amdgcn_readlane((int)mlo, l);
-                const uint64_t w = c < CBC_TK ? wr : 0ull;
-                const uint32_t p = (uint32_t)__builtin_amdgcn_readlane((int)pos, l);
+                const int j = bt * CBC_UNROLL + u;
+                const uint64_t w = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)cmhi, j) << 32) |
+                                   (uint32_t)__builtin_amdgcn_readlane((int)cmlo, j);
+                const uint32_t p = (uint32_t)__builtin_amdgcn_readlane((int)cpos, j);
                 const uint32_t rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(w >> 32),
                                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)w, 0u));
                 const uint32_t vpos = cbc_lane_select(w, (p + rank) * 2u, CBC_OOR);
@@ -137,9 +154,15 @@ __global__ __launch_bounds__(1024) void k_cbc_f16(const uint32_t *__restrict__ t
             }
 #pragma unroll
             for (int u = 0; u < CBC_UNROLL; ++u) {
+                const int j = bt * CBC_UNROLL + u;
                 const float w = bsp_h2f((uint16_t)hv[u]);
+                if constexpr (NMAX == 1) {
+                    acc[0] = fmaf(w, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cx), j)), acc[0]);
+                } else {
+                    const int c = __builtin_amdgcn_readlane(ccol, j);
 #pragma unroll
-                for (int n = 0; n < NMAX; ++n) acc[n] = fmaf(w, xsw[wave][n][src[u]], acc[n]);
+                    for (int n = 0; n < NMAX; ++n) acc[n] = fmaf(w, xsw[wave][n][c], acc[n]);
+                }
             }
         }
         __builtin_amdgcn_wave_barrier();                    // xsw is read before the next GTile writes it

@@ -39,6 +39,7 @@ Helper modes used to produce the ``profiles/`` summaries:
     python bench.py --summarize-trace DIR OUT   # rocprofv3 --kernel-trace --stats csv -> text
     python bench.py --summarize-traffic OUT --reads DIR --writes DIR --kernel FRAGMENT
     python bench.py --summarize-counters DIR OUT --kernel FRAGMENT   # rocprofv3 --pmc csv -> text
+    python bench.py --summarize-selection OUT --side LABEL:TRACE:PMC:READS:WRITES:FRAGMENT ...
 """
 from __future__ import annotations
 
@@ -378,11 +379,12 @@ def traffic_estimators(rd, wr):
             "dram_32b": (32 * g(rd, "TCC_EA0_RDREQ_DRAM_32B_sum"), 32 * g(wr, "TCC_EA0_WRREQ_WRITE_DRAM_32B_sum"))}
 
 
-def summarize_traffic(out, reads, writes, fragment, header):
-    """Traffic of one launch of the kernel matching `fragment`, with the
-    estimator that reproduces the known bytes of both calibration kernels of
-    the same run (the read probe: COPY_BYTES read; the copy: COPY_BYTES read
-    and written) within 5 %."""
+def traffic_lines(reads, writes, fragment):
+    """Counter lines, the calibration check and the traffic of one launch of
+    the kernel matching `fragment`, with the estimator that reproduces the
+    known bytes of both calibration kernels of the same run (the read probe:
+    COPY_BYTES read; the copy: COPY_BYTES read and written) within 5 %.
+    Returns (kernel, lines, bytes or None)."""
     R = _counters_by_kernel(reads, set(READ_COUNTERS))
     W = _counters_by_kernel(writes, set(WRITE_COUNTERS))
     kr, kw = _pick({k: (0, v[READ_COUNTERS[0]][1]) for k, v in R.items()}, fragment), \
@@ -391,8 +393,7 @@ def summarize_traffic(out, reads, writes, fragment, header):
     cr = _pick({k: (0, 1) for k in R}, "bitwise_not")
     pw = _pick({k: (0, 1) for k in W}, "k_probe_read")
     cw = _pick({k: (0, 1) for k in W}, "bitwise_not")
-    lines = [f"# {h}" for h in header] + [f"kernel: {kr}", f"dispatches: reads {R[kr][READ_COUNTERS[0]][1]}, "
-                                                           f"writes {W[kw][WRITE_COUNTERS[0]][1]}"]
+    lines = [f"kernel: {kr}", f"dispatches: reads {R[kr][READ_COUNTERS[0]][1]}, writes {W[kw][WRITE_COUNTERS[0]][1]}"]
     for c in READ_COUNTERS:
         lines.append(f"{c}: {R[kr].get(c, (0.0, 0))[0]:.0f}")
     for c in WRITE_COUNTERS:
@@ -408,12 +409,63 @@ def summarize_traffic(out, reads, writes, fragment, header):
                      f"{'within' if ok else 'outside'} 5 %")
         if ok and chosen is None:
             chosen = name
+    total = None
     if chosen is not None:
         k_r, k_w = traffic_estimators(R[kr], W[kw])[chosen]
+        total = k_r + k_w
         lines += [f"estimator: {chosen}", f"read_bytes_per_launch: {k_r:.0f}", f"write_bytes_per_launch: {k_w:.0f}",
-                  f"traffic_bytes_per_launch: {k_r + k_w:.0f}"]
+                  f"traffic_bytes_per_launch: {total:.0f}"]
     else:
         lines += ["estimator: none (no estimator reproduces both calibration kernels within 5 %)"]
+    return kr, lines, total
+
+
+def summarize_traffic(out, reads, writes, fragment, header):
+    """Traffic summary file of one launch (see traffic_lines), tied to the
+    current kernel sources by their digest."""
+    _, body, _ = traffic_lines(reads, writes, fragment)
+    lines = [f"# {h}" for h in header] + body + [f"source_digest: {source_digest()}"]
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def _trace_stats(d, fragment):
+    """(kernel, calls, mean us, p50 us) of the kernel matching `fragment` in
+    a rocprofv3 kernel trace."""
+    durs = {}
+    for r in _csv_rows(d, "kernel_trace.csv"):
+        durs.setdefault(r["Kernel_Name"], []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    name = _pick({k: (0, len(v)) for k, v in durs.items()}, fragment)
+    v = sorted(durs[name])
+    return name, len(v), statistics.mean(v), v[len(v) // 2]
+
+
+def _counter_means(d, fragment):
+    per, name = {}, None
+    for r in _csv_rows(d, "counter_collection.csv"):
+        if fragment in r["Kernel_Name"]:
+            name = r["Kernel_Name"]
+            per.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    return name, {k: sum(v) / len(v) for k, v in per.items()}
+
+
+def summarize_selection(out, sides, header):
+    """A/B of the kernels on either side of a selection threshold, on one
+    shape: per side the launch duration (kernel trace), the SQ counters of
+    one --pmc pass and the calibrated HBM traffic of one launch. Each side is
+    LABEL:TRACE_DIR:PMC_DIR:READS_DIR:WRITES_DIR:FRAGMENT."""
+    lines = [f"# {h}" for h in header]
+    for side in sides:
+        label, tdir, pdir, rdir, wdir, frag = side.split(":")
+        kname, calls, avg, p50 = _trace_stats(tdir, frag)
+        _, cnt = _counter_means(pdir, frag)
+        _, _, traffic = traffic_lines(rdir, wdir, frag)
+        lines.append(f"[{label}] kernel: {kname}")
+        lines.append(f"[{label}] duration_us: mean {avg:.3f}, p50 {p50:.3f} over {calls} dispatches")
+        for c in sorted(cnt):
+            lines.append(f"[{label}] {c}: {cnt[c]:.0f}")
+        lines.append(f"[{label}] traffic_bytes_per_launch: {'%.0f' % traffic if traffic is not None else 'none'}")
     lines.append(f"source_digest: {source_digest()}")
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
@@ -946,6 +998,9 @@ def main():
     ap.add_argument("--summarize-trace", nargs=2, metavar=("DIR", "OUT"))
     ap.add_argument("--summarize-traffic", metavar="OUT")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("DIR", "OUT"))
+    ap.add_argument("--summarize-selection", metavar="OUT")
+    ap.add_argument("--side", action="append", default=[],
+                    help="--summarize-selection: LABEL:TRACE_DIR:PMC_DIR:READS_DIR:WRITES_DIR:KERNEL_FRAGMENT")
     ap.add_argument("--reads"), ap.add_argument("--writes")
     ap.add_argument("--kernel", default="w4a4", help="kernel name fragment for the summaries")
     ap.add_argument("--note", action="append", default=[], help="header line for a summary")
@@ -957,6 +1012,8 @@ def main():
         return summarize_counters(args.summarize_counters[0], args.summarize_counters[1], args.kernel, args.note)
     if args.summarize_traffic:
         return summarize_traffic(args.summarize_traffic, args.reads, args.writes, args.kernel, args.note)
+    if args.summarize_selection:
+        return summarize_selection(args.summarize_selection, args.side, args.note)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the path has no "
               f"multi-GPU code; how it would shard is described with the design.", file=sys.stderr)

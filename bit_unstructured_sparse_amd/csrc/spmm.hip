@@ -69,10 +69,14 @@ struct Plan {
 
 // K ranges per block set the automatic plan gives the split-K kernels when
 // a workspace is given: 2 for fp16 past K = 4096 (4096 x 11008: 28.1 us
-// against 31.0 at N = 8, 26.0 against 27.2 at N = 1); 1 for int4 (4096 x
-// 20000 at N = 8: 23.6 us with 2 against 22.2 with 1).
+// against 31.0 at N = 8, 26.0 against 27.2 at N = 1); for int4, 2 past
+// K = 20480 (T > 320) and 1 up to it (4096 x K at N = 8, 1 against 2
+// ranges: K = 20480 22.4 / 24.2 us, 24576 26.1 / 24.1, 28672 29.7 / 30.0,
+// 32768 34.7 / 31.9; 4096 x 24576 at N = 32 35.8 / 31.0; 8192 x 24576 at
+// N = 8 50.0 / 46.6).
 int preferred_splits(int dtype, const Shape &s) {
-    return dtype == BSP_FP16 && s.T > 64 ? 2 : 1;
+    if (dtype == BSP_FP16) return s.T > 64 ? 2 : 1;
+    return s.T > 320 ? 2 : 1;
 }
 
 // The MFMA family: the 16-row block kernels (int4: streaming up to K = 4096,

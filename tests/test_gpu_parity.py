@@ -562,6 +562,24 @@ def test_f16_past_k4096_auto(dev, M, K, N):
         _assert_f16(Y.cpu().numpy(), r)
 
 
+@pytest.mark.parametrize("M,K,N,split_with_ws", [(300, 24576 + 40, 8, 2), (130, 20480, 5, 1), (64, 32768, 32, 2)])
+def test_w4a4_past_k16384_auto(dev, M, K, N, split_with_ws):
+    # int4 past K = 16384: the automatic plan is the split-K kernel, with 2 K
+    # ranges past K = 20480 when given a workspace, 1 otherwise; bit-exact
+    p = workloads.random_int4_problem(M + K + N, M, K, N, keep=0.5)
+    enc = bsp.encode(p.W)
+    ref = oracle_w4a4(p.W, p.X)
+    for ws in (None, _ws(bsp.INT4, M, K, N, enc.nnz, dev)):
+        d = bsp.describe(bsp.INT4, M, K, N, enc.nnz, workspace=ws is not None)
+        want = split_with_ws if ws is not None else 1
+        assert "-> splitk kernel=k_bsk_w4a4" in d and f"splits={want} " in d, d
+        big, Y = _y_with_canary(N, M, torch.int32, dev)
+        bsp.spmm_w4a4(enc.to_device(dev), torch.from_numpy(bsp.pack_int4(p.X)).to(dev), N, Y=Y, workspace=ws)
+        torch.cuda.synchronize()
+        assert _canary_ok(big, N, M, torch.int32), "write past the end of Y"
+        assert np.array_equal(Y.cpu().numpy(), ref), d
+
+
 @pytest.mark.parametrize("dtype", ["int4", "fp16"])
 def test_splitk_workspace_reused_across_shapes(dev, dtype):
     # one caller workspace for a large problem, then a smaller one, then the

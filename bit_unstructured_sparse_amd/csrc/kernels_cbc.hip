@@ -63,7 +63,9 @@ __global__ __launch_bounds__(1024) void k_cbc_f16(const uint32_t *__restrict__ t
                                                   uint16_t *__restrict__ Y, float *ws_part, uint32_t *ws_cnt, int S,
                                                   int G) {
     __shared__ float part[CBC_GROUPS][NMAX][CBC_TM];
-    __shared__ float xsw[CBC_GROUPS * 4][NMAX][CBC_TK + 1];   // per wavefront: x' of the GTile, then a zero
+    // per wavefront: x' of the GTile's columns (a column's N values together,
+    // read with 16-byte broadcasts), then a zero column
+    __shared__ __attribute__((aligned(16))) float xsw[CBC_GROUPS * 4][CBC_TK + 1][NMAX];
     __shared__ int flag;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int rq = wave & 3, grp = wave >> 2;              // row quarter, column group
@@ -109,8 +111,8 @@ __global__ __launch_bounds__(1024) void k_cbc_f16(const uint32_t *__restrict__ t
         const int cnt = __builtin_popcountll(todo);
 #pragma unroll
         for (int n = 0; n < NMAX; ++n) {
-            xsw[wave][n][lane] = xv[n];
-            if (lane == 0) xsw[wave][n][CBC_TK] = 0.f;
+            xsw[wave][lane][n] = xv[n];
+            if (lane == 0) xsw[wave][CBC_TK][n] = 0.f;
         }
         // the listed columns' words, value positions and activations (or
         // column numbers) to lanes 0 .. cnt - 1 in column order, the other
@@ -160,8 +162,21 @@ __global__ __launch_bounds__(1024) void k_cbc_f16(const uint32_t *__restrict__ t
                     acc[0] = fmaf(w, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cx), j)), acc[0]);
                 } else {
                     const int c = __builtin_amdgcn_readlane(ccol, j);
+                    if constexpr (NMAX % 4 == 0) {
 #pragma unroll
-                    for (int n = 0; n < NMAX; ++n) acc[n] = fmaf(w, xsw[wave][n][c], acc[n]);
+                        for (int n = 0; n < NMAX; n += 4) {
+                            const float4 x4 = *reinterpret_cast<const float4 *>(&xsw[wave][c][n]);
+                            acc[n] = fmaf(w, x4.x, acc[n]);
+                            acc[n + 1] = fmaf(w, x4.y, acc[n + 1]);
+                            acc[n + 2] = fmaf(w, x4.z, acc[n + 2]);
+                            acc[n + 3] = fmaf(w, x4.w, acc[n + 3]);
+                        }
+                    } else {
+                        static_assert(NMAX == 2, "activation widths 1, 2 or a multiple of 4");
+                        const float2 x2 = *reinterpret_cast<const float2 *>(&xsw[wave][c][0]);
+                        acc[0] = fmaf(w, x2.x, acc[0]);
+                        acc[1] = fmaf(w, x2.y, acc[1]);
+                    }
                 }
             }
         }

@@ -621,12 +621,18 @@ extern "C" int spmspv_cbc_f16(const uint32_t *tile_offsets, const uint32_t *coli
     float *part = p.S > 1 ? (float *)((uint8_t *)workspace + CBC_WS_COUNTERS) : nullptr;
     uint32_t *cnt = p.S > 1 ? (uint32_t *)workspace : nullptr;
     const unsigned grid = (unsigned)((int64_t)p.bands * p.S);
+    // the instance with the fewest activation columns that holds N
+#define CBC_LAUNCH(NM)                                                                                              \
+    hipLaunchKernelGGL(k_cbc_f16<NM>, dim3(grid), dim3(1024), 0, stream, tile_offsets, colinfo, bitmaps, values,   \
+                       (uint32_t)values_bytes, (int)M, (int)K, X, (int)N, threshold, Y, part, cnt, p.S, p.G)
     if (N == 1)
-        hipLaunchKernelGGL(k_cbc_f16<1>, dim3(grid), dim3(1024), 0, stream, tile_offsets, colinfo, bitmaps, values,
-                           (uint32_t)values_bytes, (int)M, (int)K, X, (int)N, threshold, Y, part, cnt, p.S, p.G);
+        CBC_LAUNCH(1);
+    else if (N == 2)
+        CBC_LAUNCH(2);
+    else if (N <= 4)
+        CBC_LAUNCH(4);
     else
-        hipLaunchKernelGGL(k_cbc_f16<CBC_NMAX>, dim3(grid), dim3(1024), 0, stream, tile_offsets, colinfo, bitmaps,
-                           values, (uint32_t)values_bytes, (int)M, (int)K, X, (int)N, threshold, Y, part, cnt, p.S,
-                           p.G);
+        CBC_LAUNCH(CBC_NMAX);
+#undef CBC_LAUNCH
     return launch_status();
 }

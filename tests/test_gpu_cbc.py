@@ -62,6 +62,17 @@ def test_cbc_thresholds(M, K, N, keep, quantile, workspace, dev):
     check(run(W, X, tau, dev, workspace), W, X, tau)
 
 
+@pytest.mark.parametrize("workspace", [True, False])
+def test_cbc_every_n(workspace, dev):
+    # every width from 1 to BSP_CBC_MAX_N (the kernel instances hold 1, 2, 4 or 8 activation columns)
+    W, rng = _w(91, 700, 1500, 0.4)
+    X = rng.normal(0, 1, (8, 1500)).astype(np.float16)
+    tau = float(np.quantile(np.abs(X.astype(np.float32)), 0.5))
+    enc = bsp.encode_cbc_f16(W)
+    for N in range(1, 9):
+        check(run(W, X[:N], tau, dev, workspace, enc=enc), W, X[:N], tau)
+
+
 def test_cbc_all_pruned_and_k_zero(dev):
     W, rng = _w(1, 300, 200, 0.5)
     X = rng.normal(0, 1, (2, 200)).astype(np.float16)

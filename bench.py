@@ -80,13 +80,12 @@ def algo_name(bsp, a):
 
 
 def kernel_symbol(bsp, chosen, dt, M, K, N, nnz, workspace=False):
-    """Name of the kernel a launch runs: the library's own description of its
-    plan when the automatic choice is the one timed, else the algorithm's
+    """Name of the kernel a launch runs: the library's own description of the
+    plan the timed choice (automatic or forced) takes, else the algorithm's
     kernel family."""
-    if chosen == bsp.ALGO_AUTO:
-        m = re.search(r"kernel=(\S+)", bsp.describe(dt, M, K, N, nnz, workspace=workspace))
-        if m:
-            return m.group(1)
+    m = re.search(r"kernel=(\S+)", bsp.describe(dt, M, K, N, nnz, workspace=workspace, algo=chosen))
+    if m:
+        return m.group(1)
     return KERNEL_SYMBOL[algo_name(bsp, chosen)]
 
 
@@ -108,13 +107,17 @@ def offsets_read(kernel, M, T, plan=""):
     """4-byte offsets one launch of `kernel` reads: every tile's (the plain
     row-wave kernel), one per 16-row block plus the end (the 16-row MFMA
     kernels), one per 8-row step plus the end and one half-row start per row
-    (the eight-row fp16 kernel), or the bounds of every row's chunks (the
-    split-K kernels: chunks of `chunk_tiles` tiles inside K ranges of
+    (the eight-row fp16 kernel), the ends of every row's K ranges (the
+    streamed split-K kernel), or the bounds of every row's chunks (the
+    chunked split-K kernels: chunks of `chunk_tiles` tiles inside K ranges of
     `tiles_per_split`, from the plan's description)."""
     if kernel.startswith("k_rowwave"):
         return M * T
     if kernel.startswith("k_bt8_f16"):
         return (M + 7) // 8 + 1 + M
+    if kernel.startswith("k_bsks"):
+        m_s = re.search(r"splits=(\d+)", plan)
+        return M * (int(m_s.group(1)) + 1) if m_s else M * T   # the ends of every row's K ranges
     if kernel.startswith("k_bsk"):
         m_tps, m_ct = re.search(r"tiles_per_split=(\d+)", plan), re.search(r"chunk_tiles=(\d+)", plan)
         if not (m_tps and m_ct):
@@ -607,7 +610,7 @@ def prepare(args, workload, index, n):
             bsp.spmm_w4a4(dm, x, N, Y=y, algo=chosen, workspace=ws)
 
     kernel = kernel_symbol(bsp, chosen, dt, M, K, N, enc.nnz, workspace=ws is not None)
-    plan = bsp.describe(dt, M, K, N, enc.nnz, workspace=ws is not None)
+    plan = bsp.describe(dt, M, K, N, enc.nnz, workspace=ws is not None, algo=chosen)
     return dict(problem=problem, fp16=fp16, enc=enc, dm0=dm0, copies=copies, R=R, step=step, chosen=chosen,
                 name=algo_label(kernel), kernel=kernel, dt=dt, plan=plan)
 

@@ -38,7 +38,7 @@ MAX_N = 32
 # Every symbol include/bitmap_spmm.h declares.
 EXPORTS = ["encode_bitmap_tiles", "pack_int4_activations", "spmm_bitmap_w4a4", "spmm_bitmap_w4a4_algo",
            "spmm_bitmap_w4a4_ws", "spmm_bitmap_f16", "spmm_bitmap_f16_algo", "spmm_bitmap_f16_ws",
-           "bsp_workspace_bytes", "bsp_select", "bsp_describe_selection", "bsp_describe_selection_ws",
+           "bsp_workspace_bytes", "bsp_select", "bsp_describe_selection", "bsp_describe_selection_ws", "bsp_describe_plan",
            "bsp_status_string", "bsp_version", "spmm_bitmap_f16_noalloc", "bsp_noalloc_scratch_bytes",
            "union_tile_count", "union_mask_words", "encode_union_tiles", "spmm_union_w4a4",
            "spmm_bitmap_w4a4_dq", "spmm_bitmap_w4a4_grouped", "spmm_bitmap_w2a4", "spmm_bitmap_w2a4_algo",
@@ -84,6 +84,8 @@ def load_library():
         L.bsp_noalloc_scratch_bytes.argtypes, L.bsp_noalloc_scratch_bytes.restype = [], I64
         L.bsp_describe_selection_ws.argtypes = [I32, I64, I64, I64, I64, ctypes.c_char_p, ctypes.c_size_t]
         L.bsp_describe_selection_ws.restype = I32
+        L.bsp_describe_plan.argtypes = [I32, I64, I64, I64, I64, I32, I32, ctypes.c_char_p, ctypes.c_size_t]
+        L.bsp_describe_plan.restype = I32
         L.bsp_select.argtypes, L.bsp_select.restype = [I32, I64, I64, I64, I64], I32
         L.bsp_describe_selection.argtypes = [I32, I64, I64, I64, I64, ctypes.c_char_p, ctypes.c_size_t]
         L.bsp_describe_selection.restype = I32
@@ -588,10 +590,16 @@ def select(dtype: int, M: int, K: int, N: int, nnz: int = -1) -> int:
     return int(load_library().bsp_select(dtype, M, K, N, nnz))
 
 
-def describe(dtype: int, M: int, K: int, N: int, nnz: int = -1, workspace: bool = False) -> str:
+def describe(dtype: int, M: int, K: int, N: int, nnz: int = -1, workspace: bool = False,
+             algo: int = ALGO_AUTO) -> str:
     """The plan (kernel and launch shape) of the plain entry points, or with
-    workspace=True of the *_ws entry points given a workspace."""
+    workspace=True of the *_ws entry points given a workspace; for an
+    explicit algo, the plan that choice takes (BspError if it cannot run)."""
     buf = ctypes.create_string_buffer(384)
+    if algo != ALGO_AUTO:
+        _check(load_library().bsp_describe_plan(dtype, M, K, N, nnz, algo, int(workspace), buf, 384),
+               "bsp_describe_plan")
+        return buf.value.decode()
     fn = load_library().bsp_describe_selection_ws if workspace else load_library().bsp_describe_selection
     _check(fn(dtype, M, K, N, nnz, buf, 384), "bsp_describe_selection")
     return buf.value.decode()

@@ -327,6 +327,237 @@ static size_t bsk_w4a4_lds(int nwaves, int nbs, int iseg) {
            (size_t)nbs * 16 * ((size_t)iseg * 1024 + SK_SLOT_SKEW) + 16;
 }
 
+// ------------------------------------------------------------ int4, streamed
+
+// The same work item walked as the streaming kernel walks its blocks: a set
+// of at most SKS_NBLK blocks over one K range of at most 32 TPL tiles (eight
+// wavefronts, TPL tiles per lane), the block's range of every row decoded in
+// one pass, and block i + 1's row segments in flight while block i is
+// decoded. Per block:
+//   - its 16 row segments (their ends read from the format's offsets for
+//     every block of the set at the start, with X and block 0's words) go
+//     by DMA to slots of their own, ISEG KB each plus 48 bytes (every row
+//     starts 12 banks further round than the one before it), 2 ISEG
+//     instructions per wavefront; a block with a segment longer than its
+//     slot reads its windows from global memory instead (every wavefront
+//     decides alike);
+//   - once it has landed and every wavefront has posted its row totals (one
+//     barrier), a lane's start is its segment's first nibble inside the
+//     first granule plus the tiles before its own in the row's range;
+//   - the next block's words and segments are issued before that barrier, so
+//     one transfer is in flight while each block is decoded.
+// Partials and the reduction are those of k_bsk_w4a4.
+#define SKS_NBLK 3
+#define SKS_SKEW 48u
+#define SKS_WAVES 8
+
+// LDS of the streamed kernel: selector table | row totals [NBLK][16][8] |
+// partials [nbs][8][NB * 256] ints | slots [nbs][16][ISEG KB + 48] | flag
+static size_t bsks_w4a4_lds(int nb, int nbs, int iseg) {
+    return (size_t)BT_LUT_BYTES + (size_t)SKS_NBLK * 16 * SKS_WAVES * 4 + (size_t)nbs * SKS_WAVES * nb * 1024 +
+           (size_t)nbs * 16 * ((size_t)iseg * 1024 + SKS_SKEW) + 16;
+}
+
+template <int NB, int TPL, int ISEG, bool XU>
+__global__ __launch_bounds__(512) void k_bsks_w4a4(SkArgs a) {
+    constexpr int WC = SKS_WAVES, D = 16 * ISEG / SKS_WAVES;   // DMA instructions per wavefront and block
+    extern __shared__ __attribute__((aligned(16))) uint8_t sk_smem[];
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int r = lane & 15, q = lane >> 4;
+    const int M = a.M, T = a.T, N = a.N;
+    const SkPlace pl = sk_place(a);
+    const int nblk = pl.nb_here;                       // 1 .. SKS_NBLK
+    const int tr = pl.te - pl.ts;                      // tiles of the range, <= 32 TPL
+    const int t0 = (wave * 4 + q) * TPL;               // this lane's first tile, from the range's start
+    const uint32_t xs = ((uint32_t)a.K + 1u) >> 1;
+    constexpr uint32_t slot_bytes = (uint32_t)ISEG * 1024u + SKS_SKEW;
+    constexpr uint32_t cap = (uint32_t)ISEG * 64u;     // granules a slot holds
+
+    const uint32_t lut_base = bt_lds_addr(sk_smem) + (uint32_t)(lane % BT_LUT_COPIES) * 8u;
+    int32_t *wt = reinterpret_cast<int32_t *>(sk_smem + BT_LUT_BYTES);
+    int32_t *part = wt + SKS_NBLK * 16 * WC;
+    uint8_t *slots = reinterpret_cast<uint8_t *>(part + a.nbs * WC * NB * 256);
+    int *flag = reinterpret_cast<int *>(slots + (uint32_t)a.nbs * 16u * slot_bytes);
+
+    const int set_rows = min(nblk * 16, M - pl.b0 * 16);
+    const __amdgpu_buffer_rsrc_t prs = bt_rsrc(a.payload, a.payload_bytes);
+    const __amdgpu_buffer_rsrc_t ors = bt_rsrc(a.offsets + (int64_t)pl.b0 * 16 * T, ((uint32_t)set_rows * (uint32_t)T + 1u) * 4u);
+    const __amdgpu_buffer_rsrc_t brs = bt_rsrc(a.bitmaps + (int64_t)pl.b0 * 16 * T, (uint32_t)set_rows * (uint32_t)T * 8u);
+    const __amdgpu_buffer_rsrc_t xrs = bt_rsrc(a.X, bt_x_range(N, xs));
+    asm volatile("" ::"s"(a.payload), "s"(a.X), "s"(a.Y), "s"(N));
+
+    // (1) every block's row segments (lane r: row r of each block), first
+    uint2 seg[SKS_NBLK];
+#pragma unroll
+    for (int i = 0; i < SKS_NBLK; ++i)
+        seg[i] = sk_segment(ors, i * 16 + r, i < nblk && i * 16 + r < set_rows, T, pl.ts, pl.te);
+    // (2) X slices of the lane's tiles (zeros past N or past the range)
+    uint32_t xw[NB][TPL][8];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int k = 0; k < TPL; ++k) {
+            const int n = r + 16 * nb;
+            const uint32_t off =
+                    (n < N && t0 + k < tr) ? (uint32_t)n * xs + (uint32_t)(pl.ts + t0 + k) * 32u : 0xFFFFFFE0u;
+            const bt_v4i v0 = bt_load_x16<XU>(xrs, off);
+            const bt_v4i v1 = bt_load_x16<XU>(xrs, off + 16u);
+            xw[nb][k][0] = v0.x; xw[nb][k][1] = v0.y; xw[nb][k][2] = v0.z; xw[nb][k][3] = v0.w;
+            xw[nb][k][4] = v1.x; xw[nb][k][5] = v1.y; xw[nb][k][6] = v1.z; xw[nb][k][7] = v1.w;
+        }
+    // (3) words: block 0's now, block i + 1's with its segments (tiles past
+    // the range are cleared before use; rows past the set read zeros)
+    uint64_t words[SKS_NBLK][TPL];
+    auto load_words = [&](int i) -> void {
+        const int rr = i * 16 + r;
+        const uint32_t off = ((uint32_t)rr * (uint32_t)T + (uint32_t)(pl.ts + t0)) * 8u;
+        const bt_v4i v = __builtin_bit_cast(bt_v4i, __builtin_amdgcn_raw_buffer_load_b128(brs, off, 0, BT_NT));
+        words[i][0] = ((uint64_t)(uint32_t)v.y << 32) | (uint32_t)v.x;
+        words[i][1] = ((uint64_t)(uint32_t)v.w << 32) | (uint32_t)v.z;
+        if constexpr (TPL == 3)
+            words[i][2] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(brs, off + 16u, 0, BT_NT));
+    };
+    load_words(0);
+    // (4) each block's granules and whether its segments fit their slots
+    uint32_t g0[SKS_NBLK], ng[SKS_NBLK];
+    bool fits[SKS_NBLK];
+#pragma unroll
+    for (int i = 0; i < SKS_NBLK; ++i) {
+        g0[i] = seg[i].x >> 5;
+        // the windows of a row's last tile reach 15 nibbles past its segment
+        ng[i] = seg[i].y > seg[i].x ? ((seg[i].y + 15u) >> 5) - g0[i] + 1u : 0u;
+        fits[i] = __ballot(ng[i] > cap) == 0ull;   // wave-uniform: every wavefront holds the same rows
+    }
+    // block i's DMAs: instruction j = wave + 8 d moves KB j % ISEG of row
+    // j / ISEG's segment (a fixed count per wavefront, so the compiler's own
+    // waits stay exact)
+    auto issue = [&](int i) -> void {
+        uint8_t *buf = slots + (uint32_t)i * 16u * slot_bytes;
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            const int j = wave + SKS_WAVES * d;
+            const int row = j / ISEG, k = j - row * ISEG;
+            uint32_t sg0 = 0, sng = 0;
+#pragma unroll
+            for (int ii = 0; ii < SKS_NBLK; ++ii)
+                if (ii == i) {
+                    sg0 = (uint32_t)__builtin_amdgcn_readlane((int)g0[ii], row);
+                    sng = fits[ii] ? (uint32_t)__builtin_amdgcn_readlane((int)ng[ii], row) : 0u;
+                }
+            const uint32_t u = (uint32_t)k * 64u + (uint32_t)lane;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(prs, (bt_lds_void *)(buf + (uint32_t)row * slot_bytes + (uint32_t)k * 1024u),
+                                                     16, u < sng ? (sg0 + u) * 16u : 0xFFFFFFF0u, 0, 0, BT_NT);
+        }
+    };
+    issue(0);
+    {
+        __attribute__((address_space(3))) uint64_t *lut_lds =
+                (__attribute__((address_space(3))) uint64_t *)(uintptr_t)bt_lds_addr(sk_smem);
+        for (uint32_t v = threadIdx.x; v < 256u * BT_LUT_COPIES / 8u; v += blockDim.x) {
+            const uint32_t b = v & 255u, c0 = 8u * (v >> 8);
+            const uint2 e = bt_lut_entry(b);
+            const uint64_t e64 = ((uint64_t)e.y << 32) | e.x;
+#pragma unroll
+            for (uint32_t k = 0; k < 8; ++k) lut_lds[b * BT_LUT_COPIES + c0 + ((k + v) & 7u)] = e64;
+        }
+    }
+
+    bt_v4i xb[NB][TPL][4];
+#pragma unroll
+    for (int i = 0; i < SKS_NBLK; ++i) {
+        if (i >= nblk) break;
+#pragma unroll
+        for (int k = 0; k < TPL; ++k)
+            if (t0 + k >= tr) words[i][k] = 0;
+        uint32_t sc = 0;
+#pragma unroll
+        for (int k = 0; k < TPL; ++k) sc += (uint32_t)__builtin_popcountll(words[i][k]);
+        uint32_t incl = sc;
+        {
+            const uint32_t u16 = (uint32_t)__shfl_up((int)incl, 16, 64);
+            incl += q >= 1 ? u16 : 0u;
+            const uint32_t u32 = (uint32_t)__shfl_up((int)incl, 32, 64);
+            incl += q >= 2 ? u32 : 0u;
+        }
+        int32_t *wti = wt + i * 16 * WC;
+        if (q == 3) wti[r * WC + wave] = (int32_t)incl;
+        bt_wait_vm(0);   // this wavefront's share of block i landed (nothing later is in flight)
+        if (i + 1 < nblk) {
+            load_words(i + 1);
+            issue(i + 1);
+        }
+        if (i == 0) bt_make_b<NB, TPL>(xw, xb);
+        bt_barrier_lds();   // ... everyone's, and every row total of block i
+        uint32_t before_w;
+        {
+            uint32_t pre[WC + 1];
+            pre[0] = 0;
+#pragma unroll
+            for (int w4 = 0; w4 < WC; w4 += 4) {
+                const bt_v4i t4 = *(bt_lds_v4i *)(uintptr_t)bt_lds_addr(wti + r * WC + w4);
+                pre[w4 + 1] = pre[w4] + (uint32_t)t4.x;
+                pre[w4 + 2] = pre[w4 + 1] + (uint32_t)t4.y;
+                pre[w4 + 3] = pre[w4 + 2] + (uint32_t)t4.z;
+                pre[w4 + 4] = pre[w4 + 3] + (uint32_t)t4.w;
+            }
+            before_w = pre[wave];
+        }
+        const uint32_t within = before_w + (incl - sc);   // nibbles of the row's range before this lane's tiles
+        bt_v4i acc[NB];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[nb] = bt_v4i{0, 0, 0, 0};
+        if (fits[i]) {
+            const uint32_t slot = bt_lds_addr(slots + (uint32_t)(i * 16 + r) * slot_bytes);
+            // a corrupt stream stays inside the slot
+            const uint32_t local = min((seg[i].x & 31u) + within, 2u * (uint32_t)ISEG * 1024u - 16u - sc);
+            bt_contract<NB, TPL>(words[i], local + 2u * slot, BtWinLds{}, lut_base, xb, acc);
+        } else {
+            bt_contract<NB, TPL>(words[i], seg[i].x + within, BtWinGlobal{prs, 0u}, lut_base, xb, acc);
+        }
+        int32_t *pw = part + (i * WC + wave) * NB * 256;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+            *(__attribute__((address_space(3))) bt_v4i *)(uintptr_t)bt_lds_addr(pw + nb * 256 + lane * 4) =
+                    bt_v4i{acc[nb][0] >> 8, acc[nb][1] >> 8, acc[nb][2] >> 8, acc[nb][3] >> 8};
+    }
+    bt_barrier_lds();
+    // item (block i, column block nb, lane l): rows 4 (l / 16) .. +3 of
+    // column l % 16 (the MFMA D layout), the wavefronts' partials added in order
+    int32_t *wsp = reinterpret_cast<int32_t *>(a.ws_part);
+    for (int o = threadIdx.x; o < nblk * NB * 64; o += blockDim.x) {
+        const int i = o / (NB * 64), nb = (o / 64) % NB, ln = o % 64;
+        const int n = (ln & 15) + 16 * nb;
+        if (n >= N) continue;
+        bt_v4i sum = bt_v4i{0, 0, 0, 0};
+        for (int w = 0; w < WC; ++w)
+            sum += *(bt_lds_v4i *)(uintptr_t)bt_lds_addr(part + ((i * WC + w) * NB + nb) * 256 + ln * 4);
+        const int b = pl.b0 + i, rl = 4 * (ln >> 4);
+        if (a.S == 1) {
+            const int m = b * 16 + rl;
+            int32_t *y = reinterpret_cast<int32_t *>(a.Y) + (int64_t)n * M + m;
+            const int32_t v[4] = {sum.x, sum.y, sum.z, sum.w};
+            for (int k = 0; k < 4 && m + k < M; ++k) y[k] = v[k];
+        } else {
+            int32_t *w = wsp + (((int64_t)b * a.S + pl.split) * N + n) * 16 + rl;
+            sk_ws_store(w, sum.x);
+            sk_ws_store(w + 1, sum.y);
+            sk_ws_store(w + 2, sum.z);
+            sk_ws_store(w + 3, sum.w);
+        }
+    }
+    if (a.S == 1) return;
+    if (!sk_last_arrival(a, pl, flag)) return;
+    for (int o = threadIdx.x; o < nblk * 16 * N; o += blockDim.x) {
+        const int i = o / (16 * N), n = (o / 16) % N, rl = o % 16;
+        const int b = pl.b0 + i, m = b * 16 + rl;
+        if (m >= M) continue;
+        int32_t v = 0;
+        for (int sp = 0; sp < a.S; ++sp) v += sk_ws_load(wsp + (((int64_t)b * a.S + sp) * N + n) * 16 + rl);
+        reinterpret_cast<int32_t *>(a.Y)[(int64_t)n * M + m] = v;
+    }
+    sk_reset(a, pl);
+}
+
 // ------------------------------------------------------------------ fp16
 
 // Same skeleton with one tile per lane (CT = 4 x wavefronts), u16 payload
@@ -529,6 +760,8 @@ struct SkPlan {
     unsigned grid;
     size_t lds;
     int64_t ws_bytes;   // workspace the plan needs (0 for S == 1)
+    int streamed = 0;   // k_bsks_w4a4 (int4, one pass per block and range) instead of k_bsk_*
+    int tpl = 2;        // streamed: tiles per lane
 };
 
 // Workspace layout: a fixed area of arrival counters (one uint32 per set,
@@ -583,6 +816,49 @@ static bool sk_plan(int dtype, int64_t M, int64_t K, int64_t N, int64_t payload_
     return true;
 }
 
+// Plan for the streamed int4 kernel: S >= 2 K ranges of at most 32 TPL
+// tiles (TPL 2 or 3), sets of at most SKS_NBLK blocks, and no more
+// workgroups than CUs (each holds most of the LDS, so a workgroup past the
+// CU count would wait for a whole one to finish): the fewest blocks per set
+// that allow it. Slots of one KB per row segment when the average segment
+// plus 30 % and 64 B of windows fits one, else two; a block with a longer
+// segment reads its windows from global memory.
+static bool sks_plan(int64_t M, int64_t K, int64_t N, int64_t payload_bytes, int S, SkPlan *p) {
+    if (M <= 0 || K <= 0 || N < 1 || N > 32 || S < 2 || S > SK_NBS_MAX) return false;
+    const int64_t T = (K + 63) / 64, blocks = (M + 15) / 16;
+    if (M * T + 1 > (int64_t)UINT32_MAX / 8) return false;          // 32-bit buffer ranges of words and offsets
+    {
+        const int64_t tps = (T + S - 1) / S;
+        if (tps < 2 || (S - 1) * tps >= T) return false;              // every split holds tiles
+        const int tpl = tps <= 64 ? 2 : 3;
+        if (tps > 32 * tpl) return false;
+        for (int nbs = 1; nbs <= SKS_NBLK; ++nbs) {
+            const int64_t nsets = (blocks + nbs - 1) / nbs;
+            if (nsets * S > BT_CUS || nsets > SK_WS_COUNTERS) continue;
+            const int64_t seg_avg = payload_bytes * tps / std::max<int64_t>(M * T, 1);
+            const int iseg = seg_avg + seg_avg * 3 / 10 + 64 <= 1024 ? 1 : 2;
+            const int nb = N <= 16 ? 1 : 2;
+            const size_t lds = bsks_w4a4_lds(nb, nbs, iseg);
+            if (lds > 160 * 1024) continue;
+            p->dtype = BSP_INT4;
+            p->nwaves = SKS_WAVES;
+            p->nb = nb;
+            p->nbs = nbs;
+            p->S = S;
+            p->tps = (int)tps;
+            p->iseg = iseg;
+            p->nsets = (int)nsets;
+            p->grid = (unsigned)(nsets * S);
+            p->lds = lds;
+            p->ws_bytes = sk_ws_counters_bytes() + nsets * nbs * S * N * 16 * 4;
+            p->streamed = 1;
+            p->tpl = tpl;
+            return true;
+        }
+    }
+    return false;
+}
+
 static SkArgs sk_args(const SkPlan &p, const uint64_t *bitmaps, const uint32_t *offsets, const void *payload,
                       uint32_t payload_bytes, int M, int K, const void *X, int N, void *Y, void *workspace) {
     SkArgs a;
@@ -594,8 +870,27 @@ static SkArgs sk_args(const SkPlan &p, const uint64_t *bitmaps, const uint32_t *
     return a;
 }
 
+template <int NB, int TPL, int ISEG, bool XU>
+static void launch_bsks_t(const SkPlan &p, const SkArgs &a, hipStream_t stream) {
+    (void)hipFuncSetAttribute((const void *)k_bsks_w4a4<NB, TPL, ISEG, XU>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)p.lds);
+    hipLaunchKernelGGL((k_bsks_w4a4<NB, TPL, ISEG, XU>), dim3(p.grid), dim3(64 * SKS_WAVES), p.lds, stream, a);
+}
+
+template <int NB, int TPL>
+static void launch_bsks_i(const SkPlan &p, const SkArgs &a, bool xu, hipStream_t stream) {
+    if (p.iseg == 1) { if (xu) launch_bsks_t<NB, TPL, 1, true>(p, a, stream); else launch_bsks_t<NB, TPL, 1, false>(p, a, stream); }
+    else { if (xu) launch_bsks_t<NB, TPL, 2, true>(p, a, stream); else launch_bsks_t<NB, TPL, 2, false>(p, a, stream); }
+}
+
 static void launch_bsk(const SkPlan &p, const SkArgs &a, hipStream_t stream) {
     const dim3 grid(p.grid), block(64 * p.nwaves);
+    if (p.streamed) {
+        const bool xu = a.K % 8 != 0;
+        if (p.nb == 1) { if (p.tpl == 2) launch_bsks_i<1, 2>(p, a, xu, stream); else launch_bsks_i<1, 3>(p, a, xu, stream); }
+        else { if (p.tpl == 2) launch_bsks_i<2, 2>(p, a, xu, stream); else launch_bsks_i<2, 3>(p, a, xu, stream); }
+        return;
+    }
     if (p.dtype == BSP_INT4) {
         const bool xu = a.K % 8 != 0;
 #define SK_L4(NB, XU)                                                                                       \

@@ -103,6 +103,10 @@ bool plan_mfma(int dtype, const Shape &s, int64_t pbytes, Plan *p) {
 bool plan_splitk(int dtype, const Shape &s, int64_t pbytes, int splits, Plan *p) {
     p->algo = BSP_ALGO_SPLITK;
     if (dtype == BSP_FP16 && s.K % 8 != 0) return false;
+    if (dtype == BSP_INT4 && splits > 1 && sks_plan(s.M, s.K, s.N, pbytes, splits, &p->sk)) {
+        p->kind = PK_BSK;
+        return true;
+    }
     for (; splits >= 1; splits /= 2)
         if (sk_plan(dtype, s.M, s.K, s.N, pbytes, splits, &p->sk)) {
             p->kind = PK_BSK;
@@ -166,6 +170,12 @@ void describe_plan(int dtype, const Plan &p, char *launch, size_t n) {
             snprintf(launch, n, " kernel=k_bt64_f16 grid=%u block=%d lds=%zu", p.bf.grid, 64 * p.bf.nwaves, p.bf.lds);
             break;
         case PK_BSK:
+            if (p.sk.streamed) {
+                snprintf(launch, n, " kernel=k_bsks_w4a4 grid=%u block=%d lds=%zu blocks_per_set=%d splits=%d "
+                         "tiles_per_split=%d tiles_per_lane=%d slot_kb=%d workspace=%lld", p.sk.grid, 64 * p.sk.nwaves,
+                         p.sk.lds, p.sk.nbs, p.sk.S, p.sk.tps, p.sk.tpl, p.sk.iseg, (long long)p.sk.ws_bytes);
+                break;
+            }
             snprintf(launch, n, " kernel=k_bsk_%s grid=%u block=%d lds=%zu blocks_per_set=%d splits=%d "
                      "tiles_per_split=%d chunk_tiles=%d slot_kb=%d workspace=%lld",
                      dtype == BSP_INT4 ? "w4a4" : "f16", p.sk.grid, 64 * p.sk.nwaves, p.sk.lds, p.sk.nbs, p.sk.S,
@@ -177,15 +187,22 @@ void describe_plan(int dtype, const Plan &p, char *launch, size_t n) {
     }
 }
 
-int describe(int dtype, int64_t M, int64_t K, int64_t N, int64_t nnz, bool have_ws, char *buf, size_t n) {
+int describe(int dtype, int64_t M, int64_t K, int64_t N, int64_t nnz, bool have_ws, char *buf, size_t n,
+             int algo = BSP_ALGO_AUTO) {
     if (dtype != BSP_INT4 && dtype != BSP_FP16) return BSP_E_ARG;
     if (M < 0 || K < 0 || N < 0 || N > BSP_MAX_N || buf == nullptr || n == 0) return BSP_E_ARG;
+    if (algo < BSP_ALGO_AUTO || algo > BSP_ALGO_SPLITK) return BSP_E_ARG;
     const Shape s{M, K, N, (K + 63) / 64, M * ((K + 63) / 64)};
     // payload bytes the encoder writes for nnz nonzeros (all of W when unknown)
     const int64_t nz = nnz >= 0 ? nnz : M * K;
     const int64_t pbytes = dtype == BSP_INT4 ? (nz + 1) / 2 : 2 * nz;
     Plan p;
-    choose_plan(dtype, s, pbytes, BSP_ALGO_AUTO, have_ws, &p);
+    const int rc = choose_plan(dtype, s, pbytes, algo, have_ws, &p);
+    if (rc != BSP_OK) {
+        snprintf(buf, n, "dtype=%s M=%lld K=%lld N=%lld nnz=%lld -> unsupported", dtype == BSP_INT4 ? "int4" : "fp16",
+                 (long long)M, (long long)K, (long long)N, (long long)nnz);
+        return rc;
+    }
     const char *name = p.algo == BSP_ALGO_ROWWAVE ? "rowwave" : p.algo == BSP_ALGO_MFMA ? "mfma" : "splitk";
     char launch[256] = "";
     if (M > 0 && N > 0) describe_plan(dtype, p, launch, sizeof launch);
@@ -336,6 +353,11 @@ extern "C" int bsp_describe_selection(int dtype, int64_t M, int64_t K, int64_t N
 extern "C" int bsp_describe_selection_ws(int dtype, int64_t M, int64_t K, int64_t N, int64_t nnz, char *buf,
                                          size_t n) {
     return describe(dtype, M, K, N, nnz, true, buf, n);
+}
+
+extern "C" int bsp_describe_plan(int dtype, int64_t M, int64_t K, int64_t N, int64_t nnz, int algo, int with_workspace,
+                                 char *buf, size_t n) {
+    return describe(dtype, M, K, N, nnz, with_workspace != 0, buf, n, algo);
 }
 
 extern "C" int bsp_workspace_bytes(int dtype, int64_t M, int64_t K, int64_t N, int64_t nnz, int64_t *bytes) {

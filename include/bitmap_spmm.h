@@ -245,6 +245,14 @@ int bsp_describe_selection(int dtype, int64_t M, int64_t K, int64_t N, int64_t n
  * workspace of bsp_workspace_bytes. */
 int bsp_describe_selection_ws(int dtype, int64_t M, int64_t K, int64_t N, int64_t nnz, char *buf, size_t n);
 
+/* The plan an explicit kernel choice takes: `algo` (a bsp_algo) through the
+ * *_algo entry points (with_workspace 0) or the *_ws ones given a workspace
+ * of bsp_workspace_bytes (with_workspace 1), described as above. Returns
+ * BSP_E_UNSUPPORTED (and a description saying so) when that choice cannot
+ * run the shape, BSP_E_ARG for an unknown dtype or algo. Host only. */
+int bsp_describe_plan(int dtype, int64_t M, int64_t K, int64_t N, int64_t nnz, int algo, int with_workspace,
+                      char *buf, size_t n);
+
 /*
  * spmm_bitmap_w2a4 -- Y = W * X with W's values 2-bit (encoded with dtype
  * BSP_INT2: the W2A4 setting of UnionSparse Sec. VII, Fig. 11) and X packed

@@ -469,6 +469,36 @@ def test_splitk_w4a4(dev, M, K, N, keep, with_ws):
         assert not ws[:65536].any(), "arrival counters left nonzero"
 
 
+SPLITK_STREAMED = [  # (M, K, N, keep): the streamed split-K kernel (one pass per block and K range)
+    (100, 64 * 65, 3, 0.5),      # two tiles per lane, ragged last block
+    (513, 6000, 17, 0.5),        # two column blocks, ragged last tile
+    (2000, 12287, 32, 0.3),      # three tiles per lane, X rows off a 4-byte boundary, 250 workgroups
+    (48, 8200, 1, 0.95),         # 2 KB slots
+    (4096, 8192, 8, 0.5),        # two blocks per set, 256 workgroups
+    (16, 64 * 65 + 4, 1, 0.5),   # one block
+    (4100, 11008, 16, 0.3),      # three blocks per set, the last set of two, the last block of 4 rows
+]
+
+
+@pytest.mark.parametrize("M,K,N,keep", SPLITK_STREAMED)
+def test_splitk_streamed_w4a4(dev, M, K, N, keep):
+    p = workloads.random_int4_problem(M * 7 + K + N, M, K, N, keep=keep)
+    enc = bsp.encode(p.W)
+    d = bsp.describe(bsp.INT4, M, K, N, enc.nnz, workspace=True, algo=bsp.ALGO_SPLITK)
+    assert "kernel=k_bsks_w4a4" in d, d
+    dm = enc.to_device(dev)
+    Xd = torch.from_numpy(bsp.pack_int4(p.X)).to(dev)
+    ws = _ws(bsp.INT4, M, K, N, enc.nnz, dev)
+    ref = oracle_w4a4(p.W, p.X)
+    for rep in range(2):   # the second call reuses the workspace (its counters were reset)
+        big, Y = _y_with_canary(N, M, torch.int32, dev)
+        bsp.spmm_w4a4(dm, Xd, N, Y=Y, algo=bsp.ALGO_SPLITK, workspace=ws)
+        torch.cuda.synchronize()
+        assert _canary_ok(big, N, M, torch.int32), "write past the end of Y"
+        assert np.array_equal(Y.cpu().numpy(), ref), f"call {rep}: {d}"
+    assert not ws[:65536].any(), "arrival counters left nonzero"
+
+
 SPLITK_F16 = [(4096, 11008, 8), (100, 5000, 1), (257, 64 * 130 + 8, 16), (33, 8192, 32), (64, 4096, 32),
               (4100, 4096, 17), (17, 64 * 65, 3)]
 

@@ -262,3 +262,47 @@ def test_description_names_the_launched_kernel():
     assert bsp.describe(bsp.FP16, 64, 100, 4).endswith("-> rowwave kernel=k_rowwave_f16")
     # nothing to launch
     assert "kernel=" not in bsp.describe(bsp.INT4, 0, 4096, 8)
+
+
+def test_describe_plan_of_forced_choices():
+    # bsp_describe_plan: the plan an explicit choice takes, or E_UNSUPPORTED
+    nnz = int(4096 * 11008 * 0.3)
+    d = bsp.describe(bsp.INT4, 4096, 11008, 16, nnz, workspace=True, algo=bsp.ALGO_SPLITK)
+    assert "kernel=k_bsks_w4a4" in d and "splits=2 " in d and "blocks_per_set=2 " in d and "grid=256 " in d, d
+    d = bsp.describe(bsp.INT4, 4096, 11008, 16, nnz, workspace=False, algo=bsp.ALGO_SPLITK)
+    assert "kernel=k_bsk_w4a4" in d and "splits=1 " in d, d          # no workspace: one range
+    d = bsp.describe(bsp.INT4, 300, 24616, 8, -1, workspace=True, algo=bsp.ALGO_SPLITK)
+    assert "kernel=k_bsk_w4a4" in d and "splits=2 " in d, d          # ranges past 96 tiles: chunked
+    with pytest.raises(bsp.BspError) as ei:
+        bsp.describe(bsp.FP16, 100, 4100, 3, algo=bsp.ALGO_MFMA)
+    assert ei.value.status == bsp.E_UNSUPPORTED
+    assert bsp.describe(bsp.INT4, 12288, 4096, 8, algo=bsp.ALGO_MFMA) == bsp.describe(bsp.INT4, 12288, 4096, 8)
+    assert "kernel=k_rowwave_w4a4" in bsp.describe(bsp.INT4, 64, 640, 2, algo=bsp.ALGO_ROWWAVE)
+
+
+def test_streamed_splitk_plans_fit():
+    # every streamed split-K plan: one workgroup per CU at most, its LDS
+    # within 160 KB, each K range within its lanes' tiles, and a workspace
+    # of counters plus one int32 partial per (block, range, column, row)
+    rng = np.random.default_rng(11)
+    seen = 0
+    for _ in range(400):
+        M = int(rng.integers(1, 9000))
+        K = int(rng.integers(64 * 64 + 1, 64 * 200))
+        N = int(rng.integers(1, 33))
+        keep = float(rng.uniform(0.02, 1.0))
+        nnz = int(M * K * keep)
+        d = bsp.describe(bsp.INT4, M, K, N, nnz, workspace=True, algo=bsp.ALGO_SPLITK)
+        if "k_bsks_w4a4" not in d:
+            continue
+        seen += 1
+        f = {k: int(v) for k, v in re.findall(r"(\w+)=(\d+)", d.split("->")[1])}
+        T, blocks = -(-K // 64), -(-M // 16)
+        assert f["grid"] <= 256 and f["lds"] <= 160 * 1024 and f["block"] == 512, d
+        assert f["tiles_per_split"] <= 32 * f["tiles_per_lane"] and f["tiles_per_lane"] in (2, 3), d
+        assert (f["splits"] - 1) * f["tiles_per_split"] < T <= f["splits"] * f["tiles_per_split"], d
+        nsets = -(-blocks // f["blocks_per_set"])
+        assert f["grid"] == nsets * f["splits"] and 1 <= f["blocks_per_set"] <= 3, d
+        assert f["workspace"] == 65536 + nsets * f["blocks_per_set"] * f["splits"] * N * 16 * 4, d
+        assert bsp.workspace_bytes(bsp.INT4, M, K, N, nnz) >= f["workspace"], d
+    assert seen > 50

@@ -278,6 +278,10 @@ def test_describe_plan_of_forced_choices():
     assert ei.value.status == bsp.E_UNSUPPORTED
     assert bsp.describe(bsp.INT4, 12288, 4096, 8, algo=bsp.ALGO_MFMA) == bsp.describe(bsp.INT4, 12288, 4096, 8)
     assert "kernel=k_rowwave_w4a4" in bsp.describe(bsp.INT4, 64, 640, 2, algo=bsp.ALGO_ROWWAVE)
+    for bad in (-1, 4, 99):
+        with pytest.raises(bsp.BspError) as ei:
+            bsp.describe(bsp.INT4, 64, 640, 2, algo=bad)
+        assert ei.value.status == bsp.E_ARG
 
 
 def test_streamed_splitk_plans_fit():

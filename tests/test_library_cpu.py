@@ -310,3 +310,37 @@ def test_streamed_splitk_plans_fit():
         assert f["workspace"] == 65536 + nsets * f["blocks_per_set"] * f["splits"] * N * 16 * 4, d
         assert bsp.workspace_bytes(bsp.INT4, M, K, N, nnz) >= f["workspace"], d
     assert seen > 50
+
+
+def test_every_plan_fits_the_hardware():
+    # every described launch (automatic or forced, with or without a
+    # workspace, int4 or fp16): LDS within gfx950's 160 KB per workgroup, a
+    # whole number of wavefronts up to 1024 threads, at least one workgroup
+    rng = np.random.default_rng(5)
+    seen = set()
+    for _ in range(600):
+        dt = bsp.INT4 if rng.random() < 0.6 else bsp.FP16
+        M = int(rng.integers(1, 70000))
+        K = int(rng.integers(1, 40000))
+        if dt == bsp.FP16 and rng.random() < 0.7:
+            K = K // 8 * 8 + 8
+        N = int(rng.integers(1, 33))
+        nnz = int(M * K * rng.uniform(0.02, 1.0))
+        for algo in (bsp.ALGO_AUTO, bsp.ALGO_ROWWAVE, bsp.ALGO_MFMA, bsp.ALGO_SPLITK):
+            for ws in (False, True):
+                try:
+                    d = bsp.describe(dt, M, K, N, nnz, workspace=ws, algo=algo)
+                except bsp.BspError as e:
+                    assert e.status == bsp.E_UNSUPPORTED and algo != bsp.ALGO_AUTO, d
+                    continue
+                m = re.search(r"kernel=(\S+)", d)
+                assert m, d
+                seen.add(m.group(1))
+                f = {k: int(v) for k, v in re.findall(r"(\w+)=(\d+)", d.split("->")[1])}
+                if "lds" in f:
+                    assert f["lds"] <= 160 * 1024, d
+                    assert 64 <= f["block"] <= 1024 and f["block"] % 64 == 0, d
+                    assert f["grid"] >= 1, d
+    want = {"k_bt64s_w4a4", "k_bt64_w4a4", "k_bsk_w4a4", "k_bsks_w4a4", "k_bt8_f16", "k_bt64_f16", "k_bsk_f16",
+            "k_rowwave_w4a4", "k_rowwave_f16"}
+    assert want <= seen, want - seen

@@ -1105,11 +1105,18 @@ static bool bt64_plan(int64_t M, int64_t K, int64_t N, int64_t payload_bytes, Bt
         // falls on the same banks (elsewhere the plain layout does as well or
         // better)
         const int64_t rb = (payload_bytes / std::max<int64_t>(M, 1)) % 256;
-        const int stagger = std::min<int64_t>(rb, 256 - rb) < 28;
+        int stagger = std::min<int64_t>(rb, 256 - rb) < 28;
         const int64_t need = (stagger ? est * (BTS_RUN + BTS_OVL) / BTS_RUN : est) + 1023;
         const int64_t area_kb = std::min<int64_t>(4 * p->nwaves, std::max<int64_t>(2 * p->nwaves, need / 1024));
         const int d = (int)((area_kb + p->nwaves - 1) / p->nwaves);   // DMA instructions per wavefront at most
-        if (per_wg <= BTS_NBLK && (int64_t)bts_lds(p->nwaves, p->nb, area_kb, per_wg) <= budget) {
+        // bytes an area holds; when the average block (plus its window
+        // granule) does not fit the staggered layout the plain one is taken,
+        // and when it fits neither, most blocks would read their windows from
+        // global memory: the ring kernel stages them instead (12288 x 4096
+        // at density 0.99: 16.2 us streaming, 11.4 in the ring kernel)
+        if (stagger && avg + 64 > area_kb * 1024 * BTS_RUN / (BTS_RUN + BTS_OVL)) stagger = 0;
+        const bool avg_fits = avg + 64 <= area_kb * 1024;
+        if (per_wg <= BTS_NBLK && avg_fits && (int64_t)bts_lds(p->nwaves, p->nb, area_kb, per_wg) <= budget) {
             p->streaming = d;
             p->area_kb = (int)area_kb;
             p->stagger = stagger;

@@ -344,3 +344,17 @@ def test_every_plan_fits_the_hardware():
     want = {"k_bt64s_w4a4", "k_bt64_w4a4", "k_bsk_w4a4", "k_bsks_w4a4", "k_bt8_f16", "k_bt64_f16", "k_bsk_f16",
             "k_rowwave_w4a4", "k_rowwave_f16"}
     assert want <= seen, want - seen
+
+
+def test_streaming_plan_density_rule():
+    # the streaming kernel keeps its staggered staging while the average block
+    # fits it, drops the stagger when only the plain layout holds the average
+    # block, and leaves fully dense blocks (which fit neither area) to the ring
+    # kernel, whose staging holds a whole dense block
+    M, K, N = 12288, 4096, 8
+    d50 = bsp.describe(bsp.INT4, M, K, N, M * K // 2)
+    assert "kernel=k_bt64s_w4a4" in d50 and "stagger=1" in d50, d50
+    d99 = bsp.describe(bsp.INT4, M, K, N, int(M * K * 0.99))
+    assert "kernel=k_bt64s_w4a4" in d99 and "stagger=0" in d99, d99
+    d100 = bsp.describe(bsp.INT4, M, K, N, M * K)
+    assert "kernel=k_bt64_w4a4 " in d100 and "one_pass=1" in d100, d100

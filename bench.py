@@ -547,17 +547,20 @@ def prepare(args, workload, index, n):
     dev = torch.device("cuda:0")
     bsp.load_library()
     if workload.startswith("custom:"):
-        # custom:DTYPE:M:K:N:DENSITY[:SEED] -- a seeded random problem of any
-        # shape (selection A/B runs on shapes outside the named workloads)
+        # custom:DTYPE:M:K:N:DENSITY[:SEED[:rows]] -- a seeded random problem
+        # of any shape (selection A/B runs on shapes outside the named
+        # workloads); "rows": every row keeps the same count
         parts = workload.split(":")
         dty, Mc, Kc, Nc, dens = parts[1], int(parts[2]), int(parts[3]), int(parts[4]), float(parts[5])
         seed = int(parts[6]) if len(parts) > 6 else 12345
+        rows = len(parts) > 7 and parts[7] == "rows"
+        tag = "_rows" if rows else ""
         if dty == "int4":
-            problems = [workloads.random_int4_problem(seed, Mc, Kc, Nc, keep=dens,
-                                                      name=f"custom_int4_{Mc}x{Kc}_d{dens:g}")]
+            problems = [workloads.random_int4_problem(seed, Mc, Kc, Nc, keep=dens, rows=rows,
+                                                      name=f"custom_int4_{Mc}x{Kc}_d{dens:g}{tag}")]
         else:
-            problems = [workloads.random_fp16_problem(seed, Mc, Kc, Nc, sparsity=1.0 - dens,
-                                                      name=f"custom_fp16_{Mc}x{Kc}_d{dens:g}")]
+            problems = [workloads.random_fp16_problem(seed, Mc, Kc, Nc, sparsity=1.0 - dens, rows=rows,
+                                                      name=f"custom_fp16_{Mc}x{Kc}_d{dens:g}{tag}")]
     else:
         problems = workloads.make(workload)
     problem = problems[index]
@@ -977,7 +980,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="qkv",
-                    help="tiny | qkv | ffn | lowsparse | fp16 | custom:DTYPE:M:K:N:DENSITY[:SEED]")
+                    help="tiny | qkv | ffn | lowsparse | fp16 | custom:DTYPE:M:K:N:DENSITY[:SEED[:rows]]")
     ap.add_argument("--index", type=int, default=0, help="matrix index inside the workload (ffn: 0 up, 1 down)")
     ap.add_argument("--n", type=int, default=0, help="override N (slices the workload's widest X)")
     ap.add_argument("--algo", default="auto", choices=["auto", "rowwave", "mfma", "splitk"])

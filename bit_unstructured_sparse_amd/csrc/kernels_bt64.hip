@@ -408,7 +408,17 @@ __device__ __forceinline__ BtRange bt_range(uint32_t nibA, uint32_t nibB) {
 //   [nbuf staging buffers of stage_bytes]
 // Workgroup g owns blocks [g*bq + min(g, br), ...): bq or bq + 1 of them.
 // XU: X rows are not on a 4-byte boundary (K % 8 != 0).
-template <int NB, int TPL, bool XU>
+// STG: staggered staging. Rows whose length is a multiple of 64 B put the
+// same tile of the 16 rows of a block on the same LDS banks (every row keeps
+// the same count when each output row is pruned on its own). Staggered, DMA
+// instruction j of a block stores its 1 KB with granules 61 j .. 61 j + 63 of
+// the stream: each run of 61 granules is followed by the first 3 of the next
+// (a tile's windows reach < 48 B past its first nonzero, so they stay inside
+// the instruction of its start), and every 61 granules the stream moves 48 B
+// further round the banks, so equal rows no longer line up.
+#define BT_R61_RUN 61u
+#define BT_R61_MAG 2200291u   // ceil(2^32 / (61 * 32)): umulhi(p, MAG) = p / 1952 for p < 2^20
+template <int NB, int TPL, bool XU, bool STG>
 // (The arguments the first loads need come first: they are the ones a
 // kernel-argument preload would place in registers.)
 __global__ __launch_bounds__(BT_WG_THREADS(TPL)) void k_bt64_w4a4(
@@ -546,17 +556,20 @@ __global__ __launch_bounds__(BT_WG_THREADS(TPL)) void k_bt64_w4a4(
     // have to wait for the DMAs too (the counter is in order, the loop's
     // length unknown to the compiler)
     uint32_t vm_mark[NBLK];
+    constexpr uint32_t RUN = STG ? BT_R61_RUN : 64u;   // stream granules per 1 KB DMA instruction
     auto fits = [&](int i) -> bool {
         const BtRange g = bt_range(nib[i], nib[i + 1]);
-        return g.n * 16u <= stage_bytes;
+        return (g.n + RUN - 1u) / RUN * 1024u <= stage_bytes;
     };
     auto issue_block = [&](int i) -> void {
         if (fits(i)) {
             const BtRange g = bt_range(nib[i], nib[i + 1]);
             uint8_t *buf = stage + (uint32_t)(i % (int)nbuf) * stage_bytes;
-            const uint32_t n_ins = (g.n + 63u) >> 6;
+            // lane 0 of every instruction stores a granule of the block, so
+            // each one issues (and counts)
+            const uint32_t n_ins = (g.n + RUN - 1u) / RUN;
             for (uint32_t j = (uint32_t)wave; j < n_ins; j += (uint32_t)nwaves) {
-                const uint32_t u = j * 64u + (uint32_t)lane;
+                const uint32_t u = j * RUN + (uint32_t)lane;
                 if (u < g.n)
                     __builtin_amdgcn_raw_ptr_buffer_load_lds(prs, (bt_lds_void *)(buf + j * 1024u), 16,
                                                              (g.g0 + u) * 16u, 0, 0, BT_NT);
@@ -644,8 +657,14 @@ __global__ __launch_bounds__(BT_WG_THREADS(TPL)) void k_bt64_w4a4(
             // a corrupt stream stays inside the staged granules
             p = min(p, 8u * (4u * g.n - 2u));
             // twice the buffer's address (a multiple of 32) keeps p & 7
-            p += 2u * bt_lds_addr(stage + (uint32_t)(i % (int)nbuf) * stage_bytes);
-            bt_contract<NB, TPL>(words[i], p, BtWinLds{}, lut_base, xb, acc);
+            const uint32_t base2 = 2u * bt_lds_addr(stage + (uint32_t)(i % (int)nbuf) * stage_bytes);
+            if constexpr (STG) {
+                // stream nibble pt sits 3 granules (96 nibbles) further per run of 61 before it
+                const auto tmap = [=](uint32_t pt) { return pt + base2 + __umulhi(pt, BT_R61_MAG) * 96u; };
+                bt_contract<NB, TPL, BtWinLds, decltype(tmap)>(words[i], p, BtWinLds{}, lut_base, xb, acc, tmap);
+            } else {
+                bt_contract<NB, TPL>(words[i], p + base2, BtWinLds{}, lut_base, xb, acc);
+            }
         } else {
             bt_contract<NB, TPL>(words[i], p, BtWinGlobal{prs, 4u * g.g0}, lut_base, xb, acc);
         }
@@ -1039,7 +1058,7 @@ struct BtPlan {
     uint32_t stage_bytes;   // one staging buffer
     uint32_t nbuf;          // staging buffers in the ring
     int streaming;          // > 0: the streaming variant k_bt64s_w4a4, at most this many DMA instructions per wavefront and block
-    int stagger;            // streaming variant: staggered staging (rows near a multiple of 256 B long)
+    int stagger;            // staggered staging (rows near a multiple of 256 B, ring kernel 64 B, long)
     int area_kb;            // streaming variant: KB of staging per block
     int one_pass;           // every block staged at once: one barrier before and one after the decode
     size_t lds;             // total dynamic LDS
@@ -1061,51 +1080,93 @@ static bool bt64_plan(int64_t M, int64_t K, int64_t N, int64_t payload_bytes, Bt
     const int64_t nblk_max = BT_NBLK(p->tpl);
     const int64_t blocks = (M + BT_ROWS - 1) / BT_ROWS;
     // one workgroup per CU when that leaves each at most nblk_max blocks
-    const int64_t grid = std::max<int64_t>(std::min<int64_t>(blocks, BT_CUS), (blocks + nblk_max - 1) / nblk_max);
-    p->grid = (unsigned)grid;
-    p->bq = (int)(blocks / grid);
-    p->br = (int)(blocks % grid);
-    const int64_t per_wg = (blocks + grid - 1) / grid;                  // blocks of the busiest workgroup
-    const int64_t wg_per_cu = (grid + BT_CUS - 1) / BT_CUS;
-    const int64_t budget = BT_LDS_MAX / wg_per_cu;
+    const int64_t grid0 = std::max<int64_t>(std::min<int64_t>(blocks, BT_CUS), (blocks + nblk_max - 1) / nblk_max);
+    const int64_t per_wg0 = (blocks + grid0 - 1) / grid0;                 // blocks of the busiest workgroup
+    const int64_t wg_per_cu = (grid0 + BT_CUS - 1) / BT_CUS;
     // Staging: 1.2x the average block plus 2 KB (a denser block falls back
-    // to global-memory windows), capped at the densest block.
+    // to global-memory windows), capped at the densest block; staggered, in
+    // whole runs of 61 granules per KB.
     const int64_t avg = payload_bytes / std::max<int64_t>(blocks, 1);
     const int64_t worst = (int64_t)BT_ROWS * T * 8 * wb + 64;   // a fully dense block
-    int64_t stage = std::min<int64_t>(worst, avg + avg / 5 + 2048) + 32;
-    stage = (stage + 1023) / 1024 * 1024;
+    const int64_t est = std::min<int64_t>(worst, avg + avg / 5 + 2048) + 32;
     const int64_t fixed = BT_LUT_BYTES + nblk_max * BT_ROWS * (BT_WG_THREADS(p->tpl) / 64) * 4 + 3 * p->nb * 256 * 4;
-    int64_t nbuf = (budget - fixed) / stage;
-    nbuf = std::min(nbuf, per_wg);
-    // a buffer is refilled one block after it was decoded, so a ring of one
-    // works only when it never refills
-    if (nbuf < std::min<int64_t>(2, per_wg)) {
+    struct Fit {
+        int64_t stage, grid, per_wg, budget, nbuf, one_pass;
+    };
+    // A buffer is refilled one block after it was decoded, so a ring of one
+    // works only when it never refills. When the workgroups sharing a CU
+    // leave too little for two buffers, size for one resident workgroup per
+    // CU (the grid then runs in rounds; int4 at N = 8: 8192 x 16384 51.6 ->
+    // 25.1 us, 16384 x 8192 31.1 -> 21.8, 65536 x 4096 48.3 -> 42.6); when
+    // that is still short, one block per workgroup (8192 x 8192 at density
+    // 0.9: 24.8 -> 15.7 us). nbuf = 0: the blocks are too dense to stage.
+    const auto fit = [&](bool stg) -> Fit {
+        Fit f{(stg ? (est / 16 + BT_R61_RUN) / BT_R61_RUN : (est + 1023) / 1024) * 1024, grid0, per_wg0,
+              BT_LDS_MAX / wg_per_cu, 0};
+        f.nbuf = std::min((f.budget - fixed) / f.stage, f.per_wg);
+        if (f.nbuf < std::min<int64_t>(2, f.per_wg) && wg_per_cu > 1) {
+            f.budget = BT_LDS_MAX;
+            f.nbuf = std::min((f.budget - fixed) / f.stage, f.per_wg);
+        }
+        if (f.nbuf < std::min<int64_t>(2, f.per_wg) && f.per_wg > 1 && fixed + f.stage <= BT_LDS_MAX) {
+            f.grid = blocks;
+            f.per_wg = 1;
+            f.budget = BT_LDS_MAX;
+            f.nbuf = 1;
+        }
+        if (f.nbuf < std::min<int64_t>(2, f.per_wg)) f.nbuf = 0;
+        // all of a workgroup's blocks staged at once, with room for
+        // per-wavefront partials: decode without a barrier between blocks
+        const int64_t st = f.nbuf ? f.stage : 0, nb = std::max<int64_t>(f.nbuf, 1);
+        f.one_pass = nblk_max > 1 && (st == 0 || nb >= f.per_wg) &&
+                     fixed + nb * st + f.per_wg * p->nwaves * p->nb * 256 * 4 <= f.budget;
+        return f;
+    };
+    // Staggered when the average row is within 12 B of a multiple of 64 B
+    // and the staggered buffers hold as many blocks as the plain ones, in
+    // the same number of passes (rows of one length, int4 at N = 8: 4096 x
+    // 14336 14.75 -> 12.16 us, 4096 x 11008 at N = 16 12.34 -> 11.38,
+    // 5120 x 5120 10.11 -> 9.39; iid masks 4096 x 16384 13.97 -> 13.04,
+    // 4096 x 11008 11.39 / 11.47)
+    const int64_t rb64 = (payload_bytes / std::max<int64_t>(M, 1)) % 64;
+    Fit f = fit(false);
+    p->stagger = 0;
+    if (std::min<int64_t>(rb64, 64 - rb64) < 12 && f.nbuf > 0) {
+        const Fit fs = fit(true);
+        if (fs.nbuf == f.nbuf && fs.grid == f.grid && fs.one_pass == f.one_pass) {
+            f = fs;
+            p->stagger = 1;
+        }
+    }
+    int64_t stage = f.stage, nbuf = f.nbuf;
+    const int64_t per_wg = f.per_wg, budget = f.budget;
+    p->grid = (unsigned)f.grid;
+    p->bq = (int)(blocks / f.grid);
+    p->br = (int)(blocks % f.grid);
+    if (nbuf == 0) {
         // blocks too dense to stage: every block reads its windows from
         // global memory (a zero-byte staging buffer fits no block)
         stage = 0;
         nbuf = 1;
     }
-    // all of a workgroup's blocks staged at once, with room for per-wavefront
-    // partials: decode without a barrier between blocks
     const int64_t part = per_wg * p->nwaves * p->nb * 256 * 4;
-    p->one_pass = nblk_max > 1 && (stage == 0 || nbuf >= per_wg) && fixed + nbuf * stage + part <= budget;
+    p->one_pass = (int)f.one_pass;
     p->stage_bytes = (uint32_t)stage;
     p->nbuf = (uint32_t)nbuf;
     p->lds = (size_t)(fixed + nbuf * stage + (p->one_pass ? part : 0));
     // streaming variant: D KB per wavefront and block covers the same
     // estimate as the staging buffer above
     p->streaming = 0;
-    p->stagger = 0;
     if (p->tpl == 2) {
         // staging per block: the estimate above in whole KB (with 3 extra
         // granules per 64 when staggered), at least 2 KB per wavefront
-        const int64_t est = std::min<int64_t>(worst, avg + avg / 5 + 2048) + 32;
-        // average payload bytes per row, modulo the 256 B the LDS banks
-        // span: within 28 B of a multiple, the same tile of consecutive rows
-        // falls on the same banks (elsewhere the plain layout does as well or
-        // better)
-        const int64_t rb = (payload_bytes / std::max<int64_t>(M, 1)) % 256;
-        int stagger = std::min<int64_t>(rb, 256 - rb) < 28;
+        // average payload bytes per row within 28 B of a multiple of 128:
+        // the same tile of every row, or of every other row, falls on the
+        // same LDS banks when the rows are of one length (12288 x 4096 at N =
+        // 8, rows of 1152 B: 10.45 -> 9.13 us; iid masks of that density
+        // 9.11 / 9.28; elsewhere the plain layout does as well or better)
+        const int64_t rb = (payload_bytes / std::max<int64_t>(M, 1)) % 128;
+        int stagger = std::min<int64_t>(rb, 128 - rb) < 28;
         const int64_t need = (stagger ? est * (BTS_RUN + BTS_OVL) / BTS_RUN : est) + 1023;
         const int64_t area_kb = std::min<int64_t>(4 * p->nwaves, std::max<int64_t>(2 * p->nwaves, need / 1024));
         const int d = (int)((area_kb + p->nwaves - 1) / p->nwaves);   // DMA instructions per wavefront at most
@@ -1126,15 +1187,25 @@ static bool bt64_plan(int64_t M, int64_t K, int64_t N, int64_t payload_bytes, Bt
     return true;
 }
 
+template <int NB, int TPL, bool XU, bool STG>
+static void launch_bt64_s(const BtPlan &p, const uint64_t *bitmaps, const uint32_t *offsets,
+                          const uint8_t *payload, uint32_t payload_bytes, int M, int K, const uint8_t *X, int N,
+                          int32_t *Y, const BtEpi &e, hipStream_t stream) {
+    (void)hipFuncSetAttribute((const void *)k_bt64_w4a4<NB, TPL, XU, STG>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds);
+    hipLaunchKernelGGL((k_bt64_w4a4<NB, TPL, XU, STG>), dim3(p.grid), dim3(64 * p.nwaves), p.lds, stream, offsets, M, K,
+                       p.bq, p.br, bitmaps, X, N, payload, payload_bytes, Y, p.stage_bytes, p.nbuf, p.one_pass, e.Yh,
+                       e.sw, e.sx);
+}
+
 template <int NB, int TPL, bool XU>
 static void launch_bt64_t(const BtPlan &p, const uint64_t *bitmaps, const uint32_t *offsets,
                           const uint8_t *payload, uint32_t payload_bytes, int M, int K, const uint8_t *X, int N,
                           int32_t *Y, const BtEpi &e, hipStream_t stream) {
-    (void)hipFuncSetAttribute((const void *)k_bt64_w4a4<NB, TPL, XU>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              (int)p.lds);
-    hipLaunchKernelGGL((k_bt64_w4a4<NB, TPL, XU>), dim3(p.grid), dim3(64 * p.nwaves), p.lds, stream, offsets, M, K, p.bq,
-                       p.br, bitmaps, X, N, payload, payload_bytes, Y, p.stage_bytes, p.nbuf, p.one_pass, e.Yh, e.sw,
-                       e.sx);
+    if (p.stagger)
+        launch_bt64_s<NB, TPL, XU, true>(p, bitmaps, offsets, payload, payload_bytes, M, K, X, N, Y, e, stream);
+    else
+        launch_bt64_s<NB, TPL, XU, false>(p, bitmaps, offsets, payload, payload_bytes, M, K, X, N, Y, e, stream);
 }
 
 template <bool XU>

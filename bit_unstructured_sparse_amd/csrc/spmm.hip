@@ -117,8 +117,9 @@ bool plan_splitk(int dtype, const Shape &s, int64_t pbytes, int splits, Plan *p)
 
 // Shape-aware selection (UnionSparse, Sec. I, names it without a rule; the
 // thresholds are the measured ones recorded with the design). The MFMA block
-// kernels wherever they run (int4: K <= 16384; fp16: K <= 4096, K % 8 == 0):
-// on every shape both can run they measured faster than the split-K kernel
+// kernels wherever they run (int4: K <= 16384; fp16: K <= 4096, K % 8 == 0)
+// and stage their blocks in the LDS: on every such shape both can run they
+// measured faster than the split-K kernel
 // (4096 x 11008 int4 N = 16: 11.2 us against 14.9 / 16.9 with 1 / 2 K
 // ranges; 8192 x 8192 N = 32: 16.7 against 28.0; fp16 4096 x 4096 N = 32:
 // 16.2 against 25.3). Beyond them the split-K kernel (8-24 times faster than
@@ -144,7 +145,18 @@ int choose_plan(int dtype, const Shape &s, int64_t pbytes, int algo, bool have_w
         p->kind = PK_ROWWAVE;
         return BSP_OK;
     }
-    if (plan_mfma(dtype, s, pbytes, p)) return BSP_OK;
+    if (plan_mfma(dtype, s, pbytes, p)) {
+        // int4 blocks of 128 or more tiles too dense for the LDS (density
+        // above about 0.8): the ring kernel would read every window from
+        // global memory, the split-K kernel stages 64-tile chunks (4096 x
+        // 16384 at N = 8: 39.6 -> 20.6 us at density 0.85, 43.6 -> 21.2 at
+        // 0.95)
+        Plan sk;
+        if (p->kind == PK_BT64 && !p->bt.streaming && p->bt.tpl == 8 && p->bt.stage_bytes == 0 &&
+            plan_splitk(dtype, s, pbytes, have_ws ? preferred_splits(dtype, s) : 1, &sk))
+            *p = sk;
+        return BSP_OK;
+    }
     if (plan_splitk(dtype, s, pbytes, have_ws ? preferred_splits(dtype, s) : 1, p)) return BSP_OK;
     p->kind = PK_ROWWAVE;
     p->algo = BSP_ALGO_ROWWAVE;
@@ -159,15 +171,19 @@ void describe_plan(int dtype, const Plan &p, char *launch, size_t n) {
                 snprintf(launch, n, " kernel=k_bt64s_w4a4 grid=%u block=%d lds=%zu stage_kb=%d stagger=%d", p.bt.grid,
                          64 * p.bt.nwaves, p.bt.lds, p.bt.area_kb, p.bt.stagger);
             else
-                snprintf(launch, n, " kernel=k_bt64_w4a4 grid=%u block=%d lds=%zu tiles_per_lane=%d one_pass=%d",
-                         p.bt.grid, 64 * p.bt.nwaves, p.bt.lds, p.bt.tpl, p.bt.one_pass);
+                snprintf(launch, n,
+                         " kernel=k_bt64_w4a4 grid=%u block=%d lds=%zu tiles_per_lane=%d one_pass=%d stage_kb=%u "
+                         "stage_bufs=%u stagger=%d",
+                         p.bt.grid, 64 * p.bt.nwaves, p.bt.lds, p.bt.tpl, p.bt.one_pass, p.bt.stage_bytes / 1024,
+                         p.bt.nbuf, p.bt.stagger);
             break;
         case PK_BT8F16:
             snprintf(launch, n, " kernel=k_bt8_f16 grid=%u block=%d lds=%zu stage_kb=%u step_slots=%d", p.bf8.grid,
                      64 * p.bf8.nwaves, p.bf8.lds, p.bf8.area_kb, p.bf8.nstep);
             break;
         case PK_BT64F16:
-            snprintf(launch, n, " kernel=k_bt64_f16 grid=%u block=%d lds=%zu", p.bf.grid, 64 * p.bf.nwaves, p.bf.lds);
+            snprintf(launch, n, " kernel=k_bt64_f16 grid=%u block=%d lds=%zu stage_kb=%u stage_bufs=%u", p.bf.grid,
+                     64 * p.bf.nwaves, p.bf.lds, p.bf.stage_bytes / 1024, p.bf.nbuf);
             break;
         case PK_BSK:
             if (p.sk.streamed) {

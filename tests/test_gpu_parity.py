@@ -44,10 +44,11 @@ def dev():
 
 def mfma_kernel(dtype, M, K, N, nnz):
     """The MFMA kernel a forced-MFMA call launches, from the library's plan
-    (the automatic choice is the MFMA path for every shape inside it), or
-    None for a shape outside the MFMA path."""
-    d = bsp.describe(dtype, M, K, N, nnz)
-    if "-> mfma" not in d:
+    for that choice, or None for a shape outside the MFMA path."""
+    try:
+        d = bsp.describe(dtype, M, K, N, nnz, algo=bsp.ALGO_MFMA)
+    except bsp.BspError as e:
+        assert e.status == bsp.E_UNSUPPORTED, e
         return None
     k = re.search(r"kernel=(\w+)", d).group(1)
     assert k in MFMA_KERNELS[dtype], d
@@ -467,6 +468,62 @@ def test_splitk_w4a4(dev, M, K, N, keep, with_ws):
         assert np.array_equal(Y.cpu().numpy(), ref), f"call {rep}"
     if ws is not None:
         assert not ws[:65536].any(), "arrival counters left nonzero"
+
+
+LARGE_GRIDS = [  # (M, K, N, keep, rows): int4 plans past 256 workgroups, dense blocks, equal-length rows
+    (8192, 16384, 8, 0.5, False),    # one resident workgroup per CU, two rounds
+    (5000, 12001, 3, 0.5, False),    # 313 workgroups, ragged last block, X rows off a 4-byte boundary
+    (8192, 8192, 8, 0.9, False),     # one block per workgroup
+    (65536, 4096, 8, 0.5, False),    # four blocks per workgroup, four rounds
+    (4096, 16384, 8, 0.9, False),    # too dense to stage: split-K (auto), global windows (forced)
+    (4096, 16384, 8, 0.5, True),     # every row 4096 B long
+    (12288, 4096, 8, 0.5, True),     # every row 1024 B long: staggered streaming
+]
+
+
+@functools.lru_cache(maxsize=2)
+def _large_case(M, K, N, keep, rows):
+    p = workloads.random_int4_problem(M + K + N, M, K, N, keep=keep, rows=rows)
+    return p, oracle_w4a4(p.W, p.X)
+
+
+@pytest.mark.parametrize("algo", [bsp.ALGO_AUTO, bsp.ALGO_MFMA], ids=["auto", "mfma"])
+@pytest.mark.parametrize("M,K,N,keep,rows", LARGE_GRIDS)
+def test_w4a4_large_grids_and_equal_rows(dev, M, K, N, keep, rows, algo):
+    p, ref = _large_case(M, K, N, keep, rows)
+    assert_w4a4(run_w4a4(p.W, p.X, algo, dev), p.W, p.X, ref=ref)
+
+
+@pytest.mark.parametrize("algo", F16_ALGOS, ids=lambda a: _NAMES[a])
+@pytest.mark.parametrize("N", [1, 8, 32])
+def test_f16_equal_rows(dev, algo, N):
+    # every row pruned to the same count (rows 4096 B long)
+    p = workloads.random_fp16_problem(77 + N, 4096, 4096, N, sparsity=0.5, rows=True)
+    _assert_f16(run_f16(p.W, p.X, algo, dev), oracle.spmm_f16(oracle.encode(p.W), p.X))
+
+
+EQUAL_ROWS = [  # (M, K, N, keep): every row keeps the same count; staggered staging
+    (4096, 11008, 16, 0.5),    # ring, 8 tiles per lane
+    (5120, 5120, 8, 0.5),      # ring, 4 tiles per lane, one pass
+    (1000, 11008, 32, 0.5),    # ring, two column blocks, ragged last block
+    (13824, 5120, 8, 0.5),     # ring, 432 workgroups in rounds
+    (2000, 8193, 5, 0.5),      # ring, X rows off a 4-byte boundary
+    (8192, 8192, 8, 0.72),     # ring, two buffers per workgroup, refilled
+    (40000, 4096, 8, 0.25),    # ring, 2 tiles per lane, four blocks per workgroup, one pass
+    (20000, 4096, 8, 0.25),    # ring, 2 tiles per lane, three buffers for four blocks
+    (12288, 4096, 8, 0.5625),  # streaming kernel, rows of 1152 B
+    (3000, 4096, 17, 0.5),     # streaming kernel, two column blocks
+]
+
+
+@pytest.mark.parametrize("algo", [bsp.ALGO_AUTO, bsp.ALGO_MFMA], ids=["auto", "mfma"])
+@pytest.mark.parametrize("M,K,N,keep", EQUAL_ROWS)
+def test_w4a4_staggered_equal_rows(dev, M, K, N, keep, algo):
+    p, ref = _large_case(M, K, N, keep, True)
+    enc = bsp.encode(p.W)
+    d = bsp.describe(bsp.INT4, M, K, N, enc.nnz, algo=bsp.ALGO_MFMA)
+    assert "stagger=1" in d, d
+    assert_w4a4(run_w4a4(p.W, p.X, algo, dev, enc=enc), p.W, p.X, ref=ref)
 
 
 SPLITK_STREAMED = [  # (M, K, N, keep): the streamed split-K kernel (one pass per block and K range)

@@ -239,7 +239,10 @@ def test_description_names_the_launched_kernel():
     # any K up to 16384 takes the MFMA kernels (odd K too); beyond, the split-K
     # kernel walking all of K per workgroup
     assert "-> mfma kernel=k_bt64s_w4a4 " in bsp.describe(bsp.INT4, 64, 100, 4)
-    assert "-> mfma kernel=k_bt64_w4a4 " in bsp.describe(bsp.INT4, 64, 64 * 255 + 7, 4)
+    assert "-> mfma kernel=k_bt64_w4a4 " in bsp.describe(bsp.INT4, 64, 64 * 255 + 7, 4, 64 * 16327 // 2)
+    # blocks of 128 or more tiles too dense to stage (nnz unknown: planned
+    # dense) take the split-K kernel
+    assert "-> splitk kernel=k_bsk_w4a4 " in bsp.describe(bsp.INT4, 64, 64 * 255 + 7, 4)
     d = bsp.describe(bsp.INT4, 64, 16385, 4)
     assert "-> splitk kernel=k_bsk_w4a4 " in d and "splits=1 " in d
     # fp16 beyond K = 4096: the split-K kernel (2 K ranges with a workspace)
@@ -358,3 +361,61 @@ def test_streaming_plan_density_rule():
     assert "kernel=k_bt64s_w4a4" in d99 and "stagger=0" in d99, d99
     d100 = bsp.describe(bsp.INT4, M, K, N, M * K)
     assert "kernel=k_bt64_w4a4 " in d100 and "one_pass=1" in d100, d100
+
+
+def _kv(d):
+    return dict(kv.split("=", 1) for kv in d.split("->", 1)[1].split() if "=" in kv)
+
+
+def test_ring_plans_stage_past_one_workgroup_per_cu():
+    # int4 ring kernel past 256 workgroups: staging sized for one resident
+    # workgroup per CU (the grid runs in rounds) rather than global windows
+    for M, K, N, dens, grid, bufs in [(8192, 16384, 8, 0.5, 512, 1), (16384, 16384, 8, 0.5, 1024, 1),
+                                      (5000, 12000, 3, 0.5, 313, 1), (65536, 4096, 8, 0.5, 1024, 4),
+                                      (32768, 8192, 8, 0.5, 1024, 2)]:
+        d = bsp.describe(bsp.INT4, M, K, N, int(M * K * dens))
+        kv = _kv(d)
+        assert "kernel=k_bt64_w4a4 " in d, d
+        assert int(kv["grid"]) == grid and int(kv["stage_bufs"]) == bufs, d
+        assert int(kv["stage_kb"]) > 0 and 80 * 1024 < int(kv["lds"]) <= 160 * 1024, d
+    # two blocks per workgroup that do not fit twice: one block per workgroup
+    d = bsp.describe(bsp.INT4, 8192, 8192, 8, int(8192 * 8192 * 0.9))
+    kv = _kv(d)
+    assert kv["grid"] == "512" and int(kv["stage_kb"]) > 0 and kv["stage_bufs"] == "1", d
+    # one dense 256-tile block exceeds the LDS: automatic plans take the
+    # split-K kernel, a forced MFMA call reads global windows
+    for ws in (False, True):
+        d = bsp.describe(bsp.INT4, 4096, 16384, 8, int(4096 * 16384 * 0.85), workspace=ws)
+        assert "-> splitk kernel=k_bsk_w4a4 " in d, d
+    d = bsp.describe(bsp.INT4, 4096, 16384, 8, int(4096 * 16384 * 0.85), algo=bsp.ALGO_MFMA)
+    assert "kernel=k_bt64_w4a4 " in d and "stage_kb=0 " in d, d
+    # below that density the block still stages
+    d = bsp.describe(bsp.INT4, 4096, 16384, 8, int(4096 * 16384 * 0.75))
+    assert "kernel=k_bt64_w4a4 " in d and int(_kv(d)["stage_kb"]) > 100, d
+
+
+def test_staggered_staging_rules():
+    # ring kernel: staggered when the average row is within 12 B of a
+    # multiple of 64 B (rows of one length, as row-wise pruning leaves them,
+    # would otherwise line a tile of the 16 rows up on the same LDS banks),
+    # its buffers 64/61 larger
+    for M, K, N, dens, stg in [(4096, 11008, 16, 0.5, 1), (5120, 5120, 8, 0.5, 1), (4096, 14336, 8, 0.5, 1),
+                               (4096, 16384, 8, 0.5, 1), (4096, 11008, 16, 0.3, 0), (8192, 8192, 32, 0.7, 0)]:
+        d = bsp.describe(bsp.INT4, M, K, N, int(M * K * dens))
+        kv = _kv(d)
+        assert "kernel=k_bt64_w4a4 " in d and kv["stagger"] == str(stg), d
+    plain = _kv(bsp.describe(bsp.INT4, 4096, 16384, 8, 4096 * 16384 // 2, algo=bsp.ALGO_MFMA))
+    assert plain["stagger"] == "1" and int(plain["stage_kb"]) * 1024 >= (4096 * 16384 // 4 // 256) * 64 // 61
+    # ... but not when the staggered buffers would hold fewer blocks than the
+    # plain ones (two 128-tile blocks per workgroup, rows of 3072 B), or
+    # lose the single pass (dense 64-tile blocks, three per workgroup)
+    kv = _kv(bsp.describe(bsp.INT4, 8192, 8192, 8, int(8192 * 8192 * 0.75)))
+    assert kv["stagger"] == "0" and kv["stage_bufs"] == "2", kv
+    kv = _kv(bsp.describe(bsp.INT4, 8192, 8192, 8, int(8192 * 8192 * 0.72)))
+    assert kv["stagger"] == "1" and kv["stage_bufs"] == "2", kv
+    kv = _kv(bsp.describe(bsp.INT4, 12288, 4096, 8, 12288 * 4096))
+    assert kv["stagger"] == "0" and kv["one_pass"] == "1", kv
+    # streaming kernel: rows within 28 B of a multiple of 128 B
+    for dens, stg in [(0.5, 1), (0.5625, 1), (0.25, 1), (0.35, 0), (0.4, 0)]:
+        d = bsp.describe(bsp.INT4, 12288, 4096, 8, int(12288 * 4096 * dens))
+        assert "kernel=k_bt64s_w4a4 " in d and _kv(d)["stagger"] == str(stg), (dens, d)

@@ -25,6 +25,12 @@ mask -> values -> X:
 * fp16 case: W = N(0, 0.02) cast to fp16, then the round(0.6*M*K) entries of
   smallest |W| (stable argsort on the flat index) are set to +0; X = N(0, 1)
   cast to fp16.
+* row-wise pruning (``rows=True`` in the random problems): every row keeps
+  the same count, as a pruner that ranks the weights of each output row
+  separately leaves them (Wanda, which both pages use for their end-to-end
+  runs, does so). int4: ``rng.random((M, K))`` keys, the round(keep*K)
+  smallest of each row (stable argsort) kept, then the values; fp16: the
+  round(sparsity*K) entries of smallest |W| of each row set to +0.
 
 X is returned as an ``[N][K]`` array (the K x N activation matrix stored
 column by column), drawn at the largest N of the config; a smaller N uses the
@@ -37,7 +43,7 @@ from typing import Dict, List, Tuple
 
 import numpy as np
 
-__all__ = ["Problem", "CONFIGS", "make", "int4_nonzero_values", "int4_mask_matrix",
+__all__ = ["Problem", "CONFIGS", "make", "int4_nonzero_values", "int4_mask_matrix", "int4_mask_rows_exact",
            "random_int4_problem", "config_names", "int2_nonzero_values", "int2_like", "random_int2_problem"]
 
 
@@ -87,8 +93,18 @@ def int4_mask_matrix(rng: np.random.Generator, M: int, K: int, keep) -> np.ndarr
     return rng.integers(0, 65536, size=(M, K), dtype=np.uint16) < thresh
 
 
-def _int4_weights(rng, M, K, keep) -> np.ndarray:
-    mask = int4_mask_matrix(rng, M, K, keep)
+def int4_mask_rows_exact(rng: np.random.Generator, M: int, K: int, keep: float) -> np.ndarray:
+    """Keep-mask with exactly round(keep * K) entries in every row: those of
+    the smallest uniform keys of the row."""
+    k = int(round(keep * K))
+    order = np.argsort(rng.random((M, K)), axis=1, kind="stable")
+    mask = np.zeros((M, K), dtype=bool)
+    np.put_along_axis(mask, order[:, :k], True, axis=1)
+    return mask
+
+
+def _int4_weights(rng, M, K, keep, rows: bool = False) -> np.ndarray:
+    mask = int4_mask_rows_exact(rng, M, K, keep) if rows else int4_mask_matrix(rng, M, K, keep)
     vals = int4_nonzero_values(rng, (M, K))
     return (vals * mask).astype(np.int8)
 
@@ -116,20 +132,23 @@ def random_int2_problem(seed: int, M: int, K: int, N: int, keep: float = 0.5, na
 
 
 def random_int4_problem(seed: int, M: int, K: int, N: int, keep: float = 0.5,
-                        name: str = "random") -> Problem:
-    """Small seeded int4 case of any shape (tests, edge cases)."""
+                        name: str = "random", rows: bool = False) -> Problem:
+    """Seeded int4 case of any shape (tests, edge cases); ``rows``: the same
+    count kept in every row."""
     rng = np.random.default_rng(seed)
-    W = _int4_weights(rng, M, K, keep)
+    W = _int4_weights(rng, M, K, keep, rows)
     X = int4_activations(rng, (N, K))
-    return Problem(name, "int4", W, X, dict(seed=seed, keep=keep, N=N))
+    return Problem(name, "int4", W, X, dict(seed=seed, keep=keep, N=N, rows=rows))
 
 
 def random_fp16_problem(seed: int, M: int, K: int, N: int, sparsity: float = 0.6,
-                        name: str = "random_f16") -> Problem:
+                        name: str = "random_f16", rows: bool = False) -> Problem:
+    """Seeded fp16 case of any shape; ``rows``: each row pruned by magnitude
+    to the same count."""
     rng = np.random.default_rng(seed)
-    W = _fp16_pruned(rng, M, K, sparsity)
+    W = _fp16_pruned_rows(rng, M, K, sparsity) if rows else _fp16_pruned(rng, M, K, sparsity)
     X = rng.normal(0.0, 1.0, size=(N, K)).astype(np.float16)
-    return Problem(name, "fp16", W, X, dict(seed=seed, sparsity=sparsity, N=N))
+    return Problem(name, "fp16", W, X, dict(seed=seed, sparsity=sparsity, N=N, rows=rows))
 
 
 def _fp16_pruned(rng, M, K, sparsity) -> np.ndarray:
@@ -139,6 +158,13 @@ def _fp16_pruned(rng, M, K, sparsity) -> np.ndarray:
     order = np.argsort(np.abs(flat.astype(np.float32)), kind="stable")
     flat[order[:n_prune]] = np.float16(0.0)
     return flat.reshape(M, K)
+
+
+def _fp16_pruned_rows(rng, M, K, sparsity) -> np.ndarray:
+    W = rng.normal(0.0, 0.02, size=(M, K)).astype(np.float16)
+    order = np.argsort(np.abs(W.astype(np.float32)), axis=1, kind="stable")
+    np.put_along_axis(W, order[:, :int(round(sparsity * K))], np.float16(0.0), axis=1)
+    return W
 
 
 # ---------------------------------------------------------------------------

@@ -193,7 +193,9 @@ __device__ __forceinline__ void bf_contract(uint64_t word, uint32_t p, const Win
 }
 
 // LDS layout (bytes): [selector table 128][row totals 2 x 16 x 16 ints]
-//   [partials 2 x nwaves x NB x 256 floats][nbuf staging buffers of stage_bytes]
+//   [partials P x nwaves x NB x 256 floats][nbuf staging buffers of stage_bytes]
+// with P = 2 partial sets (block i adds into set i % 2 while set (i - 1) % 2
+// is summed into Y) when a workgroup owns more than one block, else 1.
 // Workgroup g owns blocks [g*bq + min(g, br), ...): bq or bq + 1 of them.
 template <int NB>
 __global__ __launch_bounds__(1024) void k_bt64_f16(
@@ -213,8 +215,9 @@ __global__ __launch_bounds__(1024) void k_bt64_f16(
 
     uint32_t *lut_lds = reinterpret_cast<uint32_t *>(bf_smem);
     int32_t *wt = reinterpret_cast<int32_t *>(bf_smem + 128);                           // [2][16][16]
-    float *part = reinterpret_cast<float *>(wt + 2 * BF_ROWS * BF_MAX_WAVES);            // [2][nwaves][NB*256]
-    uint8_t *stage = reinterpret_cast<uint8_t *>(part + 2 * nwaves * NB * 256);
+    float *part = reinterpret_cast<float *>(wt + 2 * BF_ROWS * BF_MAX_WAVES);            // [P][nwaves][NB*256]
+    const int psets = bq + (br > 0 ? 1 : 0) > 1 ? 2 : 1;                                  // the same in every workgroup
+    uint8_t *stage = reinterpret_cast<uint8_t *>(part + psets * nwaves * NB * 256);
     const uint32_t lut = bt_lds_addr(lut_lds);
     const __amdgpu_buffer_rsrc_t prs = bt_rsrc(payload, payload_bytes);
 
@@ -714,7 +717,10 @@ static bool bf_plan(int64_t M, int64_t K, int64_t N, int64_t payload_bytes, BfPl
     const int64_t worst = (int64_t)BF_ROWS * T * 128 + 64;
     int64_t stage = std::min<int64_t>(worst, avg + avg / 5 + 2048) + 32;
     stage = (stage + 1023) / 1024 * 1024;
-    const int64_t fixed = 128 + 2 * BF_ROWS * BF_MAX_WAVES * 4 + 2 * (int64_t)p->nwaves * p->nb * 256 * 4;
+    // one set of partials when a workgroup owns a single block (the second
+    // set only overlaps a block's partials with the previous block's sum)
+    const int64_t psets = per_wg > 1 ? 2 : 1;
+    const int64_t fixed = 128 + 2 * BF_ROWS * BF_MAX_WAVES * 4 + psets * (int64_t)p->nwaves * p->nb * 256 * 4;
     int64_t nbuf = std::min<int64_t>((budget - fixed) / stage, per_wg);
     if (nbuf < std::min<int64_t>(2, per_wg)) {   // see the int4 plan
         stage = 0;

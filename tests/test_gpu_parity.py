@@ -526,6 +526,25 @@ def test_w4a4_staggered_equal_rows(dev, M, K, N, keep, algo):
     assert_w4a4(run_w4a4(p.W, p.X, algo, dev, enc=enc), p.W, p.X, ref=ref)
 
 
+F16_STAGED = [  # (M, K, N, density): the 16-row fp16 kernel staging dense blocks
+    (4096, 4096, 32, 0.75),   # one set of partials, two column blocks
+    (4096, 4096, 16, 1.0),    # every block dense
+    (4096, 4096, 12, 0.95),
+    (1000, 4096, 32, 0.75),   # ragged last block
+    (5000, 4096, 20, 0.2),    # two blocks per workgroup: two sets, two buffers
+]
+
+
+@pytest.mark.parametrize("algo", [bsp.ALGO_AUTO, bsp.ALGO_MFMA], ids=["auto", "mfma"])
+@pytest.mark.parametrize("M,K,N,dens", F16_STAGED)
+def test_f16_block_staging(dev, M, K, N, dens, algo):
+    p = workloads.random_fp16_problem(M + K + N, M, K, N, sparsity=1.0 - dens)
+    enc = bsp.encode(p.W)
+    d = bsp.describe(bsp.FP16, M, K, N, enc.nnz, algo=bsp.ALGO_MFMA)
+    assert "kernel=k_bt64_f16 " in d and "stage_kb=0 " not in d, d
+    _assert_f16(run_f16(p.W, p.X, algo, dev, enc=enc), oracle.spmm_f16(oracle.encode(p.W), p.X))
+
+
 SPLITK_STREAMED = [  # (M, K, N, keep): the streamed split-K kernel (one pass per block and K range)
     (100, 64 * 65, 3, 0.5),      # two tiles per lane, ragged last block
     (513, 6000, 17, 0.5),        # two column blocks, ragged last tile

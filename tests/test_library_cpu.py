@@ -419,3 +419,17 @@ def test_staggered_staging_rules():
     for dens, stg in [(0.5, 1), (0.5625, 1), (0.25, 1), (0.35, 0), (0.4, 0)]:
         d = bsp.describe(bsp.INT4, 12288, 4096, 8, int(12288 * 4096 * dens))
         assert "kernel=k_bt64s_w4a4 " in d and _kv(d)["stagger"] == str(stg), (dens, d)
+
+
+def test_f16_block_plan_partial_sets():
+    # the 16-row fp16 kernel keeps one set of per-wavefront partials when a
+    # workgroup owns one block (two otherwise), which leaves room to stage
+    # denser blocks
+    for N, dens in [(32, 0.6), (32, 0.75), (16, 0.95), (12, 1.0)]:
+        kv = _kv(bsp.describe(bsp.FP16, 4096, 4096, N, int(4096 * 4096 * dens)))
+        assert int(kv["stage_kb"]) > 0 and int(kv["lds"]) <= 160 * 1024, (N, dens, kv)
+    # two blocks per workgroup: two sets, two buffers
+    kv = _kv(bsp.describe(bsp.FP16, 5000, 4096, 20, int(5000 * 4096 * 0.2)))
+    assert kv["stage_bufs"] == "2" and int(kv["lds"]) == 128 + 2048 + 2 * 16 * 2 * 1024 + 2 * 1024 * int(kv["stage_kb"])
+    kv = _kv(bsp.describe(bsp.FP16, 4096, 4096, 32, int(4096 * 4096 * 0.4)))
+    assert int(kv["lds"]) == 128 + 2048 + 16 * 2 * 1024 + 1024 * int(kv["stage_kb"]), kv

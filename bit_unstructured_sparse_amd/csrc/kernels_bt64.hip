@@ -1127,13 +1127,15 @@ static bool bt64_plan(int64_t M, int64_t K, int64_t N, int64_t payload_bytes, Bt
     // the same number of passes (rows of one length, int4 at N = 8: 4096 x
     // 14336 14.75 -> 12.16 us, 4096 x 11008 at N = 16 12.34 -> 11.38,
     // 5120 x 5120 10.11 -> 9.39; iid masks 4096 x 16384 13.97 -> 13.04,
-    // 4096 x 11008 11.39 / 11.47)
+    // 4096 x 11008 11.39 / 11.47). An average row of exactly such a length
+    // (every row dense, or cut to one count) takes it even at the cost of
+    // the single pass (12288 x 4096 dense: 18.75 -> 13.10 us).
     const int64_t rb64 = (payload_bytes / std::max<int64_t>(M, 1)) % 64;
     Fit f = fit(false);
     p->stagger = 0;
     if (std::min<int64_t>(rb64, 64 - rb64) < 12 && f.nbuf > 0) {
         const Fit fs = fit(true);
-        if (fs.nbuf == f.nbuf && fs.grid == f.grid && fs.one_pass == f.one_pass) {
+        if (fs.nbuf == f.nbuf && fs.grid == f.grid && (fs.one_pass == f.one_pass || rb64 == 0)) {
             f = fs;
             p->stagger = 1;
         }

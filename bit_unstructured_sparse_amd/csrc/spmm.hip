@@ -146,14 +146,18 @@ int choose_plan(int dtype, const Shape &s, int64_t pbytes, int algo, bool have_w
         return BSP_OK;
     }
     if (plan_mfma(dtype, s, pbytes, p)) {
-        // int4 blocks of 128 or more tiles too dense for the LDS (density
-        // above about 0.8): the ring kernel would read every window from
-        // global memory, the split-K kernel stages 64-tile chunks (4096 x
-        // 16384 at N = 8: 39.6 -> 20.6 us at density 0.85, 43.6 -> 21.2 at
-        // 0.95)
+        // The int4 ring kernel at 8 tiles per lane (K > 8192) gives way to
+        // split-K (2 K ranges with a workspace) where it is at its worst:
+        // - a 256-tile block too dense for the LDS (density above about
+        //   0.8) would read every window from global memory, where the
+        //   split-K kernel stages 64-tile chunks (4096 x 16384 at N = 8:
+        //   39.6 -> 20.6 us at density 0.85, 43.6 -> 21.2 at 0.95);
+        // - two column blocks (N > 16) exceed its registers (it spills 680
+        //   to 824 B per lane): 4096 x 11008 at N = 32 35.7 -> 16.4 us
+        //   (18.1 without a workspace), 4096 x 16384 at N = 24 45.2 -> 21.8.
         Plan sk;
-        if (p->kind == PK_BT64 && !p->bt.streaming && p->bt.tpl == 8 && p->bt.stage_bytes == 0 &&
-            plan_splitk(dtype, s, pbytes, have_ws ? preferred_splits(dtype, s) : 1, &sk))
+        if (p->kind == PK_BT64 && !p->bt.streaming && p->bt.tpl == 8 && (p->bt.stage_bytes == 0 || p->bt.nb == 2) &&
+            plan_splitk(dtype, s, pbytes, have_ws ? 2 : 1, &sk))
             *p = sk;
         return BSP_OK;
     }

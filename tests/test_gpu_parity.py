@@ -511,6 +511,7 @@ EQUAL_ROWS = [  # (M, K, N, keep): every row keeps the same count; staggered sta
     (8192, 8192, 8, 0.72),     # ring, two buffers per workgroup, refilled
     (40000, 4096, 8, 0.25),    # ring, 2 tiles per lane, four blocks per workgroup, one pass
     (20000, 4096, 8, 0.25),    # ring, 2 tiles per lane, three buffers for four blocks
+    (12288, 4096, 8, 1.0),     # ring, every row dense: staggered, buffers refilled instead of one pass
     (12288, 4096, 8, 0.5625),  # streaming kernel, rows of 1152 B
     (3000, 4096, 17, 0.5),     # streaming kernel, two column blocks
 ]
@@ -543,6 +544,26 @@ def test_f16_block_staging(dev, M, K, N, dens, algo):
     d = bsp.describe(bsp.FP16, M, K, N, enc.nnz, algo=bsp.ALGO_MFMA)
     assert "kernel=k_bt64_f16 " in d and "stage_kb=0 " not in d, d
     _assert_f16(run_f16(p.W, p.X, algo, dev, enc=enc), oracle.spmm_f16(oracle.encode(p.W), p.X))
+
+
+@pytest.mark.parametrize("with_ws", [False, True], ids=["plain", "workspace"])
+@pytest.mark.parametrize("M,K,N", [(2000, 11008, 32), (1000, 16384, 17), (300, 9000, 24)])
+def test_w4a4_wide_n_past_k8192_auto(dev, M, K, N, with_ws):
+    # N > 16 at 8 tiles per lane: the automatic plan is split-K
+    p, ref = _large_case(M, K, N, 0.3, False)
+    enc = bsp.encode(p.W)
+    d = bsp.describe(bsp.INT4, M, K, N, enc.nnz, workspace=with_ws)
+    assert "-> splitk " in d, d
+    dm = enc.to_device(dev)
+    Xd = torch.from_numpy(bsp.pack_int4(p.X)).to(dev)
+    ws = _ws(bsp.INT4, M, K, N, enc.nnz, dev) if with_ws else None
+    big, Y = _y_with_canary(N, M, torch.int32, dev)
+    bsp.spmm_w4a4(dm, Xd, N, Y=Y, workspace=ws)
+    torch.cuda.synchronize()
+    assert _canary_ok(big, N, M, torch.int32), "write past the end of Y"
+    assert np.array_equal(Y.cpu().numpy(), ref), d
+    if with_ws:
+        assert not ws[:65536].any(), "arrival counters left nonzero"
 
 
 SPLITK_STREAMED = [  # (M, K, N, keep): the streamed split-K kernel (one pass per block and K range)

@@ -353,14 +353,15 @@ def test_streaming_plan_density_rule():
     # the streaming kernel keeps its staggered staging while the average block
     # fits it, drops the stagger when only the plain layout holds the average
     # block, and leaves fully dense blocks (which fit neither area) to the ring
-    # kernel, whose staging holds a whole dense block
+    # kernel, whose staging holds a whole dense block (staggered: every row
+    # is 2048 B long)
     M, K, N = 12288, 4096, 8
     d50 = bsp.describe(bsp.INT4, M, K, N, M * K // 2)
     assert "kernel=k_bt64s_w4a4" in d50 and "stagger=1" in d50, d50
     d99 = bsp.describe(bsp.INT4, M, K, N, int(M * K * 0.99))
     assert "kernel=k_bt64s_w4a4" in d99 and "stagger=0" in d99, d99
     d100 = bsp.describe(bsp.INT4, M, K, N, M * K)
-    assert "kernel=k_bt64_w4a4 " in d100 and "one_pass=1" in d100, d100
+    assert "kernel=k_bt64_w4a4 " in d100 and "stagger=1" in d100 and "stage_bufs=3" in d100, d100
 
 
 def _kv(d):
@@ -408,13 +409,17 @@ def test_staggered_staging_rules():
     assert plain["stagger"] == "1" and int(plain["stage_kb"]) * 1024 >= (4096 * 16384 // 4 // 256) * 64 // 61
     # ... but not when the staggered buffers would hold fewer blocks than the
     # plain ones (two 128-tile blocks per workgroup, rows of 3072 B), or
-    # lose the single pass (dense 64-tile blocks, three per workgroup)
+    # lose the single pass, unless the average row is an exact multiple
+    # (rows of 2048 B, dense 64-tile blocks, three per workgroup)
     kv = _kv(bsp.describe(bsp.INT4, 8192, 8192, 8, int(8192 * 8192 * 0.75)))
     assert kv["stagger"] == "0" and kv["stage_bufs"] == "2", kv
     kv = _kv(bsp.describe(bsp.INT4, 8192, 8192, 8, int(8192 * 8192 * 0.72)))
     assert kv["stagger"] == "1" and kv["stage_bufs"] == "2", kv
-    kv = _kv(bsp.describe(bsp.INT4, 12288, 4096, 8, 12288 * 4096))
+    kv = _kv(bsp.describe(bsp.INT4, 40000, 4096, 8, int(40000 * 4096 * 0.495)))   # rows of ~1014 B
     assert kv["stagger"] == "0" and kv["one_pass"] == "1", kv
+    for M, dens in [(40000, 0.5), (12288, 1.0)]:                                    # 1024 B, 2048 B
+        kv = _kv(bsp.describe(bsp.INT4, M, 4096, 8, int(M * 4096 * dens)))
+        assert kv["stagger"] == "1" and kv["one_pass"] == "0", kv
     # streaming kernel: rows within 28 B of a multiple of 128 B
     for dens, stg in [(0.5, 1), (0.5625, 1), (0.25, 1), (0.35, 0), (0.4, 0)]:
         d = bsp.describe(bsp.INT4, 12288, 4096, 8, int(12288 * 4096 * dens))
@@ -433,3 +438,18 @@ def test_f16_block_plan_partial_sets():
     assert kv["stage_bufs"] == "2" and int(kv["lds"]) == 128 + 2048 + 2 * 16 * 2 * 1024 + 2 * 1024 * int(kv["stage_kb"])
     kv = _kv(bsp.describe(bsp.FP16, 4096, 4096, 32, int(4096 * 4096 * 0.4)))
     assert int(kv["lds"]) == 128 + 2048 + 16 * 2 * 1024 + 1024 * int(kv["stage_kb"]), kv
+
+
+def test_wide_n_past_k8192_takes_split_k():
+    # two column blocks at 8 tiles per lane exceed the ring kernel's
+    # registers: N > 16 past K = 8192 goes to split-K (two K ranges with a
+    # workspace); 4 tiles per lane keeps the ring kernel
+    for N in (17, 24, 32):
+        assert "-> splitk kernel=k_bsk_w4a4 " in bsp.describe(bsp.INT4, 4096, 11008, N, 4096 * 11008 * 3 // 10)
+        d = bsp.describe(bsp.INT4, 4096, 11008, N, 4096 * 11008 * 3 // 10, workspace=True)
+        assert "-> splitk kernel=k_bsks_w4a4 " in d and "splits=2 " in d, d
+    assert "-> mfma kernel=k_bt64_w4a4 " in bsp.describe(bsp.INT4, 4096, 11008, 16, 4096 * 11008 * 3 // 10)
+    assert "-> mfma kernel=k_bt64_w4a4 " in bsp.describe(bsp.INT4, 8192, 8192, 32, 8192 * 8192 * 7 // 10)
+    # forced, the ring kernel still runs the shape
+    d = bsp.describe(bsp.INT4, 4096, 11008, 32, 4096 * 11008 * 3 // 10, algo=bsp.ALGO_MFMA)
+    assert "kernel=k_bt64_w4a4 " in d and "tiles_per_lane=8" in d, d

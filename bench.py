@@ -738,7 +738,7 @@ def _prepare_w2(args, bsp, problem, dev):
         dm, x, y = copies[i % R]
         bsp.spmm_w2a4(dm, x, N, Y=y, algo=algo)
 
-    kernel = "k_rowwave_w4a4" if algo == bsp.ALGO_ROWWAVE or K > 4096 else "k_bt64s_w2a4"
+    kernel = kernel_symbol(bsp, algo, bsp.INT2, M, K, N, enc.nnz)
     nbytes = dm0.stream_bytes(with_offsets=False) + 4 * offsets_read(kernel, M, dm0.T) + N * ((K + 1) // 2) + 4 * M * N
     return dict(problem=problem, fp16=False, enc=enc, dm0=dm0, copies=copies, R=R, step=step, chosen=algo,
                 name="w2a4", kernel=kernel, dt=bsp.INT2, plan="w2a4", nbytes=nbytes)

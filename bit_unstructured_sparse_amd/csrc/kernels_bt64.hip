@@ -416,9 +416,11 @@ __device__ __forceinline__ BtRange bt_range(uint32_t nibA, uint32_t nibB) {
 // (a tile's windows reach < 48 B past its first nonzero, so they stay inside
 // the instruction of its start), and every 61 granules the stream moves 48 B
 // further round the banks, so equal rows no longer line up.
+// WB: width of a stored weight value (4: int4; 2: int2, the W2A4 variant,
+// unstaggered).
 #define BT_R61_RUN 61u
 #define BT_R61_MAG 2200291u   // ceil(2^32 / (61 * 32)): umulhi(p, MAG) = p / 1952 for p < 2^20
-template <int NB, int TPL, bool XU, bool STG>
+template <int NB, int TPL, bool XU, bool STG, int WB = 4>
 // (The arguments the first loads need come first: they are the ones a
 // kernel-argument preload would place in registers.)
 __global__ __launch_bounds__(BT_WG_THREADS(TPL)) void k_bt64_w4a4(
@@ -426,9 +428,12 @@ __global__ __launch_bounds__(BT_WG_THREADS(TPL)) void k_bt64_w4a4(
         const uint8_t *__restrict__ X, int N, const uint8_t *__restrict__ payload, uint32_t payload_bytes,
         int32_t *__restrict__ Y, uint32_t stage_bytes, uint32_t nbuf, int one_pass, uint16_t *Yh, const float *sw,
         const float *sx) {
+    static_assert(WB == 4 || (WB == 2 && !STG), "staggered staging is for int4 streams");
     const BtEpi epi{Yh, sw, sx};
     constexpr int NBLK = BT_NBLK(TPL);
     constexpr int WC = BT_WG_THREADS(TPL) / 64;          // row-total columns: wavefronts, at most
+    constexpr uint32_t VPB = 8 / WB;                     // values per payload byte
+    constexpr int PS = WB == 4 ? 8 : 10;                 // log2 of the A x B operand scale
     extern __shared__ __attribute__((aligned(16))) uint8_t bt_smem[];
     const int nwaves = blockDim.x >> 6;
     // the wavefront index is uniform: keep it (and the loops over it) scalar
@@ -558,12 +563,12 @@ __global__ __launch_bounds__(BT_WG_THREADS(TPL)) void k_bt64_w4a4(
     uint32_t vm_mark[NBLK];
     constexpr uint32_t RUN = STG ? BT_R61_RUN : 64u;   // stream granules per 1 KB DMA instruction
     auto fits = [&](int i) -> bool {
-        const BtRange g = bt_range(nib[i], nib[i + 1]);
+        const BtRange g = bt_range<WB>(nib[i], nib[i + 1]);
         return (g.n + RUN - 1u) / RUN * 1024u <= stage_bytes;
     };
     auto issue_block = [&](int i) -> void {
         if (fits(i)) {
-            const BtRange g = bt_range(nib[i], nib[i + 1]);
+            const BtRange g = bt_range<WB>(nib[i], nib[i + 1]);
             uint8_t *buf = stage + (uint32_t)(i % (int)nbuf) * stage_bytes;
             // lane 0 of every instruction stores a granule of the block, so
             // each one issues (and counts)
@@ -622,7 +627,7 @@ __global__ __launch_bounds__(BT_WG_THREADS(TPL)) void k_bt64_w4a4(
     // decode + contract block i into acc (after its barrier)
     auto decode_block = [&](int i, bt_v4i (&acc)[NB]) -> void {
         const bool in_lds = fits(i);
-        const BtRange g = bt_range(nib[i], nib[i + 1]);
+        const BtRange g = bt_range<WB>(nib[i], nib[i + 1]);
         const int rows = min(BT_ROWS, M - (b_begin + i) * BT_ROWS);
         const int32_t *wti = wt + i * BT_ROWS * WC;
         // lane start: rows before r, wavefronts before this one, lane groups before q
@@ -647,26 +652,28 @@ __global__ __launch_bounds__(BT_WG_THREADS(TPL)) void k_bt64_w4a4(
             sc += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)sc, 0x112, 0xF, 0xF, true);   // row_shr:2
             sc += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)sc, 0x114, 0xF, 0xF, true);   // row_shr:4
             sc += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)sc, 0x118, 0xF, 0xF, true);   // row_shr:8
-            // nibble index of the lane's first nonzero, counted from the block's first granule
-            pstart = r < rows ? (nib[i] & 31u) + (sc - row_total) + before_w + (incl[i] - seg[i]) : 0u;
+            // value index of the lane's first nonzero, counted from the block's first granule
+            pstart = r < rows ? (nib[i] & (16u * VPB - 1u)) + (sc - row_total) + before_w + (incl[i] - seg[i]) : 0u;
         }
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) acc[nb] = bt_v4i{0, 0, 0, 0};
         uint32_t p = pstart;
         if (in_lds) {
             // a corrupt stream stays inside the staged granules
-            p = min(p, 8u * (4u * g.n - 2u));
-            // twice the buffer's address (a multiple of 32) keeps p & 7
-            const uint32_t base2 = 2u * bt_lds_addr(stage + (uint32_t)(i % (int)nbuf) * stage_bytes);
+            p = min(p, 16u * VPB * g.n - 8u * VPB);
+            // VPB times the buffer's address (a multiple of 16) keeps p & 7
+            const uint32_t base2 = VPB * bt_lds_addr(stage + (uint32_t)(i % (int)nbuf) * stage_bytes);
             if constexpr (STG) {
                 // stream nibble pt sits 3 granules (96 nibbles) further per run of 61 before it
                 const auto tmap = [=](uint32_t pt) { return pt + base2 + __umulhi(pt, BT_R61_MAG) * 96u; };
                 bt_contract<NB, TPL, BtWinLds, decltype(tmap)>(words[i], p, BtWinLds{}, lut_base, xb, acc, tmap);
             } else {
-                bt_contract<NB, TPL>(words[i], p + base2, BtWinLds{}, lut_base, xb, acc);
+                bt_contract<NB, TPL, BtWinLdsT<WB>, BtTileSame, WB>(words[i], p + base2, BtWinLdsT<WB>{}, lut_base,
+                                                                   xb, acc);
             }
         } else {
-            bt_contract<NB, TPL>(words[i], p, BtWinGlobal{prs, 4u * g.g0}, lut_base, xb, acc);
+            bt_contract<NB, TPL, BtWinGlobalT<WB>, BtTileSame, WB>(words[i], p, BtWinGlobalT<WB>{prs, 4u * g.g0},
+                                                                  lut_base, xb, acc);
         }
     };
 
@@ -687,7 +694,7 @@ __global__ __launch_bounds__(BT_WG_THREADS(TPL)) void k_bt64_w4a4(
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb)
                 *(__attribute__((address_space(3))) bt_v4i *)(uintptr_t)bt_lds_addr(pw + nb * 256 + lane * 4) =
-                        bt_v4i{acc[nb][0] >> 8, acc[nb][1] >> 8, acc[nb][2] >> 8, acc[nb][3] >> 8};
+                        bt_v4i{acc[nb][0] >> PS, acc[nb][1] >> PS, acc[nb][2] >> PS, acc[nb][3] >> PS};
         }
         __syncthreads();
         // Y: item (block i, column block nb, lane l) sums the wavefronts'
@@ -719,12 +726,12 @@ __global__ __launch_bounds__(BT_WG_THREADS(TPL)) void k_bt64_w4a4(
             for (int o = threadIdx.x; o < NB * 256; o += blockDim.x) sums[((i + 1) % 3) * NB * 256 + o] = 0;
         bt_v4i acc[NB];
         decode_block(i, acc);
-        // the wavefronts' partials (each exact after >> 8) meet in LDS
+        // the wavefronts' partials (each exact after >> PS) meet in LDS
         int32_t *sp = sums + (i % 3) * NB * 256;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-            for (int k = 0; k < 4; ++k) atomicAdd(&sp[(nb * 4 + k) * 64 + lane], acc[nb][k] >> 8);
+            for (int k = 0; k < 4; ++k) atomicAdd(&sp[(nb * 4 + k) * 64 + lane], acc[nb][k] >> PS);
     }
     __syncthreads();
     write_y(nblk - 1);
@@ -1133,7 +1140,7 @@ static bool bt64_plan(int64_t M, int64_t K, int64_t N, int64_t payload_bytes, Bt
     const int64_t rb64 = (payload_bytes / std::max<int64_t>(M, 1)) % 64;
     Fit f = fit(false);
     p->stagger = 0;
-    if (std::min<int64_t>(rb64, 64 - rb64) < 12 && f.nbuf > 0) {
+    if (wb == 4 && std::min<int64_t>(rb64, 64 - rb64) < 12 && f.nbuf > 0) {
         const Fit fs = fit(true);
         if (fs.nbuf == f.nbuf && fs.grid == f.grid && (fs.one_pass == f.one_pass || rb64 == 0)) {
             f = fs;
@@ -1189,15 +1196,39 @@ static bool bt64_plan(int64_t M, int64_t K, int64_t N, int64_t payload_bytes, Bt
     return true;
 }
 
-template <int NB, int TPL, bool XU, bool STG>
+template <int NB, int TPL, bool XU, bool STG, int WB = 4>
 static void launch_bt64_s(const BtPlan &p, const uint64_t *bitmaps, const uint32_t *offsets,
                           const uint8_t *payload, uint32_t payload_bytes, int M, int K, const uint8_t *X, int N,
                           int32_t *Y, const BtEpi &e, hipStream_t stream) {
-    (void)hipFuncSetAttribute((const void *)k_bt64_w4a4<NB, TPL, XU, STG>,
+    (void)hipFuncSetAttribute((const void *)k_bt64_w4a4<NB, TPL, XU, STG, WB>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds);
-    hipLaunchKernelGGL((k_bt64_w4a4<NB, TPL, XU, STG>), dim3(p.grid), dim3(64 * p.nwaves), p.lds, stream, offsets, M, K,
-                       p.bq, p.br, bitmaps, X, N, payload, payload_bytes, Y, p.stage_bytes, p.nbuf, p.one_pass, e.Yh,
-                       e.sw, e.sx);
+    hipLaunchKernelGGL((k_bt64_w4a4<NB, TPL, XU, STG, WB>), dim3(p.grid), dim3(64 * p.nwaves), p.lds, stream, offsets,
+                       M, K, p.bq, p.br, bitmaps, X, N, payload, payload_bytes, Y, p.stage_bytes, p.nbuf, p.one_pass,
+                       e.Yh, e.sw, e.sx);
+}
+
+// W2A4 through the ring kernel (K past the streaming kernel's 4096), int32 Y
+// (the plan is bt64_plan's with 2-bit values, never staggered)
+static void launch_bt64_w2a4(const BtPlan &p, const uint64_t *bitmaps, const uint32_t *offsets,
+                             const uint8_t *payload, uint32_t payload_bytes, int M, int K, const uint8_t *X, int N,
+                             int32_t *Y, hipStream_t stream) {
+    const BtEpi e{nullptr, nullptr, nullptr};
+#define BT2_LAUNCH(NB, TPL, XU) \
+    launch_bt64_s<NB, TPL, XU, false, 2>(p, bitmaps, offsets, payload, payload_bytes, M, K, X, N, Y, e, stream)
+#define BT2_LAUNCH_X(NB, TPL)              \
+    do {                                   \
+        if (K % 8 == 0)                    \
+            BT2_LAUNCH(NB, TPL, false);    \
+        else                               \
+            BT2_LAUNCH(NB, TPL, true);     \
+    } while (0)
+    if (p.nb == 1) {
+        if (p.tpl == 2) BT2_LAUNCH_X(1, 2); else if (p.tpl == 4) BT2_LAUNCH_X(1, 4); else BT2_LAUNCH_X(1, 8);
+    } else {
+        if (p.tpl == 2) BT2_LAUNCH_X(2, 2); else if (p.tpl == 4) BT2_LAUNCH_X(2, 4); else BT2_LAUNCH_X(2, 8);
+    }
+#undef BT2_LAUNCH_X
+#undef BT2_LAUNCH
 }
 
 template <int NB, int TPL, bool XU>

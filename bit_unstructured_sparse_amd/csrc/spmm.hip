@@ -207,27 +207,49 @@ void describe_plan(int dtype, const Plan &p, char *launch, size_t n) {
     }
 }
 
+// The W2A4 plan: the MFMA block kernels up to K = 16384 (2-bit values), else
+// the row-wave kernel; no split-K.
+int choose_plan_w2(const Shape &s, int64_t pbytes, int algo, Plan *p) {
+    *p = Plan{};
+    if (algo == BSP_ALGO_SPLITK) return BSP_E_UNSUPPORTED;
+    if (algo != BSP_ALGO_ROWWAVE && s.K > 0 && bt64_plan(s.M, s.K, s.N, pbytes, &p->bt, 2)) {
+        p->kind = PK_BT64;
+        p->algo = BSP_ALGO_MFMA;
+        return BSP_OK;
+    }
+    return algo == BSP_ALGO_MFMA ? BSP_E_UNSUPPORTED : BSP_OK;
+}
+
 int describe(int dtype, int64_t M, int64_t K, int64_t N, int64_t nnz, bool have_ws, char *buf, size_t n,
              int algo = BSP_ALGO_AUTO) {
-    if (dtype != BSP_INT4 && dtype != BSP_FP16) return BSP_E_ARG;
+    if (dtype != BSP_INT4 && dtype != BSP_FP16 && dtype != BSP_INT2) return BSP_E_ARG;
     if (M < 0 || K < 0 || N < 0 || N > BSP_MAX_N || buf == nullptr || n == 0) return BSP_E_ARG;
     if (algo < BSP_ALGO_AUTO || algo > BSP_ALGO_SPLITK) return BSP_E_ARG;
     const Shape s{M, K, N, (K + 63) / 64, M * ((K + 63) / 64)};
+    const char *dname = dtype == BSP_INT4 ? "int4" : dtype == BSP_FP16 ? "fp16" : "int2";
     // payload bytes the encoder writes for nnz nonzeros (all of W when unknown)
     const int64_t nz = nnz >= 0 ? nnz : M * K;
-    const int64_t pbytes = dtype == BSP_INT4 ? (nz + 1) / 2 : 2 * nz;
+    const int64_t pbytes = dtype == BSP_INT4 ? (nz + 1) / 2 : dtype == BSP_FP16 ? 2 * nz : (nz + 3) / 4;
     Plan p;
-    const int rc = choose_plan(dtype, s, pbytes, algo, have_ws, &p);
+    const int rc = dtype == BSP_INT2 ? choose_plan_w2(s, pbytes, algo, &p) : choose_plan(dtype, s, pbytes, algo, have_ws, &p);
     if (rc != BSP_OK) {
-        snprintf(buf, n, "dtype=%s M=%lld K=%lld N=%lld nnz=%lld -> unsupported", dtype == BSP_INT4 ? "int4" : "fp16",
-                 (long long)M, (long long)K, (long long)N, (long long)nnz);
+        snprintf(buf, n, "dtype=%s M=%lld K=%lld N=%lld nnz=%lld -> unsupported", dname, (long long)M, (long long)K,
+                 (long long)N, (long long)nnz);
         return rc;
     }
     const char *name = p.algo == BSP_ALGO_ROWWAVE ? "rowwave" : p.algo == BSP_ALGO_MFMA ? "mfma" : "splitk";
     char launch[256] = "";
-    if (M > 0 && N > 0) describe_plan(dtype, p, launch, sizeof launch);
-    snprintf(buf, n, "dtype=%s M=%lld K=%lld N=%lld nnz=%lld -> %s%s", dtype == BSP_INT4 ? "int4" : "fp16",
-             (long long)M, (long long)K, (long long)N, (long long)nnz, name, launch);
+    if (M > 0 && N > 0) {
+        describe_plan(dtype == BSP_INT2 ? BSP_INT4 : dtype, p, launch, sizeof launch);
+        if (dtype == BSP_INT2) {
+            // the same kernels with 2-bit values: the streaming one under its own name
+            char *k = strstr(launch, "k_bt64s_w4a4");
+            if (k != nullptr) memcpy(k, "k_bt64s_w2a4", 12);
+            if (p.kind == PK_ROWWAVE) snprintf(launch, sizeof launch, " kernel=k_rowwave_w4a4 values=2bit");
+        }
+    }
+    snprintf(buf, n, "dtype=%s M=%lld K=%lld N=%lld nnz=%lld -> %s%s", dname, (long long)M, (long long)K,
+             (long long)N, (long long)nnz, name, launch);
     return BSP_OK;
 }
 
@@ -610,15 +632,26 @@ extern "C" int spmm_bitmap_w2a4_algo(const uint64_t *bitmaps, const uint32_t *of
     Shape s;
     int rc = check_args(bitmaps, offsets, payload, payload_bytes, M, K, X, N, Y, algo, &s);
     if (rc != BSP_OK || M == 0 || N == 0) return rc;
-    if (algo == BSP_ALGO_SPLITK) return BSP_E_UNSUPPORTED;
-    BtPlan bp;
-    const bool streaming = K > 0 && bt64_plan(M, K, N, payload_bytes, &bp, 2) && bp.streaming > 0 &&
-                           ((uintptr_t)X & 3u) == 0;
-    if (algo == BSP_ALGO_MFMA && !streaming) return BSP_E_UNSUPPORTED;
-    if (streaming && algo != BSP_ALGO_ROWWAVE)
-        launch_bt64s_w2a4(bp, bitmaps, offsets, payload, (uint32_t)payload_bytes, (int)M, (int)K, X, (int)N, Y, stream);
-    else
+    // the MFMA block kernels (streaming up to K = 4096, ring up to 16384),
+    // else the row-wave kernel
+    Plan p;
+    rc = choose_plan_w2(s, payload_bytes, algo, &p);
+    if (rc != BSP_OK) return rc;
+    if (p.kind == PK_BT64 && ((uintptr_t)X & 3u) != 0) {
+        if (algo == BSP_ALGO_MFMA) return BSP_E_UNSUPPORTED;
+        p.kind = PK_ROWWAVE;
+    }
+    const BtPlan &bp = p.bt;
+    if (p.kind == PK_BT64) {
+        if (bp.streaming)
+            launch_bt64s_w2a4(bp, bitmaps, offsets, payload, (uint32_t)payload_bytes, (int)M, (int)K, X, (int)N, Y,
+                              stream);
+        else
+            launch_bt64_w2a4(bp, bitmaps, offsets, payload, (uint32_t)payload_bytes, (int)M, (int)K, X, (int)N, Y,
+                             stream);
+    } else {
         launch_rowwave_w4a4<2>(bitmaps, offsets, payload, (uint32_t)payload_bytes, (int)M, (int)K, X, (int)N, Y, stream);
+    }
     return launch_status();
 }
 

@@ -258,9 +258,11 @@ int bsp_describe_plan(int dtype, int64_t M, int64_t K, int64_t N, int64_t nnz, i
  * BSP_INT2: the W2A4 setting of UnionSparse Sec. VII, Fig. 11) and X packed
  * int4 as for spmm_bitmap_w4a4; Y int32 [N][M], exact. payload_bytes >=
  * ceil(nnz/4), a multiple of BSP_PAYLOAD_ALIGN. The automatic choice runs the
- * streaming MFMA kernel (K <= 4096, X on a 4-byte boundary) and the plain
- * kernel elsewhere; _algo forces BSP_ALGO_MFMA (BSP_E_UNSUPPORTED outside it)
- * or BSP_ALGO_ROWWAVE; BSP_ALGO_SPLITK returns BSP_E_UNSUPPORTED.
+ * MFMA block kernels (streaming up to K = 4096, the ring kernel up to 16384;
+ * X on a 4-byte boundary) and the plain kernel elsewhere; _algo forces
+ * BSP_ALGO_MFMA (BSP_E_UNSUPPORTED outside it) or BSP_ALGO_ROWWAVE;
+ * BSP_ALGO_SPLITK returns BSP_E_UNSUPPORTED. bsp_describe_selection and
+ * bsp_describe_plan with dtype BSP_INT2 describe these plans.
  */
 int spmm_bitmap_w2a4(const uint64_t *bitmaps, const uint32_t *offsets, const uint8_t *payload,
                      int64_t payload_bytes, int64_t M, int64_t K, const uint8_t *X, int64_t N,

@@ -59,8 +59,9 @@ def test_w2a4_extremes(dev):
         assert (run(W, X, bsp.ALGO_MFMA, dev) == 16 * K).all()
 
 
-def test_w2a4_past_streaming_kernel(dev):
-    p = workloads.random_int2_problem(3, 40, 8192, 4, keep=0.4)
+def test_w2a4_past_mfma_kernels(dev):
+    # past K = 16384 only the plain kernel runs W2A4; a forced MFMA call is refused
+    p = workloads.random_int2_problem(3, 40, 16400, 4, keep=0.4)
     assert np.array_equal(run(p.W, p.X, bsp.ALGO_AUTO, dev), ref(p.W, p.X))
     enc = bsp.encode(p.W, dtype=bsp.INT2)
     with pytest.raises(bsp.BspError) as ei:
@@ -68,7 +69,34 @@ def test_w2a4_past_streaming_kernel(dev):
     assert ei.value.status == bsp.E_UNSUPPORTED
 
 
-@pytest.mark.parametrize("config,index,N", [("qkv", 0, 8), ("qkv", 0, 32), ("qkv", 0, 1), ("ffn", 0, 16)])
+RING = [  # (M, K, N, keep): past the streaming kernel, the ring kernel with 2-bit values
+    (40, 8192, 4, 0.4),       # 4 tiles per lane
+    (300, 11008, 16, 0.3),    # 8 tiles per lane
+    (100, 5000, 32, 0.5),     # two column blocks, ragged last tile
+    (50, 6001, 5, 0.5),       # X rows off a 4-byte boundary
+    (70, 16384, 17, 0.95),    # two column blocks at 8 tiles per lane, near dense
+    (20000, 4096, 8, 0.5),    # more than three blocks per workgroup: the ring at 2 tiles per lane
+]
+
+
+@pytest.mark.parametrize("M,K,N,keep", RING)
+@pytest.mark.parametrize("algo", [bsp.ALGO_AUTO, bsp.ALGO_MFMA])
+def test_w2a4_ring_kernel(M, K, N, keep, algo, dev):
+    p = workloads.random_int2_problem(M * 31 + K + N, M, K, N, keep=keep)
+    d = bsp.describe(bsp.INT2, M, K, N, int(np.count_nonzero(p.W)), algo=bsp.ALGO_MFMA)
+    assert "kernel=k_bt64_w4a4 " in d, d
+    assert np.array_equal(run(p.W, p.X, algo, dev), ref(p.W, p.X))
+
+
+def test_w2a4_ring_extremes(dev):
+    for K in (4160, 8192, 16384):
+        W = np.full((48, K), -2, np.int8)
+        X = np.full((5, K), -8, np.int8)
+        assert (run(W, X, bsp.ALGO_MFMA, dev) == 16 * K).all()
+
+
+@pytest.mark.parametrize("config,index,N", [("qkv", 0, 8), ("qkv", 0, 32), ("qkv", 0, 1), ("ffn", 0, 16), ("ffn", 1, 16),
+                                            ("lowsparse", 0, 32)])
 def test_w2a4_full_workloads(config, index, N, dev):
     p = workloads.make(config)[index]
     X = p.meta.get("X_full", p.X)[:N]

@@ -43,7 +43,24 @@ def test_w2a4_host_errors():
     assert call(Y=None) == bsp.E_ARG
     assert call(pb=12) == bsp.E_ARG
     assert call(algo=bsp.ALGO_SPLITK) == bsp.E_UNSUPPORTED
-    assert call(algo=bsp.ALGO_MFMA, K=8192) == bsp.E_UNSUPPORTED        # past the streaming kernel
+    assert call(algo=bsp.ALGO_MFMA, K=16385) == bsp.E_UNSUPPORTED       # past the MFMA block kernels
     assert call(algo=bsp.ALGO_MFMA, X=ctypes.c_void_p(0x1001)) == bsp.E_UNSUPPORTED
     assert call(algo=9) == bsp.E_ARG
     assert call(M=0) == bsp.OK and call(N=0) == bsp.OK
+
+
+def test_w2a4_plan_descriptions():
+    # the W2A4 plans: the streaming kernel up to K = 4096, the ring kernel up to
+    # 16384 (2-bit values, never staggered), the plain kernel past it; no split-K
+    d = bsp.describe(bsp.INT2, 12288, 4096, 8, 12288 * 4096 // 2)
+    assert d.startswith("dtype=int2 ") and "-> mfma kernel=k_bt64s_w2a4 " in d, d
+    for K in (4097, 11008, 16384):
+        d = bsp.describe(bsp.INT2, 4096, K, 16, 4096 * K * 3 // 10)
+        assert "-> mfma kernel=k_bt64_w4a4 " in d and "stagger=0" in d, d
+    d = bsp.describe(bsp.INT2, 4096, 16385, 16, 4096 * 16385 * 3 // 10)
+    assert "-> rowwave kernel=k_rowwave_w4a4" in d, d
+    assert "-> rowwave " in bsp.describe(bsp.INT2, 4096, 11008, 16, -1, algo=bsp.ALGO_ROWWAVE)
+    for algo, K in [(bsp.ALGO_SPLITK, 11008), (bsp.ALGO_MFMA, 16385)]:
+        with pytest.raises(bsp.BspError) as ei:
+            bsp.describe(bsp.INT2, 4096, K, 16, -1, algo=algo)
+        assert ei.value.status == bsp.E_UNSUPPORTED

@@ -36,19 +36,20 @@ def _case(i):
     while M * K * N > 3e8:
         K = max(1, K // 2)
     keep = float(rng.choice([0.02, 0.1, 0.3, 0.5, 0.7, 0.95]))
-    return dt, M, K, N, keep
+    rows = bool(rng.random() < 0.3)   # every row keeps the same count (drawn last: the shapes stay)
+    return dt, M, K, N, keep, rows
 
 
 @pytest.mark.parametrize("i", range(120))
 def test_random_case(i, dev):
-    dt, M, K, N, keep = _case(i)
+    dt, M, K, N, keep, rows = _case(i)
     if dt == bsp.INT4:
-        p = workloads.random_int4_problem(20000 + i, M, K, N, keep=keep)
+        p = workloads.random_int4_problem(20000 + i, M, K, N, keep=keep, rows=rows)
         enc = bsp.encode(p.W)
         ref = oracle.spmm_w4a4(oracle.encode(p.W), pins._pack_x_for_test(p.X), N, threads=16)
         Xd = torch.from_numpy(bsp.pack_int4(p.X)).to(dev)
     else:
-        p = workloads.random_fp16_problem(20000 + i, M, K, N, sparsity=1.0 - keep)
+        p = workloads.random_fp16_problem(20000 + i, M, K, N, sparsity=1.0 - keep, rows=rows)
         enc = bsp.encode(p.W)
         ref = oracle.spmm_f16(oracle.encode(p.W), p.X, threads=16)
         Xd = torch.from_numpy(p.X).to(dev)

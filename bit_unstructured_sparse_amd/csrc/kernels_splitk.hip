@@ -793,8 +793,19 @@ static bool sk_plan(int dtype, int64_t M, int64_t K, int64_t N, int64_t payload_
     // wavefronts: enough for the split's tiles, fewer (shorter chunks, smaller
     // slots) when the slots of a dense set would not fit the LDS
     int nw = (int)std::min<int64_t>(max_waves, (std::min<int64_t>(p->tps, (int64_t)per_wave * max_waves) + per_wave - 1) / per_wave);
-    for (;; nw = nw > 1 ? nw / 2 : 0) {
-        if (nw == 0) return false;
+    // fp16 past 256 workgroups: shorter chunks (at least 4 wavefronts) so
+    // that up to 4 workgroups share a CU instead of running in rounds of one
+    // (N = 1: 5120 x 5120 34.2 -> 20.2 us, 13824 x 5120 66.7 -> 33.2, 5120 x
+    // 13824 65.9 -> 40.8, 8192 x 8192 36.9 -> 27.1; N = 8 42.1 -> 30.8); a
+    // second pass takes the whole LDS when that fails
+    const int64_t wg_per_cu =
+            dtype == BSP_FP16 ? std::min<int64_t>(4, ((int64_t)p->nsets * p->S + BT_CUS - 1) / BT_CUS) : 1;
+    for (int pass = 0;; nw = nw > 1 ? nw / 2 : 0) {
+        if (nw == 0) {
+            if (pass == 1 || wg_per_cu == 1) return false;
+            pass = 1;
+            nw = (int)std::min<int64_t>(max_waves, (std::min<int64_t>(p->tps, (int64_t)per_wave * max_waves) + per_wave - 1) / per_wave);
+        }
         const int64_t ct = (int64_t)per_wave * nw;
         // slot per row segment: the average segment of a chunk, +30 % and
         // 64 B of windows and granule alignment (at most a dense segment); a
@@ -803,7 +814,7 @@ static bool sk_plan(int dtype, int64_t M, int64_t K, int64_t N, int64_t payload_
         const int64_t seg_max = dtype == BSP_INT4 ? ct * 32 : ct * 128;
         const int iseg = (int)std::max<int64_t>(1, (std::min(seg_avg + seg_avg * 3 / 10, seg_max) + 64 + 1023) / 1024);
         const size_t lds = dtype == BSP_INT4 ? bsk_w4a4_lds(nw, p->nbs, iseg) : bsk_f16_lds(nw, p->nb, p->nbs, iseg);
-        if (lds <= 160 * 1024) {
+        if (lds <= (size_t)(160 * 1024 / (pass ? 1 : wg_per_cu)) && (pass || nw >= 4 || wg_per_cu == 1)) {
             p->nwaves = nw;
             p->iseg = iseg;
             p->lds = lds;

@@ -566,6 +566,16 @@ def test_w4a4_wide_n_past_k8192_auto(dev, M, K, N, with_ws):
         assert not ws[:65536].any(), "arrival counters left nonzero"
 
 
+@pytest.mark.parametrize("M,K,N", [(5120, 5120, 1), (13824, 5120, 3), (8200, 8192, 8), (4500, 6000, 17)])
+def test_splitk_f16_shared_cus(dev, M, K, N):
+    # fp16 split-K past 256 workgroups, two to four sharing a CU (shorter chunks)
+    p = workloads.random_fp16_problem(M + K + N, M, K, N, sparsity=0.6)
+    enc = bsp.encode(p.W)
+    d = bsp.describe(bsp.FP16, M, K, N, enc.nnz)
+    assert "-> splitk kernel=k_bsk_f16 " in d and "block=1024" not in d, d
+    _assert_f16(run_f16(p.W, p.X, bsp.ALGO_AUTO, dev, enc=enc), oracle.spmm_f16(oracle.encode(p.W), p.X))
+
+
 SPLITK_STREAMED = [  # (M, K, N, keep): the streamed split-K kernel (one pass per block and K range)
     (100, 64 * 65, 3, 0.5),      # two tiles per lane, ragged last block
     (513, 6000, 17, 0.5),        # two column blocks, ragged last tile

@@ -453,3 +453,13 @@ def test_wide_n_past_k8192_takes_split_k():
     # forced, the ring kernel still runs the shape
     d = bsp.describe(bsp.INT4, 4096, 11008, 32, 4096 * 11008 * 3 // 10, algo=bsp.ALGO_MFMA)
     assert "kernel=k_bt64_w4a4 " in d and "tiles_per_lane=8" in d, d
+
+
+def test_f16_split_plans_share_cus_past_256_workgroups():
+    # fp16 split-K past 256 workgroups: shorter chunks so that the workgroups
+    # share the CUs instead of running in rounds of one per CU
+    for M, K, maxlds, block in [(5120, 5120, 80, 512), (13824, 5120, 40, 256), (8192, 8192, 80, 512)]:
+        kv = _kv(bsp.describe(bsp.FP16, M, K, 1, int(M * K * 0.4)))
+        assert int(kv["lds"]) <= maxlds * 1024 and kv["block"] == str(block), (M, K, kv)
+    kv = _kv(bsp.describe(bsp.FP16, 4096, 11008, 1, int(4096 * 11008 * 0.4)))
+    assert kv["grid"] == "256" and kv["block"] == "1024", kv

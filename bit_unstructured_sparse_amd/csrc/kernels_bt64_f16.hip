@@ -441,7 +441,7 @@ __global__ __launch_bounds__(1024) void k_bt64_f16(
 // once step s has landed), areas used in a ring of three so that the area a
 // DMA fills was last read two barriers earlier. A step larger than the area
 // reads its windows from global memory.
-#define BF8_NSTEP_MAX 4                  // steps per workgroup, at most (NSTEP 2 or 4)
+#define BF8_NSTEP_MAX 8                  // steps per workgroup, at most (NSTEP 2, 4 or 8)
 #define BF8_WAVES 8
 
 template <int NSTEP, bool XR>
@@ -634,7 +634,7 @@ __global__ __launch_bounds__(512) void k_bt8_f16(
 // Plan of the eight-row kernel, or false when it does not apply.
 struct Bf8Plan {
     int nwaves;
-    int nstep;   // step slots per workgroup (2 or 4), a template argument
+    int nstep;   // step slots per workgroup (2, 4 or 8), a template argument
     unsigned grid;
     int sq, sr;
     uint32_t area_kb;
@@ -646,24 +646,36 @@ static bool bf8_plan(int64_t M, int64_t K, int64_t N, int64_t payload_bytes, Bf8
     const int64_t T = (K + 63) / 64, T2 = (T + 1) / 2;
     p->nwaves = (int)((T2 + 3) / 4);
     const int64_t steps = (M + 7) / 8;
-    // two steps per workgroup at least (the second streams in while the
-    // first decodes), one workgroup per CU, at most BF8_NSTEP_MAX steps each;
-    // two step slots when that suffices (the prologue loads every slot's
-    // words: fewer loads ahead of the first DMA)
-    const int64_t grid = std::max<int64_t>(std::min<int64_t>((steps + 1) / 2, BF_CUS), (steps + BF8_NSTEP_MAX - 1) / BF8_NSTEP_MAX);
-    p->nstep = (steps + grid - 1) / grid <= 2 ? 2 : BF8_NSTEP_MAX;
-    p->grid = (unsigned)grid;
-    p->sq = (int)(steps / grid);
-    p->sr = (int)(steps % grid);
-    const int64_t per_wg = (steps + grid - 1) / grid;
     // staging per step: 1.2x the average step plus 2 KB, in KB (a larger
     // step reads its windows from global memory), capped at a dense step
     const int64_t avg = payload_bytes / std::max<int64_t>(steps, 1);
     const int64_t worst = 8 * T * 128 + 64;
     const int64_t est = std::min<int64_t>(worst, avg + avg / 5 + 2048) + 32;
     p->area_kb = (uint32_t)std::max<int64_t>(1, (est + 1023) / 1024);
-    p->lds = 128 + (size_t)p->nstep * BF_ROWS * BF8_WAVES * 4 + (size_t)per_wg * p->nwaves * 256 * 4 +
-             (size_t)std::min<int64_t>(per_wg, 3) * p->area_kb * 1024;
+    const auto lds_of = [&](int64_t per_wg, int nstep) -> size_t {
+        return 128 + (size_t)nstep * BF_ROWS * BF8_WAVES * 4 + (size_t)per_wg * p->nwaves * 256 * 4 +
+               (size_t)std::min<int64_t>(per_wg, 3) * p->area_kb * 1024;
+    };
+    // two steps per workgroup at least (the second streams in while the
+    // first decodes), one workgroup per CU; two step slots when that
+    // suffices (the prologue loads every slot's words: fewer loads ahead of
+    // the first DMA). Up to 8 steps each when that keeps the grid to one
+    // workgroup per CU and fits the LDS, else up to 4 in rounds (11008 x 4096
+    // at N = 1: 24.0 us in 1.34 rounds of 4 steps, 8192 rows 13.5)
+    int64_t grid = std::max<int64_t>(std::min<int64_t>((steps + 1) / 2, BF_CUS), (steps + 3) / 4);
+    int nstep = (steps + grid - 1) / grid <= 2 ? 2 : 4;
+    const int64_t grid8 = std::max<int64_t>(std::min<int64_t>((steps + 1) / 2, BF_CUS), (steps + 7) / 8);
+    const int64_t per8 = (steps + grid8 - 1) / grid8;
+    if (per8 > 4 && grid8 <= BF_CUS && lds_of(per8, 8) <= (size_t)BF_LDS_MAX) {
+        grid = grid8;
+        nstep = 8;
+    }
+    p->nstep = nstep;
+    p->grid = (unsigned)grid;
+    p->sq = (int)(steps / grid);
+    p->sr = (int)(steps % grid);
+    const int64_t per_wg = (steps + grid - 1) / grid;
+    p->lds = lds_of(per_wg, nstep);
     return p->lds <= (size_t)BF_LDS_MAX;
 }
 
@@ -681,8 +693,10 @@ static void launch_bt8_f16(const Bf8Plan &p, const uint64_t *bitmaps, const uint
     } while (0)
     if (p.nstep == 2) {
         if (N > 4) BF8_LAUNCH(2, true); else BF8_LAUNCH(2, false);
+    } else if (p.nstep == 4) {
+        if (N > 4) BF8_LAUNCH(4, true); else BF8_LAUNCH(4, false);
     } else {
-        if (N > 4) BF8_LAUNCH(BF8_NSTEP_MAX, true); else BF8_LAUNCH(BF8_NSTEP_MAX, false);
+        if (N > 4) BF8_LAUNCH(8, true); else BF8_LAUNCH(8, false);
     }
 #undef BF8_LAUNCH
 }

@@ -576,6 +576,18 @@ def test_splitk_f16_shared_cus(dev, M, K, N):
     _assert_f16(run_f16(p.W, p.X, bsp.ALGO_AUTO, dev, enc=enc), oracle.spmm_f16(oracle.encode(p.W), p.X))
 
 
+@pytest.mark.parametrize("algo", [bsp.ALGO_AUTO, bsp.ALGO_MFMA], ids=["auto", "mfma"])
+@pytest.mark.parametrize("M,N", [(8200, 1), (11008, 8), (12288, 3)])
+def test_f16_eight_row_eight_steps(dev, M, N, algo):
+    # the eight-row fp16 kernel with up to 8 steps per workgroup (8200 rows:
+    # one workgroup of 5 steps, the rest 4)
+    p = workloads.random_fp16_problem(M + N, M, 4096, N, sparsity=0.6)
+    enc = bsp.encode(p.W)
+    d = bsp.describe(bsp.FP16, M, 4096, N, enc.nnz)
+    assert "kernel=k_bt8_f16 " in d and "step_slots=8" in d, d
+    _assert_f16(run_f16(p.W, p.X, algo, dev, enc=enc), oracle.spmm_f16(oracle.encode(p.W), p.X))
+
+
 SPLITK_STREAMED = [  # (M, K, N, keep): the streamed split-K kernel (one pass per block and K range)
     (100, 64 * 65, 3, 0.5),      # two tiles per lane, ragged last block
     (513, 6000, 17, 0.5),        # two column blocks, ragged last tile

@@ -463,3 +463,15 @@ def test_f16_split_plans_share_cus_past_256_workgroups():
         assert int(kv["lds"]) <= maxlds * 1024 and kv["block"] == str(block), (M, K, kv)
     kv = _kv(bsp.describe(bsp.FP16, 4096, 11008, 1, int(4096 * 11008 * 0.4)))
     assert kv["grid"] == "256" and kv["block"] == "1024", kv
+
+
+def test_f16_eight_row_plans_take_up_to_eight_steps():
+    # up to 8 steps per workgroup on one workgroup per CU (no rounds) when
+    # the LDS holds them; 4-step rounds otherwise
+    for M, slots, grid in [(4096, 2, 256), (8192, 4, 256), (8200, 8, 256), (11008, 8, 256), (12288, 8, 256),
+                           (16384, 4, 512)]:
+        kv = _kv(bsp.describe(bsp.FP16, M, 4096, 1, int(M * 4096 * 0.4)))
+        assert kv["step_slots"] == str(slots) and kv["grid"] == str(grid), (M, kv)
+        assert int(kv["lds"]) <= 160 * 1024
+    kv = _kv(bsp.describe(bsp.FP16, 11008, 4096, 1, int(11008 * 4096 * 0.5)))   # 8 steps would not fit
+    assert kv["step_slots"] == "4" and kv["grid"] == "344", kv

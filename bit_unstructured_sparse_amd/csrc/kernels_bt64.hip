@@ -420,7 +420,9 @@ __device__ __forceinline__ BtRange bt_range(uint32_t nibA, uint32_t nibB) {
 // unstaggered).
 #define BT_R61_RUN 61u
 #define BT_R61_MAG 2200291u   // ceil(2^32 / (61 * 32)): umulhi(p, MAG) = p / 1952 for p < 2^20
-template <int NB, int TPL, bool XU, bool STG, int WB = 4>
+// NBLK: blocks per workgroup, at most (8 / TPL, or 8 at TPL 2 past 1024
+// blocks).
+template <int NB, int TPL, bool XU, bool STG, int WB = 4, int NBLK = BT_NBLK(TPL)>
 // (The arguments the first loads need come first: they are the ones a
 // kernel-argument preload would place in registers.)
 __global__ __launch_bounds__(BT_WG_THREADS(TPL)) void k_bt64_w4a4(
@@ -430,7 +432,6 @@ __global__ __launch_bounds__(BT_WG_THREADS(TPL)) void k_bt64_w4a4(
         const float *sx) {
     static_assert(WB == 4 || (WB == 2 && !STG), "staggered staging is for int4 streams");
     const BtEpi epi{Yh, sw, sx};
-    constexpr int NBLK = BT_NBLK(TPL);
     constexpr int WC = BT_WG_THREADS(TPL) / 64;          // row-total columns: wavefronts, at most
     constexpr uint32_t VPB = 8 / WB;                     // values per payload byte
     constexpr int PS = WB == 4 ? 8 : 10;                 // log2 of the A x B operand scale
@@ -1068,6 +1069,7 @@ struct BtPlan {
     int stagger;            // staggered staging (rows near a multiple of 256 B, ring kernel 64 B, long)
     int area_kb;            // streaming variant: KB of staging per block
     int one_pass;           // every block staged at once: one barrier before and one after the decode
+    int nblk;               // ring kernel: blocks per workgroup, at most (a template argument)
     size_t lds;             // total dynamic LDS
 };
 
@@ -1084,8 +1086,13 @@ static bool bt64_plan(int64_t M, int64_t K, int64_t N, int64_t payload_bytes, Bt
     p->tpl = T <= 64 ? 2 : T <= 128 ? 4 : 8;
     p->nwaves = (int)((T + 4 * p->tpl - 1) / (4 * p->tpl));
     p->nb = N <= 16 ? 1 : 2;
-    const int64_t nblk_max = BT_NBLK(p->tpl);
     const int64_t blocks = (M + BT_ROWS - 1) / BT_ROWS;
+    // at 2 tiles per lane up to 8 blocks per workgroup where 4 would need
+    // more than one workgroup per CU (rounds): int4 at N = 8, density 0.5,
+    // 20000 x 4096 took 22.1 us in 1.22 rounds of 4, 16384 rows 12.6
+    int64_t nblk_max = BT_NBLK(p->tpl);
+    if (p->tpl == 2 && blocks > BT_CUS * nblk_max && blocks <= BT_CUS * 8) nblk_max = 8;
+    p->nblk = (int)nblk_max;
     // one workgroup per CU when that leaves each at most nblk_max blocks
     const int64_t grid0 = std::max<int64_t>(std::min<int64_t>(blocks, BT_CUS), (blocks + nblk_max - 1) / nblk_max);
     const int64_t per_wg0 = (blocks + grid0 - 1) / grid0;                 // blocks of the busiest workgroup
@@ -1196,15 +1203,30 @@ static bool bt64_plan(int64_t M, int64_t K, int64_t N, int64_t payload_bytes, Bt
     return true;
 }
 
+template <int NB, int TPL, bool XU, bool STG, int WB, int NBLK>
+static void launch_bt64_n(const BtPlan &p, const uint64_t *bitmaps, const uint32_t *offsets,
+                          const uint8_t *payload, uint32_t payload_bytes, int M, int K, const uint8_t *X, int N,
+                          int32_t *Y, const BtEpi &e, hipStream_t stream) {
+    (void)hipFuncSetAttribute((const void *)k_bt64_w4a4<NB, TPL, XU, STG, WB, NBLK>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds);
+    hipLaunchKernelGGL((k_bt64_w4a4<NB, TPL, XU, STG, WB, NBLK>), dim3(p.grid), dim3(64 * p.nwaves), p.lds, stream,
+                       offsets, M, K, p.bq, p.br, bitmaps, X, N, payload, payload_bytes, Y, p.stage_bytes, p.nbuf,
+                       p.one_pass, e.Yh, e.sw, e.sx);
+}
+
 template <int NB, int TPL, bool XU, bool STG, int WB = 4>
 static void launch_bt64_s(const BtPlan &p, const uint64_t *bitmaps, const uint32_t *offsets,
                           const uint8_t *payload, uint32_t payload_bytes, int M, int K, const uint8_t *X, int N,
                           int32_t *Y, const BtEpi &e, hipStream_t stream) {
-    (void)hipFuncSetAttribute((const void *)k_bt64_w4a4<NB, TPL, XU, STG, WB>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds);
-    hipLaunchKernelGGL((k_bt64_w4a4<NB, TPL, XU, STG, WB>), dim3(p.grid), dim3(64 * p.nwaves), p.lds, stream, offsets,
-                       M, K, p.bq, p.br, bitmaps, X, N, payload, payload_bytes, Y, p.stage_bytes, p.nbuf, p.one_pass,
-                       e.Yh, e.sw, e.sx);
+    if constexpr (TPL == 2) {
+        if (p.nblk == 8) {
+            launch_bt64_n<NB, TPL, XU, STG, WB, 8>(p, bitmaps, offsets, payload, payload_bytes, M, K, X, N, Y, e,
+                                                   stream);
+            return;
+        }
+    }
+    launch_bt64_n<NB, TPL, XU, STG, WB, BT_NBLK(TPL)>(p, bitmaps, offsets, payload, payload_bytes, M, K, X, N, Y, e,
+                                                      stream);
 }
 
 // W2A4 through the ring kernel (K past the streaming kernel's 4096), int32 Y

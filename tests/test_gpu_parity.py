@@ -475,6 +475,9 @@ LARGE_GRIDS = [  # (M, K, N, keep, rows): int4 plans past 256 workgroups, dense 
     (5000, 12001, 3, 0.5, False),    # 313 workgroups, ragged last block, X rows off a 4-byte boundary
     (8192, 8192, 8, 0.9, False),     # one block per workgroup
     (65536, 4096, 8, 0.5, False),    # four blocks per workgroup, four rounds
+    (16400, 4096, 8, 0.5, False),    # up to 8 blocks per workgroup (2 tiles per lane), 5 buffers refilled
+    (22016, 4096, 32, 0.5, False),   # the same with two column blocks
+    (20000, 4091, 5, 0.5, True),     # the same, rows of one length, X rows off a 4-byte boundary
     (4096, 16384, 8, 0.9, False),    # too dense to stage: split-K (auto), global windows (forced)
     (4096, 16384, 8, 0.5, True),     # every row 4096 B long
     (12288, 4096, 8, 0.5, True),     # every row 1024 B long: staggered streaming

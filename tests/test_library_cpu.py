@@ -475,3 +475,12 @@ def test_f16_eight_row_plans_take_up_to_eight_steps():
         assert int(kv["lds"]) <= 160 * 1024
     kv = _kv(bsp.describe(bsp.FP16, 11008, 4096, 1, int(11008 * 4096 * 0.5)))   # 8 steps would not fit
     assert kv["step_slots"] == "4" and kv["grid"] == "344", kv
+
+
+def test_ring_plans_take_eight_blocks_at_two_tiles_per_lane():
+    # K <= 4096 past 1024 blocks: up to 8 blocks per workgroup on 256
+    # workgroups instead of rounds of 4
+    for M, grid in [(16384, 256), (16400, 256), (20000, 256), (32768, 256), (33000, 516)]:
+        kv = _kv(bsp.describe(bsp.INT4, M, 4096, 8, M * 2048))
+        assert "kernel=k_bt64_w4a4 " in bsp.describe(bsp.INT4, M, 4096, 8, M * 2048)
+        assert kv["grid"] == str(grid) and int(kv["lds"]) <= 160 * 1024, (M, kv)

@@ -420,8 +420,8 @@ __device__ __forceinline__ BtRange bt_range(uint32_t nibA, uint32_t nibB) {
 // unstaggered).
 #define BT_R61_RUN 61u
 #define BT_R61_MAG 2200291u   // ceil(2^32 / (61 * 32)): umulhi(p, MAG) = p / 1952 for p < 2^20
-// NBLK: blocks per workgroup, at most (8 / TPL, or 8 at TPL 2 past 1024
-// blocks).
+// NBLK: blocks per workgroup, at most (8 / TPL; 8 at TPL 2 past 1024 blocks,
+// 4 at TPL 4 and NB 1 past 512).
 template <int NB, int TPL, bool XU, bool STG, int WB = 4, int NBLK = BT_NBLK(TPL)>
 // (The arguments the first loads need come first: they are the ones a
 // kernel-argument preload would place in registers.)
@@ -1092,6 +1092,7 @@ static bool bt64_plan(int64_t M, int64_t K, int64_t N, int64_t payload_bytes, Bt
     // 20000 x 4096 took 22.1 us in 1.22 rounds of 4, 16384 rows 12.6
     int64_t nblk_max = BT_NBLK(p->tpl);
     if (p->tpl == 2 && blocks > BT_CUS * nblk_max && blocks <= BT_CUS * 8) nblk_max = 8;
+    if (p->tpl == 4 && p->nb == 1 && blocks > BT_CUS * nblk_max && blocks <= BT_CUS * 4) nblk_max = 4;
     p->nblk = (int)nblk_max;
     // one workgroup per CU when that leaves each at most nblk_max blocks
     const int64_t grid0 = std::max<int64_t>(std::min<int64_t>(blocks, BT_CUS), (blocks + nblk_max - 1) / nblk_max);
@@ -1221,6 +1222,13 @@ static void launch_bt64_s(const BtPlan &p, const uint64_t *bitmaps, const uint32
     if constexpr (TPL == 2) {
         if (p.nblk == 8) {
             launch_bt64_n<NB, TPL, XU, STG, WB, 8>(p, bitmaps, offsets, payload, payload_bytes, M, K, X, N, Y, e,
+                                                   stream);
+            return;
+        }
+    }
+    if constexpr (TPL == 4 && NB == 1) {   // (two column blocks would spill)
+        if (p.nblk == 4) {
+            launch_bt64_n<NB, TPL, XU, STG, WB, 4>(p, bitmaps, offsets, payload, payload_bytes, M, K, X, N, Y, e,
                                                    stream);
             return;
         }

@@ -478,6 +478,8 @@ LARGE_GRIDS = [  # (M, K, N, keep, rows): int4 plans past 256 workgroups, dense 
     (16400, 4096, 8, 0.5, False),    # up to 8 blocks per workgroup (2 tiles per lane), 5 buffers refilled
     (22016, 4096, 32, 0.5, False),   # the same with two column blocks
     (20000, 4091, 5, 0.5, True),     # the same, rows of one length, X rows off a 4-byte boundary
+    (10240, 8192, 8, 0.5, False),    # up to 4 blocks per workgroup (4 tiles per lane), 3 buffers refilled
+    (11008, 5121, 16, 0.5, True),    # the same, one pass, rows of one length, X off a 4-byte boundary
     (4096, 16384, 8, 0.9, False),    # too dense to stage: split-K (auto), global windows (forced)
     (4096, 16384, 8, 0.5, True),     # every row 4096 B long
     (12288, 4096, 8, 0.5, True),     # every row 1024 B long: staggered streaming

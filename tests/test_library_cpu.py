@@ -484,3 +484,12 @@ def test_ring_plans_take_eight_blocks_at_two_tiles_per_lane():
         kv = _kv(bsp.describe(bsp.INT4, M, 4096, 8, M * 2048))
         assert "kernel=k_bt64_w4a4 " in bsp.describe(bsp.INT4, M, 4096, 8, M * 2048)
         assert kv["grid"] == str(grid) and int(kv["lds"]) <= 160 * 1024, (M, kv)
+
+
+def test_ring_plans_take_four_blocks_at_four_tiles_per_lane():
+    # 4096 < K <= 8192, N <= 16, past 512 blocks: up to 4 blocks per workgroup
+    # on 256 workgroups; two column blocks keep 2 (4 would spill)
+    for M, K, N, grid in [(8200, 8192, 8, 256), (10240, 8192, 8, 256), (13824, 5120, 16, 256), (10240, 8192, 32, 320),
+                          (16400, 8192, 8, 513)]:
+        kv = _kv(bsp.describe(bsp.INT4, M, K, N, M * K // 2))
+        assert kv["tiles_per_lane"] == "4" and kv["grid"] == str(grid) and int(kv["lds"]) <= 160 * 1024, (M, kv)

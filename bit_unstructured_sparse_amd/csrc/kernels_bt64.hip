@@ -1177,13 +1177,17 @@ static bool bt64_plan(int64_t M, int64_t K, int64_t N, int64_t payload_bytes, Bt
     if (p->tpl == 2) {
         // staging per block: the estimate above in whole KB (with 3 extra
         // granules per 64 when staggered), at least 2 KB per wavefront
-        // average payload bytes per row within 28 B of a multiple of 128:
-        // the same tile of every row, or of every other row, falls on the
-        // same LDS banks when the rows are of one length (12288 x 4096 at N =
-        // 8, rows of 1152 B: 10.45 -> 9.13 us; iid masks of that density
-        // 9.11 / 9.28; elsewhere the plain layout does as well or better)
-        const int64_t rb = (payload_bytes / std::max<int64_t>(M, 1)) % 128;
-        int stagger = std::min<int64_t>(rb, 128 - rb) < 28;
+        // average payload bytes per row within 28 B of a multiple of 256 or
+        // 12 B of a multiple of 128: the same tile of every row, or of every
+        // other row, falls on the same LDS banks when the rows are of one
+        // length (12288 x 4096 at N = 8, rows of 1152 B: 10.45 -> 9.13 us;
+        // iid masks of that density 9.11 / 9.28). Elsewhere the plain layout
+        // does as well or better (within 28 B of a multiple of 128 as well:
+        // 12288 x 4096 at density 0.3 8.16 -> 8.67 us; 4096 x 4096 at 0.95,
+        // whose blocks above the average then overflow the staggered area,
+        // 5.55 -> 7.47)
+        const int64_t rpb = payload_bytes / std::max<int64_t>(M, 1), rb = rpb % 256, rb2 = rpb % 128;
+        int stagger = std::min<int64_t>(rb, 256 - rb) < 28 || std::min<int64_t>(rb2, 128 - rb2) < 12;
         const int64_t need = (stagger ? est * (BTS_RUN + BTS_OVL) / BTS_RUN : est) + 1023;
         const int64_t area_kb = std::min<int64_t>(4 * p->nwaves, std::max<int64_t>(2 * p->nwaves, need / 1024));
         const int d = (int)((area_kb + p->nwaves - 1) / p->nwaves);   // DMA instructions per wavefront at most

@@ -780,12 +780,16 @@ static bool sk_plan(int dtype, int64_t M, int64_t K, int64_t N, int64_t payload_
     if (M <= 0 || K <= 0 || N < 1 || N > 32 || splits < 1 || splits > SK_NBS_MAX) return false;
     const int64_t T = (K + 63) / 64, blocks = (M + 15) / 16;
     if (splits > 1 && T < 2 * splits) return false;               // at least two tiles per split
-    if (splits > 1 && (blocks + splits - 1) / splits > SK_WS_COUNTERS) return false;   // one counter per set
     if (M * T + 1 > (int64_t)UINT32_MAX / 8) return false;        // 32-bit buffer ranges of words and offsets
     p->dtype = dtype;
     p->nb = N <= 16 ? 1 : 2;
     p->S = splits;
-    p->nbs = splits;
+    // blocks per set: as many as K ranges (int4), one (fp16: more, smaller
+    // workgroups that share the CUs; 4096 x 11008 at N = 1 with 2 ranges
+    // 25.6 -> 22.1 us, N = 8 27.7 -> 24.7, 4096 x 13824 33.0 -> 27.6,
+    // 11008 x 11008 72.1 -> 57.7) while one counter per block is left
+    p->nbs = dtype == BSP_FP16 && blocks <= SK_WS_COUNTERS ? 1 : splits;
+    if (splits > 1 && (blocks + p->nbs - 1) / p->nbs > SK_WS_COUNTERS) return false;   // one counter per set
     p->nsets = (int)((blocks + p->nbs - 1) / p->nbs);
     p->tps = (int)((T + splits - 1) / splits);
     const int per_wave = dtype == BSP_INT4 ? 8 : 4;                 // tiles per wavefront and chunk

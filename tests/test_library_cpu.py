@@ -249,7 +249,7 @@ def test_description_names_the_launched_kernel():
     d = bsp.describe(bsp.FP16, 4096, 11008, 8)
     assert "-> splitk kernel=k_bsk_f16 " in d and "splits=1 " in d
     d = bsp.describe(bsp.FP16, 4096, 11008, 8, workspace=True)
-    assert "-> splitk kernel=k_bsk_f16 " in d and "splits=2 " in d and "blocks_per_set=2 " in d
+    assert "-> splitk kernel=k_bsk_f16 " in d and "splits=2 " in d and "blocks_per_set=1 " in d
     # int4 with a workspace: the block kernels up to K = 16384, one K range
     # up to K = 20480, two beyond
     assert "-> mfma kernel=k_bt64_w4a4 " in bsp.describe(bsp.INT4, 4096, 11008, 16, workspace=True)

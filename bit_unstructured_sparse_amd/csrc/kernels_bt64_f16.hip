@@ -194,15 +194,17 @@ __device__ __forceinline__ void bf_contract(uint64_t word, uint32_t p, const Win
 
 // LDS layout (bytes): [selector table 128][row totals 2 x 16 x 16 ints]
 //   [partials P x nwaves x NB x 256 floats][nbuf staging buffers of stage_bytes]
-// with P = 2 partial sets (block i adds into set i % 2 while set (i - 1) % 2
-// is summed into Y) when a workgroup owns more than one block, else 1.
+// with P = psets partial sets: 2 (block i adds into set i % 2 while set
+// (i - 1) % 2 is summed into Y), or 1 (one block per workgroup; or several,
+// block i's partials written after a barrier that follows the sum of block
+// i - 1), as the plan fits them.
 // Workgroup g owns blocks [g*bq + min(g, br), ...): bq or bq + 1 of them.
 template <int NB>
 __global__ __launch_bounds__(1024) void k_bt64_f16(
         const uint64_t *__restrict__ bitmaps, const uint32_t *__restrict__ offsets,
         const uint16_t *__restrict__ payload, uint32_t payload_bytes, int M, int K,
         const uint16_t *__restrict__ X, int N, uint16_t *__restrict__ Y, uint32_t stage_bytes, uint32_t nbuf,
-        int bq, int br) {
+        int bq, int br, int psets) {
     extern __shared__ __attribute__((aligned(16))) uint8_t bf_smem[];
     const int nwaves = blockDim.x >> 6;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -216,7 +218,6 @@ __global__ __launch_bounds__(1024) void k_bt64_f16(
     uint32_t *lut_lds = reinterpret_cast<uint32_t *>(bf_smem);
     int32_t *wt = reinterpret_cast<int32_t *>(bf_smem + 128);                           // [2][16][16]
     float *part = reinterpret_cast<float *>(wt + 2 * BF_ROWS * BF_MAX_WAVES);            // [P][nwaves][NB*256]
-    const int psets = bq + (br > 0 ? 1 : 0) > 1 ? 2 : 1;                                  // the same in every workgroup
     uint8_t *stage = reinterpret_cast<uint8_t *>(part + psets * nwaves * NB * 256);
     const uint32_t lut = bt_lds_addr(lut_lds);
     const __amdgpu_buffer_rsrc_t prs = bt_rsrc(payload, payload_bytes);
@@ -330,7 +331,7 @@ __global__ __launch_bounds__(1024) void k_bt64_f16(
     auto write_y = [&](int i) -> void {
         const int m0 = (b_begin + i) * BF_ROWS;
         const int rows = min(BF_ROWS, M - m0);
-        const float *pb = part + (i & 1) * nwaves * NB * 256;
+        const float *pb = part + (psets == 2 ? (i & 1) : 0) * nwaves * NB * 256;
         // D layout of the 16x16 MFMAs: lane l, register k -> row 4*(l/16)+k, column l%16
         for (int o = threadIdx.x; o < NB * 256; o += blockDim.x) {
             const int nb = o >> 8, col = (o >> 4) & 15, rl = o & 15;
@@ -407,7 +408,8 @@ __global__ __launch_bounds__(1024) void k_bt64_f16(
         } else {
             bf_contract<NB>(words[i], p, BfWinGlobal{prs, 4u * g.g0}, lut, xb, acc);
         }
-        float *pw = part + (i & 1) * nwaves * NB * 256 + wave * NB * 256;
+        float *pw = part + (psets == 2 ? (i & 1) : 0) * nwaves * NB * 256 + wave * NB * 256;
+        if (psets == 1 && i > 0) __syncthreads();   // block i - 1's sum has read the one set
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -703,6 +705,7 @@ static void launch_bt8_f16(const Bf8Plan &p, const uint64_t *bitmaps, const uint
 
 struct BfPlan {
     int nwaves, nb;
+    int psets;   // sets of per-wavefront partials (1 or 2)
     unsigned grid;
     int bq, br;
     uint32_t stage_bytes, nbuf;
@@ -732,10 +735,20 @@ static bool bf_plan(int64_t M, int64_t K, int64_t N, int64_t payload_bytes, BfPl
     int64_t stage = std::min<int64_t>(worst, avg + avg / 5 + 2048) + 32;
     stage = (stage + 1023) / 1024 * 1024;
     // one set of partials when a workgroup owns a single block (the second
-    // set only overlaps a block's partials with the previous block's sum)
-    const int64_t psets = per_wg > 1 ? 2 : 1;
-    const int64_t fixed = 128 + 2 * BF_ROWS * BF_MAX_WAVES * 4 + psets * (int64_t)p->nwaves * p->nb * 256 * 4;
+    // set only overlaps a block's partials with the previous block's sum),
+    // or when two sets leave too little for two staging buffers
+    int64_t psets = per_wg > 1 ? 2 : 1;
+    int64_t fixed = 128 + 2 * BF_ROWS * BF_MAX_WAVES * 4 + psets * (int64_t)p->nwaves * p->nb * 256 * 4;
     int64_t nbuf = std::min<int64_t>((budget - fixed) / stage, per_wg);
+    if (psets == 2 && nbuf < 2) {
+        const int64_t fixed1 = fixed - (int64_t)p->nwaves * p->nb * 256 * 4;
+        if (std::min<int64_t>((budget - fixed1) / stage, per_wg) >= 2) {
+            psets = 1;
+            fixed = fixed1;
+            nbuf = std::min<int64_t>((budget - fixed) / stage, per_wg);
+        }
+    }
+    p->psets = (int)psets;
     if (nbuf < std::min<int64_t>(2, per_wg)) {   // see the int4 plan
         stage = 0;
         nbuf = 1;
@@ -752,7 +765,7 @@ static void launch_bf_t(const BfPlan &p, const uint64_t *bitmaps, const uint32_t
                         hipStream_t stream) {
     (void)hipFuncSetAttribute((const void *)k_bt64_f16<NB>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds);
     hipLaunchKernelGGL((k_bt64_f16<NB>), dim3(p.grid), dim3(64 * p.nwaves), p.lds, stream, bitmaps, offsets, payload,
-                       payload_bytes, M, K, X, N, Y, p.stage_bytes, p.nbuf, p.bq, p.br);
+                       payload_bytes, M, K, X, N, Y, p.stage_bytes, p.nbuf, p.bq, p.br, p.psets);
 }
 
 static void launch_bt64_f16(const BfPlan &p, const uint64_t *bitmaps, const uint32_t *offsets,

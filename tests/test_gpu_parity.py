@@ -538,6 +538,10 @@ F16_STAGED = [  # (M, K, N, density): the 16-row fp16 kernel staging dense block
     (4096, 4096, 12, 0.95),
     (1000, 4096, 32, 0.75),   # ragged last block
     (5000, 4096, 20, 0.2),    # two blocks per workgroup: two sets, two buffers
+    (8192, 4096, 16, 0.4),    # two blocks per workgroup, one set (a barrier before each block's partials)
+    (16384, 4096, 16, 0.4),   # four blocks per workgroup, one set, two buffers refilled
+    (8192, 4096, 32, 0.3),    # the same with two column blocks
+    (9000, 4096, 10, 0.4),    # two or three blocks per workgroup, ragged last block
 ]
 
 

@@ -493,3 +493,13 @@ def test_ring_plans_take_four_blocks_at_four_tiles_per_lane():
                           (16400, 8192, 8, 513)]:
         kv = _kv(bsp.describe(bsp.INT4, M, K, N, M * K // 2))
         assert kv["tiles_per_lane"] == "4" and kv["grid"] == str(grid) and int(kv["lds"]) <= 160 * 1024, (M, kv)
+
+
+def test_f16_block_plan_one_set_for_several_blocks():
+    # several blocks per workgroup: one set of partials (and a barrier per
+    # block) when two sets would leave no room for two staging buffers
+    for M, N, dens in [(8192, 16, 0.4), (16384, 16, 0.4), (8192, 32, 0.3), (9000, 10, 0.4)]:
+        kv = _kv(bsp.describe(bsp.FP16, M, 4096, N, int(M * 4096 * dens)))
+        nb = 1 if N <= 16 else 2
+        assert kv["stage_bufs"] == "2", (M, N, kv)
+        assert int(kv["lds"]) == 128 + 2048 + 16 * nb * 1024 + 2 * 1024 * int(kv["stage_kb"]), (M, N, kv)

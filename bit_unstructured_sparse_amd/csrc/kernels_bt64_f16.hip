@@ -446,7 +446,7 @@ __global__ __launch_bounds__(1024) void k_bt64_f16(
 #define BF8_NSTEP_MAX 8                  // steps per workgroup, at most (NSTEP 2, 4 or 8)
 #define BF8_WAVES 8
 
-template <int NSTEP, bool XR>
+template <int NSTEP, bool XR, bool RING = false>
 __global__ __launch_bounds__(512) void k_bt8_f16(
         const uint32_t *__restrict__ offsets, int M, int K, int sq, int sr, const uint64_t *__restrict__ bitmaps,
         const uint16_t *__restrict__ X, int N, const uint16_t *__restrict__ payload, uint32_t payload_bytes,
@@ -467,11 +467,14 @@ __global__ __launch_bounds__(512) void k_bt8_f16(
     asm volatile("" ::"s"(bitmaps), "s"(payload), "s"(X), "s"(Y), "s"(N), "s"(payload_bytes), "s"(area_kb));
 
     // LDS: selector table (128 B) | row totals [NSTEP][16][8] | partials
-    // [nstep_max][nwaves][256] floats | staging [min(nstep_max, 3)][area_kb KB]
+    // [nstep_max][nwaves][256] floats, summed into Y at the end (RING:
+    // [min(nstep_max, 2)], step i in slot i % 2, summed after the next
+    // step's barrier; 0.45 us slower at 2 steps, 1 us at 8 where both fit) |
+    // staging [min(nstep_max, 3)][area_kb KB]
     uint32_t *lut_lds = reinterpret_cast<uint32_t *>(bf_smem);
     int32_t *wt = reinterpret_cast<int32_t *>(bf_smem + 128);
     float *part = reinterpret_cast<float *>(wt + NSTEP * BF_ROWS * BF8_WAVES);
-    uint8_t *stage = reinterpret_cast<uint8_t *>(part + nstep_max * nwaves * 256);
+    uint8_t *stage = reinterpret_cast<uint8_t *>(part + (RING ? min(nstep_max, 2) : nstep_max) * nwaves * 256);
     const uint32_t area = area_kb * 1024u;
     const uint32_t cap = area_kb * 64u;           // granules an area holds
     const uint32_t lut = bt_lds_addr(lut_lds);
@@ -531,6 +534,25 @@ __global__ __launch_bounds__(512) void k_bt8_f16(
                                                      u < n ? (g.g0 + u) * 16u : 0xFFFFFFF0u, 0, 0, BT_NT);
         }
     };
+    // Y of step i (ring): item (row j, column n) adds D[j][n] and D[8 + j][8 +
+    // n] of every wavefront (lanes (j/4)*16 + n and 32 + (j/4)*16 + 8 + n,
+    // register j % 4 in the 16x16 D layout), in wavefront order; one rounding
+    // to fp16. Thread t takes item t / nwaves when t % nwaves == 0: the 64
+    // items are spread over the wavefronts.
+    auto write_step = [&](int i) -> void {
+        if ((int)threadIdx.x % nwaves != 0) return;
+        const int o = (int)threadIdx.x / nwaves, j = (o >> 3) & 7, n = o & 7;
+        const int m = (s_begin + i) * 8 + j;
+        if (n >= N || m >= M) return;
+        const int k = j & 3, l1 = (j >> 2) * 16 + n, l2 = 32 + (j >> 2) * 16 + 8 + n;
+        float sum = 0.f;
+        for (int w = 0; w < nwaves; ++w) {
+            const float *pw = part + ((i & 1) * nwaves + w) * 256 + k * 64;
+            sum += pw[l1];
+            sum += pw[l2];
+        }
+        Y[(int64_t)n * M + m] = __builtin_bit_cast(uint16_t, (_Float16)sum);
+    };
     issue(0);
     bf_h8 xb[1][8];   // X of this lane's tile, loaded behind the first DMA (below)
     bt_v4i xg[1][8];  // the same in runs of the rows, before the transpose (XR: N > 4)
@@ -584,7 +606,8 @@ __global__ __launch_bounds__(512) void k_bt8_f16(
         }
         bt_wait_vm(0);   // this wavefront's share of step i landed (nothing later in flight)
         if (i + 1 < nstep) issue(i + 1);
-        bt_barrier_lds();   // everyone's share, every half-row total of step i
+        bt_barrier_lds();   // everyone's share, every half-row total of step i, step i - 1's partials
+        if (RING && i > 0) write_step(i - 1);
 
         const BtRange g = bf_range(eb[i], eb[i + 1]);
         // element index of the lane's first nonzero, counted from the step's first granule
@@ -610,26 +633,29 @@ __global__ __launch_bounds__(512) void k_bt8_f16(
         } else {
             bf_contract<1>(word, pstart, BfWinGlobal{prs, 4u * g.g0}, lut, xb, acc);
         }
-        float *pw = part + (i * nwaves + wave) * 256;
+        // (ring: slot i % 2 was last read by step i - 2's sum, before this step's barrier)
+        float *pw = part + ((RING ? (i & 1) : i) * nwaves + wave) * 256;
 #pragma unroll
         for (int k = 0; k < 4; ++k) pw[k * 64 + lane] = acc[0][k];
     }
     bt_barrier_lds();
-    // Y: item (step i, row j, column n) adds D[j][n] and D[8 + j][8 + n] of
-    // every wavefront (lanes (j/4)*16 + n and 32 + (j/4)*16 + 8 + n, register
-    // j % 4 in the 16x16 D layout), in wavefront order; one rounding to fp16
-    for (int o = threadIdx.x; o < nstep * 64; o += blockDim.x) {
-        const int i = o >> 6, j = (o >> 3) & 7, n = o & 7;
-        const int m = (s_begin + i) * 8 + j;
-        if (n >= N || m >= M) continue;
-        const int k = j & 3, l1 = (j >> 2) * 16 + n, l2 = 32 + (j >> 2) * 16 + 8 + n;
-        float sum = 0.f;
-        for (int w = 0; w < nwaves; ++w) {
-            const float *pw = part + (i * nwaves + w) * 256 + k * 64;
-            sum += pw[l1];
-            sum += pw[l2];
+    if constexpr (RING) {
+        write_step(nstep - 1);
+    } else {
+        // every step's Y, items over all the threads
+        for (int o = threadIdx.x; o < nstep * 64; o += blockDim.x) {
+            const int i = o >> 6, j = (o >> 3) & 7, n = o & 7;
+            const int m = (s_begin + i) * 8 + j;
+            if (n >= N || m >= M) continue;
+            const int k = j & 3, l1 = (j >> 2) * 16 + n, l2 = 32 + (j >> 2) * 16 + 8 + n;
+            float sum = 0.f;
+            for (int w = 0; w < nwaves; ++w) {
+                const float *pw = part + (i * nwaves + w) * 256 + k * 64;
+                sum += pw[l1];
+                sum += pw[l2];
+            }
+            Y[(int64_t)n * M + m] = __builtin_bit_cast(uint16_t, (_Float16)sum);
         }
-        Y[(int64_t)n * M + m] = __builtin_bit_cast(uint16_t, (_Float16)sum);
     }
 }
 
@@ -637,6 +663,7 @@ __global__ __launch_bounds__(512) void k_bt8_f16(
 struct Bf8Plan {
     int nwaves;
     int nstep;   // step slots per workgroup (2, 4 or 8), a template argument
+    int ring;    // partials in a ring of two step slots (NSTEP 8 only), a template argument
     unsigned grid;
     int sq, sr;
     uint32_t area_kb;
@@ -654,8 +681,9 @@ static bool bf8_plan(int64_t M, int64_t K, int64_t N, int64_t payload_bytes, Bf8
     const int64_t worst = 8 * T * 128 + 64;
     const int64_t est = std::min<int64_t>(worst, avg + avg / 5 + 2048) + 32;
     p->area_kb = (uint32_t)std::max<int64_t>(1, (est + 1023) / 1024);
-    const auto lds_of = [&](int64_t per_wg, int nstep) -> size_t {
-        return 128 + (size_t)nstep * BF_ROWS * BF8_WAVES * 4 + (size_t)per_wg * p->nwaves * 256 * 4 +
+    const auto lds_of = [&](int64_t per_wg, int nstep, bool ring) -> size_t {
+        return 128 + (size_t)nstep * BF_ROWS * BF8_WAVES * 4 +
+               (size_t)(ring ? std::min<int64_t>(per_wg, 2) : per_wg) * p->nwaves * 256 * 4 +
                (size_t)std::min<int64_t>(per_wg, 3) * p->area_kb * 1024;
     };
     // two steps per workgroup at least (the second streams in while the
@@ -663,21 +691,32 @@ static bool bf8_plan(int64_t M, int64_t K, int64_t N, int64_t payload_bytes, Bf8
     // suffices (the prologue loads every slot's words: fewer loads ahead of
     // the first DMA). Up to 8 steps each when that keeps the grid to one
     // workgroup per CU and fits the LDS, else up to 4 in rounds (11008 x 4096
-    // at N = 1: 24.0 us in 1.34 rounds of 4 steps, 8192 rows 13.5)
+    // at N = 1: 24.0 us in 1.34 rounds of 4 steps, 8192 rows 13.5); with the
+    // partials in a ring of two slots when only that fits and the rounds
+    // would leave part of a round idle (5 to 7 steps; density 0.5: 24.7 ->
+    // 20.2 us, N = 8 27.3 -> 21.7; at 8 steps the rounds do as well)
     int64_t grid = std::max<int64_t>(std::min<int64_t>((steps + 1) / 2, BF_CUS), (steps + 3) / 4);
     int nstep = (steps + grid - 1) / grid <= 2 ? 2 : 4;
+    bool ring = false;
     const int64_t grid8 = std::max<int64_t>(std::min<int64_t>((steps + 1) / 2, BF_CUS), (steps + 7) / 8);
     const int64_t per8 = (steps + grid8 - 1) / grid8;
-    if (per8 > 4 && grid8 <= BF_CUS && lds_of(per8, 8) <= (size_t)BF_LDS_MAX) {
-        grid = grid8;
-        nstep = 8;
+    if (per8 > 4 && grid8 <= BF_CUS) {
+        if (lds_of(per8, 8, false) <= (size_t)BF_LDS_MAX) {
+            grid = grid8;
+            nstep = 8;
+        } else if (per8 < 8 && lds_of(per8, 8, true) <= (size_t)BF_LDS_MAX) {
+            grid = grid8;
+            nstep = 8;
+            ring = true;
+        }
     }
     p->nstep = nstep;
+    p->ring = ring;
     p->grid = (unsigned)grid;
     p->sq = (int)(steps / grid);
     p->sr = (int)(steps % grid);
     const int64_t per_wg = (steps + grid - 1) / grid;
-    p->lds = lds_of(per_wg, nstep);
+    p->lds = lds_of(per_wg, nstep, ring);
     return p->lds <= (size_t)BF_LDS_MAX;
 }
 
@@ -693,13 +732,23 @@ static void launch_bt8_f16(const Bf8Plan &p, const uint64_t *bitmaps, const uint
         hipLaunchKernelGGL((k_bt8_f16<S, XR>), dim3(p.grid), dim3(64 * p.nwaves), p.lds, stream, offsets, M, K, \
                            p.sq, p.sr, bitmaps, X, N, payload, payload_bytes, Y, p.area_kb);                    \
     } while (0)
+#define BF8_LAUNCH_R(S, XR)                                                                                         \
+    do {                                                                                                            \
+        (void)hipFuncSetAttribute((const void *)k_bt8_f16<S, XR, true>,                                             \
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds);                          \
+        hipLaunchKernelGGL((k_bt8_f16<S, XR, true>), dim3(p.grid), dim3(64 * p.nwaves), p.lds, stream, offsets, M, \
+                           K, p.sq, p.sr, bitmaps, X, N, payload, payload_bytes, Y, p.area_kb);                     \
+    } while (0)
     if (p.nstep == 2) {
         if (N > 4) BF8_LAUNCH(2, true); else BF8_LAUNCH(2, false);
     } else if (p.nstep == 4) {
         if (N > 4) BF8_LAUNCH(4, true); else BF8_LAUNCH(4, false);
-    } else {
+    } else if (!p.ring) {
         if (N > 4) BF8_LAUNCH(8, true); else BF8_LAUNCH(8, false);
+    } else {
+        if (N > 4) BF8_LAUNCH_R(8, true); else BF8_LAUNCH_R(8, false);
     }
+#undef BF8_LAUNCH_R
 #undef BF8_LAUNCH
 }
 

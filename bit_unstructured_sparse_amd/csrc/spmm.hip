@@ -182,8 +182,8 @@ void describe_plan(int dtype, const Plan &p, char *launch, size_t n) {
                          p.bt.nbuf, p.bt.stagger);
             break;
         case PK_BT8F16:
-            snprintf(launch, n, " kernel=k_bt8_f16 grid=%u block=%d lds=%zu stage_kb=%u step_slots=%d", p.bf8.grid,
-                     64 * p.bf8.nwaves, p.bf8.lds, p.bf8.area_kb, p.bf8.nstep);
+            snprintf(launch, n, " kernel=k_bt8_f16 grid=%u block=%d lds=%zu stage_kb=%u step_slots=%d partial_ring=%d",
+                     p.bf8.grid, 64 * p.bf8.nwaves, p.bf8.lds, p.bf8.area_kb, p.bf8.nstep, p.bf8.ring);
             break;
         case PK_BT64F16:
             snprintf(launch, n, " kernel=k_bt64_f16 grid=%u block=%d lds=%zu stage_kb=%u stage_bufs=%u", p.bf.grid,

@@ -586,14 +586,16 @@ def test_splitk_f16_shared_cus(dev, M, K, N):
 
 
 @pytest.mark.parametrize("algo", [bsp.ALGO_AUTO, bsp.ALGO_MFMA], ids=["auto", "mfma"])
-@pytest.mark.parametrize("M,N", [(8200, 1), (11008, 8), (12288, 3)])
-def test_f16_eight_row_eight_steps(dev, M, N, algo):
+@pytest.mark.parametrize("M,N,dens,ring", [(8200, 1, 0.4, 0), (11008, 8, 0.4, 0), (12288, 3, 0.4, 0),
+                                           (11008, 8, 0.5, 1), (9000, 1, 0.5, 1), (12288, 5, 0.5, 1)])
+def test_f16_eight_row_eight_steps(dev, M, N, dens, ring, algo):
     # the eight-row fp16 kernel with up to 8 steps per workgroup (8200 rows:
-    # one workgroup of 5 steps, the rest 4)
-    p = workloads.random_fp16_problem(M + N, M, 4096, N, sparsity=0.6)
+    # one workgroup of 5 steps, the rest 4), every step's partials kept or
+    # in a ring of two slots
+    p = workloads.random_fp16_problem(M + N, M, 4096, N, sparsity=1.0 - dens)
     enc = bsp.encode(p.W)
     d = bsp.describe(bsp.FP16, M, 4096, N, enc.nnz)
-    assert "kernel=k_bt8_f16 " in d and "step_slots=8" in d, d
+    assert "kernel=k_bt8_f16 " in d and "step_slots=8" in d and f"partial_ring={ring}" in d, d
     _assert_f16(run_f16(p.W, p.X, algo, dev, enc=enc), oracle.spmm_f16(oracle.encode(p.W), p.X))
 
 

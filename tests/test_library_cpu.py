@@ -473,8 +473,13 @@ def test_f16_eight_row_plans_take_up_to_eight_steps():
         kv = _kv(bsp.describe(bsp.FP16, M, 4096, 1, int(M * 4096 * 0.4)))
         assert kv["step_slots"] == str(slots) and kv["grid"] == str(grid), (M, kv)
         assert int(kv["lds"]) <= 160 * 1024
-    kv = _kv(bsp.describe(bsp.FP16, 11008, 4096, 1, int(11008 * 4096 * 0.5)))   # 8 steps would not fit
-    assert kv["step_slots"] == "4" and kv["grid"] == "344", kv
+        assert kv["partial_ring"] == "0", (M, kv)
+    # 8 steps with every step's partials would not fit: the partials in a
+    # ring of two slots, where a workgroup has 5 to 7 steps
+    kv = _kv(bsp.describe(bsp.FP16, 11008, 4096, 1, int(11008 * 4096 * 0.5)))
+    assert kv["step_slots"] == "8" and kv["partial_ring"] == "1" and kv["grid"] == "256", kv
+    kv = _kv(bsp.describe(bsp.FP16, 16384, 4096, 1, int(16384 * 4096 * 0.5)))   # 8 steps each: rounds of 4
+    assert kv["step_slots"] == "4" and kv["grid"] == "512", kv
 
 
 def test_ring_plans_take_eight_blocks_at_two_tiles_per_lane():

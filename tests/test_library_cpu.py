@@ -322,7 +322,8 @@ def test_every_plan_fits_the_hardware():
     rng = np.random.default_rng(5)
     seen = set()
     for _ in range(600):
-        dt = bsp.INT4 if rng.random() < 0.6 else bsp.FP16
+        u = rng.random()
+        dt = bsp.INT4 if u < 0.5 else bsp.FP16 if u < 0.85 else bsp.INT2
         M = int(rng.integers(1, 70000))
         K = int(rng.integers(1, 40000))
         if dt == bsp.FP16 and rng.random() < 0.7:
@@ -340,12 +341,14 @@ def test_every_plan_fits_the_hardware():
                 assert m, d
                 seen.add(m.group(1))
                 f = {k: int(v) for k, v in re.findall(r"(\w+)=(\d+)", d.split("->")[1])}
+                if f.get("partial_ring"):
+                    assert f["step_slots"] == 8, d
                 if "lds" in f:
                     assert f["lds"] <= 160 * 1024, d
                     assert 64 <= f["block"] <= 1024 and f["block"] % 64 == 0, d
                     assert f["grid"] >= 1, d
     want = {"k_bt64s_w4a4", "k_bt64_w4a4", "k_bsk_w4a4", "k_bsks_w4a4", "k_bt8_f16", "k_bt64_f16", "k_bsk_f16",
-            "k_rowwave_w4a4", "k_rowwave_f16"}
+            "k_rowwave_w4a4", "k_rowwave_f16", "k_bt64s_w2a4"}
     assert want <= seen, want - seen
 
 

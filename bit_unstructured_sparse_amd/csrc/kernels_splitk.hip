@@ -784,11 +784,13 @@ static bool sk_plan(int dtype, int64_t M, int64_t K, int64_t N, int64_t payload_
     p->dtype = dtype;
     p->nb = N <= 16 ? 1 : 2;
     p->S = splits;
-    // blocks per set: as many as K ranges (int4), one (fp16: more, smaller
-    // workgroups that share the CUs; 4096 x 11008 at N = 1 with 2 ranges
-    // 25.6 -> 22.1 us, N = 8 27.7 -> 24.7, 4096 x 13824 33.0 -> 27.6,
-    // 11008 x 11008 72.1 -> 57.7) while one counter per block is left
-    p->nbs = dtype == BSP_FP16 && blocks <= SK_WS_COUNTERS ? 1 : splits;
+    // blocks per set: as many as K ranges, or one for fp16 at N <= 8 (more,
+    // smaller workgroups that share the CUs; 4096 x 11008 at N = 1 with 2
+    // ranges 25.6 -> 22.1 us, N = 8 27.7 -> 24.7, 4096 x 13824 33.0 -> 27.6,
+    // 11008 x 11008 72.1 -> 57.7) while one counter per block is left; at
+    // larger N each workgroup's reads of X outweigh that (N = 16 32.6 ->
+    // 36.0, N = 32 50.6 -> 64.5)
+    p->nbs = dtype == BSP_FP16 && N <= 8 && blocks <= SK_WS_COUNTERS ? 1 : splits;
     if (splits > 1 && (blocks + p->nbs - 1) / p->nbs > SK_WS_COUNTERS) return false;   // one counter per set
     p->nsets = (int)((blocks + p->nbs - 1) / p->nbs);
     p->tps = (int)((T + splits - 1) / splits);

@@ -128,7 +128,7 @@ def assert_w4a4(Y, W, X, ref=None):
 
 def oracle_w4a4(W, X):
     s = oracle.encode(W)
-    return oracle.spmm_w4a4(s, _pack_for_oracle(X), X.shape[0])
+    return oracle.spmm_w4a4(s, _pack_for_oracle(X), X.shape[0], threads=16)   # rows over 16 threads: the same result
 
 
 def _pack_for_oracle(X):
@@ -316,7 +316,7 @@ def _assert_f16(y, r):
 @pytest.mark.parametrize("M,K,N", SMALL_F16)
 def test_f16_small(dev, algo, M, K, N):
     p = workloads.random_fp16_problem(M + K + N, M, K, N)
-    _assert_f16(run_f16(p.W, p.X, algo, dev), oracle.spmm_f16(oracle.encode(p.W), p.X))
+    _assert_f16(run_f16(p.W, p.X, algo, dev), oracle.spmm_f16(oracle.encode(p.W), p.X, threads=16))
 
 
 @pytest.mark.parametrize("algo", F16_ALGOS, ids=lambda a: _NAMES[a])
@@ -362,7 +362,7 @@ def test_f16_zero_and_dense(dev, algo):
     y = run_f16(W, X, algo, dev)
     assert y is None or not y.any()
     p = workloads.random_fp16_problem(3, 40, 256, 4, sparsity=0.0)
-    _assert_f16(run_f16(p.W, p.X, algo, dev), oracle.spmm_f16(oracle.encode(p.W), p.X))
+    _assert_f16(run_f16(p.W, p.X, algo, dev), oracle.spmm_f16(oracle.encode(p.W), p.X, threads=16))
 
 
 # --- the named workloads at their full sizes -------------------------------------------------
@@ -378,7 +378,7 @@ def _full_int4(config, idx, nmax):
 @functools.lru_cache(maxsize=None)
 def _full_f16(idx):
     p = workloads.make("fp16")[idx]
-    return p, oracle.spmm_f16(oracle.encode(p.W), p.X)
+    return p, oracle.spmm_f16(oracle.encode(p.W), p.X, threads=16)
 
 
 FULL_INT4 = [("tiny", 0), ("qkv", 0), ("ffn", 0), ("ffn", 1), ("lowsparse", 0)]
@@ -504,7 +504,7 @@ def test_w4a4_large_grids_and_equal_rows(dev, M, K, N, keep, rows, algo):
 def test_f16_equal_rows(dev, algo, N):
     # every row pruned to the same count (rows 4096 B long)
     p = workloads.random_fp16_problem(77 + N, 4096, 4096, N, sparsity=0.5, rows=True)
-    _assert_f16(run_f16(p.W, p.X, algo, dev), oracle.spmm_f16(oracle.encode(p.W), p.X))
+    _assert_f16(run_f16(p.W, p.X, algo, dev), oracle.spmm_f16(oracle.encode(p.W), p.X, threads=16))
 
 
 EQUAL_ROWS = [  # (M, K, N, keep): every row keeps the same count; staggered staging
@@ -552,7 +552,7 @@ def test_f16_block_staging(dev, M, K, N, dens, algo):
     enc = bsp.encode(p.W)
     d = bsp.describe(bsp.FP16, M, K, N, enc.nnz, algo=bsp.ALGO_MFMA)
     assert "kernel=k_bt64_f16 " in d and "stage_kb=0 " not in d, d
-    _assert_f16(run_f16(p.W, p.X, algo, dev, enc=enc), oracle.spmm_f16(oracle.encode(p.W), p.X))
+    _assert_f16(run_f16(p.W, p.X, algo, dev, enc=enc), oracle.spmm_f16(oracle.encode(p.W), p.X, threads=16))
 
 
 @pytest.mark.parametrize("with_ws", [False, True], ids=["plain", "workspace"])
@@ -582,7 +582,7 @@ def test_splitk_f16_shared_cus(dev, M, K, N):
     enc = bsp.encode(p.W)
     d = bsp.describe(bsp.FP16, M, K, N, enc.nnz)
     assert "-> splitk kernel=k_bsk_f16 " in d and "block=1024" not in d, d
-    _assert_f16(run_f16(p.W, p.X, bsp.ALGO_AUTO, dev, enc=enc), oracle.spmm_f16(oracle.encode(p.W), p.X))
+    _assert_f16(run_f16(p.W, p.X, bsp.ALGO_AUTO, dev, enc=enc), oracle.spmm_f16(oracle.encode(p.W), p.X, threads=16))
 
 
 @pytest.mark.parametrize("algo", [bsp.ALGO_AUTO, bsp.ALGO_MFMA], ids=["auto", "mfma"])
@@ -596,7 +596,7 @@ def test_f16_eight_row_eight_steps(dev, M, N, dens, ring, algo):
     enc = bsp.encode(p.W)
     d = bsp.describe(bsp.FP16, M, 4096, N, enc.nnz)
     assert "kernel=k_bt8_f16 " in d and "step_slots=8" in d and f"partial_ring={ring}" in d, d
-    _assert_f16(run_f16(p.W, p.X, algo, dev, enc=enc), oracle.spmm_f16(oracle.encode(p.W), p.X))
+    _assert_f16(run_f16(p.W, p.X, algo, dev, enc=enc), oracle.spmm_f16(oracle.encode(p.W), p.X, threads=16))
 
 
 SPLITK_STREAMED = [  # (M, K, N, keep): the streamed split-K kernel (one pass per block and K range)
@@ -641,7 +641,7 @@ def test_splitk_f16(dev, M, K, N, with_ws):
     dm = enc.to_device(dev)
     Xd = torch.from_numpy(p.X).to(dev)
     ws = _ws(bsp.FP16, M, K, N, enc.nnz, dev) if with_ws else None
-    r = oracle.spmm_f16(oracle.encode(p.W), p.X)
+    r = oracle.spmm_f16(oracle.encode(p.W), p.X, threads=16)
     first = None
     for rep in range(2):
         big, Y = _y_with_canary(N, M, torch.float16, dev)
@@ -713,7 +713,7 @@ def test_f16_past_k4096_auto(dev, M, K, N):
     # with a workspace, 1 without), never the plain kernel
     p = workloads.random_fp16_problem(M + K + N, M, K, N)
     enc = bsp.encode(p.W)
-    r = oracle.spmm_f16(oracle.encode(p.W), p.X)
+    r = oracle.spmm_f16(oracle.encode(p.W), p.X, threads=16)
     for ws in (None, _ws(bsp.FP16, M, K, N, enc.nnz, dev)):
         d = bsp.describe(bsp.FP16, M, K, N, enc.nnz, workspace=ws is not None)
         assert "-> splitk kernel=k_bsk_f16" in d and ("splits=2 " in d) == (ws is not None), d
@@ -761,5 +761,5 @@ def test_splitk_workspace_reused_across_shapes(dev, dtype):
             enc = bsp.encode(p.W)
             Y = bsp.spmm_f16(enc.to_device(dev), torch.from_numpy(p.X).to(dev), algo=bsp.ALGO_SPLITK, workspace=ws)
             torch.cuda.synchronize()
-            _assert_f16(Y.cpu().numpy(), oracle.spmm_f16(oracle.encode(p.W), p.X))
+            _assert_f16(Y.cpu().numpy(), oracle.spmm_f16(oracle.encode(p.W), p.X, threads=16))
     assert not ws[:65536].any()
